@@ -1,0 +1,264 @@
+"""ctypes front end of the CPU oracle (oracle/gs_oracle.cpp).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+CPU-baseline leg of the benchmark, never by the HIP library or its binding.
+
+Every function takes and returns numpy arrays in the planar layouts of the
+library ([plane][n] per Gaussian, [ch][H][W] per image).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+
+
+class OrCamera(C.Structure):
+    _fields_ = [("R", C.c_float * 9), ("t", C.c_float * 3), ("campos", C.c_float * 3),
+                ("fx", C.c_float), ("fy", C.c_float), ("cx", C.c_float), ("cy", C.c_float),
+                ("width", C.c_int32), ("height", C.c_int32), ("znear", C.c_float), ("bg", C.c_float * 3)]
+
+
+def make_camera(cam) -> OrCamera:
+    c = OrCamera()
+    c.R[:] = [float(x) for x in np.asarray(cam.R, dtype=np.float32).reshape(9)]
+    c.t[:] = [float(x) for x in np.asarray(cam.t, dtype=np.float32)]
+    c.campos[:] = [float(x) for x in np.asarray(cam.campos, dtype=np.float32)]
+    c.fx, c.fy, c.cx, c.cy = cam.fx, cam.fy, cam.cx, cam.cy
+    c.width, c.height = cam.width, cam.height
+    c.znear = cam.znear
+    c.bg[:] = [float(x) for x in cam.bg]
+    return c
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from oracle import build as _b  # noqa: WPS433 (build on first use)
+            _b.build()
+        _lib = C.CDLL(LIB_PATH)
+        _declare(_lib)
+    return _lib
+
+
+P = C.c_void_p
+I64 = C.c_int64
+I32 = C.c_int
+
+
+def _declare(L):
+    L.or_num_planes.argtypes = [I32]
+    L.or_num_planes.restype = I32
+    L.or_sh_norm.argtypes = [I32, I32]
+    L.or_sh_norm.restype = C.c_double
+    L.or_sh_basis_f64.argtypes = [P, P, P]
+    for suf in ("f32", "f64"):
+        getattr(L, f"or_preprocess_{suf}").argtypes = [I64, I32, P, P, I32] + [P] * 10
+        getattr(L, f"or_render_smooth_fwd_{suf}").argtypes = [I64] + [P] * 7 + [P, P]
+        getattr(L, f"or_render_smooth_bwd_{suf}").argtypes = [I64] + [P] * 7 + [P, P, P]
+        getattr(L, f"or_preprocess_bwd_{suf}").argtypes = [I64, I32, P, P, I32, P, P]
+        getattr(L, f"or_adam_{suf}").argtypes = [P, P, P, P, I64, I32, P, C.c_double, C.c_double,
+                                                 C.c_double, I32]
+    L.or_loss_f32.argtypes = [P, P, I32, I32, C.c_float, P, P]
+    L.or_loss_f64.argtypes = [P, P, I32, I32, C.c_double, P, P]
+    L.or_bin_sort.argtypes = [I64, P, P, P, I32, I32, P, P, P]
+    L.or_render_fwd_f32.argtypes = [I64] + [P] * 6 + [P] + [P] * 5
+    L.or_render_fwd_f32.restype = I64
+    L.or_render_untiled_f32.argtypes = [I64] + [P] * 6 + [P, P, P]
+    L.or_render_pixels_f32.argtypes = [I64] + [P] * 6 + [P, I64, P, P, P, P, P, P]
+    L.or_render_bwd_f32.argtypes = [I64] + [P] * 6 + [P] + [P] * 7
+
+
+def _p(a):
+    return a.ctypes.data_as(C.c_void_p) if a is not None else None
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_planes(deg):
+    return lib().or_num_planes(deg)
+
+
+# ----------------------------------------------------------------- forward
+def preprocess(params, sh_degree, cam, smooth=False, dtype=np.float32):
+    """Per-Gaussian projection. Returns a dict of planar arrays."""
+    params = _c(params, dtype)
+    n = params.shape[1]
+    out = dict(uv=np.zeros((2, n), dtype), conic=np.zeros((3, n), dtype), opac=np.zeros(n, dtype),
+               rgb=np.zeros((3, n), dtype), depth=np.zeros(n, dtype), rect=np.zeros((4, n), np.int32),
+               tiles=np.zeros(n, np.uint32), visible=np.zeros(n, np.uint8), cov2d=np.zeros((3, n), dtype),
+               extent=np.zeros(n, dtype))
+    fn = lib().or_preprocess_f32 if dtype == np.float32 else lib().or_preprocess_f64
+    c = make_camera(cam)
+    fn(n, sh_degree, _p(params), C.byref(c), int(smooth), _p(out["uv"]), _p(out["conic"]), _p(out["opac"]),
+       _p(out["rgb"]), _p(out["depth"]), _p(out["rect"]), _p(out["tiles"]), _p(out["visible"]),
+       _p(out["cov2d"]), _p(out["extent"]))
+    out["n"] = n
+    return out
+
+
+def bin_sort(pre, cam):
+    """Keys, ids and per-tile ranges ([2][tiles]) of the stable (tile, depth, id) order."""
+    n = pre["n"]
+    total = int(pre["tiles"].astype(np.int64).sum())
+    keys = np.zeros(total, np.uint64)
+    vals = np.zeros(total, np.uint32)
+    nt = cam.tiles_x * cam.tiles_y
+    ranges = np.zeros((2, nt), np.uint32)
+    lib().or_bin_sort(n, _p(_c(pre["depth"], np.float32)), _p(pre["rect"]), _p(pre["tiles"]), cam.tiles_x,
+                      cam.tiles_y, _p(keys), _p(vals), _p(ranges))
+    return keys, vals, ranges
+
+
+def render_fwd(pre, vals, ranges, cam):
+    n = pre["n"]
+    H, W = cam.height, cam.width
+    out = dict(rgb=np.zeros((3, H, W), np.float32), T=np.zeros((H, W), np.float32),
+               n_contrib=np.zeros((H, W), np.uint32), n_examined=np.zeros((H, W), np.uint32),
+               margin=np.zeros((H, W), np.float64))
+    c = make_camera(cam)
+    out["evals"] = int(lib().or_render_fwd_f32(
+        n, _p(pre["uv"]), _p(pre["conic"]), _p(pre["opac"]), _p(pre["rgb"]), _p(_c(vals, np.uint32)),
+        _p(_c(ranges, np.uint32)), C.byref(c), _p(out["rgb"]), _p(out["T"]), _p(out["n_contrib"]),
+        _p(out["n_examined"]), _p(out["margin"])))
+    return out
+
+
+def render_untiled(pre, cam):
+    H, W = cam.height, cam.width
+    img = np.zeros((3, H, W), np.float32)
+    T = np.zeros((H, W), np.float32)
+    c = make_camera(cam)
+    lib().or_render_untiled_f32(pre["n"], _p(pre["uv"]), _p(pre["conic"]), _p(pre["opac"]), _p(pre["rgb"]),
+                                _p(pre["depth"]), _p(pre["visible"]), C.byref(c), _p(img), _p(T))
+    return img, T
+
+
+def render_pixels(pre, vals, ranges, cam, xs, ys):
+    n = pre["n"]
+    xs = _c(xs, np.int32)
+    ys = _c(ys, np.int32)
+    k = xs.shape[0]
+    rgb = np.zeros((k, 3), np.float32)
+    T = np.zeros(k, np.float32)
+    nc = np.zeros(k, np.uint32)
+    margin = np.zeros(k, np.float64)
+    c = make_camera(cam)
+    lib().or_render_pixels_f32(n, _p(pre["uv"]), _p(pre["conic"]), _p(pre["opac"]), _p(pre["rgb"]),
+                               _p(_c(vals, np.uint32)), _p(_c(ranges, np.uint32)), C.byref(c), k, _p(xs),
+                               _p(ys), _p(rgb), _p(T), _p(nc), _p(margin))
+    return dict(rgb=rgb, T=T, n_contrib=nc, margin=margin)
+
+
+def render_bwd(pre, vals, ranges, cam, fwd, dLdI, with_margin=True):
+    n = pre["n"]
+    gscreen = np.zeros((9, n), np.float32)
+    gmargin = np.zeros(n, np.float64) if with_margin else None
+    c = make_camera(cam)
+    lib().or_render_bwd_f32(n, _p(pre["uv"]), _p(pre["conic"]), _p(pre["opac"]), _p(pre["rgb"]),
+                            _p(_c(vals, np.uint32)), _p(_c(ranges, np.uint32)), C.byref(c), _p(fwd["T"]),
+                            _p(fwd["n_contrib"]), _p(_c(dLdI, np.float32)), _p(gscreen),
+                            _p(fwd["n_examined"]) if with_margin else None,
+                            _p(fwd["margin"]) if with_margin else None, _p(gmargin))
+    return gscreen, gmargin
+
+
+def preprocess_bwd(params, sh_degree, cam, gscreen, smooth=False, dtype=np.float32):
+    params = _c(params, dtype)
+    gscreen = _c(gscreen, dtype)
+    n = params.shape[1]
+    g = np.zeros_like(params)
+    fn = lib().or_preprocess_bwd_f32 if dtype == np.float32 else lib().or_preprocess_bwd_f64
+    c = make_camera(cam)
+    fn(n, sh_degree, _p(params), C.byref(c), int(smooth), _p(gscreen), _p(g))
+    return g
+
+
+# ------------------------------------------------------------- smooth mode
+def smooth_render(params, sh_degree, cam, dtype=np.float64):
+    """Render with every threshold off (all Gaussians, all pixels, depth order)."""
+    pre = preprocess(params, sh_degree, cam, smooth=True, dtype=dtype)
+    H, W = cam.height, cam.width
+    img = np.zeros((3, H, W), dtype)
+    T = np.zeros((H, W), dtype)
+    fn = lib().or_render_smooth_fwd_f64 if dtype == np.float64 else lib().or_render_smooth_fwd_f32
+    c = make_camera(cam)
+    fn(pre["n"], _p(pre["uv"]), _p(pre["conic"]), _p(pre["opac"]), _p(pre["rgb"]), _p(pre["depth"]),
+       _p(pre["visible"]), C.byref(c), _p(img), _p(T))
+    return img, T, pre
+
+
+def smooth_grad(params, sh_degree, cam, dLdI, dtype=np.float64):
+    """Analytic gradient of sum(dLdI * smooth_render) with respect to the parameters."""
+    img, T, pre = smooth_render(params, sh_degree, cam, dtype)
+    n = pre["n"]
+    gscreen = np.zeros((9, n), dtype)
+    fn = lib().or_render_smooth_bwd_f64 if dtype == np.float64 else lib().or_render_smooth_bwd_f32
+    c = make_camera(cam)
+    fn(n, _p(pre["uv"]), _p(pre["conic"]), _p(pre["opac"]), _p(pre["rgb"]), _p(pre["depth"]),
+       _p(pre["visible"]), C.byref(c), _p(T), _p(_c(dLdI, dtype)), _p(gscreen))
+    return preprocess_bwd(params, sh_degree, cam, gscreen, smooth=True, dtype=dtype), gscreen, img
+
+
+# -------------------------------------------------------------------- loss
+def loss(img, tgt, lam=0.2, dtype=np.float64, with_grad=True):
+    """0.8 L1 + 0.2 (1 - SSIM); returns ((total, L1, SSIM), dL/dimg)."""
+    img = _c(img, dtype)
+    tgt = _c(tgt, dtype)
+    _, H, W = img.shape
+    out = np.zeros(3, dtype)
+    grad = np.zeros_like(img) if with_grad else None
+    fn = lib().or_loss_f64 if dtype == np.float64 else lib().or_loss_f32
+    fn(_p(img), _p(tgt), H, W, lam, _p(out), _p(grad))
+    return tuple(float(x) for x in out), grad
+
+
+# -------------------------------------------------------------------- Adam
+def adam(params, grads, m, v, sh_degree, lr, step, b1=0.9, b2=0.999, eps=1e-8, dtype=np.float64):
+    """Returns updated (params, m, v) as new arrays."""
+    params = np.array(params, dtype=dtype, copy=True)
+    m = np.array(m, dtype=dtype, copy=True)
+    v = np.array(v, dtype=dtype, copy=True)
+    grads = _c(grads, dtype)
+    lr = np.ascontiguousarray(lr, dtype=np.float64)
+    n = params.shape[1]
+    fn = lib().or_adam_f64 if dtype == np.float64 else lib().or_adam_f32
+    fn(_p(params), _p(grads), _p(m), _p(v), n, sh_degree, _p(lr), b1, b2, eps, step)
+    return params, m, v
+
+
+def sh_basis(d):
+    d = np.ascontiguousarray(d, np.float64)
+    Y = np.zeros(16)
+    dY = np.zeros(48)
+    lib().or_sh_basis_f64(_p(d), _p(Y), _p(dY))
+    return Y, dY.reshape(16, 3)
+
+
+# ------------------------------------------------------------ full forward
+def forward(scene_params, sh_degree, cam):
+    """Preprocess, bin/sort and render: everything the forward path produces."""
+    pre = preprocess(scene_params, sh_degree, cam)
+    keys, vals, ranges = bin_sort(pre, cam)
+    fwd = render_fwd(pre, vals, ranges, cam)
+    return pre, keys, vals, ranges, fwd
+
+
+def train_step_grads(scene_params, sh_degree, cam, target, lam=0.2):
+    """Forward, loss and backward of one camera; returns a dict of every stage's output."""
+    pre, keys, vals, ranges, fwd = forward(scene_params, sh_degree, cam)
+    (total, l1, ssim), dLdI = loss(fwd["rgb"], target, lam)
+    gscreen, gmargin = render_bwd(pre, vals, ranges, cam, fwd, dLdI.astype(np.float32))
+    gparams = preprocess_bwd(scene_params, sh_degree, cam, gscreen)
+    return dict(pre=pre, keys=keys, vals=vals, ranges=ranges, fwd=fwd, loss=(total, l1, ssim), dLdI=dLdI,
+                gscreen=gscreen, gmargin=gmargin, gparams=gparams)
