@@ -1,0 +1,189 @@
+// The C ABI declared in include/gs.h: argument checks, workspace carving and the
+// launches of the kernels in the other translation units.  No call allocates.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "gs_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int32_t hip_fail(hipError_t e, const char* where) {
+  return fail(GS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int32_t check_camera(const gs_camera* cam) {
+  if (!cam) return fail(GS_ERR_INVALID_ARG, "camera is null");
+  if (cam->width <= 0 || cam->height <= 0) return fail(GS_ERR_INVALID_ARG, "image size must be positive");
+  if (gsk::tiles_x(*cam) > 65535 || gsk::tiles_y(*cam) > 65535)
+    return fail(GS_ERR_UNSUPPORTED, "more than 65535 tiles along one image axis");
+  if (int64_t(gsk::tiles_x(*cam)) * gsk::tiles_y(*cam) > (int64_t(1) << 30))
+    return fail(GS_ERR_UNSUPPORTED, "too many tiles");
+  if (!(cam->fx > 0.0f) || !(cam->fy > 0.0f)) return fail(GS_ERR_INVALID_ARG, "focal lengths must be positive");
+  if (!(cam->znear > 0.0f)) return fail(GS_ERR_INVALID_ARG, "znear must be positive");
+  return GS_OK;
+}
+
+int32_t check_scene(const gs_scene* sc) {
+  if (!sc) return fail(GS_ERR_INVALID_ARG, "scene is null");
+  if (sc->n < 0 || sc->n >= (int64_t(1) << 31)) return fail(GS_ERR_INVALID_ARG, "n out of range");
+  if (sc->sh_degree < 0 || sc->sh_degree > 3) return fail(GS_ERR_UNSUPPORTED, "SH degree must be 0..3");
+  if (sc->n > 0 && !sc->params) return fail(GS_ERR_INVALID_ARG, "params is null");
+  if (sc->n * gsk::num_planes(sc->sh_degree) >= (int64_t(1) << 31))
+    return fail(GS_ERR_UNSUPPORTED, "n * planes must stay below 2^31");
+  return GS_OK;
+}
+
+int32_t check_proj(const gs_proj* p, int64_t n, bool need_offs) {
+  if (!p) return fail(GS_ERR_INVALID_ARG, "proj is null");
+  if (need_offs && !p->offs) return fail(GS_ERR_INVALID_ARG, "proj.offs is null");
+  if (n > 0 && (!p->splat || !p->depth || !p->rect || !p->tiles))
+    return fail(GS_ERR_INVALID_ARG, "a proj array is null");
+  return GS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gs_last_error(void) { return g_err; }
+
+size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H) {
+  switch (which_call) {
+    case GS_WS_PREPROCESS: return gsk::scan_ws_bytes(n < 0 ? 0 : n) + 256;
+    case GS_WS_BIN_SORT: return gsk::bin_sort_ws_bytes(pairs, 0);
+    case GS_WS_LOSS: return (W > 0 && H > 0) ? gsk::loss_ws_bytes(H, W) : 0;
+    default: return 0;
+  }
+}
+
+int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out, uint32_t* total_pairs, void* ws,
+                      size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int32_t st;
+  if ((st = check_scene(scene)) != GS_OK) return st;
+  if ((st = check_camera(cam)) != GS_OK) return st;
+  if ((st = check_proj(out, scene->n, true)) != GS_OK) return st;
+  if (!total_pairs) return fail(GS_ERR_INVALID_ARG, "total_pairs is null");
+  const size_t need = gs_workspace_bytes(GS_WS_PREPROCESS, scene->n, 0, 0, 0);
+  if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "preprocess workspace needs %zu bytes", need);
+  hipStream_t s = as_stream(stream);
+  const int n = int(scene->n);
+  hipError_t e = gsk::launch_preprocess_fwd(scene->params, n, scene->sh_degree, *cam, *out, s);
+  if (e != hipSuccess) return hip_fail(e, "preprocess_fwd");
+  uint64_t* total64 = static_cast<uint64_t*>(ws);
+  void* scan_ws = static_cast<char*>(ws) + 256;
+  e = gsk::launch_scan_u32(out->tiles, out->offs, n, total64, scan_ws, s);
+  if (e != hipSuccess) return hip_fail(e, "scan");
+  uint64_t host_total = 0;
+  e = hipMemcpyAsync(&host_total, total64, sizeof(uint64_t), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "pair count copy");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "preprocess sync");
+  if (host_total > 0xffffffffull)
+    return fail(GS_ERR_CAPACITY, "pair count %llu exceeds 2^32 - 1", (unsigned long long)host_total);
+  *total_pairs = uint32_t(host_total);
+  return GS_OK;
+}
+
+int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32_t total_pairs, uint64_t* keys,
+                    uint32_t* vals, uint32_t capacity, uint32_t* ranges, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int32_t st;
+  if (n < 0 || n >= (int64_t(1) << 31)) return fail(GS_ERR_INVALID_ARG, "n out of range");
+  if ((st = check_camera(cam)) != GS_OK) return st;
+  if ((st = check_proj(proj, n, true)) != GS_OK) return st;
+  if (!ranges) return fail(GS_ERR_INVALID_ARG, "ranges is null");
+  if (total_pairs > 0 && (!keys || !vals)) return fail(GS_ERR_INVALID_ARG, "keys or vals is null");
+  if (total_pairs > 0 && n == 0) return fail(GS_ERR_INVALID_ARG, "pairs without Gaussians");
+  if (capacity < total_pairs)
+    return fail(GS_ERR_CAPACITY, "key capacity %u < %u pairs", capacity, total_pairs);
+  const size_t need = gs_workspace_bytes(GS_WS_BIN_SORT, n, total_pairs, cam->width, cam->height);
+  if (total_pairs > 0 && (!ws || ws_bytes < need))
+    return fail(GS_ERR_CAPACITY, "bin_sort workspace needs %zu bytes", need);
+  hipError_t e = gsk::launch_bin_sort(*proj, int(n), *cam, total_pairs, keys, vals, ranges, ws, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "bin_sort");
+  return GS_OK;
+}
+
+int32_t gs_render_fwd(const gs_proj* proj, int64_t n, const uint32_t* vals, const uint32_t* ranges,
+                      const gs_camera* cam, float* rgb, float* T_final, uint32_t* n_contrib, void* stream) {
+  g_err[0] = 0;
+  int32_t st;
+  if (n < 0 || n >= (int64_t(1) << 31)) return fail(GS_ERR_INVALID_ARG, "n out of range");
+  if ((st = check_camera(cam)) != GS_OK) return st;
+  if ((st = check_proj(proj, n, false)) != GS_OK) return st;
+  if (!ranges || !rgb || !T_final || !n_contrib) return fail(GS_ERR_INVALID_ARG, "an output or ranges is null");
+  hipError_t e = gsk::launch_render_fwd(*proj, vals, ranges, *cam, rgb, T_final, n_contrib, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "render_fwd");
+  return GS_OK;
+}
+
+int32_t gs_loss_l1_dssim(const float* img, const float* target, int32_t H, int32_t W, float lambda_dssim,
+                         float* loss_out, float* dL_dimg, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!img || !target || !loss_out || !dL_dimg) return fail(GS_ERR_INVALID_ARG, "a loss argument is null");
+  if (H <= 0 || W <= 0) return fail(GS_ERR_INVALID_ARG, "image size must be positive");
+  if (int64_t(3) * H * W >= (int64_t(1) << 31)) return fail(GS_ERR_UNSUPPORTED, "image too large");
+  if (!(lambda_dssim >= 0.0f && lambda_dssim <= 1.0f)) return fail(GS_ERR_INVALID_ARG, "lambda must be in [0, 1]");
+  const size_t need = gs_workspace_bytes(GS_WS_LOSS, 0, 0, W, H);
+  if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "loss workspace needs %zu bytes", need);
+  hipError_t e = gsk::launch_loss(img, target, H, W, lambda_dssim, loss_out, dL_dimg, ws, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "loss");
+  return GS_OK;
+}
+
+int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t* vals, const uint32_t* ranges,
+                      const gs_camera* cam, const float* T_final, const uint32_t* n_contrib,
+                      const float* dL_dimg, float* gscreen, float* gparams, void* stream) {
+  g_err[0] = 0;
+  int32_t st;
+  if ((st = check_scene(scene)) != GS_OK) return st;
+  if ((st = check_camera(cam)) != GS_OK) return st;
+  if ((st = check_proj(proj, scene->n, false)) != GS_OK) return st;
+  if (!ranges || !T_final || !n_contrib || !dL_dimg) return fail(GS_ERR_INVALID_ARG, "a render input is null");
+  if (scene->n > 0 && (!gscreen || !gparams)) return fail(GS_ERR_INVALID_ARG, "gscreen or gparams is null");
+  hipStream_t s = as_stream(stream);
+  const int n = int(scene->n);
+  hipError_t e = gsk::launch_render_bwd(*proj, n, vals, ranges, *cam, T_final, n_contrib, dL_dimg, gscreen, s);
+  if (e != hipSuccess) return hip_fail(e, "render_bwd");
+  e = gsk::launch_preprocess_bwd(scene->params, n, scene->sh_degree, *cam, proj->tiles, gscreen, gparams, s);
+  if (e != hipSuccess) return hip_fail(e, "preprocess_bwd");
+  return GS_OK;
+}
+
+int32_t gs_adam_step(float* params, const float* grads, float* m, float* v, int64_t n, int32_t sh_degree,
+                     const float* lr, double beta1, double beta2, double eps, int32_t step, void* stream) {
+  g_err[0] = 0;
+  if (n < 0 || n >= (int64_t(1) << 31)) return fail(GS_ERR_INVALID_ARG, "n out of range");
+  if (sh_degree < 0 || sh_degree > 3) return fail(GS_ERR_UNSUPPORTED, "SH degree must be 0..3");
+  if (!lr) return fail(GS_ERR_INVALID_ARG, "lr is null");
+  if (n > 0 && (!params || !grads || !m || !v)) return fail(GS_ERR_INVALID_ARG, "an Adam array is null");
+  if (n * gsk::num_planes(sh_degree) >= (int64_t(1) << 31))
+    return fail(GS_ERR_UNSUPPORTED, "n * planes must stay below 2^31");
+  if (step < 1) return fail(GS_ERR_INVALID_ARG, "step must be >= 1");
+  if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps >= 0.0))
+    return fail(GS_ERR_INVALID_ARG, "bad Adam hyper-parameters");
+  // bias corrections in fp64 on the host
+  const double bc1 = 1.0 - pow(beta1, double(step));
+  const double bc2 = 1.0 - pow(beta2, double(step));
+  hipError_t e = gsk::launch_adam(params, grads, m, v, int(n), sh_degree, lr, float(beta1), float(beta2),
+                                  float(1.0 - beta1), float(1.0 - beta2), float(eps), float(1.0 / bc1),
+                                  float(1.0 / bc2), as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "adam");
+  return GS_OK;
+}
+
+}  // extern "C"

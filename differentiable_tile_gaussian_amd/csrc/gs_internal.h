@@ -1,0 +1,54 @@
+// Internal declarations shared by the HIP translation units of libgs.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gs.h"
+
+namespace gsk {
+
+constexpr int kTile = 16;          // 16x16 pixel tiles
+constexpr int kTilePixels = kTile * kTile;
+
+inline int tiles_x(const gs_camera& c) { return (c.width + kTile - 1) / kTile; }
+inline int tiles_y(const gs_camera& c) { return (c.height + kTile - 1) / kTile; }
+inline int num_planes(int deg) { return 11 + 3 * (deg + 1) * (deg + 1); }
+
+inline unsigned div_up(int64_t a, int64_t b) { return unsigned((a + b - 1) / b); }
+
+// ---- preprocess.hip
+hipError_t launch_preprocess_fwd(const float* params, int n, int deg, const gs_camera& cam, const gs_proj& out,
+                                 hipStream_t s);
+hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_camera& cam,
+                                 const uint32_t* tiles, const float* gscreen, float* gparams, hipStream_t s);
+
+// ---- scan.hip: exclusive prefix sum of n u32 values into out[0..n], out[n] = total.
+// The total is also written as u64 to *total64 (device) so that overflow of 32 bits is seen.
+size_t scan_ws_bytes(int64_t n);
+hipError_t launch_scan_u32(const uint32_t* in, uint32_t* out, int64_t n, uint64_t* total64, void* ws,
+                           hipStream_t s);
+
+// ---- sort.hip
+size_t bin_sort_ws_bytes(uint32_t pairs, int num_tiles);
+hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uint32_t pairs, uint64_t* keys,
+                           uint32_t* vals, uint32_t* ranges, void* ws, hipStream_t s);
+
+// ---- render.hip
+hipError_t launch_render_fwd(const gs_proj& proj, const uint32_t* vals, const uint32_t* ranges,
+                             const gs_camera& cam, float* rgb, float* T_final, uint32_t* n_contrib, hipStream_t s);
+hipError_t launch_render_bwd(const gs_proj& proj, int n, const uint32_t* vals, const uint32_t* ranges,
+                             const gs_camera& cam, const float* T_final, const uint32_t* n_contrib,
+                             const float* dL_dimg, float* gscreen, hipStream_t s);
+
+// ---- loss.hip
+size_t loss_ws_bytes(int H, int W);
+hipError_t launch_loss(const float* img, const float* target, int H, int W, float lambda, float* loss_out,
+                       float* grad, void* ws, hipStream_t s);
+
+// ---- adam.hip
+hipError_t launch_adam(float* params, const float* grads, float* m, float* v, int n, int deg, const float lr[5],
+                       float b1, float b2, float omb1, float omb2, float eps, float inv_bc1, float inv_bc2,
+                       hipStream_t s);
+
+}  // namespace gsk

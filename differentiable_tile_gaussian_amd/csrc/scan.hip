@@ -1,0 +1,142 @@
+// Exclusive prefix sum of u32 values (reduce, then scan of the block sums, then
+// apply).  Used for the per-Gaussian tile counts ([GSG] "Why tiling, and the five
+// stages": the scan that reserves each Gaussian's slot range) and for the radix
+// sort's digit histograms.  No inter-block waiting: three plain launches.
+#include "gs_internal.h"
+
+namespace gsk {
+namespace {
+
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = 8;
+constexpr int kScanTile = kScanThreads * kScanItems;   // 2048 values per block
+
+__device__ inline uint32_t wave_inclusive_scan(uint32_t v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+__device__ inline uint64_t wave_inclusive_scan64(uint64_t v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// Exclusive scan across the 256 threads of a block; returns the prefix of this
+// thread and writes the block total to *total.
+__device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
+  const int lane = __lane_id(), wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_inclusive_scan(v);
+  if (lane == 63) s_wave[wave] = inc;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+  for (int w = 0; w < kScanThreads / 64; ++w) {
+    if (w < wave) base += s_wave[w];
+    tot += s_wave[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+__global__ void __launch_bounds__(kScanThreads) scan_reduce_kernel(const uint32_t* __restrict__ in, int64_t n,
+                                                                   uint64_t* __restrict__ block_sums) {
+  __shared__ uint32_t s_wave[kScanThreads / 64];
+  const int64_t base = int64_t(blockIdx.x) * kScanTile;
+  uint32_t sum = 0;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    const int64_t idx = base + int64_t(k) * kScanThreads + threadIdx.x;
+    if (idx < n) sum += in[idx];
+  }
+  uint32_t total;
+  block_exclusive_scan(sum, s_wave, &total);
+  if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
+}
+
+// One block: exclusive scan of nb u64 block sums in place; writes the grand total.
+__global__ void __launch_bounds__(1024) scan_blocks_kernel(uint64_t* __restrict__ sums, int nb,
+                                                           uint64_t* __restrict__ total64,
+                                                           uint32_t* __restrict__ out_last) {
+  __shared__ uint64_t s_wave[16];
+  __shared__ uint64_t s_carry;
+  if (threadIdx.x == 0) s_carry = 0;
+  __syncthreads();
+  const int lane = __lane_id(), wave = threadIdx.x >> 6;
+  for (int base = 0; base < nb; base += 1024) {
+    const int idx = base + threadIdx.x;
+    const uint64_t v = idx < nb ? sums[idx] : 0;
+    const uint64_t inc = wave_inclusive_scan64(v);
+    if (lane == 63) s_wave[wave] = inc;
+    __syncthreads();
+    uint64_t pre = s_carry, tot = 0;
+    for (int w = 0; w < 16; ++w) {
+      if (w < wave) pre += s_wave[w];
+      tot += s_wave[w];
+    }
+    if (idx < nb) sums[idx] = pre + inc - v;
+    __syncthreads();
+    if (threadIdx.x == 0) s_carry += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    *total64 = s_carry;
+    *out_last = uint32_t(s_carry);
+  }
+}
+
+__global__ void __launch_bounds__(kScanThreads) scan_apply_kernel(const uint32_t* __restrict__ in, int64_t n,
+                                                                  const uint64_t* __restrict__ block_prefix,
+                                                                  uint32_t* __restrict__ out) {
+  __shared__ uint32_t s_wave[kScanThreads / 64];
+  // thread t owns kScanItems consecutive values of the block's tile
+  const int64_t base = int64_t(blockIdx.x) * kScanTile + int64_t(threadIdx.x) * kScanItems;
+  uint32_t v[kScanItems];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    v[k] = (base + k < n) ? in[base + k] : 0u;
+    sum += v[k];
+  }
+  uint32_t total;
+  uint32_t run = block_exclusive_scan(sum, s_wave, &total) + uint32_t(block_prefix[blockIdx.x]);
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    if (base + k < n) out[base + k] = run;
+    run += v[k];
+  }
+}
+
+__global__ void scan_empty_kernel(uint32_t* out, uint64_t* total64) {
+  out[0] = 0u;
+  *total64 = 0u;
+}
+
+}  // namespace
+
+size_t scan_ws_bytes(int64_t n) { return size_t(div_up(n > 0 ? n : 1, kScanTile)) * sizeof(uint64_t); }
+
+hipError_t launch_scan_u32(const uint32_t* in, uint32_t* out, int64_t n, uint64_t* total64, void* ws,
+                           hipStream_t s) {
+  if (n == 0) {
+    scan_empty_kernel<<<1, 1, 0, s>>>(out, total64);
+    return hipGetLastError();
+  }
+  const int nb = int(div_up(n, kScanTile));
+  uint64_t* sums = static_cast<uint64_t*>(ws);
+  scan_reduce_kernel<<<nb, kScanThreads, 0, s>>>(in, n, sums);
+  scan_blocks_kernel<<<1, 1024, 0, s>>>(sums, nb, total64, out + n);
+  scan_apply_kernel<<<nb, kScanThreads, 0, s>>>(in, n, sums, out);
+  return hipGetLastError();
+}
+
+}  // namespace gsk

@@ -1,0 +1,168 @@
+"""ctypes binding of libgs.so (include/gs.h).
+
+The functions below have the names of the C entry points and do argument
+marshalling only: torch tensors supply device memory and the current HIP stream,
+every step of the rasteriser runs in the library's HIP kernels.  There is no CPU
+fallback: if libgs.so is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+import torch  # noqa: F401  (loads the HIP runtime the library then binds to)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgs.so")
+
+GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_UNSUPPORTED, GS_ERR_HIP = 0, -1, -2, -3, -4
+GS_WS_PREPROCESS, GS_WS_BIN_SORT, GS_WS_LOSS = 0, 1, 2
+
+EXPORTED = ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
+            "gs_adam_step", "gs_workspace_bytes", "gs_last_error")
+
+
+class GsError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"gs status {status}: {message}")
+        self.status = status
+
+
+class GsCamera(C.Structure):
+    _fields_ = [("R", C.c_float * 9), ("t", C.c_float * 3), ("campos", C.c_float * 3),
+                ("fx", C.c_float), ("fy", C.c_float), ("cx", C.c_float), ("cy", C.c_float),
+                ("width", C.c_int32), ("height", C.c_int32), ("znear", C.c_float), ("bg", C.c_float * 3)]
+
+
+class GsScene(C.Structure):
+    _fields_ = [("n", C.c_int64), ("sh_degree", C.c_int32), ("params", C.c_void_p)]
+
+
+class GsProj(C.Structure):
+    _fields_ = [("splat", C.c_void_p), ("depth", C.c_void_p), ("rect", C.c_void_p), ("tiles", C.c_void_p),
+                ("offs", C.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    lib = C.CDLL(LIB_PATH)
+    P, I64, I32, U32 = C.c_void_p, C.c_int64, C.c_int32, C.c_uint32
+    lib.gs_preprocess.argtypes = [P, P, P, P, P, C.c_size_t, P]
+    lib.gs_bin_sort.argtypes = [P, I64, P, U32, P, P, U32, P, P, C.c_size_t, P]
+    lib.gs_render_fwd.argtypes = [P, I64, P, P, P, P, P, P, P]
+    lib.gs_loss_l1_dssim.argtypes = [P, P, I32, I32, C.c_float, P, P, P, C.c_size_t, P]
+    lib.gs_render_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P]
+    lib.gs_adam_step.argtypes = [P, P, P, P, I64, I32, P, C.c_double, C.c_double, C.c_double, I32, P]
+    lib.gs_workspace_bytes.argtypes = [I32, I64, U32, I32, I32]
+    lib.gs_workspace_bytes.restype = C.c_size_t
+    lib.gs_last_error.restype = C.c_char_p
+    for name in ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
+                 "gs_adam_step"):
+        getattr(lib, name).restype = I32
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _check(status):
+    if status != GS_OK:
+        raise GsError(status, _lib.gs_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def make_camera(cam) -> GsCamera:
+    c = GsCamera()
+    c.R[:] = [float(x) for x in np.asarray(cam.R, np.float32).reshape(9)]
+    c.t[:] = [float(x) for x in np.asarray(cam.t, np.float32)]
+    c.campos[:] = [float(x) for x in np.asarray(cam.campos, np.float32)]
+    c.fx, c.fy, c.cx, c.cy = cam.fx, cam.fy, cam.cx, cam.cy
+    c.width, c.height = cam.width, cam.height
+    c.znear = cam.znear
+    c.bg[:] = [float(x) for x in cam.bg]
+    return c
+
+
+class Proj:
+    """Device buffers of the projected state (gs_proj) for n Gaussians."""
+
+    def __init__(self, n, device="cuda"):
+        self.n = n
+        self.splat = torch.empty((max(n, 1), 12), dtype=torch.float32, device=device)
+        self.depth = torch.empty(max(n, 1), dtype=torch.float32, device=device)
+        self.rect = torch.empty((max(n, 1), 2), dtype=torch.int32, device=device)
+        self.tiles = torch.empty(max(n, 1), dtype=torch.int32, device=device)
+        self.offs = torch.empty(n + 1, dtype=torch.int32, device=device)
+        self.struct = GsProj(self.splat.data_ptr(), self.depth.data_ptr(), self.rect.data_ptr(),
+                             self.tiles.data_ptr(), self.offs.data_ptr())
+
+
+def workspace(which, n=0, pairs=0, W=0, H=0, device="cuda"):
+    nbytes = int(_lib.gs_workspace_bytes(which, n, pairs, W, H))
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def gs_workspace_bytes(which, n=0, pairs=0, W=0, H=0):
+    return int(_lib.gs_workspace_bytes(which, n, pairs, W, H))
+
+
+def gs_preprocess(params, sh_degree, cam: GsCamera, proj: Proj, ws, stream=None) -> int:
+    """Projection + tile-count scan; returns the pair count (synchronises the stream once)."""
+    n = proj.n
+    scene = GsScene(n, sh_degree, params.data_ptr() if n else None)
+    total = C.c_uint32(0)
+    _check(_lib.gs_preprocess(C.byref(scene), C.byref(cam), C.byref(proj.struct), C.byref(total), _ptr(ws),
+                              ws.numel(), _stream(stream)))
+    return int(total.value)
+
+
+def gs_bin_sort(proj: Proj, cam: GsCamera, total_pairs, keys, vals, ranges, ws, stream=None):
+    cap = keys.numel() if keys is not None else 0
+    _check(_lib.gs_bin_sort(C.byref(proj.struct), proj.n, C.byref(cam), total_pairs, _ptr(keys), _ptr(vals), cap,
+                            _ptr(ranges), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def gs_render_fwd(proj: Proj, vals, ranges, cam: GsCamera, rgb, T_final, n_contrib, stream=None):
+    _check(_lib.gs_render_fwd(C.byref(proj.struct), proj.n, _ptr(vals), _ptr(ranges), C.byref(cam), _ptr(rgb),
+                              _ptr(T_final), _ptr(n_contrib), _stream(stream)))
+
+
+def gs_loss_l1_dssim(img, target, lambda_dssim, loss_out, dL_dimg, ws, stream=None):
+    _, H, W = img.shape
+    _check(_lib.gs_loss_l1_dssim(_ptr(img), _ptr(target), H, W, float(lambda_dssim), _ptr(loss_out),
+                                 _ptr(dL_dimg), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def gs_render_bwd(params, sh_degree, proj: Proj, vals, ranges, cam: GsCamera, T_final, n_contrib, dL_dimg,
+                  gscreen, gparams, stream=None):
+    n = proj.n
+    scene = GsScene(n, sh_degree, params.data_ptr() if n else None)
+    _check(_lib.gs_render_bwd(C.byref(scene), C.byref(proj.struct), _ptr(vals), _ptr(ranges), C.byref(cam),
+                              _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimg), _ptr(gscreen), _ptr(gparams),
+                              _stream(stream)))
+
+
+def gs_adam_step(params, grads, m, v, sh_degree, lr, beta1, beta2, eps, step, stream=None):
+    n = params.shape[1] if params.dim() == 2 else 0
+    lr_arr = (C.c_float * 5)(*[float(x) for x in lr])
+    _check(_lib.gs_adam_step(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), n, sh_degree, lr_arr, float(beta1),
+                             float(beta2), float(eps), int(step), _stream(stream)))
+
+
+def gs_last_error():
+    return _lib.gs_last_error().decode()

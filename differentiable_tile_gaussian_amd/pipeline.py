@@ -1,0 +1,77 @@
+"""One training step for one camera through the C ABI, with the device buffers
+it needs kept between calls (grown only when a larger pair count appears).
+
+torch allocates memory and provides the stream; every stage runs in libgs.so.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import gs
+
+DEFAULT_LR = (1.6e-4, 5e-3, 1e-3, 5e-2, 2.5e-3)   # means, log-scales, quaternion, opacity, colour
+
+
+class Pipeline:
+    def __init__(self, params: torch.Tensor, sh_degree: int, width: int, height: int, lam: float = 0.2,
+                 lr=DEFAULT_LR, betas=(0.9, 0.999), eps=1e-8):
+        assert params.is_cuda and params.dtype == torch.float32 and params.is_contiguous()
+        self.params = params
+        self.deg = sh_degree
+        self.n = params.shape[1]
+        self.W, self.H = width, height
+        self.lam, self.lr, self.betas, self.eps = lam, lr, betas, eps
+        dev = params.device
+        self.proj = gs.Proj(self.n, dev)
+        self.ws_pre = gs.workspace(gs.GS_WS_PREPROCESS, n=self.n, device=dev)
+        tx, ty = (width + 15) // 16, (height + 15) // 16
+        self.num_tiles = tx * ty
+        self.ranges = torch.empty((2, self.num_tiles), dtype=torch.int32, device=dev)
+        self.keys = torch.empty(0, dtype=torch.int64, device=dev)
+        self.vals = torch.empty(0, dtype=torch.int32, device=dev)
+        self.ws_sort = torch.empty(0, dtype=torch.uint8, device=dev)
+        self.rgb = torch.empty((3, height, width), dtype=torch.float32, device=dev)
+        self.T = torch.empty((height, width), dtype=torch.float32, device=dev)
+        self.nc = torch.empty((height, width), dtype=torch.int32, device=dev)
+        self.ws_loss = gs.workspace(gs.GS_WS_LOSS, W=width, H=height, device=dev)
+        self.loss = torch.zeros(3, dtype=torch.float32, device=dev)
+        self.dLdI = torch.empty((3, height, width), dtype=torch.float32, device=dev)
+        self.gscreen = torch.empty((9, max(self.n, 1)), dtype=torch.float32, device=dev)
+        self.grads = torch.empty_like(params)
+        self.m = torch.zeros_like(params)
+        self.v = torch.zeros_like(params)
+        self.t = 0
+        self.pairs = 0
+
+    def _reserve(self, pairs):
+        if self.keys.numel() < pairs:
+            cap = int(pairs * 1.25) + 1024
+            self.keys = torch.empty(cap, dtype=torch.int64, device=self.params.device)
+            self.vals = torch.empty(cap, dtype=torch.int32, device=self.params.device)
+        need = gs.gs_workspace_bytes(gs.GS_WS_BIN_SORT, self.n, pairs, self.W, self.H)
+        if self.ws_sort.numel() < need:
+            self.ws_sort = torch.empty(int(need * 1.25) + 4096, dtype=torch.uint8, device=self.params.device)
+
+    def forward(self, cam: gs.GsCamera):
+        self.pairs = gs.gs_preprocess(self.params, self.deg, cam, self.proj, self.ws_pre)
+        self._reserve(self.pairs)
+        gs.gs_bin_sort(self.proj, cam, self.pairs, self.keys, self.vals, self.ranges, self.ws_sort)
+        gs.gs_render_fwd(self.proj, self.vals, self.ranges, cam, self.rgb, self.T, self.nc)
+        return self.rgb
+
+    def backward(self, cam: gs.GsCamera, target: torch.Tensor):
+        gs.gs_loss_l1_dssim(self.rgb, target, self.lam, self.loss, self.dLdI, self.ws_loss)
+        gs.gs_render_bwd(self.params, self.deg, self.proj, self.vals, self.ranges, cam, self.T, self.nc, self.dLdI,
+                         self.gscreen, self.grads)
+
+    def adam(self):
+        self.t += 1
+        gs.gs_adam_step(self.params, self.grads, self.m, self.v, self.deg, self.lr, self.betas[0], self.betas[1],
+                        self.eps, self.t)
+
+    def step(self, cam: gs.GsCamera, target: torch.Tensor, adam: bool = True):
+        self.forward(cam)
+        self.backward(cam, target)
+        if adam:
+            self.adam()
+        return self.loss

@@ -1,0 +1,177 @@
+/*
+ * gs.h -- C ABI of the MI355X (gfx950) tile-based differentiable Gaussian rasteriser.
+ *
+ * One training step for one camera is six calls, in this order:
+ *
+ *   gs_preprocess     project every Gaussian, count the 16x16 tiles it touches,
+ *                     prefix-sum the counts; returns the number of (tile, Gaussian) pairs
+ *   gs_bin_sort       emit one 64-bit key (tile << 32 | depth bits) per pair, radix-sort
+ *                     the pairs, find each tile's [start, end) range
+ *   gs_render_fwd     front-to-back alpha blending per pixel
+ *   gs_loss_l1_dssim  0.8 L1 + 0.2 (1 - SSIM) and its image gradient
+ *   gs_render_bwd     back-to-front blend with transmittance recovery, then the
+ *                     per-Gaussian chain to parameter gradients
+ *   gs_adam_step      Adam over every parameter plane
+ *
+ * Pages defining the operations (titles as they appear on the pages):
+ *   [DR]   "Differentiable rasterisation" (splat-report knowledge base)
+ *   [TBDR] "Tile-based differentiable rasterization in 3DGS" (learn-ml-visualized)
+ *   [GST]  Gaussian splatting training study deck (bailiping.com)
+ *   [GSG]  "How a computer rebuilds a real place out of soft colored dots called
+ *          Gaussian Splats" (taosengine guide)
+ *
+ * Conventions for every entry point
+ *   - Array arguments are DEVICE pointers owned by the caller, unless marked "host".
+ *     The library never allocates, frees or retains caller memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream and returns, except gs_preprocess, which
+ *     synchronises the stream once to read the pair count.
+ *   - Arrays are planar (structure of arrays), fp32 unless stated otherwise:
+ *     [plane][n] per Gaussian, [channel][H][W] per image.
+ *   - Return value: GS_OK or a negative gs_status; gs_last_error() then holds a
+ *     message (per thread).  No C++ exception crosses the ABI.  On an argument
+ *     error nothing is enqueued and no output is written.
+ *
+ * Scene parameters, planes of params[P][n], P = 11 + 3 (deg + 1)^2 (14 at SH degree 0,
+ * 59 at degree 3):
+ *   0-2 mean x, y, z | 3-5 log-scales | 6-9 quaternion w, x, y, z (need not be unit)
+ *   10 opacity logit | 11-13 colour DC r, g, b (colour units, no basis factor)
+ *   14 + 3 (k - 1) + ch, k = 1 .. (deg + 1)^2 - 1: spherical-harmonic band coefficients.
+ */
+#ifndef GS_H_
+#define GS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gs_status {
+  GS_OK = 0,
+  GS_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad camera, step < 1 ... */
+  GS_ERR_CAPACITY = -2,     /* key buffer or workspace too small, or more than 2^32 - 1 pairs */
+  GS_ERR_UNSUPPORTED = -3,  /* SH degree outside 0..3, image larger than 65535 tiles per side */
+  GS_ERR_HIP = -4           /* a HIP launch or runtime call failed */
+} gs_status;
+
+/* Pinhole camera, OpenCV axes (x right, y down, z forward): p_cam = R p_world + t.
+ * Pixel (i, j) covers [i, i+1) x [j, j+1) and is sampled at its centre (i + 0.5, j + 0.5);
+ * the image point of p_cam is (fx x/z + cx, fy y/z + cy).  [GSG] "Flattening a 3D blob";
+ * [GST] Jacobian slide.  Gaussians with z <= znear are culled. */
+typedef struct gs_camera {
+  float R[9];           /* row-major world -> camera rotation */
+  float t[3];
+  float campos[3];      /* camera centre in world coordinates (= -R^T t), used for the SH view direction */
+  float fx, fy, cx, cy; /* pixels */
+  int32_t width, height;
+  float znear;
+  float bg[3];          /* background colour behind the last Gaussian */
+} gs_camera;
+
+typedef struct gs_scene {
+  int64_t n;            /* number of Gaussians, 0 <= n < 2^31 */
+  int32_t sh_degree;    /* 0..3 */
+  const float* params;  /* device, [P][n] */
+} gs_scene;
+
+/* Projected per-Gaussian state written by gs_preprocess and read by the later calls.
+ * All members are device arrays of n entries (offs: n + 1) allocated by the caller. */
+typedef struct gs_proj {
+  float* splat;         /* [n][12] packed record: u, v, A, B, C, opacity, r, g, b, 0, 0, 0
+                           (screen centre, conic, opacity, clamped colour); zero when culled */
+  float* depth;         /* [n] camera-space z (the sort key's low 32 bits) */
+  uint32_t* rect;       /* [n][2] tile rectangle, inclusive: x0 | y0 << 16, x1 | y1 << 16 */
+  uint32_t* tiles;      /* [n] tiles touched, 0 when culled */
+  uint32_t* offs;       /* [n + 1] exclusive prefix sum of tiles; offs[n] = pair count */
+} gs_proj;
+
+/* Projection of every Gaussian and the tile count prefix sum.
+ * [GST] parameter slide (exp log-scales, sigmoid logit, normalised quaternion);
+ * [DR] "Forward" (Sigma' = J W Sigma W^T J^T) and "From a pixel error back to a quaternion"
+ * (Sigma = R S S^T R^T); [GST] Jacobian slide (J and the 0.3 px^2 dilation); [GSG]
+ * "Flattening a 3D blob into a 2D oval" (conic), "Why tiling, and the five stages" (extent
+ * rad = sqrt(2 min(4.5, ln max(255 o, 1.0001))) sqrt(lambda_max), tile rectangle, count and
+ * scan), "Spherical harmonics" (colour = DC + sum_k sh_k Y_k(normalize(mean - campos)),
+ * clamped at 0).
+ * The key path (camera-space depth, screen centre, extent, rectangle) is computed in IEEE
+ * fp32 without contraction, with exp/log/sigmoid evaluated in fp64 and rounded once, so the
+ * pair list is a deterministic function of the inputs.
+ * out: caller-allocated gs_proj for scene->n Gaussians.  total_pairs: HOST pointer,
+ * receives offs[n].  ws: device workspace of gs_workspace_bytes(GS_WS_PREPROCESS, n, 0, 0, 0)
+ * bytes.  Synchronises `stream` once.  GS_ERR_CAPACITY if the pair count exceeds 2^32 - 1. */
+int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out, uint32_t* total_pairs,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Duplicate-with-keys, depth sort and tile ranges.  [GSG] "Why tiling, and the five stages"
+ * (scatter, per-tile depth sort, ranges with the tie broken by id).  Pair j of Gaussian i
+ * (tiles in row-major order over its rectangle) gets key (ty * tiles_x + tx) << 32 |
+ * bits(depth[i]) and value i; the pairs are then sorted stably by key (LSD radix sort over
+ * the key's significant bits), i.e. by tile, then depth, then Gaussian id.
+ * keys[capacity], vals[capacity]: outputs, the first total_pairs entries are written.
+ * ranges: [2][tiles_x * tiles_y] u32, ranges[0][t] = first, ranges[1][t] = one past the last
+ * pair of tile t ((0, 0) for an empty tile).  total_pairs must be the value gs_preprocess
+ * returned for the same proj.  ws: gs_workspace_bytes(GS_WS_BIN_SORT, n, total_pairs, W, H).
+ * GS_ERR_CAPACITY (nothing written) if capacity < total_pairs or the workspace is short. */
+int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32_t total_pairs, uint64_t* keys,
+                    uint32_t* vals, uint32_t capacity, uint32_t* ranges, void* ws, size_t ws_bytes, void* stream);
+
+/* Front-to-back compositing, [GSG] "The painting itself: front-to-back alpha compositing";
+ * [GST] opacity slide (cap 0.99, skip below 1/255, early termination); [TBDR] worked
+ * examples.  For each pixel centre p and each pair of its tile in order:
+ *   e = 0.5 (A dx^2 + C dy^2) + B dx dy with d = p - (u, v); alpha = min(0.99, o exp(-e));
+ *   skip if alpha < 1/255; C += T alpha c; T *= 1 - alpha; stop once T < 1e-4.
+ * rgb[3][H][W] = C + T bg; T_final[H][W] = T; n_contrib[H][W] = 1 + (index within the tile's
+ * range) of the last blended pair, 0 if none ([DR] "The trick": only the final state is kept). */
+int32_t gs_render_fwd(const gs_proj* proj, int64_t n, const uint32_t* vals, const uint32_t* ranges,
+                      const gs_camera* cam, float* rgb, float* T_final, uint32_t* n_contrib, void* stream);
+
+/* Loss (1 - lambda) L1 + lambda (1 - SSIM) and dL/dimg.  [GST] loss slides: L1 mean over
+ * 3HW with zero subgradient at zero residual; SSIM with an 11 x 11 Gaussian window of
+ * standard deviation 1.5, C1 = 0.01^2, C2 = 0.03^2, zero padding, averaged over pixels and
+ * channels; no one-half on D-SSIM; lambda = 0.2 in the method.
+ * img, target: [3][H][W].  loss_out: device float[3] = total, L1, mean SSIM.
+ * dL_dimg: [3][H][W], overwritten.  ws: gs_workspace_bytes(GS_WS_LOSS, 0, 0, W, H). */
+int32_t gs_loss_l1_dssim(const float* img, const float* target, int32_t H, int32_t W, float lambda_dssim,
+                         float* loss_out, float* dL_dimg, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward pass.  Part 1, the blend: [DR] "The trick: recompute the blend state instead of
+ * storing it"; [GSG] "The clever bit: a single backward sweep through the blend" and "From a
+ * pixel's blame to the oval's shape and place"; [GST] compositing-derivative slide.  Each
+ * pixel walks its tile's pairs from n_contrib - 1 down to 0, recovers T_i = T_{i+1} / (1 -
+ * alpha_i), keeps S = colour behind (starting at bg T_final), and accumulates per Gaussian:
+ *   dc += g alpha T;  dalpha = sum_ch g (c T - S / (1 - alpha));  when alpha is not capped:
+ *   do += dalpha G, and through e: du, dv, dA, dB, dC.
+ * gscreen: [9][n] = du, dv, dA, dB, dC, d opacity, dr, dg, db -- zeroed and filled here.
+ * Part 2, the chain per Gaussian: [GSG] "The covariance chain" (conic -> V -> Sigma -> M ->
+ * scale and quaternion, projection off |q|), "Where the position gradient comes from"
+ * (mean path and the J(z) covariance path), "Spherical harmonics" (band gradients and the
+ * view-direction term), sigmoid.  gparams: [P][n], overwritten (zero for culled Gaussians).
+ * proj, vals, ranges, T_final and n_contrib must be those of the matching forward. */
+int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t* vals, const uint32_t* ranges,
+                      const gs_camera* cam, const float* T_final, const uint32_t* n_contrib,
+                      const float* dL_dimg, float* gscreen, float* gparams, void* stream);
+
+/* Adam, [GSG] Adam section; per-group rates [DR] "From a pixel error back to a quaternion".
+ *   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
+ *   theta -= lr_group (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
+ * params, m, v: [P][n] updated in place; grads: [P][n].  lr: HOST float[5] for the groups
+ * means, log-scales, quaternion, opacity, colour (DC and bands).  beta1, beta2, eps are host
+ * fp64 scalars: 1 - beta and the bias corrections are formed in fp64 and rounded once to
+ * fp32 for the kernel.  step t >= 1. */
+int32_t gs_adam_step(float* params, const float* grads, float* m, float* v, int64_t n, int32_t sh_degree,
+                     const float* lr, double beta1, double beta2, double eps, int32_t step, void* stream);
+
+/* Workspace sizes, in bytes, for the calls that take one. */
+enum { GS_WS_PREPROCESS = 0, GS_WS_BIN_SORT = 1, GS_WS_LOSS = 2 };
+size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* gs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GS_H_ */

@@ -1,0 +1,103 @@
+"""Helpers for the GPU-vs-oracle parity tests: run the HIP path through the C ABI
+and pull every stage's output back to numpy; tolerance checks."""
+from __future__ import annotations
+
+import numpy as np
+
+# Pixels whose forward decisions (skip at 1/255, stop at 1e-4) lie within this
+# relative distance of the threshold may legitimately flip between the GPU's exp
+# and the oracle's correctly rounded one; they are excluded from the tight check.
+MARGIN = 1e-5
+PIXEL_ATOL = 1e-5          # rendered pixels, absolute
+GRAD_RTOL = 1e-3           # parameter gradients, relative
+
+
+def gpu_forward(params_np, deg, cam):
+    import torch
+    from differentiable_tile_gaussian_amd import gs
+    from differentiable_tile_gaussian_amd.pipeline import Pipeline
+    params = torch.from_numpy(np.ascontiguousarray(params_np, np.float32)).cuda()
+    pl = Pipeline(params, deg, cam.width, cam.height)
+    c = gs.make_camera(cam)
+    pl.forward(c)
+    torch.cuda.synchronize()
+    return pl, c
+
+
+def proj_to_numpy(pl):
+    n = pl.n
+    splat = pl.proj.splat[:n].cpu().numpy()
+    rect = pl.proj.rect[:n].cpu().numpy().view(np.uint32)
+    out = dict(uv=splat[:, 0:2].T.copy(), conic=splat[:, 2:5].T.copy(), opac=splat[:, 5].copy(),
+               rgb=splat[:, 6:9].T.copy(), depth=pl.proj.depth[:n].cpu().numpy(),
+               tiles=pl.proj.tiles[:n].cpu().numpy().view(np.uint32),
+               offs=pl.proj.offs.cpu().numpy().view(np.uint32))
+    r = np.zeros((4, n), np.int64)
+    r[0] = rect[:, 0] & 0xFFFF
+    r[1] = rect[:, 0] >> 16
+    r[2] = rect[:, 1] & 0xFFFF
+    r[3] = rect[:, 1] >> 16
+    out["rect"] = r
+    return out
+
+
+def sorted_to_numpy(pl):
+    P = pl.pairs
+    keys = pl.keys[:P].cpu().numpy().view(np.uint64)
+    vals = pl.vals[:P].cpu().numpy().view(np.uint32)
+    ranges = pl.ranges.cpu().numpy().view(np.uint32)
+    return keys, vals, ranges
+
+
+def render_to_numpy(pl):
+    return dict(rgb=pl.rgb.cpu().numpy(), T=pl.T.cpu().numpy(), n_contrib=pl.nc.cpu().numpy().view(np.uint32))
+
+
+def check_preprocess(gpu, ora):
+    vis = ora["tiles"] > 0
+    np.testing.assert_array_equal(gpu["tiles"], ora["tiles"])
+    np.testing.assert_array_equal(gpu["rect"][:, vis], ora["rect"][:, vis])
+    np.testing.assert_array_equal(gpu["depth"][vis].view(np.uint32), ora["depth"][vis].view(np.uint32))
+    np.testing.assert_array_equal(gpu["uv"][:, vis], ora["uv"][:, vis])
+    np.testing.assert_array_equal(gpu["conic"][:, vis], ora["conic"][:, vis])
+    np.testing.assert_allclose(gpu["opac"][vis], ora["opac"][vis], rtol=2e-7, atol=0)
+    np.testing.assert_allclose(gpu["rgb"][:, vis], ora["rgb"][:, vis], rtol=1e-6, atol=1e-6)
+    expect_offs = np.concatenate([[0], np.cumsum(ora["tiles"].astype(np.int64))]).astype(np.uint32)
+    np.testing.assert_array_equal(gpu["offs"], expect_offs)
+
+
+def check_render(gpu, ora, margin=MARGIN):
+    ok = ora["margin"] >= margin
+    n_low = int((~ok).sum())
+    d = np.abs(gpu["rgb"] - ora["rgb"]).max(axis=0)
+    assert d[ok].max(initial=0.0) <= PIXEL_ATOL, f"max pixel diff {d[ok].max()}"
+    assert np.abs(gpu["T"] - ora["T"])[ok].max(initial=0.0) <= PIXEL_ATOL
+    np.testing.assert_array_equal(gpu["n_contrib"][ok], ora["n_contrib"][ok])
+    # pixels near a threshold: still close (one decision's worth of colour at most)
+    if n_low:
+        assert d[~ok].max() <= 5e-3 + 1.0 / 255.0
+    return n_low
+
+
+def grad_groups(deg):
+    P = 11 + 3 * (deg + 1) ** 2
+    groups = {"mean": slice(0, 3), "logscale": slice(3, 6), "quat": slice(6, 10), "logit": slice(10, 11),
+              "dc": slice(11, 14)}
+    if P > 14:
+        groups["sh"] = slice(14, P)
+    return groups
+
+
+def check_grad(g_gpu, g_ref, mask, rtol=GRAD_RTOL, name=""):
+    """Per element |d| <= rtol |ref| + rtol rms(ref), and ||d|| / ||ref|| <= rtol."""
+    a = g_gpu[..., mask].astype(np.float64)
+    b = g_ref[..., mask].astype(np.float64)
+    if b.size == 0:
+        return
+    rms = np.sqrt((b * b).mean())
+    d = np.abs(a - b)
+    bad = d > rtol * np.abs(b) + rtol * rms
+    assert not bad.any(), f"{name}: {int(bad.sum())} of {b.size} elements off, max {d.max()} (rms {rms})"
+    nb = np.linalg.norm(b)
+    if nb > 0:
+        assert np.linalg.norm(a - b) / nb <= rtol, f"{name}: relative norm {np.linalg.norm(a - b) / nb}"

@@ -1,0 +1,250 @@
+"""GPU (HIP, through the C ABI) against the CPU oracle, stage by stage.
+
+Keys, values, tile ranges, counts, rectangles and depths bit-exact; pixels within
+1e-5 absolute; gradients within 1e-3 relative (per element against |g| plus the
+group's rms, and in norm).  Pixels whose skip/stop decisions sit within 1e-5 of a
+threshold are excluded from the tight pixel check and counted; Gaussians seen by
+such pixels are excluded from the tight gradient check.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from differentiable_tile_gaussian_amd import scenes
+from tests import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _small_cases():
+    cases = []
+    for seed, (n, deg, w, h) in enumerate([(300, 0, 100, 70), (500, 1, 64, 64), (800, 2, 130, 97),
+                                          (1200, 3, 161, 33), (64, 3, 17, 300)]):
+        cases.append((seed, n, deg, w, h))
+    return cases
+
+
+def _scene_and_camera(seed, n, deg, w, h):
+    s = scenes.random_scene(100 + seed, n, deg, spread=1.3, logscale_std=0.6, logit_std=1.5)
+    th = 0.3 * seed
+    cam = scenes.look_at_origin((4.5 * math.sin(th), 0.4, -4.5 * math.cos(th)), w, h, 0.9 * max(w, h))
+    s.params[0:3] -= np.array([[0.0], [0.0], [4.5]], np.float32)   # centre the cloud on the origin
+    s.params[0:3] *= 0.8
+    return s, cam
+
+
+def _oracle_all(oracle, params, deg, cam, dLdI=None):
+    pre, keys, vals, ranges, fwd = oracle.forward(params, deg, cam)
+    out = dict(pre=pre, keys=keys, vals=vals, ranges=ranges, fwd=fwd)
+    if dLdI is not None:
+        gscreen, gmargin = oracle.render_bwd(pre, vals, ranges, cam, fwd, dLdI)
+        out["gscreen"], out["gmargin"] = gscreen, gmargin
+        out["gparams"] = oracle.preprocess_bwd(params, deg, cam, gscreen)
+    return out
+
+
+@pytest.mark.parametrize("case", _small_cases())
+def test_forward_stages_small(torch_cuda, oracle, case):
+    seed, n, deg, w, h = case
+    print(f"case seed={seed} n={n} deg={deg} {w}x{h}", flush=True)
+    s, cam = _scene_and_camera(*case)
+    o = _oracle_all(oracle, s.params, deg, cam)
+    pl, c = pu.gpu_forward(s.params, deg, cam)
+    pu.check_preprocess(pu.proj_to_numpy(pl), o["pre"])
+    assert pl.pairs == len(o["keys"]) > 0
+    keys, vals, ranges = pu.sorted_to_numpy(pl)
+    np.testing.assert_array_equal(keys, o["keys"])
+    np.testing.assert_array_equal(vals, o["vals"])
+    np.testing.assert_array_equal(ranges, o["ranges"])
+    pu.check_render(pu.render_to_numpy(pl), o["fwd"])
+
+
+@pytest.mark.parametrize("case", _small_cases())
+def test_backward_small(torch_cuda, oracle, case):
+    torch = torch_cuda
+    seed, n, deg, w, h = case
+    print(f"case seed={seed} n={n} deg={deg} {w}x{h}", flush=True)
+    s, cam = _scene_and_camera(*case)
+    dLdI = (np.random.default_rng(seed).standard_normal((3, h, w)) * 1e-3).astype(np.float32)
+    o = _oracle_all(oracle, s.params, deg, cam, dLdI)
+    pl, c = pu.gpu_forward(s.params, deg, cam)
+    pl.dLdI.copy_(torch.from_numpy(dLdI))
+    from differentiable_tile_gaussian_amd import gs
+    gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, c, pl.T, pl.nc, pl.dLdI, pl.gscreen, pl.grads)
+    torch.cuda.synchronize()
+    gscreen = pl.gscreen[:, :n].cpu().numpy()
+    gparams = pl.grads.cpu().numpy()
+    keep = o["gmargin"] >= pu.MARGIN
+    print(f"  gaussians excluded by margin: {int((~keep).sum())} of {n}", flush=True)
+    for k, name in enumerate(["u", "v", "A", "B", "C", "opacity", "r", "g", "b"]):
+        pu.check_grad(gscreen[k], o["gscreen"][k], keep, name=name)
+    for name, sl in pu.grad_groups(deg).items():
+        pu.check_grad(gparams[sl], o["gparams"][sl], keep, name=name)
+    # culled Gaussians get exactly zero
+    culled = o["pre"]["tiles"] == 0
+    assert np.all(gparams[:, culled] == 0.0)
+
+
+def test_config1_full_step(torch_cuda, oracle):
+    """The tiny workload end to end, including the loss and one Adam step."""
+    torch = torch_cuda
+    from differentiable_tile_gaussian_amd import gs
+    wl = scenes.config1()
+    cam = wl.cameras[0]
+    deg = wl.scene.sh_degree
+    target = oracle.forward(wl.target_scene.params, deg, cam)[4]["rgb"]
+    ref = oracle.train_step_grads(wl.scene.params, deg, cam, target)
+    pl, c = pu.gpu_forward(wl.scene.params, deg, cam)
+    pu.check_preprocess(pu.proj_to_numpy(pl), ref["pre"])
+    keys, vals, ranges = pu.sorted_to_numpy(pl)
+    np.testing.assert_array_equal(keys, ref["keys"])
+    np.testing.assert_array_equal(vals, ref["vals"])
+    np.testing.assert_array_equal(ranges, ref["ranges"])
+    n_low = pu.check_render(pu.render_to_numpy(pl), ref["fwd"])
+    print(f"low-margin pixels: {n_low}", flush=True)
+    tgt = torch.from_numpy(target).cuda()
+    pl.backward(c, tgt)
+    torch.cuda.synchronize()
+    loss = pl.loss.cpu().numpy()
+    np.testing.assert_allclose(loss, ref["loss"], rtol=2e-5)
+    keep = ref["gmargin"] >= pu.MARGIN
+    if n_low == 0:
+        g_img = pl.dLdI.cpu().numpy()
+        scale = np.abs(ref["dLdI"]).max()
+        assert np.abs(g_img - ref["dLdI"]).max() <= 1e-4 * scale
+    gparams = pl.grads.cpu().numpy()
+    for name, sl in pu.grad_groups(deg).items():
+        pu.check_grad(gparams[sl], ref["gparams"][sl], keep, name=name)
+    # one Adam step from zero moments, against the oracle's fp64 Adam on the GPU's gradient
+    p0 = wl.scene.params.astype(np.float64)
+    pl.adam()
+    torch.cuda.synchronize()
+    lr = np.array([1.6e-4, 5e-3, 1e-3, 5e-2, 2.5e-3])
+    p_ref, m_ref, v_ref = oracle.adam(p0, gparams.astype(np.float64), np.zeros_like(p0), np.zeros_like(p0), deg,
+                                      lr, step=1)
+    np.testing.assert_allclose(pl.params.cpu().numpy(), p_ref, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(pl.m.cpu().numpy(), m_ref, rtol=1e-6, atol=1e-12)
+    np.testing.assert_allclose(pl.v.cpu().numpy(), v_ref, rtol=1e-6, atol=1e-14)
+    del gs
+
+
+def test_loss_parity(torch_cuda, oracle):
+    torch = torch_cuda
+    from differentiable_tile_gaussian_amd import gs
+    for (h, w) in [(37, 53), (128, 128), (200, 77)]:
+        img = scenes.random_image(h * w, h, w)
+        tgt = np.clip(img + 0.1 * np.random.default_rng(w).standard_normal(img.shape).astype(np.float32), 0, 1)
+        (tot, l1, ss), g_ref = oracle.loss(img, tgt, 0.2)
+        ti, tt = torch.from_numpy(img).cuda(), torch.from_numpy(tgt).cuda()
+        out = torch.zeros(3, device="cuda")
+        g = torch.empty_like(ti)
+        ws = gs.workspace(gs.GS_WS_LOSS, W=w, H=h)
+        gs.gs_loss_l1_dssim(ti, tt, 0.2, out, g, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(out.cpu().numpy(), [tot, l1, ss], rtol=1e-5)
+        gg = g.cpu().numpy()
+        assert np.abs(gg - g_ref).max() <= 1e-4 * np.abs(g_ref).max()
+
+
+def test_adam_parity(torch_cuda, oracle):
+    torch = torch_cuda
+    from differentiable_tile_gaussian_amd import gs
+    rng = np.random.default_rng(3)
+    for n, deg in [(1003, 3), (4096, 0), (1, 1)]:
+        P = scenes.num_planes(deg)
+        th = rng.standard_normal((P, n)).astype(np.float32)
+        g = rng.standard_normal((P, n)).astype(np.float32)
+        m = (0.1 * rng.standard_normal((P, n))).astype(np.float32)
+        v = (0.01 * rng.random((P, n))).astype(np.float32)
+        lr = np.array([1.6e-4, 5e-3, 1e-3, 5e-2, 2.5e-3])
+        ref = oracle.adam(th, g, m, v, deg, lr, step=7)
+        T = [torch.from_numpy(a.copy()).cuda() for a in (th, g, m, v)]
+        gs.gs_adam_step(T[0], T[1], T[2], T[3], deg, lr, 0.9, 0.999, 1e-8, 7)
+        torch.cuda.synchronize()
+        # fp32 rounding is relative to the operands of each update, which can cancel
+        m_scale = 0.9 * np.abs(m) + 0.1 * np.abs(g)
+        v_scale = 0.999 * np.abs(v) + 0.001 * g * g
+        assert np.all(np.abs(T[2].cpu().numpy() - ref[1]) <= 1e-6 * m_scale + 1e-30)
+        assert np.all(np.abs(T[3].cpu().numpy() - ref[2]) <= 1e-6 * v_scale + 1e-30)
+        # one fp32 rounding of theta itself plus a small relative error on the step
+        bound = 1.2e-7 * np.abs(ref[0]) + 1e-5 * np.abs(th - ref[0]) + 1e-12
+        assert np.all(np.abs(T[0].cpu().numpy() - ref[0]) <= bound)
+
+
+# ---------------------------------------------------------------- edge cases
+def test_empty_scene(torch_cuda, oracle):
+    import torch
+    cam = scenes.identity_camera(40, 30, 40.0)
+    cam.bg = (0.2, 0.3, 0.4)
+    params = np.zeros((14, 0), np.float32)
+    from differentiable_tile_gaussian_amd import gs
+    from differentiable_tile_gaussian_amd.pipeline import Pipeline
+    pl = Pipeline(torch.zeros((14, 0), device="cuda"), 0, 40, 30)
+    c = gs.make_camera(cam)
+    pl.forward(c)
+    torch.cuda.synchronize()
+    assert pl.pairs == 0
+    rgb = pl.rgb.cpu().numpy()
+    np.testing.assert_allclose(rgb, np.broadcast_to(np.array(cam.bg, np.float32)[:, None, None], rgb.shape))
+    assert np.all(pl.nc.cpu().numpy() == 0) and np.all(pl.T.cpu().numpy() == 1.0)
+    pl.backward(c, torch.zeros((3, 30, 40), device="cuda"))
+    torch.cuda.synchronize()
+    del params, oracle
+
+
+def test_single_gaussian_and_all_culled(torch_cuda, oracle):
+    cam = scenes.identity_camera(48, 48, 60.0)
+    s = scenes.random_scene(5, 1, 0)
+    s.params[0:3, 0] = (0.0, 0.0, 3.0)
+    o = _oracle_all(oracle, s.params, 0, cam)
+    pl, c = pu.gpu_forward(s.params, 0, cam)
+    pu.check_preprocess(pu.proj_to_numpy(pl), o["pre"])
+    pu.check_render(pu.render_to_numpy(pl), o["fwd"])
+    # everything behind the camera or with a zero quaternion
+    s2 = scenes.random_scene(6, 200, 0)
+    s2.params[2, :100] = -s2.params[2, :100]
+    s2.params[6:10, 100:] = 0.0
+    pl2, _ = pu.gpu_forward(s2.params, 0, cam)
+    assert pl2.pairs == 0
+    assert np.all(pl2.proj.tiles.cpu().numpy() == 0)
+
+
+def test_all_in_one_tile_and_non_finite(torch_cuda, oracle):
+    cam = scenes.identity_camera(64, 64, 200.0, 8.0, 8.0)
+    s = scenes.random_scene(8, 700, 3, spread=0.01, logscale_mean=math.log(0.002), logscale_std=0.2)
+    s.params[3, 0] = np.nan          # non-finite scale: culled, not binned
+    s.params[0, 1] = np.inf
+    o = _oracle_all(oracle, s.params, 3, cam)
+    assert o["pre"]["tiles"][0] == 0 and o["pre"]["tiles"][1] == 0
+    pl, c = pu.gpu_forward(s.params, 3, cam)
+    pu.check_preprocess(pu.proj_to_numpy(pl), o["pre"])
+    keys, vals, ranges = pu.sorted_to_numpy(pl)
+    np.testing.assert_array_equal(keys, o["keys"])
+    np.testing.assert_array_equal(vals, o["vals"])
+    np.testing.assert_array_equal(ranges, o["ranges"])
+    pu.check_render(pu.render_to_numpy(pl), o["fwd"])
+
+
+def test_capacity_error_writes_nothing(torch_cuda):
+    import torch
+    from differentiable_tile_gaussian_amd import gs
+    cam = scenes.identity_camera(64, 64, 60.0)
+    s = scenes.random_scene(9, 300, 0)
+    pl, c = pu.gpu_forward(s.params, 0, cam)
+    keys = torch.full((pl.pairs - 1,), 7, dtype=torch.int64, device="cuda")
+    vals = torch.full((pl.pairs - 1,), 7, dtype=torch.int32, device="cuda")
+    ranges = torch.full((2, 16), 7, dtype=torch.int32, device="cuda")
+    with pytest.raises(gs.GsError) as e:
+        gs.gs_bin_sort(pl.proj, c, pl.pairs, keys, vals, ranges, pl.ws_sort)
+    assert e.value.status == gs.GS_ERR_CAPACITY
+    torch.cuda.synchronize()
+    assert int(keys.min()) == 7 and int(ranges.min()) == 7
