@@ -1,0 +1,212 @@
+"""Benchmark: full training steps of the 6M-Gaussian, SH-degree-3, 1920x1080 workload.
+
+One step = preprocess + bin/sort + forward blend + L1/D-SSIM loss + backward
+blend and chain + Adam over every parameter, for one of 100 seeded orbit
+cameras (in order).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 100] [--warmup 5] [--no-cpu-baseline]
+
+Only one GPU is used; --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD_CFG = 5
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+# Algorithmic bytes of Adam per parameter: read theta, g, m, v; write theta, m, v (fp32).
+ADAM_BYTES_PER_PARAM = 28
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=WORKLOAD_CFG, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-report", action="store_true", help="also print per-stage times to stderr")
+    return ap.parse_args()
+
+
+def make_targets(wl, cams, Pipeline, torch):
+    """Target images: renders of the perturbed copy of the scene (or of the second scene),
+    one per camera, computed before timing."""
+    tp = torch.from_numpy(wl.target_scene.params).cuda()
+    tpl = Pipeline(tp, wl.target_scene.sh_degree, wl.cameras[0].width, wl.cameras[0].height)
+    out = [tpl.forward(c).clone() for c in cams]
+    del tpl, tp
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+class StageTimer:
+    """HIP events on the stream the library launches on (torch's current stream)."""
+
+    NAMES = ("preprocess", "bin_sort", "render_fwd", "loss", "render_bwd", "adam")
+
+    def __init__(self, torch, steps):
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.NAMES) + 1)] for _ in range(steps)]
+
+    def mark(self, step, k):
+        self.ev[step][k].record()
+
+    def per_stage_ms(self):
+        t = np.array([[self.ev[s][k].elapsed_time(self.ev[s][k + 1]) for k in range(len(self.NAMES))]
+                      for s in range(len(self.ev))])
+        return t
+
+
+def run_steps(pl, cams, targets, first, count, timer=None, gs=None):
+    for s in range(count):
+        idx = (first + s) % len(cams)
+        c, tgt = cams[idx], targets[idx]
+        if timer: timer.mark(s, 0)
+        pl.pairs = gs.gs_preprocess(pl.params, pl.deg, c, pl.proj, pl.ws_pre)
+        pl._reserve(pl.pairs)
+        if timer: timer.mark(s, 1)
+        gs.gs_bin_sort(pl.proj, c, pl.pairs, pl.keys, pl.vals, pl.ranges, pl.ws_sort)
+        if timer: timer.mark(s, 2)
+        gs.gs_render_fwd(pl.proj, pl.vals, pl.ranges, c, pl.rgb, pl.T, pl.nc, pl.ws_render)
+        if timer: timer.mark(s, 3)
+        gs.gs_loss_l1_dssim(pl.rgb, tgt, pl.lam, pl.loss, pl.dLdI, pl.ws_loss)
+        if timer: timer.mark(s, 4)
+        gs.gs_render_bwd(pl.params, pl.deg, pl.proj, pl.vals, pl.ranges, c, pl.T, pl.nc, pl.dLdI, pl.gscreen,
+                         pl.grads, pl.ws_render)
+        if timer: timer.mark(s, 5)
+        pl.adam()
+        if timer: timer.mark(s, 6)
+
+
+def count_evals(pl, torch):
+    """Gaussian-pixel evaluations of the last forward/backward: the forward examines
+    entries up to the stopping one (n_contrib for stopped pixels, the whole tile list
+    otherwise); the backward walks n_contrib entries."""
+    H, W = pl.H, pl.W
+    tx = (W + 15) // 16
+    ys = torch.arange(H, device="cuda") // 16
+    xs = torch.arange(W, device="cuda") // 16
+    tile = ys[:, None] * tx + xs[None, :]
+    rng = pl.ranges.long()
+    length = (rng[1] - rng[0])[tile]
+    nc = pl.nc.long()
+    stopped = pl.T < 1e-4
+    fwd = torch.where(stopped, nc, length).sum().item()
+    bwd = nc.sum().item()
+    return int(fwd), int(bwd)
+
+
+def cpu_baseline(wl):
+    """The oracle (test infrastructure) on one training step: camera 0, all stages, one core."""
+    from oracle import oracle as O
+    cam = wl.cameras[0]
+    p = wl.scene.params
+    deg = wl.scene.sh_degree
+    # a seeded synthetic target: the oracle's cost does not depend on the target's content
+    tgt = np.random.default_rng(7).random((3, cam.height, cam.width), dtype=np.float32)
+    lr = np.array([1.6e-4, 5e-3, 1e-3, 5e-2, 2.5e-3])
+    t0 = time.perf_counter()
+    r = O.train_step_grads(p, deg, cam, tgt)
+    z = np.zeros_like(p)
+    O.adam(p, r["gparams"], z, z, deg, lr, step=1, dtype=np.float32)
+    dt = time.perf_counter() - t0
+    return dict(value=1.0 / dt, unit="iter/s", cores=1, kind="oracle",
+                sample=f"one full training step (camera 0 of {len(wl.cameras)}: preprocess, bin/sort, forward, "
+                       f"loss, backward, chain, Adam over {p.size} parameters) of the same workload, "
+                       f"single-threaded fp32 oracle, seeded synthetic target; {dt:.1f} s",
+                seconds=dt, evals=int(r["fwd"]["evals"] + int(r["fwd"]["n_contrib"].sum())))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this rasteriser runs on one GPU; multi-GPU runs are not part of this build "
+                                   f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})"}))
+        sys.exit(2)
+    import torch
+    from differentiable_tile_gaussian_amd import gs, scenes
+    from differentiable_tile_gaussian_amd.pipeline import Pipeline
+
+    torch.cuda.set_device(0)
+    t_setup = time.perf_counter()
+    wl = scenes.CONFIGS[args.workload]()
+    cams = [gs.make_camera(c) for c in wl.cameras]
+    cam0 = wl.cameras[0]
+    targets = make_targets(wl, cams, Pipeline, torch)
+    params = torch.from_numpy(wl.scene.params).cuda()
+    n, deg = wl.scene.n, wl.scene.sh_degree
+    P = params.shape[0]
+    pl = Pipeline(params, deg, cam0.width, cam0.height)
+    setup_s = time.perf_counter() - t_setup
+
+    run_steps(pl, cams, targets, 0, args.warmup, gs=gs)
+    torch.cuda.synchronize()
+    timer = StageTimer(torch, args.steps)
+    t0 = time.perf_counter()
+    run_steps(pl, cams, targets, args.warmup, args.steps, timer=timer, gs=gs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = timer.per_stage_ms()
+    ms_per_step = wall * 1000.0 / args.steps
+
+    # evaluation counts: replay the same cameras from the same starting state, untimed
+    params2 = torch.from_numpy(wl.scene.params).cuda()
+    pl2 = Pipeline(params2, deg, cam0.width, cam0.height)
+    run_steps(pl2, cams, targets, 0, args.warmup, gs=gs)
+    ev_f = ev_b = 0
+    for s in range(args.steps):
+        run_steps(pl2, cams, targets, args.warmup + s, 1, gs=gs)
+        f, b = count_evals(pl2, torch)
+        ev_f += f
+        ev_b += b
+    del pl2, params2
+    t_fb = (stage[:, 2].sum() + stage[:, 4].sum()) / 1000.0
+
+    # roofline of the dominant kernel: Adam, one launch per step over all P*n parameters
+    adam_ms = float(stage[:, 5].mean())
+    adam_bytes = ADAM_BYTES_PER_PARAM * P * n
+    achieved = adam_bytes / (adam_ms / 1000.0) / 1e9
+    out = {
+        "metric": "fwd+bwd raster iterations/sec and Gaussian-pixel evals/s; % of HBM/VALU roofline",
+        "value": round(1000.0 / ms_per_step, 3),
+        "unit": "iter/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "gaussians": n, "sh_degree": deg, "image": [cam0.width, cam0.height],
+                   "cameras": len(cams), "step": "preprocess+sort+fwd+loss+bwd+adam", "parallelism": "none"},
+        "evals_per_s": round((ev_f + ev_b) / t_fb, 1),
+        "evals_per_step": {"fwd": ev_f // args.steps, "bwd": ev_b // args.steps},
+        "stage_ms": {k: round(float(stage[:, i].mean()), 4) for i, k in enumerate(StageTimer.NAMES)},
+        "roofline": {"kernel": "adam_vec4_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": adam_bytes},
+        "setup_s": round(setup_s, 2),
+    }
+    if not args.no_cpu_baseline and args.workload == WORKLOAD_CFG:
+        cb = cpu_baseline(wl)
+        out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    if args.stage_report:
+        print(json.dumps({"stage_ms_all": stage.round(4).tolist()}), file=sys.stderr)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

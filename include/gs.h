@@ -123,9 +123,11 @@ int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32
  *   e = 0.5 (A dx^2 + C dy^2) + B dx dy with d = p - (u, v); alpha = min(0.99, o exp(-e));
  *   skip if alpha < 1/255; C += T alpha c; T *= 1 - alpha; stop once T < 1e-4.
  * rgb[3][H][W] = C + T bg; T_final[H][W] = T; n_contrib[H][W] = 1 + (index within the tile's
- * range) of the last blended pair, 0 if none ([DR] "The trick": only the final state is kept). */
+ * range) of the last blended pair, 0 if none ([DR] "The trick": only the final state is kept).
+ * ws: gs_workspace_bytes(GS_WS_RENDER, 0, 0, W, H) bytes (the tiles' processing order). */
 int32_t gs_render_fwd(const gs_proj* proj, int64_t n, const uint32_t* vals, const uint32_t* ranges,
-                      const gs_camera* cam, float* rgb, float* T_final, uint32_t* n_contrib, void* stream);
+                      const gs_camera* cam, float* rgb, float* T_final, uint32_t* n_contrib, void* ws,
+                      size_t ws_bytes, void* stream);
 
 /* Loss (1 - lambda) L1 + lambda (1 - SSIM) and dL/dimg.  [GST] loss slides: L1 mean over
  * 3HW with zero subgradient at zero residual; SSIM with an 11 x 11 Gaussian window of
@@ -148,10 +150,12 @@ int32_t gs_loss_l1_dssim(const float* img, const float* target, int32_t H, int32
  * scale and quaternion, projection off |q|), "Where the position gradient comes from"
  * (mean path and the J(z) covariance path), "Spherical harmonics" (band gradients and the
  * view-direction term), sigmoid.  gparams: [P][n], overwritten (zero for culled Gaussians).
- * proj, vals, ranges, T_final and n_contrib must be those of the matching forward. */
+ * proj, vals, ranges, T_final and n_contrib must be those of the matching forward.
+ * ws: gs_workspace_bytes(GS_WS_RENDER, 0, 0, W, H) bytes. */
 int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t* vals, const uint32_t* ranges,
                       const gs_camera* cam, const float* T_final, const uint32_t* n_contrib,
-                      const float* dL_dimg, float* gscreen, float* gparams, void* stream);
+                      const float* dL_dimg, float* gscreen, float* gparams, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /* Adam, [GSG] Adam section; per-group rates [DR] "From a pixel error back to a quaternion".
  *   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
@@ -164,7 +168,7 @@ int32_t gs_adam_step(float* params, const float* grads, float* m, float* v, int6
                      const float* lr, double beta1, double beta2, double eps, int32_t step, void* stream);
 
 /* Workspace sizes, in bytes, for the calls that take one. */
-enum { GS_WS_PREPROCESS = 0, GS_WS_BIN_SORT = 1, GS_WS_LOSS = 2 };
+enum { GS_WS_PREPROCESS = 0, GS_WS_BIN_SORT = 1, GS_WS_LOSS = 2, GS_WS_RENDER = 3 };
 size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H);
 
 /* Message of the last failed call on this thread ("" if none). */

@@ -71,7 +71,10 @@ def test_argument_errors_without_gpu(gs):
     # loss with a bad lambda
     assert L.gs_loss_l1_dssim(1, 1, 8, 8, C.c_float(1.5), 1, 1, 1, 1 << 30, None) == gs.GS_ERR_INVALID_ARG
     # negative n
-    assert L.gs_render_fwd(C.byref(proj), -1, None, None, C.byref(cam), 1, 1, 1, None) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_render_fwd(C.byref(proj), -1, None, None, C.byref(cam), 1, 1, 1, None, 0,
+                           None) == gs.GS_ERR_INVALID_ARG
+    # render without its workspace
+    assert L.gs_render_fwd(C.byref(proj), 10, 1, 1, C.byref(cam), 1, 1, 1, None, 0, None) == gs.GS_ERR_CAPACITY
 
 
 def test_workspace_sizes_grow_with_the_problem(gs):

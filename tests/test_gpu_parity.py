@@ -79,7 +79,8 @@ def test_backward_small(torch_cuda, oracle, case):
     pl, c = pu.gpu_forward(s.params, deg, cam)
     pl.dLdI.copy_(torch.from_numpy(dLdI))
     from differentiable_tile_gaussian_amd import gs
-    gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, c, pl.T, pl.nc, pl.dLdI, pl.gscreen, pl.grads)
+    gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, c, pl.T, pl.nc, pl.dLdI, pl.gscreen, pl.grads,
+                     pl.ws_render)
     torch.cuda.synchronize()
     gscreen = pl.gscreen[:, :n].cpu().numpy()
     gparams = pl.grads.cpu().numpy()
