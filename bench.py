@@ -77,11 +77,12 @@ def run_steps(pl, cams, targets, first, count, timer=None, gs=None):
         if timer: timer.mark(s, 1)
         gs.gs_bin_sort(pl.proj, c, pl.pairs, pl.keys, pl.vals, pl.ranges, pl.ws_sort)
         if timer: timer.mark(s, 2)
-        gs.gs_render_fwd(pl.proj, pl.vals, pl.ranges, c, pl.rgb, pl.T, pl.nc, pl.ws_render)
+        gs.gs_render_fwd(pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.rgb, pl.T, pl.nc, pl.ws_render)
         if timer: timer.mark(s, 3)
         gs.gs_loss_l1_dssim(pl.rgb, tgt, pl.lam, pl.loss, pl.dLdI, pl.ws_loss)
         if timer: timer.mark(s, 4)
-        gs.gs_render_bwd(pl.params, pl.deg, pl.proj, pl.vals, pl.ranges, c, pl.T, pl.nc, pl.dLdI, pl.gscreen,
+        gs.gs_render_bwd(pl.params, pl.deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI,
+                         pl.gscreen,
                          pl.grads, pl.ws_render)
         if timer: timer.mark(s, 5)
         pl.adam()

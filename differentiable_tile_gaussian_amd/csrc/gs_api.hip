@@ -60,12 +60,31 @@ extern "C" {
 
 const char* gs_last_error(void) { return g_err; }
 
+int32_t gs_set_tuning(int32_t key, int64_t value) {
+  g_err[0] = 0;
+  if (value < 4 || value > (int64_t(1) << 24) || (value & 3))
+    return fail(GS_ERR_INVALID_ARG, "tuning value must be a multiple of 4 in [4, 2^24]");
+  switch (key) {
+    case GS_TUNE_SPLIT_FIRST: gsk::set_render_split(int(value), gsk::render_split_chunk()); return GS_OK;
+    case GS_TUNE_SPLIT_CHUNK: gsk::set_render_split(gsk::render_split_first(), int(value)); return GS_OK;
+    default: return fail(GS_ERR_INVALID_ARG, "unknown tuning key %d", key);
+  }
+}
+
+int64_t gs_get_tuning(int32_t key) {
+  switch (key) {
+    case GS_TUNE_SPLIT_FIRST: return gsk::render_split_first();
+    case GS_TUNE_SPLIT_CHUNK: return gsk::render_split_chunk();
+    default: return -1;
+  }
+}
+
 size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H) {
   switch (which_call) {
     case GS_WS_PREPROCESS: return gsk::scan_ws_bytes(n < 0 ? 0 : n) + 256;
     case GS_WS_BIN_SORT: return gsk::bin_sort_ws_bytes(pairs, 0);
     case GS_WS_LOSS: return (W > 0 && H > 0) ? gsk::loss_ws_bytes(H, W) : 0;
-    case GS_WS_RENDER: return (W > 0 && H > 0) ? gsk::render_ws_bytes(W, H) : 0;
+    case GS_WS_RENDER: return (W > 0 && H > 0) ? gsk::render_ws_bytes(W, H, pairs) : 0;
     default: return 0;
   }
 }
@@ -120,18 +139,19 @@ int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32
 }
 
 int32_t gs_render_fwd(const gs_proj* proj, int64_t n, const uint32_t* vals, const uint32_t* ranges,
-                      const gs_camera* cam, float* rgb, float* T_final, uint32_t* n_contrib, void* ws,
-                      size_t ws_bytes, void* stream) {
+                      uint32_t total_pairs, const gs_camera* cam, float* rgb, float* T_final,
+                      uint32_t* n_contrib, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   int32_t st;
   if (n < 0 || n >= (int64_t(1) << 31)) return fail(GS_ERR_INVALID_ARG, "n out of range");
   if ((st = check_camera(cam)) != GS_OK) return st;
   if ((st = check_proj(proj, n, false)) != GS_OK) return st;
   if (!ranges || !rgb || !T_final || !n_contrib) return fail(GS_ERR_INVALID_ARG, "an output or ranges is null");
-  const size_t need = gs_workspace_bytes(GS_WS_RENDER, 0, 0, cam->width, cam->height);
+  if (total_pairs > 0 && !vals) return fail(GS_ERR_INVALID_ARG, "vals is null");
+  const size_t need = gs_workspace_bytes(GS_WS_RENDER, n, total_pairs, cam->width, cam->height);
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "render workspace needs %zu bytes", need);
-  hipError_t e =
-      gsk::launch_render_fwd(*proj, vals, ranges, *cam, rgb, T_final, n_contrib, ws, as_stream(stream));
+  hipError_t e = gsk::launch_render_fwd(*proj, vals, ranges, *cam, total_pairs, rgb, T_final, n_contrib, ws,
+                                        as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "render_fwd");
   return GS_OK;
 }
@@ -151,9 +171,9 @@ int32_t gs_loss_l1_dssim(const float* img, const float* target, int32_t H, int32
 }
 
 int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t* vals, const uint32_t* ranges,
-                      const gs_camera* cam, const float* T_final, const uint32_t* n_contrib,
-                      const float* dL_dimg, float* gscreen, float* gparams, void* ws, size_t ws_bytes,
-                      void* stream) {
+                      uint32_t total_pairs, const gs_camera* cam, const float* T_final,
+                      const uint32_t* n_contrib, const float* dL_dimg, float* gscreen, float* gparams, void* ws,
+                      size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   int32_t st;
   if ((st = check_scene(scene)) != GS_OK) return st;
@@ -161,12 +181,13 @@ int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t
   if ((st = check_proj(proj, scene->n, false)) != GS_OK) return st;
   if (!ranges || !T_final || !n_contrib || !dL_dimg) return fail(GS_ERR_INVALID_ARG, "a render input is null");
   if (scene->n > 0 && (!gscreen || !gparams)) return fail(GS_ERR_INVALID_ARG, "gscreen or gparams is null");
-  const size_t need = gs_workspace_bytes(GS_WS_RENDER, 0, 0, cam->width, cam->height);
+  if (total_pairs > 0 && !vals) return fail(GS_ERR_INVALID_ARG, "vals is null");
+  const size_t need = gs_workspace_bytes(GS_WS_RENDER, scene->n, total_pairs, cam->width, cam->height);
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "render workspace needs %zu bytes", need);
   hipStream_t s = as_stream(stream);
   const int n = int(scene->n);
-  hipError_t e =
-      gsk::launch_render_bwd(*proj, n, vals, ranges, *cam, T_final, n_contrib, dL_dimg, gscreen, ws, s);
+  hipError_t e = gsk::launch_render_bwd(*proj, n, vals, ranges, *cam, total_pairs, T_final, n_contrib, dL_dimg,
+                                        gscreen, ws, s);
   if (e != hipSuccess) return hip_fail(e, "render_bwd");
   e = gsk::launch_preprocess_bwd(scene->params, n, scene->sh_degree, *cam, proj->tiles, gscreen, gparams, s);
   if (e != hipSuccess) return hip_fail(e, "preprocess_bwd");

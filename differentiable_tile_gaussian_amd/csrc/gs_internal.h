@@ -35,13 +35,17 @@ hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uin
                            uint32_t* vals, uint32_t* ranges, void* ws, hipStream_t s);
 
 // ---- render.hip
-size_t render_ws_bytes(int W, int H);
+int32_t set_render_split(int first, int chunk);
+int render_split_first();
+int render_split_chunk();
+size_t render_ws_bytes(int W, int H, uint32_t pairs);
 hipError_t launch_render_fwd(const gs_proj& proj, const uint32_t* vals, const uint32_t* ranges,
-                             const gs_camera& cam, float* rgb, float* T_final, uint32_t* n_contrib, void* ws,
-                             hipStream_t s);
+                             const gs_camera& cam, uint32_t pairs, float* rgb, float* T_final,
+                             uint32_t* n_contrib, void* ws, hipStream_t s);
 hipError_t launch_render_bwd(const gs_proj& proj, int n, const uint32_t* vals, const uint32_t* ranges,
-                             const gs_camera& cam, const float* T_final, const uint32_t* n_contrib,
-                             const float* dL_dimg, float* gscreen, void* ws, hipStream_t s);
+                             const gs_camera& cam, uint32_t pairs, const float* T_final,
+                             const uint32_t* n_contrib, const float* dL_dimg, float* gscreen, void* ws,
+                             hipStream_t s);
 
 // ---- loss.hip
 size_t loss_ws_bytes(int H, int W);

@@ -1,18 +1,41 @@
 // Tile blend kernels: front-to-back forward and back-to-front backward.
 //
-// One 256-thread block per 16x16 tile, one thread per pixel; blocks take the
-// tiles longest list first (a one-block bucket sort by log2 of the list length)
-// so that the long lists start at once and the short ones fill in behind them.
-// A tile's sorted pair list is walked in batches of 256: the block gathers the
-// batch's records into LDS (double-buffered: the next batch's global gather is
-// issued before the current batch is blended), then every pixel reads them as
-// wave-wide broadcasts.
+// Short path.  One 256-thread block per 16x16 tile, one thread per pixel; blocks
+// take the tiles longest list first (a one-block bucket sort by log2 of the list
+// length).  A tile's sorted pair list is walked in batches of 256: the block
+// gathers a batch's records into LDS (double-buffered: the next batch's gather is
+// issued before the current one is blended) and every pixel reads them as
+// wave-wide broadcasts.  The per-entry arithmetic is branch-free: a pair that is
+// skipped (alpha below 1/255) or comes after the pixel stopped is blended with
+// alpha = 0, which leaves T and the colour unchanged bit for bit, so the result is
+// that of the sequential walk with `continue` and `break`.
 //
-// The per-entry arithmetic is branch-free.  A pair that is skipped (alpha below
-// 1/255) or that comes after the pixel stopped is blended with alpha = 0, which
-// leaves T and the colour unchanged bit for bit, so the result is the one of the
-// sequential walk with `continue` and `break`.  Waves leave the batch loop as soon
-// as all their pixels have stopped.
+// Split path.  One block can only use one CU, and a few tiles carry lists of tens
+// of thousands of pairs, so the first `first` pairs of every tile are walked as
+// above and a tile whose pixels are not all finished then is split: its remaining
+// pairs form chunks of `chunk` pairs that separate blocks walk at the same time.
+//   chunk 0   continues the exact walk from the carried state;
+//   chunk c>0 walks from T = 1 (the local transmittance and colour of the chunk),
+//             stops a pixel once its local T drops below 1e-4 (then the overall T
+//             has too) and drops pixels that an earlier chunk has already
+//             saturated (a per-pixel "first saturating chunk" marker, polled);
+//   combine   per pixel, chains the chunks: T_front(c+1) = T_front(c) T_c and
+//             colour += T_front(c) C_c, until the product falls below 1e-4;
+//   re-walk   the chunk where that happens is walked again from T_front with the
+//             test T_front * T_local < 1e-4 to find the exact last pair;
+//   finalize  writes the pixel and, back to front, the state at each chunk end
+//             that the backward needs (T there and S, the colour behind it,
+//             accumulated from the background and each chunk's own colour sum).
+// The split path keeps per pixel one boundary state per chunk of a split tile.
+// It changes only where products are rounded (T_front T_local instead of one
+// running product).
+//
+// Backward.  Each pixel walks from its last contributing pair back to the first,
+// recovering T by division and carrying S ([DR] "The trick"); every entry's nine
+// partials are summed over the wave (transposed butterfly), then over the block's
+// waves in LDS, then added to the Gaussian's gradient with one set of global
+// atomics per (tile or chunk, Gaussian).  Split tiles run one block per chunk, each
+// starting from the boundary state the forward left.
 //
 // The conic is prescaled when staged: q = a' dx^2 + b' dx dy + c' dy^2 with
 // (a', b', c') = -log2(e) (A/2, B, C/2), so the Gaussian factor exp(-e) is one exp2.
@@ -24,6 +47,8 @@
 // derivative slide.  ([GSG] is "How a computer rebuilds a real place out of soft
 // colored dots called Gaussian Splats", [DR] "Differentiable rasterisation",
 // [GST] the Gaussian splatting training study deck.)
+#include <algorithm>
+
 #include "gs_internal.h"
 
 namespace gsk {
@@ -34,8 +59,74 @@ constexpr float kAlphaMin = 1.0f / 255.0f;
 constexpr float kAlphaCap = 0.99f;
 constexpr float kTStop = 1e-4f;
 constexpr float kLog2e = 1.44269504088896341f;
+constexpr uint32_t kFlag = 0x80000000u;
+constexpr uint32_t kIdx = 0x7fffffffu;
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workspace of one render (forward and its backward).  Per-slot arrays hold 256
+// entries per split tile, per-item arrays 256 entries per chunk.
+struct SplitWs {
+  uint32_t* order;        // [NT] tiles, longest list first
+  uint32_t* counters;     // [0] split tiles (slots), [1] chunks (items)
+  int32_t* slot_of_tile;  // [NT] slot or -1
+  uint32_t* slot_tile;    // [S]
+  uint32_t* slot_first;   // [S] first item of the slot
+  uint32_t* slot_nch;     // [S] chunks of the slot
+  uint2* items;           // [I] (slot, chunk)
+  float4* st4;            // [S][256] T and colour after the first segment
+  uint32_t* stl;          // [S][256] last pair | done flag
+  uint32_t* sat;          // [S][256] first chunk that saturated the pixel
+  float4* part4;          // [I][256] chunk partials, later (T_end, S_end) boundaries
+  uint32_t* partl;        // [I][256] last pair in the chunk | stop flag
+  int32_t* stopc;         // [S][256] chunk holding the last pair (-1: first segment, nch: none)
+  float4* fin4;           // [S][256] final (or front) T and colour
+  uint32_t* finl;         // [S][256] final (or front) last pair
+  float4* bnd1;           // [S][256] T and S at the end of the first segment
+};
+
+inline size_t a256(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct SplitDims {
+  size_t NT, S, I;
+};
+
+SplitDims split_dims(int W, int H, uint32_t pairs, int first, int chunk) {
+  SplitDims d;
+  d.NT = size_t((W + kTile - 1) / kTile) * ((H + kTile - 1) / kTile);
+  d.S = std::min(d.NT, size_t(pairs) / size_t(first) + 1);
+  d.I = size_t(pairs) / size_t(chunk) + d.S + 1;
+  return d;
+}
+
+SplitWs carve(void* ws, const SplitDims& d) {
+  char* p = static_cast<char*>(ws);
+  SplitWs w;
+  auto take = [&](size_t bytes) { char* q = p; p += a256(bytes); return q; };
+  w.order = reinterpret_cast<uint32_t*>(take(d.NT * 4));
+  w.counters = reinterpret_cast<uint32_t*>(take(8));
+  w.slot_of_tile = reinterpret_cast<int32_t*>(take(d.NT * 4));
+  w.slot_tile = reinterpret_cast<uint32_t*>(take(d.S * 4));
+  w.slot_first = reinterpret_cast<uint32_t*>(take(d.S * 4));
+  w.slot_nch = reinterpret_cast<uint32_t*>(take(d.S * 4));
+  w.items = reinterpret_cast<uint2*>(take(d.I * 8));
+  w.st4 = reinterpret_cast<float4*>(take(d.S * 256 * 16));
+  w.stl = reinterpret_cast<uint32_t*>(take(d.S * 256 * 4));
+  w.sat = reinterpret_cast<uint32_t*>(take(d.S * 256 * 4));
+  w.part4 = reinterpret_cast<float4*>(take(d.I * 256 * 16));
+  w.partl = reinterpret_cast<uint32_t*>(take(d.I * 256 * 4));
+  w.stopc = reinterpret_cast<int32_t*>(take(d.S * 256 * 4));
+  w.fin4 = reinterpret_cast<float4*>(take(d.S * 256 * 16));
+  w.finl = reinterpret_cast<uint32_t*>(take(d.S * 256 * 4));
+  w.bnd1 = reinterpret_cast<float4*>(take(d.S * 256 * 16));
+  return w;
+}
+
+size_t carve_bytes(const SplitDims& d) {
+  return a256(d.NT * 4) + a256(8) + a256(d.NT * 4) + 3 * a256(d.S * 4) + a256(d.I * 8) + a256(d.S * 256 * 16) +
+         2 * a256(d.S * 256 * 4) + a256(d.I * 256 * 16) + a256(d.I * 256 * 4) + a256(d.S * 256 * 4) +
+         a256(d.S * 256 * 16) + a256(d.S * 256 * 4) + a256(d.S * 256 * 16);
+}
 
 // ---------------------------------------------------------------- tile order
 // Tiles sorted by bucket 32 - clz(length), longest bucket first (order within a
@@ -67,7 +158,20 @@ __global__ void __launch_bounds__(1024) tile_order_kernel(const uint32_t* __rest
   }
 }
 
-// Record as staged in LDS for the forward: (u, v, a', b'), (c', opacity, r, g), b.
+__global__ void split_init_kernel(uint32_t* __restrict__ counters, int32_t* __restrict__ slot_of_tile,
+                                  int num_tiles) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < 2) counters[i] = 0u;
+  if (i < num_tiles) slot_of_tile[i] = -1;
+}
+
+// ------------------------------------------------------------ forward walk
+struct FwdLds {
+  float4 a[2][kBatch];   // u, v, a', b'
+  float4 b[2][kBatch];   // c', opacity, r, g
+  float c[2][kBatch];    // b
+};
+
 __device__ inline void stage_fwd(const float4* __restrict__ splat, uint32_t g, float4& a, float4& b, float& c) {
   const float4 r0 = splat[3 * g], r1 = splat[3 * g + 1];
   c = splat[3 * g + 2].x;
@@ -75,84 +179,296 @@ __device__ inline void stage_fwd(const float4* __restrict__ splat, uint32_t g, f
   b = make_float4(-0.5f * kLog2e * r1.x, r1.y, r1.z, r1.w);
 }
 
+struct PixelFwd {
+  float T, c0, c1, c2;
+  uint32_t last;   // 1 + index (within the tile's list) of the last blended pair, 0 if none
+  bool done;
+};
+
+// Walks the pairs [lo, hi) of a tile list starting at `start`.  A pixel stops once
+// pre * T < 1e-4 (pre = 1 for a walk whose T is the overall transmittance).  With
+// POLL, a pixel also stops when sat[tid] < chunk_id; a pixel that saturates here
+// records chunk_id in sat[tid].  Must be called by all 256 threads of the block.
+template <bool POLL>
+__device__ void fwd_walk(FwdLds& L, const float4* __restrict__ splat, const uint32_t* __restrict__ vals,
+                         uint32_t start, int lo, int hi, float fx, float fy, float pre, PixelFwd& s,
+                         uint32_t* sat, uint32_t chunk_id) {
+  const int tid = threadIdx.x;
+  if (lo >= hi) return;
+  {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    float c = 0.f;
+    if (lo + tid < hi) stage_fwd(splat, vals[start + uint32_t(lo + tid)], a, b, c);
+    L.a[0][tid] = a; L.b[0][tid] = b; L.c[0][tid] = c;
+  }
+  __syncthreads();
+  bool reported = s.done;
+  int buf = 0;
+  for (int base = lo; base < hi; base += kBatch) {
+    const int nxt = base + kBatch + tid;
+    float4 na = make_float4(0.f, 0.f, 0.f, 0.f), nb = na;
+    float nc = 0.f;
+    if (nxt < hi) stage_fwd(splat, vals[start + uint32_t(nxt)], na, nb, nc);
+    const int cnt = min(kBatch, hi - base);
+    if (!__all(s.done)) {
+      for (int j = 0; j < cnt; j += 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float4 a = L.a[buf][j + k];
+          const float4 b = L.b[buf][j + k];
+          const float cb = L.c[buf][j + k];
+          const float dx = fx - a.x, dy = fy - a.y;
+          const float q = a.z * dx * dx + a.w * dx * dy + b.x * dy * dy;
+          float alpha = fminf(kAlphaCap, b.y * fast_exp2(q));
+          const bool ok = !s.done && alpha >= kAlphaMin;
+          alpha = ok ? alpha : 0.0f;
+          const float w = alpha * s.T;
+          s.c0 += w * b.z;
+          s.c1 += w * b.w;
+          s.c2 += w * cb;
+          s.T = s.T * (1.0f - alpha);
+          s.last = ok ? uint32_t(base + j + k + 1) : s.last;
+          s.done = s.done || (pre * s.T < kTStop);
+        }
+        if (__all(s.done)) break;
+      }
+    }
+    if (base + kBatch < hi) {
+      L.a[buf ^ 1][tid] = na; L.b[buf ^ 1][tid] = nb; L.c[buf ^ 1][tid] = nc;
+    }
+    if (POLL) {
+      if (s.done && !reported) {
+        atomicMin(&sat[tid], chunk_id);
+        reported = true;
+      }
+      if (!s.done) {
+        const uint32_t first_sat = __hip_atomic_load(&sat[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (first_sat < chunk_id) {
+          s.done = true;
+          reported = true;
+        }
+      }
+    }
+    if (__syncthreads_count(s.done) == kBatch) break;
+    buf ^= 1;
+  }
+}
+
+// Phase 1: the first `first` pairs of every tile; tiles that are not finished then
+// are registered for the split path and write no output here.
 __global__ void __launch_bounds__(256) render_fwd_kernel(const float4* __restrict__ splat,
                                                           const uint32_t* __restrict__ vals,
-                                                          const uint32_t* __restrict__ ranges,
-                                                          const uint32_t* __restrict__ order, int num_tiles, int tx,
-                                                          int W, int H, float bg0, float bg1, float bg2,
-                                                          float* __restrict__ rgb, float* __restrict__ T_final,
+                                                          const uint32_t* __restrict__ ranges, SplitWs ws,
+                                                          int num_tiles, int tx, int W, int H, float bg0, float bg1,
+                                                          float bg2, int first, int chunk, float* __restrict__ rgb,
+                                                          float* __restrict__ T_final,
                                                           uint32_t* __restrict__ n_contrib) {
-  __shared__ float4 s_a[2][kBatch];
-  __shared__ float4 s_b[2][kBatch];
-  __shared__ float s_c[2][kBatch];
-  const int tile = int(order[blockIdx.x]);
+  __shared__ FwdLds L;
+  __shared__ uint32_t s_slot, s_first, s_nch;
+  const int tile = int(ws.order[blockIdx.x]);
   const int tid = threadIdx.x;
   const int px = (tile % tx) * kTile + (tid & (kTile - 1));
   const int py = (tile / tx) * kTile + (tid >> 4);
   const bool inside = px < W && py < H;
-  const float fx = float(px) + 0.5f, fy = float(py) + 0.5f;
   const uint32_t start = ranges[tile];
   const int n = int(ranges[num_tiles + tile] - start);
-  float T = 1.0f, c0 = 0.0f, c1 = 0.0f, c2 = 0.0f;
-  uint32_t last = 0;
-  bool done = !inside;
-  if (n > 0) {
-    {
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-      float c = 0.f;
-      if (tid < n) stage_fwd(splat, vals[start + tid], a, b, c);
-      s_a[0][tid] = a; s_b[0][tid] = b; s_c[0][tid] = c;
-    }
-    __syncthreads();
-    int buf = 0;
-    for (int base = 0; base < n; base += kBatch) {
-      // gather the next batch while this one is blended (zero records pad the tail: opacity 0)
-      const int nxt = base + kBatch + tid;
-      float4 na = make_float4(0.f, 0.f, 0.f, 0.f), nb = na;
-      float nc = 0.f;
-      if (nxt < n) stage_fwd(splat, vals[start + nxt], na, nb, nc);
-      const int cnt = min(kBatch, n - base);
-      if (!__all(done)) {
-        for (int j = 0; j < cnt; j += 4) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float4 a = s_a[buf][j + k];
-            const float4 b = s_b[buf][j + k];
-            const float cb = s_c[buf][j + k];
-            const float dx = fx - a.x, dy = fy - a.y;
-            const float q = a.z * dx * dx + a.w * dx * dy + b.x * dy * dy;
-            float alpha = fminf(kAlphaCap, b.y * fast_exp2(q));
-            const bool ok = !done && alpha >= kAlphaMin;
-            alpha = ok ? alpha : 0.0f;
-            const float w = alpha * T;
-            c0 += w * b.z;
-            c1 += w * b.w;
-            c2 += w * cb;
-            T = T * (1.0f - alpha);
-            last = ok ? uint32_t(base + j + k + 1) : last;
-            done = done || (T < kTStop);
-          }
-          if (__all(done)) break;
-        }
+  PixelFwd s{1.0f, 0.0f, 0.0f, 0.0f, 0u, !inside};
+  fwd_walk<false>(L, splat, vals, start, 0, min(n, first), float(px) + 0.5f, float(py) + 0.5f, 1.0f, s, nullptr,
+                  0u);
+  if (n > first) {
+    if (__syncthreads_count(s.done) < kBatch) {
+      if (tid == 0) {
+        const uint32_t slot = atomicAdd(&ws.counters[0], 1u);
+        const uint32_t nch = uint32_t((n - first + chunk - 1) / chunk);
+        const uint32_t fi = atomicAdd(&ws.counters[1], nch);
+        ws.slot_tile[slot] = uint32_t(tile);
+        ws.slot_first[slot] = fi;
+        ws.slot_nch[slot] = nch;
+        ws.slot_of_tile[tile] = int32_t(slot);
+        s_slot = slot; s_first = fi; s_nch = nch;
       }
-      if (base + kBatch < n) {
-        s_a[buf ^ 1][tid] = na; s_b[buf ^ 1][tid] = nb; s_c[buf ^ 1][tid] = nc;
-      }
-      if (__syncthreads_count(done) == kBatch) break;
-      buf ^= 1;
+      __syncthreads();
+      const size_t o = size_t(s_slot) * 256 + tid;
+      ws.st4[o] = make_float4(s.T, s.c0, s.c1, s.c2);
+      ws.stl[o] = s.last | (s.done ? kFlag : 0u);
+      ws.sat[o] = s.done ? 0u : 0xffffffffu;
+      for (uint32_t c = tid; c < s_nch; c += 256) ws.items[s_first + c] = make_uint2(s_slot, c);
+      return;
     }
   }
   if (inside) {
     const int p = py * W + px;
     const int HW = W * H;
-    rgb[p] = c0 + T * bg0;
-    rgb[HW + p] = c1 + T * bg1;
-    rgb[2 * HW + p] = c2 + T * bg2;
-    T_final[p] = T;
-    n_contrib[p] = last;
+    rgb[p] = s.c0 + s.T * bg0;
+    rgb[HW + p] = s.c1 + s.T * bg1;
+    rgb[2 * HW + p] = s.c2 + s.T * bg2;
+    T_final[p] = s.T;
+    n_contrib[p] = s.last;
   }
 }
 
+// Phase 2: one block per chunk of a split tile.
+__global__ void __launch_bounds__(256) split_chunk_kernel(const float4* __restrict__ splat,
+                                                           const uint32_t* __restrict__ vals,
+                                                           const uint32_t* __restrict__ ranges, SplitWs ws,
+                                                           int num_tiles, int tx, int first, int chunk) {
+  __shared__ FwdLds L;
+  const uint32_t item = blockIdx.x;
+  if (item >= ws.counters[1]) return;
+  const uint2 sc = ws.items[item];
+  const uint32_t slot = sc.x, c = sc.y;
+  const int tile = int(ws.slot_tile[slot]);
+  const int tid = threadIdx.x;
+  const int px = (tile % tx) * kTile + (tid & (kTile - 1));
+  const int py = (tile / tx) * kTile + (tid >> 4);
+  const uint32_t start = ranges[tile];
+  const int n = int(ranges[num_tiles + tile] - start);
+  const int lo = first + int(c) * chunk, hi = min(lo + chunk, n);
+  const size_t so = size_t(slot) * 256 + tid;
+  const bool done0 = (ws.stl[so] & kFlag) != 0u;
+  PixelFwd s{c == 0 ? ws.st4[so].x : 1.0f, 0.0f, 0.0f, 0.0f, 0u, done0};
+  if (c == 0)
+    fwd_walk<false>(L, splat, vals, start, lo, hi, float(px) + 0.5f, float(py) + 0.5f, 1.0f, s, nullptr, 0u);
+  else
+    fwd_walk<true>(L, splat, vals, start, lo, hi, float(px) + 0.5f, float(py) + 0.5f, 1.0f, s, ws.sat + size_t(slot) * 256,
+                   c);
+  const size_t io = size_t(item) * 256 + tid;
+  ws.part4[io] = make_float4(s.T, s.c0, s.c1, s.c2);
+  // chunk 0 continues the exact walk: its flag means "stopped here"
+  const bool stopped0 = c == 0 && !done0 && s.T < kTStop;
+  ws.partl[io] = s.last | (stopped0 ? kFlag : 0u);
+  if (c == 0 && stopped0) atomicMin(&ws.sat[so], 0u);
+}
+
+// Phase 3: per split tile and pixel, chain the chunks and find the one holding the stop.
+__global__ void __launch_bounds__(256) split_combine_kernel(SplitWs ws) {
+  const uint32_t slot = blockIdx.x;
+  if (slot >= ws.counters[0]) return;
+  const int tid = threadIdx.x;
+  const size_t so = size_t(slot) * 256 + tid;
+  const uint32_t fi = ws.slot_first[slot], nch = ws.slot_nch[slot];
+  const uint32_t l1 = ws.stl[so];
+  const float4 s1 = ws.st4[so];
+  float T = s1.x, c0 = s1.y, c1 = s1.z, c2 = s1.w;
+  uint32_t last = l1 & kIdx;
+  int32_t stop;
+  if (l1 & kFlag) {
+    stop = -1;
+  } else {
+    const size_t o0 = size_t(fi) * 256 + tid;
+    const float4 p0 = ws.part4[o0];   // absolute T after chunk 0 and the colour chunk 0 added
+    const uint32_t l0 = ws.partl[o0];
+    T = p0.x;
+    c0 += p0.y; c1 += p0.z; c2 += p0.w;
+    if (l0 & kIdx) last = l0 & kIdx;
+    if (l0 & kFlag) {
+      stop = 0;
+    } else {
+      stop = int32_t(nch);
+      for (uint32_t c = 1; c < nch; ++c) {
+        const size_t oc = size_t(fi + c) * 256 + tid;
+        const float4 pc = ws.part4[oc];
+        const float Tn = T * pc.x;
+        if (Tn < kTStop) {
+          stop = int32_t(c);
+          break;
+        }
+        const float a0 = T * pc.y, a1 = T * pc.z, a2 = T * pc.w;
+        ws.part4[oc] = make_float4(Tn, a0, a1, a2);   // T at the chunk end, colour it added
+        c0 += a0; c1 += a1; c2 += a2;
+        T = Tn;
+        const uint32_t lc = ws.partl[oc] & kIdx;
+        if (lc) last = lc;
+      }
+    }
+  }
+  ws.stopc[so] = stop;
+  ws.fin4[so] = make_float4(T, c0, c1, c2);
+  ws.finl[so] = last;
+}
+
+// Phase 4: walk again the chunk that holds a pixel's stop, from T_front, to find the pair.
+__global__ void __launch_bounds__(256) split_rewalk_kernel(const float4* __restrict__ splat,
+                                                            const uint32_t* __restrict__ vals,
+                                                            const uint32_t* __restrict__ ranges, SplitWs ws,
+                                                            int num_tiles, int tx, int first, int chunk) {
+  __shared__ FwdLds L;
+  const uint32_t item = blockIdx.x;
+  if (item >= ws.counters[1]) return;
+  const uint2 sc = ws.items[item];
+  const uint32_t slot = sc.x, c = sc.y;
+  if (c == 0) return;
+  const int tid = threadIdx.x;
+  const size_t so = size_t(slot) * 256 + tid;
+  const bool need = ws.stopc[so] == int32_t(c);
+  if (__syncthreads_count(need) == 0) return;
+  const int tile = int(ws.slot_tile[slot]);
+  const int px = (tile % tx) * kTile + (tid & (kTile - 1));
+  const int py = (tile / tx) * kTile + (tid >> 4);
+  const uint32_t start = ranges[tile];
+  const int n = int(ranges[num_tiles + tile] - start);
+  const int lo = first + int(c) * chunk, hi = min(lo + chunk, n);
+  float4 front = make_float4(1.f, 0.f, 0.f, 0.f);
+  uint32_t lastf = 0;
+  if (need) {
+    front = ws.fin4[so];
+    lastf = ws.finl[so];
+  }
+  PixelFwd s{1.0f, 0.0f, 0.0f, 0.0f, 0u, !need};
+  fwd_walk<false>(L, splat, vals, start, lo, hi, float(px) + 0.5f, float(py) + 0.5f, front.x, s, nullptr, 0u);
+  if (need) {
+    const float a0 = front.x * s.c0, a1 = front.x * s.c1, a2 = front.x * s.c2;
+    const float Tf = front.x * s.T;
+    ws.fin4[so] = make_float4(Tf, front.y + a0, front.z + a1, front.w + a2);
+    ws.finl[so] = s.last ? s.last : lastf;
+    ws.part4[size_t(item) * 256 + tid] = make_float4(Tf, a0, a1, a2);
+  }
+}
+
+// Phase 5: outputs of split tiles, and the chunk-end states for the backward
+// (T there and S = colour behind, summed from the background forward).
+__global__ void __launch_bounds__(256) split_finalize_kernel(SplitWs ws, int tx, int W, int H, float bg0,
+                                                              float bg1, float bg2, float* __restrict__ rgb,
+                                                              float* __restrict__ T_final,
+                                                              uint32_t* __restrict__ n_contrib) {
+  const uint32_t slot = blockIdx.x;
+  if (slot >= ws.counters[0]) return;
+  const int tid = threadIdx.x;
+  const int tile = int(ws.slot_tile[slot]);
+  const int px = (tile % tx) * kTile + (tid & (kTile - 1));
+  const int py = (tile / tx) * kTile + (tid >> 4);
+  const size_t so = size_t(slot) * 256 + tid;
+  const int32_t stop = ws.stopc[so];
+  const float4 f = ws.fin4[so];
+  if (px < W && py < H) {
+    const int p = py * W + px;
+    const int HW = W * H;
+    rgb[p] = f.y + f.x * bg0;
+    rgb[HW + p] = f.z + f.x * bg1;
+    rgb[2 * HW + p] = f.w + f.x * bg2;
+    T_final[p] = f.x;
+    n_contrib[p] = ws.finl[so];
+  }
+  if (stop < 0) return;
+  const uint32_t fi = ws.slot_first[slot], nch = ws.slot_nch[slot];
+  float S0 = bg0 * f.x, S1 = bg1 * f.x, S2 = bg2 * f.x;
+  int c = stop;
+  if (uint32_t(stop) < nch) {
+    const float4 ps = ws.part4[size_t(fi + stop) * 256 + tid];
+    S0 += ps.y; S1 += ps.z; S2 += ps.w;
+  } else {
+    c = int(nch);
+  }
+  for (--c; c >= 0; --c) {
+    const size_t oc = size_t(fi + uint32_t(c)) * 256 + tid;
+    const float4 pc = ws.part4[oc];
+    ws.part4[oc] = make_float4(pc.x, S0, S1, S2);
+    S0 += pc.y; S1 += pc.z; S2 += pc.w;
+  }
+  ws.bnd1[so] = make_float4(ws.st4[so].x, S0, S1, S2);
+}
+
+// ----------------------------------------------------------- backward walk
 // Sum 9 per-lane values over the 64 lanes of a wave.  Values 0..7 use a transposed
 // butterfly (each exchange halves the values a lane carries), value 8 a plain one.
 // On return lane l holds the total of value (l >> 3) in v[0] and every lane holds
@@ -190,7 +506,15 @@ __device__ inline void wave_sum9(float* v) {
   for (int d = 32; d >= 1; d >>= 1) v[8] += __shfl_xor(v[8], d, 64);
 }
 
-// Record as staged in LDS for the backward: (u, v, a', b'), (c', opacity, r, g), (b, A, B, C).
+struct BwdLds {
+  float4 a[2][kBatch];     // u, v, a', b'
+  float4 b[2][kBatch];     // c', opacity, r, g
+  float4 c[2][kBatch];     // b, A, B, C
+  uint32_t id[2][kBatch];
+  float acc[9][kBatch];    // per-entry sums over the block's waves
+  uint32_t top;
+};
+
 __device__ inline void stage_bwd(const float4* __restrict__ splat, uint32_t g, float4& a, float4& b, float4& c) {
   const float4 r0 = splat[3 * g], r1 = splat[3 * g + 1], r2 = splat[3 * g + 2];
   a = make_float4(r0.x, r0.y, -0.5f * kLog2e * r0.z, -kLog2e * r0.w);
@@ -198,95 +522,70 @@ __device__ inline void stage_bwd(const float4* __restrict__ splat, uint32_t g, f
   c = make_float4(r2.x, r0.z, r0.w, r1.x);
 }
 
-__global__ void __launch_bounds__(256) render_bwd_kernel(const float4* __restrict__ splat,
-                                                          const uint32_t* __restrict__ vals,
-                                                          const uint32_t* __restrict__ ranges,
-                                                          const uint32_t* __restrict__ order, int num_tiles, int tx,
-                                                          int W, int H, float bg0, float bg1, float bg2,
-                                                          const float* __restrict__ T_final,
-                                                          const uint32_t* __restrict__ n_contrib,
-                                                          const float* __restrict__ dL_dimg, int n,
-                                                          float* __restrict__ gscreen) {
-  __shared__ float4 s_a[2][kBatch];
-  __shared__ float4 s_b[2][kBatch];
-  __shared__ float4 s_c[2][kBatch];
-  __shared__ uint32_t s_id[2][kBatch];
-  __shared__ float s_acc[9][kBatch];     // per-entry sums over the block's four waves
-  __shared__ uint32_t s_max;
-  const int tile = int(order[blockIdx.x]);
+struct PixelBwd {
+  float T, S0, S1, S2;    // transmittance behind the next pair to walk, colour behind it
+  float g0, g1, g2;       // dL/dpixel
+  int top;                // pairs [lo, top) are walked, top - 1 first
+};
+
+// Walks pairs top-1 .. lo (top per pixel, at most hi) of a tile list, adding
+// each pair's partials to gscreen.  Must be called by all 256 threads.
+__device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint32_t* __restrict__ vals,
+                         uint32_t start, int lo, float fx, float fy, PixelBwd& s, int n,
+                         float* __restrict__ gscreen) {
   const int tid = threadIdx.x;
   const int lane = __lane_id();
-  const int px = (tile % tx) * kTile + (tid & (kTile - 1));
-  const int py = (tile / tx) * kTile + (tid >> 4);
-  const bool inside = px < W && py < H;
-  const float fx = float(px) + 0.5f, fy = float(py) + 0.5f;
-  const uint32_t start = ranges[tile];
-  const int HW = W * H;
-  const int p = py * W + px;
-  uint32_t nc = 0;
-  float T = 0.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
-  if (inside) {
-    nc = n_contrib[p];
-    T = T_final[p];
-    g0 = dL_dimg[p];
-    g1 = dL_dimg[HW + p];
-    g2 = dL_dimg[2 * HW + p];
-  }
-  float S0 = bg0 * T, S1 = bg1 * T, S2 = bg2 * T;
-  if (tid == 0) s_max = 0u;
+  if (tid == 0) L.top = 0u;
 #pragma unroll
-  for (int k = 0; k < 9; ++k) s_acc[k][tid] = 0.0f;
+  for (int k = 0; k < 9; ++k) L.acc[k][tid] = 0.0f;
   __syncthreads();
-  if (nc > 0) atomicMax(&s_max, nc);
-  // largest n_contrib of this wave: entries at or beyond it need no work from this wave
-  uint32_t wave_max = nc;
+  if (s.top > lo) atomicMax(&L.top, uint32_t(s.top));
+  int wave_top = s.top;
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) wave_max = max(wave_max, uint32_t(__shfl_xor(int(wave_max), d, 64)));
+  for (int d = 32; d >= 1; d >>= 1) wave_top = max(wave_top, __shfl_xor(wave_top, d, 64));
   __syncthreads();
-  const int max_nc = int(s_max);
-  if (max_nc == 0) return;
-  // batch k covers local entries [hi - 256, hi), walked from hi - 1 down
-  int hi = max_nc;
+  int hi = int(L.top);
+  if (hi <= lo) return;
   {
-    const int lo = max(hi - kBatch, 0);
+    const int blo = max(hi - kBatch, lo);
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a, c = a;
     uint32_t g = 0;
-    if (lo + tid < hi) {
-      g = vals[start + uint32_t(lo + tid)];
+    if (blo + tid < hi) {
+      g = vals[start + uint32_t(blo + tid)];
       stage_bwd(splat, g, a, b, c);
     }
-    s_a[0][tid] = a; s_b[0][tid] = b; s_c[0][tid] = c; s_id[0][tid] = g;
+    L.a[0][tid] = a; L.b[0][tid] = b; L.c[0][tid] = c; L.id[0][tid] = g;
   }
   __syncthreads();
   int buf = 0;
-  while (hi > 0) {
-    const int lo = max(hi - kBatch, 0);
-    // gather the next (earlier) batch
-    const int nhi = lo, nlo = max(nhi - kBatch, 0);
+  while (hi > lo) {
+    const int blo = max(hi - kBatch, lo);
+    const int nhi = blo, nlo = max(nhi - kBatch, lo);
     float4 na = make_float4(0.f, 0.f, 0.f, 0.f), nb = na, ncr = na;
     uint32_t ng = 0;
     if (nlo + tid < nhi) {
       ng = vals[start + uint32_t(nlo + tid)];
       stage_bwd(splat, ng, na, nb, ncr);
     }
-    const int jtop = min(hi, int(wave_max)) - 1;
-    for (int j = jtop; j >= lo; --j) {
-      const int e = j - lo;
-      const float4 a = s_a[buf][e];
-      const float4 b = s_b[buf][e];
-      const float4 c = s_c[buf][e];
+    const int jtop = min(hi, wave_top) - 1;
+    for (int j = jtop; j >= blo; --j) {
+      const int e = j - blo;
+      const float4 a = L.a[buf][e];
+      const float4 b = L.b[buf][e];
+      const float4 c = L.c[buf][e];
       const float dx = fx - a.x, dy = fy - a.y;
       const float q = a.z * dx * dx + a.w * dx * dy + b.x * dy * dy;
       const float G = fast_exp2(q);
       const float araw = b.y * G;
       const float alpha = fminf(kAlphaCap, araw);
-      const bool ok = uint32_t(j) < nc && alpha >= kAlphaMin;
+      const bool ok = j < s.top && alpha >= kAlphaMin;
       if (__ballot(ok) == 0) continue;
       float v[9];
       const float inv = __builtin_amdgcn_rcpf(1.0f - alpha);
-      const float Tn = T * inv;           // transmittance in front of this entry
+      const float Tn = s.T * inv;           // transmittance in front of this pair
       const float w = alpha * Tn;
-      const float galpha = g0 * (b.z * Tn - S0 * inv) + g1 * (b.w * Tn - S1 * inv) + g2 * (c.x * Tn - S2 * inv);
+      const float galpha =
+          s.g0 * (b.z * Tn - s.S0 * inv) + s.g1 * (b.w * Tn - s.S1 * inv) + s.g2 * (c.x * Tn - s.S2 * inv);
       const bool unc = ok && araw <= kAlphaCap;
       const float ge = unc ? -galpha * araw : 0.0f;
       v[0] = -ge * (c.y * dx + c.z * dy);
@@ -295,37 +594,117 @@ __global__ void __launch_bounds__(256) render_bwd_kernel(const float4* __restric
       v[3] = ge * dx * dy;
       v[4] = ge * 0.5f * dy * dy;
       v[5] = unc ? galpha * G : 0.0f;
-      v[6] = ok ? g0 * w : 0.0f;
-      v[7] = ok ? g1 * w : 0.0f;
-      v[8] = ok ? g2 * w : 0.0f;
+      v[6] = ok ? s.g0 * w : 0.0f;
+      v[7] = ok ? s.g1 * w : 0.0f;
+      v[8] = ok ? s.g2 * w : 0.0f;
       if (ok) {
-        S0 += b.z * w;
-        S1 += b.w * w;
-        S2 += c.x * w;
-        T = Tn;
+        s.S0 += b.z * w;
+        s.S1 += b.w * w;
+        s.S2 += c.x * w;
+        s.T = Tn;
       }
       wave_sum9(v);
-      if ((lane & 7) == 0) atomicAdd(&s_acc[lane >> 3][e], v[0]);
-      if (lane == 0) atomicAdd(&s_acc[8][e], v[8]);
+      if ((lane & 7) == 0) atomicAdd(&L.acc[lane >> 3][e], v[0]);
+      if (lane == 0) atomicAdd(&L.acc[8][e], v[8]);
     }
     if (nlo < nhi) {
-      s_a[buf ^ 1][tid] = na; s_b[buf ^ 1][tid] = nb; s_c[buf ^ 1][tid] = ncr; s_id[buf ^ 1][tid] = ng;
+      L.a[buf ^ 1][tid] = na; L.b[buf ^ 1][tid] = nb; L.c[buf ^ 1][tid] = ncr; L.id[buf ^ 1][tid] = ng;
     }
     __syncthreads();
-    // one set of global atomics per (tile, Gaussian)
-    if (tid < hi - lo) {
-      const uint32_t g = s_id[buf][tid];
+    if (tid < hi - blo) {
+      const uint32_t g = L.id[buf][tid];
 #pragma unroll
       for (int k = 0; k < 9; ++k) {
-        const float val = s_acc[k][tid];
+        const float val = L.acc[k][tid];
         if (val != 0.0f) atomicAdd(&gscreen[k * n + g], val);
-        s_acc[k][tid] = 0.0f;
+        L.acc[k][tid] = 0.0f;
       }
     }
     __syncthreads();
-    hi = lo;
+    hi = blo;
     buf ^= 1;
   }
+}
+
+// Every tile's first segment (the whole list for tiles that were not split).
+__global__ void __launch_bounds__(256) render_bwd_kernel(const float4* __restrict__ splat,
+                                                          const uint32_t* __restrict__ vals,
+                                                          const uint32_t* __restrict__ ranges, SplitWs ws,
+                                                          int num_tiles, int tx, int W, int H, float bg0, float bg1,
+                                                          float bg2, int first, const float* __restrict__ T_final,
+                                                          const uint32_t* __restrict__ n_contrib,
+                                                          const float* __restrict__ dL_dimg, int n,
+                                                          float* __restrict__ gscreen) {
+  __shared__ BwdLds L;
+  const int tile = int(ws.order[blockIdx.x]);
+  const int tid = threadIdx.x;
+  const int px = (tile % tx) * kTile + (tid & (kTile - 1));
+  const int py = (tile / tx) * kTile + (tid >> 4);
+  const bool inside = px < W && py < H;
+  const uint32_t start = ranges[tile];
+  PixelBwd s{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0};
+  if (inside) {
+    const int HW = W * H, p = py * W + px;
+    s.g0 = dL_dimg[p];
+    s.g1 = dL_dimg[HW + p];
+    s.g2 = dL_dimg[2 * HW + p];
+    const int32_t slot = ws.slot_of_tile[tile];
+    if (slot >= 0 && ws.stopc[size_t(slot) * 256 + tid] >= 0) {
+      // the pixel's pairs continue past the first segment: start from its end state
+      const float4 b = ws.bnd1[size_t(slot) * 256 + tid];
+      s.T = b.x; s.S0 = b.y; s.S1 = b.z; s.S2 = b.w;
+      s.top = first;
+    } else {
+      s.T = T_final[p];
+      s.S0 = bg0 * s.T; s.S1 = bg1 * s.T; s.S2 = bg2 * s.T;
+      s.top = int(n_contrib[p]);
+    }
+  }
+  bwd_walk(L, splat, vals, start, 0, float(px) + 0.5f, float(py) + 0.5f, s, n, gscreen);
+}
+
+// One block per chunk of a split tile.
+__global__ void __launch_bounds__(256) split_bwd_kernel(const float4* __restrict__ splat,
+                                                         const uint32_t* __restrict__ vals,
+                                                         const uint32_t* __restrict__ ranges, SplitWs ws,
+                                                         int num_tiles, int tx, int W, int H, float bg0, float bg1,
+                                                         float bg2, int first, int chunk,
+                                                         const float* __restrict__ T_final,
+                                                         const uint32_t* __restrict__ n_contrib,
+                                                         const float* __restrict__ dL_dimg, int n,
+                                                         float* __restrict__ gscreen) {
+  __shared__ BwdLds L;
+  const uint32_t item = blockIdx.x;
+  if (item >= ws.counters[1]) return;
+  const uint2 sc = ws.items[item];
+  const uint32_t slot = sc.x, c = sc.y;
+  const int tile = int(ws.slot_tile[slot]);
+  const int tid = threadIdx.x;
+  const int px = (tile % tx) * kTile + (tid & (kTile - 1));
+  const int py = (tile / tx) * kTile + (tid >> 4);
+  const bool inside = px < W && py < H;
+  const uint32_t start = ranges[tile];
+  const int len = int(ranges[num_tiles + tile] - start);
+  const int lo = first + int(c) * chunk, hi = min(lo + chunk, len);
+  const size_t so = size_t(slot) * 256 + tid;
+  PixelBwd s{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, lo};
+  const int32_t stop = ws.stopc[so];
+  if (inside && stop >= int32_t(c)) {
+    const int HW = W * H, p = py * W + px;
+    s.g0 = dL_dimg[p];
+    s.g1 = dL_dimg[HW + p];
+    s.g2 = dL_dimg[2 * HW + p];
+    if (stop == int32_t(c)) {
+      s.T = T_final[p];
+      s.S0 = bg0 * s.T; s.S1 = bg1 * s.T; s.S2 = bg2 * s.T;
+      s.top = int(n_contrib[p]);
+    } else {
+      const float4 b = ws.part4[size_t(item) * 256 + tid];
+      s.T = b.x; s.S0 = b.y; s.S1 = b.z; s.S2 = b.w;
+      s.top = hi;
+    }
+  }
+  bwd_walk(L, splat, vals, start, lo, float(px) + 0.5f, float(py) + 0.5f, s, n, gscreen);
 }
 
 __global__ void zero_f32_kernel(float* __restrict__ p, int64_t count) {
@@ -333,34 +712,66 @@ __global__ void zero_f32_kernel(float* __restrict__ p, int64_t count) {
   if (i < count) p[i] = 0.0f;
 }
 
+int g_first = 2048;
+int g_chunk = 1024;
+
 }  // namespace
 
-size_t render_ws_bytes(int W, int H) { return size_t((W + kTile - 1) / kTile) * ((H + kTile - 1) / kTile) * 4 + 256; }
+int render_split_first() { return g_first; }
+int render_split_chunk() { return g_chunk; }
+
+int32_t set_render_split(int first, int chunk) {
+  if (first < 4 || chunk < 4 || (first & 3) || (chunk & 3) || first > (1 << 24) || chunk > (1 << 24)) return -1;
+  g_first = first;
+  g_chunk = chunk;
+  return 0;
+}
+
+size_t render_ws_bytes(int W, int H, uint32_t pairs) {
+  return carve_bytes(split_dims(W, H, pairs, g_first, g_chunk)) + 256;
+}
 
 hipError_t launch_render_fwd(const gs_proj& proj, const uint32_t* vals, const uint32_t* ranges,
-                             const gs_camera& cam, float* rgb, float* T_final, uint32_t* n_contrib, void* ws,
-                             hipStream_t s) {
+                             const gs_camera& cam, uint32_t pairs, float* rgb, float* T_final,
+                             uint32_t* n_contrib, void* wsp, hipStream_t s) {
   const int tx = tiles_x(cam), ty = tiles_y(cam);
   const int num_tiles = tx * ty;
-  uint32_t* order = static_cast<uint32_t*>(ws);
-  tile_order_kernel<<<1, 1024, 0, s>>>(ranges, num_tiles, order);
-  render_fwd_kernel<<<num_tiles, 256, 0, s>>>(reinterpret_cast<const float4*>(proj.splat), vals, ranges, order,
-                                              num_tiles, tx, cam.width, cam.height, cam.bg[0], cam.bg[1], cam.bg[2],
-                                              rgb, T_final, n_contrib);
+  const SplitDims d = split_dims(cam.width, cam.height, pairs, g_first, g_chunk);
+  const SplitWs ws = carve(wsp, d);
+  const float4* splat = reinterpret_cast<const float4*>(proj.splat);
+  split_init_kernel<<<div_up(num_tiles, 256), 256, 0, s>>>(ws.counters, ws.slot_of_tile, num_tiles);
+  tile_order_kernel<<<1, 1024, 0, s>>>(ranges, num_tiles, ws.order);
+  render_fwd_kernel<<<num_tiles, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, cam.width, cam.height,
+                                              cam.bg[0], cam.bg[1], cam.bg[2], g_first, g_chunk, rgb, T_final,
+                                              n_contrib);
+  if (pairs > uint32_t(g_first)) {
+    const unsigned items = unsigned(d.I), slots = unsigned(d.S);
+    split_chunk_kernel<<<items, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, g_first, g_chunk);
+    split_combine_kernel<<<slots, 256, 0, s>>>(ws);
+    split_rewalk_kernel<<<items, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, g_first, g_chunk);
+    split_finalize_kernel<<<slots, 256, 0, s>>>(ws, tx, cam.width, cam.height, cam.bg[0], cam.bg[1], cam.bg[2], rgb,
+                                                T_final, n_contrib);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_render_bwd(const gs_proj& proj, int n, const uint32_t* vals, const uint32_t* ranges,
-                             const gs_camera& cam, const float* T_final, const uint32_t* n_contrib,
-                             const float* dL_dimg, float* gscreen, void* ws, hipStream_t s) {
+                             const gs_camera& cam, uint32_t pairs, const float* T_final, const uint32_t* n_contrib,
+                             const float* dL_dimg, float* gscreen, void* wsp, hipStream_t s) {
   const int tx = tiles_x(cam), ty = tiles_y(cam);
   const int num_tiles = tx * ty;
-  uint32_t* order = static_cast<uint32_t*>(ws);
+  const SplitDims d = split_dims(cam.width, cam.height, pairs, g_first, g_chunk);
+  const SplitWs ws = carve(wsp, d);
+  const float4* splat = reinterpret_cast<const float4*>(proj.splat);
   if (n > 0) zero_f32_kernel<<<div_up(9 * int64_t(n), 256), 256, 0, s>>>(gscreen, 9 * int64_t(n));
-  tile_order_kernel<<<1, 1024, 0, s>>>(ranges, num_tiles, order);
-  render_bwd_kernel<<<num_tiles, 256, 0, s>>>(reinterpret_cast<const float4*>(proj.splat), vals, ranges, order,
-                                              num_tiles, tx, cam.width, cam.height, cam.bg[0], cam.bg[1], cam.bg[2],
-                                              T_final, n_contrib, dL_dimg, n, gscreen);
+  render_bwd_kernel<<<num_tiles, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, cam.width, cam.height,
+                                              cam.bg[0], cam.bg[1], cam.bg[2], g_first, T_final, n_contrib, dL_dimg,
+                                              n, gscreen);
+  if (pairs > uint32_t(g_first)) {
+    split_bwd_kernel<<<unsigned(d.I), 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, cam.width, cam.height,
+                                                   cam.bg[0], cam.bg[1], cam.bg[2], g_first, g_chunk, T_final,
+                                                   n_contrib, dL_dimg, n, gscreen);
+  }
   return hipGetLastError();
 }
 

@@ -18,9 +18,10 @@ LIB_PATH = os.path.join(_HERE, "libgs.so")
 
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_UNSUPPORTED, GS_ERR_HIP = 0, -1, -2, -3, -4
 GS_WS_PREPROCESS, GS_WS_BIN_SORT, GS_WS_LOSS, GS_WS_RENDER = 0, 1, 2, 3
+GS_TUNE_SPLIT_FIRST, GS_TUNE_SPLIT_CHUNK = 0, 1
 
 EXPORTED = ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
-            "gs_adam_step", "gs_workspace_bytes", "gs_last_error")
+            "gs_adam_step", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning", "gs_last_error")
 
 
 class GsError(RuntimeError):
@@ -51,9 +52,13 @@ def _load():
     P, I64, I32, U32 = C.c_void_p, C.c_int64, C.c_int32, C.c_uint32
     lib.gs_preprocess.argtypes = [P, P, P, P, P, C.c_size_t, P]
     lib.gs_bin_sort.argtypes = [P, I64, P, U32, P, P, U32, P, P, C.c_size_t, P]
-    lib.gs_render_fwd.argtypes = [P, I64, P, P, P, P, P, P, P, C.c_size_t, P]
+    lib.gs_render_fwd.argtypes = [P, I64, P, P, U32, P, P, P, P, P, C.c_size_t, P]
     lib.gs_loss_l1_dssim.argtypes = [P, P, I32, I32, C.c_float, P, P, P, C.c_size_t, P]
-    lib.gs_render_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
+    lib.gs_render_bwd.argtypes = [P, P, P, P, U32, P, P, P, P, P, P, P, C.c_size_t, P]
+    lib.gs_set_tuning.argtypes = [I32, I64]
+    lib.gs_set_tuning.restype = I32
+    lib.gs_get_tuning.argtypes = [I32]
+    lib.gs_get_tuning.restype = I64
     lib.gs_adam_step.argtypes = [P, P, P, P, I64, I32, P, C.c_double, C.c_double, C.c_double, I32, P]
     lib.gs_workspace_bytes.argtypes = [I32, I64, U32, I32, I32]
     lib.gs_workspace_bytes.restype = C.c_size_t
@@ -137,9 +142,9 @@ def gs_bin_sort(proj: Proj, cam: GsCamera, total_pairs, keys, vals, ranges, ws, 
                             _ptr(ranges), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
-def gs_render_fwd(proj: Proj, vals, ranges, cam: GsCamera, rgb, T_final, n_contrib, ws, stream=None):
-    _check(_lib.gs_render_fwd(C.byref(proj.struct), proj.n, _ptr(vals), _ptr(ranges), C.byref(cam), _ptr(rgb),
-                              _ptr(T_final), _ptr(n_contrib), _ptr(ws), ws.numel(), _stream(stream)))
+def gs_render_fwd(proj: Proj, vals, ranges, total_pairs, cam: GsCamera, rgb, T_final, n_contrib, ws, stream=None):
+    _check(_lib.gs_render_fwd(C.byref(proj.struct), proj.n, _ptr(vals), _ptr(ranges), total_pairs, C.byref(cam),
+                              _ptr(rgb), _ptr(T_final), _ptr(n_contrib), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def gs_loss_l1_dssim(img, target, lambda_dssim, loss_out, dL_dimg, ws, stream=None):
@@ -148,11 +153,12 @@ def gs_loss_l1_dssim(img, target, lambda_dssim, loss_out, dL_dimg, ws, stream=No
                                  _ptr(dL_dimg), _ptr(ws), ws.numel(), _stream(stream)))
 
 
-def gs_render_bwd(params, sh_degree, proj: Proj, vals, ranges, cam: GsCamera, T_final, n_contrib, dL_dimg,
+def gs_render_bwd(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam: GsCamera, T_final, n_contrib, dL_dimg,
                   gscreen, gparams, ws, stream=None):
     n = proj.n
     scene = GsScene(n, sh_degree, params.data_ptr() if n else None)
-    _check(_lib.gs_render_bwd(C.byref(scene), C.byref(proj.struct), _ptr(vals), _ptr(ranges), C.byref(cam),
+    _check(_lib.gs_render_bwd(C.byref(scene), C.byref(proj.struct), _ptr(vals), _ptr(ranges), total_pairs,
+                              C.byref(cam),
                               _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimg), _ptr(gscreen), _ptr(gparams),
                               _ptr(ws), ws.numel(), _stream(stream)))
 
@@ -162,6 +168,14 @@ def gs_adam_step(params, grads, m, v, sh_degree, lr, beta1, beta2, eps, step, st
     lr_arr = (C.c_float * 5)(*[float(x) for x in lr])
     _check(_lib.gs_adam_step(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), n, sh_degree, lr_arr, float(beta1),
                              float(beta2), float(eps), int(step), _stream(stream)))
+
+
+def gs_set_tuning(key, value):
+    _check(_lib.gs_set_tuning(key, int(value)))
+
+
+def gs_get_tuning(key):
+    return int(_lib.gs_get_tuning(key))
 
 
 def gs_last_error():

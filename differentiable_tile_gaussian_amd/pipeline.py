@@ -34,7 +34,7 @@ class Pipeline:
         self.T = torch.empty((height, width), dtype=torch.float32, device=dev)
         self.nc = torch.empty((height, width), dtype=torch.int32, device=dev)
         self.ws_loss = gs.workspace(gs.GS_WS_LOSS, W=width, H=height, device=dev)
-        self.ws_render = gs.workspace(gs.GS_WS_RENDER, W=width, H=height, device=dev)
+        self.ws_render = torch.empty(0, dtype=torch.uint8, device=dev)
         self.loss = torch.zeros(3, dtype=torch.float32, device=dev)
         self.dLdI = torch.empty((3, height, width), dtype=torch.float32, device=dev)
         self.gscreen = torch.empty((9, max(self.n, 1)), dtype=torch.float32, device=dev)
@@ -52,17 +52,22 @@ class Pipeline:
         need = gs.gs_workspace_bytes(gs.GS_WS_BIN_SORT, self.n, pairs, self.W, self.H)
         if self.ws_sort.numel() < need:
             self.ws_sort = torch.empty(int(need * 1.25) + 4096, dtype=torch.uint8, device=self.params.device)
+        need = gs.gs_workspace_bytes(gs.GS_WS_RENDER, self.n, pairs, self.W, self.H)
+        if self.ws_render.numel() < need:
+            self.ws_render = torch.empty(int(need * 1.25) + 4096, dtype=torch.uint8, device=self.params.device)
 
     def forward(self, cam: gs.GsCamera):
         self.pairs = gs.gs_preprocess(self.params, self.deg, cam, self.proj, self.ws_pre)
         self._reserve(self.pairs)
         gs.gs_bin_sort(self.proj, cam, self.pairs, self.keys, self.vals, self.ranges, self.ws_sort)
-        gs.gs_render_fwd(self.proj, self.vals, self.ranges, cam, self.rgb, self.T, self.nc, self.ws_render)
+        gs.gs_render_fwd(self.proj, self.vals, self.ranges, self.pairs, cam, self.rgb, self.T, self.nc,
+                         self.ws_render)
         return self.rgb
 
     def backward(self, cam: gs.GsCamera, target: torch.Tensor):
         gs.gs_loss_l1_dssim(self.rgb, target, self.lam, self.loss, self.dLdI, self.ws_loss)
-        gs.gs_render_bwd(self.params, self.deg, self.proj, self.vals, self.ranges, cam, self.T, self.nc, self.dLdI,
+        gs.gs_render_bwd(self.params, self.deg, self.proj, self.vals, self.ranges, self.pairs, cam, self.T, self.nc,
+                         self.dLdI,
                          self.gscreen, self.grads, self.ws_render)
 
     def adam(self):

@@ -124,10 +124,13 @@ int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32
  *   skip if alpha < 1/255; C += T alpha c; T *= 1 - alpha; stop once T < 1e-4.
  * rgb[3][H][W] = C + T bg; T_final[H][W] = T; n_contrib[H][W] = 1 + (index within the tile's
  * range) of the last blended pair, 0 if none ([DR] "The trick": only the final state is kept).
- * ws: gs_workspace_bytes(GS_WS_RENDER, 0, 0, W, H) bytes (the tiles' processing order). */
+ * total_pairs: the pair count of the sort.  ws: gs_workspace_bytes(GS_WS_RENDER, n, total_pairs,
+ * W, H) bytes; it keeps the state that the matching gs_render_bwd reads (the tile order and, for
+ * tiles whose list is walked in parallel chunks, the per-chunk boundary states), so pass the same
+ * ws, unmodified, to that backward. */
 int32_t gs_render_fwd(const gs_proj* proj, int64_t n, const uint32_t* vals, const uint32_t* ranges,
-                      const gs_camera* cam, float* rgb, float* T_final, uint32_t* n_contrib, void* ws,
-                      size_t ws_bytes, void* stream);
+                      uint32_t total_pairs, const gs_camera* cam, float* rgb, float* T_final,
+                      uint32_t* n_contrib, void* ws, size_t ws_bytes, void* stream);
 
 /* Loss (1 - lambda) L1 + lambda (1 - SSIM) and dL/dimg.  [GST] loss slides: L1 mean over
  * 3HW with zero subgradient at zero residual; SSIM with an 11 x 11 Gaussian window of
@@ -150,12 +153,12 @@ int32_t gs_loss_l1_dssim(const float* img, const float* target, int32_t H, int32
  * scale and quaternion, projection off |q|), "Where the position gradient comes from"
  * (mean path and the J(z) covariance path), "Spherical harmonics" (band gradients and the
  * view-direction term), sigmoid.  gparams: [P][n], overwritten (zero for culled Gaussians).
- * proj, vals, ranges, T_final and n_contrib must be those of the matching forward.
- * ws: gs_workspace_bytes(GS_WS_RENDER, 0, 0, W, H) bytes. */
+ * proj, vals, ranges, total_pairs, T_final, n_contrib and ws must be those of the matching
+ * forward (ws as that forward left it). */
 int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t* vals, const uint32_t* ranges,
-                      const gs_camera* cam, const float* T_final, const uint32_t* n_contrib,
-                      const float* dL_dimg, float* gscreen, float* gparams, void* ws, size_t ws_bytes,
-                      void* stream);
+                      uint32_t total_pairs, const gs_camera* cam, const float* T_final,
+                      const uint32_t* n_contrib, const float* dL_dimg, float* gscreen, float* gparams, void* ws,
+                      size_t ws_bytes, void* stream);
 
 /* Adam, [GSG] Adam section; per-group rates [DR] "From a pixel error back to a quaternion".
  *   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
@@ -170,6 +173,15 @@ int32_t gs_adam_step(float* params, const float* grads, float* m, float* v, int6
 /* Workspace sizes, in bytes, for the calls that take one. */
 enum { GS_WS_PREPROCESS = 0, GS_WS_BIN_SORT = 1, GS_WS_LOSS = 2, GS_WS_RENDER = 3 };
 size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H);
+
+/* Tuning of the blend's work split (process-wide; set before sizing workspaces, and not between a
+ * forward and its backward).  Every tile's first GS_TUNE_SPLIT_FIRST pairs are walked by one
+ * block; a tile with pixels still unfinished then has its remaining pairs walked in parallel
+ * chunks of GS_TUNE_SPLIT_CHUNK pairs.  Values: multiples of 4 in [4, 2^24]; defaults 2048, 1024.
+ * The results do not depend on these values beyond rounding. */
+enum { GS_TUNE_SPLIT_FIRST = 0, GS_TUNE_SPLIT_CHUNK = 1 };
+int32_t gs_set_tuning(int32_t key, int64_t value);
+int64_t gs_get_tuning(int32_t key);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* gs_last_error(void);

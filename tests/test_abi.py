@@ -71,10 +71,14 @@ def test_argument_errors_without_gpu(gs):
     # loss with a bad lambda
     assert L.gs_loss_l1_dssim(1, 1, 8, 8, C.c_float(1.5), 1, 1, 1, 1 << 30, None) == gs.GS_ERR_INVALID_ARG
     # negative n
-    assert L.gs_render_fwd(C.byref(proj), -1, None, None, C.byref(cam), 1, 1, 1, None, 0,
+    assert L.gs_render_fwd(C.byref(proj), -1, None, None, 0, C.byref(cam), 1, 1, 1, None, 0,
                            None) == gs.GS_ERR_INVALID_ARG
     # render without its workspace
-    assert L.gs_render_fwd(C.byref(proj), 10, 1, 1, C.byref(cam), 1, 1, 1, None, 0, None) == gs.GS_ERR_CAPACITY
+    assert L.gs_render_fwd(C.byref(proj), 10, 1, 1, 100, C.byref(cam), 1, 1, 1, None, 0, None) == gs.GS_ERR_CAPACITY
+    # tuning values are checked
+    assert L.gs_set_tuning(gs.GS_TUNE_SPLIT_CHUNK, 6) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_set_tuning(77, 1024) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_get_tuning(gs.GS_TUNE_SPLIT_FIRST) == 2048
 
 
 def test_workspace_sizes_grow_with_the_problem(gs):

@@ -79,8 +79,8 @@ def test_backward_small(torch_cuda, oracle, case):
     pl, c = pu.gpu_forward(s.params, deg, cam)
     pl.dLdI.copy_(torch.from_numpy(dLdI))
     from differentiable_tile_gaussian_amd import gs
-    gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, c, pl.T, pl.nc, pl.dLdI, pl.gscreen, pl.grads,
-                     pl.ws_render)
+    gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI, pl.gscreen,
+                     pl.grads, pl.ws_render)
     torch.cuda.synchronize()
     gscreen = pl.gscreen[:, :n].cpu().numpy()
     gparams = pl.grads.cpu().numpy()
@@ -249,3 +249,61 @@ def test_capacity_error_writes_nothing(torch_cuda):
     assert e.value.status == gs.GS_ERR_CAPACITY
     torch.cuda.synchronize()
     assert int(keys.min()) == 7 and int(ranges.min()) == 7
+
+
+# ------------------------------------------------------------- split path
+# Small split sizes force every long tile through the chunked forward (exact first
+# segment, speculative chunks, combine, re-walk of the stopping chunk) and the
+# chunk-parallel backward; results must still match the sequential oracle.
+def _deep_case():
+    s = scenes.random_scene(501, 2500, 1, spread=2.5, logscale_mean=math.log(0.12), logscale_std=0.4,
+                            logit_mean=0.5, logit_std=1.0)
+    cam = scenes.identity_camera(72, 56, 60.0)
+    return s, cam
+
+
+@pytest.fixture
+def split_tuning(torch_cuda):
+    from differentiable_tile_gaussian_amd import gs
+    old = (gs.gs_get_tuning(gs.GS_TUNE_SPLIT_FIRST), gs.gs_get_tuning(gs.GS_TUNE_SPLIT_CHUNK))
+
+    def set_(first, chunk):
+        gs.gs_set_tuning(gs.GS_TUNE_SPLIT_FIRST, first)
+        gs.gs_set_tuning(gs.GS_TUNE_SPLIT_CHUNK, chunk)
+
+    yield set_
+    set_(*old)
+
+
+@pytest.mark.parametrize("tune", [(16, 8), (64, 32), (12, 4), (256, 128)])
+@pytest.mark.parametrize("which", ["deep", "small3", "small2"])
+def test_split_path_parity(torch_cuda, oracle, split_tuning, tune, which):
+    torch = torch_cuda
+    from differentiable_tile_gaussian_amd import gs
+    split_tuning(*tune)
+    if which == "deep":
+        s, cam = _deep_case()
+    else:
+        s, cam = _scene_and_camera(*_small_cases()[int(which[-1])])
+    deg = s.sh_degree
+    print(f"split {which} first={tune[0]} chunk={tune[1]}", flush=True)
+    dLdI = (np.random.default_rng(11).standard_normal((3, cam.height, cam.width)) * 1e-3).astype(np.float32)
+    o = _oracle_all(oracle, s.params, deg, cam, dLdI)
+    lens = (o["ranges"][1].astype(np.int64) - o["ranges"][0])
+    if lens.max() <= tune[0] + tune[1]:
+        pytest.skip("no tile list long enough for this split size")
+    pl, c = pu.gpu_forward(s.params, deg, cam)
+    n_low = pu.check_render(pu.render_to_numpy(pl), o["fwd"])
+    pl.dLdI.copy_(torch.from_numpy(dLdI))
+    gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI, pl.gscreen,
+                     pl.grads, pl.ws_render)
+    torch.cuda.synchronize()
+    keep = o["gmargin"] >= pu.MARGIN
+    gscreen = pl.gscreen[:, :s.n].cpu().numpy()
+    for k, name in enumerate(["u", "v", "A", "B", "C", "opacity", "r", "g", "b"]):
+        pu.check_grad(gscreen[k], o["gscreen"][k], keep, name=name)
+    g = pl.grads.cpu().numpy()
+    for name, sl in pu.grad_groups(deg).items():
+        pu.check_grad(g[sl], o["gparams"][sl], keep, name=name)
+    stopped = float((o["fwd"]["T"] < 1e-4).mean())
+    print(f"  low-margin px {n_low}, excluded G {int((~keep).sum())}, saturated px {stopped:.2f}", flush=True)
