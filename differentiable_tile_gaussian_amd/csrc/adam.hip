@@ -3,60 +3,84 @@
 // learning rates, [DR] "From a pixel error back to a quaternion").
 //   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
 //   theta -= lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
-// Streaming: 16 bytes read and 12 written per parameter; one block row per plane so the
-// group's rate is uniform per block; float4 accesses when the plane length allows.
+// Streaming, HBM-bound: 16 bytes read and 12 written per parameter.  One block row
+// per plane (the group's rate is uniform per block); each thread keeps four
+// independent 16-byte accesses of each of the four streams in flight, and the
+// accesses are non-temporal (every byte is touched once per step).
 #include "gs_internal.h"
 
 namespace gsk {
 namespace {
 
+typedef float f4 __attribute__((ext_vector_type(4)));
+
 struct Rates { float lr[5]; };
+struct Hyper { float b1, b2, omb1, omb2, eps, inv_bc1, inv_bc2; };
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
 
 __device__ inline int plane_group(int plane) {
   return plane < 3 ? 0 : plane < 6 ? 1 : plane < 10 ? 2 : plane == 10 ? 3 : 4;
 }
 
-struct Hyper { float b1, b2, omb1, omb2, eps, inv_bc1, inv_bc2; };
-
-__device__ inline float adam_one(float& th, float g, float& m, float& v, float lr, const Hyper& h) {
+__device__ inline float adam_one(float th, float g, float& m, float& v, float lr, const Hyper& h) {
   m = h.b1 * m + h.omb1 * g;
   v = h.b2 * v + h.omb2 * g * g;
-  const float inv_bc1 = h.inv_bc1, inv_bc2 = h.inv_bc2, eps = h.eps;
-  const float mh = m * inv_bc1, vh = v * inv_bc2;
-  th = th - lr * mh / (sqrtf(vh) + eps);
-  return th;
+  const float mh = m * h.inv_bc1, vh = v * h.inv_bc2;
+  return th - lr * mh / (sqrtf(vh) + h.eps);
 }
 
-__global__ void __launch_bounds__(256) adam_vec4_kernel(float4* __restrict__ params, const float4* __restrict__ grads,
-                                                         float4* __restrict__ m, float4* __restrict__ v, int n4,
-                                                         Rates rates, Hyper h) {
+__global__ void __launch_bounds__(kThreads) adam_vec4_kernel(f4* __restrict__ params, const f4* __restrict__ grads,
+                                                              f4* __restrict__ m, f4* __restrict__ v, int n4,
+                                                              Rates rates, Hyper h) {
   const int plane = blockIdx.y;
   const float lr = rates.lr[plane_group(plane)];
   const size_t base = size_t(plane) * n4;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x) {
-    const size_t k = base + i;
-    float4 th = params[k], gg = grads[k], mm = m[k], vv = v[k];
-    adam_one(th.x, gg.x, mm.x, vv.x, lr, h);
-    adam_one(th.y, gg.y, mm.y, vv.y, lr, h);
-    adam_one(th.z, gg.z, mm.z, vv.z, lr, h);
-    adam_one(th.w, gg.w, mm.w, vv.w, lr, h);
-    params[k] = th;
-    m[k] = mm;
-    v[k] = vv;
+  const int i0 = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  f4 th[kUnroll], gg[kUnroll], mm[kUnroll], vv[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int i = i0 + u * kThreads;
+    if (i < n4) {
+      const size_t k = base + i;
+      th[u] = __builtin_nontemporal_load(&params[k]);
+      gg[u] = __builtin_nontemporal_load(&grads[k]);
+      mm[u] = __builtin_nontemporal_load(&m[k]);
+      vv[u] = __builtin_nontemporal_load(&v[k]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int i = i0 + u * kThreads;
+    if (i < n4) {
+      const size_t k = base + i;
+      f4 t = th[u], mu = mm[u], vu = vv[u];
+      float mx = mu.x, my = mu.y, mz = mu.z, mw = mu.w, vx = vu.x, vy = vu.y, vz = vu.z, vw = vu.w;
+      t.x = adam_one(t.x, gg[u].x, mx, vx, lr, h);
+      t.y = adam_one(t.y, gg[u].y, my, vy, lr, h);
+      t.z = adam_one(t.z, gg[u].z, mz, vz, lr, h);
+      t.w = adam_one(t.w, gg[u].w, mw, vw, lr, h);
+      mu = f4{mx, my, mz, mw};
+      vu = f4{vx, vy, vz, vw};
+      __builtin_nontemporal_store(t, &params[k]);
+      __builtin_nontemporal_store(mu, &m[k]);
+      __builtin_nontemporal_store(vu, &v[k]);
+    }
   }
 }
 
-__global__ void __launch_bounds__(256) adam_scalar_kernel(float* __restrict__ params, const float* __restrict__ grads,
-                                                           float* __restrict__ m, float* __restrict__ v, int n,
-                                                           Rates rates, Hyper h) {
+__global__ void __launch_bounds__(kThreads) adam_scalar_kernel(float* __restrict__ params,
+                                                                const float* __restrict__ grads,
+                                                                float* __restrict__ m, float* __restrict__ v, int n,
+                                                                Rates rates, Hyper h) {
   const int plane = blockIdx.y;
   const float lr = rates.lr[plane_group(plane)];
   const size_t base = size_t(plane) * n;
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
     const size_t k = base + i;
-    float th = params[k], mm = m[k], vv = v[k];
-    adam_one(th, grads[k], mm, vv, lr, h);
-    params[k] = th;
+    float mm = m[k], vv = v[k];
+    params[k] = adam_one(params[k], grads[k], mm, vv, lr, h);
     m[k] = mm;
     v[k] = vv;
   }
@@ -77,13 +101,12 @@ hipError_t launch_adam(float* params, const float* grads, float* m, float* v, in
                        (reinterpret_cast<uintptr_t>(v) % 16) == 0;
   if (aligned) {
     const int n4 = n / 4;
-    const unsigned bx = div_up(n4, 256) < 64u ? div_up(n4, 256) : 64u;
-    adam_vec4_kernel<<<dim3(bx, P), 256, 0, s>>>(reinterpret_cast<float4*>(params),
-                                                 reinterpret_cast<const float4*>(grads),
-                                                 reinterpret_cast<float4*>(m), reinterpret_cast<float4*>(v), n4, r, h);
+    adam_vec4_kernel<<<dim3(div_up(n4, kThreads * kUnroll), P), kThreads, 0, s>>>(
+        reinterpret_cast<f4*>(params), reinterpret_cast<const f4*>(grads), reinterpret_cast<f4*>(m),
+        reinterpret_cast<f4*>(v), n4, r, h);
   } else {
     const unsigned bx = div_up(n, 256) < 256u ? div_up(n, 256) : 256u;
-    adam_scalar_kernel<<<dim3(bx, P), 256, 0, s>>>(params, grads, m, v, n, r, h);
+    adam_scalar_kernel<<<dim3(bx, P), kThreads, 0, s>>>(params, grads, m, v, n, r, h);
   }
   return hipGetLastError();
 }

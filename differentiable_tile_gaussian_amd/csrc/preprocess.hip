@@ -267,30 +267,28 @@ __global__ void __launch_bounds__(256) preprocess_fwd_kernel(const float* __rest
   }
 }
 
-// Backward chain for one Gaussian.  gscreen planes: 0 u, 1 v, 2 A, 3 B, 4 C, 5 opacity,
-// 6-8 colour.  [GSG] "From a pixel's blame to the oval's shape and place" (sigmoid),
-// "The covariance chain" (dV = -K G K, dSigma = T^T H T, dT = 2 H T Sigma, dM = 2 dSigma M,
-// scale and quaternion, projection off |q|), "Where the position gradient comes from",
-// "Spherical harmonics" (dL/dsh_k = dRGB Y_k and the view-direction term); [GST] Jacobian slide.
+// Backward chain, split in two kernels so each keeps few registers (and many waves
+// in flight on a streaming, HBM-bound pass).  gscreen planes: 0 u, 1 v, 2 A, 3 B,
+// 4 C, 5 opacity, 6-8 colour.
+//
+// Colour part ([GSG] "Spherical harmonics": dL/dsh_k = dRGB Y_k, and the
+// view-direction term; the clamp at zero passes no gradient): writes the DC and
+// band gradients and, at degree > 0, the direction term of the mean gradient.
 template <int DEG>
-__global__ void __launch_bounds__(256) preprocess_bwd_kernel(const float* __restrict__ params, int n,
-                                                              gs_camera cam, const uint32_t* __restrict__ tiles,
-                                                              const float* __restrict__ gscreen,
-                                                              float* __restrict__ gparams) {
+__global__ void __launch_bounds__(256) chain_colour_kernel(const float* __restrict__ params, int n, gs_camera cam,
+                                                            const uint32_t* __restrict__ tiles,
+                                                            const float* __restrict__ gscreen,
+                                                            float* __restrict__ gparams) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   constexpr int K = (DEG + 1) * (DEG + 1) - 1;
   constexpr int P = 11 + 3 * (K + 1);
-  Proj g;
-  if (tiles[i] == 0u || !project_geometry(params, n, i, cam, g)) {
-    for (int pl = 0; pl < P; ++pl) gparams[pl * n + i] = 0.0f;
+  if (tiles[i] == 0u) {
+    for (int pl = 11; pl < P; ++pl) gparams[pl * n + i] = 0.0f;
+    if (K > 0)
+      for (int c = 0; c < 3; ++c) gparams[c * n + i] = 0.0f;
     return;
   }
-  const float gu = gscreen[i], gv = gscreen[n + i], gA = gscreen[2 * n + i], gB = gscreen[3 * n + i],
-              gC = gscreen[4 * n + i], go = gscreen[5 * n + i];
-  // opacity logit through the sigmoid
-  gparams[10 * n + i] = go * g.o * (1.0f - g.o);
-  // colour: the clamp at zero passes no gradient; DC, bands, then the view direction
   float Y[16];
   float dir[3] = {0.f, 0.f, 0.f};
   float dlen = 1.0f;
@@ -305,7 +303,6 @@ __global__ void __launch_bounds__(256) preprocess_bwd_kernel(const float* __rest
     gc[ch] = raw[ch] < 0.0f ? 0.0f : gscreen[(6 + ch) * n + i];
     gparams[(11 + ch) * n + i] = gc[ch];
   }
-  float gm[3] = {0.f, 0.f, 0.f};
   if (K > 0) {
     float wk[16];
     for (int k = 1; k <= K; ++k) {
@@ -320,8 +317,34 @@ __global__ void __launch_bounds__(256) preprocess_bwd_kernel(const float* __rest
     float gdir[3] = {0.f, 0.f, 0.f};
     sh_grad_dot(dir[0], dir[1], dir[2], wk, K, gdir);
     const float dd = dir[0] * gdir[0] + dir[1] * gdir[1] + dir[2] * gdir[2];
-    for (int a = 0; a < 3; ++a) gm[a] += (gdir[a] - dir[a] * dd) / dlen;
+    for (int a = 0; a < 3; ++a) gparams[a * n + i] = (gdir[a] - dir[a] * dd) / dlen;
   }
+}
+
+// Geometry part ([GSG] "From a pixel's blame to the oval's shape and place" (sigmoid),
+// "The covariance chain" (dV = -K G K, dSigma = T^T H T, dT = 2 H T Sigma,
+// dM = 2 dSigma M, scale and quaternion, projection off |q|), "Where the position
+// gradient comes from"; [GST] Jacobian slide): writes the mean (adding the colour
+// part's direction term at degree > 0), log-scale, quaternion and logit gradients.
+template <int DEG>
+__global__ void __launch_bounds__(256) chain_geometry_kernel(const float* __restrict__ params, int n, gs_camera cam,
+                                                              const uint32_t* __restrict__ tiles,
+                                                              const float* __restrict__ gscreen,
+                                                              float* __restrict__ gparams) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  Proj g;
+  if (tiles[i] == 0u || !project_geometry(params, n, i, cam, g)) {
+    for (int pl = 0; pl < 11; ++pl) gparams[pl * n + i] = 0.0f;
+    return;
+  }
+  const float gu = gscreen[i], gv = gscreen[n + i], gA = gscreen[2 * n + i], gB = gscreen[3 * n + i],
+              gC = gscreen[4 * n + i], go = gscreen[5 * n + i];
+  // opacity logit through the sigmoid
+  gparams[10 * n + i] = go * g.o * (1.0f - g.o);
+  float gm[3] = {0.f, 0.f, 0.f};
+  if (DEG > 0)
+    for (int a = 0; a < 3; ++a) gm[a] = gparams[a * n + i];
   // conic -> dilated covariance: dV' = -K Gk K with Gk = [[gA, gB/2], [gB/2, gC]]
   const float hB = 0.5f * gB;
   const float kg00 = g.A * gA + g.B * hB, kg01 = g.A * hB + g.B * gC;
@@ -356,10 +379,10 @@ __global__ void __launch_bounds__(256) preprocess_bwd_kernel(const float* __rest
   const float dJ12 = dT1[0] * cam.R[6] + dT1[1] * cam.R[7] + dT1[2] * cam.R[8];
   const float pz = g.p[2], pz2 = pz * pz, pz3 = pz2 * pz;
   const float fx = cam.fx, fy = cam.fy;
-  float dp0 = dJ02 * (-fx / pz2) + gu * fx / pz;
-  float dp1 = dJ12 * (-fy / pz2) + gv * fy / pz;
-  float dp2 = dJ00 * (-fx / pz2) + dJ02 * (2.0f * fx * g.p[0] / pz3) + dJ11 * (-fy / pz2) +
-              dJ12 * (2.0f * fy * g.p[1] / pz3) - gu * fx * g.p[0] / pz2 - gv * fy * g.p[1] / pz2;
+  const float dp0 = dJ02 * (-fx / pz2) + gu * fx / pz;
+  const float dp1 = dJ12 * (-fy / pz2) + gv * fy / pz;
+  const float dp2 = dJ00 * (-fx / pz2) + dJ02 * (2.0f * fx * g.p[0] / pz3) + dJ11 * (-fy / pz2) +
+                    dJ12 * (2.0f * fy * g.p[1] / pz3) - gu * fx * g.p[0] / pz2 - gv * fy * g.p[1] / pz2;
   // p = W m + t: dm = W^T dp
   for (int c = 0; c < 3; ++c) gm[c] += cam.R[c] * dp0 + cam.R[3 + c] * dp1 + cam.R[6 + c] * dp2;
   for (int c = 0; c < 3; ++c) gparams[c * n + i] = gm[c];
@@ -411,10 +434,22 @@ hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_c
   if (n == 0) return hipSuccess;
   const dim3 grid(div_up(n, 256)), block(256);
   switch (deg) {
-    case 0: preprocess_bwd_kernel<0><<<grid, block, 0, s>>>(params, n, cam, tiles, gscreen, gparams); break;
-    case 1: preprocess_bwd_kernel<1><<<grid, block, 0, s>>>(params, n, cam, tiles, gscreen, gparams); break;
-    case 2: preprocess_bwd_kernel<2><<<grid, block, 0, s>>>(params, n, cam, tiles, gscreen, gparams); break;
-    default: preprocess_bwd_kernel<3><<<grid, block, 0, s>>>(params, n, cam, tiles, gscreen, gparams); break;
+    case 0:
+      chain_colour_kernel<0><<<grid, block, 0, s>>>(params, n, cam, tiles, gscreen, gparams);
+      chain_geometry_kernel<0><<<grid, block, 0, s>>>(params, n, cam, tiles, gscreen, gparams);
+      break;
+    case 1:
+      chain_colour_kernel<1><<<grid, block, 0, s>>>(params, n, cam, tiles, gscreen, gparams);
+      chain_geometry_kernel<1><<<grid, block, 0, s>>>(params, n, cam, tiles, gscreen, gparams);
+      break;
+    case 2:
+      chain_colour_kernel<2><<<grid, block, 0, s>>>(params, n, cam, tiles, gscreen, gparams);
+      chain_geometry_kernel<2><<<grid, block, 0, s>>>(params, n, cam, tiles, gscreen, gparams);
+      break;
+    default:
+      chain_colour_kernel<3><<<grid, block, 0, s>>>(params, n, cam, tiles, gscreen, gparams);
+      chain_geometry_kernel<3><<<grid, block, 0, s>>>(params, n, cam, tiles, gscreen, gparams);
+      break;
   }
   return hipGetLastError();
 }
