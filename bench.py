@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--workload", type=int, default=WORKLOAD_CFG, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-report", action="store_true", help="also print per-stage times to stderr")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, copy a 1 GiB buffer three times (a plain copy of known size, the "
+                         "reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -105,6 +108,25 @@ def count_evals(pl, torch):
     fwd = torch.where(stopped, nc, length).sum().item()
     bwd = nc.sum().item()
     return int(fwd), int(bwd)
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, if
+    the kernel's source is unchanged since the counters were taken; otherwise None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "pmc_traffic_train_step_6m_1080p.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        parts = line.split()
+        if len(parts) >= 2 and parts[0] == "traffic" and parts[1] == kernel:
+            kv = dict(p.split("=", 1) for p in parts[2:])
+            src = os.path.join(ROOT, kv["source"])
+            if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["sha256"]:
+                return None
+            return (float(kv["fetch_kib"]) * float(kv["fetch_scale"]) +
+                    float(kv["write_kib"]) * float(kv["write_scale"])) * 1024.0
+    return None
 
 
 def cpu_baseline(wl):
@@ -198,12 +220,19 @@ def main():
         "stage_ms": {k: round(float(stage[:, i].mean()), 4) for i, k in enumerate(StageTimer.NAMES)},
         "roofline": {"kernel": "adam_vec4_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": adam_bytes},
+                     "traffic": measured_traffic("adam_vec4_kernel"), "bytes_per_launch": adam_bytes},
         "setup_s": round(setup_s, 2),
     }
     if not args.no_cpu_baseline and args.workload == WORKLOAD_CFG:
         cb = cpu_baseline(wl)
         out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    if args.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes"] = int(src.numel() * 4)
     if args.stage_report:
         print(json.dumps({"stage_ms_all": stage.round(4).tolist()}), file=sys.stderr)
     print(json.dumps(out))
