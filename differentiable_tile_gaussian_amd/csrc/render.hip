@@ -469,41 +469,58 @@ __global__ void __launch_bounds__(256) split_finalize_kernel(SplitWs ws, int tx,
 }
 
 // ----------------------------------------------------------- backward walk
+// Lane exchanges without LDS: gfx950's v_permlane32_swap / v_permlane16_swap swap
+// half-waves / adjacent rows between two registers, DPP moves within a row.
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+constexpr int kRowRor8 = 0x128;       // lane i <- lane i ^ 8 within a 16-lane row
+constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7 - i within each 8 lanes
+constexpr int kQuadXor2 = 0x4e;       // quad_perm [2, 3, 0, 1]
+constexpr int kQuadXor1 = 0xb1;       // quad_perm [1, 0, 3, 2]
+
+// a from lanes 0-31 and b from lanes 32-63 summed pairwise: lanes 0-31 get
+// a(l) + a(l+32), lanes 32-63 get b(l-32) + b(l).
+__device__ inline float fold32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Same between adjacent 16-lane rows: even rows get a(l) + a(l+16), odd rows b(l-16) + b(l).
+__device__ inline float fold16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum 9 per-lane values over the 64 lanes of a wave.  Values 0..7 use a transposed
 // butterfly (each exchange halves the values a lane carries), value 8 a plain one.
 // On return lane l holds the total of value (l >> 3) in v[0] and every lane holds
-// the total of value 8 in v[8].
+// the total of value 8 in v[8].  All lanes of the wave must be active.
 __device__ inline void wave_sum9(float* v) {
   const int lane = __lane_id();
-  {
-    const bool hi = lane & 32;
+  // distance 32: lanes 0-31 keep values 0-3, lanes 32-63 values 4-7
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float send = hi ? v[k] : v[k + 4];
-      const float keep = hi ? v[k + 4] : v[k];
-      v[k] = keep + __shfl_xor(send, 32, 64);
-    }
-  }
-  {
-    const bool hi = lane & 16;
+  for (int k = 0; k < 4; ++k) v[k] = fold32(v[k], v[k + 4]);
+  v[8] = fold32(v[8], v[8]);
+  // distance 16: even rows keep the first of each pair, odd rows the second
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const float send = hi ? v[k] : v[k + 2];
-      const float keep = hi ? v[k + 2] : v[k];
-      v[k] = keep + __shfl_xor(send, 16, 64);
-    }
-  }
+  for (int k = 0; k < 2; ++k) v[k] = fold16(v[k], v[k + 2]);
+  v[8] = fold16(v[8], v[8]);
+  // distance 8 within a row
   {
     const bool hi = lane & 8;
     const float send = hi ? v[0] : v[1];
     const float keep = hi ? v[1] : v[0];
-    v[0] = keep + __shfl_xor(send, 8, 64);
+    v[0] = keep + dpp<kRowRor8>(send);
   }
-  v[0] += __shfl_xor(v[0], 4, 64);
-  v[0] += __shfl_xor(v[0], 2, 64);
-  v[0] += __shfl_xor(v[0], 1, 64);
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v[8] += __shfl_xor(v[8], d, 64);
+  v[8] += dpp<kRowRor8>(v[8]);
+  // the last three lane bits: plain sums over 8 lanes
+  v[0] += dpp<kRowHalfMirror>(v[0]);
+  v[8] += dpp<kRowHalfMirror>(v[8]);
+  v[0] += dpp<kQuadXor2>(v[0]);
+  v[8] += dpp<kQuadXor2>(v[8]);
+  v[0] += dpp<kQuadXor1>(v[0]);
+  v[8] += dpp<kQuadXor1>(v[8]);
 }
 
 struct BwdLds {
