@@ -1,8 +1,12 @@
 """Benchmark: full training steps of the 6M-Gaussian, SH-degree-3, 1920x1080 workload.
 
 One step = preprocess + bin/sort + forward blend + L1/D-SSIM loss + backward
-blend and chain + Adam over every parameter, for one of 100 seeded orbit
+blend and chain with Adam applied to every parameter, for one of 100 seeded orbit
 cameras (in order).  Prints one JSON line.
+
+The roofline object describes the kernel that takes the most time per step (found
+from a warm-up with every launch timed); during the timed steps the library brackets
+that kernel's launches with HIP events on its own stream.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 5] [--no-cpu-baseline]
 
@@ -23,8 +27,28 @@ sys.path.insert(0, ROOT)
 
 WORKLOAD_CFG = 5
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
-# Algorithmic bytes of Adam per parameter: read theta, g, m, v; write theta, m, v (fp32).
-ADAM_BYTES_PER_PARAM = 28
+
+
+def kernel_bytes(kernel, n, deg, P):
+    """Algorithmic HBM bytes of one launch of the streaming kernels (fp32 everywhere).
+
+    adam_vec4       per parameter: read theta, g, m, v; write theta, m, v            28 B
+    chain_colour    (Adam fused) per Gaussian: tile count 4, mean 12, colour gradient 12,
+                    read + write theta/m/v of the 3(K+1) colour planes 24 each, write
+                    the view-direction partial 12
+    chain_geometry  (Adam fused) per Gaussian: tile count 4, screen gradients 9 x 4,
+                    read + write theta/m/v of the 11 geometry planes 24 each
+    preprocess_fwd  per Gaussian: read all P planes, write splat 48, depth 4, rect 8,
+                    tile count 4
+    """
+    K1 = (deg + 1) ** 2
+    table = {
+        "adam_vec4": 28 * P * n,
+        "chain_colour": (4 + 12 + 12 + 24 * 3 * K1 + 12) * n,
+        "chain_geometry": (4 + 36 + 24 * 11) * n,
+        "preprocess_fwd": (4 * P + 48 + 4 + 8 + 4) * n,
+    }
+    return table.get(kernel)
 
 
 def parse():
@@ -56,7 +80,7 @@ def make_targets(wl, cams, Pipeline, torch):
 class StageTimer:
     """HIP events on the stream the library launches on (torch's current stream)."""
 
-    NAMES = ("preprocess", "bin_sort", "render_fwd", "loss", "render_bwd", "adam")
+    NAMES = ("preprocess", "bin_sort", "render_fwd", "loss", "render_bwd_adam")
 
     def __init__(self, torch, steps):
         self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.NAMES) + 1)] for _ in range(steps)]
@@ -84,12 +108,10 @@ def run_steps(pl, cams, targets, first, count, timer=None, gs=None):
         if timer: timer.mark(s, 3)
         gs.gs_loss_l1_dssim(pl.rgb, tgt, pl.lam, pl.loss, pl.dLdI, pl.ws_loss)
         if timer: timer.mark(s, 4)
-        gs.gs_render_bwd(pl.params, pl.deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI,
-                         pl.gscreen,
-                         pl.grads, pl.ws_render)
+        pl.t += 1
+        gs.gs_render_bwd_adam(pl.params, pl.deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI,
+                              pl.gscreen, pl.m, pl.v, pl.lr, pl.betas[0], pl.betas[1], pl.eps, pl.t, pl.ws_render)
         if timer: timer.mark(s, 5)
-        pl.adam()
-        if timer: timer.mark(s, 6)
 
 
 def count_evals(pl, torch):
@@ -173,13 +195,22 @@ def main():
     pl = Pipeline(params, deg, cam0.width, cam0.height)
     setup_s = time.perf_counter() - t_setup
 
+    # warm-up with every kernel launch timed: per-kernel time per step, and the dominant kernel
+    gs.gs_profile_enable(True)
     run_steps(pl, cams, targets, 0, args.warmup, gs=gs)
     torch.cuda.synchronize()
+    warm = gs.gs_profile_query()
+    kernel_ms = {k: ms / max(args.warmup, 1) for k, (cnt, ms) in warm.items()}
+    dominant = max(kernel_ms, key=kernel_ms.get)
+    # timed steps: only the dominant kernel's launches carry events
+    gs.gs_profile_enable(True, dominant)
     timer = StageTimer(torch, args.steps)
     t0 = time.perf_counter()
     run_steps(pl, cams, targets, args.warmup, args.steps, timer=timer, gs=gs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    live = gs.gs_profile_query()[dominant]
+    gs.gs_profile_enable(False)
     stage = timer.per_stage_ms()
     ms_per_step = wall * 1000.0 / args.steps
 
@@ -196,10 +227,19 @@ def main():
     del pl2, params2
     t_fb = (stage[:, 2].sum() + stage[:, 4].sum()) / 1000.0
 
-    # roofline of the dominant kernel: Adam, one launch per step over all P*n parameters
-    adam_ms = float(stage[:, 5].mean())
-    adam_bytes = ADAM_BYTES_PER_PARAM * P * n
-    achieved = adam_bytes / (adam_ms / 1000.0) / 1e9
+    # roofline of the dominant kernel from its live launch times
+    dom_launches, dom_ms = live
+    dom_avg_ms = dom_ms / dom_launches
+    dom_bytes = kernel_bytes(dominant, n, deg, P)
+    if dom_bytes is not None:
+        achieved = dom_bytes / (dom_avg_ms / 1000.0) / 1e9
+        roof = {"kernel": dominant + "_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dominant + "_kernel"), "bytes_per_launch": dom_bytes,
+                "avg_launch_ms": round(dom_avg_ms, 4), "launches": dom_launches}
+    else:
+        roof = {"kernel": dominant + "_kernel", "bound": None, "achieved": None, "peak": None, "unit": None,
+                "frac": None, "traffic": None, "avg_launch_ms": round(dom_avg_ms, 4), "launches": dom_launches}
     out = {
         "metric": "fwd+bwd raster iterations/sec and Gaussian-pixel evals/s; % of HBM/VALU roofline",
         "value": round(1000.0 / ms_per_step, 3),
@@ -214,13 +254,12 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "gaussians": n, "sh_degree": deg, "image": [cam0.width, cam0.height],
-                   "cameras": len(cams), "step": "preprocess+sort+fwd+loss+bwd+adam", "parallelism": "none"},
+                   "cameras": len(cams), "step": "preprocess+sort+fwd+loss+bwd+chain+adam (fused)", "parallelism": "none"},
         "evals_per_s": round((ev_f + ev_b) / t_fb, 1),
         "evals_per_step": {"fwd": ev_f // args.steps, "bwd": ev_b // args.steps},
         "stage_ms": {k: round(float(stage[:, i].mean()), 4) for i, k in enumerate(StageTimer.NAMES)},
-        "roofline": {"kernel": "adam_vec4_kernel", "bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("adam_vec4_kernel"), "bytes_per_launch": adam_bytes},
+        "kernel_ms_per_step": {k: round(v, 4) for k, v in sorted(kernel_ms.items(), key=lambda kv: -kv[1])},
+        "roofline": roof,
         "setup_s": round(setup_s, 2),
     }
     if not args.no_cpu_baseline and args.workload == WORKLOAD_CFG:

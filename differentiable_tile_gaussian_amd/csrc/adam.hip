@@ -7,35 +7,23 @@
 // per plane (the group's rate is uniform per block); each thread keeps four
 // independent 16-byte accesses of each of the four streams in flight, and the
 // accesses are non-temporal (every byte is touched once per step).
-#include "gs_internal.h"
+#include "adam_math.h"
+#include "profile.h"
 
 namespace gsk {
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-struct Rates { float lr[5]; };
-struct Hyper { float b1, b2, omb1, omb2, eps, inv_bc1, inv_bc2; };
-
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 
-__device__ inline int plane_group(int plane) {
-  return plane < 3 ? 0 : plane < 6 ? 1 : plane < 10 ? 2 : plane == 10 ? 3 : 4;
-}
-
-__device__ inline float adam_one(float th, float g, float& m, float& v, float lr, const Hyper& h) {
-  m = h.b1 * m + h.omb1 * g;
-  v = h.b2 * v + h.omb2 * g * g;
-  const float mh = m * h.inv_bc1, vh = v * h.inv_bc2;
-  return th - lr * mh / (sqrtf(vh) + h.eps);
-}
 
 __global__ void __launch_bounds__(kThreads) adam_vec4_kernel(f4* __restrict__ params, const f4* __restrict__ grads,
                                                               f4* __restrict__ m, f4* __restrict__ v, int n4,
-                                                              Rates rates, Hyper h) {
+                                                              const AdamArgs h) {
   const int plane = blockIdx.y;
-  const float lr = rates.lr[plane_group(plane)];
+  const float lr = h.lr[adam_group(plane)];
   const size_t base = size_t(plane) * n4;
   const int i0 = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
   f4 th[kUnroll], gg[kUnroll], mm[kUnroll], vv[kUnroll];
@@ -57,10 +45,10 @@ __global__ void __launch_bounds__(kThreads) adam_vec4_kernel(f4* __restrict__ pa
       const size_t k = base + i;
       f4 t = th[u], mu = mm[u], vu = vv[u];
       float mx = mu.x, my = mu.y, mz = mu.z, mw = mu.w, vx = vu.x, vy = vu.y, vz = vu.z, vw = vu.w;
-      t.x = adam_one(t.x, gg[u].x, mx, vx, lr, h);
-      t.y = adam_one(t.y, gg[u].y, my, vy, lr, h);
-      t.z = adam_one(t.z, gg[u].z, mz, vz, lr, h);
-      t.w = adam_one(t.w, gg[u].w, mw, vw, lr, h);
+      t.x = adam_update(t.x, gg[u].x, mx, vx, lr, h);
+      t.y = adam_update(t.y, gg[u].y, my, vy, lr, h);
+      t.z = adam_update(t.z, gg[u].z, mz, vz, lr, h);
+      t.w = adam_update(t.w, gg[u].w, mw, vw, lr, h);
       mu = f4{mx, my, mz, mw};
       vu = f4{vx, vy, vz, vw};
       __builtin_nontemporal_store(t, &params[k]);
@@ -73,14 +61,14 @@ __global__ void __launch_bounds__(kThreads) adam_vec4_kernel(f4* __restrict__ pa
 __global__ void __launch_bounds__(kThreads) adam_scalar_kernel(float* __restrict__ params,
                                                                 const float* __restrict__ grads,
                                                                 float* __restrict__ m, float* __restrict__ v, int n,
-                                                                Rates rates, Hyper h) {
+                                                                const AdamArgs h) {
   const int plane = blockIdx.y;
-  const float lr = rates.lr[plane_group(plane)];
+  const float lr = h.lr[adam_group(plane)];
   const size_t base = size_t(plane) * n;
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
     const size_t k = base + i;
     float mm = m[k], vv = v[k];
-    params[k] = adam_one(params[k], grads[k], mm, vv, lr, h);
+    params[k] = adam_update(params[k], grads[k], mm, vv, lr, h);
     m[k] = mm;
     v[k] = vv;
   }
@@ -92,21 +80,27 @@ hipError_t launch_adam(float* params, const float* grads, float* m, float* v, in
                        float b1, float b2, float omb1, float omb2, float eps, float inv_bc1, float inv_bc2,
                        hipStream_t s) {
   if (n == 0) return hipSuccess;
-  const Hyper h{b1, b2, omb1, omb2, eps, inv_bc1, inv_bc2};
-  Rates r;
-  for (int k = 0; k < 5; ++k) r.lr[k] = lr[k];
+  AdamArgs h;
+  for (int k = 0; k < 5; ++k) h.lr[k] = lr[k];
+  h.b1 = b1; h.b2 = b2; h.omb1 = omb1; h.omb2 = omb2; h.eps = eps; h.inv_bc1 = inv_bc1; h.inv_bc2 = inv_bc2;
   const int P = num_planes(deg);
   const bool aligned = (n % 4) == 0 && (reinterpret_cast<uintptr_t>(params) % 16) == 0 &&
                        (reinterpret_cast<uintptr_t>(grads) % 16) == 0 && (reinterpret_cast<uintptr_t>(m) % 16) == 0 &&
                        (reinterpret_cast<uintptr_t>(v) % 16) == 0;
   if (aligned) {
     const int n4 = n / 4;
-    adam_vec4_kernel<<<dim3(div_up(n4, kThreads * kUnroll), P), kThreads, 0, s>>>(
-        reinterpret_cast<f4*>(params), reinterpret_cast<const f4*>(grads), reinterpret_cast<f4*>(m),
-        reinterpret_cast<f4*>(v), n4, r, h);
+    {
+      GSK_PROF("adam_vec4", s);
+      adam_vec4_kernel<<<dim3(div_up(n4, kThreads * kUnroll), P), kThreads, 0, s>>>(
+          reinterpret_cast<f4*>(params), reinterpret_cast<const f4*>(grads), reinterpret_cast<f4*>(m),
+          reinterpret_cast<f4*>(v), n4, h);
+    }
   } else {
     const unsigned bx = div_up(n, 256) < 256u ? div_up(n, 256) : 256u;
-    adam_scalar_kernel<<<dim3(bx, P), kThreads, 0, s>>>(params, grads, m, v, n, r, h);
+    {
+      GSK_PROF("adam_scalar", s);
+      adam_scalar_kernel<<<dim3(bx, P), kThreads, 0, s>>>(params, grads, m, v, n, h);
+    }
   }
   return hipGetLastError();
 }

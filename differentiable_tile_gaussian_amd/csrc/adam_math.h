@@ -1,0 +1,39 @@
+// Adam update of one parameter, shared by the standalone Adam kernel (adam.hip)
+// and the backward chain with Adam fused in (chain.hip).  [GSG] Adam section of
+// "How a computer rebuilds a real place out of soft colored dots called Gaussian
+// Splats"; per-group rates, [DR] "From a pixel error back to a quaternion".
+//   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
+//   theta -= lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
+// 1 - beta and the bias corrections are formed in fp64 on the host.
+#pragma once
+
+#include "gs_internal.h"
+
+namespace gsk {
+
+struct AdamArgs {
+  float lr[5];          // means, log-scales, quaternion, opacity, colour
+  float b1, b2, omb1, omb2, eps, inv_bc1, inv_bc2;
+};
+
+__device__ inline int adam_group(int plane) {
+  return plane < 3 ? 0 : plane < 6 ? 1 : plane < 10 ? 2 : plane == 10 ? 3 : 4;
+}
+
+__device__ inline float adam_update(float th, float g, float& m, float& v, float lr, const AdamArgs& a) {
+  m = a.b1 * m + a.omb1 * g;
+  v = a.b2 * v + a.omb2 * g * g;
+  const float mh = m * a.inv_bc1, vh = v * a.inv_bc2;
+  return th - lr * mh / (sqrtf(vh) + a.eps);
+}
+
+// One parameter of plane `pl`, Gaussian i: update in place from gradient g.
+__device__ inline void adam_apply(float* __restrict__ params, float* __restrict__ m, float* __restrict__ v,
+                                  size_t k, int pl, float g, const AdamArgs& a) {
+  float mm = m[k], vv = v[k];
+  params[k] = adam_update(params[k], g, mm, vv, a.lr[adam_group(pl)], a);
+  m[k] = mm;
+  v[k] = vv;
+}
+
+}  // namespace gsk

@@ -1,0 +1,243 @@
+// Backward chain per Gaussian: screen-space gradients -> parameter gradients, and
+// optionally Adam applied on the spot (without writing the gradient to memory).
+//
+// Two kernels keep register use low on this streaming, HBM-bound pass:
+//   colour part    one wave per colour channel for 64 Gaussians: the DC and band
+//                  gradients of that channel ([GSG] "Spherical harmonics": dL/dsh_k =
+//                  dRGB Y_k; the clamp at zero passes no gradient) and its share of the
+//                  view-direction term, summed over the three channels in LDS;
+//   geometry part  one thread per Gaussian: mean (projected-mean path, J(z) covariance
+//                  path, plus the direction term), log-scales, quaternion and opacity
+//                  logit ([GSG] "From a pixel's blame to the oval's shape and place",
+//                  "The covariance chain", "Where the position gradient comes from";
+//                  [GST] Jacobian slide).
+// gscreen planes: 0 u, 1 v, 2 A, 3 B, 4 C, 5 opacity, 6-8 colour.  The direction term
+// passes from the first kernel to the second through the mean planes of gparams, or,
+// with Adam fused, through gscreen planes 6-8 once the colour part has read them.
+//
+// Compiled without floating-point contraction, like the forward projection, so the
+// recomputed projection is the forward's bit for bit.
+#include "adam_math.h"
+#include "projection.h"
+#include "profile.h"
+
+namespace gsk {
+namespace {
+
+using namespace proj;
+
+template <int DEG, bool ADAM>
+__global__ void __launch_bounds__(192) chain_colour_kernel(float* __restrict__ params, int n, gs_camera cam,
+                                                            const uint32_t* __restrict__ tiles,
+                                                            float* __restrict__ gscreen, float* __restrict__ gparams,
+                                                            float* __restrict__ m, float* __restrict__ v,
+                                                            AdamArgs a) {
+  constexpr int K = (DEG + 1) * (DEG + 1) - 1;
+  __shared__ float s_gdir[3][3][64];
+  const int lane = threadIdx.x & 63, ch = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + lane;
+  const bool valid = i < n;
+  const bool vis = valid && tiles[i] != 0u;
+  float dir[3] = {0.f, 0.f, 0.f};
+  float dlen = 1.0f;
+  float Y[16];
+  if (K > 0 && vis) {
+    dlen = view_dir(params, n, i, cam, dir);
+    sh_eval(dir[0], dir[1], dir[2], Y);
+  }
+  float coef[K + 1];
+  float gc = 0.0f;
+  if (valid) {
+    coef[0] = params[(11 + ch) * n + i];
+#pragma unroll
+    for (int k = 1; k <= K; ++k) coef[k] = params[(14 + 3 * (k - 1) + ch) * n + i];
+  }
+  if (vis) {
+    float raw = coef[0];
+#pragma unroll
+    for (int k = 1; k <= K; ++k) raw = raw + coef[k] * Y[k];
+    gc = raw < 0.0f ? 0.0f : gscreen[(6 + ch) * n + i];
+  }
+  if (K > 0) {
+    float gd[3] = {0.f, 0.f, 0.f};
+    if (vis) {
+      float wk[16];
+#pragma unroll
+      for (int k = 1; k <= K; ++k) wk[k] = gc * coef[k];
+      sh_grad_dot(dir[0], dir[1], dir[2], wk, K, gd);
+    }
+#pragma unroll
+    for (int c = 0; c < 3; ++c) s_gdir[ch][c][lane] = gd[c];
+  }
+  if (valid) {
+#pragma unroll
+    for (int k = 0; k <= K; ++k) {
+      const int pl = k == 0 ? 11 + ch : 14 + 3 * (k - 1) + ch;
+      const float g = k == 0 ? gc : (vis ? gc * Y[k] : 0.0f);
+      const size_t o = size_t(pl) * n + i;
+      if (ADAM) {
+        float mm = m[o], vv = v[o];
+        params[o] = adam_update(coef[k], g, mm, vv, a.lr[4], a);
+        m[o] = mm;
+        v[o] = vv;
+      } else {
+        gparams[o] = g;
+      }
+    }
+  }
+  if (K > 0) {
+    __syncthreads();
+    if (ch == 0 && valid) {
+      float gt[3], out[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 3; ++c) gt[c] = s_gdir[0][c][lane] + s_gdir[1][c][lane] + s_gdir[2][c][lane];
+      if (vis) {
+        const float dd = dir[0] * gt[0] + dir[1] * gt[1] + dir[2] * gt[2];
+#pragma unroll
+        for (int c = 0; c < 3; ++c) out[c] = (gt[c] - dir[c] * dd) / dlen;
+      }
+      float* dst = ADAM ? gscreen + size_t(6) * n : gparams;
+#pragma unroll
+      for (int c = 0; c < 3; ++c) dst[size_t(c) * n + i] = out[c];
+    }
+  }
+}
+
+template <int DEG, bool ADAM>
+__global__ void __launch_bounds__(256) chain_geometry_kernel(float* __restrict__ params, int n, gs_camera cam,
+                                                              const uint32_t* __restrict__ tiles,
+                                                              const float* __restrict__ gscreen,
+                                                              float* __restrict__ gparams, float* __restrict__ m,
+                                                              float* __restrict__ v, AdamArgs a) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float gp[11];
+#pragma unroll
+  for (int k = 0; k < 11; ++k) gp[k] = 0.0f;
+  if (DEG > 0) {
+    const float* src = ADAM ? gscreen + size_t(6) * n : gparams;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) gp[c] = src[size_t(c) * n + i];
+  }
+  Proj g;
+  if (tiles[i] != 0u && project_geometry(params, n, i, cam, g)) {
+    const float gu = gscreen[i], gv = gscreen[n + i], gA = gscreen[2 * n + i], gB = gscreen[3 * n + i],
+                gC = gscreen[4 * n + i], go = gscreen[5 * n + i];
+    // opacity logit through the sigmoid
+    gp[10] = go * g.o * (1.0f - g.o);
+    // conic -> dilated covariance: dV' = -K Gk K with Gk = [[gA, gB/2], [gB/2, gC]]
+    const float hB = 0.5f * gB;
+    const float kg00 = g.A * gA + g.B * hB, kg01 = g.A * hB + g.B * gC;
+    const float kg10 = g.B * gA + g.C * hB, kg11 = g.B * hB + g.C * gC;
+    const float p00 = kg00 * g.A + kg01 * g.B, p01 = kg00 * g.B + kg01 * g.C;
+    const float p10 = kg10 * g.A + kg11 * g.B, p11 = kg10 * g.B + kg11 * g.C;
+    const float gV00 = -p00, gV01 = -(p01 + p10), gV11 = -p11;
+    // V = T Sigma T^T: H = [[gV00, gV01/2], [gV01/2, gV11]]
+    const float h00 = gV00, h01 = 0.5f * gV01, h11 = gV11;
+    // U = H T (rows u0, u1)
+    float u0[3], u1[3];
+    for (int k = 0; k < 3; ++k) {
+      u0[k] = h00 * g.t0[k] + h01 * g.t1[k];
+      u1[k] = h01 * g.t0[k] + h11 * g.t1[k];
+    }
+    // dSigma = T^T H T = t0 u0^T + t1 u1^T (symmetric)
+    float dS[3][3];
+    for (int r = 0; r < 3; ++r)
+      for (int c = 0; c < 3; ++c) dS[r][c] = g.t0[r] * u0[c] + g.t1[r] * u1[c];
+    // dT = 2 H T Sigma = 2 U Sigma
+    const float* S = g.Sig;
+    const float Sf[3][3] = {{S[0], S[1], S[2]}, {S[1], S[3], S[4]}, {S[2], S[4], S[5]}};
+    float dT0[3], dT1[3];
+    for (int c = 0; c < 3; ++c) {
+      dT0[c] = 2.0f * (u0[0] * Sf[0][c] + u0[1] * Sf[1][c] + u0[2] * Sf[2][c]);
+      dT1[c] = 2.0f * (u1[0] * Sf[0][c] + u1[1] * Sf[1][c] + u1[2] * Sf[2][c]);
+    }
+    // T = J W: dJ = dT W^T; only J00, J02, J11, J12 depend on the position
+    const float dJ00 = dT0[0] * cam.R[0] + dT0[1] * cam.R[1] + dT0[2] * cam.R[2];
+    const float dJ02 = dT0[0] * cam.R[6] + dT0[1] * cam.R[7] + dT0[2] * cam.R[8];
+    const float dJ11 = dT1[0] * cam.R[3] + dT1[1] * cam.R[4] + dT1[2] * cam.R[5];
+    const float dJ12 = dT1[0] * cam.R[6] + dT1[1] * cam.R[7] + dT1[2] * cam.R[8];
+    const float pz = g.p[2], pz2 = pz * pz, pz3 = pz2 * pz;
+    const float fx = cam.fx, fy = cam.fy;
+    const float dp0 = dJ02 * (-fx / pz2) + gu * fx / pz;
+    const float dp1 = dJ12 * (-fy / pz2) + gv * fy / pz;
+    const float dp2 = dJ00 * (-fx / pz2) + dJ02 * (2.0f * fx * g.p[0] / pz3) + dJ11 * (-fy / pz2) +
+                      dJ12 * (2.0f * fy * g.p[1] / pz3) - gu * fx * g.p[0] / pz2 - gv * fy * g.p[1] / pz2;
+    // p = W m + t: dm = W^T dp
+    for (int c = 0; c < 3; ++c) gp[c] += cam.R[c] * dp0 + cam.R[3 + c] * dp1 + cam.R[6 + c] * dp2;
+    // Sigma = M M^T: dM = 2 dSigma M
+    float dM[3][3];
+    for (int r = 0; r < 3; ++r)
+      for (int c = 0; c < 3; ++c)
+        dM[r][c] = 2.0f * (dS[r][0] * g.M[c] + dS[r][1] * g.M[3 + c] + dS[r][2] * g.M[6 + c]);
+    // M = Rq diag(s): d log s_j = s_j sum_r dM_rj Rq_rj
+    for (int j = 0; j < 3; ++j)
+      gp[3 + j] = (dM[0][j] * g.Rq[j] + dM[1][j] * g.Rq[3 + j] + dM[2][j] * g.Rq[6 + j]) * g.s[j];
+    // dRq = dM diag(s), then the derivative of the unit-quaternion rotation matrix
+    float dR[3][3];
+    for (int r = 0; r < 3; ++r)
+      for (int c = 0; c < 3; ++c) dR[r][c] = dM[r][c] * g.s[c];
+    const float w = g.q[0], x = g.q[1], y = g.q[2], z = g.q[3];
+    float gq[4];
+    gq[0] = 2.0f * (-z * dR[0][1] + y * dR[0][2] + z * dR[1][0] - x * dR[1][2] - y * dR[2][0] + x * dR[2][1]);
+    gq[1] = 2.0f * (y * dR[0][1] + z * dR[0][2] + y * dR[1][0] - 2.0f * x * dR[1][1] - w * dR[1][2] +
+                    z * dR[2][0] + w * dR[2][1] - 2.0f * x * dR[2][2]);
+    gq[2] = 2.0f * (-2.0f * y * dR[0][0] + x * dR[0][1] + w * dR[0][2] + x * dR[1][0] + z * dR[1][2] -
+                    w * dR[2][0] + z * dR[2][1] - 2.0f * y * dR[2][2]);
+    gq[3] = 2.0f * (-2.0f * z * dR[0][0] - w * dR[0][1] + x * dR[0][2] + w * dR[1][0] - 2.0f * z * dR[1][1] +
+                    y * dR[1][2] + x * dR[2][0] + y * dR[2][1]);
+    const float qd = (w * gq[0] + x * gq[1]) + (y * gq[2] + z * gq[3]);
+    for (int k = 0; k < 4; ++k) gp[6 + k] = (gq[k] - g.q[k] * qd) / g.ql;
+  }
+#pragma unroll
+  for (int pl = 0; pl < 11; ++pl) {
+    const size_t o = size_t(pl) * n + i;
+    if (ADAM)
+      adam_apply(params, m, v, o, pl, gp[pl], a);
+    else
+      gparams[o] = gp[pl];
+  }
+}
+
+template <int DEG, bool ADAM>
+void launch_chain_deg(float* params, int n, const gs_camera& cam, const uint32_t* tiles, float* gscreen,
+                      float* gparams, float* m, float* v, const AdamArgs& a, hipStream_t s) {
+  {
+    GSK_PROF("chain_colour", s);
+    chain_colour_kernel<DEG, ADAM><<<div_up(n, 64), 192, 0, s>>>(params, n, cam, tiles, gscreen, gparams, m, v, a);
+  }
+  {
+    GSK_PROF("chain_geometry", s);
+    chain_geometry_kernel<DEG, ADAM><<<div_up(n, 256), 256, 0, s>>>(params, n, cam, tiles, gscreen, gparams, m, v, a);
+  }
+}
+
+template <bool ADAM>
+void launch_chain_mode(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles, float* gscreen,
+                       float* gparams, float* m, float* v, const AdamArgs& a, hipStream_t s) {
+  switch (deg) {
+    case 0: launch_chain_deg<0, ADAM>(params, n, cam, tiles, gscreen, gparams, m, v, a, s); break;
+    case 1: launch_chain_deg<1, ADAM>(params, n, cam, tiles, gscreen, gparams, m, v, a, s); break;
+    case 2: launch_chain_deg<2, ADAM>(params, n, cam, tiles, gscreen, gparams, m, v, a, s); break;
+    default: launch_chain_deg<3, ADAM>(params, n, cam, tiles, gscreen, gparams, m, v, a, s); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_camera& cam,
+                                 const uint32_t* tiles, float* gscreen, float* gparams, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  launch_chain_mode<false>(const_cast<float*>(params), n, deg, cam, tiles, gscreen, gparams, nullptr, nullptr,
+                           AdamArgs{}, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_chain_adam(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
+                             float* gscreen, float* m, float* v, const AdamArgs& a, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  launch_chain_mode<true>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, s);
+  return hipGetLastError();
+}
+
+}  // namespace gsk

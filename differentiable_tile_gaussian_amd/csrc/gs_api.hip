@@ -4,7 +4,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include "adam_math.h"
 #include "gs_internal.h"
+#include "profile.h"
 
 namespace {
 
@@ -69,6 +71,22 @@ int32_t gs_set_tuning(int32_t key, int64_t value) {
     case GS_TUNE_SPLIT_CHUNK: gsk::set_render_split(gsk::render_split_first(), int(value)); return GS_OK;
     default: return fail(GS_ERR_INVALID_ARG, "unknown tuning key %d", key);
   }
+}
+
+int32_t gs_profile_enable(int32_t on, const char* only) {
+  g_err[0] = 0;
+  gsk::profile_enable(on != 0, only);
+  return GS_OK;
+}
+
+int32_t gs_profile_query(int32_t max_names, char* names, int64_t* launches, double* total_ms) {
+  g_err[0] = 0;
+  if (max_names < 0) return fail(GS_ERR_INVALID_ARG, "max_names must be >= 0");
+  if (max_names > 0 && (!names || !launches || !total_ms)) return fail(GS_ERR_INVALID_ARG, "null output buffer");
+  int32_t written = 0;
+  const hipError_t e = gsk::profile_query(max_names, names, launches, total_ms, &written);
+  if (e != hipSuccess) return hip_fail(e, "gs_profile_query");
+  return written;
 }
 
 int64_t gs_get_tuning(int32_t key) {
@@ -191,6 +209,59 @@ int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t
   if (e != hipSuccess) return hip_fail(e, "render_bwd");
   e = gsk::launch_preprocess_bwd(scene->params, n, scene->sh_degree, *cam, proj->tiles, gscreen, gparams, s);
   if (e != hipSuccess) return hip_fail(e, "preprocess_bwd");
+  return GS_OK;
+}
+
+static int32_t check_adam(int64_t n, int32_t sh_degree, const float* lr, double beta1, double beta2, double eps,
+                          int32_t step) {
+  if (n < 0 || n >= (int64_t(1) << 31)) return fail(GS_ERR_INVALID_ARG, "n out of range");
+  if (sh_degree < 0 || sh_degree > 3) return fail(GS_ERR_UNSUPPORTED, "SH degree must be 0..3");
+  if (!lr) return fail(GS_ERR_INVALID_ARG, "lr is null");
+  if (n * gsk::num_planes(sh_degree) >= (int64_t(1) << 31))
+    return fail(GS_ERR_UNSUPPORTED, "n * planes must stay below 2^31");
+  if (step < 1) return fail(GS_ERR_INVALID_ARG, "step must be >= 1");
+  if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps >= 0.0))
+    return fail(GS_ERR_INVALID_ARG, "bad Adam hyper-parameters");
+  return GS_OK;
+}
+
+static gsk::AdamArgs adam_args(const float* lr, double beta1, double beta2, double eps, int32_t step) {
+  gsk::AdamArgs a;
+  for (int k = 0; k < 5; ++k) a.lr[k] = lr[k];
+  a.b1 = float(beta1);
+  a.b2 = float(beta2);
+  a.omb1 = float(1.0 - beta1);
+  a.omb2 = float(1.0 - beta2);
+  a.eps = float(eps);
+  a.inv_bc1 = float(1.0 / (1.0 - pow(beta1, double(step))));
+  a.inv_bc2 = float(1.0 / (1.0 - pow(beta2, double(step))));
+  return a;
+}
+
+int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs_proj* proj, const uint32_t* vals,
+                           const uint32_t* ranges, uint32_t total_pairs, const gs_camera* cam,
+                           const float* T_final, const uint32_t* n_contrib, const float* dL_dimg, float* gscreen,
+                           float* m, float* v, const float* lr, double beta1, double beta2, double eps,
+                           int32_t step, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int32_t st;
+  const gs_scene scene{n, sh_degree, params};
+  if ((st = check_scene(&scene)) != GS_OK) return st;
+  if ((st = check_adam(n, sh_degree, lr, beta1, beta2, eps, step)) != GS_OK) return st;
+  if ((st = check_camera(cam)) != GS_OK) return st;
+  if ((st = check_proj(proj, n, false)) != GS_OK) return st;
+  if (!ranges || !T_final || !n_contrib || !dL_dimg) return fail(GS_ERR_INVALID_ARG, "a render input is null");
+  if (n > 0 && (!gscreen || !m || !v)) return fail(GS_ERR_INVALID_ARG, "gscreen, m or v is null");
+  if (total_pairs > 0 && !vals) return fail(GS_ERR_INVALID_ARG, "vals is null");
+  const size_t need = gs_workspace_bytes(GS_WS_RENDER, n, total_pairs, cam->width, cam->height);
+  if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "render workspace needs %zu bytes", need);
+  hipStream_t s = as_stream(stream);
+  hipError_t e = gsk::launch_render_bwd(*proj, int(n), vals, ranges, *cam, total_pairs, T_final, n_contrib,
+                                        dL_dimg, gscreen, ws, s);
+  if (e != hipSuccess) return hip_fail(e, "render_bwd");
+  e = gsk::launch_chain_adam(params, int(n), sh_degree, *cam, proj->tiles, gscreen, m, v,
+                             adam_args(lr, beta1, beta2, eps, step), s);
+  if (e != hipSuccess) return hip_fail(e, "chain_adam");
   return GS_OK;
 }
 

@@ -20,8 +20,13 @@ inline unsigned div_up(int64_t a, int64_t b) { return unsigned((a + b - 1) / b);
 // ---- preprocess.hip
 hipError_t launch_preprocess_fwd(const float* params, int n, int deg, const gs_camera& cam, const gs_proj& out,
                                  hipStream_t s);
+
+// ---- chain.hip (gscreen planes 6-8 are read; with Adam they are then overwritten)
+struct AdamArgs;
 hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_camera& cam,
-                                 const uint32_t* tiles, const float* gscreen, float* gparams, hipStream_t s);
+                                 const uint32_t* tiles, float* gscreen, float* gparams, hipStream_t s);
+hipError_t launch_chain_adam(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
+                             float* gscreen, float* m, float* v, const AdamArgs& a, hipStream_t s);
 
 // ---- scan.hip: exclusive prefix sum of n u32 values into out[0..n], out[n] = total.
 // The total is also written as u64 to *total64 (device) so that overflow of 32 bits is seen.

@@ -17,6 +17,7 @@
 #include <math.h>
 
 #include "gs_internal.h"
+#include "profile.h"
 
 namespace gsk {
 namespace {
@@ -227,10 +228,19 @@ hipError_t launch_loss(const float* img, const float* target, int H, int W, floa
   float* cmap = reinterpret_cast<float*>(p); p += align256(NE * 4);
   float* partial = reinterpret_cast<float*>(p);
   const dim3 grid(div_up(W, kTW), div_up(H, kTH), 3);
-  ssim_fwd_kernel<<<grid, 256, 0, s>>>(img, target, H, W, win, amap, bmap, cmap, partial);
-  ssim_bwd_kernel<<<grid, 256, 0, s>>>(img, target, H, W, win, lambda, amap, bmap, cmap, grad);
+  {
+    GSK_PROF("ssim_fwd", s);
+    ssim_fwd_kernel<<<grid, 256, 0, s>>>(img, target, H, W, win, amap, bmap, cmap, partial);
+  }
+  {
+    GSK_PROF("ssim_bwd", s);
+    ssim_bwd_kernel<<<grid, 256, 0, s>>>(img, target, H, W, win, lambda, amap, bmap, cmap, grad);
+  }
   const int nb = int(grid.x * grid.y * grid.z);
-  loss_finalize_kernel<<<1, 256, 0, s>>>(partial, nb, 1.0 / double(NE), lambda, loss_out);
+  {
+    GSK_PROF("loss_finalize", s);
+    loss_finalize_kernel<<<1, 256, 0, s>>>(partial, nb, 1.0 / double(NE), lambda, loss_out);
+  }
   return hipGetLastError();
 }
 

@@ -1,0 +1,199 @@
+// Projection of one Gaussian and its spherical-harmonic colour: the device
+// functions shared by the forward projection (preprocess.hip) and the backward
+// chain (chain.hip).  Both translation units are compiled without floating-point
+// contraction, so the chain recomputes exactly the values the forward produced.
+//
+// Pages (titles as they appear on the pages):
+//   [DR]  "Differentiable rasterisation";  [GST] Gaussian splatting training study deck;
+//   [GSG] "How a computer rebuilds a real place out of soft colored dots called Gaussian Splats".
+#pragma once
+
+#include "gs_internal.h"
+
+namespace gsk {
+namespace proj {
+
+
+// Real spherical harmonics, Condon-Shortley phase (the sign convention of the
+// degree-1 and degree-2 patterns printed in [GSG] "Spherical harmonics").
+// Constants: sqrt((2l+1)/(4 pi) (l-|m|)!/(l+|m|)!) (x sqrt 2 for m != 0) times the
+// leading factor of the associated Legendre polynomial written in x, y, z.
+constexpr float kSH1 = 0.488602511902919920f;   // band 1
+constexpr float kSH2xy = 1.09254843059207907f;  // 2xy, yz, xz terms of band 2
+constexpr float kSH2z = 0.315391565252520050f;  // 2z^2 - x^2 - y^2
+constexpr float kSH2xx = 0.546274215296039535f; // x^2 - y^2
+constexpr float kSH3a = 0.590043589926643510f;  // y(3x^2-y^2), x(x^2-3y^2)
+constexpr float kSH3b = 2.89061144264055405f;   // xyz
+constexpr float kSH3c = 0.457045799464465737f;  // y(4z^2-x^2-y^2), x(4z^2-x^2-y^2)
+constexpr float kSH3d = 0.373176332590115391f;  // z(2z^2-3x^2-3y^2)
+constexpr float kSH3e = 1.44530572132027735f;   // z(x^2-y^2)
+
+// Basis values Y[1..15] at unit direction (x, y, z); Y[0] is not used.
+__device__ inline void sh_eval(float x, float y, float z, float* Y) {
+  const float xx = x * x, yy = y * y, zz = z * z;
+  Y[1] = -kSH1 * y;
+  Y[2] = kSH1 * z;
+  Y[3] = -kSH1 * x;
+  Y[4] = kSH2xy * x * y;
+  Y[5] = -kSH2xy * y * z;
+  Y[6] = kSH2z * (2.0f * zz - xx - yy);
+  Y[7] = -kSH2xy * x * z;
+  Y[8] = kSH2xx * (xx - yy);
+  Y[9] = -kSH3a * y * (3.0f * xx - yy);
+  Y[10] = kSH3b * x * y * z;
+  Y[11] = -kSH3c * y * (4.0f * zz - xx - yy);
+  Y[12] = kSH3d * z * (2.0f * zz - 3.0f * xx - 3.0f * yy);
+  Y[13] = -kSH3c * x * (4.0f * zz - xx - yy);
+  Y[14] = kSH3e * z * (xx - yy);
+  Y[15] = -kSH3a * x * (xx - 3.0f * yy);
+}
+
+// g . dY/d(x, y, z) for a per-basis weight vector w[1..K] (K = active bands), accumulated
+// into out[3]: the derivative of sum_k w_k Y_k(x, y, z) as a polynomial in x, y, z.
+__device__ inline void sh_grad_dot(float x, float y, float z, const float* w, int K, float* out) {
+  const float xx = x * x, yy = y * y, zz = z * z;
+  float gx = 0.f, gy = 0.f, gz = 0.f;
+  if (K >= 3) {
+    gy += -kSH1 * w[1];
+    gz += kSH1 * w[2];
+    gx += -kSH1 * w[3];
+  }
+  if (K >= 8) {
+    gx += kSH2xy * y * w[4];          gy += kSH2xy * x * w[4];
+    gy += -kSH2xy * z * w[5];         gz += -kSH2xy * y * w[5];
+    gx += -2.0f * kSH2z * x * w[6];   gy += -2.0f * kSH2z * y * w[6];   gz += 4.0f * kSH2z * z * w[6];
+    gx += -kSH2xy * z * w[7];         gz += -kSH2xy * x * w[7];
+    gx += 2.0f * kSH2xx * x * w[8];   gy += -2.0f * kSH2xx * y * w[8];
+  }
+  if (K >= 15) {
+    gx += -kSH3a * 6.0f * x * y * w[9];
+    gy += -kSH3a * (3.0f * xx - 3.0f * yy) * w[9];
+    gx += kSH3b * y * z * w[10];  gy += kSH3b * x * z * w[10];  gz += kSH3b * x * y * w[10];
+    gx += -kSH3c * (-2.0f * x * y) * w[11];
+    gy += -kSH3c * (4.0f * zz - xx - 3.0f * yy) * w[11];
+    gz += -kSH3c * 8.0f * y * z * w[11];
+    gx += kSH3d * (-6.0f * x * z) * w[12];
+    gy += kSH3d * (-6.0f * y * z) * w[12];
+    gz += kSH3d * (6.0f * zz - 3.0f * xx - 3.0f * yy) * w[12];
+    gx += -kSH3c * (4.0f * zz - 3.0f * xx - yy) * w[13];
+    gy += -kSH3c * (-2.0f * x * y) * w[13];
+    gz += -kSH3c * 8.0f * x * z * w[13];
+    gx += kSH3e * 2.0f * x * z * w[14];  gy += -kSH3e * 2.0f * y * z * w[14];  gz += kSH3e * (xx - yy) * w[14];
+    gx += -kSH3a * (3.0f * xx - 3.0f * yy) * w[15];
+    gy += -kSH3a * (-6.0f * x * y) * w[15];
+  }
+  out[0] += gx;
+  out[1] += gy;
+  out[2] += gz;
+}
+
+// Intermediate quantities of the projection of one Gaussian.
+struct Proj {
+  float p[3];            // camera-space centre
+  float xz, yz, u, v;
+  float s[3];            // scales
+  float ql, q[4];        // |q| and the normalised quaternion
+  float Rq[9];           // rotation, row-major
+  float M[9];            // Rq diag(s)
+  float Sig[6];          // 00 01 02 11 12 22
+  float t0[3], t1[3];    // rows of T = J W
+  float a, b, c, det;    // dilated screen covariance
+  float A, B, C;         // conic
+  float o;
+};
+
+// Geometry of one Gaussian ([GST] parameter and Jacobian slides; [DR] "Forward";
+// [GSG] "Flattening a 3D blob into a 2D oval").  Returns false when culled (behind the
+// near plane, zero quaternion, non-positive determinant).
+__device__ inline bool project_geometry(const float* __restrict__ params, int n, int i, const gs_camera& cam,
+                                        Proj& g) {
+  const float mx = params[i], my = params[n + i], mz = params[2 * n + i];
+  for (int r = 0; r < 3; ++r)
+    g.p[r] = ((cam.R[3 * r] * mx + cam.R[3 * r + 1] * my) + cam.R[3 * r + 2] * mz) + cam.t[r];
+  if (!(g.p[2] > cam.znear)) return false;
+  g.xz = g.p[0] / g.p[2];
+  g.yz = g.p[1] / g.p[2];
+  g.u = cam.fx * g.xz + cam.cx;
+  g.v = cam.fy * g.yz + cam.cy;
+  for (int k = 0; k < 3; ++k) g.s[k] = float(exp(double(params[(3 + k) * n + i])));
+  const float qw = params[6 * n + i], qx = params[7 * n + i], qy = params[8 * n + i], qz = params[9 * n + i];
+  const float n2 = ((qw * qw + qx * qx) + qy * qy) + qz * qz;
+  if (!(n2 > 0.0f)) return false;
+  g.ql = sqrtf(n2);
+  g.q[0] = qw / g.ql; g.q[1] = qx / g.ql; g.q[2] = qy / g.ql; g.q[3] = qz / g.ql;
+  const float w = g.q[0], x = g.q[1], y = g.q[2], z = g.q[3];
+  g.Rq[0] = 1.0f - 2.0f * (y * y + z * z);
+  g.Rq[1] = 2.0f * (x * y - w * z);
+  g.Rq[2] = 2.0f * (x * z + w * y);
+  g.Rq[3] = 2.0f * (x * y + w * z);
+  g.Rq[4] = 1.0f - 2.0f * (x * x + z * z);
+  g.Rq[5] = 2.0f * (y * z - w * x);
+  g.Rq[6] = 2.0f * (x * z - w * y);
+  g.Rq[7] = 2.0f * (y * z + w * x);
+  g.Rq[8] = 1.0f - 2.0f * (x * x + y * y);
+  for (int r = 0; r < 3; ++r)
+    for (int k = 0; k < 3; ++k) g.M[3 * r + k] = g.Rq[3 * r + k] * g.s[k];
+  const float* M = g.M;
+  // Sigma = M M^T
+  g.Sig[0] = (M[0] * M[0] + M[1] * M[1]) + M[2] * M[2];
+  g.Sig[1] = (M[0] * M[3] + M[1] * M[4]) + M[2] * M[5];
+  g.Sig[2] = (M[0] * M[6] + M[1] * M[7]) + M[2] * M[8];
+  g.Sig[3] = (M[3] * M[3] + M[4] * M[4]) + M[5] * M[5];
+  g.Sig[4] = (M[3] * M[6] + M[4] * M[7]) + M[5] * M[8];
+  g.Sig[5] = (M[6] * M[6] + M[7] * M[7]) + M[8] * M[8];
+  // T = J W with J = [fx/z, 0, -fx x/z^2; 0, fy/z, -fy y/z^2]
+  const float J00 = cam.fx / g.p[2];
+  const float J02 = -(cam.fx * g.xz) / g.p[2];
+  const float J11 = cam.fy / g.p[2];
+  const float J12 = -(cam.fy * g.yz) / g.p[2];
+  for (int k = 0; k < 3; ++k) {
+    g.t0[k] = J00 * cam.R[k] + J02 * cam.R[6 + k];
+    g.t1[k] = J11 * cam.R[3 + k] + J12 * cam.R[6 + k];
+  }
+  const float* S = g.Sig;
+  // rows of Sigma in full: (S0 S1 S2 / S1 S3 S4 / S2 S4 S5)
+  const float w00 = (S[0] * g.t0[0] + S[1] * g.t0[1]) + S[2] * g.t0[2];
+  const float w01 = (S[1] * g.t0[0] + S[3] * g.t0[1]) + S[4] * g.t0[2];
+  const float w02 = (S[2] * g.t0[0] + S[4] * g.t0[1]) + S[5] * g.t0[2];
+  const float w10 = (S[0] * g.t1[0] + S[1] * g.t1[1]) + S[2] * g.t1[2];
+  const float w11 = (S[1] * g.t1[0] + S[3] * g.t1[1]) + S[4] * g.t1[2];
+  const float w12 = (S[2] * g.t1[0] + S[4] * g.t1[1]) + S[5] * g.t1[2];
+  const float V00 = (g.t0[0] * w00 + g.t0[1] * w01) + g.t0[2] * w02;
+  const float V01 = (g.t1[0] * w00 + g.t1[1] * w01) + g.t1[2] * w02;
+  const float V11 = (g.t1[0] * w10 + g.t1[1] * w11) + g.t1[2] * w12;
+  g.a = V00 + 0.3f;   // 0.3 px^2 dilation ([GST] Jacobian slide)
+  g.b = V01;
+  g.c = V11 + 0.3f;
+  g.det = g.a * g.c - g.b * g.b;
+  if (!(g.det > 0.0f)) return false;
+  g.A = g.c / g.det;
+  g.B = -g.b / g.det;
+  g.C = g.a / g.det;
+  g.o = float(1.0 / (1.0 + exp(-double(params[10 * n + i]))));
+  return true;
+}
+
+// View direction dir = normalize(mean - campos) and its length ([GSG] "Spherical harmonics").
+__device__ inline float view_dir(const float* __restrict__ params, int n, int i, const gs_camera& cam,
+                                 float* dir) {
+  const float d0 = params[i] - cam.campos[0], d1 = params[n + i] - cam.campos[1],
+              d2 = params[2 * n + i] - cam.campos[2];
+  const float len = sqrtf((d0 * d0 + d1 * d1) + d2 * d2);
+  dir[0] = d0 / len;
+  dir[1] = d1 / len;
+  dir[2] = d2 / len;
+  return len;
+}
+
+// Colour before the clamp: DC + sum_k sh_k Y_k.
+__device__ inline void sh_colour(const float* __restrict__ params, int n, int i, int K, const float* Y,
+                                 float* raw) {
+  for (int ch = 0; ch < 3; ++ch) {
+    float col = params[(11 + ch) * n + i];
+    for (int k = 1; k <= K; ++k) col = col + params[(14 + 3 * (k - 1) + ch) * n + i] * Y[k];
+    raw[ch] = col;
+  }
+}
+
+}  // namespace proj
+}  // namespace gsk

@@ -50,6 +50,7 @@
 #include <algorithm>
 
 #include "gs_internal.h"
+#include "profile.h"
 
 namespace gsk {
 namespace {
@@ -756,18 +757,39 @@ hipError_t launch_render_fwd(const gs_proj& proj, const uint32_t* vals, const ui
   const SplitDims d = split_dims(cam.width, cam.height, pairs, g_first, g_chunk);
   const SplitWs ws = carve(wsp, d);
   const float4* splat = reinterpret_cast<const float4*>(proj.splat);
-  split_init_kernel<<<div_up(num_tiles, 256), 256, 0, s>>>(ws.counters, ws.slot_of_tile, num_tiles);
-  tile_order_kernel<<<1, 1024, 0, s>>>(ranges, num_tiles, ws.order);
-  render_fwd_kernel<<<num_tiles, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, cam.width, cam.height,
-                                              cam.bg[0], cam.bg[1], cam.bg[2], g_first, g_chunk, rgb, T_final,
-                                              n_contrib);
+  {
+    GSK_PROF("split_init", s);
+    split_init_kernel<<<div_up(num_tiles, 256), 256, 0, s>>>(ws.counters, ws.slot_of_tile, num_tiles);
+  }
+  {
+    GSK_PROF("tile_order", s);
+    tile_order_kernel<<<1, 1024, 0, s>>>(ranges, num_tiles, ws.order);
+  }
+  {
+    GSK_PROF("render_fwd", s);
+    render_fwd_kernel<<<num_tiles, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, cam.width, cam.height,
+                                                cam.bg[0], cam.bg[1], cam.bg[2], g_first, g_chunk, rgb, T_final,
+                                                n_contrib);
+  }
   if (pairs > uint32_t(g_first)) {
     const unsigned items = unsigned(d.I), slots = unsigned(d.S);
-    split_chunk_kernel<<<items, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, g_first, g_chunk);
-    split_combine_kernel<<<slots, 256, 0, s>>>(ws);
-    split_rewalk_kernel<<<items, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, g_first, g_chunk);
-    split_finalize_kernel<<<slots, 256, 0, s>>>(ws, tx, cam.width, cam.height, cam.bg[0], cam.bg[1], cam.bg[2], rgb,
-                                                T_final, n_contrib);
+    {
+      GSK_PROF("split_chunk", s);
+      split_chunk_kernel<<<items, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, g_first, g_chunk);
+    }
+    {
+      GSK_PROF("split_combine", s);
+      split_combine_kernel<<<slots, 256, 0, s>>>(ws);
+    }
+    {
+      GSK_PROF("split_rewalk", s);
+      split_rewalk_kernel<<<items, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, g_first, g_chunk);
+    }
+    {
+      GSK_PROF("split_finalize", s);
+      split_finalize_kernel<<<slots, 256, 0, s>>>(ws, tx, cam.width, cam.height, cam.bg[0], cam.bg[1], cam.bg[2], rgb,
+                                                  T_final, n_contrib);
+    }
   }
   return hipGetLastError();
 }
@@ -780,14 +802,23 @@ hipError_t launch_render_bwd(const gs_proj& proj, int n, const uint32_t* vals, c
   const SplitDims d = split_dims(cam.width, cam.height, pairs, g_first, g_chunk);
   const SplitWs ws = carve(wsp, d);
   const float4* splat = reinterpret_cast<const float4*>(proj.splat);
-  if (n > 0) zero_f32_kernel<<<div_up(9 * int64_t(n), 256), 256, 0, s>>>(gscreen, 9 * int64_t(n));
-  render_bwd_kernel<<<num_tiles, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, cam.width, cam.height,
-                                              cam.bg[0], cam.bg[1], cam.bg[2], g_first, T_final, n_contrib, dL_dimg,
-                                              n, gscreen);
+  if (n > 0) {
+    GSK_PROF("zero_f32", s);
+    zero_f32_kernel<<<div_up(9 * int64_t(n), 256), 256, 0, s>>>(gscreen, 9 * int64_t(n));
+  }
+  {
+    GSK_PROF("render_bwd", s);
+    render_bwd_kernel<<<num_tiles, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, cam.width, cam.height,
+                                                cam.bg[0], cam.bg[1], cam.bg[2], g_first, T_final, n_contrib, dL_dimg,
+                                                n, gscreen);
+  }
   if (pairs > uint32_t(g_first)) {
-    split_bwd_kernel<<<unsigned(d.I), 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, cam.width, cam.height,
-                                                   cam.bg[0], cam.bg[1], cam.bg[2], g_first, g_chunk, T_final,
-                                                   n_contrib, dL_dimg, n, gscreen);
+    {
+      GSK_PROF("split_bwd", s);
+      split_bwd_kernel<<<unsigned(d.I), 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, cam.width, cam.height,
+                                                     cam.bg[0], cam.bg[1], cam.bg[2], g_first, g_chunk, T_final,
+                                                     n_contrib, dL_dimg, n, gscreen);
+    }
   }
   return hipGetLastError();
 }

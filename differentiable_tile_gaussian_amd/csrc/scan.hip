@@ -3,6 +3,7 @@
 // stages": the scan that reserves each Gaussian's slot range) and for the radix
 // sort's digit histograms.  No inter-block waiting: three plain launches.
 #include "gs_internal.h"
+#include "profile.h"
 
 namespace gsk {
 namespace {
@@ -128,14 +129,26 @@ size_t scan_ws_bytes(int64_t n) { return size_t(div_up(n > 0 ? n : 1, kScanTile)
 hipError_t launch_scan_u32(const uint32_t* in, uint32_t* out, int64_t n, uint64_t* total64, void* ws,
                            hipStream_t s) {
   if (n == 0) {
-    scan_empty_kernel<<<1, 1, 0, s>>>(out, total64);
+    {
+      GSK_PROF("scan_empty", s);
+      scan_empty_kernel<<<1, 1, 0, s>>>(out, total64);
+    }
     return hipGetLastError();
   }
   const int nb = int(div_up(n, kScanTile));
   uint64_t* sums = static_cast<uint64_t*>(ws);
-  scan_reduce_kernel<<<nb, kScanThreads, 0, s>>>(in, n, sums);
-  scan_blocks_kernel<<<1, 1024, 0, s>>>(sums, nb, total64, out + n);
-  scan_apply_kernel<<<nb, kScanThreads, 0, s>>>(in, n, sums, out);
+  {
+    GSK_PROF("scan_reduce", s);
+    scan_reduce_kernel<<<nb, kScanThreads, 0, s>>>(in, n, sums);
+  }
+  {
+    GSK_PROF("scan_blocks", s);
+    scan_blocks_kernel<<<1, 1024, 0, s>>>(sums, nb, total64, out + n);
+  }
+  {
+    GSK_PROF("scan_apply", s);
+    scan_apply_kernel<<<nb, kScanThreads, 0, s>>>(in, n, sums, out);
+  }
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@
 //                            local reorder through LDS, coalesced scatter.
 // tile_ranges    first / one-past-last pair of each tile.
 #include "gs_internal.h"
+#include "profile.h"
 
 namespace gsk {
 namespace {
@@ -201,7 +202,10 @@ hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uin
                            uint32_t* vals, uint32_t* ranges, void* ws, hipStream_t s) {
   const int tx = tiles_x(cam), ty = tiles_y(cam);
   const int num_tiles = tx * ty;
-  fill_u32_kernel<<<div_up(2 * int64_t(num_tiles), 256), 256, 0, s>>>(ranges, 2 * int64_t(num_tiles), 0u);
+  {
+    GSK_PROF("fill_u32", s);
+    fill_u32_kernel<<<div_up(2 * int64_t(num_tiles), 256), 256, 0, s>>>(ranges, 2 * int64_t(num_tiles), 0u);
+  }
   if (pairs == 0) return hipGetLastError();
   SortWs w = carve(ws, pairs);
   // significant key bits: 32 depth bits + enough for the largest tile id
@@ -212,22 +216,34 @@ hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uin
   uint32_t* v_src = (passes & 1) ? w.vals_alt : vals;
   uint64_t* k_dst = (passes & 1) ? keys : w.keys_alt;
   uint32_t* v_dst = (passes & 1) ? vals : w.vals_alt;
-  emit_keys_kernel<<<div_up(pairs, 256), 256, 0, s>>>(proj.offs, n, proj.depth,
-                                                      reinterpret_cast<const uint2*>(proj.rect), pairs, tx, k_src,
-                                                      v_src);
+  {
+    GSK_PROF("emit_keys", s);
+    emit_keys_kernel<<<div_up(pairs, 256), 256, 0, s>>>(proj.offs, n, proj.depth,
+                                                        reinterpret_cast<const uint2*>(proj.rect), pairs, tx, k_src,
+                                                        v_src);
+  }
   const int nb = int(div_up(pairs, kSortTile));
   const int64_t hist_n = int64_t(kRadix) * nb;
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = 8 * pass;
-    radix_upsweep_kernel<<<nb, kSortThreads, 0, s>>>(k_src, pairs, shift, nb, w.hist);
+    {
+      GSK_PROF("radix_upsweep", s);
+      radix_upsweep_kernel<<<nb, kSortThreads, 0, s>>>(k_src, pairs, shift, nb, w.hist);
+    }
     hipError_t e = launch_scan_u32(w.hist, w.hist_scan, hist_n, w.total64, w.scan_ws, s);
     if (e != hipSuccess) return e;
-    radix_downsweep_kernel<<<nb, kSortThreads, 0, s>>>(k_src, v_src, pairs, shift, nb, w.hist, w.hist_scan, k_dst,
-                                                       v_dst);
+    {
+      GSK_PROF("radix_downsweep", s);
+      radix_downsweep_kernel<<<nb, kSortThreads, 0, s>>>(k_src, v_src, pairs, shift, nb, w.hist, w.hist_scan, k_dst,
+                                                         v_dst);
+    }
     uint64_t* tk = k_src; k_src = k_dst; k_dst = tk;
     uint32_t* tv = v_src; v_src = v_dst; v_dst = tv;
   }
-  tile_ranges_kernel<<<div_up(pairs, 256), 256, 0, s>>>(keys, pairs, num_tiles, ranges);
+  {
+    GSK_PROF("tile_ranges", s);
+    tile_ranges_kernel<<<div_up(pairs, 256), 256, 0, s>>>(keys, pairs, num_tiles, ranges);
+  }
   return hipGetLastError();
 }
 

@@ -21,7 +21,8 @@ GS_WS_PREPROCESS, GS_WS_BIN_SORT, GS_WS_LOSS, GS_WS_RENDER = 0, 1, 2, 3
 GS_TUNE_SPLIT_FIRST, GS_TUNE_SPLIT_CHUNK = 0, 1
 
 EXPORTED = ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
-            "gs_adam_step", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning", "gs_last_error")
+            "gs_adam_step", "gs_render_bwd_adam", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
+            "gs_profile_enable", "gs_profile_query", "gs_last_error")
 
 
 class GsError(RuntimeError):
@@ -55,11 +56,18 @@ def _load():
     lib.gs_render_fwd.argtypes = [P, I64, P, P, U32, P, P, P, P, P, C.c_size_t, P]
     lib.gs_loss_l1_dssim.argtypes = [P, P, I32, I32, C.c_float, P, P, P, C.c_size_t, P]
     lib.gs_render_bwd.argtypes = [P, P, P, P, U32, P, P, P, P, P, P, P, C.c_size_t, P]
+    lib.gs_render_bwd_adam.argtypes = [P, I64, I32, P, P, P, U32, P, P, P, P, P, P, P, P, C.c_double, C.c_double,
+                                       C.c_double, I32, P, C.c_size_t, P]
+    lib.gs_render_bwd_adam.restype = I32
     lib.gs_set_tuning.argtypes = [I32, I64]
     lib.gs_set_tuning.restype = I32
     lib.gs_get_tuning.argtypes = [I32]
     lib.gs_get_tuning.restype = I64
     lib.gs_adam_step.argtypes = [P, P, P, P, I64, I32, P, C.c_double, C.c_double, C.c_double, I32, P]
+    lib.gs_profile_enable.argtypes = [I32, C.c_char_p]
+    lib.gs_profile_enable.restype = I32
+    lib.gs_profile_query.argtypes = [I32, P, P, P]
+    lib.gs_profile_query.restype = I32
     lib.gs_workspace_bytes.argtypes = [I32, I64, U32, I32, I32]
     lib.gs_workspace_bytes.restype = C.c_size_t
     lib.gs_last_error.restype = C.c_char_p
@@ -170,12 +178,38 @@ def gs_adam_step(params, grads, m, v, sh_degree, lr, beta1, beta2, eps, step, st
                              float(beta2), float(eps), int(step), _stream(stream)))
 
 
+def gs_render_bwd_adam(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam: GsCamera, T_final,
+                       n_contrib, dL_dimg, gscreen, m, v, lr, beta1, beta2, eps, step, ws, stream=None):
+    lr_arr = (C.c_float * 5)(*[float(x) for x in lr])
+    _check(_lib.gs_render_bwd_adam(_ptr(params), proj.n, sh_degree, C.byref(proj.struct), _ptr(vals), _ptr(ranges),
+                                   total_pairs, C.byref(cam), _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimg),
+                                   _ptr(gscreen), _ptr(m), _ptr(v), lr_arr, float(beta1), float(beta2),
+                                   float(eps), int(step), _ptr(ws), ws.numel(), _stream(stream)))
+
+
 def gs_set_tuning(key, value):
     _check(_lib.gs_set_tuning(key, int(value)))
 
 
 def gs_get_tuning(key):
     return int(_lib.gs_get_tuning(key))
+
+
+def gs_profile_enable(on, only=None):
+    """Start (on=True) or stop per-kernel event timing; `only` restricts it to one kernel name."""
+    _check(_lib.gs_profile_enable(1 if on else 0, only.encode() if only else None))
+
+
+def gs_profile_query(max_names=64):
+    """{kernel name: (launches, summed milliseconds)} for the launches recorded since enabling."""
+    names = C.create_string_buffer(64 * max_names)
+    launches = (C.c_int64 * max_names)()
+    total_ms = (C.c_double * max_names)()
+    k = _lib.gs_profile_query(max_names, C.cast(names, C.c_void_p), C.cast(launches, C.c_void_p),
+                              C.cast(total_ms, C.c_void_p))
+    _check(min(k, 0))
+    return {names.raw[64 * i:64 * (i + 1)].split(b"\0", 1)[0].decode(): (int(launches[i]), float(total_ms[i]))
+            for i in range(k)}
 
 
 def gs_last_error():

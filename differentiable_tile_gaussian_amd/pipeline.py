@@ -75,8 +75,19 @@ class Pipeline:
         gs.gs_adam_step(self.params, self.grads, self.m, self.v, self.deg, self.lr, self.betas[0], self.betas[1],
                         self.eps, self.t)
 
-    def step(self, cam: gs.GsCamera, target: torch.Tensor, adam: bool = True):
+    def backward_adam(self, cam: gs.GsCamera, target: torch.Tensor):
+        """Loss, backward and Adam with the chain and Adam fused (no gradient written)."""
+        gs.gs_loss_l1_dssim(self.rgb, target, self.lam, self.loss, self.dLdI, self.ws_loss)
+        self.t += 1
+        gs.gs_render_bwd_adam(self.params, self.deg, self.proj, self.vals, self.ranges, self.pairs, cam, self.T,
+                              self.nc, self.dLdI, self.gscreen, self.m, self.v, self.lr, self.betas[0],
+                              self.betas[1], self.eps, self.t, self.ws_render)
+
+    def step(self, cam: gs.GsCamera, target: torch.Tensor, adam: bool = True, fused: bool = True):
         self.forward(cam)
+        if adam and fused:
+            self.backward_adam(cam, target)
+            return self.loss
         self.backward(cam, target)
         if adam:
             self.adam()

@@ -170,6 +170,17 @@ int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t
 int32_t gs_adam_step(float* params, const float* grads, float* m, float* v, int64_t n, int32_t sh_degree,
                      const float* lr, double beta1, double beta2, double eps, int32_t step, void* stream);
 
+/* gs_render_bwd followed by gs_adam_step, fused: the chain applies Adam to each parameter as
+ * soon as its gradient is known, so the parameter gradient is never written to memory (it
+ * saves two passes over [P][n] floats).  Same arguments and results as the two calls, with
+ * params updated in place; gscreen is scratch here: on return its planes 6-8 hold the mean
+ * gradient's view-direction term instead of the colour gradients. */
+int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs_proj* proj, const uint32_t* vals,
+                           const uint32_t* ranges, uint32_t total_pairs, const gs_camera* cam,
+                           const float* T_final, const uint32_t* n_contrib, const float* dL_dimg, float* gscreen,
+                           float* m, float* v, const float* lr, double beta1, double beta2, double eps,
+                           int32_t step, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace sizes, in bytes, for the calls that take one. */
 enum { GS_WS_PREPROCESS = 0, GS_WS_BIN_SORT = 1, GS_WS_LOSS = 2, GS_WS_RENDER = 3 };
 size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H);
@@ -182,6 +193,18 @@ size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t
 enum { GS_TUNE_SPLIT_FIRST = 0, GS_TUNE_SPLIT_CHUNK = 1 };
 int32_t gs_set_tuning(int32_t key, int64_t value);
 int64_t gs_get_tuning(int32_t key);
+
+/* Optional per-kernel timing (instrumentation, not part of the method).  gs_profile_enable(1, only)
+ * makes every later library call bracket each kernel launch whose name equals `only` (every
+ * launch if `only` is NULL or "") with two HIP events recorded on the call's stream;
+ * gs_profile_enable(0, NULL) stops it.  Either call waits for and drops the records held.
+ * gs_profile_query waits for the recorded events and writes, per kernel name in first-seen
+ * order, the name (NUL-terminated, in 64-byte slots of `names`), the number of launches and the
+ * summed elapsed milliseconds; it returns the number of names written (at most max_names) or a
+ * negative gs_status.  Host buffers, owned by the caller.  Not thread-safe against concurrent
+ * library calls on other threads. */
+int32_t gs_profile_enable(int32_t on, const char* only);
+int32_t gs_profile_query(int32_t max_names, char* names, int64_t* launches, double* total_ms);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* gs_last_error(void);

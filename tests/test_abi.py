@@ -90,6 +90,18 @@ def test_workspace_sizes_grow_with_the_problem(gs):
     assert gs.gs_workspace_bytes(99, 1, 1, 1, 1) == 0
 
 
+def test_profile_calls_without_gpu(gs):
+    # nothing recorded yet: enabling, querying and disabling touch no device
+    gs.gs_profile_enable(True, "render_fwd")
+    assert gs.gs_profile_query() == {}
+    gs.gs_profile_enable(False)
+    lib = gs.lib()
+    assert lib.gs_profile_query(-1, None, None, None) == gs.GS_ERR_INVALID_ARG
+    assert "max_names" in gs.gs_last_error()
+    assert lib.gs_profile_query(4, None, None, None) == gs.GS_ERR_INVALID_ARG
+    assert lib.gs_profile_query(0, None, None, None) == 0
+
+
 def test_product_path_does_not_reference_the_oracle():
     pkg = os.path.join(ROOT, "differentiable_tile_gaussian_amd")
     for dirpath, _, files in os.walk(pkg):

@@ -307,3 +307,52 @@ def test_split_path_parity(torch_cuda, oracle, split_tuning, tune, which):
         pu.check_grad(g[sl], o["gparams"][sl], keep, name=name)
     stopped = float((o["fwd"]["T"] < 1e-4).mean())
     print(f"  low-margin px {n_low}, excluded G {int((~keep).sum())}, saturated px {stopped:.2f}", flush=True)
+
+
+# ------------------------------------------------------- fused backward + Adam
+@pytest.mark.parametrize("case", [_small_cases()[0], _small_cases()[3], "cfg1"])
+def test_fused_backward_adam(torch_cuda, oracle, case):
+    """gs_render_bwd_adam equals gs_render_bwd followed by gs_adam_step, and the oracle's
+    fp64 Adam applied to the oracle's gradient, on two consecutive steps."""
+    torch = torch_cuda
+    from differentiable_tile_gaussian_amd import gs
+    if case == "cfg1":
+        wl = scenes.config1()
+        s, cam = wl.scene, wl.cameras[0]
+    else:
+        s, cam = _scene_and_camera(*case)
+    deg = s.sh_degree
+    P = scenes.num_planes(deg)
+    rng = np.random.default_rng(17)
+    m0 = (1e-3 * rng.standard_normal((P, s.n))).astype(np.float32)
+    v0 = (1e-6 * rng.random((P, s.n))).astype(np.float32)
+    lr = (1.6e-4, 5e-3, 1e-3, 5e-2, 2.5e-3)
+    dLdI = (rng.standard_normal((3, cam.height, cam.width)) * 1e-3).astype(np.float32)
+    results = {}
+    for mode in ("separate", "fused"):
+        pl, c = pu.gpu_forward(s.params, deg, cam)
+        pl.m.copy_(torch.from_numpy(m0))
+        pl.v.copy_(torch.from_numpy(v0))
+        pl.dLdI.copy_(torch.from_numpy(dLdI))
+        if mode == "separate":
+            gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI,
+                             pl.gscreen, pl.grads, pl.ws_render)
+            gs.gs_adam_step(pl.params, pl.grads, pl.m, pl.v, deg, lr, 0.9, 0.999, 1e-8, 3)
+        else:
+            gs.gs_render_bwd_adam(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI,
+                                  pl.gscreen, pl.m, pl.v, lr, 0.9, 0.999, 1e-8, 3, pl.ws_render)
+        torch.cuda.synchronize()
+        results[mode] = [t.cpu().numpy() for t in (pl.params, pl.m, pl.v)]
+    th0 = s.params.astype(np.float64)
+    for a, b in zip(results["separate"], results["fused"]):
+        np.testing.assert_allclose(b, a, rtol=2e-6, atol=1e-9)
+    # against the oracle: gradient from the oracle, Adam in fp64
+    o = _oracle_all(oracle, s.params, deg, cam, dLdI)
+    p_ref, m_ref, v_ref = oracle.adam(th0, o["gparams"].astype(np.float64), m0, v0, deg, np.array(lr), step=3)
+    keep = o["gmargin"] >= pu.MARGIN
+    # compare the applied updates (theta_new - theta) group by group with the gradient tolerance
+    upd_gpu = results["fused"][0].astype(np.float64) - th0
+    upd_ref = p_ref - th0
+    for name, sl in pu.grad_groups(deg).items():
+        pu.check_grad(upd_gpu[sl], upd_ref[sl], keep, rtol=2e-3, name="update " + name)
+    pu.check_grad(results["fused"][1].astype(np.float64), m_ref, keep, name="m")
