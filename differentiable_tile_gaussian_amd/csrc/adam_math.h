@@ -27,13 +27,4 @@ __device__ inline float adam_update(float th, float g, float& m, float& v, float
   return th - lr * mh / (sqrtf(vh) + a.eps);
 }
 
-// One parameter of plane `pl`, Gaussian i: update in place from gradient g.
-__device__ inline void adam_apply(float* __restrict__ params, float* __restrict__ m, float* __restrict__ v,
-                                  size_t k, int pl, float g, const AdamArgs& a) {
-  float mm = m[k], vv = v[k];
-  params[k] = adam_update(params[k], g, mm, vv, a.lr[adam_group(pl)], a);
-  m[k] = mm;
-  v[k] = vv;
-}
-
 }  // namespace gsk

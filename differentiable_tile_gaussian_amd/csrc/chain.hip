@@ -26,6 +26,9 @@ namespace {
 
 using namespace proj;
 
+// Plane of colour coefficient k (0 = DC, 1.. = bands) of channel ch.
+__device__ inline int colour_plane(int k, int ch) { return k == 0 ? 11 + ch : 14 + 3 * (k - 1) + ch; }
+
 template <int DEG, bool ADAM>
 __global__ void __launch_bounds__(192) chain_colour_kernel(float* __restrict__ params, int n, gs_camera cam,
                                                             const uint32_t* __restrict__ tiles,
@@ -33,30 +36,52 @@ __global__ void __launch_bounds__(192) chain_colour_kernel(float* __restrict__ p
                                                             float* __restrict__ m, float* __restrict__ v,
                                                             AdamArgs a) {
   constexpr int K = (DEG + 1) * (DEG + 1) - 1;
+  constexpr int P = 11 + 3 * (K + 1);
   __shared__ float s_gdir[3][3][64];
   const int lane = threadIdx.x & 63, ch = threadIdx.x >> 6;
   const int i = blockIdx.x * 64 + lane;
   const bool valid = i < n;
-  const bool vis = valid && tiles[i] != 0u;
+  // This block's 64 Gaussians are one group of the blocked layout: each plane is a
+  // contiguous 256-byte row and the whole colour part one 12 KB stretch per array.
+  const size_t gb = size_t(blockIdx.x) * P * kGB + lane;
+  // Every load of this lane is issued before any arithmetic (the pass is a stream;
+  // a load that waited on another would add a memory round trip).
+  uint32_t ntile = 0;
+  float mean[3] = {0.f, 0.f, 0.f};
+  float coef[K + 1], mo[ADAM ? K + 1 : 1], vo[ADAM ? K + 1 : 1];
+  float gcol = 0.0f;
+  if (valid) {
+    ntile = tiles[i];
+    if (K > 0) {
+#pragma unroll
+      for (int c = 0; c < 3; ++c) mean[c] = params[gb + c * kGB];
+    }
+#pragma unroll
+    for (int k = 0; k <= K; ++k) coef[k] = __builtin_nontemporal_load(params + gb + colour_plane(k, ch) * kGB);
+    gcol = gscreen[(6 + ch) * n + i];
+    if (ADAM) {
+#pragma unroll
+      for (int k = 0; k <= K; ++k) {
+        const size_t o = gb + colour_plane(k, ch) * kGB;
+        mo[k] = __builtin_nontemporal_load(m + o);
+        vo[k] = __builtin_nontemporal_load(v + o);
+      }
+    }
+  }
+  const bool vis = valid && ntile != 0u;
   float dir[3] = {0.f, 0.f, 0.f};
   float dlen = 1.0f;
   float Y[16];
   if (K > 0 && vis) {
-    dlen = view_dir(params, n, i, cam, dir);
+    dlen = view_dir_from(mean[0], mean[1], mean[2], cam, dir);
     sh_eval(dir[0], dir[1], dir[2], Y);
   }
-  float coef[K + 1];
   float gc = 0.0f;
-  if (valid) {
-    coef[0] = params[(11 + ch) * n + i];
-#pragma unroll
-    for (int k = 1; k <= K; ++k) coef[k] = params[(14 + 3 * (k - 1) + ch) * n + i];
-  }
   if (vis) {
     float raw = coef[0];
 #pragma unroll
     for (int k = 1; k <= K; ++k) raw = raw + coef[k] * Y[k];
-    gc = raw < 0.0f ? 0.0f : gscreen[(6 + ch) * n + i];
+    gc = raw < 0.0f ? 0.0f : gcol;
   }
   if (K > 0) {
     float gd[3] = {0.f, 0.f, 0.f};
@@ -72,14 +97,12 @@ __global__ void __launch_bounds__(192) chain_colour_kernel(float* __restrict__ p
   if (valid) {
 #pragma unroll
     for (int k = 0; k <= K; ++k) {
-      const int pl = k == 0 ? 11 + ch : 14 + 3 * (k - 1) + ch;
       const float g = k == 0 ? gc : (vis ? gc * Y[k] : 0.0f);
-      const size_t o = size_t(pl) * n + i;
+      const size_t o = gb + colour_plane(k, ch) * kGB;
       if (ADAM) {
-        float mm = m[o], vv = v[o];
-        params[o] = adam_update(coef[k], g, mm, vv, a.lr[4], a);
-        m[o] = mm;
-        v[o] = vv;
+        __builtin_nontemporal_store(adam_update(coef[k], g, mo[k], vo[k], a.lr[4], a), params + o);
+        __builtin_nontemporal_store(mo[k], m + o);
+        __builtin_nontemporal_store(vo[k], v + o);
       } else {
         gparams[o] = g;
       }
@@ -96,9 +119,14 @@ __global__ void __launch_bounds__(192) chain_colour_kernel(float* __restrict__ p
 #pragma unroll
         for (int c = 0; c < 3; ++c) out[c] = (gt[c] - dir[c] * dd) / dlen;
       }
-      float* dst = ADAM ? gscreen + size_t(6) * n : gparams;
+      // to the mean planes of gparams, or (Adam fused) to gscreen planes 6-8
 #pragma unroll
-      for (int c = 0; c < 3; ++c) dst[size_t(c) * n + i] = out[c];
+      for (int c = 0; c < 3; ++c) {
+        if (ADAM)
+          gscreen[size_t(6 + c) * n + i] = out[c];
+        else
+          gparams[gb + c * kGB] = out[c];
+      }
     }
   }
 }
@@ -109,20 +137,33 @@ __global__ void __launch_bounds__(256) chain_geometry_kernel(float* __restrict__
                                                               const float* __restrict__ gscreen,
                                                               float* __restrict__ gparams, float* __restrict__ m,
                                                               float* __restrict__ v, AdamArgs a) {
+  constexpr int P = 11 + 3 * (DEG + 1) * (DEG + 1);
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  float gp[11];
+  const size_t gb = size_t(i / kGB) * P * kGB + (i % kGB);
+  // all loads first (see the colour kernel)
+  const uint32_t ntile = tiles[i];
+  float th[11], gs6[6], gp[11], mo[ADAM ? 11 : 1], vo[ADAM ? 11 : 1];
+#pragma unroll
+  for (int k = 0; k < 11; ++k) th[k] = __builtin_nontemporal_load(params + gb + k * kGB);
+#pragma unroll
+  for (int k = 0; k < 6; ++k) gs6[k] = gscreen[size_t(k) * n + i];
 #pragma unroll
   for (int k = 0; k < 11; ++k) gp[k] = 0.0f;
   if (DEG > 0) {
-    const float* src = ADAM ? gscreen + size_t(6) * n : gparams;
 #pragma unroll
-    for (int c = 0; c < 3; ++c) gp[c] = src[size_t(c) * n + i];
+    for (int c = 0; c < 3; ++c) gp[c] = ADAM ? gscreen[size_t(6 + c) * n + i] : gparams[gb + c * kGB];
+  }
+  if (ADAM) {
+#pragma unroll
+    for (int k = 0; k < 11; ++k) {
+      mo[k] = __builtin_nontemporal_load(m + gb + k * kGB);
+      vo[k] = __builtin_nontemporal_load(v + gb + k * kGB);
+    }
   }
   Proj g;
-  if (tiles[i] != 0u && project_geometry(params, n, i, cam, g)) {
-    const float gu = gscreen[i], gv = gscreen[n + i], gA = gscreen[2 * n + i], gB = gscreen[3 * n + i],
-                gC = gscreen[4 * n + i], go = gscreen[5 * n + i];
+  if (ntile != 0u && project_geometry_from(th, cam, g)) {
+    const float gu = gs6[0], gv = gs6[1], gA = gs6[2], gB = gs6[3], gC = gs6[4], go = gs6[5];
     // opacity logit through the sigmoid
     gp[10] = go * g.o * (1.0f - g.o);
     // conic -> dilated covariance: dV' = -K Gk K with Gk = [[gA, gB/2], [gB/2, gC]]
@@ -191,11 +232,14 @@ __global__ void __launch_bounds__(256) chain_geometry_kernel(float* __restrict__
   }
 #pragma unroll
   for (int pl = 0; pl < 11; ++pl) {
-    const size_t o = size_t(pl) * n + i;
-    if (ADAM)
-      adam_apply(params, m, v, o, pl, gp[pl], a);
-    else
+    const size_t o = gb + pl * kGB;
+    if (ADAM) {
+      __builtin_nontemporal_store(adam_update(th[pl], gp[pl], mo[pl], vo[pl], a.lr[adam_group(pl)], a), params + o);
+      __builtin_nontemporal_store(mo[pl], m + o);
+      __builtin_nontemporal_store(vo[pl], v + o);
+    } else {
       gparams[o] = gp[pl];
+    }
   }
 }
 

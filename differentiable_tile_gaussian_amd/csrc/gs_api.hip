@@ -43,8 +43,8 @@ int32_t check_scene(const gs_scene* sc) {
   if (sc->n < 0 || sc->n >= (int64_t(1) << 31)) return fail(GS_ERR_INVALID_ARG, "n out of range");
   if (sc->sh_degree < 0 || sc->sh_degree > 3) return fail(GS_ERR_UNSUPPORTED, "SH degree must be 0..3");
   if (sc->n > 0 && !sc->params) return fail(GS_ERR_INVALID_ARG, "params is null");
-  if (sc->n * gsk::num_planes(sc->sh_degree) >= (int64_t(1) << 31))
-    return fail(GS_ERR_UNSUPPORTED, "n * planes must stay below 2^31");
+  if (gsk::param_floats(sc->n, gsk::num_planes(sc->sh_degree)) >= (size_t(1) << 31))
+    return fail(GS_ERR_UNSUPPORTED, "gs_param_floats(n, sh_degree) must stay below 2^31");
   return GS_OK;
 }
 
@@ -217,8 +217,8 @@ static int32_t check_adam(int64_t n, int32_t sh_degree, const float* lr, double 
   if (n < 0 || n >= (int64_t(1) << 31)) return fail(GS_ERR_INVALID_ARG, "n out of range");
   if (sh_degree < 0 || sh_degree > 3) return fail(GS_ERR_UNSUPPORTED, "SH degree must be 0..3");
   if (!lr) return fail(GS_ERR_INVALID_ARG, "lr is null");
-  if (n * gsk::num_planes(sh_degree) >= (int64_t(1) << 31))
-    return fail(GS_ERR_UNSUPPORTED, "n * planes must stay below 2^31");
+  if (gsk::param_floats(n, gsk::num_planes(sh_degree)) >= (size_t(1) << 31))
+    return fail(GS_ERR_UNSUPPORTED, "gs_param_floats(n, sh_degree) must stay below 2^31");
   if (step < 1) return fail(GS_ERR_INVALID_ARG, "step must be >= 1");
   if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps >= 0.0))
     return fail(GS_ERR_INVALID_ARG, "bad Adam hyper-parameters");
@@ -272,8 +272,8 @@ int32_t gs_adam_step(float* params, const float* grads, float* m, float* v, int6
   if (sh_degree < 0 || sh_degree > 3) return fail(GS_ERR_UNSUPPORTED, "SH degree must be 0..3");
   if (!lr) return fail(GS_ERR_INVALID_ARG, "lr is null");
   if (n > 0 && (!params || !grads || !m || !v)) return fail(GS_ERR_INVALID_ARG, "an Adam array is null");
-  if (n * gsk::num_planes(sh_degree) >= (int64_t(1) << 31))
-    return fail(GS_ERR_UNSUPPORTED, "n * planes must stay below 2^31");
+  if (gsk::param_floats(n, gsk::num_planes(sh_degree)) >= (size_t(1) << 31))
+    return fail(GS_ERR_UNSUPPORTED, "gs_param_floats(n, sh_degree) must stay below 2^31");
   if (step < 1) return fail(GS_ERR_INVALID_ARG, "step must be >= 1");
   if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps >= 0.0))
     return fail(GS_ERR_INVALID_ARG, "bad Adam hyper-parameters");
@@ -284,6 +284,38 @@ int32_t gs_adam_step(float* params, const float* grads, float* m, float* v, int6
                                   float(1.0 - beta1), float(1.0 - beta2), float(eps), float(1.0 / bc1),
                                   float(1.0 / bc2), as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "adam");
+  return GS_OK;
+}
+
+size_t gs_param_floats(int64_t n, int32_t sh_degree) {
+  if (n < 0 || sh_degree < 0 || sh_degree > 3) return 0;
+  return gsk::param_floats(n, gsk::num_planes(sh_degree));
+}
+
+static int32_t check_layout(const float* a, const float* b, int64_t n, int32_t sh_degree) {
+  if (n < 0 || n >= (int64_t(1) << 31)) return fail(GS_ERR_INVALID_ARG, "n out of range");
+  if (sh_degree < 0 || sh_degree > 3) return fail(GS_ERR_UNSUPPORTED, "SH degree must be 0..3");
+  if (n > 0 && (!a || !b)) return fail(GS_ERR_INVALID_ARG, "a layout array is null");
+  if (gsk::param_floats(n, gsk::num_planes(sh_degree)) >= (size_t(1) << 31))
+    return fail(GS_ERR_UNSUPPORTED, "gs_param_floats(n, sh_degree) must stay below 2^31");
+  return GS_OK;
+}
+
+int32_t gs_params_to_blocked(const float* planar, float* blocked, int64_t n, int32_t sh_degree, void* stream) {
+  g_err[0] = 0;
+  int32_t st;
+  if ((st = check_layout(planar, blocked, n, sh_degree)) != GS_OK) return st;
+  hipError_t e = gsk::launch_to_blocked(planar, blocked, int(n), gsk::num_planes(sh_degree), as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "to_blocked");
+  return GS_OK;
+}
+
+int32_t gs_params_from_blocked(const float* blocked, float* planar, int64_t n, int32_t sh_degree, void* stream) {
+  g_err[0] = 0;
+  int32_t st;
+  if ((st = check_layout(blocked, planar, n, sh_degree)) != GS_OK) return st;
+  hipError_t e = gsk::launch_from_blocked(blocked, planar, int(n), gsk::num_planes(sh_degree), as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "from_blocked");
   return GS_OK;
 }
 

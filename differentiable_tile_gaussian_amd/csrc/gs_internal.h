@@ -17,6 +17,17 @@ inline int num_planes(int deg) { return 11 + 3 * (deg + 1) * (deg + 1); }
 
 inline unsigned div_up(int64_t a, int64_t b) { return unsigned((a + b - 1) / b); }
 
+// Blocked per-Gaussian parameter layout: groups of kGB Gaussians, each group holding
+// its P planes of kGB floats one after another.  Parameter p of Gaussian i is at
+// ((i / kGB) P + p) kGB + i % kGB.
+constexpr int kGB = 64;
+inline size_t param_floats(int64_t n, int P) { return size_t((n + kGB - 1) / kGB) * kGB * size_t(P); }
+// Address of plane 0 of Gaussian i (plane p is kGB * p floats further on).
+template <typename T>
+__host__ __device__ inline T* gaussian_base(T* params, int i, int P) {
+  return params + size_t(i / kGB) * size_t(P) * kGB + (i % kGB);
+}
+
 // ---- preprocess.hip
 hipError_t launch_preprocess_fwd(const float* params, int n, int deg, const gs_camera& cam, const gs_proj& out,
                                  hipStream_t s);
@@ -57,7 +68,11 @@ size_t loss_ws_bytes(int H, int W);
 hipError_t launch_loss(const float* img, const float* target, int H, int W, float lambda, float* loss_out,
                        float* grad, void* ws, hipStream_t s);
 
-// ---- adam.hip
+// ---- layout.hip: planar [P][n] <-> blocked (padding written as zero)
+hipError_t launch_to_blocked(const float* planar, float* blocked, int n, int P, hipStream_t s);
+hipError_t launch_from_blocked(const float* blocked, float* planar, int n, int P, hipStream_t s);
+
+// ---- adam.hip (blocked arrays; padding slots are not touched)
 hipError_t launch_adam(float* params, const float* grads, float* m, float* v, int n, int deg, const float lr[5],
                        float b1, float b2, float omb1, float omb2, float eps, float inv_bc1, float inv_bc2,
                        hipStream_t s);

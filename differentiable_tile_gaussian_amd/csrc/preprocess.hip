@@ -7,7 +7,8 @@
 // and rounded once.  Division and square root are the correctly rounded fp32
 // operations (the HIP default).
 //
-// One thread per Gaussian; params are read plane by plane (coalesced SoA).
+// One thread per Gaussian; each parameter plane of a group of 64 Gaussians is one
+// contiguous 256-byte row of the blocked layout, read by one wave.
 //
 // Pages (titles as they appear on the pages):
 //   [DR]  "Differentiable rasterisation";  [GST] Gaussian splatting training study deck;
@@ -28,19 +29,21 @@ __global__ void __launch_bounds__(256) preprocess_fwd_kernel(const float* __rest
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   constexpr int K = (DEG + 1) * (DEG + 1) - 1;
+  constexpr int P = 11 + 3 * (K + 1);
+  const float* g0 = gaussian_base(params, i, P);
   Proj g;
-  bool vis = project_geometry(params, n, i, cam, g);
+  bool vis = project_geometry(g0, cam, g);
   float rgb[3] = {0.f, 0.f, 0.f};
   uint32_t x0 = 0, y0 = 0, x1 = 0, y1 = 0, cnt = 0;
   if (vis) {
     float Y[16];
     if (K > 0) {
       float dir[3];
-      view_dir(params, n, i, cam, dir);
+      view_dir(g0, cam, dir);
       sh_eval(dir[0], dir[1], dir[2], Y);
     }
     float raw[3];
-    sh_colour(params, n, i, K, Y, raw);
+    sh_colour(g0, K, Y, raw);
     bool finite = __builtin_isfinite(g.u) && __builtin_isfinite(g.v) && __builtin_isfinite(g.A) &&
                   __builtin_isfinite(g.B) && __builtin_isfinite(g.C) && __builtin_isfinite(g.o);
     for (int ch = 0; ch < 3; ++ch) {

@@ -105,9 +105,9 @@ struct Proj {
 // Geometry of one Gaussian ([GST] parameter and Jacobian slides; [DR] "Forward";
 // [GSG] "Flattening a 3D blob into a 2D oval").  Returns false when culled (behind the
 // near plane, zero quaternion, non-positive determinant).
-__device__ inline bool project_geometry(const float* __restrict__ params, int n, int i, const gs_camera& cam,
-                                        Proj& g) {
-  const float mx = params[i], my = params[n + i], mz = params[2 * n + i];
+// th: the 11 geometry parameters (mean 0-2, log-scales 3-5, quaternion 6-9, logit 10).
+__device__ inline bool project_geometry_from(const float* th, const gs_camera& cam, Proj& g) {
+  const float mx = th[0], my = th[1], mz = th[2];
   for (int r = 0; r < 3; ++r)
     g.p[r] = ((cam.R[3 * r] * mx + cam.R[3 * r + 1] * my) + cam.R[3 * r + 2] * mz) + cam.t[r];
   if (!(g.p[2] > cam.znear)) return false;
@@ -115,8 +115,8 @@ __device__ inline bool project_geometry(const float* __restrict__ params, int n,
   g.yz = g.p[1] / g.p[2];
   g.u = cam.fx * g.xz + cam.cx;
   g.v = cam.fy * g.yz + cam.cy;
-  for (int k = 0; k < 3; ++k) g.s[k] = float(exp(double(params[(3 + k) * n + i])));
-  const float qw = params[6 * n + i], qx = params[7 * n + i], qy = params[8 * n + i], qz = params[9 * n + i];
+  for (int k = 0; k < 3; ++k) g.s[k] = float(exp(double(th[3 + k])));
+  const float qw = th[6], qx = th[7], qy = th[8], qz = th[9];
   const float n2 = ((qw * qw + qx * qx) + qy * qy) + qz * qz;
   if (!(n2 > 0.0f)) return false;
   g.ql = sqrtf(n2);
@@ -169,15 +169,21 @@ __device__ inline bool project_geometry(const float* __restrict__ params, int n,
   g.A = g.c / g.det;
   g.B = -g.b / g.det;
   g.C = g.a / g.det;
-  g.o = float(1.0 / (1.0 + exp(-double(params[10 * n + i]))));
+  g.o = float(1.0 / (1.0 + exp(-double(th[10]))));
   return true;
 }
 
+// The same, reading the 11 geometry planes of one Gaussian; g0 = gaussian_base(params, i, P).
+__device__ inline bool project_geometry(const float* __restrict__ g0, const gs_camera& cam, Proj& g) {
+  float th[11];
+#pragma unroll
+  for (int k = 0; k < 11; ++k) th[k] = g0[k * kGB];
+  return project_geometry_from(th, cam, g);
+}
+
 // View direction dir = normalize(mean - campos) and its length ([GSG] "Spherical harmonics").
-__device__ inline float view_dir(const float* __restrict__ params, int n, int i, const gs_camera& cam,
-                                 float* dir) {
-  const float d0 = params[i] - cam.campos[0], d1 = params[n + i] - cam.campos[1],
-              d2 = params[2 * n + i] - cam.campos[2];
+__device__ inline float view_dir_from(float mx, float my, float mz, const gs_camera& cam, float* dir) {
+  const float d0 = mx - cam.campos[0], d1 = my - cam.campos[1], d2 = mz - cam.campos[2];
   const float len = sqrtf((d0 * d0 + d1 * d1) + d2 * d2);
   dir[0] = d0 / len;
   dir[1] = d1 / len;
@@ -185,12 +191,15 @@ __device__ inline float view_dir(const float* __restrict__ params, int n, int i,
   return len;
 }
 
+__device__ inline float view_dir(const float* __restrict__ g0, const gs_camera& cam, float* dir) {
+  return view_dir_from(g0[0], g0[kGB], g0[2 * kGB], cam, dir);
+}
+
 // Colour before the clamp: DC + sum_k sh_k Y_k.
-__device__ inline void sh_colour(const float* __restrict__ params, int n, int i, int K, const float* Y,
-                                 float* raw) {
+__device__ inline void sh_colour(const float* __restrict__ g0, int K, const float* Y, float* raw) {
   for (int ch = 0; ch < 3; ++ch) {
-    float col = params[(11 + ch) * n + i];
-    for (int k = 1; k <= K; ++k) col = col + params[(14 + 3 * (k - 1) + ch) * n + i] * Y[k];
+    float col = g0[(11 + ch) * kGB];
+    for (int k = 1; k <= K; ++k) col = col + g0[(14 + 3 * (k - 1) + ch) * kGB] * Y[k];
     raw[ch] = col;
   }
 }

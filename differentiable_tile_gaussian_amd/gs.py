@@ -22,7 +22,8 @@ GS_TUNE_SPLIT_FIRST, GS_TUNE_SPLIT_CHUNK = 0, 1
 
 EXPORTED = ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
             "gs_adam_step", "gs_render_bwd_adam", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
-            "gs_profile_enable", "gs_profile_query", "gs_last_error")
+            "gs_profile_enable", "gs_profile_query", "gs_param_floats", "gs_params_to_blocked",
+            "gs_params_from_blocked", "gs_last_error")
 
 
 class GsError(RuntimeError):
@@ -68,6 +69,12 @@ def _load():
     lib.gs_profile_enable.restype = I32
     lib.gs_profile_query.argtypes = [I32, P, P, P]
     lib.gs_profile_query.restype = I32
+    lib.gs_param_floats.argtypes = [I64, I32]
+    lib.gs_param_floats.restype = C.c_size_t
+    lib.gs_params_to_blocked.argtypes = [P, P, I64, I32, P]
+    lib.gs_params_to_blocked.restype = I32
+    lib.gs_params_from_blocked.argtypes = [P, P, I64, I32, P]
+    lib.gs_params_from_blocked.restype = I32
     lib.gs_workspace_bytes.argtypes = [I32, I64, U32, I32, I32]
     lib.gs_workspace_bytes.restype = C.c_size_t
     lib.gs_last_error.restype = C.c_char_p
@@ -134,9 +141,50 @@ def gs_workspace_bytes(which, n=0, pairs=0, W=0, H=0):
     return int(_lib.gs_workspace_bytes(which, n, pairs, W, H))
 
 
+def gs_param_floats(n, sh_degree):
+    return int(_lib.gs_param_floats(n, sh_degree))
+
+
+def _blocked(t, n, sh_degree):
+    """Check that a tensor can hold a blocked parameter array for n Gaussians."""
+    need = gs_param_floats(n, sh_degree)
+    if t is None or t.dtype != torch.float32 or not t.is_contiguous() or t.numel() < need:
+        raise ValueError(f"expected a contiguous float32 tensor of at least {need} floats (blocked layout)")
+    return t
+
+
+def empty_blocked(n, sh_degree, device="cuda", zero=False):
+    """A device tensor of gs_param_floats(n, sh_degree) floats, shaped [groups][P][64]."""
+    P = 11 + 3 * (sh_degree + 1) ** 2
+    groups = max((n + 63) // 64, 1)
+    f = torch.zeros if zero else torch.empty
+    return f((groups, P, 64), dtype=torch.float32, device=device)
+
+
+def to_blocked(planar, sh_degree, out=None, stream=None):
+    """[P][n] device tensor -> blocked layout (gs_params_to_blocked)."""
+    assert planar.dim() == 2 and planar.is_contiguous() and planar.dtype == torch.float32
+    n = planar.shape[1]
+    out = empty_blocked(n, sh_degree, planar.device) if out is None else _blocked(out, n, sh_degree)
+    _check(_lib.gs_params_to_blocked(_ptr(planar), _ptr(out), n, sh_degree, _stream(stream)))
+    return out
+
+
+def from_blocked(blocked, n, sh_degree, out=None, stream=None):
+    """Blocked layout -> [P][n] device tensor (gs_params_from_blocked)."""
+    _blocked(blocked, n, sh_degree)
+    P = 11 + 3 * (sh_degree + 1) ** 2
+    out = torch.empty((P, n), dtype=torch.float32, device=blocked.device) if out is None else out
+    assert out.shape == (P, n) and out.is_contiguous()
+    _check(_lib.gs_params_from_blocked(_ptr(blocked), _ptr(out), n, sh_degree, _stream(stream)))
+    return out
+
+
 def gs_preprocess(params, sh_degree, cam: GsCamera, proj: Proj, ws, stream=None) -> int:
-    """Projection + tile-count scan; returns the pair count (synchronises the stream once)."""
+    """Projection + tile-count scan; returns the pair count (synchronises the stream once).
+    params: blocked layout for proj.n Gaussians."""
     n = proj.n
+    _blocked(params, n, sh_degree)
     scene = GsScene(n, sh_degree, params.data_ptr() if n else None)
     total = C.c_uint32(0)
     _check(_lib.gs_preprocess(C.byref(scene), C.byref(cam), C.byref(proj.struct), C.byref(total), _ptr(ws),
@@ -164,6 +212,8 @@ def gs_loss_l1_dssim(img, target, lambda_dssim, loss_out, dL_dimg, ws, stream=No
 def gs_render_bwd(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam: GsCamera, T_final, n_contrib, dL_dimg,
                   gscreen, gparams, ws, stream=None):
     n = proj.n
+    _blocked(params, n, sh_degree)
+    _blocked(gparams, n, sh_degree)
     scene = GsScene(n, sh_degree, params.data_ptr() if n else None)
     _check(_lib.gs_render_bwd(C.byref(scene), C.byref(proj.struct), _ptr(vals), _ptr(ranges), total_pairs,
                               C.byref(cam),
@@ -171,8 +221,9 @@ def gs_render_bwd(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam:
                               _ptr(ws), ws.numel(), _stream(stream)))
 
 
-def gs_adam_step(params, grads, m, v, sh_degree, lr, beta1, beta2, eps, step, stream=None):
-    n = params.shape[1] if params.dim() == 2 else 0
+def gs_adam_step(params, grads, m, v, n, sh_degree, lr, beta1, beta2, eps, step, stream=None):
+    for t in (params, grads, m, v):
+        _blocked(t, n, sh_degree)
     lr_arr = (C.c_float * 5)(*[float(x) for x in lr])
     _check(_lib.gs_adam_step(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), n, sh_degree, lr_arr, float(beta1),
                              float(beta2), float(eps), int(step), _stream(stream)))
@@ -180,6 +231,8 @@ def gs_adam_step(params, grads, m, v, sh_degree, lr, beta1, beta2, eps, step, st
 
 def gs_render_bwd_adam(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam: GsCamera, T_final,
                        n_contrib, dL_dimg, gscreen, m, v, lr, beta1, beta2, eps, step, ws, stream=None):
+    for t in (params, m, v):
+        _blocked(t, proj.n, sh_degree)
     lr_arr = (C.c_float * 5)(*[float(x) for x in lr])
     _check(_lib.gs_render_bwd_adam(_ptr(params), proj.n, sh_degree, C.byref(proj.struct), _ptr(vals), _ptr(ranges),
                                    total_pairs, C.byref(cam), _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimg),

@@ -15,10 +15,12 @@ DEFAULT_LR = (1.6e-4, 5e-3, 1e-3, 5e-2, 2.5e-3)   # means, log-scales, quaternio
 class Pipeline:
     def __init__(self, params: torch.Tensor, sh_degree: int, width: int, height: int, lam: float = 0.2,
                  lr=DEFAULT_LR, betas=(0.9, 0.999), eps=1e-8):
+        """params: [P][n] float32 device tensor (plane-major); it is copied into the
+        library's blocked layout, in which params, grads, m and v are then kept."""
         assert params.is_cuda and params.dtype == torch.float32 and params.is_contiguous()
-        self.params = params
         self.deg = sh_degree
         self.n = params.shape[1]
+        self.params = gs.to_blocked(params, sh_degree)
         self.W, self.H = width, height
         self.lam, self.lr, self.betas, self.eps = lam, lr, betas, eps
         dev = params.device
@@ -38,11 +40,19 @@ class Pipeline:
         self.loss = torch.zeros(3, dtype=torch.float32, device=dev)
         self.dLdI = torch.empty((3, height, width), dtype=torch.float32, device=dev)
         self.gscreen = torch.empty((9, max(self.n, 1)), dtype=torch.float32, device=dev)
-        self.grads = torch.empty_like(params)
-        self.m = torch.zeros_like(params)
-        self.v = torch.zeros_like(params)
+        self.grads = gs.empty_blocked(self.n, sh_degree, dev, zero=True)
+        self.m = gs.empty_blocked(self.n, sh_degree, dev, zero=True)
+        self.v = gs.empty_blocked(self.n, sh_degree, dev, zero=True)
         self.t = 0
         self.pairs = 0
+
+    def planar(self, blocked: torch.Tensor) -> torch.Tensor:
+        """[P][n] copy of one of the blocked arrays (params, grads, m, v)."""
+        return gs.from_blocked(blocked, self.n, self.deg)
+
+    def set_planar(self, blocked: torch.Tensor, planar: torch.Tensor):
+        """Overwrite one of the blocked arrays from a [P][n] tensor."""
+        gs.to_blocked(planar.to(blocked.device).contiguous(), self.deg, out=blocked)
 
     def _reserve(self, pairs):
         if self.keys.numel() < pairs:
@@ -72,8 +82,8 @@ class Pipeline:
 
     def adam(self):
         self.t += 1
-        gs.gs_adam_step(self.params, self.grads, self.m, self.v, self.deg, self.lr, self.betas[0], self.betas[1],
-                        self.eps, self.t)
+        gs.gs_adam_step(self.params, self.grads, self.m, self.v, self.n, self.deg, self.lr, self.betas[0],
+                        self.betas[1], self.eps, self.t)
 
     def backward_adam(self, cam: gs.GsCamera, target: torch.Tensor):
         """Loss, backward and Adam with the chain and Adam fused (no gradient written)."""

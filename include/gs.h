@@ -26,17 +26,25 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on that stream and returns, except gs_preprocess, which
  *     synchronises the stream once to read the pair count.
- *   - Arrays are planar (structure of arrays), fp32 unless stated otherwise:
- *     [plane][n] per Gaussian, [channel][H][W] per image.
+ *   - Arrays are fp32 unless stated otherwise.  Per-Gaussian parameter arrays
+ *     (params, gradients, Adam moments) use the blocked layout below; other
+ *     per-Gaussian arrays are planar, [plane][n]; images are [channel][H][W].
  *   - Return value: GS_OK or a negative gs_status; gs_last_error() then holds a
  *     message (per thread).  No C++ exception crosses the ABI.  On an argument
  *     error nothing is enqueued and no output is written.
  *
- * Scene parameters, planes of params[P][n], P = 11 + 3 (deg + 1)^2 (14 at SH degree 0,
- * 59 at degree 3):
+ * Scene parameters: P = 11 + 3 (deg + 1)^2 planes (14 at SH degree 0, 59 at degree 3):
  *   0-2 mean x, y, z | 3-5 log-scales | 6-9 quaternion w, x, y, z (need not be unit)
  *   10 opacity logit | 11-13 colour DC r, g, b (colour units, no basis factor)
  *   14 + 3 (k - 1) + ch, k = 1 .. (deg + 1)^2 - 1: spherical-harmonic band coefficients.
+ *
+ * Blocked parameter layout: the Gaussians are taken in groups of 64; a group stores its
+ * P planes one after another, 64 floats each, so parameter p of Gaussian i is at
+ *   ((i / 64) * P + p) * 64 + i % 64
+ * and an array holds gs_param_floats(n, deg) = ceil(n / 64) * 64 * P floats.  The slots of
+ * Gaussians i >= n in the last group are padding: never read as parameters, and left
+ * untouched by every call except gs_params_to_blocked (which zeroes them).  Each group's
+ * parameters are one contiguous stretch, which is what the per-Gaussian passes stream.
  */
 #ifndef GS_H_
 #define GS_H_
@@ -73,7 +81,7 @@ typedef struct gs_camera {
 typedef struct gs_scene {
   int64_t n;            /* number of Gaussians, 0 <= n < 2^31 */
   int32_t sh_degree;    /* 0..3 */
-  const float* params;  /* device, [P][n] */
+  const float* params;  /* device, blocked layout, gs_param_floats(n, sh_degree) floats */
 } gs_scene;
 
 /* Projected per-Gaussian state written by gs_preprocess and read by the later calls.
@@ -152,7 +160,8 @@ int32_t gs_loss_l1_dssim(const float* img, const float* target, int32_t H, int32
  * Part 2, the chain per Gaussian: [GSG] "The covariance chain" (conic -> V -> Sigma -> M ->
  * scale and quaternion, projection off |q|), "Where the position gradient comes from"
  * (mean path and the J(z) covariance path), "Spherical harmonics" (band gradients and the
- * view-direction term), sigmoid.  gparams: [P][n], overwritten (zero for culled Gaussians).
+ * view-direction term), sigmoid.  gparams: blocked layout, every Gaussian's P parameters
+ * overwritten (zero for culled Gaussians); padding untouched.
  * proj, vals, ranges, total_pairs, T_final, n_contrib and ws must be those of the matching
  * forward (ws as that forward left it). */
 int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t* vals, const uint32_t* ranges,
@@ -163,7 +172,8 @@ int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t
 /* Adam, [GSG] Adam section; per-group rates [DR] "From a pixel error back to a quaternion".
  *   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
  *   theta -= lr_group (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
- * params, m, v: [P][n] updated in place; grads: [P][n].  lr: HOST float[5] for the groups
+ * params, m, v: blocked layout, updated in place (padding untouched); grads: blocked layout.
+ * Arrays 16-byte aligned take the vectorised kernel.  lr: HOST float[5] for the groups
  * means, log-scales, quaternion, opacity, colour (DC and bands).  beta1, beta2, eps are host
  * fp64 scalars: 1 - beta and the bias corrections are formed in fp64 and rounded once to
  * fp32 for the kernel.  step t >= 1. */
@@ -172,7 +182,7 @@ int32_t gs_adam_step(float* params, const float* grads, float* m, float* v, int6
 
 /* gs_render_bwd followed by gs_adam_step, fused: the chain applies Adam to each parameter as
  * soon as its gradient is known, so the parameter gradient is never written to memory (it
- * saves two passes over [P][n] floats).  Same arguments and results as the two calls, with
+ * saves two passes over the parameter arrays).  Same arguments and results as the two calls, with
  * params updated in place; gscreen is scratch here: on return its planes 6-8 hold the mean
  * gradient's view-direction term instead of the colour gradients. */
 int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs_proj* proj, const uint32_t* vals,
@@ -180,6 +190,15 @@ int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs
                            const float* T_final, const uint32_t* n_contrib, const float* dL_dimg, float* gscreen,
                            float* m, float* v, const float* lr, double beta1, double beta2, double eps,
                            int32_t step, void* ws, size_t ws_bytes, void* stream);
+
+/* Layout of the per-Gaussian parameter arrays (see the blocked layout above).
+ * gs_param_floats: floats in a blocked array for n Gaussians (0 for bad arguments).
+ * gs_params_to_blocked: planar [P][n] -> blocked, padding zeroed; gs_params_from_blocked:
+ * blocked -> planar [P][n].  Device arrays owned by the caller, not overlapping; the
+ * conversion is enqueued on `stream`. */
+size_t gs_param_floats(int64_t n, int32_t sh_degree);
+int32_t gs_params_to_blocked(const float* planar, float* blocked, int64_t n, int32_t sh_degree, void* stream);
+int32_t gs_params_from_blocked(const float* blocked, float* planar, int64_t n, int32_t sh_degree, void* stream);
 
 /* Workspace sizes, in bytes, for the calls that take one. */
 enum { GS_WS_PREPROCESS = 0, GS_WS_BIN_SORT = 1, GS_WS_LOSS = 2, GS_WS_RENDER = 3 };

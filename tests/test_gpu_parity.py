@@ -83,7 +83,7 @@ def test_backward_small(torch_cuda, oracle, case):
                      pl.grads, pl.ws_render)
     torch.cuda.synchronize()
     gscreen = pl.gscreen[:, :n].cpu().numpy()
-    gparams = pl.grads.cpu().numpy()
+    gparams = pl.planar(pl.grads).cpu().numpy()
     keep = o["gmargin"] >= pu.MARGIN
     print(f"  gaussians excluded by margin: {int((~keep).sum())} of {n}", flush=True)
     for k, name in enumerate(["u", "v", "A", "B", "C", "opacity", "r", "g", "b"]):
@@ -122,7 +122,7 @@ def test_config1_full_step(torch_cuda, oracle):
         g_img = pl.dLdI.cpu().numpy()
         scale = np.abs(ref["dLdI"]).max()
         assert np.abs(g_img - ref["dLdI"]).max() <= 1e-4 * scale
-    gparams = pl.grads.cpu().numpy()
+    gparams = pl.planar(pl.grads).cpu().numpy()
     for name, sl in pu.grad_groups(deg).items():
         pu.check_grad(gparams[sl], ref["gparams"][sl], keep, name=name)
     # one Adam step from zero moments, against the oracle's fp64 Adam on the GPU's gradient
@@ -132,9 +132,9 @@ def test_config1_full_step(torch_cuda, oracle):
     lr = np.array([1.6e-4, 5e-3, 1e-3, 5e-2, 2.5e-3])
     p_ref, m_ref, v_ref = oracle.adam(p0, gparams.astype(np.float64), np.zeros_like(p0), np.zeros_like(p0), deg,
                                       lr, step=1)
-    np.testing.assert_allclose(pl.params.cpu().numpy(), p_ref, rtol=1e-6, atol=1e-7)
-    np.testing.assert_allclose(pl.m.cpu().numpy(), m_ref, rtol=1e-6, atol=1e-12)
-    np.testing.assert_allclose(pl.v.cpu().numpy(), v_ref, rtol=1e-6, atol=1e-14)
+    np.testing.assert_allclose(pl.planar(pl.params).cpu().numpy(), p_ref, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(pl.planar(pl.m).cpu().numpy(), m_ref, rtol=1e-6, atol=1e-12)
+    np.testing.assert_allclose(pl.planar(pl.v).cpu().numpy(), v_ref, rtol=1e-6, atol=1e-14)
     del gs
 
 
@@ -156,11 +156,42 @@ def test_loss_parity(torch_cuda, oracle):
         assert np.abs(gg - g_ref).max() <= 1e-4 * np.abs(g_ref).max()
 
 
-def test_adam_parity(torch_cuda, oracle):
+def _blocked_np(planar):
+    """The blocked layout written out from its definition (numpy), padding NaN."""
+    P, n = planar.shape
+    groups = (n + 63) // 64
+    out = np.full((groups, P, 64), np.nan, np.float32)
+    for i in range(n):
+        out[i // 64, :, i % 64] = planar[:, i]
+    return out
+
+
+@pytest.mark.parametrize("n,deg", [(1, 0), (64, 3), (129, 1), (1003, 2)])
+def test_layout_round_trip(torch_cuda, n, deg):
+    torch = torch_cuda
+    from differentiable_tile_gaussian_amd import gs
+    P = scenes.num_planes(deg)
+    a = np.random.default_rng(n).standard_normal((P, n)).astype(np.float32)
+    b = gs.to_blocked(torch.from_numpy(a).cuda(), deg)
+    torch.cuda.synchronize()
+    assert b.numel() == gs.gs_param_floats(n, deg) == ((n + 63) // 64) * 64 * P
+    want = _blocked_np(a)
+    got = b.cpu().numpy()
+    pad = np.isnan(want)
+    np.testing.assert_array_equal(got[~pad], want[~pad])
+    assert np.all(got[pad] == 0.0)
+    back = gs.from_blocked(b, n, deg).cpu().numpy()
+    np.testing.assert_array_equal(back, a)
+
+
+@pytest.mark.parametrize("aligned", [True, False])
+def test_adam_parity(torch_cuda, oracle, aligned):
+    """gs_adam_step on blocked arrays (the vector kernel when 16-byte aligned, the
+    scalar one otherwise) against the oracle's fp64 Adam; padding is left untouched."""
     torch = torch_cuda
     from differentiable_tile_gaussian_amd import gs
     rng = np.random.default_rng(3)
-    for n, deg in [(1003, 3), (4096, 0), (1, 1)]:
+    for n, deg in [(1003, 3), (4096, 0), (1, 1), (130, 2)]:
         P = scenes.num_planes(deg)
         th = rng.standard_normal((P, n)).astype(np.float32)
         g = rng.standard_normal((P, n)).astype(np.float32)
@@ -168,17 +199,29 @@ def test_adam_parity(torch_cuda, oracle):
         v = (0.01 * rng.random((P, n))).astype(np.float32)
         lr = np.array([1.6e-4, 5e-3, 1e-3, 5e-2, 2.5e-3])
         ref = oracle.adam(th, g, m, v, deg, lr, step=7)
-        T = [torch.from_numpy(a.copy()).cuda() for a in (th, g, m, v)]
-        gs.gs_adam_step(T[0], T[1], T[2], T[3], deg, lr, 0.9, 0.999, 1e-8, 7)
+        nf = gs.gs_param_floats(n, deg)
+        T = []
+        for a in (th, g, m, v):
+            buf = torch.full((nf + 1,), 7.0, dtype=torch.float32, device="cuda")
+            t = buf[:nf] if aligned else buf[1:]
+            gs.to_blocked(torch.from_numpy(a).cuda(), deg, out=t)
+            padding = np.isnan(_blocked_np(a).reshape(-1))
+            t[torch.from_numpy(padding).cuda()] = 7.0     # sentinel in the padding slots
+            T.append(t)
+        gs.gs_adam_step(T[0], T[1], T[2], T[3], n, deg, lr, 0.9, 0.999, 1e-8, 7)
         torch.cuda.synchronize()
+        out = [gs.from_blocked(t, n, deg).cpu().numpy() for t in T]
+        padmask = np.isnan(_blocked_np(th).reshape(-1))
+        for t in (T[0], T[2], T[3]):
+            assert np.all(t.cpu().numpy()[padmask] == 7.0)
         # fp32 rounding is relative to the operands of each update, which can cancel
         m_scale = 0.9 * np.abs(m) + 0.1 * np.abs(g)
         v_scale = 0.999 * np.abs(v) + 0.001 * g * g
-        assert np.all(np.abs(T[2].cpu().numpy() - ref[1]) <= 1e-6 * m_scale + 1e-30)
-        assert np.all(np.abs(T[3].cpu().numpy() - ref[2]) <= 1e-6 * v_scale + 1e-30)
+        assert np.all(np.abs(out[2] - ref[1]) <= 1e-6 * m_scale + 1e-30)
+        assert np.all(np.abs(out[3] - ref[2]) <= 1e-6 * v_scale + 1e-30)
         # one fp32 rounding of theta itself plus a small relative error on the step
         bound = 1.2e-7 * np.abs(ref[0]) + 1e-5 * np.abs(th - ref[0]) + 1e-12
-        assert np.all(np.abs(T[0].cpu().numpy() - ref[0]) <= bound)
+        assert np.all(np.abs(out[0] - ref[0]) <= bound)
 
 
 # ---------------------------------------------------------------- edge cases
@@ -302,7 +345,7 @@ def test_split_path_parity(torch_cuda, oracle, split_tuning, tune, which):
     gscreen = pl.gscreen[:, :s.n].cpu().numpy()
     for k, name in enumerate(["u", "v", "A", "B", "C", "opacity", "r", "g", "b"]):
         pu.check_grad(gscreen[k], o["gscreen"][k], keep, name=name)
-    g = pl.grads.cpu().numpy()
+    g = pl.planar(pl.grads).cpu().numpy()
     for name, sl in pu.grad_groups(deg).items():
         pu.check_grad(g[sl], o["gparams"][sl], keep, name=name)
     stopped = float((o["fwd"]["T"] < 1e-4).mean())
@@ -331,18 +374,18 @@ def test_fused_backward_adam(torch_cuda, oracle, case):
     results = {}
     for mode in ("separate", "fused"):
         pl, c = pu.gpu_forward(s.params, deg, cam)
-        pl.m.copy_(torch.from_numpy(m0))
-        pl.v.copy_(torch.from_numpy(v0))
+        pl.set_planar(pl.m, torch.from_numpy(m0))
+        pl.set_planar(pl.v, torch.from_numpy(v0))
         pl.dLdI.copy_(torch.from_numpy(dLdI))
         if mode == "separate":
             gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI,
                              pl.gscreen, pl.grads, pl.ws_render)
-            gs.gs_adam_step(pl.params, pl.grads, pl.m, pl.v, deg, lr, 0.9, 0.999, 1e-8, 3)
+            gs.gs_adam_step(pl.params, pl.grads, pl.m, pl.v, s.n, deg, lr, 0.9, 0.999, 1e-8, 3)
         else:
             gs.gs_render_bwd_adam(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI,
                                   pl.gscreen, pl.m, pl.v, lr, 0.9, 0.999, 1e-8, 3, pl.ws_render)
         torch.cuda.synchronize()
-        results[mode] = [t.cpu().numpy() for t in (pl.params, pl.m, pl.v)]
+        results[mode] = [pl.planar(t).cpu().numpy() for t in (pl.params, pl.m, pl.v)]
     th0 = s.params.astype(np.float64)
     for a, b in zip(results["separate"], results["fused"]):
         np.testing.assert_allclose(b, a, rtol=2e-6, atol=1e-9)
