@@ -134,7 +134,8 @@ def count_evals(pl, torch):
 
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, if
-    the kernel's source is unchanged since the counters were taken; otherwise None."""
+    the sources the kernel is built from are unchanged since the counters were taken
+    (sha256 over their contents, in the listed order); otherwise None."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "pmc_traffic_train_step_6m_1080p.md")
     if not os.path.exists(path):
@@ -143,11 +144,13 @@ def measured_traffic(kernel):
         parts = line.split()
         if len(parts) >= 2 and parts[0] == "traffic" and parts[1] == kernel:
             kv = dict(p.split("=", 1) for p in parts[2:])
-            src = os.path.join(ROOT, kv["source"])
-            if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["sha256"]:
+            h = hashlib.sha256()
+            for src in kv["sources"].split(","):
+                h.update(open(os.path.join(ROOT, src), "rb").read())
+            if h.hexdigest() != kv["sha256"]:
                 return None
-            return (float(kv["fetch_kib"]) * float(kv["fetch_scale"]) +
-                    float(kv["write_kib"]) * float(kv["write_scale"])) * 1024.0
+            return round((float(kv["fetch_kib"]) * float(kv["fetch_scale"]) +
+                          float(kv["write_kib"]) * float(kv["write_scale"])) * 1024.0)
     return None
 
 
