@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=WORKLOAD_CFG, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split", default=None,
+                    help="FIRST,CHUNK: pairs every tile walks in one block, and the chunk size of the "
+                         "parallel walk of longer lists (library defaults if omitted)")
     ap.add_argument("--stage-report", action="store_true", help="also print per-stage times to stderr")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy a 1 GiB buffer three times (a plain copy of known size, the "
@@ -187,6 +190,11 @@ def main():
     from differentiable_tile_gaussian_amd.pipeline import Pipeline
 
     torch.cuda.set_device(0)
+    if args.split:
+        first, chunk = (int(x) for x in args.split.split(","))
+        gs.gs_set_tuning(gs.GS_TUNE_SPLIT_FIRST, first)
+        gs.gs_set_tuning(gs.GS_TUNE_SPLIT_CHUNK, chunk)
+    split = [gs.gs_get_tuning(gs.GS_TUNE_SPLIT_FIRST), gs.gs_get_tuning(gs.GS_TUNE_SPLIT_CHUNK)]
     t_setup = time.perf_counter()
     wl = scenes.CONFIGS[args.workload]()
     cams = [gs.make_camera(c) for c in wl.cameras]
@@ -257,7 +265,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "gaussians": n, "sh_degree": deg, "image": [cam0.width, cam0.height],
-                   "cameras": len(cams), "step": "preprocess+sort+fwd+loss+bwd+chain+adam (fused)", "parallelism": "none"},
+                   "cameras": len(cams), "step": "preprocess+sort+fwd+loss+bwd+chain+adam (fused)", "parallelism": "none",
+                   "blend_split": split},
         "evals_per_s": round((ev_f + ev_b) / t_fb, 1),
         "evals_per_step": {"fwd": ev_f // args.steps, "bwd": ev_b // args.steps},
         "stage_ms": {k: round(float(stage[:, i].mean()), 4) for i, k in enumerate(StageTimer.NAMES)},

@@ -55,6 +55,12 @@
 namespace gsk {
 namespace {
 
+// Pixel of thread tid within its 16x16 tile: each wave of 64 threads covers one 8x8
+// quadrant (a squarer footprint than four rows, so the pixels of a wave stop after
+// more similar numbers of pairs and fewer lanes idle while the wave walks on).
+__device__ inline int pixel_x(int tid) { return ((tid >> 6) & 1) * 8 + (tid & 7); }
+__device__ inline int pixel_y(int tid) { return (tid >> 7) * 8 + ((tid >> 3) & 7); }
+
 constexpr int kBatch = 256;
 constexpr float kAlphaMin = 1.0f / 255.0f;
 constexpr float kAlphaCap = 0.99f;
@@ -268,8 +274,8 @@ __global__ void __launch_bounds__(256) render_fwd_kernel(const float4* __restric
   __shared__ uint32_t s_slot, s_first, s_nch;
   const int tile = int(ws.order[blockIdx.x]);
   const int tid = threadIdx.x;
-  const int px = (tile % tx) * kTile + (tid & (kTile - 1));
-  const int py = (tile / tx) * kTile + (tid >> 4);
+  const int px = (tile % tx) * kTile + pixel_x(tid);
+  const int py = (tile / tx) * kTile + pixel_y(tid);
   const bool inside = px < W && py < H;
   const uint32_t start = ranges[tile];
   const int n = int(ranges[num_tiles + tile] - start);
@@ -320,8 +326,8 @@ __global__ void __launch_bounds__(256) split_chunk_kernel(const float4* __restri
   const uint32_t slot = sc.x, c = sc.y;
   const int tile = int(ws.slot_tile[slot]);
   const int tid = threadIdx.x;
-  const int px = (tile % tx) * kTile + (tid & (kTile - 1));
-  const int py = (tile / tx) * kTile + (tid >> 4);
+  const int px = (tile % tx) * kTile + pixel_x(tid);
+  const int py = (tile / tx) * kTile + pixel_y(tid);
   const uint32_t start = ranges[tile];
   const int n = int(ranges[num_tiles + tile] - start);
   const int lo = first + int(c) * chunk, hi = min(lo + chunk, n);
@@ -404,8 +410,8 @@ __global__ void __launch_bounds__(256) split_rewalk_kernel(const float4* __restr
   const bool need = ws.stopc[so] == int32_t(c);
   if (__syncthreads_count(need) == 0) return;
   const int tile = int(ws.slot_tile[slot]);
-  const int px = (tile % tx) * kTile + (tid & (kTile - 1));
-  const int py = (tile / tx) * kTile + (tid >> 4);
+  const int px = (tile % tx) * kTile + pixel_x(tid);
+  const int py = (tile / tx) * kTile + pixel_y(tid);
   const uint32_t start = ranges[tile];
   const int n = int(ranges[num_tiles + tile] - start);
   const int lo = first + int(c) * chunk, hi = min(lo + chunk, n);
@@ -436,8 +442,8 @@ __global__ void __launch_bounds__(256) split_finalize_kernel(SplitWs ws, int tx,
   if (slot >= ws.counters[0]) return;
   const int tid = threadIdx.x;
   const int tile = int(ws.slot_tile[slot]);
-  const int px = (tile % tx) * kTile + (tid & (kTile - 1));
-  const int py = (tile / tx) * kTile + (tid >> 4);
+  const int px = (tile % tx) * kTile + pixel_x(tid);
+  const int py = (tile / tx) * kTile + pixel_y(tid);
   const size_t so = size_t(slot) * 256 + tid;
   const int32_t stop = ws.stopc[so];
   const float4 f = ws.fin4[so];
@@ -656,8 +662,8 @@ __global__ void __launch_bounds__(256) render_bwd_kernel(const float4* __restric
   __shared__ BwdLds L;
   const int tile = int(ws.order[blockIdx.x]);
   const int tid = threadIdx.x;
-  const int px = (tile % tx) * kTile + (tid & (kTile - 1));
-  const int py = (tile / tx) * kTile + (tid >> 4);
+  const int px = (tile % tx) * kTile + pixel_x(tid);
+  const int py = (tile / tx) * kTile + pixel_y(tid);
   const bool inside = px < W && py < H;
   const uint32_t start = ranges[tile];
   PixelBwd s{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0};
@@ -698,8 +704,8 @@ __global__ void __launch_bounds__(256) split_bwd_kernel(const float4* __restrict
   const uint32_t slot = sc.x, c = sc.y;
   const int tile = int(ws.slot_tile[slot]);
   const int tid = threadIdx.x;
-  const int px = (tile % tx) * kTile + (tid & (kTile - 1));
-  const int py = (tile / tx) * kTile + (tid >> 4);
+  const int px = (tile % tx) * kTile + pixel_x(tid);
+  const int py = (tile / tx) * kTile + pixel_y(tid);
   const bool inside = px < W && py < H;
   const uint32_t start = ranges[tile];
   const int len = int(ranges[num_tiles + tile] - start);
@@ -731,7 +737,7 @@ __global__ void zero_f32_kernel(float* __restrict__ p, int64_t count) {
 }
 
 int g_first = 2048;
-int g_chunk = 1024;
+int g_chunk = 512;
 
 }  // namespace
 

@@ -207,7 +207,7 @@ size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t
 /* Tuning of the blend's work split (process-wide; set before sizing workspaces, and not between a
  * forward and its backward).  Every tile's first GS_TUNE_SPLIT_FIRST pairs are walked by one
  * block; a tile with pixels still unfinished then has its remaining pairs walked in parallel
- * chunks of GS_TUNE_SPLIT_CHUNK pairs.  Values: multiples of 4 in [4, 2^24]; defaults 2048, 1024.
+ * chunks of GS_TUNE_SPLIT_CHUNK pairs.  Values: multiples of 4 in [4, 2^24]; defaults 2048, 512.
  * The results do not depend on these values beyond rounding. */
 enum { GS_TUNE_SPLIT_FIRST = 0, GS_TUNE_SPLIT_CHUNK = 1 };
 int32_t gs_set_tuning(int32_t key, int64_t value);
