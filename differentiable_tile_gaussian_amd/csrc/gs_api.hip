@@ -100,7 +100,7 @@ int64_t gs_get_tuning(int32_t key) {
 size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H) {
   switch (which_call) {
     case GS_WS_PREPROCESS: return gsk::scan_ws_bytes(n < 0 ? 0 : n) + 256;
-    case GS_WS_BIN_SORT: return gsk::bin_sort_ws_bytes(pairs, 0);
+    case GS_WS_BIN_SORT: return gsk::bin_sort_ws_bytes(n < 0 ? 0 : n, pairs);
     case GS_WS_LOSS: return (W > 0 && H > 0) ? gsk::loss_ws_bytes(H, W) : 0;
     case GS_WS_RENDER: return (W > 0 && H > 0) ? gsk::render_ws_bytes(W, H, pairs) : 0;
     default: return 0;
@@ -136,13 +136,13 @@ int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out,
   return GS_OK;
 }
 
-int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32_t total_pairs, uint64_t* keys,
+int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32_t total_pairs, uint32_t* keys,
                     uint32_t* vals, uint32_t capacity, uint32_t* ranges, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   int32_t st;
   if (n < 0 || n >= (int64_t(1) << 31)) return fail(GS_ERR_INVALID_ARG, "n out of range");
   if ((st = check_camera(cam)) != GS_OK) return st;
-  if ((st = check_proj(proj, n, true)) != GS_OK) return st;
+  if ((st = check_proj(proj, n, false)) != GS_OK) return st;
   if (!ranges) return fail(GS_ERR_INVALID_ARG, "ranges is null");
   if (total_pairs > 0 && (!keys || !vals)) return fail(GS_ERR_INVALID_ARG, "keys or vals is null");
   if (total_pairs > 0 && n == 0) return fail(GS_ERR_INVALID_ARG, "pairs without Gaussians");

@@ -46,8 +46,8 @@ hipError_t launch_scan_u32(const uint32_t* in, uint32_t* out, int64_t n, uint64_
                            hipStream_t s);
 
 // ---- sort.hip
-size_t bin_sort_ws_bytes(uint32_t pairs, int num_tiles);
-hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uint32_t pairs, uint64_t* keys,
+size_t bin_sort_ws_bytes(int64_t n, uint32_t pairs);
+hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uint32_t pairs, uint32_t* keys,
                            uint32_t* vals, uint32_t* ranges, void* ws, hipStream_t s);
 
 // ---- render.hip

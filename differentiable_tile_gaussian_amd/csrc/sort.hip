@@ -1,17 +1,30 @@
-// Duplicate-with-keys, depth sort and tile ranges ([GSG] "Why tiling, and the
-// five stages": scatter, sort, segment boundaries; ties broken by Gaussian id).
+// Binning and depth sort ([GSG] "Why tiling, and the five stages": scatter, sort,
+// segment boundaries; ties broken by Gaussian id).  The pairs end up ordered by
+// tile, then depth, then Gaussian id, built in three steps:
 //
-// emit_keys      one thread per pair: binary search of the pair index in the
-//                tile-count prefix sum finds the owning Gaussian, the offset within
-//                its rectangle gives the tile (row-major).  Coalesced 12-byte writes.
-// radix passes   stable LSD radix sort of (u64 key, u32 value) on the key's
-//                significant bits, 8 bits per pass, reduce-then-scan:
-//                  upsweep   per-block digit histogram (LDS atomics)
-//                  scan      exclusive prefix over the digit-major [256][blocks] table
-//                  downsweep stable in-block ranking with 64-lane ballots (no
-//                            match-any on CDNA: 8 ballots give each lane its peer mask),
-//                            local reorder through LDS, coalesced scatter.
-// tile_ranges    first / one-past-last pair of each tile.
+//   depth sort    the visible Gaussians (tile count > 0), in id order, are sorted by
+//                 the bits of their (positive) depth with a stable LSD radix sort;
+//                 the first pass also compacts them, so later passes only see the
+//                 visible ones.  Result: visible Gaussian ids by (depth, id).
+//   emit          their tile counts, in that order, are prefix-summed; one thread
+//                 per pair finds its Gaussian by binary search in the sums and
+//                 writes (tile id, Gaussian id): the pairs of each Gaussian are
+//                 consecutive and the Gaussians are in (depth, id) order.
+//   tile sort     a stable LSD radix sort of the pairs by tile id, so within a
+//                 tile they keep the (depth, id) order.
+//   tile_ranges   first / one-past-last pair of each tile.
+//
+// Radix passes use 8-bit digits, reduce-then-scan:
+//   upsweep   per-block digit histogram (LDS atomics)
+//   scan      exclusive prefix over the digit-major [256][blocks] table
+//   downsweep stable in-block ranking with 64-lane ballots (no match-any on CDNA:
+//             8 ballots give each lane its peer mask), local reorder through LDS,
+//             coalesced scatter.
+// Sorting the Gaussians by depth once, instead of every pair by a 64-bit (tile, depth)
+// key, replaces six passes over 12-byte pairs by four passes over the visible
+// Gaussians (about 40 % of them at the orbit cameras) and two over 8-byte pairs.
+#include <algorithm>
+
 #include "gs_internal.h"
 #include "profile.h"
 
@@ -20,62 +33,82 @@ namespace {
 
 constexpr int kSortThreads = 256;
 constexpr int kSortItems = 16;
-constexpr int kSortTile = kSortThreads * kSortItems;   // 4096 pairs per block
+constexpr int kSortTile = kSortThreads * kSortItems;   // 4096 items per block
 constexpr int kRadix = 256;
+constexpr int kDepthPasses = 4;                         // 31 significant bits of a positive float
 
-__global__ void __launch_bounds__(256) emit_keys_kernel(const uint32_t* __restrict__ offs, int n,
-                                                         const float* __restrict__ depth,
-                                                         const uint2* __restrict__ rect, uint32_t pairs, int tx,
-                                                         uint64_t* __restrict__ keys, uint32_t* __restrict__ vals) {
-  const uint32_t p = blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= pairs) return;
-  // largest g with offs[g] <= p (offs is non-decreasing, offs[n] = pairs > p)
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (offs[mid] <= p) lo = mid; else hi = mid - 1;
+// Where a radix pass reads its items from.
+enum Source {
+  kFromKeys = 0,      // keys[idx], vals[idx], idx < count (count on the device if count_dev)
+  kFromDepth = 1      // depth bits of Gaussian idx, value idx; only Gaussians with tiles[idx] > 0
+};
+
+struct PassIn {
+  const uint32_t* keys;
+  const uint32_t* vals;
+  const float* depth;
+  const uint32_t* tiles;
+  uint32_t count;
+  const uint32_t* count_dev;
+};
+
+template <int SRC>
+__device__ inline bool load_item(const PassIn& in, uint32_t count, uint32_t idx, uint32_t& key, uint32_t& val) {
+  if (idx >= count) return false;
+  if (SRC == kFromDepth) {
+    if (in.tiles[idx] == 0u) return false;
+    key = __float_as_uint(in.depth[idx]);
+    val = idx;
+  } else {
+    key = in.keys[idx];
+    val = in.vals[idx];
   }
-  const int g = lo;
-  const uint32_t j = p - offs[g];
-  const uint2 r = rect[g];
-  const uint32_t x0 = r.x & 0xffffu, y0 = r.x >> 16, x1 = r.y & 0xffffu;
-  const uint32_t w = x1 - x0 + 1;
-  const uint32_t tile = (y0 + j / w) * uint32_t(tx) + (x0 + j % w);
-  keys[p] = (uint64_t(tile) << 32) | uint64_t(__float_as_uint(depth[g]));
-  vals[p] = uint32_t(g);
+  return true;
 }
 
-__global__ void __launch_bounds__(kSortThreads) radix_upsweep_kernel(const uint64_t* __restrict__ keys,
-                                                                      uint32_t pairs, int shift, int nb,
+__device__ inline uint32_t pass_count(const PassIn& in) { return in.count_dev ? *in.count_dev : in.count; }
+
+template <int SRC>
+__global__ void __launch_bounds__(kSortThreads) radix_upsweep_kernel(PassIn in, int shift, int nb,
                                                                       uint32_t* __restrict__ hist) {
   __shared__ uint32_t s_hist[kRadix];
   s_hist[threadIdx.x] = 0u;
   __syncthreads();
+  const uint32_t count = pass_count(in);
   const uint32_t base = blockIdx.x * kSortTile;
+  if (base < count) {
 #pragma unroll 4
-  for (int k = 0; k < kSortItems; ++k) {
-    const uint32_t idx = base + k * kSortThreads + threadIdx.x;
-    if (idx < pairs) atomicAdd(&s_hist[uint32_t(keys[idx] >> shift) & 0xffu], 1u);
+    for (int k = 0; k < kSortItems; ++k) {
+      uint32_t key = 0, val = 0;
+      if (load_item<SRC>(in, count, base + k * kSortThreads + threadIdx.x, key, val))
+        atomicAdd(&s_hist[(key >> shift) & 0xffu], 1u);
+    }
   }
   __syncthreads();
   hist[threadIdx.x * nb + blockIdx.x] = s_hist[threadIdx.x];
 }
 
+// hist_scan has kRadix * nb + 1 entries, the last one the total: with kFromDepth
+// that is the number of visible Gaussians, which block 0 stores to *count_out.
+template <int SRC>
 __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
-    const uint64_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, uint32_t pairs, int shift, int nb,
-    const uint32_t* __restrict__ hist, const uint32_t* __restrict__ hist_scan, uint64_t* __restrict__ keys_out,
-    uint32_t* __restrict__ vals_out) {
-  __shared__ uint64_t s_keys[kSortTile];
+    PassIn in, int shift, int nb, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ hist_scan,
+    uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint32_t* __restrict__ count_out) {
+  __shared__ uint32_t s_keys[kSortTile];
   __shared__ uint32_t s_vals[kSortTile];
   __shared__ uint32_t s_wave_cnt[kSortThreads / 64][kRadix];
-  __shared__ uint32_t s_run[kRadix];      // pairs of each digit already placed in this block
+  __shared__ uint32_t s_run[kRadix];      // items of each digit already placed in this block
   __shared__ uint32_t s_local[kRadix];    // block-local start of each digit
   __shared__ uint32_t s_global[kRadix];   // global start of (digit, this block)
   __shared__ uint32_t s_wtot[kSortThreads / 64];
 
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid >> 6;
+  if (count_out && blockIdx.x == 0 && tid == 0) *count_out = hist_scan[kRadix * nb];
+  const uint32_t count = pass_count(in);
   const uint32_t base = blockIdx.x * kSortTile;
+  if (base >= count) return;   // uniform per block
   // digit counts of this block and their block-local exclusive prefix
+  uint32_t block_total;
   {
     const uint32_t cnt = hist[tid * nb + blockIdx.x];
     s_global[tid] = hist_scan[tid * nb + blockIdx.x];
@@ -88,7 +121,11 @@ __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
     if (lane == 63) s_wtot[wave] = v;
     __syncthreads();
     uint32_t pre = 0;
-    for (int w = 0; w < wave; ++w) pre += s_wtot[w];
+    block_total = 0;
+    for (int w = 0; w < kSortThreads / 64; ++w) {
+      if (w < wave) pre += s_wtot[w];
+      block_total += s_wtot[w];
+    }
     s_local[tid] = pre + v - cnt;
     s_run[tid] = 0u;
     for (int w = 0; w < kSortThreads / 64; ++w) s_wave_cnt[w][tid] = 0u;
@@ -96,15 +133,9 @@ __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
   __syncthreads();
   const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
   for (int r = 0; r < kSortItems; ++r) {
-    const uint32_t idx = base + r * kSortThreads + tid;
-    const bool valid = idx < pairs;
-    uint64_t key = 0;
-    uint32_t val = 0, d = 0;
-    if (valid) {
-      key = keys_in[idx];
-      val = vals_in[idx];
-      d = uint32_t(key >> shift) & 0xffu;
-    }
+    uint32_t key = 0, val = 0;
+    const bool valid = load_item<SRC>(in, count, base + r * kSortThreads + tid, key, val);
+    const uint32_t d = valid ? (key >> shift) & 0xffu : 0u;
     // lanes of this wave holding the same digit
     uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -133,14 +164,46 @@ __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
     }
     __syncthreads();
   }
-  const uint32_t count = pairs - base < uint32_t(kSortTile) ? pairs - base : uint32_t(kSortTile);
-  for (uint32_t k = tid; k < count; k += kSortThreads) {
-    const uint64_t key = s_keys[k];
-    const uint32_t d = uint32_t(key >> shift) & 0xffu;
+  for (uint32_t k = tid; k < block_total; k += kSortThreads) {
+    const uint32_t key = s_keys[k];
+    const uint32_t d = (key >> shift) & 0xffu;
     const uint32_t dst = s_global[d] + (k - s_local[d]);
     keys_out[dst] = key;
     vals_out[dst] = s_vals[k];
   }
+}
+
+// Tile counts of the depth-sorted visible Gaussians (zero past the visible count).
+__global__ void __launch_bounds__(256) gather_counts_kernel(const uint32_t* __restrict__ sorted_ids,
+                                                             const uint32_t* __restrict__ n_vis,
+                                                             const uint32_t* __restrict__ tiles, int n,
+                                                             uint32_t* __restrict__ counts) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n) return;
+  counts[r] = uint32_t(r) < *n_vis ? tiles[sorted_ids[r]] : 0u;
+}
+
+// One thread per pair: the Gaussian (in depth order) that owns it, and its tile.
+__global__ void __launch_bounds__(256) emit_pairs_kernel(const uint32_t* __restrict__ pos,
+                                                          const uint32_t* __restrict__ n_vis,
+                                                          const uint32_t* __restrict__ sorted_ids,
+                                                          const uint2* __restrict__ rect, uint32_t pairs, int tx,
+                                                          uint32_t* __restrict__ keys, uint32_t* __restrict__ vals) {
+  const uint32_t p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= pairs) return;
+  // largest r with pos[r] <= p; pos is strictly increasing over the visible Gaussians
+  int lo = 0, hi = int(*n_vis) - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pos[mid] <= p) lo = mid; else hi = mid - 1;
+  }
+  const uint32_t g = sorted_ids[lo];
+  const uint32_t j = p - pos[lo];
+  const uint2 r = rect[g];
+  const uint32_t x0 = r.x & 0xffffu, y0 = r.x >> 16, x1 = r.y & 0xffffu;
+  const uint32_t w = x1 - x0 + 1;
+  keys[p] = (y0 + j / w) * uint32_t(tx) + (x0 + j % w);
+  vals[p] = g;
 }
 
 __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t count, uint32_t value) {
@@ -148,13 +211,14 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t count, uint32_
   if (i < count) p[i] = value;
 }
 
-__global__ void __launch_bounds__(256) tile_ranges_kernel(const uint64_t* __restrict__ keys, uint32_t pairs,
+__global__ void __launch_bounds__(256) tile_ranges_kernel(const uint32_t* __restrict__ tile_of_pair, uint32_t pairs,
                                                            int num_tiles, uint32_t* __restrict__ ranges) {
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= pairs) return;
-  const uint32_t t = uint32_t(keys[i] >> 32);
-  if (i == 0 || uint32_t(keys[i - 1] >> 32) != t) ranges[t] = i;
-  if (i == pairs - 1 || uint32_t(keys[i + 1] >> 32) != t) ranges[num_tiles + t] = i + 1;
+  const uint32_t t = tile_of_pair[i];
+  if (t >= uint32_t(num_tiles)) return;   // only if total_pairs disagrees with the tile counts
+  if (i == 0 || tile_of_pair[i - 1] != t) ranges[t] = i;
+  if (i == pairs - 1 || tile_of_pair[i + 1] != t) ranges[num_tiles + t] = i + 1;
 }
 
 inline int bits_for(uint32_t max_value) {
@@ -163,42 +227,71 @@ inline int bits_for(uint32_t max_value) {
   return b;
 }
 
+inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
 struct SortWs {
-  uint64_t* keys_alt;
-  uint32_t* vals_alt;
-  uint32_t* hist;
-  uint32_t* hist_scan;
+  uint32_t *dk[2], *dv[2];      // depth sort ping-pong, n each
+  uint32_t* counts;             // n
+  uint32_t* pos;                // n + 1
+  uint32_t *keys_alt, *vals_alt;   // pairs each
+  uint32_t *hist, *hist_scan;   // kRadix * nb (+ 1)
   uint64_t* total64;
+  uint32_t* n_vis;
   void* scan_ws;
 };
 
-inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+int blocks_for(int64_t items) { return int(div_up(items > 0 ? items : 1, kSortTile)); }
 
-SortWs carve(void* ws, uint32_t pairs) {
-  const int nb = int(div_up(pairs > 0 ? pairs : 1, kSortTile));
+// Carves the workspace; returns its size (w may be null to only size it).
+size_t carve(void* ws, int64_t n, uint32_t pairs, SortWs* w) {
+  const int nb = std::max(blocks_for(n), blocks_for(pairs));
   const int64_t hist_n = int64_t(kRadix) * nb;
+  const size_t sn = align256(size_t(n) * 4), sp = align256(size_t(pairs) * 4);
+  size_t off = 0;
   char* p = static_cast<char*>(ws);
-  SortWs w;
-  w.keys_alt = reinterpret_cast<uint64_t*>(p); p += align256(size_t(pairs) * 8);
-  w.vals_alt = reinterpret_cast<uint32_t*>(p); p += align256(size_t(pairs) * 4);
-  w.hist = reinterpret_cast<uint32_t*>(p); p += align256(size_t(hist_n) * 4);
-  w.hist_scan = reinterpret_cast<uint32_t*>(p); p += align256(size_t(hist_n + 1) * 4);
-  w.total64 = reinterpret_cast<uint64_t*>(p); p += 256;
-  w.scan_ws = p;
-  return w;
+  auto take = [&](size_t bytes) {
+    char* r = p ? p + off : nullptr;
+    off += align256(bytes);
+    return reinterpret_cast<uint32_t*>(r);
+  };
+  SortWs t;
+  for (int k = 0; k < 2; ++k) {
+    t.dk[k] = take(sn);
+    t.dv[k] = take(sn);
+  }
+  t.counts = take(sn);
+  t.pos = take(size_t(n + 1) * 4);
+  t.keys_alt = take(sp);
+  t.vals_alt = take(sp);
+  t.hist = take(size_t(hist_n) * 4);
+  t.hist_scan = take(size_t(hist_n + 1) * 4);
+  t.total64 = reinterpret_cast<uint64_t*>(take(8));
+  t.n_vis = take(4);
+  t.scan_ws = take(scan_ws_bytes(std::max<int64_t>(hist_n, n)));
+  if (w) *w = t;
+  return off;
+}
+
+template <int SRC>
+hipError_t radix_pass(const PassIn& in, int nb, int shift, const SortWs& w, uint32_t* keys_out,
+                      uint32_t* vals_out, uint32_t* count_out, hipStream_t s) {
+  {
+    GSK_PROF("radix_upsweep", s);
+    radix_upsweep_kernel<SRC><<<nb, kSortThreads, 0, s>>>(in, shift, nb, w.hist);
+  }
+  hipError_t e = launch_scan_u32(w.hist, w.hist_scan, int64_t(kRadix) * nb, w.total64, w.scan_ws, s);
+  if (e != hipSuccess) return e;
+  GSK_PROF("radix_downsweep", s);
+  radix_downsweep_kernel<SRC><<<nb, kSortThreads, 0, s>>>(in, shift, nb, w.hist, w.hist_scan, keys_out, vals_out,
+                                                          count_out);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-size_t bin_sort_ws_bytes(uint32_t pairs, int num_tiles) {
-  (void)num_tiles;
-  const int nb = int(div_up(pairs > 0 ? pairs : 1, kSortTile));
-  const int64_t hist_n = int64_t(kRadix) * nb;
-  return align256(size_t(pairs) * 8) + align256(size_t(pairs) * 4) + align256(size_t(hist_n) * 4) +
-         align256(size_t(hist_n + 1) * 4) + 256 + align256(scan_ws_bytes(hist_n));
-}
+size_t bin_sort_ws_bytes(int64_t n, uint32_t pairs) { return carve(nullptr, n, pairs, nullptr); }
 
-hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uint32_t pairs, uint64_t* keys,
+hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uint32_t pairs, uint32_t* keys,
                            uint32_t* vals, uint32_t* ranges, void* ws, hipStream_t s) {
   const int tx = tiles_x(cam), ty = tiles_y(cam);
   const int num_tiles = tx * ty;
@@ -207,37 +300,49 @@ hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uin
     fill_u32_kernel<<<div_up(2 * int64_t(num_tiles), 256), 256, 0, s>>>(ranges, 2 * int64_t(num_tiles), 0u);
   }
   if (pairs == 0) return hipGetLastError();
-  SortWs w = carve(ws, pairs);
-  // significant key bits: 32 depth bits + enough for the largest tile id
-  const int key_bits = 32 + bits_for(uint32_t(num_tiles - 1));
-  const int passes = (key_bits + 7) / 8;
-  // emit into the buffer that makes the last pass land in keys/vals
-  uint64_t* k_src = (passes & 1) ? w.keys_alt : keys;
-  uint32_t* v_src = (passes & 1) ? w.vals_alt : vals;
-  uint64_t* k_dst = (passes & 1) ? keys : w.keys_alt;
-  uint32_t* v_dst = (passes & 1) ? vals : w.vals_alt;
+  SortWs w;
+  carve(ws, n, pairs, &w);
+  hipError_t e;
+
+  // 1. visible Gaussians by (depth, id): the first pass compacts, the rest ping-pong
+  const int nbg = blocks_for(n);
   {
-    GSK_PROF("emit_keys", s);
-    emit_keys_kernel<<<div_up(pairs, 256), 256, 0, s>>>(proj.offs, n, proj.depth,
-                                                        reinterpret_cast<const uint2*>(proj.rect), pairs, tx, k_src,
-                                                        v_src);
+    PassIn in{nullptr, nullptr, proj.depth, proj.tiles, uint32_t(n), nullptr};
+    if ((e = radix_pass<kFromDepth>(in, nbg, 0, w, w.dk[0], w.dv[0], w.n_vis, s)) != hipSuccess) return e;
   }
-  const int nb = int(div_up(pairs, kSortTile));
-  const int64_t hist_n = int64_t(kRadix) * nb;
-  for (int pass = 0; pass < passes; ++pass) {
-    const int shift = 8 * pass;
-    {
-      GSK_PROF("radix_upsweep", s);
-      radix_upsweep_kernel<<<nb, kSortThreads, 0, s>>>(k_src, pairs, shift, nb, w.hist);
-    }
-    hipError_t e = launch_scan_u32(w.hist, w.hist_scan, hist_n, w.total64, w.scan_ws, s);
-    if (e != hipSuccess) return e;
-    {
-      GSK_PROF("radix_downsweep", s);
-      radix_downsweep_kernel<<<nb, kSortThreads, 0, s>>>(k_src, v_src, pairs, shift, nb, w.hist, w.hist_scan, k_dst,
-                                                         v_dst);
-    }
-    uint64_t* tk = k_src; k_src = k_dst; k_dst = tk;
+  for (int pass = 1; pass < kDepthPasses; ++pass) {
+    const int src = (pass - 1) & 1;
+    PassIn in{w.dk[src], w.dv[src], nullptr, nullptr, 0u, w.n_vis};
+    if ((e = radix_pass<kFromKeys>(in, nbg, 8 * pass, w, w.dk[src ^ 1], w.dv[src ^ 1], nullptr, s)) != hipSuccess)
+      return e;
+  }
+  const uint32_t* sorted_ids = w.dv[(kDepthPasses - 1) & 1];
+
+  // 2. pairs in that order: (tile, Gaussian)
+  {
+    GSK_PROF("gather_counts", s);
+    gather_counts_kernel<<<div_up(n, 256), 256, 0, s>>>(sorted_ids, w.n_vis, proj.tiles, n, w.counts);
+  }
+  if ((e = launch_scan_u32(w.counts, w.pos, n, w.total64, w.scan_ws, s)) != hipSuccess) return e;
+  const int tile_passes = (bits_for(uint32_t(num_tiles - 1)) + 7) / 8;
+  // emit into the buffer that makes the last tile pass land in keys / vals
+  uint32_t* k_src = (tile_passes & 1) ? w.keys_alt : keys;
+  uint32_t* v_src = (tile_passes & 1) ? w.vals_alt : vals;
+  uint32_t* k_dst = (tile_passes & 1) ? keys : w.keys_alt;
+  uint32_t* v_dst = (tile_passes & 1) ? vals : w.vals_alt;
+  {
+    GSK_PROF("emit_pairs", s);
+    emit_pairs_kernel<<<div_up(pairs, 256), 256, 0, s>>>(w.pos, w.n_vis, sorted_ids,
+                                                         reinterpret_cast<const uint2*>(proj.rect), pairs, tx, k_src,
+                                                         v_src);
+  }
+
+  // 3. stable sort of the pairs by tile
+  const int nbp = blocks_for(pairs);
+  for (int pass = 0; pass < tile_passes; ++pass) {
+    PassIn in{k_src, v_src, nullptr, nullptr, pairs, nullptr};
+    if ((e = radix_pass<kFromKeys>(in, nbp, 8 * pass, w, k_dst, v_dst, nullptr, s)) != hipSuccess) return e;
+    uint32_t* tk = k_src; k_src = k_dst; k_dst = tk;
     uint32_t* tv = v_src; v_src = v_dst; v_dst = tv;
   }
   {

@@ -29,7 +29,7 @@ class Pipeline:
         tx, ty = (width + 15) // 16, (height + 15) // 16
         self.num_tiles = tx * ty
         self.ranges = torch.empty((2, self.num_tiles), dtype=torch.int32, device=dev)
-        self.keys = torch.empty(0, dtype=torch.int64, device=dev)
+        self.keys = torch.empty(0, dtype=torch.int32, device=dev)
         self.vals = torch.empty(0, dtype=torch.int32, device=dev)
         self.ws_sort = torch.empty(0, dtype=torch.uint8, device=dev)
         self.rgb = torch.empty((3, height, width), dtype=torch.float32, device=dev)
@@ -57,7 +57,7 @@ class Pipeline:
     def _reserve(self, pairs):
         if self.keys.numel() < pairs:
             cap = int(pairs * 1.25) + 1024
-            self.keys = torch.empty(cap, dtype=torch.int64, device=self.params.device)
+            self.keys = torch.empty(cap, dtype=torch.int32, device=self.params.device)
             self.vals = torch.empty(cap, dtype=torch.int32, device=self.params.device)
         need = gs.gs_workspace_bytes(gs.GS_WS_BIN_SORT, self.n, pairs, self.W, self.H)
         if self.ws_sort.numel() < need:

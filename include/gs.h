@@ -5,8 +5,9 @@
  *
  *   gs_preprocess     project every Gaussian, count the 16x16 tiles it touches,
  *                     prefix-sum the counts; returns the number of (tile, Gaussian) pairs
- *   gs_bin_sort       emit one 64-bit key (tile << 32 | depth bits) per pair, radix-sort
- *                     the pairs, find each tile's [start, end) range
+ *   gs_bin_sort       order the (tile, Gaussian) pairs by tile, then depth, then id
+ *                     (depth sort of the visible Gaussians, emission, stable tile sort),
+ *                     find each tile's [start, end) range
  *   gs_render_fwd     front-to-back alpha blending per pixel
  *   gs_loss_l1_dssim  0.8 L1 + 0.2 (1 - SSIM) and its image gradient
  *   gs_render_bwd     back-to-front blend with transmittance recovery, then the
@@ -113,16 +114,21 @@ int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out,
                       void* ws, size_t ws_bytes, void* stream);
 
 /* Duplicate-with-keys, depth sort and tile ranges.  [GSG] "Why tiling, and the five stages"
- * (scatter, per-tile depth sort, ranges with the tie broken by id).  Pair j of Gaussian i
- * (tiles in row-major order over its rectangle) gets key (ty * tiles_x + tx) << 32 |
- * bits(depth[i]) and value i; the pairs are then sorted stably by key (LSD radix sort over
- * the key's significant bits), i.e. by tile, then depth, then Gaussian id.
- * keys[capacity], vals[capacity]: outputs, the first total_pairs entries are written.
- * ranges: [2][tiles_x * tiles_y] u32, ranges[0][t] = first, ranges[1][t] = one past the last
- * pair of tile t ((0, 0) for an empty tile).  total_pairs must be the value gs_preprocess
- * returned for the same proj.  ws: gs_workspace_bytes(GS_WS_BIN_SORT, n, total_pairs, W, H).
- * GS_ERR_CAPACITY (nothing written) if capacity < total_pairs or the workspace is short. */
-int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32_t total_pairs, uint64_t* keys,
+ * (scatter, per-tile depth sort, ranges with the tie broken by id).  Every (tile, Gaussian)
+ * pair of a visible Gaussian i (tile count > 0; tiles in row-major order over its rectangle)
+ * is produced once, and the pairs are ordered by tile id (ty * tiles_x + tx), then by the
+ * Gaussian's depth (as the bits of the positive float, i.e. numerically), then by i -- the
+ * order of the 64-bit key tile << 32 | bits(depth[i]) with ties by id.  Computed as a stable
+ * radix sort of the visible Gaussians by depth, emission of their pairs in that order, and a
+ * stable radix sort of the pairs by tile.
+ * keys[capacity]: tile id of each sorted pair; vals[capacity]: its Gaussian id; the first
+ * total_pairs entries are written.  ranges: [2][tiles_x * tiles_y] u32, ranges[0][t] = first,
+ * ranges[1][t] = one past the last pair of tile t ((0, 0) for an empty tile).  proj: the
+ * depth, rect and tiles arrays of gs_preprocess (offs is not read); total_pairs must be the
+ * value gs_preprocess returned for the same proj.  ws: gs_workspace_bytes(GS_WS_BIN_SORT, n,
+ * total_pairs, W, H).  GS_ERR_CAPACITY (nothing written) if capacity < total_pairs or the
+ * workspace is short. */
+int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32_t total_pairs, uint32_t* keys,
                     uint32_t* vals, uint32_t capacity, uint32_t* ranges, void* ws, size_t ws_bytes, void* stream);
 
 /* Front-to-back compositing, [GSG] "The painting itself: front-to-back alpha compositing";

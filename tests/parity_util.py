@@ -24,6 +24,11 @@ def gpu_forward(params_np, deg, cam):
     return pl, c
 
 
+def tile_of_key(keys64):
+    """Tile ids of the oracle's 64-bit sort keys (tile << 32 | depth bits)."""
+    return (np.asarray(keys64, np.uint64) >> np.uint64(32)).astype(np.uint32)
+
+
 def proj_to_numpy(pl):
     n = pl.n
     splat = pl.proj.splat[:n].cpu().numpy()
@@ -43,7 +48,7 @@ def proj_to_numpy(pl):
 
 def sorted_to_numpy(pl):
     P = pl.pairs
-    keys = pl.keys[:P].cpu().numpy().view(np.uint64)
+    keys = pl.keys[:P].cpu().numpy().view(np.uint32)    # tile id of each sorted pair
     vals = pl.vals[:P].cpu().numpy().view(np.uint32)
     ranges = pl.ranges.cpu().numpy().view(np.uint32)
     return keys, vals, ranges

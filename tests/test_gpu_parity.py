@@ -62,7 +62,7 @@ def test_forward_stages_small(torch_cuda, oracle, case):
     pu.check_preprocess(pu.proj_to_numpy(pl), o["pre"])
     assert pl.pairs == len(o["keys"]) > 0
     keys, vals, ranges = pu.sorted_to_numpy(pl)
-    np.testing.assert_array_equal(keys, o["keys"])
+    np.testing.assert_array_equal(keys, pu.tile_of_key(o["keys"]))
     np.testing.assert_array_equal(vals, o["vals"])
     np.testing.assert_array_equal(ranges, o["ranges"])
     pu.check_render(pu.render_to_numpy(pl), o["fwd"])
@@ -107,7 +107,7 @@ def test_config1_full_step(torch_cuda, oracle):
     pl, c = pu.gpu_forward(wl.scene.params, deg, cam)
     pu.check_preprocess(pu.proj_to_numpy(pl), ref["pre"])
     keys, vals, ranges = pu.sorted_to_numpy(pl)
-    np.testing.assert_array_equal(keys, ref["keys"])
+    np.testing.assert_array_equal(keys, pu.tile_of_key(ref["keys"]))
     np.testing.assert_array_equal(vals, ref["vals"])
     np.testing.assert_array_equal(ranges, ref["ranges"])
     n_low = pu.check_render(pu.render_to_numpy(pl), ref["fwd"])
@@ -272,7 +272,7 @@ def test_all_in_one_tile_and_non_finite(torch_cuda, oracle):
     pl, c = pu.gpu_forward(s.params, 3, cam)
     pu.check_preprocess(pu.proj_to_numpy(pl), o["pre"])
     keys, vals, ranges = pu.sorted_to_numpy(pl)
-    np.testing.assert_array_equal(keys, o["keys"])
+    np.testing.assert_array_equal(keys, pu.tile_of_key(o["keys"]))
     np.testing.assert_array_equal(vals, o["vals"])
     np.testing.assert_array_equal(ranges, o["ranges"])
     pu.check_render(pu.render_to_numpy(pl), o["fwd"])
@@ -284,7 +284,7 @@ def test_capacity_error_writes_nothing(torch_cuda):
     cam = scenes.identity_camera(64, 64, 60.0)
     s = scenes.random_scene(9, 300, 0)
     pl, c = pu.gpu_forward(s.params, 0, cam)
-    keys = torch.full((pl.pairs - 1,), 7, dtype=torch.int64, device="cuda")
+    keys = torch.full((pl.pairs - 1,), 7, dtype=torch.int32, device="cuda")
     vals = torch.full((pl.pairs - 1,), 7, dtype=torch.int32, device="cuda")
     ranges = torch.full((2, 16), 7, dtype=torch.int32, device="cuda")
     with pytest.raises(gs.GsError) as e:
