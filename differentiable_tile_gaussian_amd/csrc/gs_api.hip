@@ -48,12 +48,59 @@ int32_t check_scene(const gs_scene* sc) {
   return GS_OK;
 }
 
-int32_t check_proj(const gs_proj* p, int64_t n, bool need_offs) {
+int32_t check_proj(const gs_proj* p, int64_t n, bool need_order) {
   if (!p) return fail(GS_ERR_INVALID_ARG, "proj is null");
-  if (need_offs && !p->offs) return fail(GS_ERR_INVALID_ARG, "proj.offs is null");
+  if (need_order && (!p->offs || !p->n_visible || (n > 0 && !p->order)))
+    return fail(GS_ERR_INVALID_ARG, "proj.offs, proj.order or proj.n_visible is null");
   if (n > 0 && (!p->splat || !p->depth || !p->rect || !p->tiles))
     return fail(GS_ERR_INVALID_ARG, "a proj array is null");
   return GS_OK;
+}
+
+inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Preprocess workspace: pair count, per-block tile sums, depth-order state.
+struct PreWs {
+  uint64_t* total64;
+  uint32_t* block_tiles;
+  void* depth_ws;
+};
+
+size_t pre_ws_bytes(int64_t n) {
+  return 256 + align256(size_t(gsk::div_up(n > 0 ? n : 1, 256)) * 4) + gsk::depth_order_ws_bytes(n);
+}
+
+PreWs carve_pre(void* ws, int64_t n) {
+  char* p = static_cast<char*>(ws);
+  PreWs w;
+  w.total64 = reinterpret_cast<uint64_t*>(p);
+  w.block_tiles = reinterpret_cast<uint32_t*>(p + 256);
+  w.depth_ws = p + 256 + align256(size_t(gsk::div_up(n > 0 ? n : 1, 256)) * 4);
+  return w;
+}
+
+// Pinned host word the pair count is copied into, and the event that marks the copy,
+// one per device and host thread, created on first use and kept for the process.
+struct HostSlot {
+  uint64_t* pinned = nullptr;
+  hipEvent_t copied = nullptr;
+};
+
+HostSlot* host_slot() {
+  thread_local HostSlot slots[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  HostSlot& h = slots[dev];
+  if (!h.pinned) {
+    void* p = nullptr;
+    if (hipHostMalloc(&p, sizeof(uint64_t), hipHostMallocDefault) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&h.copied, hipEventDisableTiming) != hipSuccess) {
+      (void)hipHostFree(p);
+      return nullptr;
+    }
+    h.pinned = static_cast<uint64_t*>(p);
+  }
+  return &h;
 }
 
 }  // namespace
@@ -99,8 +146,8 @@ int64_t gs_get_tuning(int32_t key) {
 
 size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H) {
   switch (which_call) {
-    case GS_WS_PREPROCESS: return gsk::scan_ws_bytes(n < 0 ? 0 : n) + 256;
-    case GS_WS_BIN_SORT: return gsk::bin_sort_ws_bytes(n < 0 ? 0 : n, pairs);
+    case GS_WS_PREPROCESS: return pre_ws_bytes(n < 0 ? 0 : n);
+    case GS_WS_BIN_SORT: return gsk::bin_sort_ws_bytes(pairs);
     case GS_WS_LOSS: return (W > 0 && H > 0) ? gsk::loss_ws_bytes(H, W) : 0;
     case GS_WS_RENDER: return (W > 0 && H > 0) ? gsk::render_ws_bytes(W, H, pairs) : 0;
     default: return 0;
@@ -119,17 +166,26 @@ int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out,
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "preprocess workspace needs %zu bytes", need);
   hipStream_t s = as_stream(stream);
   const int n = int(scene->n);
-  hipError_t e = gsk::launch_preprocess_fwd(scene->params, n, scene->sh_degree, *cam, *out, s);
+  PreWs w = carve_pre(ws, n);
+  hipError_t e = gsk::launch_preprocess_fwd(scene->params, n, scene->sh_degree, *cam, *out, w.block_tiles,
+                                            w.total64, s);
   if (e != hipSuccess) return hip_fail(e, "preprocess_fwd");
-  uint64_t* total64 = static_cast<uint64_t*>(ws);
-  void* scan_ws = static_cast<char*>(ws) + 256;
-  e = gsk::launch_scan_u32(out->tiles, out->offs, n, total64, scan_ws, s);
-  if (e != hipSuccess) return hip_fail(e, "scan");
-  uint64_t host_total = 0;
-  e = hipMemcpyAsync(&host_total, total64, sizeof(uint64_t), hipMemcpyDeviceToHost, s);
-  if (e != hipSuccess) return hip_fail(e, "pair count copy");
-  e = hipStreamSynchronize(s);
+  // the pair count goes to the host while the depth order is computed
+  HostSlot* hs = host_slot();
+  if (!hs) return fail(GS_ERR_HIP, "cannot set up the pinned pair-count buffer");
+  if (n > 0) {
+    e = hipMemcpyAsync(hs->pinned, w.total64, sizeof(uint64_t), hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "pair count copy");
+  } else {
+    *hs->pinned = 0;
+  }
+  e = hipEventRecord(hs->copied, s);
+  if (e != hipSuccess) return hip_fail(e, "pair count event");
+  e = gsk::launch_depth_order(*out, n, w.depth_ws, s);
+  if (e != hipSuccess) return hip_fail(e, "depth order");
+  e = hipEventSynchronize(hs->copied);
   if (e != hipSuccess) return hip_fail(e, "preprocess sync");
+  const uint64_t host_total = *hs->pinned;
   if (host_total > 0xffffffffull)
     return fail(GS_ERR_CAPACITY, "pair count %llu exceeds 2^32 - 1", (unsigned long long)host_total);
   *total_pairs = uint32_t(host_total);
@@ -142,7 +198,7 @@ int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32
   int32_t st;
   if (n < 0 || n >= (int64_t(1) << 31)) return fail(GS_ERR_INVALID_ARG, "n out of range");
   if ((st = check_camera(cam)) != GS_OK) return st;
-  if ((st = check_proj(proj, n, false)) != GS_OK) return st;
+  if ((st = check_proj(proj, n, true)) != GS_OK) return st;
   if (!ranges) return fail(GS_ERR_INVALID_ARG, "ranges is null");
   if (total_pairs > 0 && (!keys || !vals)) return fail(GS_ERR_INVALID_ARG, "keys or vals is null");
   if (total_pairs > 0 && n == 0) return fail(GS_ERR_INVALID_ARG, "pairs without Gaussians");

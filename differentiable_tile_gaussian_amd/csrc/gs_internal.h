@@ -29,8 +29,9 @@ __host__ __device__ inline T* gaussian_base(T* params, int i, int P) {
 }
 
 // ---- preprocess.hip
+// block_tiles: div_up(n, 256) per-block sums of the tile counts; *total_pairs their sum.
 hipError_t launch_preprocess_fwd(const float* params, int n, int deg, const gs_camera& cam, const gs_proj& out,
-                                 hipStream_t s);
+                                 uint32_t* block_tiles, uint64_t* total_pairs, hipStream_t s);
 
 // ---- chain.hip (gscreen planes 6-8 are read; with Adam they are then overwritten)
 struct AdamArgs;
@@ -46,7 +47,11 @@ hipError_t launch_scan_u32(const uint32_t* in, uint32_t* out, int64_t n, uint64_
                            hipStream_t s);
 
 // ---- sort.hip
-size_t bin_sort_ws_bytes(int64_t n, uint32_t pairs);
+// depth order of the visible Gaussians (proj.order, proj.n_visible) and the pair
+// offsets in that order (proj.offs); then emission and the tile sort of the pairs
+size_t depth_order_ws_bytes(int64_t n);
+hipError_t launch_depth_order(const gs_proj& proj, int n, void* ws, hipStream_t s);
+size_t bin_sort_ws_bytes(uint32_t pairs);
 hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uint32_t pairs, uint32_t* keys,
                            uint32_t* vals, uint32_t* ranges, void* ws, hipStream_t s);
 

@@ -21,13 +21,38 @@ namespace {
 
 using namespace proj;
 
+// Half-widths of a box around (u, v) outside which no pixel centre can get
+// alpha >= 1/255 from this Gaussian, for the blend's per-quadrant skipping.  The
+// blend tests o exp(-e) >= 1/255 with e from the fp32 conic (A, B, C), so the box
+// bounds the ellipse e <= ln(255 o) of that conic: |dx| <= sqrt(2 t C / (A C - B^2)),
+// |dy| <= sqrt(2 t A / (A C - B^2)), evaluated in fp64 from the fp32 conic and widened
+// to cover the blend's fp32 evaluation of e: t by 1 % + 0.01, the half-widths by
+// 1 % + 0.05 px.  With A C / (A C - B^2) <= 1000 the rounding error of e stays below
+// 0.2 % of e (about 0.01 at the box), inside the margin; more elongated conics get an
+// unbounded box.  Negative when o < e^-0.001 / 255 (no pixel can reach 1/255);
+// infinite when the fp32 conic is not positive definite.
+__device__ inline void blend_box(const Proj& g, float& hx, float& hy) {
+  const double t = log(double(g.o) * 255.0);
+  if (!(t > -1e-3)) {
+    hx = hy = -1.0f;
+    return;
+  }
+  const double A = g.A, B = g.B, C = g.C;
+  const double det = A * C - B * B;
+  if (!(det > 0.0) || !(A > 0.0) || !(C > 0.0) || !(A * C <= 1000.0 * det)) {
+    hx = hy = __builtin_inff();
+    return;
+  }
+  const double tm = t + 0.01 + 0.01 * fabs(t);
+  hx = float(sqrt(2.0 * tm * C / det) * 1.01 + 0.05);
+  hy = float(sqrt(2.0 * tm * A / det) * 1.01 + 0.05);
+}
+
+// One Gaussian: writes its projected record and returns its tile count.
 template <int DEG>
-__global__ void __launch_bounds__(256) preprocess_fwd_kernel(const float* __restrict__ params, int n,
-                                                              gs_camera cam, int tx, int ty, float4* __restrict__ splat,
-                                                              float* __restrict__ depth, uint2* __restrict__ rect,
-                                                              uint32_t* __restrict__ tiles) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
+__device__ inline uint32_t project_one(const float* __restrict__ params, int i, const gs_camera& cam, int tx, int ty,
+                                       float4* __restrict__ splat, float* __restrict__ depth,
+                                       uint2* __restrict__ rect, uint32_t* __restrict__ tiles) {
   constexpr int K = (DEG + 1) * (DEG + 1) - 1;
   constexpr int P = 11 + 3 * (K + 1);
   const float* g0 = gaussian_base(params, i, P);
@@ -77,7 +102,9 @@ __global__ void __launch_bounds__(256) preprocess_fwd_kernel(const float* __rest
   if (vis) {
     splat[3 * i + 0] = make_float4(g.u, g.v, g.A, g.B);
     splat[3 * i + 1] = make_float4(g.C, g.o, rgb[0], rgb[1]);
-    splat[3 * i + 2] = make_float4(rgb[2], 0.f, 0.f, 0.f);
+    float hx, hy;
+    blend_box(g, hx, hy);
+    splat[3 * i + 2] = make_float4(rgb[2], hx, hy, 0.f);
     depth[i] = g.p[2];
     rect[i] = make_uint2(x0 | (y0 << 16), x1 | (y1 << 16));
     tiles[i] = cnt;
@@ -90,24 +117,64 @@ __global__ void __launch_bounds__(256) preprocess_fwd_kernel(const float* __rest
     rect[i] = make_uint2(0u, 0u);
     tiles[i] = 0u;
   }
+  return vis ? cnt : 0u;
+}
+
+template <int DEG>
+__global__ void __launch_bounds__(256) preprocess_fwd_kernel(const float* __restrict__ params, int n,
+                                                              gs_camera cam, int tx, int ty, float4* __restrict__ splat,
+                                                              float* __restrict__ depth, uint2* __restrict__ rect,
+                                                              uint32_t* __restrict__ tiles,
+                                                              uint32_t* __restrict__ block_tiles) {
+  __shared__ uint32_t s_wave[4];
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t cnt = i < n ? project_one<DEG>(params, i, cam, tx, ty, splat, depth, rect, tiles) : 0u;
+  // the block's total of tile counts (the pair count is the sum over blocks)
+  uint32_t v = cnt;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  if (__lane_id() == 0) s_wave[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) block_tiles[blockIdx.x] = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+}
+
+// Sum of the per-block tile counts (one block).
+__global__ void __launch_bounds__(1024) sum_counts_kernel(const uint32_t* __restrict__ block_tiles, int nb,
+                                                           uint64_t* __restrict__ total) {
+  __shared__ uint64_t s_wave[16];
+  uint64_t v = 0;
+  for (int k = threadIdx.x; k < nb; k += 1024) v += block_tiles[k];
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  if (__lane_id() == 0) s_wave[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t t = 0;
+    for (int w = 0; w < 16; ++w) t += s_wave[w];
+    *total = t;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_preprocess_fwd(const float* params, int n, int deg, const gs_camera& cam, const gs_proj& out,
-                                 hipStream_t s) {
+                                 uint32_t* block_tiles, uint64_t* total_pairs, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const dim3 grid(div_up(n, 256)), block(256);
   const int tx = tiles_x(cam), ty = tiles_y(cam);
   float4* splat = reinterpret_cast<float4*>(out.splat);
   uint2* rect = reinterpret_cast<uint2*>(out.rect);
-  GSK_PROF("preprocess_fwd", s);
-  switch (deg) {
-    case 0: preprocess_fwd_kernel<0><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles); break;
-    case 1: preprocess_fwd_kernel<1><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles); break;
-    case 2: preprocess_fwd_kernel<2><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles); break;
-    default: preprocess_fwd_kernel<3><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles); break;
+  {
+    GSK_PROF("preprocess_fwd", s);
+    switch (deg) {
+      case 0: preprocess_fwd_kernel<0><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles); break;
+      case 1: preprocess_fwd_kernel<1><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles); break;
+      case 2: preprocess_fwd_kernel<2><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles); break;
+      default: preprocess_fwd_kernel<3><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles); break;
+    }
   }
+  GSK_PROF("sum_counts", s);
+  sum_counts_kernel<<<1, 1024, 0, s>>>(block_tiles, int(grid.x), total_pairs);
   return hipGetLastError();
 }
 

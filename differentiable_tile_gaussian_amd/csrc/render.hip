@@ -60,6 +60,9 @@ namespace {
 // more similar numbers of pairs and fewer lanes idle while the wave walks on).
 __device__ inline int pixel_x(int tid) { return ((tid >> 6) & 1) * 8 + (tid & 7); }
 __device__ inline int pixel_y(int tid) { return (tid >> 7) * 8 + ((tid >> 3) & 7); }
+// Pixel coordinates of a tile's corner.
+__device__ inline float tile_ox(int tile, int tx) { return float((tile % tx) * kTile); }
+__device__ inline float tile_oy(int tile, int tx) { return float((tile / tx) * kTile); }
 
 constexpr int kBatch = 256;
 constexpr float kAlphaMin = 1.0f / 255.0f;
@@ -173,17 +176,40 @@ __global__ void split_init_kernel(uint32_t* __restrict__ counters, int32_t* __re
 }
 
 // ------------------------------------------------------------ forward walk
+// Quadrant mask of a pair in the tile with corner (ox, oy): bit 2 * qy + qx is set
+// unless the pair's box (u +- bx, v +- by), outside which no pixel centre gets
+// alpha >= 1/255, misses the pixel centres of 8x8 quadrant (qx, qy).  The walks
+// skip a pair in a quadrant whose bit is clear: every pixel there would have skipped
+// it, so the results are unchanged.
+__device__ inline uint32_t quad_mask(float u, float v, float bx, float by, float ox, float oy) {
+  if (bx < 0.0f) return 0u;                                // reaches no pixel
+  if (!(bx <= 3.0e38f) || !(by <= 3.0e38f)) return 0xfu;   // unbounded
+  const float x0 = u - bx - ox, x1 = u + bx - ox, y0 = v - by - oy, y1 = v + by - oy;
+  const bool xl = x0 <= 7.5f && x1 >= 0.5f, xr = x0 <= 15.5f && x1 >= 8.5f;
+  const bool yt = y0 <= 7.5f && y1 >= 0.5f, yb = y0 <= 15.5f && y1 >= 8.5f;
+  return uint32_t(xl && yt) | (uint32_t(xr && yt) << 1) | (uint32_t(xl && yb) << 2) | (uint32_t(xr && yb) << 3);
+}
+
+// The walking wave's bits of a batch's masks, 64 entries per word.
+__device__ inline uint64_t quad_bits(const uint32_t* m, int group) {
+  const uint32_t quad = threadIdx.x >> 6;
+  return __ballot((m[group * 64 + __lane_id()] >> quad) & 1u);
+}
+
 struct FwdLds {
   float4 a[2][kBatch];   // u, v, a', b'
   float4 b[2][kBatch];   // c', opacity, r, g
   float c[2][kBatch];    // b
+  uint32_t m[2][kBatch]; // quadrant masks
 };
 
-__device__ inline void stage_fwd(const float4* __restrict__ splat, uint32_t g, float4& a, float4& b, float& c) {
-  const float4 r0 = splat[3 * g], r1 = splat[3 * g + 1];
-  c = splat[3 * g + 2].x;
+__device__ inline void stage_fwd(const float4* __restrict__ splat, uint32_t g, float ox, float oy, float4& a,
+                                 float4& b, float& c, uint32_t& m) {
+  const float4 r0 = splat[3 * g], r1 = splat[3 * g + 1], r2 = splat[3 * g + 2];
+  c = r2.x;
   a = make_float4(r0.x, r0.y, -0.5f * kLog2e * r0.z, -kLog2e * r0.w);
   b = make_float4(-0.5f * kLog2e * r1.x, r1.y, r1.z, r1.w);
+  m = quad_mask(r0.x, r0.y, r2.y, r2.z, ox, oy);
 }
 
 struct PixelFwd {
@@ -198,15 +224,16 @@ struct PixelFwd {
 // records chunk_id in sat[tid].  Must be called by all 256 threads of the block.
 template <bool POLL>
 __device__ void fwd_walk(FwdLds& L, const float4* __restrict__ splat, const uint32_t* __restrict__ vals,
-                         uint32_t start, int lo, int hi, float fx, float fy, float pre, PixelFwd& s,
-                         uint32_t* sat, uint32_t chunk_id) {
+                         uint32_t start, int lo, int hi, float ox, float oy, float fx, float fy, float pre,
+                         PixelFwd& s, uint32_t* sat, uint32_t chunk_id) {
   const int tid = threadIdx.x;
   if (lo >= hi) return;
   {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
     float c = 0.f;
-    if (lo + tid < hi) stage_fwd(splat, vals[start + uint32_t(lo + tid)], a, b, c);
-    L.a[0][tid] = a; L.b[0][tid] = b; L.c[0][tid] = c;
+    uint32_t m = 0u;
+    if (lo + tid < hi) stage_fwd(splat, vals[start + uint32_t(lo + tid)], ox, oy, a, b, c, m);
+    L.a[0][tid] = a; L.b[0][tid] = b; L.c[0][tid] = c; L.m[0][tid] = m;
   }
   __syncthreads();
   bool reported = s.done;
@@ -215,33 +242,44 @@ __device__ void fwd_walk(FwdLds& L, const float4* __restrict__ splat, const uint
     const int nxt = base + kBatch + tid;
     float4 na = make_float4(0.f, 0.f, 0.f, 0.f), nb = na;
     float nc = 0.f;
-    if (nxt < hi) stage_fwd(splat, vals[start + uint32_t(nxt)], na, nb, nc);
-    const int cnt = min(kBatch, hi - base);
-    if (!__all(s.done)) {
-      for (int j = 0; j < cnt; j += 4) {
+    uint32_t nm = 0u;
+    if (nxt < hi) stage_fwd(splat, vals[start + uint32_t(nxt)], ox, oy, na, nb, nc, nm);
+    // walk the batch entries whose quadrant bit is set, in order, four at a time
+    bool all_done = __all(s.done);
+    for (int grp = 0; grp < kBatch / 64 && !all_done; ++grp) {
+      uint64_t bits = quad_bits(L.m[buf], grp);
+      while (bits && !all_done) {
+        int e[4];
+        bool v[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float4 a = L.a[buf][j + k];
-          const float4 b = L.b[buf][j + k];
-          const float cb = L.c[buf][j + k];
+          v[k] = bits != 0;
+          e[k] = grp * 64 + (v[k] ? int(__builtin_ctzll(bits)) : 0);
+          bits &= bits - 1;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float4 a = L.a[buf][e[k]];
+          const float4 b = L.b[buf][e[k]];
+          const float cb = L.c[buf][e[k]];
           const float dx = fx - a.x, dy = fy - a.y;
           const float q = a.z * dx * dx + a.w * dx * dy + b.x * dy * dy;
           float alpha = fminf(kAlphaCap, b.y * fast_exp2(q));
-          const bool ok = !s.done && alpha >= kAlphaMin;
+          const bool ok = v[k] && !s.done && alpha >= kAlphaMin;
           alpha = ok ? alpha : 0.0f;
           const float w = alpha * s.T;
           s.c0 += w * b.z;
           s.c1 += w * b.w;
           s.c2 += w * cb;
           s.T = s.T * (1.0f - alpha);
-          s.last = ok ? uint32_t(base + j + k + 1) : s.last;
+          s.last = ok ? uint32_t(base + e[k] + 1) : s.last;
           s.done = s.done || (pre * s.T < kTStop);
         }
-        if (__all(s.done)) break;
+        all_done = __all(s.done);
       }
     }
     if (base + kBatch < hi) {
-      L.a[buf ^ 1][tid] = na; L.b[buf ^ 1][tid] = nb; L.c[buf ^ 1][tid] = nc;
+      L.a[buf ^ 1][tid] = na; L.b[buf ^ 1][tid] = nb; L.c[buf ^ 1][tid] = nc; L.m[buf ^ 1][tid] = nm;
     }
     if (POLL) {
       if (s.done && !reported) {
@@ -280,8 +318,8 @@ __global__ void __launch_bounds__(256) render_fwd_kernel(const float4* __restric
   const uint32_t start = ranges[tile];
   const int n = int(ranges[num_tiles + tile] - start);
   PixelFwd s{1.0f, 0.0f, 0.0f, 0.0f, 0u, !inside};
-  fwd_walk<false>(L, splat, vals, start, 0, min(n, first), float(px) + 0.5f, float(py) + 0.5f, 1.0f, s, nullptr,
-                  0u);
+  fwd_walk<false>(L, splat, vals, start, 0, min(n, first), tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f,
+                  float(py) + 0.5f, 1.0f, s, nullptr, 0u);
   if (n > first) {
     if (__syncthreads_count(s.done) < kBatch) {
       if (tid == 0) {
@@ -335,10 +373,11 @@ __global__ void __launch_bounds__(256) split_chunk_kernel(const float4* __restri
   const bool done0 = (ws.stl[so] & kFlag) != 0u;
   PixelFwd s{c == 0 ? ws.st4[so].x : 1.0f, 0.0f, 0.0f, 0.0f, 0u, done0};
   if (c == 0)
-    fwd_walk<false>(L, splat, vals, start, lo, hi, float(px) + 0.5f, float(py) + 0.5f, 1.0f, s, nullptr, 0u);
+    fwd_walk<false>(L, splat, vals, start, lo, hi, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f,
+                    float(py) + 0.5f, 1.0f, s, nullptr, 0u);
   else
-    fwd_walk<true>(L, splat, vals, start, lo, hi, float(px) + 0.5f, float(py) + 0.5f, 1.0f, s, ws.sat + size_t(slot) * 256,
-                   c);
+    fwd_walk<true>(L, splat, vals, start, lo, hi, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f,
+                   float(py) + 0.5f, 1.0f, s, ws.sat + size_t(slot) * 256, c);
   const size_t io = size_t(item) * 256 + tid;
   ws.part4[io] = make_float4(s.T, s.c0, s.c1, s.c2);
   // chunk 0 continues the exact walk: its flag means "stopped here"
@@ -422,7 +461,8 @@ __global__ void __launch_bounds__(256) split_rewalk_kernel(const float4* __restr
     lastf = ws.finl[so];
   }
   PixelFwd s{1.0f, 0.0f, 0.0f, 0.0f, 0u, !need};
-  fwd_walk<false>(L, splat, vals, start, lo, hi, float(px) + 0.5f, float(py) + 0.5f, front.x, s, nullptr, 0u);
+  fwd_walk<false>(L, splat, vals, start, lo, hi, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f,
+                  float(py) + 0.5f, front.x, s, nullptr, 0u);
   if (need) {
     const float a0 = front.x * s.c0, a1 = front.x * s.c1, a2 = front.x * s.c2;
     const float Tf = front.x * s.T;
@@ -535,15 +575,18 @@ struct BwdLds {
   float4 b[2][kBatch];     // c', opacity, r, g
   float4 c[2][kBatch];     // b, A, B, C
   uint32_t id[2][kBatch];
+  uint32_t m[2][kBatch];   // quadrant masks
   float acc[9][kBatch];    // per-entry sums over the block's waves
   uint32_t top;
 };
 
-__device__ inline void stage_bwd(const float4* __restrict__ splat, uint32_t g, float4& a, float4& b, float4& c) {
+__device__ inline void stage_bwd(const float4* __restrict__ splat, uint32_t g, float ox, float oy, float4& a,
+                                 float4& b, float4& c, uint32_t& m) {
   const float4 r0 = splat[3 * g], r1 = splat[3 * g + 1], r2 = splat[3 * g + 2];
   a = make_float4(r0.x, r0.y, -0.5f * kLog2e * r0.z, -kLog2e * r0.w);
   b = make_float4(-0.5f * kLog2e * r1.x, r1.y, r1.z, r1.w);
   c = make_float4(r2.x, r0.z, r0.w, r1.x);
+  m = quad_mask(r0.x, r0.y, r2.y, r2.z, ox, oy);
 }
 
 struct PixelBwd {
@@ -555,7 +598,7 @@ struct PixelBwd {
 // Walks pairs top-1 .. lo (top per pixel, at most hi) of a tile list, adding
 // each pair's partials to gscreen.  Must be called by all 256 threads.
 __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint32_t* __restrict__ vals,
-                         uint32_t start, int lo, float fx, float fy, PixelBwd& s, int n,
+                         uint32_t start, int lo, float ox, float oy, float fx, float fy, PixelBwd& s, int n,
                          float* __restrict__ gscreen) {
   const int tid = threadIdx.x;
   const int lane = __lane_id();
@@ -573,12 +616,12 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
   {
     const int blo = max(hi - kBatch, lo);
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a, c = a;
-    uint32_t g = 0;
+    uint32_t g = 0, m = 0u;
     if (blo + tid < hi) {
       g = vals[start + uint32_t(blo + tid)];
-      stage_bwd(splat, g, a, b, c);
+      stage_bwd(splat, g, ox, oy, a, b, c, m);
     }
-    L.a[0][tid] = a; L.b[0][tid] = b; L.c[0][tid] = c; L.id[0][tid] = g;
+    L.a[0][tid] = a; L.b[0][tid] = b; L.c[0][tid] = c; L.id[0][tid] = g; L.m[0][tid] = m;
   }
   __syncthreads();
   int buf = 0;
@@ -586,53 +629,64 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
     const int blo = max(hi - kBatch, lo);
     const int nhi = blo, nlo = max(nhi - kBatch, lo);
     float4 na = make_float4(0.f, 0.f, 0.f, 0.f), nb = na, ncr = na;
-    uint32_t ng = 0;
+    uint32_t ng = 0, nm = 0u;
     if (nlo + tid < nhi) {
       ng = vals[start + uint32_t(nlo + tid)];
-      stage_bwd(splat, ng, na, nb, ncr);
+      stage_bwd(splat, ng, ox, oy, na, nb, ncr, nm);
     }
-    const int jtop = min(hi, wave_top) - 1;
-    for (int j = jtop; j >= blo; --j) {
-      const int e = j - blo;
-      const float4 a = L.a[buf][e];
-      const float4 b = L.b[buf][e];
-      const float4 c = L.c[buf][e];
-      const float dx = fx - a.x, dy = fy - a.y;
-      const float q = a.z * dx * dx + a.w * dx * dy + b.x * dy * dy;
-      const float G = fast_exp2(q);
-      const float araw = b.y * G;
-      const float alpha = fminf(kAlphaCap, araw);
-      const bool ok = j < s.top && alpha >= kAlphaMin;
-      if (__ballot(ok) == 0) continue;
-      float v[9];
-      const float inv = __builtin_amdgcn_rcpf(1.0f - alpha);
-      const float Tn = s.T * inv;           // transmittance in front of this pair
-      const float w = alpha * Tn;
-      const float galpha =
-          s.g0 * (b.z * Tn - s.S0 * inv) + s.g1 * (b.w * Tn - s.S1 * inv) + s.g2 * (c.x * Tn - s.S2 * inv);
-      const bool unc = ok && araw <= kAlphaCap;
-      const float ge = unc ? -galpha * araw : 0.0f;
-      v[0] = -ge * (c.y * dx + c.z * dy);
-      v[1] = -ge * (c.z * dx + c.w * dy);
-      v[2] = ge * 0.5f * dx * dx;
-      v[3] = ge * dx * dy;
-      v[4] = ge * 0.5f * dy * dy;
-      v[5] = unc ? galpha * G : 0.0f;
-      v[6] = ok ? s.g0 * w : 0.0f;
-      v[7] = ok ? s.g1 * w : 0.0f;
-      v[8] = ok ? s.g2 * w : 0.0f;
-      if (ok) {
-        s.S0 += b.z * w;
-        s.S1 += b.w * w;
-        s.S2 += c.x * w;
-        s.T = Tn;
+    // entries 0 .. etop of the batch whose quadrant bit is set, last to first
+    const int etop = min(hi, wave_top) - 1 - blo;
+    for (int grp = kBatch / 64 - 1; grp >= 0; --grp) {
+      if (grp * 64 > etop) continue;
+      uint64_t bits = quad_bits(L.m[buf], grp);
+      const int top_bit = etop - grp * 64;
+      if (top_bit < 63) bits &= (uint64_t(2) << top_bit) - 1;
+      while (bits) {
+        const int eb = 63 - int(__builtin_clzll(bits));
+        bits &= ~(uint64_t(1) << eb);
+        const int e = grp * 64 + eb;
+        const int j = blo + e;
+        const float4 a = L.a[buf][e];
+        const float4 b = L.b[buf][e];
+        const float4 c = L.c[buf][e];
+        const float dx = fx - a.x, dy = fy - a.y;
+        const float q = a.z * dx * dx + a.w * dx * dy + b.x * dy * dy;
+        const float G = fast_exp2(q);
+        const float araw = b.y * G;
+        const float alpha = fminf(kAlphaCap, araw);
+        const bool ok = j < s.top && alpha >= kAlphaMin;
+        if (__ballot(ok) == 0) continue;
+        float v[9];
+        const float inv = __builtin_amdgcn_rcpf(1.0f - alpha);
+        const float Tn = s.T * inv;           // transmittance in front of this pair
+        const float w = alpha * Tn;
+        const float galpha =
+            s.g0 * (b.z * Tn - s.S0 * inv) + s.g1 * (b.w * Tn - s.S1 * inv) + s.g2 * (c.x * Tn - s.S2 * inv);
+        const bool unc = ok && araw <= kAlphaCap;
+        const float ge = unc ? -galpha * araw : 0.0f;
+        v[0] = -ge * (c.y * dx + c.z * dy);
+        v[1] = -ge * (c.z * dx + c.w * dy);
+        v[2] = ge * 0.5f * dx * dx;
+        v[3] = ge * dx * dy;
+        v[4] = ge * 0.5f * dy * dy;
+        v[5] = unc ? galpha * G : 0.0f;
+        v[6] = ok ? s.g0 * w : 0.0f;
+        v[7] = ok ? s.g1 * w : 0.0f;
+        v[8] = ok ? s.g2 * w : 0.0f;
+        if (ok) {
+          s.S0 += b.z * w;
+          s.S1 += b.w * w;
+          s.S2 += c.x * w;
+          s.T = Tn;
+        }
+        wave_sum9(v);
+        if ((lane & 7) == 0) atomicAdd(&L.acc[lane >> 3][e], v[0]);
+        if (lane == 0) atomicAdd(&L.acc[8][e], v[8]);
       }
-      wave_sum9(v);
-      if ((lane & 7) == 0) atomicAdd(&L.acc[lane >> 3][e], v[0]);
-      if (lane == 0) atomicAdd(&L.acc[8][e], v[8]);
     }
     if (nlo < nhi) {
       L.a[buf ^ 1][tid] = na; L.b[buf ^ 1][tid] = nb; L.c[buf ^ 1][tid] = ncr; L.id[buf ^ 1][tid] = ng;
+      L.m[buf ^ 1][tid] = nm;
     }
     __syncthreads();
     if (tid < hi - blo) {
@@ -684,7 +738,8 @@ __global__ void __launch_bounds__(256) render_bwd_kernel(const float4* __restric
       s.top = int(n_contrib[p]);
     }
   }
-  bwd_walk(L, splat, vals, start, 0, float(px) + 0.5f, float(py) + 0.5f, s, n, gscreen);
+  bwd_walk(L, splat, vals, start, 0, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f, float(py) + 0.5f, s, n,
+           gscreen);
 }
 
 // One block per chunk of a split tile.
@@ -728,7 +783,8 @@ __global__ void __launch_bounds__(256) split_bwd_kernel(const float4* __restrict
       s.top = hi;
     }
   }
-  bwd_walk(L, splat, vals, start, lo, float(px) + 0.5f, float(py) + 0.5f, s, n, gscreen);
+  bwd_walk(L, splat, vals, start, lo, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f, float(py) + 0.5f, s, n,
+           gscreen);
 }
 
 __global__ void zero_f32_kernel(float* __restrict__ p, int64_t count) {

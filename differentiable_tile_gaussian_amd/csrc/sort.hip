@@ -90,10 +90,13 @@ __global__ void __launch_bounds__(kSortThreads) radix_upsweep_kernel(PassIn in, 
 
 // hist_scan has kRadix * nb + 1 entries, the last one the total: with kFromDepth
 // that is the number of visible Gaussians, which block 0 stores to *count_out.
+// With tiles_out, the item's value (a Gaussian id) is also looked up in val_tiles
+// and its tile count written beside it.
 template <int SRC>
 __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
     PassIn in, int shift, int nb, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ hist_scan,
-    uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint32_t* __restrict__ count_out) {
+    uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint32_t* __restrict__ count_out,
+    const uint32_t* __restrict__ val_tiles, uint32_t* __restrict__ tiles_out) {
   __shared__ uint32_t s_keys[kSortTile];
   __shared__ uint32_t s_vals[kSortTile];
   __shared__ uint32_t s_wave_cnt[kSortThreads / 64][kRadix];
@@ -170,35 +173,53 @@ __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
     const uint32_t dst = s_global[d] + (k - s_local[d]);
     keys_out[dst] = key;
     vals_out[dst] = s_vals[k];
+    if (tiles_out) tiles_out[dst] = val_tiles[s_vals[k]];
   }
-}
-
-// Tile counts of the depth-sorted visible Gaussians (zero past the visible count).
-__global__ void __launch_bounds__(256) gather_counts_kernel(const uint32_t* __restrict__ sorted_ids,
-                                                             const uint32_t* __restrict__ n_vis,
-                                                             const uint32_t* __restrict__ tiles, int n,
-                                                             uint32_t* __restrict__ counts) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= n) return;
-  counts[r] = uint32_t(r) < *n_vis ? tiles[sorted_ids[r]] : 0u;
 }
 
 // One thread per pair: the Gaussian (in depth order) that owns it, and its tile.
-__global__ void __launch_bounds__(256) emit_pairs_kernel(const uint32_t* __restrict__ pos,
+// offs[r] is the first pair of the r-th visible Gaussian in depth order.  The
+// block's 256 pairs belong to at most 256 consecutive Gaussians: two searches in
+// global memory find them, their offsets go to LDS, and each thread searches there.
+__global__ void __launch_bounds__(256) emit_pairs_kernel(const uint32_t* __restrict__ offs,
                                                           const uint32_t* __restrict__ n_vis,
-                                                          const uint32_t* __restrict__ sorted_ids,
-                                                          const uint2* __restrict__ rect, uint32_t pairs, int tx,
-                                                          uint32_t* __restrict__ keys, uint32_t* __restrict__ vals) {
-  const uint32_t p = blockIdx.x * blockDim.x + threadIdx.x;
+                                                          const uint32_t* __restrict__ order,
+                                                          const uint2* __restrict__ rect, int n, uint32_t pairs,
+                                                          int tx, uint32_t* __restrict__ keys,
+                                                          uint32_t* __restrict__ vals) {
+  __shared__ uint32_t s_offs[256];
+  __shared__ int s_r[2];
+  const uint32_t p0 = blockIdx.x * 256u;
+  if (threadIdx.x < 2) {
+    // largest r with offs[r] <= target; offs is strictly increasing over the visible Gaussians
+    const uint32_t last = p0 + 255u < pairs ? p0 + 255u : pairs - 1u;
+    const uint32_t target = threadIdx.x == 0 ? p0 : last;
+    int lo = 0, hi = int(*n_vis) - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (offs[mid] <= target) lo = mid; else hi = mid - 1;
+    }
+    s_r[threadIdx.x] = lo;
+  }
+  __syncthreads();
+  const int r0 = s_r[0];
+  const int k = min(s_r[1] - r0 + 1, 256);
+  if (int(threadIdx.x) < k) s_offs[threadIdx.x] = offs[r0 + int(threadIdx.x)];
+  __syncthreads();
+  const uint32_t p = p0 + threadIdx.x;
   if (p >= pairs) return;
-  // largest r with pos[r] <= p; pos is strictly increasing over the visible Gaussians
-  int lo = 0, hi = int(*n_vis) - 1;
+  int lo = 0, hi = k - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (pos[mid] <= p) lo = mid; else hi = mid - 1;
+    if (s_offs[mid] <= p) lo = mid; else hi = mid - 1;
   }
-  const uint32_t g = sorted_ids[lo];
-  const uint32_t j = p - pos[lo];
+  const uint32_t g = order[r0 + lo];
+  if (g >= uint32_t(n)) {   // only if total_pairs disagrees with the projection
+    keys[p] = 0xffffffffu;
+    vals[p] = 0u;
+    return;
+  }
+  const uint32_t j = p - s_offs[lo];
   const uint2 r = rect[g];
   const uint32_t x0 = r.x & 0xffffu, y0 = r.x >> 16, x1 = r.y & 0xffffu;
   const uint32_t w = x1 - x0 + 1;
@@ -229,52 +250,73 @@ inline int bits_for(uint32_t max_value) {
 
 inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
-struct SortWs {
-  uint32_t *dk[2], *dv[2];      // depth sort ping-pong, n each
-  uint32_t* counts;             // n
-  uint32_t* pos;                // n + 1
-  uint32_t *keys_alt, *vals_alt;   // pairs each
+int blocks_for(int64_t items) { return int(div_up(items > 0 ? items : 1, kSortTile)); }
+
+// Bump allocator over a workspace; with a null base it only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  uint32_t* take(size_t bytes) {
+    char* r = base ? base + off : nullptr;
+    off += align256(bytes);
+    return reinterpret_cast<uint32_t*>(r);
+  }
+};
+
+struct RadixWs {
   uint32_t *hist, *hist_scan;   // kRadix * nb (+ 1)
   uint64_t* total64;
-  uint32_t* n_vis;
   void* scan_ws;
 };
 
-int blocks_for(int64_t items) { return int(div_up(items > 0 ? items : 1, kSortTile)); }
-
-// Carves the workspace; returns its size (w may be null to only size it).
-size_t carve(void* ws, int64_t n, uint32_t pairs, SortWs* w) {
-  const int nb = std::max(blocks_for(n), blocks_for(pairs));
+RadixWs carve_radix(Carver& c, int nb, int64_t also_scan) {
   const int64_t hist_n = int64_t(kRadix) * nb;
-  const size_t sn = align256(size_t(n) * 4), sp = align256(size_t(pairs) * 4);
-  size_t off = 0;
-  char* p = static_cast<char*>(ws);
-  auto take = [&](size_t bytes) {
-    char* r = p ? p + off : nullptr;
-    off += align256(bytes);
-    return reinterpret_cast<uint32_t*>(r);
-  };
-  SortWs t;
-  for (int k = 0; k < 2; ++k) {
-    t.dk[k] = take(sn);
-    t.dv[k] = take(sn);
-  }
-  t.counts = take(sn);
-  t.pos = take(size_t(n + 1) * 4);
-  t.keys_alt = take(sp);
-  t.vals_alt = take(sp);
-  t.hist = take(size_t(hist_n) * 4);
-  t.hist_scan = take(size_t(hist_n + 1) * 4);
-  t.total64 = reinterpret_cast<uint64_t*>(take(8));
-  t.n_vis = take(4);
-  t.scan_ws = take(scan_ws_bytes(std::max<int64_t>(hist_n, n)));
-  if (w) *w = t;
-  return off;
+  RadixWs w;
+  w.hist = c.take(size_t(hist_n) * 4);
+  w.hist_scan = c.take(size_t(hist_n + 1) * 4);
+  w.total64 = reinterpret_cast<uint64_t*>(c.take(8));
+  w.scan_ws = c.take(scan_ws_bytes(std::max<int64_t>(hist_n, also_scan)));
+  return w;
+}
+
+struct DepthWs {
+  uint32_t *dk[2], *dv;         // ping-pong with proj.order, n each
+  uint32_t* counts;             // n: tile counts in depth order
+  RadixWs r;
+};
+
+size_t carve_depth(void* ws, int64_t n, DepthWs* out) {
+  Carver c{static_cast<char*>(ws)};
+  DepthWs w;
+  const size_t sn = size_t(n) * 4;
+  w.dk[0] = c.take(sn);
+  w.dk[1] = c.take(sn);
+  w.dv = c.take(sn);
+  w.counts = c.take(sn);
+  w.r = carve_radix(c, blocks_for(n), n);
+  if (out) *out = w;
+  return c.off;
+}
+
+struct PairWs {
+  uint32_t *keys_alt, *vals_alt;   // pairs each
+  RadixWs r;
+};
+
+size_t carve_pairs(void* ws, uint32_t pairs, PairWs* out) {
+  Carver c{static_cast<char*>(ws)};
+  PairWs w;
+  w.keys_alt = c.take(size_t(pairs) * 4);
+  w.vals_alt = c.take(size_t(pairs) * 4);
+  w.r = carve_radix(c, blocks_for(pairs), 0);
+  if (out) *out = w;
+  return c.off;
 }
 
 template <int SRC>
-hipError_t radix_pass(const PassIn& in, int nb, int shift, const SortWs& w, uint32_t* keys_out,
-                      uint32_t* vals_out, uint32_t* count_out, hipStream_t s) {
+hipError_t radix_pass(const PassIn& in, int nb, int shift, const RadixWs& w, uint32_t* keys_out,
+                      uint32_t* vals_out, uint32_t* count_out, const uint32_t* val_tiles, uint32_t* tiles_out,
+                      hipStream_t s) {
   {
     GSK_PROF("radix_upsweep", s);
     radix_upsweep_kernel<SRC><<<nb, kSortThreads, 0, s>>>(in, shift, nb, w.hist);
@@ -283,13 +325,51 @@ hipError_t radix_pass(const PassIn& in, int nb, int shift, const SortWs& w, uint
   if (e != hipSuccess) return e;
   GSK_PROF("radix_downsweep", s);
   radix_downsweep_kernel<SRC><<<nb, kSortThreads, 0, s>>>(in, shift, nb, w.hist, w.hist_scan, keys_out, vals_out,
-                                                          count_out);
+                                                          count_out, val_tiles, tiles_out);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t bin_sort_ws_bytes(int64_t n, uint32_t pairs) { return carve(nullptr, n, pairs, nullptr); }
+size_t depth_order_ws_bytes(int64_t n) { return carve_depth(nullptr, n, nullptr); }
+
+hipError_t launch_depth_order(const gs_proj& proj, int n, void* ws, hipStream_t s) {
+  if (n == 0) {
+    GSK_PROF("fill_u32", s);
+    fill_u32_kernel<<<1, 256, 0, s>>>(proj.offs, 1, 0u);
+    fill_u32_kernel<<<1, 256, 0, s>>>(proj.n_visible, 1, 0u);
+    return hipGetLastError();
+  }
+  DepthWs w;
+  carve_depth(ws, n, &w);
+  hipError_t e;
+  const int nb = blocks_for(n);
+  {
+    GSK_PROF("fill_u32", s);
+    fill_u32_kernel<<<div_up(n, 256), 256, 0, s>>>(w.counts, n, 0u);
+  }
+  // pass 0 compacts the visible Gaussians into (dk[0], dv); later passes alternate
+  // with (dk[1], order), so the fourth lands in proj.order
+  {
+    PassIn in{nullptr, nullptr, proj.depth, proj.tiles, uint32_t(n), nullptr};
+    if ((e = radix_pass<kFromDepth>(in, nb, 0, w.r, w.dk[0], w.dv, proj.n_visible, nullptr, nullptr, s)) !=
+        hipSuccess)
+      return e;
+  }
+  for (int pass = 1; pass < kDepthPasses; ++pass) {
+    const bool odd = pass & 1;
+    PassIn in{odd ? w.dk[0] : w.dk[1], odd ? w.dv : proj.order, nullptr, nullptr, 0u, proj.n_visible};
+    const bool last = pass == kDepthPasses - 1;
+    if ((e = radix_pass<kFromKeys>(in, nb, 8 * pass, w.r, odd ? w.dk[1] : w.dk[0], odd ? proj.order : w.dv,
+                                   nullptr, last ? proj.tiles : nullptr, last ? w.counts : nullptr, s)) !=
+        hipSuccess)
+      return e;
+  }
+  // offs: first pair of each visible Gaussian in depth order; offs[n] = the pair count
+  return launch_scan_u32(w.counts, proj.offs, n, w.r.total64, w.r.scan_ws, s);
+}
+
+size_t bin_sort_ws_bytes(uint32_t pairs) { return carve_pairs(nullptr, pairs, nullptr); }
 
 hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uint32_t pairs, uint32_t* keys,
                            uint32_t* vals, uint32_t* ranges, void* ws, hipStream_t s) {
@@ -300,30 +380,9 @@ hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uin
     fill_u32_kernel<<<div_up(2 * int64_t(num_tiles), 256), 256, 0, s>>>(ranges, 2 * int64_t(num_tiles), 0u);
   }
   if (pairs == 0) return hipGetLastError();
-  SortWs w;
-  carve(ws, n, pairs, &w);
+  PairWs w;
+  carve_pairs(ws, pairs, &w);
   hipError_t e;
-
-  // 1. visible Gaussians by (depth, id): the first pass compacts, the rest ping-pong
-  const int nbg = blocks_for(n);
-  {
-    PassIn in{nullptr, nullptr, proj.depth, proj.tiles, uint32_t(n), nullptr};
-    if ((e = radix_pass<kFromDepth>(in, nbg, 0, w, w.dk[0], w.dv[0], w.n_vis, s)) != hipSuccess) return e;
-  }
-  for (int pass = 1; pass < kDepthPasses; ++pass) {
-    const int src = (pass - 1) & 1;
-    PassIn in{w.dk[src], w.dv[src], nullptr, nullptr, 0u, w.n_vis};
-    if ((e = radix_pass<kFromKeys>(in, nbg, 8 * pass, w, w.dk[src ^ 1], w.dv[src ^ 1], nullptr, s)) != hipSuccess)
-      return e;
-  }
-  const uint32_t* sorted_ids = w.dv[(kDepthPasses - 1) & 1];
-
-  // 2. pairs in that order: (tile, Gaussian)
-  {
-    GSK_PROF("gather_counts", s);
-    gather_counts_kernel<<<div_up(n, 256), 256, 0, s>>>(sorted_ids, w.n_vis, proj.tiles, n, w.counts);
-  }
-  if ((e = launch_scan_u32(w.counts, w.pos, n, w.total64, w.scan_ws, s)) != hipSuccess) return e;
   const int tile_passes = (bits_for(uint32_t(num_tiles - 1)) + 7) / 8;
   // emit into the buffer that makes the last tile pass land in keys / vals
   uint32_t* k_src = (tile_passes & 1) ? w.keys_alt : keys;
@@ -332,16 +391,17 @@ hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uin
   uint32_t* v_dst = (tile_passes & 1) ? vals : w.vals_alt;
   {
     GSK_PROF("emit_pairs", s);
-    emit_pairs_kernel<<<div_up(pairs, 256), 256, 0, s>>>(w.pos, w.n_vis, sorted_ids,
-                                                         reinterpret_cast<const uint2*>(proj.rect), pairs, tx, k_src,
-                                                         v_src);
+    emit_pairs_kernel<<<div_up(pairs, 256), 256, 0, s>>>(proj.offs, proj.n_visible, proj.order,
+                                                         reinterpret_cast<const uint2*>(proj.rect), n, pairs, tx,
+                                                         k_src, v_src);
   }
-
-  // 3. stable sort of the pairs by tile
+  // stable sort of the pairs by tile
   const int nbp = blocks_for(pairs);
   for (int pass = 0; pass < tile_passes; ++pass) {
     PassIn in{k_src, v_src, nullptr, nullptr, pairs, nullptr};
-    if ((e = radix_pass<kFromKeys>(in, nbp, 8 * pass, w, k_dst, v_dst, nullptr, s)) != hipSuccess) return e;
+    if ((e = radix_pass<kFromKeys>(in, nbp, 8 * pass, w.r, k_dst, v_dst, nullptr, nullptr, nullptr, s)) !=
+        hipSuccess)
+      return e;
     uint32_t* tk = k_src; k_src = k_dst; k_dst = tk;
     uint32_t* tv = v_src; v_src = v_dst; v_dst = tv;
   }

@@ -3,10 +3,11 @@
  *
  * One training step for one camera is six calls, in this order:
  *
- *   gs_preprocess     project every Gaussian, count the 16x16 tiles it touches,
- *                     prefix-sum the counts; returns the number of (tile, Gaussian) pairs
+ *   gs_preprocess     project every Gaussian, count the 16x16 tiles it touches, order
+ *                     the visible ones by depth and prefix-sum their counts in that
+ *                     order; returns the number of (tile, Gaussian) pairs
  *   gs_bin_sort       order the (tile, Gaussian) pairs by tile, then depth, then id
- *                     (depth sort of the visible Gaussians, emission, stable tile sort),
+ *                     (emission in the depth order of gs_preprocess, stable tile sort),
  *                     find each tile's [start, end) range
  *   gs_render_fwd     front-to-back alpha blending per pixel
  *   gs_loss_l1_dssim  0.8 L1 + 0.2 (1 - SSIM) and its image gradient
@@ -25,8 +26,8 @@
  *   - Array arguments are DEVICE pointers owned by the caller, unless marked "host".
  *     The library never allocates, frees or retains caller memory.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
- *     enqueues work on that stream and returns, except gs_preprocess, which
- *     synchronises the stream once to read the pair count.
+ *     enqueues work on that stream and returns, except gs_preprocess, which waits
+ *     for the pair count.
  *   - Arrays are fp32 unless stated otherwise.  Per-Gaussian parameter arrays
  *     (params, gradients, Adam moments) use the blocked layout below; other
  *     per-Gaussian arrays are planar, [plane][n]; images are [channel][H][W].
@@ -86,14 +87,22 @@ typedef struct gs_scene {
 } gs_scene;
 
 /* Projected per-Gaussian state written by gs_preprocess and read by the later calls.
- * All members are device arrays of n entries (offs: n + 1) allocated by the caller. */
+ * Device arrays allocated by the caller. */
 typedef struct gs_proj {
-  float* splat;         /* [n][12] packed record: u, v, A, B, C, opacity, r, g, b, 0, 0, 0
-                           (screen centre, conic, opacity, clamped colour); zero when culled */
+  float* splat;         /* [n][12] packed record: u, v, A, B, C, opacity, r, g, b, hx, hy, 0
+                           (screen centre, conic, opacity, clamped colour, and the half-widths
+                           of a box around (u, v) outside which no pixel centre gets
+                           alpha >= 1/255: negative if none can, infinite if unbounded);
+                           zero when culled */
   float* depth;         /* [n] camera-space z (the sort key's low 32 bits) */
   uint32_t* rect;       /* [n][2] tile rectangle, inclusive: x0 | y0 << 16, x1 | y1 << 16 */
   uint32_t* tiles;      /* [n] tiles touched, 0 when culled */
-  uint32_t* offs;       /* [n + 1] exclusive prefix sum of tiles; offs[n] = pair count */
+  uint32_t* order;      /* [n] ids of the visible Gaussians (tiles > 0) ordered by depth, then id;
+                           the first *n_visible entries are written */
+  uint32_t* n_visible;  /* [1] number of visible Gaussians */
+  uint32_t* offs;       /* [n + 1] exclusive prefix sum of tiles[order[r]] over r (0 past the
+                           visible ones): offs[r] is the first pair of the r-th Gaussian in depth
+                           order; offs[n] = pair count */
 } gs_proj;
 
 /* Projection of every Gaussian and the tile count prefix sum.
@@ -106,10 +115,16 @@ typedef struct gs_proj {
  * clamped at 0).
  * The key path (camera-space depth, screen centre, extent, rectangle) is computed in IEEE
  * fp32 without contraction, with exp/log/sigmoid evaluated in fp64 and rounded once, so the
- * pair list is a deterministic function of the inputs.
+ * pair list is a deterministic function of the inputs.  The visible Gaussians are also put
+ * in depth order (stable radix sort of the depth bits, so ties keep id order) for the
+ * binning: out->order, out->n_visible and out->offs.
  * out: caller-allocated gs_proj for scene->n Gaussians.  total_pairs: HOST pointer,
- * receives offs[n].  ws: device workspace of gs_workspace_bytes(GS_WS_PREPROCESS, n, 0, 0, 0)
- * bytes.  Synchronises `stream` once.  GS_ERR_CAPACITY if the pair count exceeds 2^32 - 1. */
+ * receives the pair count (= offs[n]).  ws: device workspace of
+ * gs_workspace_bytes(GS_WS_PREPROCESS, n, 0, 0, 0) bytes.  Waits for the pair count only:
+ * it is copied to the host before the depth ordering is enqueued, which may still be
+ * running on `stream` when the call returns.  The library keeps one pinned 8-byte host
+ * word and one event per device and host thread for this copy.  GS_ERR_CAPACITY if the
+ * pair count exceeds 2^32 - 1. */
 int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out, uint32_t* total_pairs,
                       void* ws, size_t ws_bytes, void* stream);
 
@@ -118,13 +133,13 @@ int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out,
  * pair of a visible Gaussian i (tile count > 0; tiles in row-major order over its rectangle)
  * is produced once, and the pairs are ordered by tile id (ty * tiles_x + tx), then by the
  * Gaussian's depth (as the bits of the positive float, i.e. numerically), then by i -- the
- * order of the 64-bit key tile << 32 | bits(depth[i]) with ties by id.  Computed as a stable
- * radix sort of the visible Gaussians by depth, emission of their pairs in that order, and a
- * stable radix sort of the pairs by tile.
+ * order of the 64-bit key tile << 32 | bits(depth[i]) with ties by id.  Computed from the
+ * depth order gs_preprocess made: the pairs are emitted Gaussian by Gaussian in that order,
+ * then stably radix-sorted by tile.
  * keys[capacity]: tile id of each sorted pair; vals[capacity]: its Gaussian id; the first
  * total_pairs entries are written.  ranges: [2][tiles_x * tiles_y] u32, ranges[0][t] = first,
- * ranges[1][t] = one past the last pair of tile t ((0, 0) for an empty tile).  proj: the
- * depth, rect and tiles arrays of gs_preprocess (offs is not read); total_pairs must be the
+ * ranges[1][t] = one past the last pair of tile t ((0, 0) for an empty tile).  proj: as
+ * gs_preprocess left it (order, n_visible, offs and rect are read); total_pairs must be the
  * value gs_preprocess returned for the same proj.  ws: gs_workspace_bytes(GS_WS_BIN_SORT, n,
  * total_pairs, W, H).  GS_ERR_CAPACITY (nothing written) if capacity < total_pairs or the
  * workspace is short. */

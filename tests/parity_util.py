@@ -34,9 +34,11 @@ def proj_to_numpy(pl):
     splat = pl.proj.splat[:n].cpu().numpy()
     rect = pl.proj.rect[:n].cpu().numpy().view(np.uint32)
     out = dict(uv=splat[:, 0:2].T.copy(), conic=splat[:, 2:5].T.copy(), opac=splat[:, 5].copy(),
-               rgb=splat[:, 6:9].T.copy(), depth=pl.proj.depth[:n].cpu().numpy(),
+               rgb=splat[:, 6:9].T.copy(), box=splat[:, 9:11].T.copy(), depth=pl.proj.depth[:n].cpu().numpy(),
                tiles=pl.proj.tiles[:n].cpu().numpy().view(np.uint32),
-               offs=pl.proj.offs.cpu().numpy().view(np.uint32))
+               offs=pl.proj.offs.cpu().numpy().view(np.uint32),
+               order=pl.proj.order[:n].cpu().numpy().view(np.uint32),
+               n_visible=int(pl.proj.n_visible.cpu().numpy().view(np.uint32)[0]))
     r = np.zeros((4, n), np.int64)
     r[0] = rect[:, 0] & 0xFFFF
     r[1] = rect[:, 0] >> 16
@@ -67,8 +69,35 @@ def check_preprocess(gpu, ora):
     np.testing.assert_array_equal(gpu["conic"][:, vis], ora["conic"][:, vis])
     np.testing.assert_allclose(gpu["opac"][vis], ora["opac"][vis], rtol=2e-7, atol=0)
     np.testing.assert_allclose(gpu["rgb"][:, vis], ora["rgb"][:, vis], rtol=1e-6, atol=1e-6)
-    expect_offs = np.concatenate([[0], np.cumsum(ora["tiles"].astype(np.int64))]).astype(np.uint32)
+    check_blend_box(gpu, vis)
+    # depth order of the visible Gaussians: by the depth's bits, then by id
+    ids = np.nonzero(vis)[0]
+    order = ids[np.lexsort((ids, ora["depth"][ids].view(np.uint32)))]
+    assert gpu["n_visible"] == len(order)
+    np.testing.assert_array_equal(gpu["order"][:len(order)], order)
+    n = len(ora["tiles"])
+    counts = np.zeros(n, np.int64)
+    counts[:len(order)] = ora["tiles"][order]
+    expect_offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.uint32)
     np.testing.assert_array_equal(gpu["offs"], expect_offs)
+
+
+def check_blend_box(gpu, vis):
+    """The box (u +- hx, v +- hy) must contain every point where o exp(-e) >= 1/255 for
+    e = (A dx^2 + C dy^2) / 2 + B dx dy with the record's own conic: the ellipse's
+    half-widths sqrt(2 t C / (A C - B^2)), sqrt(2 t A / (A C - B^2)), t = ln(255 o)."""
+    A, B, C = (gpu["conic"][k][vis].astype(np.float64) for k in range(3))
+    o = gpu["opac"][vis].astype(np.float64)
+    hx, hy = gpu["box"][0][vis], gpu["box"][1][vis]
+    t = np.log(255.0 * o)
+    none = t <= -1e-3
+    assert np.all(hx[none] < 0) and np.all(hy[none] < 0)
+    det = A * C - B * B
+    ok = ~none & (det > 0)
+    need_x = np.sqrt(2 * np.maximum(t[ok], 0) * C[ok] / det[ok])
+    need_y = np.sqrt(2 * np.maximum(t[ok], 0) * A[ok] / det[ok])
+    assert np.all(hx[ok] >= need_x) and np.all(hy[ok] >= need_y)
+    assert np.all(np.isinf(hx[~none & ~(det > 0)]))
 
 
 def check_render(gpu, ora, margin=MARGIN):
