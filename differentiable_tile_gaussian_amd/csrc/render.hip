@@ -190,17 +190,39 @@ __device__ inline uint32_t quad_mask(float u, float v, float bx, float by, float
   return uint32_t(xl && yt) | (uint32_t(xr && yt) << 1) | (uint32_t(xl && yb) << 2) | (uint32_t(xr && yb) << 3);
 }
 
-// The walking wave's bits of a batch's masks, 64 entries per word.
-__device__ inline uint64_t quad_bits(const uint32_t* m, int group) {
+// Index of a zero-opacity record after each batch (alpha 0: blending it changes nothing).
+constexpr int kPad = kBatch;
+constexpr int kListLen = kBatch + 4;
+
+// Writes to list, in increasing order, the entries 0 .. last of a batch whose bit for
+// the calling wave's quadrant is set, padded with kPad to a multiple of 4; returns
+// the padded length.  Wave-local: the list is read back by the same wave.
+__device__ inline int build_list(const uint32_t* m, int last, uint16_t* list) {
+  const int lane = __lane_id();
   const uint32_t quad = threadIdx.x >> 6;
-  return __ballot((m[group * 64 + __lane_id()] >> quad) & 1u);
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  int cnt = 0;
+  for (int grp = 0; grp < kBatch / 64 && grp * 64 <= last; ++grp) {
+    const int e = grp * 64 + lane;
+    const bool bit = e <= last && ((m[e] >> quad) & 1u);
+    const uint64_t bal = __ballot(bit);
+    if (bit) list[cnt + __popcll(bal & below)] = uint16_t(e);
+    cnt += __popcll(bal);
+  }
+  const int pad = (4 - (cnt & 3)) & 3;
+  if (lane < pad) list[cnt + lane] = uint16_t(kPad);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  return cnt + pad;
 }
 
 struct FwdLds {
-  float4 a[2][kBatch];   // u, v, a', b'
-  float4 b[2][kBatch];   // c', opacity, r, g
-  float c[2][kBatch];    // b
-  uint32_t m[2][kBatch]; // quadrant masks
+  float4 a[2][kBatch + 1];    // u, v, a', b'  (entry kPad: zero record)
+  float4 b[2][kBatch + 1];    // c', opacity, r, g
+  float c[2][kBatch + 1];     // b
+  uint32_t m[2][kBatch];      // quadrant masks
+  uint16_t list[4][kListLen]; // per wave: the batch entries it walks
 };
 
 __device__ inline void stage_fwd(const float4* __restrict__ splat, uint32_t g, float ox, float oy, float4& a,
@@ -234,8 +256,14 @@ __device__ void fwd_walk(FwdLds& L, const float4* __restrict__ splat, const uint
     uint32_t m = 0u;
     if (lo + tid < hi) stage_fwd(splat, vals[start + uint32_t(lo + tid)], ox, oy, a, b, c, m);
     L.a[0][tid] = a; L.b[0][tid] = b; L.c[0][tid] = c; L.m[0][tid] = m;
+    if (tid < 2) {
+      L.a[tid][kPad] = make_float4(0.f, 0.f, 0.f, 0.f);
+      L.b[tid][kPad] = make_float4(0.f, 0.f, 0.f, 0.f);
+      L.c[tid][kPad] = 0.f;
+    }
   }
   __syncthreads();
+  uint16_t* list = L.list[tid >> 6];
   bool reported = s.done;
   int buf = 0;
   for (int base = lo; base < hi; base += kBatch) {
@@ -246,33 +274,27 @@ __device__ void fwd_walk(FwdLds& L, const float4* __restrict__ splat, const uint
     if (nxt < hi) stage_fwd(splat, vals[start + uint32_t(nxt)], ox, oy, na, nb, nc, nm);
     // walk the batch entries whose quadrant bit is set, in order, four at a time
     bool all_done = __all(s.done);
-    for (int grp = 0; grp < kBatch / 64 && !all_done; ++grp) {
-      uint64_t bits = quad_bits(L.m[buf], grp);
-      while (bits && !all_done) {
-        int e[4];
-        bool v[4];
+    if (!all_done) {
+      const int len = build_list(L.m[buf], kBatch - 1, list);
+      for (int k = 0; k < len && !all_done; k += 4) {
+        const uint2 ix = *reinterpret_cast<const uint2*>(list + k);
+        const int e[4] = {int(ix.x & 0xffffu), int(ix.x >> 16), int(ix.y & 0xffffu), int(ix.y >> 16)};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          v[k] = bits != 0;
-          e[k] = grp * 64 + (v[k] ? int(__builtin_ctzll(bits)) : 0);
-          bits &= bits - 1;
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float4 a = L.a[buf][e[k]];
-          const float4 b = L.b[buf][e[k]];
-          const float cb = L.c[buf][e[k]];
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 a = L.a[buf][e[q4]];
+          const float4 b = L.b[buf][e[q4]];
+          const float cb = L.c[buf][e[q4]];
           const float dx = fx - a.x, dy = fy - a.y;
           const float q = a.z * dx * dx + a.w * dx * dy + b.x * dy * dy;
           float alpha = fminf(kAlphaCap, b.y * fast_exp2(q));
-          const bool ok = v[k] && !s.done && alpha >= kAlphaMin;
+          const bool ok = !s.done && alpha >= kAlphaMin;
           alpha = ok ? alpha : 0.0f;
           const float w = alpha * s.T;
           s.c0 += w * b.z;
           s.c1 += w * b.w;
           s.c2 += w * cb;
           s.T = s.T * (1.0f - alpha);
-          s.last = ok ? uint32_t(base + e[k] + 1) : s.last;
+          s.last = ok ? uint32_t(base + e[q4] + 1) : s.last;
           s.done = s.done || (pre * s.T < kTStop);
         }
         all_done = __all(s.done);
@@ -577,6 +599,7 @@ struct BwdLds {
   uint32_t id[2][kBatch];
   uint32_t m[2][kBatch];   // quadrant masks
   float acc[9][kBatch];    // per-entry sums over the block's waves
+  uint16_t list[4][kListLen];
   uint32_t top;
 };
 
@@ -624,6 +647,7 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
     L.a[0][tid] = a; L.b[0][tid] = b; L.c[0][tid] = c; L.id[0][tid] = g; L.m[0][tid] = m;
   }
   __syncthreads();
+  uint16_t* list = L.list[tid >> 6];
   int buf = 0;
   while (hi > lo) {
     const int blo = max(hi - kBatch, lo);
@@ -636,53 +660,47 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
     }
     // entries 0 .. etop of the batch whose quadrant bit is set, last to first
     const int etop = min(hi, wave_top) - 1 - blo;
-    for (int grp = kBatch / 64 - 1; grp >= 0; --grp) {
-      if (grp * 64 > etop) continue;
-      uint64_t bits = quad_bits(L.m[buf], grp);
-      const int top_bit = etop - grp * 64;
-      if (top_bit < 63) bits &= (uint64_t(2) << top_bit) - 1;
-      while (bits) {
-        const int eb = 63 - int(__builtin_clzll(bits));
-        bits &= ~(uint64_t(1) << eb);
-        const int e = grp * 64 + eb;
-        const int j = blo + e;
-        const float4 a = L.a[buf][e];
-        const float4 b = L.b[buf][e];
-        const float4 c = L.c[buf][e];
-        const float dx = fx - a.x, dy = fy - a.y;
-        const float q = a.z * dx * dx + a.w * dx * dy + b.x * dy * dy;
-        const float G = fast_exp2(q);
-        const float araw = b.y * G;
-        const float alpha = fminf(kAlphaCap, araw);
-        const bool ok = j < s.top && alpha >= kAlphaMin;
-        if (__ballot(ok) == 0) continue;
-        float v[9];
-        const float inv = __builtin_amdgcn_rcpf(1.0f - alpha);
-        const float Tn = s.T * inv;           // transmittance in front of this pair
-        const float w = alpha * Tn;
-        const float galpha =
-            s.g0 * (b.z * Tn - s.S0 * inv) + s.g1 * (b.w * Tn - s.S1 * inv) + s.g2 * (c.x * Tn - s.S2 * inv);
-        const bool unc = ok && araw <= kAlphaCap;
-        const float ge = unc ? -galpha * araw : 0.0f;
-        v[0] = -ge * (c.y * dx + c.z * dy);
-        v[1] = -ge * (c.z * dx + c.w * dy);
-        v[2] = ge * 0.5f * dx * dx;
-        v[3] = ge * dx * dy;
-        v[4] = ge * 0.5f * dy * dy;
-        v[5] = unc ? galpha * G : 0.0f;
-        v[6] = ok ? s.g0 * w : 0.0f;
-        v[7] = ok ? s.g1 * w : 0.0f;
-        v[8] = ok ? s.g2 * w : 0.0f;
-        if (ok) {
-          s.S0 += b.z * w;
-          s.S1 += b.w * w;
-          s.S2 += c.x * w;
-          s.T = Tn;
-        }
-        wave_sum9(v);
-        if ((lane & 7) == 0) atomicAdd(&L.acc[lane >> 3][e], v[0]);
-        if (lane == 0) atomicAdd(&L.acc[8][e], v[8]);
+    int len = etop >= 0 ? build_list(L.m[buf], etop, list) : 0;
+    while (len > 0 && list[len - 1] == uint16_t(kPad)) --len;
+    for (int k = len - 1; k >= 0; --k) {
+      const int e = list[k];
+      const int j = blo + e;
+      const float4 a = L.a[buf][e];
+      const float4 b = L.b[buf][e];
+      const float4 c = L.c[buf][e];
+      const float dx = fx - a.x, dy = fy - a.y;
+      const float q = a.z * dx * dx + a.w * dx * dy + b.x * dy * dy;
+      const float G = fast_exp2(q);
+      const float araw = b.y * G;
+      const float alpha = fminf(kAlphaCap, araw);
+      const bool ok = j < s.top && alpha >= kAlphaMin;
+      if (__ballot(ok) == 0) continue;
+      float v[9];
+      const float inv = __builtin_amdgcn_rcpf(1.0f - alpha);
+      const float Tn = s.T * inv;           // transmittance in front of this pair
+      const float w = alpha * Tn;
+      const float galpha =
+          s.g0 * (b.z * Tn - s.S0 * inv) + s.g1 * (b.w * Tn - s.S1 * inv) + s.g2 * (c.x * Tn - s.S2 * inv);
+      const bool unc = ok && araw <= kAlphaCap;
+      const float ge = unc ? -galpha * araw : 0.0f;
+      v[0] = -ge * (c.y * dx + c.z * dy);
+      v[1] = -ge * (c.z * dx + c.w * dy);
+      v[2] = ge * 0.5f * dx * dx;
+      v[3] = ge * dx * dy;
+      v[4] = ge * 0.5f * dy * dy;
+      v[5] = unc ? galpha * G : 0.0f;
+      v[6] = ok ? s.g0 * w : 0.0f;
+      v[7] = ok ? s.g1 * w : 0.0f;
+      v[8] = ok ? s.g2 * w : 0.0f;
+      if (ok) {
+        s.S0 += b.z * w;
+        s.S1 += b.w * w;
+        s.S2 += c.x * w;
+        s.T = Tn;
       }
+      wave_sum9(v);
+      if ((lane & 7) == 0) atomicAdd(&L.acc[lane >> 3][e], v[0]);
+      if (lane == 0) atomicAdd(&L.acc[8][e], v[8]);
     }
     if (nlo < nhi) {
       L.a[buf ^ 1][tid] = na; L.b[buf ^ 1][tid] = nb; L.c[buf ^ 1][tid] = ncr; L.id[buf ^ 1][tid] = ng;
