@@ -34,8 +34,14 @@
 // recovering T by division and carrying S ([DR] "The trick"); every entry's nine
 // partials are summed over the wave (transposed butterfly), then over the block's
 // waves in LDS, then added to the Gaussian's gradient with one set of global
-// atomics per (tile or chunk, Gaussian).  Split tiles run one block per chunk, each
-// starting from the boundary state the forward left.
+// atomics per (tile or chunk, Gaussian).  The geometric partials are summed as the
+// moments of dL/de (dx, dy, dx^2, dx dy, dy^2 weighted); the conic turns them into
+// du, dv, dA, dB, dC once per entry when the block flushes its sums.  Split tiles run
+// one block per chunk, each starting from the boundary state the forward left.
+//
+// Both walks skip, per 8x8 quadrant, the pairs whose box (stored by the projection:
+// no pixel centre outside it reaches alpha >= 1/255) misses the quadrant; each wave
+// walks a list of the batch entries its quadrant needs.
 //
 // The conic is prescaled when staged: q = a' dx^2 + b' dx dy + c' dy^2 with
 // (a', b', c') = -log2(e) (A/2, B, C/2), so the Gaussian factor exp(-e) is one exp2.
@@ -675,29 +681,31 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
       const float alpha = fminf(kAlphaCap, araw);
       const bool ok = j < s.top && alpha >= kAlphaMin;
       if (__ballot(ok) == 0) continue;
-      float v[9];
-      const float inv = __builtin_amdgcn_rcpf(1.0f - alpha);
+      // a pixel that does not blend this pair sees alpha 0: 1 / (1 - 0) is exactly 1,
+      // so its T and S come through unchanged and all its partials are 0
+      const float a_ok = ok ? alpha : 0.0f;
+      const float inv = __builtin_amdgcn_rcpf(1.0f - a_ok);
       const float Tn = s.T * inv;           // transmittance in front of this pair
-      const float w = alpha * Tn;
+      const float w = a_ok * Tn;
       const float galpha =
           s.g0 * (b.z * Tn - s.S0 * inv) + s.g1 * (b.w * Tn - s.S1 * inv) + s.g2 * (c.x * Tn - s.S2 * inv);
       const bool unc = ok && araw <= kAlphaCap;
-      const float ge = unc ? -galpha * araw : 0.0f;
-      v[0] = -ge * (c.y * dx + c.z * dy);
-      v[1] = -ge * (c.z * dx + c.w * dy);
-      v[2] = ge * 0.5f * dx * dx;
-      v[3] = ge * dx * dy;
-      v[4] = ge * 0.5f * dy * dy;
+      const float ge = unc ? -galpha * araw : 0.0f;   // dL/de
+      // the moments of dL/de over the pixels; the conic is applied when they are flushed
+      float v[9];
+      v[0] = ge * dx;
+      v[1] = ge * dy;
+      v[2] = v[0] * dx;
+      v[3] = v[0] * dy;
+      v[4] = v[1] * dy;
       v[5] = unc ? galpha * G : 0.0f;
-      v[6] = ok ? s.g0 * w : 0.0f;
-      v[7] = ok ? s.g1 * w : 0.0f;
-      v[8] = ok ? s.g2 * w : 0.0f;
-      if (ok) {
-        s.S0 += b.z * w;
-        s.S1 += b.w * w;
-        s.S2 += c.x * w;
-        s.T = Tn;
-      }
+      v[6] = s.g0 * w;
+      v[7] = s.g1 * w;
+      v[8] = s.g2 * w;
+      s.S0 += b.z * w;
+      s.S1 += b.w * w;
+      s.S2 += c.x * w;
+      s.T = Tn;
       wave_sum9(v);
       if ((lane & 7) == 0) atomicAdd(&L.acc[lane >> 3][e], v[0]);
       if (lane == 0) atomicAdd(&L.acc[8][e], v[8]);
@@ -708,13 +716,24 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
     }
     __syncthreads();
     if (tid < hi - blo) {
+      // e = (A dx^2 + C dy^2) / 2 + B dx dy: du = -(A M_x + B M_y), dv = -(B M_x + C M_y),
+      // dA = M_xx / 2, dB = M_xy, dC = M_yy / 2 for the moments M of dL/de
       const uint32_t g = L.id[buf][tid];
+      const float4 cn = L.c[buf][tid];   // b, A, B, C
+      float val[9];
 #pragma unroll
       for (int k = 0; k < 9; ++k) {
-        const float val = L.acc[k][tid];
-        if (val != 0.0f) atomicAdd(&gscreen[k * n + g], val);
+        val[k] = L.acc[k][tid];
         L.acc[k][tid] = 0.0f;
       }
+      const float mx = val[0], my = val[1];
+      val[0] = -(cn.y * mx + cn.z * my);
+      val[1] = -(cn.z * mx + cn.w * my);
+      val[2] *= 0.5f;
+      val[4] *= 0.5f;
+#pragma unroll
+      for (int k = 0; k < 9; ++k)
+        if (val[k] != 0.0f) atomicAdd(&gscreen[k * n + g], val[k]);
     }
     __syncthreads();
     hi = blo;
