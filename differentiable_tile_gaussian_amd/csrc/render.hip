@@ -741,17 +741,31 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
   }
 }
 
-// Every tile's first segment (the whole list for tiles that were not split).
-__global__ void __launch_bounds__(256) render_bwd_kernel(const float4* __restrict__ splat,
-                                                          const uint32_t* __restrict__ vals,
-                                                          const uint32_t* __restrict__ ranges, SplitWs ws,
-                                                          int num_tiles, int tx, int W, int H, float bg0, float bg1,
-                                                          float bg2, int first, const float* __restrict__ T_final,
-                                                          const uint32_t* __restrict__ n_contrib,
-                                                          const float* __restrict__ dL_dimg, int n,
-                                                          float* __restrict__ gscreen) {
-  __shared__ BwdLds L;
-  const int tile = int(ws.order[blockIdx.x]);
+struct BwdArgs {
+  const float4* splat;
+  const uint32_t* vals;
+  const uint32_t* ranges;
+  int num_tiles, tx, W, H;
+  float bg0, bg1, bg2;
+  int first, chunk;
+  const float* T_final;
+  const uint32_t* n_contrib;
+  const float* dL_dimg;
+  int n;
+  float* gscreen;
+};
+
+// A tile's first segment (the whole list for tiles that were not split).
+__device__ void bwd_tile(BwdLds& L, const BwdArgs& A, const SplitWs& ws, int tile) {
+  const float4* __restrict__ splat = A.splat;
+  const uint32_t* __restrict__ vals = A.vals;
+  const uint32_t* __restrict__ ranges = A.ranges;
+  const int tx = A.tx, W = A.W, H = A.H, first = A.first, n = A.n;
+  const float bg0 = A.bg0, bg1 = A.bg1, bg2 = A.bg2;
+  const float* __restrict__ T_final = A.T_final;
+  const uint32_t* __restrict__ n_contrib = A.n_contrib;
+  const float* __restrict__ dL_dimg = A.dL_dimg;
+  float* __restrict__ gscreen = A.gscreen;
   const int tid = threadIdx.x;
   const int px = (tile % tx) * kTile + pixel_x(tid);
   const int py = (tile / tx) * kTile + pixel_y(tid);
@@ -779,19 +793,17 @@ __global__ void __launch_bounds__(256) render_bwd_kernel(const float4* __restric
            gscreen);
 }
 
-// One block per chunk of a split tile.
-__global__ void __launch_bounds__(256) split_bwd_kernel(const float4* __restrict__ splat,
-                                                         const uint32_t* __restrict__ vals,
-                                                         const uint32_t* __restrict__ ranges, SplitWs ws,
-                                                         int num_tiles, int tx, int W, int H, float bg0, float bg1,
-                                                         float bg2, int first, int chunk,
-                                                         const float* __restrict__ T_final,
-                                                         const uint32_t* __restrict__ n_contrib,
-                                                         const float* __restrict__ dL_dimg, int n,
-                                                         float* __restrict__ gscreen) {
-  __shared__ BwdLds L;
-  const uint32_t item = blockIdx.x;
-  if (item >= ws.counters[1]) return;
+// One chunk of a split tile.
+__device__ void bwd_chunk(BwdLds& L, const BwdArgs& A, const SplitWs& ws, uint32_t item) {
+  const float4* __restrict__ splat = A.splat;
+  const uint32_t* __restrict__ vals = A.vals;
+  const uint32_t* __restrict__ ranges = A.ranges;
+  const int num_tiles = A.num_tiles, tx = A.tx, W = A.W, H = A.H, first = A.first, chunk = A.chunk, n = A.n;
+  const float bg0 = A.bg0, bg1 = A.bg1, bg2 = A.bg2;
+  const float* __restrict__ T_final = A.T_final;
+  const uint32_t* __restrict__ n_contrib = A.n_contrib;
+  const float* __restrict__ dL_dimg = A.dL_dimg;
+  float* __restrict__ gscreen = A.gscreen;
   const uint2 sc = ws.items[item];
   const uint32_t slot = sc.x, c = sc.y;
   const int tile = int(ws.slot_tile[slot]);
@@ -822,6 +834,23 @@ __global__ void __launch_bounds__(256) split_bwd_kernel(const float4* __restrict
   }
   bwd_walk(L, splat, vals, start, lo, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f, float(py) + 0.5f, s, n,
            gscreen);
+}
+
+// The backward of every tile's first segment and of every chunk of the split tiles,
+// in one launch: blocks [0, num_tiles) take the tiles longest first, the blocks
+// after them the chunks, which are independent of the first segments (each starts
+// from the state the forward left at its end) and so fill the CUs that the last
+// long first segments leave idle.
+__global__ void __launch_bounds__(256) render_bwd_kernel(BwdArgs A, SplitWs ws) {
+  __shared__ BwdLds L;
+  const uint32_t b = blockIdx.x;
+  if (b < uint32_t(A.num_tiles)) {
+    bwd_tile(L, A, ws, int(ws.order[b]));
+  } else {
+    const uint32_t item = b - uint32_t(A.num_tiles);
+    if (item >= ws.counters[1]) return;
+    bwd_chunk(L, A, ws, item);
+  }
 }
 
 __global__ void zero_f32_kernel(float* __restrict__ p, int64_t count) {
@@ -905,19 +934,12 @@ hipError_t launch_render_bwd(const gs_proj& proj, int n, const uint32_t* vals, c
     GSK_PROF("zero_f32", s);
     zero_f32_kernel<<<div_up(9 * int64_t(n), 256), 256, 0, s>>>(gscreen, 9 * int64_t(n));
   }
+  const BwdArgs A{splat, vals, ranges, num_tiles, tx, cam.width, cam.height, cam.bg[0], cam.bg[1], cam.bg[2],
+                  g_first, g_chunk, T_final, n_contrib, dL_dimg, n, gscreen};
+  const unsigned blocks = unsigned(num_tiles) + (pairs > uint32_t(g_first) ? unsigned(d.I) : 0u);
   {
     GSK_PROF("render_bwd", s);
-    render_bwd_kernel<<<num_tiles, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, cam.width, cam.height,
-                                                cam.bg[0], cam.bg[1], cam.bg[2], g_first, T_final, n_contrib, dL_dimg,
-                                                n, gscreen);
-  }
-  if (pairs > uint32_t(g_first)) {
-    {
-      GSK_PROF("split_bwd", s);
-      split_bwd_kernel<<<unsigned(d.I), 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, cam.width, cam.height,
-                                                     cam.bg[0], cam.bg[1], cam.bg[2], g_first, g_chunk, T_final,
-                                                     n_contrib, dL_dimg, n, gscreen);
-    }
+    render_bwd_kernel<<<blocks, 256, 0, s>>>(A, ws);
   }
   return hipGetLastError();
 }
