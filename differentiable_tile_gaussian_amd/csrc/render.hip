@@ -439,20 +439,34 @@ __global__ void __launch_bounds__(256) split_combine_kernel(SplitWs ws) {
       stop = 0;
     } else {
       stop = int32_t(nch);
-      for (uint32_t c = 1; c < nch; ++c) {
-        const size_t oc = size_t(fi + c) * 256 + tid;
-        const float4 pc = ws.part4[oc];
-        const float Tn = T * pc.x;
-        if (Tn < kTStop) {
-          stop = int32_t(c);
-          break;
+      // chunks in groups of eight: their partials are loaded before they are chained
+      constexpr int kG = 8;
+      for (uint32_t c0g = 1; c0g < nch && stop == int32_t(nch); c0g += kG) {
+        float4 pc[kG];
+        uint32_t lc[kG];
+#pragma unroll
+        for (int k = 0; k < kG; ++k) {
+          const uint32_t c = c0g + k;
+          if (c < nch) {
+            pc[k] = ws.part4[size_t(fi + c) * 256 + tid];
+            lc[k] = ws.partl[size_t(fi + c) * 256 + tid] & kIdx;
+          }
         }
-        const float a0 = T * pc.y, a1 = T * pc.z, a2 = T * pc.w;
-        ws.part4[oc] = make_float4(Tn, a0, a1, a2);   // T at the chunk end, colour it added
-        c0 += a0; c1 += a1; c2 += a2;
-        T = Tn;
-        const uint32_t lc = ws.partl[oc] & kIdx;
-        if (lc) last = lc;
+#pragma unroll
+        for (int k = 0; k < kG; ++k) {
+          const uint32_t c = c0g + k;
+          if (c >= nch || stop != int32_t(nch)) break;
+          const float Tn = T * pc[k].x;
+          if (Tn < kTStop) {
+            stop = int32_t(c);
+            break;
+          }
+          const float a0 = T * pc[k].y, a1 = T * pc[k].z, a2 = T * pc[k].w;
+          ws.part4[size_t(fi + c) * 256 + tid] = make_float4(Tn, a0, a1, a2);   // T at the chunk end, colour it added
+          c0 += a0; c1 += a1; c2 += a2;
+          T = Tn;
+          if (lc[k]) last = lc[k];
+        }
       }
     }
   }
@@ -534,11 +548,19 @@ __global__ void __launch_bounds__(256) split_finalize_kernel(SplitWs ws, int tx,
   } else {
     c = int(nch);
   }
-  for (--c; c >= 0; --c) {
-    const size_t oc = size_t(fi + uint32_t(c)) * 256 + tid;
-    const float4 pc = ws.part4[oc];
-    ws.part4[oc] = make_float4(pc.x, S0, S1, S2);
-    S0 += pc.y; S1 += pc.z; S2 += pc.w;
+  // chunks c - 1 .. 0, back to front, in groups of eight loaded ahead
+  constexpr int kG = 8;
+  for (int top = c - 1; top >= 0; top -= kG) {
+    float4 pc[kG];
+#pragma unroll
+    for (int k = 0; k < kG; ++k)
+      if (top - k >= 0) pc[k] = ws.part4[size_t(fi + uint32_t(top - k)) * 256 + tid];
+#pragma unroll
+    for (int k = 0; k < kG; ++k) {
+      if (top - k < 0) break;
+      ws.part4[size_t(fi + uint32_t(top - k)) * 256 + tid] = make_float4(pc[k].x, S0, S1, S2);
+      S0 += pc[k].y; S1 += pc[k].z; S2 += pc[k].w;
+    }
   }
   ws.bnd1[so] = make_float4(ws.st4[so].x, S0, S1, S2);
 }
