@@ -177,38 +177,41 @@ __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
   }
 }
 
+// For every block of 256 pairs, the visible Gaussian (in depth order) that owns its
+// first pair: Gaussian r owns pairs [offs[r], offs[r + 1]) and marks the blocks
+// whose first pair falls there.  One thread per Gaussian.
+__global__ void __launch_bounds__(256) block_starts_kernel(const uint32_t* __restrict__ offs,
+                                                            const uint32_t* __restrict__ n_vis, int n,
+                                                            uint32_t pairs, uint32_t* __restrict__ block_first) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n || uint32_t(r) >= *n_vis) return;
+  const uint32_t b0 = (offs[r] + 255u) >> 8, e = min(offs[r + 1], pairs);
+  for (uint32_t b = b0; (b << 8) < e; ++b) block_first[b] = uint32_t(r);
+}
+
 // One thread per pair: the Gaussian (in depth order) that owns it, and its tile.
 // offs[r] is the first pair of the r-th visible Gaussian in depth order.  The
-// block's 256 pairs belong to at most 256 consecutive Gaussians: two searches in
-// global memory find them, their offsets go to LDS, and each thread searches there.
+// block's 256 pairs belong to at most 256 consecutive Gaussians starting with
+// block_first[block]; their offsets go to LDS and each thread searches there.
 __global__ void __launch_bounds__(256) emit_pairs_kernel(const uint32_t* __restrict__ offs,
                                                           const uint32_t* __restrict__ n_vis,
+                                                          const uint32_t* __restrict__ block_first,
                                                           const uint32_t* __restrict__ order,
                                                           const uint2* __restrict__ rect, int n, uint32_t pairs,
                                                           int tx, uint32_t* __restrict__ keys,
                                                           uint32_t* __restrict__ vals) {
   __shared__ uint32_t s_offs[256];
-  __shared__ int s_r[2];
   const uint32_t p0 = blockIdx.x * 256u;
-  if (threadIdx.x < 2) {
-    // largest r with offs[r] <= target; offs is strictly increasing over the visible Gaussians
-    const uint32_t last = p0 + 255u < pairs ? p0 + 255u : pairs - 1u;
-    const uint32_t target = threadIdx.x == 0 ? p0 : last;
-    int lo = 0, hi = int(*n_vis) - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (offs[mid] <= target) lo = mid; else hi = mid - 1;
-    }
-    s_r[threadIdx.x] = lo;
-  }
-  __syncthreads();
-  const int r0 = s_r[0];
-  const int k = min(s_r[1] - r0 + 1, 256);
-  if (int(threadIdx.x) < k) s_offs[threadIdx.x] = offs[r0 + int(threadIdx.x)];
+  const int nv = int(*n_vis);
+  const uint32_t bf = block_first[blockIdx.x];
+  const int r0 = int(bf < uint32_t(nv) ? bf : uint32_t(max(nv - 1, 0)));
+  // Gaussians past the visible ones (or past the block) get an offset above every pair
+  const int k = min(256, nv - r0);
+  s_offs[threadIdx.x] = int(threadIdx.x) < k ? offs[r0 + int(threadIdx.x)] : 0xffffffffu;
   __syncthreads();
   const uint32_t p = p0 + threadIdx.x;
   if (p >= pairs) return;
-  int lo = 0, hi = k - 1;
+  int lo = 0, hi = max(k, 1) - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (s_offs[mid] <= p) lo = mid; else hi = mid - 1;
@@ -300,6 +303,7 @@ size_t carve_depth(void* ws, int64_t n, DepthWs* out) {
 
 struct PairWs {
   uint32_t *keys_alt, *vals_alt;   // pairs each
+  uint32_t* block_first;           // one per 256 pairs
   RadixWs r;
 };
 
@@ -308,6 +312,7 @@ size_t carve_pairs(void* ws, uint32_t pairs, PairWs* out) {
   PairWs w;
   w.keys_alt = c.take(size_t(pairs) * 4);
   w.vals_alt = c.take(size_t(pairs) * 4);
+  w.block_first = c.take(size_t(div_up(pairs > 0 ? pairs : 1, 256)) * 4);
   w.r = carve_radix(c, blocks_for(pairs), 0);
   if (out) *out = w;
   return c.off;
@@ -390,8 +395,12 @@ hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uin
   uint32_t* k_dst = (tile_passes & 1) ? keys : w.keys_alt;
   uint32_t* v_dst = (tile_passes & 1) ? vals : w.vals_alt;
   {
+    GSK_PROF("block_starts", s);
+    block_starts_kernel<<<div_up(n, 256), 256, 0, s>>>(proj.offs, proj.n_visible, n, pairs, w.block_first);
+  }
+  {
     GSK_PROF("emit_pairs", s);
-    emit_pairs_kernel<<<div_up(pairs, 256), 256, 0, s>>>(proj.offs, proj.n_visible, proj.order,
+    emit_pairs_kernel<<<div_up(pairs, 256), 256, 0, s>>>(proj.offs, proj.n_visible, w.block_first, proj.order,
                                                          reinterpret_cast<const uint2*>(proj.rect), n, pairs, tx,
                                                          k_src, v_src);
   }
