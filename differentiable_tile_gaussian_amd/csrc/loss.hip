@@ -7,7 +7,9 @@
 //
 // The 2-D window is the outer product of the normalised 1-D window, so the five
 // local moments are computed with a horizontal then a vertical 11-tap pass through
-// LDS (32x16 output pixels per block, 5-pixel halo).
+// LDS (32x16 output pixels per block, 5-pixel halo).  Each thread makes four
+// adjacent outputs of a row in the horizontal pass (14 inputs read once) and two
+// adjacent rows of a column in the vertical pass, reusing the taps in registers.
 //   ssim_fwd   moments -> SSIM per pixel, the three derivative maps
 //                a = dS/dmu_x - 2 mu_x dS/dvar_x - mu_y dS/dcov,  b = dS/dvar_x,  c = dS/dcov,
 //              and per-block partial sums of SSIM and |x - y|
@@ -46,13 +48,20 @@ __device__ inline void reduce_block_2(float& a, float& b, float* s_tmp) {
   }
 }
 
+// Horizontal pass for row r: outputs 4g .. 4g+3 of the 32-wide tile from the 14 inputs
+// 4g .. 4g+13 of the 42-wide row (each input read once into registers).
+constexpr int kHG = 4;                  // outputs per thread, horizontal
+constexpr int kHItems = kPH * (kTW / kHG);   // 208 (row, group) items
+constexpr int kVG = 2;                  // outputs per thread, vertical
+static_assert((kTW * kTH) / kVG == 256, "one vertical item per thread");
+
 __global__ void __launch_bounds__(256) ssim_fwd_kernel(const float* __restrict__ img, const float* __restrict__ tgt,
                                                         int H, int W, Window win, float* __restrict__ amap,
                                                         float* __restrict__ bmap, float* __restrict__ cmap,
                                                         float* __restrict__ partial) {
   __shared__ float sx[kPH][kPW + 1];
   __shared__ float sy[kPH][kPW + 1];
-  __shared__ float hs[5][kPH][kTW + 1];
+  __shared__ float4 hs[5][kPH][kTW / 4];   // horizontal sums of x, y, xx, yy, xy
   __shared__ float s_tmp[8];
   const int ch = blockIdx.z;
   const int x0 = blockIdx.x * kTW, y0 = blockIdx.y * kTH;
@@ -67,51 +76,78 @@ __global__ void __launch_bounds__(256) ssim_fwd_kernel(const float* __restrict__
     sy[r][c] = in ? Y[size_t(gy) * W + gx] : 0.0f;
   }
   __syncthreads();
-  for (int k = threadIdx.x; k < kPH * kTW; k += 256) {
-    const int r = k / kTW, c = k % kTW;
-    float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f, m4 = 0.f;
+  if (threadIdx.x < kHItems) {
+    const int r = threadIdx.x / (kTW / kHG), g = threadIdx.x % (kTW / kHG);
+    float xv[kHG + 10], yv[kHG + 10];
 #pragma unroll
-    for (int j = 0; j < 11; ++j) {
-      const float xv = sx[r][c + j], yv = sy[r][c + j], wj = win.w[j];
-      m0 += wj * xv;
-      m1 += wj * yv;
-      m2 += wj * xv * xv;
-      m3 += wj * yv * yv;
-      m4 += wj * xv * yv;
+    for (int j = 0; j < kHG + 10; ++j) {
+      xv[j] = sx[r][kHG * g + j];
+      yv[j] = sy[r][kHG * g + j];
     }
-    hs[0][r][c] = m0; hs[1][r][c] = m1; hs[2][r][c] = m2; hs[3][r][c] = m3; hs[4][r][c] = m4;
+    float m[5][kHG];
+#pragma unroll
+    for (int o = 0; o < kHG; ++o) {
+      m[0][o] = m[1][o] = m[2][o] = m[3][o] = m[4][o] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 11; ++j) {
+        const float wj = win.w[j], xj = xv[o + j], yj = yv[o + j];
+        m[0][o] += wj * xj;
+        m[1][o] += wj * yj;
+        m[2][o] += wj * (xj * xj);
+        m[3][o] += wj * (yj * yj);
+        m[4][o] += wj * (xj * yj);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 5; ++q) hs[q][r][g] = make_float4(m[q][0], m[q][1], m[q][2], m[q][3]);
   }
   __syncthreads();
   const float C1 = 0.01f * 0.01f, C2 = 0.03f * 0.03f;
   float ssim_acc = 0.f, l1_acc = 0.f;
-  for (int k = threadIdx.x; k < kTH * kTW; k += 256) {
-    const int r = k / kTW, c = k % kTW;
-    const int gy = y0 + r, gx = x0 + c;
-    if (gy >= H || gx >= W) continue;
-    float mx = 0.f, my = 0.f, exx = 0.f, eyy = 0.f, exy = 0.f;
+  {
+    // vertical pass: column c, output rows kVG h .. kVG h + 1
+    const int c = threadIdx.x % kTW, h = threadIdx.x / kTW;
+    const float* hsf = reinterpret_cast<const float*>(hs);
+    float v[5][kVG];
 #pragma unroll
-    for (int i = 0; i < 11; ++i) {
-      const float wi = win.w[i];
-      mx += wi * hs[0][r + i][c];
-      my += wi * hs[1][r + i][c];
-      exx += wi * hs[2][r + i][c];
-      eyy += wi * hs[3][r + i][c];
-      exy += wi * hs[4][r + i][c];
+    for (int o = 0; o < kVG; ++o) v[0][o] = v[1][o] = v[2][o] = v[3][o] = v[4][o] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kVG + 10; ++i) {
+      const int rr = kVG * h + i;
+      float t[5];
+#pragma unroll
+      for (int q = 0; q < 5; ++q) t[q] = hsf[(q * kPH + rr) * kTW + c];
+#pragma unroll
+      for (int o = 0; o < kVG; ++o) {
+        const int j = i - o;
+        if (j >= 0 && j < 11) {
+          const float wj = win.w[j];
+#pragma unroll
+          for (int q = 0; q < 5; ++q) v[q][o] += wj * t[q];
+        }
+      }
     }
-    const float sxx = exx - mx * mx, syy = eyy - my * my, sxy = exy - mx * my;
-    const float A1 = 2.f * mx * my + C1, A2 = 2.f * sxy + C2;
-    const float B1 = mx * mx + my * my + C1, B2 = sxx + syy + C2;
-    const float inv = 1.0f / (B1 * B2);
-    const float S = A1 * A2 * inv;
-    const float dmu = 2.f * my * A2 * inv - 2.f * mx * S / B1;
-    const float dvar = -S / B2;
-    const float dcov = 2.f * A1 * inv;
-    const size_t o = ch * HW + size_t(gy) * W + gx;
-    amap[o] = dmu - 2.f * mx * dvar - my * dcov;
-    bmap[o] = dvar;
-    cmap[o] = dcov;
-    ssim_acc += S;
-    l1_acc += fabsf(sx[r + kR][c + kR] - sy[r + kR][c + kR]);
+#pragma unroll
+    for (int o = 0; o < kVG; ++o) {
+      const int r = kVG * h + o;
+      const int gy = y0 + r, gx = x0 + c;
+      if (gy >= H || gx >= W) continue;
+      const float mx = v[0][o], my = v[1][o], exx = v[2][o], eyy = v[3][o], exy = v[4][o];
+      const float sxx = exx - mx * mx, syy = eyy - my * my, sxy = exy - mx * my;
+      const float A1 = 2.f * mx * my + C1, A2 = 2.f * sxy + C2;
+      const float B1 = mx * mx + my * my + C1, B2 = sxx + syy + C2;
+      const float inv = 1.0f / (B1 * B2);
+      const float S = A1 * A2 * inv;
+      const float dmu = 2.f * my * A2 * inv - 2.f * mx * S / B1;
+      const float dvar = -S / B2;
+      const float dcov = 2.f * A1 * inv;
+      const size_t oo = ch * HW + size_t(gy) * W + gx;
+      amap[oo] = dmu - 2.f * mx * dvar - my * dcov;
+      bmap[oo] = dvar;
+      cmap[oo] = dcov;
+      ssim_acc += S;
+      l1_acc += fabsf(sx[r + kR][c + kR] - sy[r + kR][c + kR]);
+    }
   }
   reduce_block_2(ssim_acc, l1_acc, s_tmp);
   if (threadIdx.x == 0) {
@@ -127,7 +163,7 @@ __global__ void __launch_bounds__(256) ssim_bwd_kernel(const float* __restrict__
                                                         const float* __restrict__ bmap,
                                                         const float* __restrict__ cmap, float* __restrict__ grad) {
   __shared__ float sa[3][kPH][kPW + 1];
-  __shared__ float hs[3][kPH][kTW + 1];
+  __shared__ float4 hs[3][kPH][kTW / 4];
   const int ch = blockIdx.z;
   const int x0 = blockIdx.x * kTW, y0 = blockIdx.y * kTH;
   const size_t HW = size_t(H) * W;
@@ -141,38 +177,56 @@ __global__ void __launch_bounds__(256) ssim_bwd_kernel(const float* __restrict__
     for (int m = 0; m < 3; ++m) sa[m][r][c] = in ? maps[m][o] : 0.0f;
   }
   __syncthreads();
-  for (int k = threadIdx.x; k < kPH * kTW; k += 256) {
-    const int r = k / kTW, c = k % kTW;
-    float m0 = 0.f, m1 = 0.f, m2 = 0.f;
+  if (threadIdx.x < kHItems) {
+    const int r = threadIdx.x / (kTW / kHG), g = threadIdx.x % (kTW / kHG);
 #pragma unroll
-    for (int j = 0; j < 11; ++j) {
-      const float wj = win.w[j];
-      m0 += wj * sa[0][r][c + j];
-      m1 += wj * sa[1][r][c + j];
-      m2 += wj * sa[2][r][c + j];
+    for (int m = 0; m < 3; ++m) {
+      float in[kHG + 10];
+#pragma unroll
+      for (int j = 0; j < kHG + 10; ++j) in[j] = sa[m][r][kHG * g + j];
+      float out[kHG];
+#pragma unroll
+      for (int o = 0; o < kHG; ++o) {
+        out[o] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 11; ++j) out[o] += win.w[j] * in[o + j];
+      }
+      hs[m][r][g] = make_float4(out[0], out[1], out[2], out[3]);
     }
-    hs[0][r][c] = m0; hs[1][r][c] = m1; hs[2][r][c] = m2;
   }
   __syncthreads();
   const float invN = 1.0f / float(3 * HW);
   const float kl1 = (1.0f - lambda) * invN, kss = -lambda * invN;
-  for (int k = threadIdx.x; k < kTH * kTW; k += 256) {
-    const int r = k / kTW, c = k % kTW;
-    const int gy = y0 + r, gx = x0 + c;
-    if (gy >= H || gx >= W) continue;
-    float ba = 0.f, bb = 0.f, bc = 0.f;
+  const int c = threadIdx.x % kTW, h = threadIdx.x / kTW;
+  const float* hsf = reinterpret_cast<const float*>(hs);
+  float v[3][kVG];
 #pragma unroll
-    for (int i = 0; i < 11; ++i) {
-      const float wi = win.w[i];
-      ba += wi * hs[0][r + i][c];
-      bb += wi * hs[1][r + i][c];
-      bc += wi * hs[2][r + i][c];
+  for (int o = 0; o < kVG; ++o) v[0][o] = v[1][o] = v[2][o] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kVG + 10; ++i) {
+    const int rr = kVG * h + i;
+    float t[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) t[q] = hsf[(q * kPH + rr) * kTW + c];
+#pragma unroll
+    for (int o = 0; o < kVG; ++o) {
+      const int j = i - o;
+      if (j >= 0 && j < 11) {
+        const float wj = win.w[j];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) v[q][o] += wj * t[q];
+      }
     }
-    const size_t o = ch * HW + size_t(gy) * W + gx;
-    const float xv = img[o], yv = tgt[o];
+  }
+#pragma unroll
+  for (int o = 0; o < kVG; ++o) {
+    const int gy = y0 + kVG * h + o, gx = x0 + c;
+    if (gy >= H || gx >= W) continue;
+    const size_t oo = ch * HW + size_t(gy) * W + gx;
+    const float xv = img[oo], yv = tgt[oo];
     const float d = xv - yv;
     const float sgn = d > 0.f ? 1.f : (d < 0.f ? -1.f : 0.f);
-    grad[o] = kl1 * sgn + kss * (ba + 2.f * xv * bb + yv * bc);
+    grad[oo] = kl1 * sgn + kss * (v[0][o] + 2.f * xv * v[1][o] + yv * v[2][o]);
   }
 }
 
