@@ -280,20 +280,51 @@ Fwd<R> project(const R* params, int64_t n, int64_t i, int deg, const Camera& cam
 struct PixelTrace {        // per-pixel bookkeeping of the forward decisions
   uint32_t n_contrib;      // 1 + local index of the last blended entry (0 if none)
   uint32_t n_examined;     // entries examined, including the one that stopped the walk
-  double margin;           // smallest relative distance of a skip/stop decision to its threshold
+  double margin;           // smallest conditioned distance of a skip/stop decision to its threshold
+};
+
+// Decision margins.  A 32-bit evaluation of alpha = o exp(-e), e the conic's
+// quadratic form at (dx, dy), carries a relative error of a few units of
+// rounding times 1 + S, with S the sum of the magnitudes of the form's terms:
+// S exceeds e wherever the cross term cancels the squares (thin, tilted
+// footprints far from their centre), and then the rounding of each term is
+// amplified by S / e.  The transmittance after a run of blends inherits, per
+// blended entry, that error times alpha / (1 - alpha) plus one rounding.  A
+// decision's margin is its relative distance to the threshold divided by this
+// scale, so that a margin of m means the decision survives any evaluation whose
+// per-unit error is below m (about 1e-6 covers two differently ordered fp32
+// evaluations with one-ulp exp).
+inline double exponent_scale(double A, double B, double C, double dx, double dy) {
+  return 1.0 + 0.5 * (std::fabs(A) * dx * dx + std::fabs(C) * dy * dy) + std::fabs(B * dx * dy);
+}
+
+// One thresholded decision of a pixel's walk: entry k of the walked list, and
+// which test (alpha below 1/255, transmittance below the stop value after the
+// entry, alpha above the cap).  Used to log the decisions close to their
+// threshold and to take one of them the other way.
+enum DecisionKind : int { kDecSkip = 0, kDecStop = 1, kDecCap = 2 };
+struct Decision {
+  int64_t k;
+  int kind;
 };
 
 // Front-to-back compositing of one pixel over an ordered list, [GSG] "The
 // painting itself: front-to-back alpha compositing"; weights as in [GST]
 // opacity slide and [TBDR] worked examples.  In smooth mode nothing is capped,
 // skipped or stopped.
+//
+// flip (optional) takes one decision the other way; close (optional) receives
+// every decision whose margin is below close_below (the cap decision included,
+// which changes no forward value but the backward's dependence on the entry).
 template <class R>
 void blend_pixel(R px, R py, const uint32_t* list, int64_t len, const R* uv, const R* conic, const R* opac,
                  const R* rgb, int64_t n, const R bg[3], bool smooth, R out[3], R* T_out, PixelTrace* tr,
-                 int64_t* evals) {
+                 int64_t* evals, const Decision* flip = nullptr, std::vector<Decision>* close = nullptr,
+                 double close_below = 0.0) {
   R T = R(1);
   R C[3] = {R(0), R(0), R(0)};
   PixelTrace t{0, 0, std::numeric_limits<double>::infinity()};
+  double tscale = 1.0;     // conditioning of T (see exponent_scale)
   for (int64_t k = 0; k < len; ++k) {
     const uint32_t g = list[k];
     t.n_examined = uint32_t(k + 1);
@@ -302,18 +333,34 @@ void blend_pixel(R px, R py, const uint32_t* list, int64_t len, const R* uv, con
     const R A = conic[g], B = conic[n + g], Cc = conic[2 * n + g];
     const R e = R(0.5) * (A * dx * dx + Cc * dy * dy) + B * dx * dy;
     const R G = exp_r(-e);
-    R alpha = opac[g] * G;
+    const R araw = opac[g] * G;
+    R alpha = araw;
     if (!smooth) {
-      alpha = std::min(R(kAlphaCap), alpha);
-      t.margin = std::min(t.margin, std::fabs(double(alpha) - double(alpha_min<R>())) / double(alpha_min<R>()));
-      if (alpha < alpha_min<R>()) continue;
+      const bool capped = araw >= R(kAlphaCap);
+      alpha = std::min(R(kAlphaCap), araw);
+      const double ascale = exponent_scale(double(A), double(B), double(Cc), double(dx), double(dy));
+      const double mskip = std::fabs(double(alpha) - double(alpha_min<R>())) / double(alpha_min<R>()) / ascale;
+      t.margin = std::min(t.margin, mskip);
+      if (close) {
+        if (mskip < close_below) close->push_back({k, kDecSkip});
+        if (std::fabs(double(araw) - kAlphaCap) / kAlphaCap / ascale < close_below) close->push_back({k, kDecCap});
+      }
+      bool skip = alpha < alpha_min<R>();
+      if (flip && flip->k == k && flip->kind == kDecSkip) skip = !skip;
+      if (skip) continue;
+      // a capped alpha is exact; closeness to the cap is the backward's concern
+      tscale += 1.0 + (capped ? 0.0 : ascale * double(alpha) / (1.0 - double(alpha)));
     }
     for (int ch = 0; ch < 3; ++ch) C[ch] = C[ch] + T * alpha * rgb[ch * n + g];
     T = T * (R(1) - alpha);
     t.n_contrib = uint32_t(k + 1);
     if (!smooth) {
-      t.margin = std::min(t.margin, std::fabs(double(T) - kTStop) / kTStop);
-      if (T < R(kTStop)) break;
+      const double mstop = std::fabs(double(T) - kTStop) / kTStop / tscale;
+      t.margin = std::min(t.margin, mstop);
+      if (close && mstop < close_below) close->push_back({k, kDecStop});
+      bool stop = T < R(kTStop);
+      if (flip && flip->k == k && flip->kind == kDecStop) stop = !stop;
+      if (stop) break;
     }
   }
   for (int ch = 0; ch < 3; ++ch) out[ch] = C[ch] + T * bg[ch];
@@ -327,10 +374,12 @@ void blend_pixel(R px, R py, const uint32_t* list, int64_t len, const R* uv, con
 // per-entry derivatives of [GST] compositing slide (dI/dalpha_i = T_i (c_i - C_tail),
 // dI/dc_i = T_i alpha_i) and of [GSG] "From a pixel's blame to the oval's shape and place".
 // gscreen planes: 0 u, 1 v, 2 A, 3 B, 4 C, 5 opacity, 6-8 colour.
+// flip (optional) takes one skip or cap decision the other way, as the forward
+// walk that produced T_final and n_walk did.
 template <class R>
 void blend_pixel_bwd(R px, R py, const uint32_t* list, int64_t n_walk, const R* uv, const R* conic,
                      const R* opac, const R* rgb, int64_t n, const R bg[3], bool smooth, R T_final,
-                     const R gI[3], R* gscreen) {
+                     const R gI[3], R* gscreen, const Decision* flip = nullptr) {
   R T = T_final;
   R S[3];
   for (int ch = 0; ch < 3; ++ch) S[ch] = bg[ch] * T_final;
@@ -346,7 +395,10 @@ void blend_pixel_bwd(R px, R py, const uint32_t* list, int64_t n_walk, const R* 
     if (!smooth) {
       capped = araw > R(kAlphaCap);
       alpha = std::min(R(kAlphaCap), araw);
-      if (alpha < alpha_min<R>()) continue;
+      bool skip = alpha < alpha_min<R>();
+      if (flip && flip->k == k && flip->kind == kDecSkip) skip = !skip;
+      if (flip && flip->k == k && flip->kind == kDecCap) capped = !capped;
+      if (skip) continue;
     }
     T = T / (R(1) - alpha);              // transmittance in front of this entry
     const R wgt = alpha * T;
@@ -758,40 +810,88 @@ void or_render_pixels_f32(int64_t n, const float* uv, const float* conic, const 
   }
 }
 
-// Tiled backward blend: gscreen [9][n] is overwritten.  If margin/n_examined
-// (forward outputs) are given, gmargin[n] receives, per Gaussian, the smallest
-// decision margin of any pixel that examined it, also counting the alpha-cap
-// decision of each examined entry.
+// Tiled backward blend: gscreen [9][n] is overwritten.
 void or_render_bwd_f32(int64_t n, const float* uv, const float* conic, const float* opac, const float* rgb,
                        const uint32_t* vals, const uint32_t* ranges, const Camera* cam, const float* T_final,
-                       const uint32_t* n_contrib, const float* dLdI, float* gscreen, const uint32_t* n_examined,
-                       const double* margin, double* gmargin) {
+                       const uint32_t* n_contrib, const float* dLdI, float* gscreen) {
   const int W = cam->width, H = cam->height, tx = tiles_x(*cam);
   const int64_t HW = int64_t(W) * H;
   const float bg[3] = {cam->bg[0], cam->bg[1], cam->bg[2]};
   for (int64_t k = 0; k < 9 * n; ++k) gscreen[k] = 0.0f;
-  if (gmargin)
-    for (int64_t k = 0; k < n; ++k) gmargin[k] = std::numeric_limits<double>::infinity();
   for (int y = 0; y < H; ++y)
     for (int x = 0; x < W; ++x) {
       const int64_t t = int64_t(y / kTile) * tx + x / kTile;
       const uint32_t s = ranges[t];
       const int64_t p = int64_t(y) * W + x;
       const float gI[3] = {dLdI[p], dLdI[HW + p], dLdI[2 * HW + p]};
-      const float px = float(x) + 0.5f, py = float(y) + 0.5f;
-      blend_pixel_bwd<float>(px, py, vals + s, n_contrib[p], uv, conic, opac, rgb, n, bg, false, T_final[p], gI,
-                             gscreen);
-      if (gmargin && n_examined && margin) {
-        for (uint32_t k = 0; k < n_examined[p]; ++k) {
-          const uint32_t g = vals[s + k];
-          const float dx = px - uv[g], dy = py - uv[n + g];
-          const float e = 0.5f * (conic[g] * dx * dx + conic[2 * n + g] * dy * dy) + conic[n + g] * dx * dy;
-          const double araw = double(opac[g] * exp_r(-e));
-          const double mcap = std::fabs(araw - kAlphaCap) / kAlphaCap;
-          gmargin[g] = std::min(gmargin[g], std::min(margin[p], mcap));
-        }
-      }
+      blend_pixel_bwd<float>(float(x) + 0.5f, float(y) + 0.5f, vals + s, n_contrib[p], uv, conic, opac, rgb, n,
+                             bg, false, T_final[p], gI, gscreen);
     }
+}
+
+// What rounding could change.  For every pixel, each decision whose margin (see
+// exponent_scale) is below `below` is taken the other way, one at a time, and the
+// pixel is blended forward and backward again (the backward from the flipped
+// forward's transmittance and last entry, with the incoming image gradient dLdI
+// unchanged).  Summed over those flips:
+//   px_risk [2][H][W]  absolute change of the colour (largest channel) and of T;
+//   nc_lo, nc_hi [H][W] the range of last-entry counts the flips produce (the
+//                       unflipped count included);
+//   grisk [9][n]        absolute change of each Gaussian's nine screen partials.
+// Pixels with no such decision add nothing.  Returns the number of flips taken.
+int64_t or_flip_risk_f32(int64_t n, const float* uv, const float* conic, const float* opac, const float* rgb,
+                         const uint32_t* vals, const uint32_t* ranges, const Camera* cam, const float* dLdI,
+                         double below, float* px_risk, uint32_t* nc_lo, uint32_t* nc_hi, float* grisk) {
+  const int W = cam->width, H = cam->height, tx = tiles_x(*cam), ty = tiles_y(*cam);
+  const int64_t nt = int64_t(tx) * ty, HW = int64_t(W) * H;
+  const float bg[3] = {cam->bg[0], cam->bg[1], cam->bg[2]};
+  for (int64_t k = 0; k < 9 * n; ++k) grisk[k] = 0.0f;
+  std::vector<Decision> close;
+  // one pixel's partials, unflipped and flipped, kept at zero outside the entries just written
+  std::vector<float> g0(size_t(9 * n), 0.0f), g1(size_t(9 * n), 0.0f);
+  int64_t flips = 0;
+  for (int y = 0; y < H; ++y)
+    for (int x = 0; x < W; ++x) {
+      const int64_t t = int64_t(y / kTile) * tx + x / kTile, p = int64_t(y) * W + x;
+      const uint32_t s = ranges[t];
+      const uint32_t* list = vals + s;
+      const int64_t len = int64_t(ranges[nt + t]) - s;
+      const float px = float(x) + 0.5f, py = float(y) + 0.5f;
+      float out[3], T;
+      PixelTrace tr;
+      close.clear();
+      blend_pixel<float>(px, py, list, len, uv, conic, opac, rgb, n, bg, false, out, &T, &tr, nullptr, nullptr,
+                         &close, below);
+      px_risk[p] = px_risk[HW + p] = 0.0f;
+      nc_lo[p] = nc_hi[p] = tr.n_contrib;
+      if (close.empty()) continue;
+      const float gI[3] = {dLdI[p], dLdI[HW + p], dLdI[2 * HW + p]};
+      blend_pixel_bwd<float>(px, py, list, tr.n_contrib, uv, conic, opac, rgb, n, bg, false, T, gI, g0.data());
+      for (const Decision& f : close) {
+        float out1[3], T1;
+        PixelTrace tr1;
+        blend_pixel<float>(px, py, list, len, uv, conic, opac, rgb, n, bg, false, out1, &T1, &tr1, nullptr, &f);
+        float dc = 0.0f;
+        for (int ch = 0; ch < 3; ++ch) dc = std::max(dc, std::fabs(out1[ch] - out[ch]));
+        px_risk[p] += dc;
+        px_risk[HW + p] += std::fabs(T1 - T);
+        nc_lo[p] = std::min(nc_lo[p], tr1.n_contrib);
+        nc_hi[p] = std::max(nc_hi[p], tr1.n_contrib);
+        blend_pixel_bwd<float>(px, py, list, tr1.n_contrib, uv, conic, opac, rgb, n, bg, false, T1, gI, g1.data(),
+                               &f);
+        const uint32_t upto = std::max(tr.n_contrib, tr1.n_contrib);
+        for (uint32_t j = 0; j < upto; ++j)
+          for (int c = 0; c < 9; ++c) {
+            const size_t o = size_t(c) * n + list[j];
+            grisk[o] += std::fabs(g1[o] - g0[o]);
+            g1[o] = 0.0f;
+          }
+        ++flips;
+      }
+      for (uint32_t j = 0; j < tr.n_contrib; ++j)
+        for (int c = 0; c < 9; ++c) g0[size_t(c) * n + list[j]] = 0.0f;
+    }
+  return flips;
 }
 
 #define OR_SMOOTH(R, SUF)                                                                                      \

@@ -74,7 +74,9 @@ def _declare(L):
     L.or_render_fwd_f32.restype = I64
     L.or_render_untiled_f32.argtypes = [I64] + [P] * 6 + [P, P, P]
     L.or_render_pixels_f32.argtypes = [I64] + [P] * 6 + [P, I64, P, P, P, P, P, P]
-    L.or_render_bwd_f32.argtypes = [I64] + [P] * 6 + [P] + [P] * 7
+    L.or_render_bwd_f32.argtypes = [I64] + [P] * 6 + [P] + [P] * 4
+    L.or_flip_risk_f32.argtypes = [I64] + [P] * 6 + [P, P, C.c_double, P, P, P, P]
+    L.or_flip_risk_f32.restype = I64
 
 
 def _p(a):
@@ -160,17 +162,38 @@ def render_pixels(pre, vals, ranges, cam, xs, ys):
     return dict(rgb=rgb, T=T, n_contrib=nc, margin=margin)
 
 
-def render_bwd(pre, vals, ranges, cam, fwd, dLdI, with_margin=True):
+def render_bwd(pre, vals, ranges, cam, fwd, dLdI):
+    """Screen-space partials [9][n] (u, v, A, B, C, opacity, r, g, b)."""
     n = pre["n"]
     gscreen = np.zeros((9, n), np.float32)
-    gmargin = np.zeros(n, np.float64) if with_margin else None
     c = make_camera(cam)
     lib().or_render_bwd_f32(n, _p(pre["uv"]), _p(pre["conic"]), _p(pre["opac"]), _p(pre["rgb"]),
                             _p(_c(vals, np.uint32)), _p(_c(ranges, np.uint32)), C.byref(c), _p(fwd["T"]),
-                            _p(fwd["n_contrib"]), _p(_c(dLdI, np.float32)), _p(gscreen),
-                            _p(fwd["n_examined"]) if with_margin else None,
-                            _p(fwd["margin"]) if with_margin else None, _p(gmargin))
-    return gscreen, gmargin
+                            _p(fwd["n_contrib"]), _p(_c(dLdI, np.float32)), _p(gscreen))
+    return gscreen
+
+
+# Decisions whose conditioned margin is below this are taken the other way by
+# flip_risk.  Two fp32 evaluations of alpha (different operation order, FMA, a
+# one-ulp exp) differ by at most about 14 roundings, 8.4e-7, per unit of the
+# conditioning scale; 1e-5 leaves a factor of twelve.
+RISK_BELOW = 1e-5
+
+
+def flip_risk(pre, vals, ranges, cam, dLdI, below=RISK_BELOW):
+    """How much an fp32 evaluation other than the oracle's could move each output:
+    px [2][H][W] (colour, largest channel; T), nc_lo / nc_hi [H][W] (range of
+    n_contrib), g [9][n] (screen partials), and the number of flips taken."""
+    n = pre["n"]
+    H, W = cam.height, cam.width
+    out = dict(px=np.zeros((2, H, W), np.float32), nc_lo=np.zeros((H, W), np.uint32),
+               nc_hi=np.zeros((H, W), np.uint32), g=np.zeros((9, n), np.float32))
+    c = make_camera(cam)
+    out["flips"] = int(lib().or_flip_risk_f32(
+        n, _p(pre["uv"]), _p(pre["conic"]), _p(pre["opac"]), _p(pre["rgb"]), _p(_c(vals, np.uint32)),
+        _p(_c(ranges, np.uint32)), C.byref(c), _p(_c(dLdI, np.float32)), float(below), _p(out["px"]),
+        _p(out["nc_lo"]), _p(out["nc_hi"]), _p(out["g"])))
+    return out
 
 
 def preprocess_bwd(params, sh_degree, cam, gscreen, smooth=False, dtype=np.float32):
@@ -255,10 +278,12 @@ def forward(scene_params, sh_degree, cam):
 
 
 def train_step_grads(scene_params, sh_degree, cam, target, lam=0.2):
-    """Forward, loss and backward of one camera; returns a dict of every stage's output."""
+    """Forward, loss and backward of one camera; returns a dict of every stage's output and
+    the flip risk of the blend decisions."""
     pre, keys, vals, ranges, fwd = forward(scene_params, sh_degree, cam)
     (total, l1, ssim), dLdI = loss(fwd["rgb"], target, lam)
-    gscreen, gmargin = render_bwd(pre, vals, ranges, cam, fwd, dLdI.astype(np.float32))
+    gscreen = render_bwd(pre, vals, ranges, cam, fwd, dLdI.astype(np.float32))
     gparams = preprocess_bwd(scene_params, sh_degree, cam, gscreen)
+    risk = flip_risk(pre, vals, ranges, cam, dLdI.astype(np.float32))
     return dict(pre=pre, keys=keys, vals=vals, ranges=ranges, fwd=fwd, loss=(total, l1, ssim), dLdI=dLdI,
-                gscreen=gscreen, gmargin=gmargin, gparams=gparams)
+                gscreen=gscreen, gparams=gparams, risk=risk)

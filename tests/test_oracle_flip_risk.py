@@ -1,0 +1,145 @@
+"""Pins of the oracle's flip risk: taking one near-threshold blend decision the
+other way must change the outputs exactly as much as a plain render of an input
+nudged across that threshold does.  The nudged render goes through the ordinary
+forward and backward, not through the flip machinery.  No GPU needed."""
+import math
+
+import numpy as np
+
+from tests.test_oracle_pins import axis_camera, hand_scene
+
+# pixel (0, 0) has its centre on the principal point: a Gaussian on the optical
+# axis sits exactly on it (dx = dy = 0, so its alpha there is its opacity)
+TINY = 0.004          # world scale at depth 5: a footprint well inside one pixel
+WIDE = 0.5
+
+
+def _dLdI(cam):
+    return (np.random.default_rng(3).standard_normal((3, cam.height, cam.width)) * 1e-2).astype(np.float32)
+
+
+def _run(oracle, p, cam):
+    pre, keys, vals, ranges, fwd = oracle.forward(p, 0, cam)
+    dLdI = _dLdI(cam)
+    gs = oracle.render_bwd(pre, vals, ranges, cam, fwd, dLdI)
+    risk = oracle.flip_risk(pre, vals, ranges, cam, dLdI)
+    return pre, fwd, gs, risk
+
+
+def _logits_near(oracle, cam, target_alpha, count=4001):
+    """float32 logits around logit(target) and the opacity each gives after projection."""
+    l0 = np.float32(math.log(target_alpha / (1.0 - target_alpha)))
+    steps = np.arange(-(count // 2), count // 2 + 1)
+    ls = np.nextafter(l0, np.float32(np.inf)) - l0
+    logits = (l0 + steps.astype(np.float32) * ls).astype(np.float32)
+    p = hand_scene([dict(mean=(0, 0, 5.0), scale=TINY, logit=float(x)) for x in logits])
+    p[10] = logits
+    pre = oracle.preprocess(p, 0, cam)
+    return logits, pre["opac"]
+
+
+def test_no_flip_far_from_thresholds(oracle):
+    cam = axis_camera()
+    p = hand_scene([dict(mean=(0, 0, 4.0), scale=WIDE, opacity=0.6, colour=(1, 0, 0)),
+                    dict(mean=(0, 0, 6.0), scale=WIDE, opacity=0.5, colour=(0, 0, 1))])
+    pre, fwd, gs, risk = _run(oracle, p, cam)
+    # the wide footprints reach 1/255 somewhere; only pixels near that contour may flip
+    near = ~(risk["px"][0] > 0)
+    assert near[0, 0] and risk["nc_lo"][0, 0] == risk["nc_hi"][0, 0] == fwd["n_contrib"][0, 0]
+    assert np.all(risk["nc_lo"] <= fwd["n_contrib"]) and np.all(fwd["n_contrib"] <= risk["nc_hi"])
+
+
+def test_skip_flip_equals_nudged_render(oracle):
+    cam = axis_camera()
+    amin = np.float32(1.0) / np.float32(255.0)
+    logits, opac = _logits_near(oracle, cam, float(amin))
+    below = np.nonzero(opac < amin)[0].max()          # the largest opacity still skipped
+    above = below + 1                                   # the smallest one blended
+    assert opac[above] >= amin and (amin - opac[below]) / amin < 1e-6
+
+    def scene(lg):
+        p = hand_scene([dict(mean=(0, 0, 4.0), scale=TINY, opacity=0.5, colour=(1.0, 0.2, 0.1)),
+                        dict(mean=(0, 0, 5.0), scale=TINY, logit=0.0, colour=(0.1, 0.9, 0.3)),
+                        dict(mean=(0, 0, 6.0), scale=WIDE, opacity=0.7, colour=(0.2, 0.3, 1.0))])
+        p[10, 1] = lg
+        return p
+
+    pre0, fwd0, gs0, risk = _run(oracle, scene(logits[below]), cam)
+    pre1, fwd1, gs1, _ = _run(oracle, scene(logits[above]), cam)
+    assert risk["flips"] >= 1
+    d = np.abs(fwd1["rgb"][:, 0, 0] - fwd0["rgb"][:, 0, 0]).max()
+    assert d > 1e-4                                     # the nudge really changes the pixel
+    np.testing.assert_allclose(risk["px"][0, 0, 0], d, rtol=1e-3)
+    np.testing.assert_allclose(risk["px"][1, 0, 0], abs(fwd1["T"][0, 0] - fwd0["T"][0, 0]), rtol=1e-3)
+    # pixel (0, 0) is the only one the nudge changes; all three Gaussians' partials move there
+    other = np.ones((cam.height, cam.width), bool)
+    other[0, 0] = False
+    assert np.abs(fwd1["rgb"] - fwd0["rgb"])[:, other].max() == 0.0
+    dg = np.abs(gs1 - gs0).astype(np.float64)
+    # the flip moves exactly these amounts, up to the alpha difference of the two opacities
+    np.testing.assert_allclose(risk["g"], dg, rtol=2e-3, atol=1e-9)
+    assert dg[5, 1] > 0 and dg[5, 2] > 0
+
+
+def test_stop_flip_equals_nudged_render(oracle):
+    cam = axis_camera()
+    # T after the first two entries: 0.1 (alpha 0.9), then 0.001 (alpha capped at 0.99)
+    front = [dict(mean=(0, 0, 3.0), scale=TINY, opacity=0.9, colour=(1.0, 0.0, 0.0)),
+             dict(mean=(0, 0, 3.5), scale=TINY, opacity=0.999, colour=(0.0, 1.0, 0.0))]
+    pre = oracle.preprocess(hand_scene(front), 0, cam)
+    T2 = np.float32(1.0)
+    for a in pre["opac"]:
+        T2 = np.float32(T2 * np.float32(1.0 - min(np.float32(0.99), a)))
+    # the third entry brings T to within a hair of the stop value 1e-4
+    logits, opac = _logits_near(oracle, cam, 1.0 - 1e-4 / float(T2))
+    T3 = (T2 * (np.float32(1.0) - opac)).astype(np.float32)
+    stop = np.float32(1e-4)
+    cont = np.nonzero(T3 >= stop)[0]
+    k = cont[np.argmin(T3[cont])]                       # continues, closest to the threshold
+    kk = np.nonzero(T3 < stop)[0]
+    kk = kk[np.argmax(T3[kk])]                          # stops, closest to the threshold
+    assert (T3[k] - stop) / stop < 2e-6
+
+    def scene(lg):
+        p = hand_scene(front + [dict(mean=(0, 0, 4.0), scale=TINY, logit=0.0, colour=(0.0, 0.0, 1.0)),
+                                dict(mean=(0, 0, 5.0), scale=TINY, opacity=0.6, colour=(1.0, 1.0, 0.0))])
+        p[10, 2] = lg
+        return p
+
+    pre0, fwd0, gs0, risk = _run(oracle, scene(logits[k]), cam)
+    pre1, fwd1, gs1, _ = _run(oracle, scene(logits[kk]), cam)
+    assert fwd0["n_contrib"][0, 0] == 4 and fwd1["n_contrib"][0, 0] == 3
+    assert risk["nc_lo"][0, 0] == 3 and risk["nc_hi"][0, 0] == 4
+    d = np.abs(fwd1["rgb"][:, 0, 0] - fwd0["rgb"][:, 0, 0]).max()
+    np.testing.assert_allclose(risk["px"][0, 0, 0], d, rtol=1e-2)
+    dg = np.abs(gs1 - gs0).astype(np.float64)
+    # the fourth entry's partials appear or vanish; the rest move by the nudge's alpha change
+    np.testing.assert_allclose(risk["g"][:, 3], dg[:, 3], rtol=1e-2, atol=1e-12)
+    assert dg[5, 3] > 0
+
+
+def test_cap_flip_equals_nudged_gradient(oracle):
+    cam = axis_camera()
+    cap = np.float32(0.99)
+    logits, opac = _logits_near(oracle, cam, 0.99)
+    over = np.nonzero(opac > cap)[0].min()              # capped: no gradient through alpha
+    under = np.nonzero(opac < cap)[0].max()             # not capped
+    assert (opac[over] - cap) / cap < 1e-6
+
+    def scene(lg):
+        p = hand_scene([dict(mean=(0, 0, 4.0), scale=TINY, logit=0.0, colour=(0.3, 0.6, 0.9)),
+                        dict(mean=(0, 0, 6.0), scale=WIDE, opacity=0.5, colour=(1.0, 0.5, 0.0))])
+        p[10, 0] = lg
+        return p
+
+    pre0, fwd0, gs0, risk = _run(oracle, scene(logits[over]), cam)
+    pre1, fwd1, gs1, _ = _run(oracle, scene(logits[under]), cam)
+    # the forward does not see the cap decision
+    assert risk["px"][0, 0, 0] == 0 and risk["px"][1, 0, 0] == 0
+    assert risk["nc_lo"][0, 0] == risk["nc_hi"][0, 0]
+    # at pixel (0, 0) the capped entry passes nothing through alpha; uncapped, its opacity
+    # partial appears (the neighbours, uncapped either way, move only by the nudge)
+    assert risk["g"][5, 0] > 0
+    np.testing.assert_allclose(risk["g"][5, 0], abs(gs1[5, 0] - gs0[5, 0]), rtol=1e-3)
+    # on the axis the position and conic partials vanish at that pixel
+    assert np.all(risk["g"][0:5, 0] == 0)

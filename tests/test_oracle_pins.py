@@ -88,7 +88,7 @@ def test_compositing_derivative_closed_form(oracle):
     for ch in range(3):
         dLdI = np.zeros((3, cam.height, cam.width), np.float32)
         dLdI[ch, 0, 0] = 1.0
-        gs, _ = oracle.render_bwd(pre, vals, ranges, cam, fwd, dLdI)
+        gs = oracle.render_bwd(pre, vals, ranges, cam, fwd, dLdI)
         dIda[:, ch] = gs[5]        # centre of both footprints: G = 1, so dL/do = dL/dalpha
         dIdc[:, ch] = gs[6 + ch]
     np.testing.assert_allclose(dIda[0], g["expected_dI_dalpha_front"], atol=1e-6)
@@ -120,7 +120,7 @@ def test_opacity_gradient_worked_example(oracle):
     assert abs(loss - g["expected_loss"]) < 1e-6
     dLdI = np.zeros((3, cam.height, cam.width), np.float32)
     dLdI[:, 0, 0] = 2.0 * (I - tgt)
-    gs, _ = oracle.render_bwd(pre, vals, ranges, cam, fwd, dLdI)
+    gs = oracle.render_bwd(pre, vals, ranges, cam, fwd, dLdI)
     assert abs(gs[5, 0] - g["expected_dL_dopacity"]) < 1e-6
     gp = oracle.preprocess_bwd(p, 0, cam, gs)
     # through the sigmoid: d o / d logit = o (1 - o) = 0.25
@@ -149,7 +149,7 @@ def test_centre_gradient_worked_example(oracle):
     assert abs(alpha - g["expected_dI_dm"]) < 1e-6          # I (p - m) / s^2 with p - m = s = 1
     dLdI = np.zeros((3, cam.height, cam.width), np.float32)
     dLdI[0, 0, 1] = g["dL_dI"]
-    gs, _ = oracle.render_bwd(pre, vals, ranges, cam, fwd, dLdI)
+    gs = oracle.render_bwd(pre, vals, ranges, cam, fwd, dLdI)
     assert abs(gs[0, 0] - g["dL_dI"] * g["expected_dI_dm"]) < 1e-6
     assert abs(gs[1, 0]) < 1e-7
     gp = oracle.preprocess_bwd(p, 0, cam, gs)
