@@ -157,6 +157,33 @@ def measured_traffic(kernel):
     return None
 
 
+VALU_PEAK = 256 * 4 * 2.4e9 / 4      # wave64 VALU instructions/s: one per SIMD every 4 cycles
+
+
+def measured_valu():
+    """VALU issue fraction of the blend kernels from the committed rocprofv3 SQ counter
+    summary (wave instructions per dispatch over that run's average duration, against
+    VALU_PEAK), for each kernel whose sources are unchanged since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "pmc_valu_blend_6m_1080p.md")
+    out = {}
+    if not os.path.exists(path):
+        return out
+    for line in open(path):
+        parts = line.split()
+        if len(parts) >= 2 and parts[0] == "valu":
+            kv = dict(p.split("=", 1) for p in parts[2:])
+            h = hashlib.sha256()
+            for src in kv["sources"].split(","):
+                h.update(open(os.path.join(ROOT, src), "rb").read())
+            if h.hexdigest() != kv["sha256"]:
+                continue
+            insts, ns = float(kv["wave_insts"]), float(kv["avg_ns"])
+            out[parts[1]] = {"wave_insts": insts, "avg_us": round(ns / 1000.0, 1),
+                             "frac": round(insts / (ns * 1e-9) / VALU_PEAK, 3)}
+    return out
+
+
 def cpu_baseline(wl):
     """The oracle (test infrastructure) on one training step: camera 0, all stages, one core."""
     from oracle import oracle as O
@@ -182,8 +209,12 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this rasteriser runs on one GPU; multi-GPU runs are not part of this build "
+        print(json.dumps({"error": "this rasteriser runs on one GPU; runs on several GPUs are not supported "
                                    f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})"}))
+        sys.exit(2)
+    if args.warmup < 1 or args.steps < 1:
+        print(json.dumps({"error": "--warmup and --steps must be at least 1 (a warm-up step picks the kernel "
+                                   "whose roofline the timed steps measure)"}))
         sys.exit(2)
     import torch
     from differentiable_tile_gaussian_amd import gs, scenes
@@ -206,12 +237,17 @@ def main():
     pl = Pipeline(params, deg, cam0.width, cam0.height)
     setup_s = time.perf_counter() - t_setup
 
-    # warm-up with every kernel launch timed: per-kernel time per step, and the dominant kernel
+    # warm-up: the first step untimed (code objects load, caches are cold), then every
+    # kernel launch of the remaining warm-up steps timed: per-kernel time per step and the
+    # dominant kernel
+    cold = 1 if args.warmup >= 2 else 0
+    run_steps(pl, cams, targets, 0, cold, gs=gs)
+    torch.cuda.synchronize()
     gs.gs_profile_enable(True)
-    run_steps(pl, cams, targets, 0, args.warmup, gs=gs)
+    run_steps(pl, cams, targets, cold, args.warmup - cold, gs=gs)
     torch.cuda.synchronize()
     warm = gs.gs_profile_query()
-    kernel_ms = {k: ms / max(args.warmup, 1) for k, (cnt, ms) in warm.items()}
+    kernel_ms = {k: ms / max(args.warmup - cold, 1) for k, (cnt, ms) in warm.items()}
     dominant = max(kernel_ms, key=kernel_ms.get)
     # timed steps: only the dominant kernel's launches carry events
     gs.gs_profile_enable(True, dominant)
@@ -271,6 +307,7 @@ def main():
         "evals_per_step": {"fwd": ev_f // args.steps, "bwd": ev_b // args.steps},
         "stage_ms": {k: round(float(stage[:, i].mean()), 4) for i, k in enumerate(StageTimer.NAMES)},
         "kernel_ms_per_step": {k: round(v, 4) for k, v in sorted(kernel_ms.items(), key=lambda kv: -kv[1])},
+        "blend_valu": {"bound": "alu", "peak": VALU_PEAK, "unit": "wave instr/s", "kernels": measured_valu()},
         "roofline": roof,
         "setup_s": round(setup_s, 2),
     }
