@@ -376,10 +376,24 @@ void blend_pixel(R px, R py, const uint32_t* list, int64_t len, const R* uv, con
 // gscreen planes: 0 u, 1 v, 2 A, 3 B, 4 C, 5 opacity, 6-8 colour.
 // flip (optional) takes one skip or cap decision the other way, as the forward
 // walk that produced T_final and n_walk did.
+//
+// mass (optional, [2][9][n] doubles, and count [n]) records how large the terms are
+// that each partial sums, so that a reordered or differently rounded evaluation can be
+// bounded: mass[0] adds |term| and mass[1] adds |term| (2 n_walk + 16) (the terms'
+// own rounding grows with the walk that recovers T and S), count the pixels that
+// contribute.  Terms are counted by the magnitudes of their factors (the colour
+// difference inside dL/dalpha and the conic products inside du, dv unexpanded), so
+// that cancellation inside one pixel's term is covered too.
 template <class R>
 void blend_pixel_bwd(R px, R py, const uint32_t* list, int64_t n_walk, const R* uv, const R* conic,
                      const R* opac, const R* rgb, int64_t n, const R bg[3], bool smooth, R T_final,
-                     const R gI[3], R* gscreen, const Decision* flip = nullptr) {
+                     const R gI[3], R* gscreen, const Decision* flip = nullptr, double* mass = nullptr,
+                     uint32_t* count = nullptr) {
+  const double wdepth = 2.0 * double(n_walk) + 16.0;
+  auto add_mass = [&](int plane, uint32_t g, double m) {
+    mass[int64_t(plane) * n + g] += m;
+    mass[int64_t(9 + plane) * n + g] += m * wdepth;
+  };
   R T = T_final;
   R S[3];
   for (int ch = 0; ch < 3; ++ch) S[ch] = bg[ch] * T_final;
@@ -403,11 +417,18 @@ void blend_pixel_bwd(R px, R py, const uint32_t* list, int64_t n_walk, const R* 
     T = T / (R(1) - alpha);              // transmittance in front of this entry
     const R wgt = alpha * T;
     R galpha = R(0);
+    double gam = 0.0;                    // magnitude of the terms of dL/dalpha
     for (int ch = 0; ch < 3; ++ch) {
       gscreen[(6 + ch) * n + g] += gI[ch] * wgt;
       galpha += gI[ch] * (rgb[ch * n + g] * T - S[ch] / (R(1) - alpha));
+      if (mass) {
+        gam += std::fabs(double(gI[ch])) * (std::fabs(double(rgb[ch * n + g])) * double(T) +
+                                             std::fabs(double(S[ch])) / (1.0 - double(alpha)));
+        add_mass(6 + ch, g, std::fabs(double(gI[ch]) * double(wgt)));
+      }
       S[ch] += rgb[ch * n + g] * wgt;
     }
+    if (count) ++count[g];
     if (capped) continue;                // alpha = 0.99 does not depend on opacity or position
     gscreen[5 * n + g] += galpha * G;    // d alpha / d opacity = G
     const R ge = -galpha * araw;         // d alpha / d e = -alpha
@@ -416,6 +437,15 @@ void blend_pixel_bwd(R px, R py, const uint32_t* list, int64_t n_walk, const R* 
     gscreen[4 * n + g] += ge * R(0.5) * dy * dy;
     gscreen[0 * n + g] += -ge * (A * dx + B * dy);   // d e / d u = -(A dx + B dy)
     gscreen[1 * n + g] += -ge * (B * dx + Cc * dy);
+    if (mass) {
+      const double me = gam * double(araw), ax = std::fabs(double(dx)), ay = std::fabs(double(dy));
+      add_mass(5, g, gam * double(G));
+      add_mass(2, g, me * 0.5 * ax * ax);
+      add_mass(3, g, me * ax * ay);
+      add_mass(4, g, me * 0.5 * ay * ay);
+      add_mass(0, g, me * (std::fabs(double(A)) * ax + std::fabs(double(B)) * ay));
+      add_mass(1, g, me * (std::fabs(double(B)) * ax + std::fabs(double(Cc)) * ay));
+    }
   }
 }
 
@@ -810,14 +840,20 @@ void or_render_pixels_f32(int64_t n, const float* uv, const float* conic, const 
   }
 }
 
-// Tiled backward blend: gscreen [9][n] is overwritten.
+// Tiled backward blend: gscreen [9][n] is overwritten; mass ([2][9][n]) and count
+// ([n]), when given, are overwritten with the term magnitudes blend_pixel_bwd records.
 void or_render_bwd_f32(int64_t n, const float* uv, const float* conic, const float* opac, const float* rgb,
                        const uint32_t* vals, const uint32_t* ranges, const Camera* cam, const float* T_final,
-                       const uint32_t* n_contrib, const float* dLdI, float* gscreen) {
+                       const uint32_t* n_contrib, const float* dLdI, float* gscreen, double* mass,
+                       uint32_t* count) {
   const int W = cam->width, H = cam->height, tx = tiles_x(*cam);
   const int64_t HW = int64_t(W) * H;
   const float bg[3] = {cam->bg[0], cam->bg[1], cam->bg[2]};
   for (int64_t k = 0; k < 9 * n; ++k) gscreen[k] = 0.0f;
+  if (mass)
+    for (int64_t k = 0; k < 18 * n; ++k) mass[k] = 0.0;
+  if (count)
+    for (int64_t k = 0; k < n; ++k) count[k] = 0u;
   for (int y = 0; y < H; ++y)
     for (int x = 0; x < W; ++x) {
       const int64_t t = int64_t(y / kTile) * tx + x / kTile;
@@ -825,7 +861,26 @@ void or_render_bwd_f32(int64_t n, const float* uv, const float* conic, const flo
       const int64_t p = int64_t(y) * W + x;
       const float gI[3] = {dLdI[p], dLdI[HW + p], dLdI[2 * HW + p]};
       blend_pixel_bwd<float>(float(x) + 0.5f, float(y) + 0.5f, vals + s, n_contrib[p], uv, conic, opac, rgb, n,
-                             bg, false, T_final[p], gI, gscreen);
+                             bg, false, T_final[p], gI, gscreen, nullptr, mass, count);
+    }
+}
+
+// The same backward in double (thresholds and the walk of or_render_bwd_f32, every
+// product and sum in fp64), for checking the fp32 evaluation's rounding.
+void or_render_bwd_f64(int64_t n, const double* uv, const double* conic, const double* opac, const double* rgb,
+                       const uint32_t* vals, const uint32_t* ranges, const Camera* cam, const double* T_final,
+                       const uint32_t* n_contrib, const double* dLdI, double* gscreen) {
+  const int W = cam->width, H = cam->height, tx = tiles_x(*cam);
+  const int64_t HW = int64_t(W) * H;
+  const double bg[3] = {cam->bg[0], cam->bg[1], cam->bg[2]};
+  for (int64_t k = 0; k < 9 * n; ++k) gscreen[k] = 0.0;
+  for (int y = 0; y < H; ++y)
+    for (int x = 0; x < W; ++x) {
+      const int64_t t = int64_t(y / kTile) * tx + x / kTile;
+      const int64_t p = int64_t(y) * W + x;
+      const double gI[3] = {dLdI[p], dLdI[HW + p], dLdI[2 * HW + p]};
+      blend_pixel_bwd<double>(double(x) + 0.5, double(y) + 0.5, vals + ranges[t], n_contrib[p], uv, conic, opac,
+                              rgb, n, bg, false, T_final[p], gI, gscreen);
     }
 }
 

@@ -74,7 +74,8 @@ def _declare(L):
     L.or_render_fwd_f32.restype = I64
     L.or_render_untiled_f32.argtypes = [I64] + [P] * 6 + [P, P, P]
     L.or_render_pixels_f32.argtypes = [I64] + [P] * 6 + [P, I64, P, P, P, P, P, P]
-    L.or_render_bwd_f32.argtypes = [I64] + [P] * 6 + [P] + [P] * 4
+    L.or_render_bwd_f32.argtypes = [I64] + [P] * 6 + [P] + [P] * 6
+    L.or_render_bwd_f64.argtypes = [I64] + [P] * 6 + [P] + [P] * 4
     L.or_flip_risk_f32.argtypes = [I64] + [P] * 6 + [P, P, C.c_double, P, P, P, P]
     L.or_flip_risk_f32.restype = I64
 
@@ -162,15 +163,41 @@ def render_pixels(pre, vals, ranges, cam, xs, ys):
     return dict(rgb=rgb, T=T, n_contrib=nc, margin=margin)
 
 
-def render_bwd(pre, vals, ranges, cam, fwd, dLdI):
-    """Screen-space partials [9][n] (u, v, A, B, C, opacity, r, g, b)."""
+def render_bwd(pre, vals, ranges, cam, fwd, dLdI, with_mass=False):
+    """Screen-space partials [9][n] (u, v, A, B, C, opacity, r, g, b).  With with_mass,
+    also (mass [2][9][n], count [n]): the magnitudes of the terms each partial sums
+    (plain, and weighted by twice the walk length plus 16) and the contributing pixels."""
     n = pre["n"]
     gscreen = np.zeros((9, n), np.float32)
+    mass = np.zeros((2, 9, n), np.float64) if with_mass else None
+    count = np.zeros(n, np.uint32) if with_mass else None
     c = make_camera(cam)
     lib().or_render_bwd_f32(n, _p(pre["uv"]), _p(pre["conic"]), _p(pre["opac"]), _p(pre["rgb"]),
                             _p(_c(vals, np.uint32)), _p(_c(ranges, np.uint32)), C.byref(c), _p(fwd["T"]),
-                            _p(fwd["n_contrib"]), _p(_c(dLdI, np.float32)), _p(gscreen))
+                            _p(fwd["n_contrib"]), _p(_c(dLdI, np.float32)), _p(gscreen),
+                            _p(mass) if with_mass else None, _p(count) if with_mass else None)
+    return (gscreen, mass, count) if with_mass else gscreen
+
+
+def render_bwd_f64(pre, vals, ranges, cam, fwd, dLdI):
+    """render_bwd with every operation in fp64 (same thresholds, same walk lengths)."""
+    n = pre["n"]
+    d = lambda a: _c(a, np.float64)
+    gscreen = np.zeros((9, n), np.float64)
+    c = make_camera(cam)
+    lib().or_render_bwd_f64(n, _p(d(pre["uv"])), _p(d(pre["conic"])), _p(d(pre["opac"])), _p(d(pre["rgb"])),
+                            _p(_c(vals, np.uint32)), _p(_c(ranges, np.uint32)), C.byref(c), _p(d(fwd["T"])),
+                            _p(fwd["n_contrib"]), _p(d(dLdI)), _p(gscreen))
     return gscreen
+
+
+def rounding_slack(mass, count):
+    """Bound [9][n] on the difference between two fp32 evaluations of the screen partials
+    that sum the same terms in different orders with differently rounded terms: each
+    term carries at most about (2 walk + 16) roundings of its magnitude, and a sum of
+    count terms at most count roundings of their total magnitude (unit 2^-24, both
+    sides)."""
+    return (2.0 ** -22) * mass[1] + (2.0 ** -23) * count.astype(np.float64) * mass[0]
 
 
 # Decisions whose conditioned margin is below this are taken the other way by
@@ -282,8 +309,8 @@ def train_step_grads(scene_params, sh_degree, cam, target, lam=0.2):
     the flip risk of the blend decisions."""
     pre, keys, vals, ranges, fwd = forward(scene_params, sh_degree, cam)
     (total, l1, ssim), dLdI = loss(fwd["rgb"], target, lam)
-    gscreen = render_bwd(pre, vals, ranges, cam, fwd, dLdI.astype(np.float32))
+    gscreen, mass, count = render_bwd(pre, vals, ranges, cam, fwd, dLdI.astype(np.float32), with_mass=True)
     gparams = preprocess_bwd(scene_params, sh_degree, cam, gscreen)
     risk = flip_risk(pre, vals, ranges, cam, dLdI.astype(np.float32))
     return dict(pre=pre, keys=keys, vals=vals, ranges=ranges, fwd=fwd, loss=(total, l1, ssim), dLdI=dLdI,
-                gscreen=gscreen, gparams=gparams, risk=risk)
+                gscreen=gscreen, gparams=gparams, risk=risk, slack=rounding_slack(mass, count))

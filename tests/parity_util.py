@@ -178,10 +178,12 @@ def check_grad(g_gpu, g_ref, mask=None, rtol=GRAD_RTOL, name="", risk=None):
 SCREEN = ["u", "v", "A", "B", "C", "opacity", "r", "g", "b"]
 
 
-def check_screen_grads(gscreen, ref_gscreen, grisk, planes=range(9)):
-    """The nine screen partials of every Gaussian, to GRAD_RTOL plus their flip risk."""
+def check_screen_grads(gscreen, ref_gscreen, grisk, slack=None, planes=range(9)):
+    """The nine screen partials of every Gaussian, to GRAD_RTOL plus their flip risk and,
+    when given, the oracle's rounding slack (atomic reordering and per-term rounding)."""
     for k in planes:
-        check_grad(gscreen[k], ref_gscreen[k], name=SCREEN[k], risk=grisk[k])
+        r = grisk[k].astype(np.float64) + (0.0 if slack is None else slack[k])
+        check_grad(gscreen[k], ref_gscreen[k], name=SCREEN[k], risk=r)
 
 
 def calm(grisk, ref_gscreen, rtol=GRAD_RTOL):
@@ -190,3 +192,37 @@ def calm(grisk, ref_gscreen, rtol=GRAD_RTOL):
     g = ref_gscreen.astype(np.float64)
     rms = np.sqrt((g * g).mean(axis=1, keepdims=True))
     return np.all(grisk <= CALM * rtol * (np.abs(g) + rms), axis=0)
+
+
+def check_param_grads(g_gpu, ref, oracle, params, deg, cam, keep, rtol=GRAD_RTOL):
+    """Parameter gradients of the calm Gaussians, group by group: GRAD_RTOL of the element
+    plus GRAD_RTOL of the group's rms, and, for the Gaussians where that is not enough,
+    the screen-level flip risk and rounding slack carried through the chain by the oracle
+    (the chain is linear in the screen partials, so each plane's bound is chained on its
+    own and the magnitudes added)."""
+    bound_screen = ref["risk"]["g"].astype(np.float64) + ref["slack"]
+    for name, sl in grad_groups(deg).items():
+        a = g_gpu[sl][:, keep].astype(np.float64)
+        b = ref["gparams"][sl][:, keep].astype(np.float64)
+        if b.size == 0:
+            continue
+        rms = np.sqrt((b * b).mean())
+        d = np.abs(a - b)
+        tol = rtol * np.abs(b) + rtol * rms
+        bad_cols = np.nonzero((d > tol).any(axis=0))[0]
+        if bad_cols.size:
+            idx = np.nonzero(keep)[0][bad_cols]
+            sub = np.ascontiguousarray(params[:, idx])
+            extra = np.zeros((params.shape[0], idx.size))
+            for k in range(9):
+                gs_k = np.zeros((9, idx.size), np.float32)
+                gs_k[k] = bound_screen[k, idx]
+                extra += np.abs(oracle.preprocess_bwd(sub, deg, cam, gs_k).astype(np.float64))
+            tol[:, bad_cols] += extra[sl]
+        bad = d > tol
+        assert not bad.any(), (f"{name}: {int(bad.sum())} of {b.size} elements off, max excess "
+                               f"{(d - tol).max()} (rms {rms})")
+        nb = np.linalg.norm(b)
+        if nb > 0:
+            assert np.linalg.norm(d) <= rtol * nb + np.linalg.norm(tol - rtol * np.abs(b) - rtol * rms), \
+                f"{name}: relative norm {np.linalg.norm(d) / nb}"

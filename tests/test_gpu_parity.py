@@ -46,8 +46,9 @@ def _oracle_all(oracle, params, deg, cam, dLdI=None):
     pre, keys, vals, ranges, fwd = oracle.forward(params, deg, cam)
     out = dict(pre=pre, keys=keys, vals=vals, ranges=ranges, fwd=fwd)
     if dLdI is not None:
-        gscreen = oracle.render_bwd(pre, vals, ranges, cam, fwd, dLdI)
+        gscreen, mass, count = oracle.render_bwd(pre, vals, ranges, cam, fwd, dLdI, with_mass=True)
         out["gscreen"] = gscreen
+        out["slack"] = oracle.rounding_slack(mass, count)
         out["gparams"] = oracle.preprocess_bwd(params, deg, cam, gscreen)
     else:
         dLdI = np.zeros((3, cam.height, cam.width), np.float32)
@@ -87,17 +88,16 @@ def test_backward_small(torch_cuda, oracle, case):
     torch.cuda.synchronize()
     gscreen = pl.gscreen[:, :n].cpu().numpy()
     gparams = pl.planar(pl.grads).cpu().numpy()
-    pu.check_screen_grads(gscreen, o["gscreen"], o["risk"]["g"])
+    pu.check_screen_grads(gscreen, o["gscreen"], o["risk"]["g"], o["slack"])
     keep = pu.calm(o["risk"]["g"], o["gscreen"])
     print(f"  flips {o['risk']['flips']}, gaussians not calm: {int((~keep).sum())} of {n}", flush=True)
-    for name, sl in pu.grad_groups(deg).items():
-        pu.check_grad(gparams[sl], o["gparams"][sl], keep, name=name)
+    pu.check_param_grads(gparams, o, oracle, s.params, deg, cam, keep)
     # culled Gaussians get exactly zero
     culled = o["pre"]["tiles"] == 0
     assert np.all(gparams[:, culled] == 0.0)
 
 
-def _full_step_checks(torch, gs, pl, c, ref, target, deg):
+def _full_step_checks(torch, gs, oracle, pl, c, ref, target, params, deg, cam):
     """Every stage of one step against the oracle: projection, pairs and ranges
     bit-exact; pixels, loss and image gradient; then the backward fed the oracle's
     image gradient (so that only the blend's own decisions can differ): all screen
@@ -117,11 +117,10 @@ def _full_step_checks(torch, gs, pl, c, ref, target, deg):
     gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI, pl.gscreen,
                      pl.grads, pl.ws_render)
     torch.cuda.synchronize()
-    pu.check_screen_grads(pl.gscreen[:, :n].cpu().numpy(), ref["gscreen"], ref["risk"]["g"])
+    pu.check_screen_grads(pl.gscreen[:, :n].cpu().numpy(), ref["gscreen"], ref["risk"]["g"], ref["slack"])
     keep = pu.calm(ref["risk"]["g"], ref["gscreen"])
     g = pl.planar(pl.grads).cpu().numpy()
-    for name, sl in pu.grad_groups(deg).items():
-        pu.check_grad(g[sl], ref["gparams"][sl], keep, name=name)
+    pu.check_param_grads(g, ref, oracle, params, deg, cam, keep)
     print(f"  flips {ref['risk']['flips']} over {n_flip} px; image-gradient elements checked {n_img}; "
           f"Gaussians not calm {int((~keep).sum())} of {n}", flush=True)
     return g
@@ -137,7 +136,7 @@ def test_config1_full_step(torch_cuda, oracle):
     target = oracle.forward(wl.target_scene.params, deg, cam)[4]["rgb"]
     ref = oracle.train_step_grads(wl.scene.params, deg, cam, target)
     pl, c = pu.gpu_forward(wl.scene.params, deg, cam)
-    gparams = _full_step_checks(torch, gs, pl, c, ref, target, deg)
+    gparams = _full_step_checks(torch, gs, oracle, pl, c, ref, target, wl.scene.params, deg, cam)
     # one Adam step from zero moments, against the oracle's fp64 Adam on the GPU's gradient
     p0 = wl.scene.params.astype(np.float64)
     pl.adam()
@@ -354,11 +353,10 @@ def test_split_path_parity(torch_cuda, oracle, split_tuning, tune, which):
     gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI, pl.gscreen,
                      pl.grads, pl.ws_render)
     torch.cuda.synchronize()
-    pu.check_screen_grads(pl.gscreen[:, :s.n].cpu().numpy(), o["gscreen"], o["risk"]["g"])
+    pu.check_screen_grads(pl.gscreen[:, :s.n].cpu().numpy(), o["gscreen"], o["risk"]["g"], o["slack"])
     keep = pu.calm(o["risk"]["g"], o["gscreen"])
     g = pl.planar(pl.grads).cpu().numpy()
-    for name, sl in pu.grad_groups(deg).items():
-        pu.check_grad(g[sl], o["gparams"][sl], keep, name=name)
+    pu.check_param_grads(g, o, oracle, s.params, deg, cam, keep)
     stopped = float((o["fwd"]["T"] < 1e-4).mean())
     print(f"  flippable px {n_flip}, not calm G {int((~keep).sum())}, saturated px {stopped:.2f}", flush=True)
 
@@ -431,7 +429,7 @@ def test_workload_full_step(torch_cuda, oracle, cfg):
     ref = oracle.train_step_grads(wl.scene.params, deg, cam, target)
     print(f"  oracle done: {len(ref['keys'])} pairs", flush=True)
     pl, c = pu.gpu_forward(wl.scene.params, deg, cam)
-    g = _full_step_checks(torch, gs, pl, c, ref, target, deg)
+    g = _full_step_checks(torch, gs, oracle, pl, c, ref, target, wl.scene.params, deg, cam)
     # the fused backward with Adam from zero moments: step one moves each parameter by
     # -lr g / (|g| + eps) of its (fused, recomputed) gradient; where the sign of g is well
     # determined this must match the unfused gradient's prediction
