@@ -194,7 +194,7 @@ def cpu_baseline(wl):
     tgt = np.random.default_rng(7).random((3, cam.height, cam.width), dtype=np.float32)
     lr = np.array([1.6e-4, 5e-3, 1e-3, 5e-2, 2.5e-3])
     t0 = time.perf_counter()
-    r = O.train_step_grads(p, deg, cam, tgt)
+    r = O.train_step(p, deg, cam, tgt)
     z = np.zeros_like(p)
     O.adam(p, r["gparams"], z, z, deg, lr, step=1, dtype=np.float32)
     dt = time.perf_counter() - t0

@@ -304,13 +304,26 @@ def forward(scene_params, sh_degree, cam):
     return pre, keys, vals, ranges, fwd
 
 
-def train_step_grads(scene_params, sh_degree, cam, target, lam=0.2):
-    """Forward, loss and backward of one camera; returns a dict of every stage's output and
-    the flip risk of the blend decisions."""
+def train_step(scene_params, sh_degree, cam, target, lam=0.2, with_mass=False):
+    """The method's step for one camera: forward, loss, backward blend and chain (Adam is
+    oracle.adam).  Returns a dict of every stage's output; with_mass adds the term
+    magnitudes of the screen partials (render_bwd)."""
     pre, keys, vals, ranges, fwd = forward(scene_params, sh_degree, cam)
     (total, l1, ssim), dLdI = loss(fwd["rgb"], target, lam)
-    gscreen, mass, count = render_bwd(pre, vals, ranges, cam, fwd, dLdI.astype(np.float32), with_mass=True)
+    r = render_bwd(pre, vals, ranges, cam, fwd, dLdI.astype(np.float32), with_mass=with_mass)
+    gscreen = r[0] if with_mass else r
     gparams = preprocess_bwd(scene_params, sh_degree, cam, gscreen)
-    risk = flip_risk(pre, vals, ranges, cam, dLdI.astype(np.float32))
-    return dict(pre=pre, keys=keys, vals=vals, ranges=ranges, fwd=fwd, loss=(total, l1, ssim), dLdI=dLdI,
-                gscreen=gscreen, gparams=gparams, risk=risk, slack=rounding_slack(mass, count))
+    out = dict(pre=pre, keys=keys, vals=vals, ranges=ranges, fwd=fwd, loss=(total, l1, ssim), dLdI=dLdI,
+               gscreen=gscreen, gparams=gparams)
+    if with_mass:
+        out["mass"], out["count"] = r[1], r[2]
+    return out
+
+
+def train_step_grads(scene_params, sh_degree, cam, target, lam=0.2):
+    """train_step plus what the parity checks need: the flip risk of the blend decisions
+    and the rounding slack of the screen partials."""
+    out = train_step(scene_params, sh_degree, cam, target, lam, with_mass=True)
+    out["risk"] = flip_risk(out["pre"], out["vals"], out["ranges"], cam, out["dLdI"].astype(np.float32))
+    out["slack"] = rounding_slack(out.pop("mass"), out.pop("count"))
+    return out
