@@ -33,19 +33,15 @@ def kernel_bytes(kernel, n, deg, P):
     """Algorithmic HBM bytes of one launch of the streaming kernels (fp32 everywhere).
 
     adam_vec4       per parameter: read theta, g, m, v; write theta, m, v            28 B
-    chain_colour    (Adam fused) per Gaussian: tile count 4, mean 12, colour gradient 12,
-                    read + write theta/m/v of the 3(K+1) colour planes 24 each, write
-                    the view-direction partial 12
-    chain_geometry  (Adam fused) per Gaussian: tile count 4, screen gradients 9 x 4,
-                    read + write theta/m/v of the 11 geometry planes 24 each
+    chain           (Adam fused) per Gaussian: tile count 4, the nine screen gradients
+                    36, read + write theta/m/v of all P planes 24 each
     preprocess_fwd  per Gaussian: read all P planes, write splat 48, depth 4, rect 8,
                     tile count 4
     """
     K1 = (deg + 1) ** 2
     table = {
         "adam_vec4": 28 * P * n,
-        "chain_colour": (4 + 12 + 12 + 24 * 3 * K1 + 12) * n,
-        "chain_geometry": (4 + 36 + 24 * 11) * n,
+        "chain": (4 + 36 + 24 * P) * n,
         "preprocess_fwd": (4 * P + 48 + 4 + 8 + 4) * n,
     }
     return table.get(kernel)

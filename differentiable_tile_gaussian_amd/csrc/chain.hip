@@ -1,19 +1,18 @@
 // Backward chain per Gaussian: screen-space gradients -> parameter gradients, and
 // optionally Adam applied on the spot (without writing the gradient to memory).
 //
-// Two kernels keep register use low on this streaming, HBM-bound pass:
-//   colour part    one wave per colour channel for 64 Gaussians: the DC and band
-//                  gradients of that channel ([GSG] "Spherical harmonics": dL/dsh_k =
-//                  dRGB Y_k; the clamp at zero passes no gradient) and its share of the
-//                  view-direction term, summed over the three channels in LDS;
-//   geometry part  one thread per Gaussian: mean (projected-mean path, J(z) covariance
-//                  path, plus the direction term), log-scales, quaternion and opacity
-//                  logit ([GSG] "From a pixel's blame to the oval's shape and place",
-//                  "The covariance chain", "Where the position gradient comes from";
-//                  [GST] Jacobian slide).
-// gscreen planes: 0 u, 1 v, 2 A, 3 B, 4 C, 5 opacity, 6-8 colour.  The direction term
-// passes from the first kernel to the second through the mean planes of gparams, or,
-// with Adam fused, through gscreen planes 6-8 once the colour part has read them.
+// One block per group of 64 Gaussians (one group of the blocked layout), four waves:
+//   waves 0-2  one colour channel each: the DC and band gradients of that channel
+//              ([GSG] "Spherical harmonics": dL/dsh_k = dRGB Y_k; the clamp at zero
+//              passes no gradient) and its share of the view-direction term;
+//   wave 3     one thread per Gaussian: mean (projected-mean path, J(z) covariance
+//              path, plus the direction term the colour waves leave in LDS),
+//              log-scales, quaternion and opacity logit ([GSG] "From a pixel's blame
+//              to the oval's shape and place", "The covariance chain", "Where the
+//              position gradient comes from"; [GST] Jacobian slide).
+// Wave 3 loads the geometry planes and hands the means and tile counts to the colour
+// waves through LDS; every parameter, moment and screen-gradient byte crosses HBM once.
+// gscreen planes: 0 u, 1 v, 2 A, 3 B, 4 C, 5 opacity, 6-8 colour (read only).
 //
 // Compiled without floating-point contraction, like the forward projection, so the
 // recomputed projection is the forward's bit for bit.
@@ -30,32 +29,49 @@ using namespace proj;
 __device__ inline int colour_plane(int k, int ch) { return k == 0 ? 11 + ch : 14 + 3 * (k - 1) + ch; }
 
 template <int DEG, bool ADAM>
-__global__ void __launch_bounds__(192) chain_colour_kernel(float* __restrict__ params, int n, gs_camera cam,
-                                                            const uint32_t* __restrict__ tiles,
-                                                            float* __restrict__ gscreen, float* __restrict__ gparams,
-                                                            float* __restrict__ m, float* __restrict__ v,
-                                                            AdamArgs a) {
+__global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, int n, gs_camera cam,
+                                                     const uint32_t* __restrict__ tiles,
+                                                     const float* __restrict__ gscreen, float* __restrict__ gparams,
+                                                     float* __restrict__ m, float* __restrict__ v, AdamArgs a) {
   constexpr int K = (DEG + 1) * (DEG + 1) - 1;
   constexpr int P = 11 + 3 * (K + 1);
-  __shared__ float s_gdir[3][3][64];
-  const int lane = threadIdx.x & 63, ch = threadIdx.x >> 6;
+  __shared__ float s_gdir[3][3][64];   // view-direction partials of each colour channel
+  __shared__ float s_mean[3][64];
+  __shared__ uint32_t s_tile[64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int i = blockIdx.x * 64 + lane;
   const bool valid = i < n;
   // This block's 64 Gaussians are one group of the blocked layout: each plane is a
-  // contiguous 256-byte row and the whole colour part one 12 KB stretch per array.
+  // contiguous 256-byte row.  Waves 0-2 take the colour planes of one channel each,
+  // wave 3 the eleven geometry planes.  Every load of a lane is issued before any
+  // arithmetic (the pass is a stream; a load that waited on another would add a
+  // memory round trip).  (Separate code paths per wave kind, with the barriers
+  // inside each, use fewer registers but ran slower.)
   const size_t gb = size_t(blockIdx.x) * P * kGB + lane;
-  // Every load of this lane is issued before any arithmetic (the pass is a stream;
-  // a load that waited on another would add a memory round trip).
+  const int ch = wv;   // colour waves
   uint32_t ntile = 0;
-  float mean[3] = {0.f, 0.f, 0.f};
-  float coef[K + 1], mo[ADAM ? K + 1 : 1], vo[ADAM ? K + 1 : 1];
+  float th[11], gs6[6], mo[ADAM ? 11 : 1], vo[ADAM ? 11 : 1];
+  float coef[K + 1], cmo[ADAM ? K + 1 : 1], cvo[ADAM ? K + 1 : 1];
   float gcol = 0.0f;
-  if (valid) {
-    ntile = tiles[i];
-    if (K > 0) {
+  if (wv == 3) {
+    if (valid) {
+      ntile = tiles[i];
 #pragma unroll
-      for (int c = 0; c < 3; ++c) mean[c] = params[gb + c * kGB];
+      for (int k = 0; k < 11; ++k) th[k] = __builtin_nontemporal_load(params + gb + k * kGB);
+#pragma unroll
+      for (int k = 0; k < 6; ++k) gs6[k] = gscreen[size_t(k) * n + i];
+      if (ADAM) {
+#pragma unroll
+        for (int k = 0; k < 11; ++k) {
+          mo[k] = __builtin_nontemporal_load(m + gb + k * kGB);
+          vo[k] = __builtin_nontemporal_load(v + gb + k * kGB);
+        }
+      }
     }
+    s_tile[lane] = ntile;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) s_mean[c][lane] = valid ? th[c] : 0.0f;
+  } else if (valid) {
 #pragma unroll
     for (int k = 0; k <= K; ++k) coef[k] = __builtin_nontemporal_load(params + gb + colour_plane(k, ch) * kGB);
     gcol = gscreen[(6 + ch) * n + i];
@@ -63,103 +79,68 @@ __global__ void __launch_bounds__(192) chain_colour_kernel(float* __restrict__ p
 #pragma unroll
       for (int k = 0; k <= K; ++k) {
         const size_t o = gb + colour_plane(k, ch) * kGB;
-        mo[k] = __builtin_nontemporal_load(m + o);
-        vo[k] = __builtin_nontemporal_load(v + o);
+        cmo[k] = __builtin_nontemporal_load(m + o);
+        cvo[k] = __builtin_nontemporal_load(v + o);
       }
     }
   }
-  const bool vis = valid && ntile != 0u;
-  float dir[3] = {0.f, 0.f, 0.f};
-  float dlen = 1.0f;
-  float Y[16];
-  if (K > 0 && vis) {
-    dlen = view_dir_from(mean[0], mean[1], mean[2], cam, dir);
-    sh_eval(dir[0], dir[1], dir[2], Y);
-  }
-  float gc = 0.0f;
-  if (vis) {
-    float raw = coef[0];
-#pragma unroll
-    for (int k = 1; k <= K; ++k) raw = raw + coef[k] * Y[k];
-    gc = raw < 0.0f ? 0.0f : gcol;
-  }
-  if (K > 0) {
-    float gd[3] = {0.f, 0.f, 0.f};
+  __syncthreads();   // tile counts and means
+  if (wv < 3) {
+    const bool vis = valid && s_tile[lane] != 0u;
+    float dir[3] = {0.f, 0.f, 0.f};
+    float Y[16];
+    if (K > 0 && vis) {
+      view_dir_from(s_mean[0][lane], s_mean[1][lane], s_mean[2][lane], cam, dir);
+      sh_eval(dir[0], dir[1], dir[2], Y);
+    }
+    float gc = 0.0f;
     if (vis) {
-      float wk[16];
+      float raw = coef[0];
 #pragma unroll
-      for (int k = 1; k <= K; ++k) wk[k] = gc * coef[k];
-      sh_grad_dot(dir[0], dir[1], dir[2], wk, K, gd);
+      for (int k = 1; k <= K; ++k) raw = raw + coef[k] * Y[k];
+      gc = raw < 0.0f ? 0.0f : gcol;
     }
-#pragma unroll
-    for (int c = 0; c < 3; ++c) s_gdir[ch][c][lane] = gd[c];
-  }
-  if (valid) {
-#pragma unroll
-    for (int k = 0; k <= K; ++k) {
-      const float g = k == 0 ? gc : (vis ? gc * Y[k] : 0.0f);
-      const size_t o = gb + colour_plane(k, ch) * kGB;
-      if (ADAM) {
-        __builtin_nontemporal_store(adam_update(coef[k], g, mo[k], vo[k], a.lr[4], a), params + o);
-        __builtin_nontemporal_store(mo[k], m + o);
-        __builtin_nontemporal_store(vo[k], v + o);
-      } else {
-        gparams[o] = g;
-      }
-    }
-  }
-  if (K > 0) {
-    __syncthreads();
-    if (ch == 0 && valid) {
-      float gt[3], out[3] = {0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 3; ++c) gt[c] = s_gdir[0][c][lane] + s_gdir[1][c][lane] + s_gdir[2][c][lane];
+    if (K > 0) {
+      float gd[3] = {0.f, 0.f, 0.f};
       if (vis) {
-        const float dd = dir[0] * gt[0] + dir[1] * gt[1] + dir[2] * gt[2];
+        float wk[16];
 #pragma unroll
-        for (int c = 0; c < 3; ++c) out[c] = (gt[c] - dir[c] * dd) / dlen;
+        for (int k = 1; k <= K; ++k) wk[k] = gc * coef[k];
+        sh_grad_dot(dir[0], dir[1], dir[2], wk, K, gd);
       }
-      // to the mean planes of gparams, or (Adam fused) to gscreen planes 6-8
 #pragma unroll
-      for (int c = 0; c < 3; ++c) {
-        if (ADAM)
-          gscreen[size_t(6 + c) * n + i] = out[c];
-        else
-          gparams[gb + c * kGB] = out[c];
+      for (int c = 0; c < 3; ++c) s_gdir[ch][c][lane] = gd[c];
+    }
+    if (valid) {
+#pragma unroll
+      for (int k = 0; k <= K; ++k) {
+        const float g = k == 0 ? gc : (vis ? gc * Y[k] : 0.0f);
+        const size_t o = gb + colour_plane(k, ch) * kGB;
+        if (ADAM) {
+          __builtin_nontemporal_store(adam_update(coef[k], g, cmo[k], cvo[k], a.lr[4], a), params + o);
+          __builtin_nontemporal_store(cmo[k], m + o);
+          __builtin_nontemporal_store(cvo[k], v + o);
+        } else {
+          gparams[o] = g;
+        }
       }
     }
   }
-}
-
-template <int DEG, bool ADAM>
-__global__ void __launch_bounds__(256) chain_geometry_kernel(float* __restrict__ params, int n, gs_camera cam,
-                                                              const uint32_t* __restrict__ tiles,
-                                                              const float* __restrict__ gscreen,
-                                                              float* __restrict__ gparams, float* __restrict__ m,
-                                                              float* __restrict__ v, AdamArgs a) {
-  constexpr int P = 11 + 3 * (DEG + 1) * (DEG + 1);
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const size_t gb = size_t(i / kGB) * P * kGB + (i % kGB);
-  // all loads first (see the colour kernel)
-  const uint32_t ntile = tiles[i];
-  float th[11], gs6[6], gp[11], mo[ADAM ? 11 : 1], vo[ADAM ? 11 : 1];
-#pragma unroll
-  for (int k = 0; k < 11; ++k) th[k] = __builtin_nontemporal_load(params + gb + k * kGB);
-#pragma unroll
-  for (int k = 0; k < 6; ++k) gs6[k] = gscreen[size_t(k) * n + i];
+  __syncthreads();   // view-direction partials of the three channels
+  if (wv != 3 || !valid) return;
+  float gp[11];
 #pragma unroll
   for (int k = 0; k < 11; ++k) gp[k] = 0.0f;
-  if (DEG > 0) {
+  if (K > 0 && ntile != 0u) {
+    // the colour's view-direction term, projected off the unit direction
+    float dir[3];
+    const float dlen = view_dir_from(th[0], th[1], th[2], cam, dir);
+    float gt[3];
 #pragma unroll
-    for (int c = 0; c < 3; ++c) gp[c] = ADAM ? gscreen[size_t(6 + c) * n + i] : gparams[gb + c * kGB];
-  }
-  if (ADAM) {
+    for (int c = 0; c < 3; ++c) gt[c] = s_gdir[0][c][lane] + s_gdir[1][c][lane] + s_gdir[2][c][lane];
+    const float dd = dir[0] * gt[0] + dir[1] * gt[1] + dir[2] * gt[2];
 #pragma unroll
-    for (int k = 0; k < 11; ++k) {
-      mo[k] = __builtin_nontemporal_load(m + gb + k * kGB);
-      vo[k] = __builtin_nontemporal_load(v + gb + k * kGB);
-    }
+    for (int c = 0; c < 3; ++c) gp[c] = (gt[c] - dir[c] * dd) / dlen;
   }
   Proj g;
   if (ntile != 0u && project_geometry_from(th, cam, g)) {
@@ -243,21 +224,16 @@ __global__ void __launch_bounds__(256) chain_geometry_kernel(float* __restrict__
   }
 }
 
+
 template <int DEG, bool ADAM>
-void launch_chain_deg(float* params, int n, const gs_camera& cam, const uint32_t* tiles, float* gscreen,
+void launch_chain_deg(float* params, int n, const gs_camera& cam, const uint32_t* tiles, const float* gscreen,
                       float* gparams, float* m, float* v, const AdamArgs& a, hipStream_t s) {
-  {
-    GSK_PROF("chain_colour", s);
-    chain_colour_kernel<DEG, ADAM><<<div_up(n, 64), 192, 0, s>>>(params, n, cam, tiles, gscreen, gparams, m, v, a);
-  }
-  {
-    GSK_PROF("chain_geometry", s);
-    chain_geometry_kernel<DEG, ADAM><<<div_up(n, 256), 256, 0, s>>>(params, n, cam, tiles, gscreen, gparams, m, v, a);
-  }
+  GSK_PROF("chain", s);
+  chain_kernel<DEG, ADAM><<<div_up(n, 64), 256, 0, s>>>(params, n, cam, tiles, gscreen, gparams, m, v, a);
 }
 
 template <bool ADAM>
-void launch_chain_mode(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles, float* gscreen,
+void launch_chain_mode(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles, const float* gscreen,
                        float* gparams, float* m, float* v, const AdamArgs& a, hipStream_t s) {
   switch (deg) {
     case 0: launch_chain_deg<0, ADAM>(params, n, cam, tiles, gscreen, gparams, m, v, a, s); break;
@@ -270,7 +246,7 @@ void launch_chain_mode(float* params, int n, int deg, const gs_camera& cam, cons
 }  // namespace
 
 hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_camera& cam,
-                                 const uint32_t* tiles, float* gscreen, float* gparams, hipStream_t s) {
+                                 const uint32_t* tiles, const float* gscreen, float* gparams, hipStream_t s) {
   if (n == 0) return hipSuccess;
   launch_chain_mode<false>(const_cast<float*>(params), n, deg, cam, tiles, gscreen, gparams, nullptr, nullptr,
                            AdamArgs{}, s);
@@ -278,7 +254,7 @@ hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_c
 }
 
 hipError_t launch_chain_adam(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
-                             float* gscreen, float* m, float* v, const AdamArgs& a, hipStream_t s) {
+                             const float* gscreen, float* m, float* v, const AdamArgs& a, hipStream_t s) {
   if (n == 0) return hipSuccess;
   launch_chain_mode<true>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, s);
   return hipGetLastError();

@@ -33,12 +33,12 @@ __host__ __device__ inline T* gaussian_base(T* params, int i, int P) {
 hipError_t launch_preprocess_fwd(const float* params, int n, int deg, const gs_camera& cam, const gs_proj& out,
                                  uint32_t* block_tiles, uint64_t* total_pairs, hipStream_t s);
 
-// ---- chain.hip (gscreen planes 6-8 are read; with Adam they are then overwritten)
+// ---- chain.hip (gscreen is read only)
 struct AdamArgs;
 hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_camera& cam,
-                                 const uint32_t* tiles, float* gscreen, float* gparams, hipStream_t s);
+                                 const uint32_t* tiles, const float* gscreen, float* gparams, hipStream_t s);
 hipError_t launch_chain_adam(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
-                             float* gscreen, float* m, float* v, const AdamArgs& a, hipStream_t s);
+                             const float* gscreen, float* m, float* v, const AdamArgs& a, hipStream_t s);
 
 // ---- scan.hip: exclusive prefix sum of n u32 values into out[0..n], out[n] = total.
 // The total is also written as u64 to *total64 (device) so that overflow of 32 bits is seen.

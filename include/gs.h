@@ -204,8 +204,8 @@ int32_t gs_adam_step(float* params, const float* grads, float* m, float* v, int6
 /* gs_render_bwd followed by gs_adam_step, fused: the chain applies Adam to each parameter as
  * soon as its gradient is known, so the parameter gradient is never written to memory (it
  * saves two passes over the parameter arrays).  Same arguments and results as the two calls, with
- * params updated in place; gscreen is scratch here: on return its planes 6-8 hold the mean
- * gradient's view-direction term instead of the colour gradients. */
+ * params updated in place; gscreen holds the screen-space partials on return, as after
+ * gs_render_bwd. */
 int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs_proj* proj, const uint32_t* vals,
                            const uint32_t* ranges, uint32_t total_pairs, const gs_camera* cam,
                            const float* T_final, const uint32_t* n_contrib, const float* dL_dimg, float* gscreen,
