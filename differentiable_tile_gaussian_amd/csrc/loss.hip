@@ -5,17 +5,24 @@
 // of standard deviation 1.5 (normalised), C1 = 0.01^2, C2 = 0.03^2, zero padding,
 // and is averaged over pixels and channels; D-SSIM carries no one-half.
 //
-// The 2-D window is the outer product of the normalised 1-D window, so the five
-// local moments are computed with a horizontal then a vertical 11-tap pass through
-// LDS (32x16 output pixels per block, 5-pixel halo).  Each thread makes four
-// adjacent outputs of a row in the horizontal pass (14 inputs read once) and two
-// adjacent rows of a column in the vertical pass, reusing the taps in registers.
-//   ssim_fwd   moments -> SSIM per pixel, the three derivative maps
-//                a = dS/dmu_x - 2 mu_x dS/dvar_x - mu_y dS/dcov,  b = dS/dvar_x,  c = dS/dcov,
-//              and per-block partial sums of SSIM and |x - y|
-//   ssim_bwd   dL/dx = (1-lambda)/N sign(x-y) - lambda/N (w*a + 2 x (w*b) + y (w*c))
-//              (w* = the same zero-padded window; it is symmetric, so it is its own adjoint)
-//   finalize   sums the partials (fp64) into total, L1, mean SSIM
+// The 2-D window is the outer product of the normalised 1-D window w.  Per pixel the
+// SSIM map needs the five local moments (w*x, w*y, w*xx, w*yy, w*xy); its gradient is
+//   dL/dx = (1-lambda)/N sign(x-y) - lambda/N (w*a + 2 x (w*b) + y (w*c))
+// with the derivative maps a = dS/dmu_x - 2 mu_x dS/dvar_x - mu_y dS/dcov,
+// b = dS/dvar_x, c = dS/dcov (w* is the same zero-padded window; it is symmetric, so
+// it is its own adjoint).
+//
+// One kernel does both passes over a strip of rows, sliding down the image one row
+// per step.  A block of kSW threads owns kSW adjacent "moment" columns; the middle
+// kSW - 10 of them are its output columns.  At step i the block stages input row i
+// in LDS, each thread takes the horizontal moments of its column at row i and keeps
+// the last eleven in registers (a ring, so the vertical sums need no LDS); with
+// them it finishes the moments, SSIM and a, b, c of row i - 5, puts a, b, c in LDS,
+// takes their horizontal sums at its column and keeps the last eleven of those; and
+// with those finishes the gradient of row i - 10.  Inputs outside the image are
+// zero, and so are a, b, c there.  The a, b, c maps never leave the chip.
+//   loss_finalize   sums the per-block SSIM and |x - y| partials (fp64) into total,
+//                   L1 and mean SSIM
 #include <math.h>
 
 #include "gs_internal.h"
@@ -24,209 +31,180 @@
 namespace gsk {
 namespace {
 
-constexpr int kTW = 32, kTH = 16, kR = 5;
-constexpr int kPW = kTW + 2 * kR;   // 42
-constexpr int kPH = kTH + 2 * kR;   // 26
+constexpr int kR = 5;                 // window radius
+constexpr int kSW = 128;              // moment columns per block (threads)
+constexpr int kSO = kSW - 2 * kR;     // output columns per block
+constexpr int kSIn = kSW + 2 * kR;    // input columns staged per row
+constexpr int kRing = 2 * kR + 1;     // 11
+constexpr int kSR = 35;               // output rows per block: the kSR + 4 kR steps of a
+constexpr int kSteps = kSR + 4 * kR;  // strip are a whole number of ring turns, so the
+static_assert(kSteps % kRing == 0, "whole ring turns");   // step loop unrolls with static slots
 
 struct Window { float w[11]; };
 
-__device__ inline void reduce_block_2(float& a, float& b, float* s_tmp) {
-  const int lane = __lane_id(), wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    a += __shfl_xor(a, d, 64);
-    b += __shfl_xor(b, d, 64);
-  }
-  if (lane == 0) {
-    s_tmp[2 * wave] = a;
-    s_tmp[2 * wave + 1] = b;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    a = 0.f; b = 0.f;
-    for (int w = 0; w < 4; ++w) { a += s_tmp[2 * w]; b += s_tmp[2 * w + 1]; }
-  }
+__device__ inline float load_or_zero(const float* __restrict__ p, int row, int col, int H, int W) {
+  return (row >= 0 && row < H && col >= 0 && col < W) ? p[size_t(row) * W + col] : 0.0f;
 }
 
-// Horizontal pass for row r: outputs 4g .. 4g+3 of the 32-wide tile from the 14 inputs
-// 4g .. 4g+13 of the 42-wide row (each input read once into registers).
-constexpr int kHG = 4;                  // outputs per thread, horizontal
-constexpr int kHItems = kPH * (kTW / kHG);   // 208 (row, group) items
-constexpr int kVG = 2;                  // outputs per thread, vertical
-static_assert((kTW * kTH) / kVG == 256, "one vertical item per thread");
-
-__global__ void __launch_bounds__(256) ssim_fwd_kernel(const float* __restrict__ img, const float* __restrict__ tgt,
-                                                        int H, int W, Window win, float* __restrict__ amap,
-                                                        float* __restrict__ bmap, float* __restrict__ cmap,
-                                                        float* __restrict__ partial) {
-  __shared__ float sx[kPH][kPW + 1];
-  __shared__ float sy[kPH][kPW + 1];
-  __shared__ float4 hs[5][kPH][kTW / 4];   // horizontal sums of x, y, xx, yy, xy
-  __shared__ float s_tmp[8];
+__global__ void __launch_bounds__(kSW) ssim_fused_kernel(const float* __restrict__ img,
+                                                         const float* __restrict__ tgt, int H, int W, Window win,
+                                                         float kl1, float kss, float* __restrict__ grad,
+                                                         float* __restrict__ partial) {
+  // the last twelve input rows, row i in slot (i - first row) % 12: one more than the
+  // eleven a step reads, so a row is rewritten only after a full step has passed its
+  // last reader (the gradient of row i, read at step i + 10)
+  __shared__ float s_x[kRing + 1][kSIn], s_y[kRing + 1][kSIn];
+  __shared__ float s_abc[2][3][kSW];
+  __shared__ float s_tmp[2 * (kSW / 64)];
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid >> 6;
   const int ch = blockIdx.z;
-  const int x0 = blockIdx.x * kTW, y0 = blockIdx.y * kTH;
+  const int x0 = blockIdx.x * kSO, y0 = blockIdx.y * kSR;
+  const int cf = x0 - kR + tid;                       // this thread's moment column
+  const bool out_col = tid >= kR && tid < kSW - kR && cf < W;
   const size_t HW = size_t(H) * W;
-  const float* X = img + ch * HW;
-  const float* Y = tgt + ch * HW;
-  for (int k = threadIdx.x; k < kPH * kPW; k += 256) {
-    const int r = k / kPW, c = k % kPW;
-    const int gy = y0 + r - kR, gx = x0 + c - kR;
-    const bool in = gy >= 0 && gy < H && gx >= 0 && gx < W;
-    sx[r][c] = in ? X[size_t(gy) * W + gx] : 0.0f;
-    sy[r][c] = in ? Y[size_t(gy) * W + gx] : 0.0f;
-  }
-  __syncthreads();
-  if (threadIdx.x < kHItems) {
-    const int r = threadIdx.x / (kTW / kHG), g = threadIdx.x % (kTW / kHG);
-    float xv[kHG + 10], yv[kHG + 10];
-#pragma unroll
-    for (int j = 0; j < kHG + 10; ++j) {
-      xv[j] = sx[r][kHG * g + j];
-      yv[j] = sy[r][kHG * g + j];
-    }
-    float m[5][kHG];
-#pragma unroll
-    for (int o = 0; o < kHG; ++o) {
-      m[0][o] = m[1][o] = m[2][o] = m[3][o] = m[4][o] = 0.f;
-#pragma unroll
-      for (int j = 0; j < 11; ++j) {
-        const float wj = win.w[j], xj = xv[o + j], yj = yv[o + j];
-        m[0][o] += wj * xj;
-        m[1][o] += wj * yj;
-        m[2][o] += wj * (xj * xj);
-        m[3][o] += wj * (yj * yj);
-        m[4][o] += wj * (xj * yj);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 5; ++q) hs[q][r][g] = make_float4(m[q][0], m[q][1], m[q][2], m[q][3]);
-  }
-  __syncthreads();
+  const float* __restrict__ X = img + ch * HW;
+  const float* __restrict__ Y = tgt + ch * HW;
   const float C1 = 0.01f * 0.01f, C2 = 0.03f * 0.03f;
-  float ssim_acc = 0.f, l1_acc = 0.f;
-  {
-    // vertical pass: column c, output rows kVG h .. kVG h + 1
-    const int c = threadIdx.x % kTW, h = threadIdx.x / kTW;
-    const float* hsf = reinterpret_cast<const float*>(hs);
-    float v[5][kVG];
+  // input column x0 - 2 kR + k for k in [0, kSIn): thread tid stages k = tid and,
+  // for tid < 2 kR, k = kSW + tid
+  const int cin0 = x0 - 2 * kR + tid, cin1 = x0 - 2 * kR + kSW + tid;
+  const int ifirst = y0 - 2 * kR, ilast = y0 + kSR + 2 * kR - 1;
+  float px0 = load_or_zero(X, ifirst, cin0, H, W), py0 = load_or_zero(Y, ifirst, cin0, H, W);
+  float px1 = 0.0f, py1 = 0.0f;
+  if (tid < 2 * kR) {
+    px1 = load_or_zero(X, ifirst, cin1, H, W);
+    py1 = load_or_zero(Y, ifirst, cin1, H, W);
+  }
+  float hm[kRing][5], ga[kRing][3];
 #pragma unroll
-    for (int o = 0; o < kVG; ++o) v[0][o] = v[1][o] = v[2][o] = v[3][o] = v[4][o] = 0.f;
+  for (int u = 0; u < kRing; ++u) {
 #pragma unroll
-    for (int i = 0; i < kVG + 10; ++i) {
-      const int rr = kVG * h + i;
-      float t[5];
+    for (int q = 0; q < 5; ++q) hm[u][q] = 0.0f;
 #pragma unroll
-      for (int q = 0; q < 5; ++q) t[q] = hsf[(q * kPH + rr) * kTW + c];
+    for (int q = 0; q < 3; ++q) ga[u][q] = 0.0f;
+  }
+  float ssim_acc = 0.0f, l1_acc = 0.0f;
+  for (int turn = 0; turn < kSteps / kRing; ++turn) {
 #pragma unroll
-      for (int o = 0; o < kVG; ++o) {
-        const int j = i - o;
-        if (j >= 0 && j < 11) {
+    for (int u = 0; u < kRing; ++u) {
+      const int i = ifirst + turn * kRing + u;   // the register ring slot of step i is u
+      const int b = i & 1;
+      const int k = turn * kRing + u;
+      const int row_i = k % (kRing + 1), row_r = (k + kRing + 1 - kR) % (kRing + 1),
+                row_q = (k + kRing + 1 - 2 * kR) % (kRing + 1);   // LDS slots of rows i, i-5, i-10
+      s_x[row_i][tid] = px0;
+      s_y[row_i][tid] = py0;
+      if (tid < 2 * kR) {
+        s_x[row_i][kSW + tid] = px1;
+        s_y[row_i][kSW + tid] = py1;
+      }
+      if (i < ilast) {   // the next row's loads are in flight during this step
+        px0 = load_or_zero(X, i + 1, cin0, H, W);
+        py0 = load_or_zero(Y, i + 1, cin0, H, W);
+        if (tid < 2 * kR) {
+          px1 = load_or_zero(X, i + 1, cin1, H, W);
+          py1 = load_or_zero(Y, i + 1, cin1, H, W);
+        }
+      }
+      __syncthreads();
+      {
+        float m[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) {
+          const float wj = win.w[j], xv = s_x[row_i][tid + j], yv = s_y[row_i][tid + j];
+          m[0] += wj * xv;
+          m[1] += wj * yv;
+          m[2] += wj * (xv * xv);
+          m[3] += wj * (yv * yv);
+          m[4] += wj * (xv * yv);
+        }
+#pragma unroll
+        for (int q = 0; q < 5; ++q) hm[u][q] = m[q];
+      }
+      if (i >= y0) {
+        // moments, SSIM and a, b, c of row r = i - 5 (ring slots of steps i-10 .. i)
+        const int r = i - kR;
+        float mv[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) {
           const float wj = win.w[j];
 #pragma unroll
-          for (int q = 0; q < 5; ++q) v[q][o] += wj * t[q];
+          for (int q = 0; q < 5; ++q) mv[q] += wj * hm[(u + 1 + j) % kRing][q];
+        }
+        float a = 0.f, bb = 0.f, c = 0.f;
+        if (r >= 0 && r < H && cf >= 0 && cf < W) {
+          const float mx = mv[0], my = mv[1], exx = mv[2], eyy = mv[3], exy = mv[4];
+          const float sxx = exx - mx * mx, syy = eyy - my * my, sxy = exy - mx * my;
+          const float A1 = 2.f * mx * my + C1, A2 = 2.f * sxy + C2;
+          const float B1 = mx * mx + my * my + C1, B2 = sxx + syy + C2;
+          const float inv = 1.0f / (B1 * B2);
+          const float S = A1 * A2 * inv;
+          const float dmu = 2.f * my * A2 * inv - 2.f * mx * S / B1;
+          const float dvar = -S / B2;
+          const float dcov = 2.f * A1 * inv;
+          a = dmu - 2.f * mx * dvar - my * dcov;
+          bb = dvar;
+          c = dcov;
+          if (out_col && r >= y0 && r < y0 + kSR) {
+            ssim_acc += S;
+            l1_acc += fabsf(s_x[row_r][tid + kR] - s_y[row_r][tid + kR]);
+          }
+        }
+        s_abc[b][0][tid] = a;
+        s_abc[b][1][tid] = bb;
+        s_abc[b][2][tid] = c;
+      }
+      __syncthreads();
+      if (i >= y0) {
+        float g[3] = {0.f, 0.f, 0.f};
+        if (tid >= kR && tid < kSW - kR) {
+#pragma unroll
+          for (int j = 0; j < kRing; ++j) {
+            const float wj = win.w[j];
+#pragma unroll
+            for (int q = 0; q < 3; ++q) g[q] += wj * s_abc[b][q][tid - kR + j];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 3; ++q) ga[u][q] = g[q];
+      }
+      if (i >= y0 + 2 * kR) {
+        // gradient of row q = i - 10: vertical sums of the horizontal sums of a, b, c
+        // at rows q-5 .. q+5 (steps i-10 .. i); x, y of row q were staged at step i-10
+        const int q = i - 2 * kR;
+        float cv[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) {
+          const float wj = win.w[j];
+#pragma unroll
+          for (int t = 0; t < 3; ++t) cv[t] += wj * ga[(u + 1 + j) % kRing][t];
+        }
+        if (out_col && q < H) {
+          const float xv = s_x[row_q][tid + kR], yv = s_y[row_q][tid + kR];
+          const float d = xv - yv;
+          const float sgn = d > 0.f ? 1.f : (d < 0.f ? -1.f : 0.f);
+          grad[ch * HW + size_t(q) * W + cf] = kl1 * sgn + kss * (cv[0] + 2.f * xv * cv[1] + yv * cv[2]);
         }
       }
     }
-#pragma unroll
-    for (int o = 0; o < kVG; ++o) {
-      const int r = kVG * h + o;
-      const int gy = y0 + r, gx = x0 + c;
-      if (gy >= H || gx >= W) continue;
-      const float mx = v[0][o], my = v[1][o], exx = v[2][o], eyy = v[3][o], exy = v[4][o];
-      const float sxx = exx - mx * mx, syy = eyy - my * my, sxy = exy - mx * my;
-      const float A1 = 2.f * mx * my + C1, A2 = 2.f * sxy + C2;
-      const float B1 = mx * mx + my * my + C1, B2 = sxx + syy + C2;
-      const float inv = 1.0f / (B1 * B2);
-      const float S = A1 * A2 * inv;
-      const float dmu = 2.f * my * A2 * inv - 2.f * mx * S / B1;
-      const float dvar = -S / B2;
-      const float dcov = 2.f * A1 * inv;
-      const size_t oo = ch * HW + size_t(gy) * W + gx;
-      amap[oo] = dmu - 2.f * mx * dvar - my * dcov;
-      bmap[oo] = dvar;
-      cmap[oo] = dcov;
-      ssim_acc += S;
-      l1_acc += fabsf(sx[r + kR][c + kR] - sy[r + kR][c + kR]);
-    }
   }
-  reduce_block_2(ssim_acc, l1_acc, s_tmp);
-  if (threadIdx.x == 0) {
-    const int b = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
-    partial[2 * b] = ssim_acc;
-    partial[2 * b + 1] = l1_acc;
-  }
-}
-
-__global__ void __launch_bounds__(256) ssim_bwd_kernel(const float* __restrict__ img, const float* __restrict__ tgt,
-                                                        int H, int W, Window win, float lambda,
-                                                        const float* __restrict__ amap,
-                                                        const float* __restrict__ bmap,
-                                                        const float* __restrict__ cmap, float* __restrict__ grad) {
-  __shared__ float sa[3][kPH][kPW + 1];
-  __shared__ float4 hs[3][kPH][kTW / 4];
-  const int ch = blockIdx.z;
-  const int x0 = blockIdx.x * kTW, y0 = blockIdx.y * kTH;
-  const size_t HW = size_t(H) * W;
-  const float* maps[3] = {amap + ch * HW, bmap + ch * HW, cmap + ch * HW};
-  for (int k = threadIdx.x; k < kPH * kPW; k += 256) {
-    const int r = k / kPW, c = k % kPW;
-    const int gy = y0 + r - kR, gx = x0 + c - kR;
-    const bool in = gy >= 0 && gy < H && gx >= 0 && gx < W;
-    const size_t o = size_t(gy) * W + gx;
+  // block sums of SSIM and |x - y|
 #pragma unroll
-    for (int m = 0; m < 3; ++m) sa[m][r][c] = in ? maps[m][o] : 0.0f;
+  for (int d = 32; d >= 1; d >>= 1) {
+    ssim_acc += __shfl_xor(ssim_acc, d, 64);
+    l1_acc += __shfl_xor(l1_acc, d, 64);
+  }
+  if (lane == 0) {
+    s_tmp[2 * wave] = ssim_acc;
+    s_tmp[2 * wave + 1] = l1_acc;
   }
   __syncthreads();
-  if (threadIdx.x < kHItems) {
-    const int r = threadIdx.x / (kTW / kHG), g = threadIdx.x % (kTW / kHG);
-#pragma unroll
-    for (int m = 0; m < 3; ++m) {
-      float in[kHG + 10];
-#pragma unroll
-      for (int j = 0; j < kHG + 10; ++j) in[j] = sa[m][r][kHG * g + j];
-      float out[kHG];
-#pragma unroll
-      for (int o = 0; o < kHG; ++o) {
-        out[o] = 0.f;
-#pragma unroll
-        for (int j = 0; j < 11; ++j) out[o] += win.w[j] * in[o + j];
-      }
-      hs[m][r][g] = make_float4(out[0], out[1], out[2], out[3]);
-    }
-  }
-  __syncthreads();
-  const float invN = 1.0f / float(3 * HW);
-  const float kl1 = (1.0f - lambda) * invN, kss = -lambda * invN;
-  const int c = threadIdx.x % kTW, h = threadIdx.x / kTW;
-  const float* hsf = reinterpret_cast<const float*>(hs);
-  float v[3][kVG];
-#pragma unroll
-  for (int o = 0; o < kVG; ++o) v[0][o] = v[1][o] = v[2][o] = 0.f;
-#pragma unroll
-  for (int i = 0; i < kVG + 10; ++i) {
-    const int rr = kVG * h + i;
-    float t[3];
-#pragma unroll
-    for (int q = 0; q < 3; ++q) t[q] = hsf[(q * kPH + rr) * kTW + c];
-#pragma unroll
-    for (int o = 0; o < kVG; ++o) {
-      const int j = i - o;
-      if (j >= 0 && j < 11) {
-        const float wj = win.w[j];
-#pragma unroll
-        for (int q = 0; q < 3; ++q) v[q][o] += wj * t[q];
-      }
-    }
-  }
-#pragma unroll
-  for (int o = 0; o < kVG; ++o) {
-    const int gy = y0 + kVG * h + o, gx = x0 + c;
-    if (gy >= H || gx >= W) continue;
-    const size_t oo = ch * HW + size_t(gy) * W + gx;
-    const float xv = img[oo], yv = tgt[oo];
-    const float d = xv - yv;
-    const float sgn = d > 0.f ? 1.f : (d < 0.f ? -1.f : 0.f);
-    grad[oo] = kl1 * sgn + kss * (v[0][o] + 2.f * xv * v[1][o] + yv * v[2][o]);
+  if (tid == 0) {
+    float sa = 0.f, sb = 0.f;
+    for (int w = 0; w < kSW / 64; ++w) { sa += s_tmp[2 * w]; sb += s_tmp[2 * w + 1]; }
+    const int blk = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    partial[2 * blk] = sa;
+    partial[2 * blk + 1] = sb;
   }
 }
 
@@ -261,9 +239,8 @@ inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 }  // namespace
 
 size_t loss_ws_bytes(int H, int W) {
-  const size_t NE = size_t(3) * H * W;
-  const size_t nb = size_t(div_up(W, kTW)) * div_up(H, kTH) * 3;
-  return 3 * align256(NE * 4) + align256(nb * 2 * 4);
+  const size_t nb = size_t(div_up(W, kSO)) * div_up(H, kSR) * 3;
+  return align256(nb * 2 * 4);
 }
 
 hipError_t launch_loss(const float* img, const float* target, int H, int W, float lambda, float* loss_out,
@@ -276,19 +253,13 @@ hipError_t launch_loss(const float* img, const float* target, int H, int W, floa
   }
   for (int j = 0; j < 11; ++j) win.w[j] = float(wd[j] / wsum);
   const size_t NE = size_t(3) * H * W;
-  char* p = static_cast<char*>(ws);
-  float* amap = reinterpret_cast<float*>(p); p += align256(NE * 4);
-  float* bmap = reinterpret_cast<float*>(p); p += align256(NE * 4);
-  float* cmap = reinterpret_cast<float*>(p); p += align256(NE * 4);
-  float* partial = reinterpret_cast<float*>(p);
-  const dim3 grid(div_up(W, kTW), div_up(H, kTH), 3);
+  float* partial = static_cast<float*>(ws);
+  const dim3 grid(div_up(W, kSO), div_up(H, kSR), 3);
+  const float invN = 1.0f / float(NE);
   {
-    GSK_PROF("ssim_fwd", s);
-    ssim_fwd_kernel<<<grid, 256, 0, s>>>(img, target, H, W, win, amap, bmap, cmap, partial);
-  }
-  {
-    GSK_PROF("ssim_bwd", s);
-    ssim_bwd_kernel<<<grid, 256, 0, s>>>(img, target, H, W, win, lambda, amap, bmap, cmap, grad);
+    GSK_PROF("ssim", s);
+    ssim_fused_kernel<<<grid, kSW, 0, s>>>(img, target, H, W, win, (1.0f - lambda) * invN, -lambda * invN, grad,
+                                           partial);
   }
   const int nb = int(grid.x * grid.y * grid.z);
   {
