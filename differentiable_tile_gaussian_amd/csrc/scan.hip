@@ -1,7 +1,9 @@
-// Exclusive prefix sum of u32 values (reduce, then scan of the block sums, then
-// apply).  Used for the per-Gaussian tile counts ([GSG] "Why tiling, and the five
-// stages": the scan that reserves each Gaussian's slot range) and for the radix
-// sort's digit histograms.  No inter-block waiting: three plain launches.
+// Exclusive prefix sum of u32 values (reduce, then apply).  Used for the per-Gaussian
+// tile counts ([GSG] "Why tiling, and the five stages": the scan that reserves each
+// Gaussian's slot range) and for the radix sort's digit histograms.  No inter-block
+// waiting: two plain launches.  The first writes one sum per tile of 2048 values; in
+// the second each block adds up the sums of the tiles before its own (a few hundred
+// at most here, one or a few per thread) and scans its tile.
 #include "gs_internal.h"
 #include "profile.h"
 
@@ -17,16 +19,6 @@ __device__ inline uint32_t wave_inclusive_scan(uint32_t v) {
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const uint32_t t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
-  return v;
-}
-
-__device__ inline uint64_t wave_inclusive_scan64(uint64_t v) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint64_t t = __shfl_up(v, d, 64);
     if (lane >= d) v += t;
   }
   return v;
@@ -64,41 +56,30 @@ __global__ void __launch_bounds__(kScanThreads) scan_reduce_kernel(const uint32_
   if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
 }
 
-// One block: exclusive scan of nb u64 block sums in place; writes the grand total.
-__global__ void __launch_bounds__(1024) scan_blocks_kernel(uint64_t* __restrict__ sums, int nb,
-                                                           uint64_t* __restrict__ total64,
-                                                           uint32_t* __restrict__ out_last) {
-  __shared__ uint64_t s_wave[16];
-  __shared__ uint64_t s_carry;
-  if (threadIdx.x == 0) s_carry = 0;
-  __syncthreads();
-  const int lane = __lane_id(), wave = threadIdx.x >> 6;
-  for (int base = 0; base < nb; base += 1024) {
-    const int idx = base + threadIdx.x;
-    const uint64_t v = idx < nb ? sums[idx] : 0;
-    const uint64_t inc = wave_inclusive_scan64(v);
-    if (lane == 63) s_wave[wave] = inc;
-    __syncthreads();
-    uint64_t pre = s_carry, tot = 0;
-    for (int w = 0; w < 16; ++w) {
-      if (w < wave) pre += s_wave[w];
-      tot += s_wave[w];
-    }
-    if (idx < nb) sums[idx] = pre + inc - v;
-    __syncthreads();
-    if (threadIdx.x == 0) s_carry += tot;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    *total64 = s_carry;
-    *out_last = uint32_t(s_carry);
-  }
-}
-
 __global__ void __launch_bounds__(kScanThreads) scan_apply_kernel(const uint32_t* __restrict__ in, int64_t n,
-                                                                  const uint64_t* __restrict__ block_prefix,
-                                                                  uint32_t* __restrict__ out) {
+                                                                  const uint64_t* __restrict__ block_sums, int nb,
+                                                                  uint32_t* __restrict__ out,
+                                                                  uint64_t* __restrict__ total64) {
   __shared__ uint32_t s_wave[kScanThreads / 64];
+  __shared__ uint64_t s_part[kScanThreads / 64];
+  // the sums of the tiles before this one (the last block also adds its own: the total)
+  const int upto = blockIdx.x == gridDim.x - 1 ? nb : int(blockIdx.x);
+  uint64_t pre = 0;
+  for (int t = threadIdx.x; t < upto; t += kScanThreads) pre += block_sums[t];
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) pre += __shfl_xor(pre, d, 64);
+  if (__lane_id() == 0) s_part[threadIdx.x >> 6] = pre;
+  __syncthreads();
+  pre = 0;
+#pragma unroll
+  for (int w = 0; w < kScanThreads / 64; ++w) pre += s_part[w];
+  if (blockIdx.x == gridDim.x - 1) {
+    if (threadIdx.x == 0) {
+      *total64 = pre;
+      out[n] = uint32_t(pre);
+    }
+    pre -= block_sums[nb - 1];
+  }
   // thread t owns kScanItems consecutive values of the block's tile
   const int64_t base = int64_t(blockIdx.x) * kScanTile + int64_t(threadIdx.x) * kScanItems;
   uint32_t v[kScanItems];
@@ -109,7 +90,7 @@ __global__ void __launch_bounds__(kScanThreads) scan_apply_kernel(const uint32_t
     sum += v[k];
   }
   uint32_t total;
-  uint32_t run = block_exclusive_scan(sum, s_wave, &total) + uint32_t(block_prefix[blockIdx.x]);
+  uint32_t run = block_exclusive_scan(sum, s_wave, &total) + uint32_t(pre);
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
     if (base + k < n) out[base + k] = run;
@@ -142,12 +123,8 @@ hipError_t launch_scan_u32(const uint32_t* in, uint32_t* out, int64_t n, uint64_
     scan_reduce_kernel<<<nb, kScanThreads, 0, s>>>(in, n, sums);
   }
   {
-    GSK_PROF("scan_blocks", s);
-    scan_blocks_kernel<<<1, 1024, 0, s>>>(sums, nb, total64, out + n);
-  }
-  {
     GSK_PROF("scan_apply", s);
-    scan_apply_kernel<<<nb, kScanThreads, 0, s>>>(in, n, sums, out);
+    scan_apply_kernel<<<nb, kScanThreads, 0, s>>>(in, n, sums, nb, out, total64);
   }
   return hipGetLastError();
 }
