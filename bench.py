@@ -302,6 +302,7 @@ def main():
         "evals_per_s": round((ev_f + ev_b) / t_fb, 1),
         "evals_per_step": {"fwd": ev_f // args.steps, "bwd": ev_b // args.steps},
         "stage_ms": {k: round(float(stage[:, i].mean()), 4) for i, k in enumerate(StageTimer.NAMES)},
+        "stage_ms_median": {k: round(float(np.median(stage[:, i])), 4) for i, k in enumerate(StageTimer.NAMES)},
         "kernel_ms_per_step": {k: round(v, 4) for k, v in sorted(kernel_ms.items(), key=lambda kv: -kv[1])},
         "blend_valu": {"bound": "alu", "peak": VALU_PEAK, "unit": "wave instr/s", "kernels": measured_valu()},
         "roofline": roof,
