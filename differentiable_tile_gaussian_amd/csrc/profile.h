@@ -26,13 +26,13 @@ struct ProfScope {
   ProfScope(const char* n, hipStream_t s) : name(n), stream(s) {
     if (profile_on() && profile_wants(name)) {
       a = profile_event();
-      hipEventRecord(a, stream);
+      (void)hipEventRecord(a, stream);   // a failed record leaves the launch untimed
     }
   }
   ~ProfScope() {
     if (a) {
       hipEvent_t b = profile_event();
-      hipEventRecord(b, stream);
+      (void)hipEventRecord(b, stream);
       profile_record(name, a, b);
     }
   }

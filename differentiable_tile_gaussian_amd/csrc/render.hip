@@ -890,6 +890,13 @@ __global__ void zero_f32_kernel(float* __restrict__ p, int64_t count) {
   if (i < count) p[i] = 0.0f;
 }
 
+// 16-byte non-temporal stores over count4 groups of four floats (a pure write stream).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__global__ void zero_f32x4_kernel(f32x4* __restrict__ p, int64_t count4) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < count4) __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, p + i);
+}
+
 int g_first = 2048;
 int g_chunk = 512;
 
@@ -964,7 +971,13 @@ hipError_t launch_render_bwd(const gs_proj& proj, int n, const uint32_t* vals, c
   const float4* splat = reinterpret_cast<const float4*>(proj.splat);
   if (n > 0) {
     GSK_PROF("zero_f32", s);
-    zero_f32_kernel<<<div_up(9 * int64_t(n), 256), 256, 0, s>>>(gscreen, 9 * int64_t(n));
+    const int64_t count = 9 * int64_t(n);
+    if (reinterpret_cast<uintptr_t>(gscreen) % 16 == 0) {
+      zero_f32x4_kernel<<<div_up(count / 4, 256), 256, 0, s>>>(reinterpret_cast<f32x4*>(gscreen), count / 4);
+      if (count % 4) zero_f32_kernel<<<1, 4, 0, s>>>(gscreen + (count / 4) * 4, count % 4);
+    } else {
+      zero_f32_kernel<<<div_up(count, 256), 256, 0, s>>>(gscreen, count);
+    }
   }
   const BwdArgs A{splat, vals, ranges, num_tiles, tx, cam.width, cam.height, cam.bg[0], cam.bg[1], cam.bg[2],
                   g_first, g_chunk, T_final, n_contrib, dL_dimg, n, gscreen};
