@@ -125,9 +125,11 @@ __global__ void __launch_bounds__(256) preprocess_fwd_kernel(const float* __rest
                                                               gs_camera cam, int tx, int ty, float4* __restrict__ splat,
                                                               float* __restrict__ depth, uint2* __restrict__ rect,
                                                               uint32_t* __restrict__ tiles,
-                                                              uint32_t* __restrict__ block_tiles) {
+                                                              uint32_t* __restrict__ block_tiles,
+                                                              uint64_t* __restrict__ total) {
   __shared__ uint32_t s_wave[4];
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) *total = 0u;   // sum_counts_kernel adds into it after this kernel
   const uint32_t cnt = i < n ? project_one<DEG>(params, i, cam, tx, ty, splat, depth, rect, tiles) : 0u;
   // the block's total of tile counts (the pair count is the sum over blocks)
   uint32_t v = cnt;
@@ -138,12 +140,13 @@ __global__ void __launch_bounds__(256) preprocess_fwd_kernel(const float* __rest
   if (threadIdx.x == 0) block_tiles[blockIdx.x] = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
 }
 
-// Sum of the per-block tile counts (one block).
+// Sum of the per-block tile counts: each block adds up 1024 of them and adds its sum
+// to *total (zeroed by the projection kernel).
 __global__ void __launch_bounds__(1024) sum_counts_kernel(const uint32_t* __restrict__ block_tiles, int nb,
                                                            uint64_t* __restrict__ total) {
   __shared__ uint64_t s_wave[16];
-  uint64_t v = 0;
-  for (int k = threadIdx.x; k < nb; k += 1024) v += block_tiles[k];
+  const int k = blockIdx.x * 1024 + threadIdx.x;
+  uint64_t v = k < nb ? block_tiles[k] : 0u;
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
   if (__lane_id() == 0) s_wave[threadIdx.x >> 6] = v;
@@ -151,7 +154,7 @@ __global__ void __launch_bounds__(1024) sum_counts_kernel(const uint32_t* __rest
   if (threadIdx.x == 0) {
     uint64_t t = 0;
     for (int w = 0; w < 16; ++w) t += s_wave[w];
-    *total = t;
+    atomicAdd(reinterpret_cast<unsigned long long*>(total), static_cast<unsigned long long>(t));
   }
 }
 
@@ -167,14 +170,14 @@ hipError_t launch_preprocess_fwd(const float* params, int n, int deg, const gs_c
   {
     GSK_PROF("preprocess_fwd", s);
     switch (deg) {
-      case 0: preprocess_fwd_kernel<0><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles); break;
-      case 1: preprocess_fwd_kernel<1><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles); break;
-      case 2: preprocess_fwd_kernel<2><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles); break;
-      default: preprocess_fwd_kernel<3><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles); break;
+      case 0: preprocess_fwd_kernel<0><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles, total_pairs); break;
+      case 1: preprocess_fwd_kernel<1><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles, total_pairs); break;
+      case 2: preprocess_fwd_kernel<2><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles, total_pairs); break;
+      default: preprocess_fwd_kernel<3><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles, total_pairs); break;
     }
   }
   GSK_PROF("sum_counts", s);
-  sum_counts_kernel<<<1, 1024, 0, s>>>(block_tiles, int(grid.x), total_pairs);
+  sum_counts_kernel<<<div_up(grid.x, 1024), 1024, 0, s>>>(block_tiles, int(grid.x), total_pairs);
   return hipGetLastError();
 }
 

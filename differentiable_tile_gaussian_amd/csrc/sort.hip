@@ -235,14 +235,35 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t count, uint32_
   if (i < count) p[i] = value;
 }
 
+// Four consecutive pairs per thread (one 16-byte load when the keys are 16-byte
+// aligned); a pair whose tile differs from its left neighbour starts that tile's
+// range, one whose tile differs from its right neighbour ends it.
 __global__ void __launch_bounds__(256) tile_ranges_kernel(const uint32_t* __restrict__ tile_of_pair, uint32_t pairs,
-                                                           int num_tiles, uint32_t* __restrict__ ranges) {
-  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= pairs) return;
-  const uint32_t t = tile_of_pair[i];
-  if (t >= uint32_t(num_tiles)) return;   // only if total_pairs disagrees with the tile counts
-  if (i == 0 || tile_of_pair[i - 1] != t) ranges[t] = i;
-  if (i == pairs - 1 || tile_of_pair[i + 1] != t) ranges[num_tiles + t] = i + 1;
+                                                           int num_tiles, uint32_t* __restrict__ ranges,
+                                                           bool aligned) {
+  const uint32_t i0 = 4u * (blockIdx.x * blockDim.x + threadIdx.x);
+  if (i0 >= pairs) return;
+  uint32_t t[4];
+  if (aligned && i0 + 3 < pairs) {
+    const uint4 q = reinterpret_cast<const uint4*>(tile_of_pair)[i0 / 4];
+    t[0] = q.x; t[1] = q.y; t[2] = q.z; t[3] = q.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t[k] = i0 + k < pairs ? tile_of_pair[i0 + k] : 0u;
+  }
+  const uint32_t left = i0 > 0 ? tile_of_pair[i0 - 1] : 0u;
+  const uint32_t right = i0 + 4 < pairs ? tile_of_pair[i0 + 4] : 0u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t i = i0 + k;
+    if (i >= pairs) break;
+    const uint32_t tk = t[k];
+    if (tk >= uint32_t(num_tiles)) continue;   // only if total_pairs disagrees with the tile counts
+    const uint32_t l = k == 0 ? left : t[k - 1];
+    const uint32_t r = k == 3 ? right : t[k + 1];
+    if (i == 0 || l != tk) ranges[tk] = i;
+    if (i == pairs - 1 || r != tk) ranges[num_tiles + tk] = i + 1;
+  }
 }
 
 inline int bits_for(uint32_t max_value) {
@@ -416,7 +437,8 @@ hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uin
   }
   {
     GSK_PROF("tile_ranges", s);
-    tile_ranges_kernel<<<div_up(pairs, 256), 256, 0, s>>>(keys, pairs, num_tiles, ranges);
+    tile_ranges_kernel<<<div_up(div_up(pairs, 4), 256), 256, 0, s>>>(
+        keys, pairs, num_tiles, ranges, reinterpret_cast<uintptr_t>(keys) % 16 == 0);
   }
   return hipGetLastError();
 }
