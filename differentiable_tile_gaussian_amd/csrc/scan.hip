@@ -59,7 +59,7 @@ __global__ void __launch_bounds__(kScanThreads) scan_reduce_kernel(const uint32_
 __global__ void __launch_bounds__(kScanThreads) scan_apply_kernel(const uint32_t* __restrict__ in, int64_t n,
                                                                   const uint64_t* __restrict__ block_sums, int nb,
                                                                   uint32_t* __restrict__ out,
-                                                                  uint64_t* __restrict__ total64) {
+                                                                  uint64_t* __restrict__ total64, bool vec) {
   __shared__ uint32_t s_wave[kScanThreads / 64];
   __shared__ uint64_t s_part[kScanThreads / 64];
   // the sums of the tiles before this one (the last block also adds its own: the total)
@@ -82,19 +82,34 @@ __global__ void __launch_bounds__(kScanThreads) scan_apply_kernel(const uint32_t
   }
   // thread t owns kScanItems consecutive values of the block's tile
   const int64_t base = int64_t(blockIdx.x) * kScanTile + int64_t(threadIdx.x) * kScanItems;
+  // (16-byte loads and stores where the arrays allow them and the values are all there)
+  const bool full = vec && base + kScanItems <= n;
   uint32_t v[kScanItems];
   uint32_t sum = 0;
+  if (full) {
+    const uint4 q0 = reinterpret_cast<const uint4*>(in + base)[0], q1 = reinterpret_cast<const uint4*>(in + base)[1];
+    v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w; v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
+  } else {
 #pragma unroll
-  for (int k = 0; k < kScanItems; ++k) {
-    v[k] = (base + k < n) ? in[base + k] : 0u;
-    sum += v[k];
+    for (int k = 0; k < kScanItems; ++k) v[k] = (base + k < n) ? in[base + k] : 0u;
   }
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) sum += v[k];
   uint32_t total;
   uint32_t run = block_exclusive_scan(sum, s_wave, &total) + uint32_t(pre);
+  uint32_t o[kScanItems];
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
-    if (base + k < n) out[base + k] = run;
+    o[k] = run;
     run += v[k];
+  }
+  if (full) {
+    reinterpret_cast<uint4*>(out + base)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<uint4*>(out + base)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k)
+      if (base + k < n) out[base + k] = o[k];
   }
 }
 
@@ -124,7 +139,8 @@ hipError_t launch_scan_u32(const uint32_t* in, uint32_t* out, int64_t n, uint64_
   }
   {
     GSK_PROF("scan_apply", s);
-    scan_apply_kernel<<<nb, kScanThreads, 0, s>>>(in, n, sums, nb, out, total64);
+    const bool vec = reinterpret_cast<uintptr_t>(in) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0;
+    scan_apply_kernel<<<nb, kScanThreads, 0, s>>>(in, n, sums, nb, out, total64, vec);
   }
   return hipGetLastError();
 }

@@ -235,6 +235,20 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t count, uint32_
   if (i < count) p[i] = value;
 }
 
+// Zero fill with 16-byte stores; p 16-byte aligned.
+__global__ void zero_u32x4_kernel(uint4* __restrict__ p, int64_t count4) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < count4) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+void zero_u32(uint32_t* p, int64_t count, hipStream_t s) {
+  if (count <= 0) return;
+  GSK_PROF("fill_u32", s);
+  const int64_t c4 = reinterpret_cast<uintptr_t>(p) % 16 == 0 ? count / 4 : 0;
+  if (c4 > 0) zero_u32x4_kernel<<<div_up(c4, 256), 256, 0, s>>>(reinterpret_cast<uint4*>(p), c4);
+  if (count > 4 * c4) fill_u32_kernel<<<div_up(count - 4 * c4, 256), 256, 0, s>>>(p + 4 * c4, count - 4 * c4, 0u);
+}
+
 // Four consecutive pairs per thread (one 16-byte load when the keys are 16-byte
 // aligned); a pair whose tile differs from its left neighbour starts that tile's
 // range, one whose tile differs from its right neighbour ends it.
@@ -370,10 +384,7 @@ hipError_t launch_depth_order(const gs_proj& proj, int n, void* ws, hipStream_t 
   carve_depth(ws, n, &w);
   hipError_t e;
   const int nb = blocks_for(n);
-  {
-    GSK_PROF("fill_u32", s);
-    fill_u32_kernel<<<div_up(n, 256), 256, 0, s>>>(w.counts, n, 0u);
-  }
+  zero_u32(w.counts, n, s);
   // pass 0 compacts the visible Gaussians into (dk[0], dv); later passes alternate
   // with (dk[1], order), so the fourth lands in proj.order
   {
