@@ -17,9 +17,10 @@
 // Radix passes use 8-bit digits, reduce-then-scan:
 //   upsweep   per-block digit histogram (LDS atomics)
 //   scan      exclusive prefix over the digit-major [256][blocks] table
-//   downsweep stable in-block ranking with 64-lane ballots (no match-any on CDNA:
-//             8 ballots give each lane its peer mask), local reorder through LDS,
-//             coalesced scatter.
+//   downsweep each wave ranks its 1024 consecutive items against a wave-private digit
+//             histogram (64-lane ballots: no match-any on CDNA, 8 ballots give each
+//             lane its peer mask), one barrier turns the four histograms into run
+//             starts, then a local reorder through LDS and a coalesced scatter.
 // Sorting the Gaussians by depth once, instead of every pair by a 64-bit (tile, depth)
 // key, replaces six passes over 12-byte pairs by four passes over the visible
 // Gaussians (about 40 % of them at the orbit cameras) and two over 8-byte pairs.
@@ -99,8 +100,7 @@ __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
     const uint32_t* __restrict__ val_tiles, uint32_t* __restrict__ tiles_out) {
   __shared__ uint32_t s_keys[kSortTile];
   __shared__ uint32_t s_vals[kSortTile];
-  __shared__ uint32_t s_wave_cnt[kSortThreads / 64][kRadix];
-  __shared__ uint32_t s_run[kRadix];      // items of each digit already placed in this block
+  __shared__ uint32_t s_whist[kSortThreads / 64][kRadix];   // per-wave digit counts, then starts
   __shared__ uint32_t s_local[kRadix];    // block-local start of each digit
   __shared__ uint32_t s_global[kRadix];   // global start of (digit, this block)
   __shared__ uint32_t s_wtot[kSortThreads / 64];
@@ -130,16 +130,24 @@ __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
       block_total += s_wtot[w];
     }
     s_local[tid] = pre + v - cnt;
-    s_run[tid] = 0u;
-    for (int w = 0; w < kSortThreads / 64; ++w) s_wave_cnt[w][tid] = 0u;
+    for (int w = 0; w < kSortThreads / 64; ++w) s_whist[w][tid] = 0u;
   }
   __syncthreads();
+  // Each wave ranks its own 1024 consecutive items, 64 per round, with a wave-private
+  // digit histogram: an item's rank among equal digits of its wave is the histogram
+  // before its round plus its rank in the round (8 ballots give each lane its peers;
+  // CDNA has no match-any).  Waves, rounds and lanes follow the items' order, so the
+  // placement is stable.
+  constexpr int kWaveItems = kSortTile / (kSortThreads / 64);
+  constexpr int kRounds = kWaveItems / 64;
   const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
-  for (int r = 0; r < kSortItems; ++r) {
-    uint32_t key = 0, val = 0;
-    const bool valid = load_item<SRC>(in, count, base + r * kSortThreads + tid, key, val);
-    const uint32_t d = valid ? (key >> shift) & 0xffu : 0u;
-    // lanes of this wave holding the same digit
+  uint32_t key[kRounds], val[kRounds], rk[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    key[r] = 0u;
+    val[r] = 0u;
+    const bool valid = load_item<SRC>(in, count, base + wave * kWaveItems + r * 64 + lane, key[r], val[r]);
+    const uint32_t d = (key[r] >> shift) & 0xffu;
     uint64_t peers = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -147,26 +155,34 @@ __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
       const uint64_t m = __ballot(bit);
       peers &= bit ? m : ~m;
     }
+    const uint32_t before = valid ? s_whist[wave][d] : 0u;
     const uint32_t rank = __popcll(peers & lt_mask);
-    if (valid && rank == 0) s_wave_cnt[wave][d] = uint32_t(__popcll(peers));
-    __syncthreads();
-    if (valid) {
-      uint32_t pos = s_local[d] + s_run[d] + rank;
-      for (int w = 0; w < wave; ++w) pos += s_wave_cnt[w][d];
-      s_keys[pos] = key;
-      s_vals[pos] = val;
-    }
-    __syncthreads();
-    {
-      uint32_t add = 0;
-      for (int w = 0; w < kSortThreads / 64; ++w) {
-        add += s_wave_cnt[w][tid];
-        s_wave_cnt[w][tid] = 0u;
-      }
-      s_run[tid] += add;
-    }
-    __syncthreads();
+    // the read above is issued before this write, and one wave's LDS operations are
+    // performed in order
+    if (valid && rank == 0) s_whist[wave][d] = before + uint32_t(__popcll(peers));
+    rk[r] = valid ? before + rank : 0xffffffffu;
   }
+  __syncthreads();
+  // per digit, the start of each wave's run: block-local start plus the earlier waves
+  {
+    uint32_t acc = s_local[tid];
+#pragma unroll
+    for (int w = 0; w < kSortThreads / 64; ++w) {
+      const uint32_t t = s_whist[w][tid];
+      s_whist[w][tid] = acc;
+      acc += t;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    if (rk[r] != 0xffffffffu) {
+      const uint32_t pos = s_whist[wave][(key[r] >> shift) & 0xffu] + rk[r];
+      s_keys[pos] = key[r];
+      s_vals[pos] = val[r];
+    }
+  }
+  __syncthreads();
   for (uint32_t k = tid; k < block_total; k += kSortThreads) {
     const uint32_t key = s_keys[k];
     const uint32_t d = (key >> shift) & 0xffu;
