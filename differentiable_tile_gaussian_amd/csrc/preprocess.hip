@@ -26,26 +26,28 @@ using namespace proj;
 // blend tests o exp(-e) >= 1/255 with e from the fp32 conic (A, B, C), so the box
 // bounds the ellipse e <= ln(255 o) of that conic: |dx| <= sqrt(2 t C / (A C - B^2)),
 // |dy| <= sqrt(2 t A / (A C - B^2)), evaluated in fp64 from the fp32 conic and widened
-// to cover the blend's fp32 evaluation of e: t by 1 % + 0.01, the half-widths by
-// 1 % + 0.05 px.  With A C / (A C - B^2) <= 1000 the rounding error of e stays below
+// to cover the blend's fp32 evaluation of e: t by 1 % + 0.01 (the widened value is
+// returned in tm, for the blend's finer per-quadrant test of e itself), the half-widths
+// by 1 % + 0.05 px.  With A C / (A C - B^2) <= 1000 the rounding error of e stays below
 // 0.2 % of e (about 0.01 at the box), inside the margin; more elongated conics get an
 // unbounded box.  Negative when o < e^-0.001 / 255 (no pixel can reach 1/255);
-// infinite when the fp32 conic is not positive definite.
-__device__ inline void blend_box(const Proj& g, float& hx, float& hy) {
+// infinite (box and tm) when the fp32 conic is not positive definite.
+__device__ inline void blend_box(const Proj& g, float& hx, float& hy, float& tm_out) {
   const double t = log(double(g.o) * 255.0);
   if (!(t > -1e-3)) {
-    hx = hy = -1.0f;
+    hx = hy = tm_out = -1.0f;
     return;
   }
   const double A = g.A, B = g.B, C = g.C;
   const double det = A * C - B * B;
   if (!(det > 0.0) || !(A > 0.0) || !(C > 0.0) || !(A * C <= 1000.0 * det)) {
-    hx = hy = __builtin_inff();
+    hx = hy = tm_out = __builtin_inff();
     return;
   }
   const double tm = t + 0.01 + 0.01 * fabs(t);
   hx = float(sqrt(2.0 * tm * C / det) * 1.01 + 0.05);
   hy = float(sqrt(2.0 * tm * A / det) * 1.01 + 0.05);
+  tm_out = float(tm);
 }
 
 // One Gaussian: writes its projected record and returns its tile count.
@@ -102,9 +104,9 @@ __device__ inline uint32_t project_one(const float* __restrict__ params, int i, 
   if (vis) {
     splat[3 * i + 0] = make_float4(g.u, g.v, g.A, g.B);
     splat[3 * i + 1] = make_float4(g.C, g.o, rgb[0], rgb[1]);
-    float hx, hy;
-    blend_box(g, hx, hy);
-    splat[3 * i + 2] = make_float4(rgb[2], hx, hy, 0.f);
+    float hx, hy, tm;
+    blend_box(g, hx, hy, tm);
+    splat[3 * i + 2] = make_float4(rgb[2], hx, hy, tm);
     depth[i] = g.p[2];
     rect[i] = make_uint2(x0 | (y0 << 16), x1 | (y1 << 16));
     tiles[i] = cnt;

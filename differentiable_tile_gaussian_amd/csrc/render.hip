@@ -196,6 +196,53 @@ __device__ inline uint32_t quad_mask(float u, float v, float bx, float by, float
   return uint32_t(xl && yt) | (uint32_t(xr && yt) << 1) | (uint32_t(xl && yb) << 2) | (uint32_t(xr && yb) << 3);
 }
 
+// Narrows a quadrant mask with the ellipse itself: clears the bit of each quadrant whose
+// rectangle of pixel centres holds no point with e = A X^2 / 2 + B X Y + C Y^2 / 2 <= tm
+// (X, Y relative to (u, v)), tm being ln(255 o) widened for the blend's fp32 evaluation of
+// e, here widened again by 1 % + 0.01 for this evaluation.  The minimum of e over a
+// rectangle without the centre lies on its boundary, on each edge at the edge's own
+// minimiser (Y = -B X / C on a vertical edge, X = -B Y / A on a horizontal one) clamped
+// to the edge; the rectangle covers the quadrant's pixel centres, so the test only errs
+// towards keeping a bit.  tm is infinite for an unbounded box and the mask is left as is.
+__device__ inline uint32_t ellipse_mask(uint32_t m, float u, float v, float A, float B, float C, float tm,
+                                        float ox, float oy) {
+  if (m == 0u || !(tm <= 3.0e38f)) return m;
+  const float thr = fmaf(tm, 1.01f, 0.01f);
+  const float ha = 0.5f * A, hc = 0.5f * C;
+  const float sy = -B * __builtin_amdgcn_rcpf(C), sx = -B * __builtin_amdgcn_rcpf(A);
+  // pixel-centre lines 0.5, 7.5, 8.5, 15.5 from the tile corner, relative to the centre
+  const float xs[4] = {(ox + 0.5f) - u, (ox + 7.5f) - u, (ox + 8.5f) - u, (ox + 15.5f) - u};
+  const float ys[4] = {(oy + 0.5f) - v, (oy + 7.5f) - v, (oy + 8.5f) - v, (oy + 15.5f) - v};
+  float emin[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) emin[q] = __builtin_inff();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int h = k >> 1;   // the half (quadrant column or row) the line bounds
+    // vertical edge X = xs[k] of quadrants (h, 0) and (h, 1)
+    const float X = xs[k], Y = ys[k];
+    const float lx = X * ha, ly = Y * hc;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const float y = __builtin_amdgcn_fmed3f(sy * X, ys[2 * r], ys[2 * r + 1]);
+      const float ev = X * fmaf(B, y, lx) + hc * y * y;
+      emin[2 * r + h] = fminf(emin[2 * r + h], ev);
+      // horizontal edge Y = ys[k] of quadrants (0, h) and (1, h)
+      const float x = __builtin_amdgcn_fmed3f(sx * Y, xs[2 * r], xs[2 * r + 1]);
+      const float eh = Y * fmaf(B, x, ly) + ha * x * x;
+      emin[2 * h + r] = fminf(emin[2 * h + r], eh);
+    }
+  }
+  uint32_t out = 0u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int qx = q & 1, qy = q >> 1;
+    const bool inside = xs[2 * qx] <= 0.0f && xs[2 * qx + 1] >= 0.0f && ys[2 * qy] <= 0.0f && ys[2 * qy + 1] >= 0.0f;
+    out |= uint32_t(inside || emin[q] <= thr) << q;
+  }
+  return m & out;
+}
+
 // Index of a zero-opacity record after each batch (alpha 0: blending it changes nothing).
 constexpr int kPad = kBatch;
 constexpr int kListLen = kBatch + 4;
@@ -237,7 +284,7 @@ __device__ inline void stage_fwd(const float4* __restrict__ splat, uint32_t g, f
   c = r2.x;
   a = make_float4(r0.x, r0.y, -0.5f * kLog2e * r0.z, -kLog2e * r0.w);
   b = make_float4(-0.5f * kLog2e * r1.x, r1.y, r1.z, r1.w);
-  m = quad_mask(r0.x, r0.y, r2.y, r2.z, ox, oy);
+  m = ellipse_mask(quad_mask(r0.x, r0.y, r2.y, r2.z, ox, oy), r0.x, r0.y, r0.z, r0.w, r1.x, r2.w, ox, oy);
 }
 
 struct PixelFwd {
@@ -641,7 +688,7 @@ __device__ inline void stage_bwd(const float4* __restrict__ splat, uint32_t g, f
   a = make_float4(r0.x, r0.y, -0.5f * kLog2e * r0.z, -kLog2e * r0.w);
   b = make_float4(-0.5f * kLog2e * r1.x, r1.y, r1.z, r1.w);
   c = r2.x;
-  m = quad_mask(r0.x, r0.y, r2.y, r2.z, ox, oy);
+  m = ellipse_mask(quad_mask(r0.x, r0.y, r2.y, r2.z, ox, oy), r0.x, r0.y, r0.z, r0.w, r1.x, r2.w, ox, oy);
 }
 
 struct PixelBwd {

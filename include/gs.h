@@ -89,11 +89,13 @@ typedef struct gs_scene {
 /* Projected per-Gaussian state written by gs_preprocess and read by the later calls.
  * Device arrays allocated by the caller. */
 typedef struct gs_proj {
-  float* splat;         /* [n][12] packed record: u, v, A, B, C, opacity, r, g, b, hx, hy, 0
-                           (screen centre, conic, opacity, clamped colour, and the half-widths
+  float* splat;         /* [n][12] packed record: u, v, A, B, C, opacity, r, g, b, hx, hy, tm
+                           (screen centre, conic, opacity, clamped colour, the half-widths
                            of a box around (u, v) outside which no pixel centre gets
-                           alpha >= 1/255: negative if none can, infinite if unbounded);
-                           zero when culled */
+                           alpha >= 1/255: negative if none can, infinite if unbounded, and
+                           tm, ln(255 opacity) widened by 1 % + 0.01: the bound on the
+                           exponent within which a pixel can reach 1/255, negative or
+                           infinite with the box); zero when culled */
   float* depth;         /* [n] camera-space z (the sort key's low 32 bits) */
   uint32_t* rect;       /* [n][2] tile rectangle, inclusive: x0 | y0 << 16, x1 | y1 << 16 */
   uint32_t* tiles;      /* [n] tiles touched, 0 when culled */

@@ -38,7 +38,7 @@ def proj_to_numpy(pl):
     splat = pl.proj.splat[:n].cpu().numpy()
     rect = pl.proj.rect[:n].cpu().numpy().view(np.uint32)
     out = dict(uv=splat[:, 0:2].T.copy(), conic=splat[:, 2:5].T.copy(), opac=splat[:, 5].copy(),
-               rgb=splat[:, 6:9].T.copy(), box=splat[:, 9:11].T.copy(), depth=pl.proj.depth[:n].cpu().numpy(),
+               rgb=splat[:, 6:9].T.copy(), box=splat[:, 9:11].T.copy(), cull_t=splat[:, 11].copy(), depth=pl.proj.depth[:n].cpu().numpy(),
                tiles=pl.proj.tiles[:n].cpu().numpy().view(np.uint32),
                offs=pl.proj.offs.cpu().numpy().view(np.uint32),
                order=pl.proj.order[:n].cpu().numpy().view(np.uint32),
@@ -89,7 +89,8 @@ def check_preprocess(gpu, ora):
 def check_blend_box(gpu, vis):
     """The box (u +- hx, v +- hy) must contain every point where o exp(-e) >= 1/255 for
     e = (A dx^2 + C dy^2) / 2 + B dx dy with the record's own conic: the ellipse's
-    half-widths sqrt(2 t C / (A C - B^2)), sqrt(2 t A / (A C - B^2)), t = ln(255 o)."""
+    half-widths sqrt(2 t C / (A C - B^2)), sqrt(2 t A / (A C - B^2)), t = ln(255 o);
+    the record's exponent bound tm may not be below t."""
     A, B, C = (gpu["conic"][k][vis].astype(np.float64) for k in range(3))
     o = gpu["opac"][vis].astype(np.float64)
     hx, hy = gpu["box"][0][vis], gpu["box"][1][vis]
@@ -102,6 +103,11 @@ def check_blend_box(gpu, vis):
     need_y = np.sqrt(2 * np.maximum(t[ok], 0) * A[ok] / det[ok])
     assert np.all(hx[ok] >= need_x) and np.all(hy[ok] >= need_y)
     assert np.all(np.isinf(hx[~none & ~(det > 0)]))
+    # the exponent bound the blend's per-quadrant ellipse test uses: at least t where
+    # the box is finite, infinite with it
+    tm = gpu["cull_t"][vis]
+    fin = np.isfinite(hx)
+    assert np.all(tm[~none & fin] >= t[~none & fin]) and np.all(np.isinf(tm[~none & ~fin]))
 
 
 def flipped_pixels(risk):
