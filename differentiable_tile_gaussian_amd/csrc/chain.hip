@@ -12,7 +12,7 @@
 //              position gradient comes from"; [GST] Jacobian slide).
 // Wave 3 loads the geometry planes and hands the means and tile counts to the colour
 // waves through LDS; every parameter, moment and screen-gradient byte crosses HBM once.
-// gscreen planes: 0 u, 1 v, 2 A, 3 B, 4 C, 5 opacity, 6-8 colour (read only).
+// gscreen: [n][9] per Gaussian: 0 u, 1 v, 2 A, 3 B, 4 C, 5 opacity, 6-8 colour (read only).
 //
 // Compiled without floating-point contraction, like the forward projection, so the
 // recomputed projection is the forward's bit for bit.
@@ -59,7 +59,7 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
 #pragma unroll
       for (int k = 0; k < 11; ++k) th[k] = __builtin_nontemporal_load(params + gb + k * kGB);
 #pragma unroll
-      for (int k = 0; k < 6; ++k) gs6[k] = gscreen[size_t(k) * n + i];
+      for (int k = 0; k < 6; ++k) gs6[k] = gscreen[size_t(i) * 9 + k];
       if (ADAM) {
 #pragma unroll
         for (int k = 0; k < 11; ++k) {
@@ -74,7 +74,7 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
   } else if (valid) {
 #pragma unroll
     for (int k = 0; k <= K; ++k) coef[k] = __builtin_nontemporal_load(params + gb + colour_plane(k, ch) * kGB);
-    gcol = gscreen[(6 + ch) * n + i];
+    gcol = gscreen[size_t(i) * 9 + 6 + ch];
     if (ADAM) {
 #pragma unroll
       for (int k = 0; k <= K; ++k) {

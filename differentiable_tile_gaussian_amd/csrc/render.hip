@@ -71,6 +71,7 @@ __device__ inline float tile_ox(int tile, int tx) { return float((tile % tx) * k
 __device__ inline float tile_oy(int tile, int tx) { return float((tile / tx) * kTile); }
 
 constexpr int kBatch = 256;
+constexpr int kBlock = 256;   // threads of a tile block: one per pixel
 constexpr float kAlphaMin = 1.0f / 255.0f;
 constexpr float kAlphaCap = 0.99f;
 constexpr float kTStop = 1e-4f;
@@ -677,7 +678,7 @@ struct BwdLds {
   float c[2][kBwdBatch];      // b
   uint32_t id[2][kBwdBatch];
   uint32_t m[2][kBwdBatch];   // quadrant masks
-  float acc[9][kBwdBatch];    // per-entry sums over the block's waves
+  float acc[kBwdBatch][9];    // per-entry sums over the block's waves (entry-major, as gscreen)
   uint16_t list[4][kBwdBatch + 4];
   uint32_t top;
 };
@@ -700,14 +701,14 @@ struct PixelBwd {
 // Walks pairs top-1 .. lo (top per pixel, at most hi) of a tile list, adding
 // each pair's partials to gscreen.  Must be called by all 256 threads.
 __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint32_t* __restrict__ vals,
-                         uint32_t start, int lo, float ox, float oy, float fx, float fy, PixelBwd& s, int n,
+                         uint32_t start, int lo, float ox, float oy, float fx, float fy, PixelBwd& s,
                          float* __restrict__ gscreen) {
   const int tid = threadIdx.x;
   const int lane = __lane_id();
   if (tid == 0) L.top = 0u;
   if (tid < kBwdBatch) {
 #pragma unroll
-    for (int k = 0; k < 9; ++k) L.acc[k][tid] = 0.0f;
+    for (int k = 0; k < 9; ++k) L.acc[tid][k] = 0.0f;
   }
   __syncthreads();
   if (s.top > lo) atomicMax(&L.top, uint32_t(s.top));
@@ -784,8 +785,8 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
       s.S2 += cb * w;
       s.T = Tn;
       wave_sum9(v);
-      if ((lane & 7) == 0) atomicAdd(&L.acc[lane >> 3][e], v[0]);
-      if (lane == 0) atomicAdd(&L.acc[8][e], v[8]);
+      if ((lane & 7) == 0) atomicAdd(&L.acc[e][lane >> 3], v[0]);
+      if (lane == 0) atomicAdd(&L.acc[e][8], v[8]);
     }
     if (tid < kBwdBatch && nlo < nhi) {
       L.a[buf ^ 1][tid] = na; L.b[buf ^ 1][tid] = nb; L.c[buf ^ 1][tid] = ncr; L.id[buf ^ 1][tid] = ng;
@@ -795,24 +796,27 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
     if (tid < hi - blo) {
       // e = (A dx^2 + C dy^2) / 2 + B dx dy: du = -(A M_x + B M_y), dv = -(B M_x + C M_y),
       // dA = M_xx / 2, dB = M_xy, dC = M_yy / 2 for the moments M of dL/de
-      const uint32_t g = L.id[buf][tid];
-      // the unscaled conic back from the staged coefficients (a' = -log2(e) A / 2, ...)
+      // (the unscaled conic back from the staged coefficients: a' = -log2(e) A / 2, ...)
       const float cA = L.a[buf][tid].z * (-2.0f / kLog2e), cB = L.a[buf][tid].w * (-1.0f / kLog2e),
                   cC = L.b[buf][tid].x * (-2.0f / kLog2e);
-      float val[9];
-#pragma unroll
-      for (int k = 0; k < 9; ++k) {
-        val[k] = L.acc[k][tid];
-        L.acc[k][tid] = 0.0f;
+      const float mx = L.acc[tid][0], my = L.acc[tid][1];
+      L.acc[tid][0] = -(cA * mx + cB * my);
+      L.acc[tid][1] = -(cB * mx + cC * my);
+      L.acc[tid][2] *= 0.5f;
+      L.acc[tid][4] *= 0.5f;
+    }
+    __syncthreads();
+    {
+      // one thread per (entry, partial) in gscreen's own order, so that the atomics of a
+      // wave land on a few cache lines (about 7 entries of 36 bytes) instead of 64
+      const float* flat = &L.acc[0][0];
+      const int cnt9 = (hi - blo) * 9;
+      for (int idx = tid; idx < cnt9; idx += kBlock) {
+        const int e = idx / 9;
+        const float x = flat[idx];
+        if (x != 0.0f) atomicAdd(&gscreen[size_t(L.id[buf][e]) * 9 + (idx - 9 * e)], x);
+        (&L.acc[0][0])[idx] = 0.0f;
       }
-      const float mx = val[0], my = val[1];
-      val[0] = -(cA * mx + cB * my);
-      val[1] = -(cB * mx + cC * my);
-      val[2] *= 0.5f;
-      val[4] *= 0.5f;
-#pragma unroll
-      for (int k = 0; k < 9; ++k)
-        if (val[k] != 0.0f) atomicAdd(&gscreen[k * n + g], val[k]);
     }
     __syncthreads();
     hi = blo;
@@ -868,8 +872,7 @@ __device__ void bwd_tile(BwdLds& L, const BwdArgs& A, const SplitWs& ws, int til
       s.top = int(n_contrib[p]);
     }
   }
-  bwd_walk(L, splat, vals, start, 0, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f, float(py) + 0.5f, s, n,
-           gscreen);
+  bwd_walk(L, splat, vals, start, 0, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f, float(py) + 0.5f, s, gscreen);
 }
 
 // One chunk of a split tile.
@@ -911,8 +914,7 @@ __device__ void bwd_chunk(BwdLds& L, const BwdArgs& A, const SplitWs& ws, uint32
       s.top = hi;
     }
   }
-  bwd_walk(L, splat, vals, start, lo, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f, float(py) + 0.5f, s, n,
-           gscreen);
+  bwd_walk(L, splat, vals, start, lo, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f, float(py) + 0.5f, s, gscreen);
 }
 
 // The backward of every tile's first segment and of every chunk of the split tiles,

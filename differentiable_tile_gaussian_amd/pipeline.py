@@ -39,7 +39,7 @@ class Pipeline:
         self.ws_render = torch.empty(0, dtype=torch.uint8, device=dev)
         self.loss = torch.zeros(3, dtype=torch.float32, device=dev)
         self.dLdI = torch.empty((3, height, width), dtype=torch.float32, device=dev)
-        self.gscreen = torch.empty((9, max(self.n, 1)), dtype=torch.float32, device=dev)
+        self.gscreen = torch.empty((max(self.n, 1), 9), dtype=torch.float32, device=dev)
         self.grads = gs.empty_blocked(self.n, sh_degree, dev, zero=True)
         self.m = gs.empty_blocked(self.n, sh_degree, dev, zero=True)
         self.v = gs.empty_blocked(self.n, sh_degree, dev, zero=True)

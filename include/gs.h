@@ -179,7 +179,8 @@ int32_t gs_loss_l1_dssim(const float* img, const float* target, int32_t H, int32
  * alpha_i), keeps S = colour behind (starting at bg T_final), and accumulates per Gaussian:
  *   dc += g alpha T;  dalpha = sum_ch g (c T - S / (1 - alpha));  when alpha is not capped:
  *   do += dalpha G, and through e: du, dv, dA, dB, dC.
- * gscreen: [9][n] = du, dv, dA, dB, dC, d opacity, dr, dg, db -- zeroed and filled here.
+ * gscreen: [n][9], per Gaussian du, dv, dA, dB, dC, d opacity, dr, dg, db (Gaussian-major,
+ * so that the partials of one pair share a cache line) -- zeroed and filled here.
  * Part 2, the chain per Gaussian: [GSG] "The covariance chain" (conic -> V -> Sigma -> M ->
  * scale and quaternion, projection off |q|), "Where the position gradient comes from"
  * (mean path and the J(z) covariance path), "Spherical harmonics" (band gradients and the

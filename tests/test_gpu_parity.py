@@ -86,7 +86,7 @@ def test_backward_small(torch_cuda, oracle, case):
     gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI, pl.gscreen,
                      pl.grads, pl.ws_render)
     torch.cuda.synchronize()
-    gscreen = pl.gscreen[:, :n].cpu().numpy()
+    gscreen = pl.gscreen[:n].T.cpu().numpy()
     gparams = pl.planar(pl.grads).cpu().numpy()
     pu.check_screen_grads(gscreen, o["gscreen"], o["risk"]["g"], o["slack"])
     keep = pu.calm(o["risk"]["g"], o["gscreen"])
@@ -117,7 +117,7 @@ def _full_step_checks(torch, gs, oracle, pl, c, ref, target, params, deg, cam):
     gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI, pl.gscreen,
                      pl.grads, pl.ws_render)
     torch.cuda.synchronize()
-    pu.check_screen_grads(pl.gscreen[:, :n].cpu().numpy(), ref["gscreen"], ref["risk"]["g"], ref["slack"])
+    pu.check_screen_grads(pl.gscreen[:n].T.cpu().numpy(), ref["gscreen"], ref["risk"]["g"], ref["slack"])
     keep = pu.calm(ref["risk"]["g"], ref["gscreen"])
     g = pl.planar(pl.grads).cpu().numpy()
     pu.check_param_grads(g, ref, oracle, params, deg, cam, keep)
@@ -353,7 +353,7 @@ def test_split_path_parity(torch_cuda, oracle, split_tuning, tune, which):
     gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI, pl.gscreen,
                      pl.grads, pl.ws_render)
     torch.cuda.synchronize()
-    pu.check_screen_grads(pl.gscreen[:, :s.n].cpu().numpy(), o["gscreen"], o["risk"]["g"], o["slack"])
+    pu.check_screen_grads(pl.gscreen[:s.n].T.cpu().numpy(), o["gscreen"], o["risk"]["g"], o["slack"])
     keep = pu.calm(o["risk"]["g"], o["gscreen"])
     g = pl.planar(pl.grads).cpu().numpy()
     pu.check_param_grads(g, o, oracle, s.params, deg, cam, keep)
