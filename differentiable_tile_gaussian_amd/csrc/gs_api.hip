@@ -50,8 +50,8 @@ int32_t check_scene(const gs_scene* sc) {
 
 int32_t check_proj(const gs_proj* p, int64_t n, bool need_order) {
   if (!p) return fail(GS_ERR_INVALID_ARG, "proj is null");
-  if (need_order && (!p->offs || !p->n_visible || (n > 0 && !p->order)))
-    return fail(GS_ERR_INVALID_ARG, "proj.offs, proj.order or proj.n_visible is null");
+  if (need_order && (!p->offs || !p->n_visible || (n > 0 && (!p->order || !p->rect_order))))
+    return fail(GS_ERR_INVALID_ARG, "proj.offs, proj.order, proj.rect_order or proj.n_visible is null");
   if (n > 0 && (!p->splat || !p->depth || !p->rect || !p->tiles))
     return fail(GS_ERR_INVALID_ARG, "a proj array is null");
   return GS_OK;

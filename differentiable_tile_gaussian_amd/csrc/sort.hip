@@ -57,9 +57,11 @@ template <int SRC>
 __device__ inline bool load_item(const PassIn& in, uint32_t count, uint32_t idx, uint32_t& key, uint32_t& val) {
   if (idx >= count) return false;
   if (SRC == kFromDepth) {
-    if (in.tiles[idx] == 0u) return false;
+    // both loads issued before either is tested
+    const uint32_t t = in.tiles[idx];
     key = __float_as_uint(in.depth[idx]);
     val = idx;
+    if (t == 0u) return false;
   } else {
     key = in.keys[idx];
     val = in.vals[idx];
@@ -91,13 +93,13 @@ __global__ void __launch_bounds__(kSortThreads) radix_upsweep_kernel(PassIn in, 
 
 // hist_scan has kRadix * nb + 1 entries, the last one the total: with kFromDepth
 // that is the number of visible Gaussians, which block 0 stores to *count_out.
-// With tiles_out, the item's value (a Gaussian id) is also looked up in val_tiles
-// and its tile count written beside it.
+// With rect_out, the item's value (a Gaussian id) is also looked up in val_rect and
+// its tile rectangle and tile count written beside it (in the output order).
 template <int SRC>
 __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
     PassIn in, int shift, int nb, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ hist_scan,
     uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint32_t* __restrict__ count_out,
-    const uint32_t* __restrict__ val_tiles, uint32_t* __restrict__ tiles_out) {
+    const uint2* __restrict__ val_rect, uint2* __restrict__ rect_out, uint32_t* __restrict__ counts_out) {
   __shared__ uint32_t s_keys[kSortTile];
   __shared__ uint32_t s_vals[kSortTile];
   __shared__ uint32_t s_whist[kSortThreads / 64][kRadix];   // per-wave digit counts, then starts
@@ -189,7 +191,11 @@ __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
     const uint32_t dst = s_global[d] + (k - s_local[d]);
     keys_out[dst] = key;
     vals_out[dst] = s_vals[k];
-    if (tiles_out) tiles_out[dst] = val_tiles[s_vals[k]];
+    if (rect_out) {
+      const uint2 r = val_rect[s_vals[k]];
+      rect_out[dst] = r;
+      counts_out[dst] = ((r.y & 0xffffu) - (r.x & 0xffffu) + 1u) * ((r.y >> 16) - (r.x >> 16) + 1u);
+    }
   }
 }
 
@@ -206,14 +212,15 @@ __global__ void __launch_bounds__(256) block_starts_kernel(const uint32_t* __res
 }
 
 // One thread per pair: the Gaussian (in depth order) that owns it, and its tile.
-// offs[r] is the first pair of the r-th visible Gaussian in depth order.  The
-// block's 256 pairs belong to at most 256 consecutive Gaussians starting with
-// block_first[block]; their offsets go to LDS and each thread searches there.
+// offs[r] is the first pair of the r-th visible Gaussian in depth order and
+// rect_order[r] its tile rectangle.  The block's 256 pairs belong to at most 256
+// consecutive Gaussians starting with block_first[block]; their offsets go to LDS
+// and each thread searches there.
 __global__ void __launch_bounds__(256) emit_pairs_kernel(const uint32_t* __restrict__ offs,
                                                           const uint32_t* __restrict__ n_vis,
                                                           const uint32_t* __restrict__ block_first,
                                                           const uint32_t* __restrict__ order,
-                                                          const uint2* __restrict__ rect, int n, uint32_t pairs,
+                                                          const uint2* __restrict__ rect_order, int n, uint32_t pairs,
                                                           int tx, uint32_t* __restrict__ keys,
                                                           uint32_t* __restrict__ vals) {
   __shared__ uint32_t s_offs[256];
@@ -239,7 +246,7 @@ __global__ void __launch_bounds__(256) emit_pairs_kernel(const uint32_t* __restr
     return;
   }
   const uint32_t j = p - s_offs[lo];
-  const uint2 r = rect[g];
+  const uint2 r = rect_order[r0 + lo];
   const uint32_t x0 = r.x & 0xffffu, y0 = r.x >> 16, x1 = r.y & 0xffffu;
   const uint32_t w = x1 - x0 + 1;
   keys[p] = (y0 + j / w) * uint32_t(tx) + (x0 + j % w);
@@ -371,8 +378,8 @@ size_t carve_pairs(void* ws, uint32_t pairs, PairWs* out) {
 
 template <int SRC>
 hipError_t radix_pass(const PassIn& in, int nb, int shift, const RadixWs& w, uint32_t* keys_out,
-                      uint32_t* vals_out, uint32_t* count_out, const uint32_t* val_tiles, uint32_t* tiles_out,
-                      hipStream_t s) {
+                      uint32_t* vals_out, uint32_t* count_out, const uint2* val_rect, uint2* rect_out,
+                      uint32_t* counts_out, hipStream_t s) {
   {
     GSK_PROF("radix_upsweep", s);
     radix_upsweep_kernel<SRC><<<nb, kSortThreads, 0, s>>>(in, shift, nb, w.hist);
@@ -381,7 +388,7 @@ hipError_t radix_pass(const PassIn& in, int nb, int shift, const RadixWs& w, uin
   if (e != hipSuccess) return e;
   GSK_PROF("radix_downsweep", s);
   radix_downsweep_kernel<SRC><<<nb, kSortThreads, 0, s>>>(in, shift, nb, w.hist, w.hist_scan, keys_out, vals_out,
-                                                          count_out, val_tiles, tiles_out);
+                                                          count_out, val_rect, rect_out, counts_out);
   return hipGetLastError();
 }
 
@@ -405,8 +412,8 @@ hipError_t launch_depth_order(const gs_proj& proj, int n, void* ws, hipStream_t 
   // with (dk[1], order), so the fourth lands in proj.order
   {
     PassIn in{nullptr, nullptr, proj.depth, proj.tiles, uint32_t(n), nullptr};
-    if ((e = radix_pass<kFromDepth>(in, nb, 0, w.r, w.dk[0], w.dv, proj.n_visible, nullptr, nullptr, s)) !=
-        hipSuccess)
+    if ((e = radix_pass<kFromDepth>(in, nb, 0, w.r, w.dk[0], w.dv, proj.n_visible, nullptr, nullptr, nullptr,
+                                    s)) != hipSuccess)
       return e;
   }
   for (int pass = 1; pass < kDepthPasses; ++pass) {
@@ -414,8 +421,9 @@ hipError_t launch_depth_order(const gs_proj& proj, int n, void* ws, hipStream_t 
     PassIn in{odd ? w.dk[0] : w.dk[1], odd ? w.dv : proj.order, nullptr, nullptr, 0u, proj.n_visible};
     const bool last = pass == kDepthPasses - 1;
     if ((e = radix_pass<kFromKeys>(in, nb, 8 * pass, w.r, odd ? w.dk[1] : w.dk[0], odd ? proj.order : w.dv,
-                                   nullptr, last ? proj.tiles : nullptr, last ? w.counts : nullptr, s)) !=
-        hipSuccess)
+                                   nullptr, last ? reinterpret_cast<const uint2*>(proj.rect) : nullptr,
+                                   last ? reinterpret_cast<uint2*>(proj.rect_order) : nullptr,
+                                   last ? w.counts : nullptr, s)) != hipSuccess)
       return e;
   }
   // offs: first pair of each visible Gaussian in depth order; offs[n] = the pair count
@@ -449,14 +457,14 @@ hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uin
   {
     GSK_PROF("emit_pairs", s);
     emit_pairs_kernel<<<div_up(pairs, 256), 256, 0, s>>>(proj.offs, proj.n_visible, w.block_first, proj.order,
-                                                         reinterpret_cast<const uint2*>(proj.rect), n, pairs, tx,
-                                                         k_src, v_src);
+                                                         reinterpret_cast<const uint2*>(proj.rect_order), n, pairs,
+                                                         tx, k_src, v_src);
   }
   // stable sort of the pairs by tile
   const int nbp = blocks_for(pairs);
   for (int pass = 0; pass < tile_passes; ++pass) {
     PassIn in{k_src, v_src, nullptr, nullptr, pairs, nullptr};
-    if ((e = radix_pass<kFromKeys>(in, nbp, 8 * pass, w.r, k_dst, v_dst, nullptr, nullptr, nullptr, s)) !=
+    if ((e = radix_pass<kFromKeys>(in, nbp, 8 * pass, w.r, k_dst, v_dst, nullptr, nullptr, nullptr, nullptr, s)) !=
         hipSuccess)
       return e;
     uint32_t* tk = k_src; k_src = k_dst; k_dst = tk;

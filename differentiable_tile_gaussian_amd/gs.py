@@ -44,7 +44,7 @@ class GsScene(C.Structure):
 
 class GsProj(C.Structure):
     _fields_ = [("splat", C.c_void_p), ("depth", C.c_void_p), ("rect", C.c_void_p), ("tiles", C.c_void_p),
-                ("order", C.c_void_p), ("n_visible", C.c_void_p), ("offs", C.c_void_p)]
+                ("order", C.c_void_p), ("n_visible", C.c_void_p), ("offs", C.c_void_p), ("rect_order", C.c_void_p)]
 
 
 def _load():
@@ -130,9 +130,10 @@ class Proj:
         self.order = torch.empty(max(n, 1), dtype=torch.int32, device=device)
         self.n_visible = torch.empty(1, dtype=torch.int32, device=device)
         self.offs = torch.empty(n + 1, dtype=torch.int32, device=device)
+        self.rect_order = torch.empty((max(n, 1), 2), dtype=torch.int32, device=device)
         self.struct = GsProj(self.splat.data_ptr(), self.depth.data_ptr(), self.rect.data_ptr(),
                              self.tiles.data_ptr(), self.order.data_ptr(), self.n_visible.data_ptr(),
-                             self.offs.data_ptr())
+                             self.offs.data_ptr(), self.rect_order.data_ptr())
 
 
 def workspace(which, n=0, pairs=0, W=0, H=0, device="cuda"):

@@ -105,6 +105,8 @@ typedef struct gs_proj {
   uint32_t* offs;       /* [n + 1] exclusive prefix sum of tiles[order[r]] over r (0 past the
                            visible ones): offs[r] is the first pair of the r-th Gaussian in depth
                            order; offs[n] = pair count */
+  uint32_t* rect_order; /* [n][2] rect of the r-th visible Gaussian in depth order (the first
+                           *n_visible entries are written), read by gs_bin_sort */
 } gs_proj;
 
 /* Projection of every Gaussian and the tile count prefix sum.
@@ -119,7 +121,7 @@ typedef struct gs_proj {
  * fp32 without contraction, with exp/log/sigmoid evaluated in fp64 and rounded once, so the
  * pair list is a deterministic function of the inputs.  The visible Gaussians are also put
  * in depth order (stable radix sort of the depth bits, so ties keep id order) for the
- * binning: out->order, out->n_visible and out->offs.
+ * binning: out->order, out->n_visible, out->offs and out->rect_order.
  * out: caller-allocated gs_proj for scene->n Gaussians.  total_pairs: HOST pointer,
  * receives the pair count (= offs[n]).  ws: device workspace of
  * gs_workspace_bytes(GS_WS_PREPROCESS, n, 0, 0, 0) bytes.  Waits for the pair count only:
@@ -141,7 +143,7 @@ int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out,
  * keys[capacity]: tile id of each sorted pair; vals[capacity]: its Gaussian id; the first
  * total_pairs entries are written.  ranges: [2][tiles_x * tiles_y] u32, ranges[0][t] = first,
  * ranges[1][t] = one past the last pair of tile t ((0, 0) for an empty tile).  proj: as
- * gs_preprocess left it (order, n_visible, offs and rect are read); total_pairs must be the
+ * gs_preprocess left it (order, n_visible, offs and rect_order are read); total_pairs must be the
  * value gs_preprocess returned for the same proj.  ws: gs_workspace_bytes(GS_WS_BIN_SORT, n,
  * total_pairs, W, H).  GS_ERR_CAPACITY (nothing written) if capacity < total_pairs or the
  * workspace is short. */

@@ -42,6 +42,7 @@ def proj_to_numpy(pl):
                tiles=pl.proj.tiles[:n].cpu().numpy().view(np.uint32),
                offs=pl.proj.offs.cpu().numpy().view(np.uint32),
                order=pl.proj.order[:n].cpu().numpy().view(np.uint32),
+               rect_order=pl.proj.rect_order[:n].cpu().numpy().view(np.uint32),
                n_visible=int(pl.proj.n_visible.cpu().numpy().view(np.uint32)[0]))
     r = np.zeros((4, n), np.int64)
     r[0] = rect[:, 0] & 0xFFFF
@@ -79,6 +80,10 @@ def check_preprocess(gpu, ora):
     order = ids[np.lexsort((ids, ora["depth"][ids].view(np.uint32)))]
     assert gpu["n_visible"] == len(order)
     np.testing.assert_array_equal(gpu["order"][:len(order)], order)
+    # the rectangles in that order, packed as in rect (x0 | y0 << 16, x1 | y1 << 16)
+    ro = gpu["rect_order"][:len(order)].astype(np.int64)
+    np.testing.assert_array_equal(np.stack([ro[:, 0] & 0xFFFF, ro[:, 0] >> 16, ro[:, 1] & 0xFFFF, ro[:, 1] >> 16]),
+                                  ora["rect"][:, order])
     n = len(ora["tiles"])
     counts = np.zeros(n, np.int64)
     counts[:len(order)] = ora["tiles"][order]

@@ -49,7 +49,7 @@ def test_argument_errors_without_gpu(gs):
     assert "scene" in gs.gs_last_error()
     # unsupported SH degree
     sc = gs.GsScene(10, 4, 1234)
-    proj = gs.GsProj(1, 1, 1, 1, 1, 1, 1)
+    proj = gs.GsProj(1, 1, 1, 1, 1, 1, 1, 1)
     assert L.gs_preprocess(C.byref(sc), C.byref(cam), C.byref(proj), C.byref(total), None, 0,
                            None) == gs.GS_ERR_UNSUPPORTED
     # zero-sized image
