@@ -248,10 +248,12 @@ __device__ inline uint32_t ellipse_mask(uint32_t m, float u, float v, float A, f
 constexpr int kPad = kBatch;
 constexpr int kListLen = kBatch + 4;
 
-// Writes to list, in increasing order, the entries 0 .. last of a batch whose bit for
-// the calling wave's quadrant is set, padded with kPad to a multiple of 4; returns
-// the padded length.  Wave-local: the list is read back by the same wave.
-__device__ inline int build_list(const uint32_t* m, int last, uint16_t* list) {
+// Writes to list, in increasing order, base + scale * e for the entries e = 0 .. last
+// of a batch whose bit for the calling wave's quadrant is set, padded with
+// base + scale * kPad to a multiple of 4; returns the padded length.  Wave-local: the
+// list is read back by the same wave.
+template <typename T>
+__device__ inline int build_list(const uint32_t* m, int last, T* list, uint32_t base, uint32_t scale) {
   const int lane = __lane_id();
   const uint32_t quad = threadIdx.x >> 6;
   const uint64_t below = (uint64_t(1) << lane) - 1;
@@ -260,31 +262,62 @@ __device__ inline int build_list(const uint32_t* m, int last, uint16_t* list) {
     const int e = grp * 64 + lane;
     const bool bit = e <= last && ((m[e] >> quad) & 1u);
     const uint64_t bal = __ballot(bit);
-    if (bit) list[cnt + __popcll(bal & below)] = uint16_t(e);
+    if (bit) list[cnt + __popcll(bal & below)] = T(base + scale * uint32_t(e));
     cnt += __popcll(bal);
   }
   const int pad = (4 - (cnt & 3)) & 3;
-  if (lane < pad) list[cnt + lane] = uint16_t(kPad);
+  if (lane < pad) list[cnt + lane] = T(base + scale * uint32_t(kPad));
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   return cnt + pad;
 }
 
-struct FwdLds {
-  float4 a[2][kBatch + 1];    // u, v, a', b'  (entry kPad: zero record)
-  float4 b[2][kBatch + 1];    // c', opacity, r, g
-  float c[2][kBatch + 1];     // b
-  uint32_t m[2][kBatch];      // quadrant masks
-  uint16_t list[4][kListLen]; // per wave: the batch entries it walks
+// The blend's coefficients of a pair from its record: a = (u, v, a', b'),
+// b = (c', log2 o, r, g) with (a', b', c') = -log2(e) (A/2, B, C/2), so that
+// o exp(-e) = exp2(pair_q(...)).  A record that no pixel may blend has log2 o = -inf.
+__device__ inline void stage_coeffs(const float4& r0, const float4& r1, float4& a, float4& b) {
+  a = make_float4(r0.x, r0.y, -0.5f * kLog2e * r0.z, -kLog2e * r0.w);
+  b = make_float4(-0.5f * kLog2e * r1.x, __builtin_amdgcn_logf(r1.y), r1.z, r1.w);
+}
+constexpr float kNoOpacity = -__builtin_inff();   // log2 of a zero opacity
+
+// q = a' dx^2 + b' dx dy + c' dy^2 + log2 o.  Both walks evaluate it with this one
+// sequence of roundings (explicit fma and products, nothing left to contraction), so
+// the backward recomputes exactly the alpha = min(0.99, exp2(q)) the forward blended.
+__device__ inline float pair_q(float ap, float bp, float cp, float lo2, float dx, float dy) {
+  const float t = fmaf(ap, dx, __fmul_rn(bp, dy));
+  return fmaf(t, dx, fmaf(__fmul_rn(cp, dy), dy, lo2));
+}
+
+// A forward batch entry: one 48-byte LDS record, so that a wave reads an entry with
+// three loads off one address (the walk lists hold the records' byte offsets).
+struct FwdRec {
+  float4 a;   // u, v, a', b'
+  float4 b;   // c', log2 o, r, g
+  float4 c;   // b, 1 + index of the pair in the tile's list (bits), unused, unused
 };
 
-__device__ inline void stage_fwd(const float4* __restrict__ splat, uint32_t g, float ox, float oy, float4& a,
-                                 float4& b, float& c, uint32_t& m) {
+struct FwdLds {
+  FwdRec rec[2][kBatch + 1];  // entry kPad: a record no pixel blends
+  uint32_t m[2][kBatch];      // quadrant masks
+  uint32_t list[4][kListLen]; // per wave: byte offsets (within rec) of the entries it walks
+};
+
+__device__ inline FwdRec empty_fwd_rec() {
+  FwdRec r;
+  r.a = make_float4(0.f, 0.f, 0.f, 0.f);
+  r.b = make_float4(0.f, kNoOpacity, 0.f, 0.f);
+  r.c = make_float4(0.f, 0.f, 0.f, 0.f);
+  return r;
+}
+
+// Record and quadrant mask of Gaussian g as the pair with index idx in its tile's list.
+__device__ inline void stage_fwd(const float4* __restrict__ splat, uint32_t g, int idx, float ox, float oy,
+                                 FwdRec& r, uint32_t& m) {
   const float4 r0 = splat[3 * g], r1 = splat[3 * g + 1], r2 = splat[3 * g + 2];
-  c = r2.x;
-  a = make_float4(r0.x, r0.y, -0.5f * kLog2e * r0.z, -kLog2e * r0.w);
-  b = make_float4(-0.5f * kLog2e * r1.x, r1.y, r1.z, r1.w);
+  stage_coeffs(r0, r1, r.a, r.b);
+  r.c = make_float4(r2.x, __uint_as_float(uint32_t(idx + 1)), 0.f, 0.f);
   m = ellipse_mask(quad_mask(r0.x, r0.y, r2.y, r2.z, ox, oy), r0.x, r0.y, r0.z, r0.w, r1.x, r2.w, ox, oy);
 }
 
@@ -305,57 +338,52 @@ __device__ void fwd_walk(FwdLds& L, const float4* __restrict__ splat, const uint
   const int tid = threadIdx.x;
   if (lo >= hi) return;
   {
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-    float c = 0.f;
+    FwdRec r = empty_fwd_rec();
     uint32_t m = 0u;
-    if (lo + tid < hi) stage_fwd(splat, vals[start + uint32_t(lo + tid)], ox, oy, a, b, c, m);
-    L.a[0][tid] = a; L.b[0][tid] = b; L.c[0][tid] = c; L.m[0][tid] = m;
-    if (tid < 2) {
-      L.a[tid][kPad] = make_float4(0.f, 0.f, 0.f, 0.f);
-      L.b[tid][kPad] = make_float4(0.f, 0.f, 0.f, 0.f);
-      L.c[tid][kPad] = 0.f;
-    }
+    if (lo + tid < hi) stage_fwd(splat, vals[start + uint32_t(lo + tid)], lo + tid, ox, oy, r, m);
+    L.rec[0][tid] = r; L.m[0][tid] = m;
+    if (tid < 2) L.rec[tid][kPad] = empty_fwd_rec();
   }
   __syncthreads();
-  uint16_t* list = L.list[tid >> 6];
+  uint32_t* list = L.list[tid >> 6];
+  const char* recs = reinterpret_cast<const char*>(&L.rec[0][0]);
   bool reported = s.done;
   int buf = 0;
   for (int base = lo; base < hi; base += kBatch) {
     const int nxt = base + kBatch + tid;
-    float4 na = make_float4(0.f, 0.f, 0.f, 0.f), nb = na;
-    float nc = 0.f;
+    FwdRec nr = empty_fwd_rec();
     uint32_t nm = 0u;
-    if (nxt < hi) stage_fwd(splat, vals[start + uint32_t(nxt)], ox, oy, na, nb, nc, nm);
+    if (nxt < hi) stage_fwd(splat, vals[start + uint32_t(nxt)], nxt, ox, oy, nr, nm);
     // walk the batch entries whose quadrant bit is set, in order, four at a time
     bool all_done = __all(s.done);
     if (!all_done) {
-      const int len = build_list(L.m[buf], kBatch - 1, list);
+      const int len = build_list(L.m[buf], kBatch - 1, list, uint32_t(buf * (kBatch + 1) * sizeof(FwdRec)),
+                                 uint32_t(sizeof(FwdRec)));
       for (int k = 0; k < len && !all_done; k += 4) {
-        const uint2 ix = *reinterpret_cast<const uint2*>(list + k);
-        const int e[4] = {int(ix.x & 0xffffu), int(ix.x >> 16), int(ix.y & 0xffffu), int(ix.y >> 16)};
+        const uint4 ix = *reinterpret_cast<const uint4*>(list + k);
+        const uint32_t off[4] = {ix.x, ix.y, ix.z, ix.w};
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 a = L.a[buf][e[q4]];
-          const float4 b = L.b[buf][e[q4]];
-          const float cb = L.c[buf][e[q4]];
+          const FwdRec& r = *reinterpret_cast<const FwdRec*>(recs + off[q4]);
+          const float4 a = r.a, b = r.b;
+          const float2 c = make_float2(r.c.x, r.c.y);
           const float dx = fx - a.x, dy = fy - a.y;
-          const float q = a.z * dx * dx + a.w * dx * dy + b.x * dy * dy;
-          float alpha = fminf(kAlphaCap, b.y * fast_exp2(q));
+          float alpha = fminf(kAlphaCap, fast_exp2(pair_q(a.z, a.w, b.x, b.y, dx, dy)));
           const bool ok = !s.done && alpha >= kAlphaMin;
           alpha = ok ? alpha : 0.0f;
           const float w = alpha * s.T;
           s.c0 += w * b.z;
           s.c1 += w * b.w;
-          s.c2 += w * cb;
+          s.c2 += w * c.x;
           s.T = s.T * (1.0f - alpha);
-          s.last = ok ? uint32_t(base + e[q4] + 1) : s.last;
+          s.last = ok ? __float_as_uint(c.y) : s.last;
           s.done = s.done || (pre * s.T < kTStop);
         }
         all_done = __all(s.done);
       }
     }
     if (base + kBatch < hi) {
-      L.a[buf ^ 1][tid] = na; L.b[buf ^ 1][tid] = nb; L.c[buf ^ 1][tid] = nc; L.m[buf ^ 1][tid] = nm;
+      L.rec[buf ^ 1][tid] = nr; L.m[buf ^ 1][tid] = nm;
     }
     if (POLL) {
       if (s.done && !reported) {
@@ -674,7 +702,7 @@ constexpr int kBwdBatch = 128;
 
 struct BwdLds {
   float4 a[2][kBwdBatch];     // u, v, a', b'
-  float4 b[2][kBwdBatch];     // c', opacity, r, g
+  float4 b[2][kBwdBatch];     // c', log2 o, r, g
   float c[2][kBwdBatch];      // b
   uint32_t id[2][kBwdBatch];
   uint32_t m[2][kBwdBatch];   // quadrant masks
@@ -686,8 +714,7 @@ struct BwdLds {
 __device__ inline void stage_bwd(const float4* __restrict__ splat, uint32_t g, float ox, float oy, float4& a,
                                  float4& b, float& c, uint32_t& m) {
   const float4 r0 = splat[3 * g], r1 = splat[3 * g + 1], r2 = splat[3 * g + 2];
-  a = make_float4(r0.x, r0.y, -0.5f * kLog2e * r0.z, -kLog2e * r0.w);
-  b = make_float4(-0.5f * kLog2e * r1.x, r1.y, r1.z, r1.w);
+  stage_coeffs(r0, r1, a, b);
   c = r2.x;
   m = ellipse_mask(quad_mask(r0.x, r0.y, r2.y, r2.z, ox, oy), r0.x, r0.y, r0.z, r0.w, r1.x, r2.w, ox, oy);
 }
@@ -720,7 +747,7 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
   if (hi <= lo) return;
   if (tid < kBwdBatch) {
     const int blo = max(hi - kBwdBatch, lo);
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = make_float4(0.f, kNoOpacity, 0.f, 0.f);
     float c = 0.f;
     uint32_t g = 0, m = 0u;
     if (blo + tid < hi) {
@@ -735,7 +762,7 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
   while (hi > lo) {
     const int blo = max(hi - kBwdBatch, lo);
     const int nhi = blo, nlo = max(nhi - kBwdBatch, lo);
-    float4 na = make_float4(0.f, 0.f, 0.f, 0.f), nb = na;
+    float4 na = make_float4(0.f, 0.f, 0.f, 0.f), nb = make_float4(0.f, kNoOpacity, 0.f, 0.f);
     float ncr = 0.f;
     uint32_t ng = 0, nm = 0u;
     if (tid < kBwdBatch && nlo + tid < nhi) {
@@ -744,7 +771,7 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
     }
     // entries 0 .. etop of the batch whose quadrant bit is set, last to first
     const int etop = min(hi, wave_top) - 1 - blo;
-    int len = etop >= 0 ? build_list(L.m[buf], etop, list) : 0;
+    int len = etop >= 0 ? build_list(L.m[buf], etop, list, 0u, 1u) : 0;
     while (len > 0 && list[len - 1] == uint16_t(kPad)) --len;
     for (int k = len - 1; k >= 0; --k) {
       const int e = list[k];
@@ -753,9 +780,7 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
       const float4 b = L.b[buf][e];
       const float cb = L.c[buf][e];
       const float dx = fx - a.x, dy = fy - a.y;
-      const float q = a.z * dx * dx + a.w * dx * dy + b.x * dy * dy;
-      const float G = fast_exp2(q);
-      const float araw = b.y * G;
+      const float araw = fast_exp2(pair_q(a.z, a.w, b.x, b.y, dx, dy));   // o exp(-e)
       const float alpha = fminf(kAlphaCap, araw);
       const bool ok = j < s.top && alpha >= kAlphaMin;
       if (__ballot(ok) == 0) continue;
@@ -768,15 +793,16 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
       const float galpha =
           s.g0 * (b.z * Tn - s.S0 * inv) + s.g1 * (b.w * Tn - s.S1 * inv) + s.g2 * (cb * Tn - s.S2 * inv);
       const bool unc = ok && araw <= kAlphaCap;
-      const float ge = unc ? -galpha * araw : 0.0f;   // dL/de
-      // the moments of dL/de over the pixels; the conic is applied when they are flushed
+      const float ge = unc ? -galpha * araw : 0.0f;   // dL/de = -o dL/do
+      // the moments of dL/de over the pixels; the conic (and 1 / o for the opacity) is
+      // applied when they are flushed
       float v[9];
       v[0] = ge * dx;
       v[1] = ge * dy;
       v[2] = v[0] * dx;
       v[3] = v[0] * dy;
       v[4] = v[1] * dy;
-      v[5] = unc ? galpha * G : 0.0f;
+      v[5] = -ge;
       v[6] = s.g0 * w;
       v[7] = s.g1 * w;
       v[8] = s.g2 * w;
@@ -804,6 +830,9 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
       L.acc[tid][1] = -(cB * mx + cC * my);
       L.acc[tid][2] *= 0.5f;
       L.acc[tid][4] *= 0.5f;
+      // the opacity's sum is o dL/do (nonzero only if some pixel blended, so o > 0)
+      const float so = L.acc[tid][5];
+      if (so != 0.0f) L.acc[tid][5] = so * fast_exp2(-L.b[buf][tid].y);
     }
     __syncthreads();
     {
