@@ -43,8 +43,9 @@
 // no pixel centre outside it reaches alpha >= 1/255) misses the quadrant; each wave
 // walks a list of the batch entries its quadrant needs.
 //
-// The conic is prescaled when staged: q = a' dx^2 + b' dx dy + c' dy^2 with
-// (a', b', c') = -log2(e) (A/2, B, C/2), so the Gaussian factor exp(-e) is one exp2.
+// The conic is prescaled and the opacity taken to the exponent when a pair is staged:
+// q = a' dx^2 + b' dx dy + c' dy^2 + log2 o with (a', b', c') = -log2(e) (A/2, B, C/2),
+// so o exp(-e) is one exp2.
 //
 // Pages: [GSG] "The painting itself: front-to-back alpha compositing", "The clever
 // bit: a single backward sweep through the blend", "From a pixel's blame to the
