@@ -29,20 +29,22 @@ WORKLOAD_CFG = 5
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 
 
-def kernel_bytes(kernel, n, deg, P):
+def kernel_bytes(kernel, n, deg, P, fuse=True):
     """Algorithmic HBM bytes of one launch of the streaming kernels (fp32 everywhere).
 
     adam_vec4       per parameter: read theta, g, m, v; write theta, m, v            28 B
     chain           (Adam fused) per Gaussian: tile count 4, the nine screen gradients
-                    36, read + write theta/m/v of all P planes 24 each
+                    36, read + write theta/m/v of all P planes 24 each; with the next
+                    camera's projection also its record: splat 48, depth 4, rect 8,
+                    tile count 4
     preprocess_fwd  per Gaussian: read all P planes, write splat 48, depth 4, rect 8,
                     tile count 4
     """
-    K1 = (deg + 1) ** 2
+    record = 48 + 4 + 8 + 4
     table = {
         "adam_vec4": 28 * P * n,
-        "chain": (4 + 36 + 24 * P) * n,
-        "preprocess_fwd": (4 * P + 48 + 4 + 8 + 4) * n,
+        "chain": (4 + 36 + 24 * P + (record if fuse else 0)) * n,
+        "preprocess_fwd": (4 * P + record) * n,
     }
     return table.get(kernel)
 
@@ -58,6 +60,9 @@ def parse():
                     help="FIRST,CHUNK: pairs every tile walks in one block, and the chunk size of the "
                          "parallel walk of longer lists (library defaults if omitted)")
     ap.add_argument("--stage-report", action="store_true", help="also print per-stage times to stderr")
+    ap.add_argument("--no-fuse-projection", action="store_true",
+                    help="project each step's camera in its own preprocess call instead of in the previous "
+                         "step's update")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy a 1 GiB buffer three times (a plain copy of known size, the "
                          "reference for hardware byte counters)")
@@ -77,7 +82,9 @@ def make_targets(wl, cams, Pipeline, torch):
 
 
 class StageTimer:
-    """HIP events on the stream the library launches on (torch's current stream)."""
+    """HIP events on the stream the library launches on (torch's current stream).  With
+    the projection fused into the previous step's update, "preprocess" is empty and
+    "render_bwd_adam" also holds the next camera's projection and depth order."""
 
     NAMES = ("preprocess", "bin_sort", "render_fwd", "loss", "render_bwd_adam")
 
@@ -93,12 +100,17 @@ class StageTimer:
         return t
 
 
-def run_steps(pl, cams, targets, first, count, timer=None, gs=None):
+def run_steps(pl, cams, targets, first, count, timer=None, gs=None, fuse=True):
+    """Steps first .. first + count - 1 of the camera sequence.  With fuse, each step's
+    update also projects the scene for the next step's camera (so a step's projection
+    is normally done by the step before it; the very first is done on its own)."""
     for s in range(count):
         idx = (first + s) % len(cams)
         c, tgt = cams[idx], targets[idx]
         if timer: timer.mark(s, 0)
-        pl.pairs = gs.gs_preprocess(pl.params, pl.deg, c, pl.proj, pl.ws_pre)
+        if not (fuse and pl.projected_for is c):
+            pl.pairs = gs.gs_preprocess(pl.params, pl.deg, c, pl.proj, pl.ws_pre)
+        pl.projected_for = None
         pl._reserve(pl.pairs)
         if timer: timer.mark(s, 1)
         gs.gs_bin_sort(pl.proj, c, pl.pairs, pl.keys, pl.vals, pl.ranges, pl.ws_sort)
@@ -108,8 +120,17 @@ def run_steps(pl, cams, targets, first, count, timer=None, gs=None):
         gs.gs_loss_l1_dssim(pl.rgb, tgt, pl.lam, pl.loss, pl.dLdI, pl.ws_loss)
         if timer: timer.mark(s, 4)
         pl.t += 1
-        gs.gs_render_bwd_adam(pl.params, pl.deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI,
-                              pl.gscreen, pl.m, pl.v, pl.lr, pl.betas[0], pl.betas[1], pl.eps, pl.t, pl.ws_render)
+        if fuse:
+            nxt = (idx + 1) % len(cams)
+            pl.pairs = gs.gs_render_bwd_adam_project(pl.params, pl.deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c,
+                                                     pl.T, pl.nc, pl.dLdI, pl.gscreen, pl.m, pl.v, pl.lr,
+                                                     pl.betas[0], pl.betas[1], pl.eps, pl.t, pl.ws_render,
+                                                     cams[nxt], pl.proj, pl.ws_pre)
+            pl.projected_for = cams[nxt]
+        else:
+            gs.gs_render_bwd_adam(pl.params, pl.deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc,
+                                  pl.dLdI, pl.gscreen, pl.m, pl.v, pl.lr, pl.betas[0], pl.betas[1], pl.eps, pl.t,
+                                  pl.ws_render)
         if timer: timer.mark(s, 5)
 
 
@@ -222,6 +243,7 @@ def main():
         gs.gs_set_tuning(gs.GS_TUNE_SPLIT_FIRST, first)
         gs.gs_set_tuning(gs.GS_TUNE_SPLIT_CHUNK, chunk)
     split = [gs.gs_get_tuning(gs.GS_TUNE_SPLIT_FIRST), gs.gs_get_tuning(gs.GS_TUNE_SPLIT_CHUNK)]
+    fuse = not args.no_fuse_projection
     t_setup = time.perf_counter()
     wl = scenes.CONFIGS[args.workload]()
     cams = [gs.make_camera(c) for c in wl.cameras]
@@ -237,10 +259,10 @@ def main():
     # kernel launch of the remaining warm-up steps timed: per-kernel time per step and the
     # dominant kernel
     cold = 1 if args.warmup >= 2 else 0
-    run_steps(pl, cams, targets, 0, cold, gs=gs)
+    run_steps(pl, cams, targets, 0, cold, gs=gs, fuse=fuse)
     torch.cuda.synchronize()
     gs.gs_profile_enable(True)
-    run_steps(pl, cams, targets, cold, args.warmup - cold, gs=gs)
+    run_steps(pl, cams, targets, cold, args.warmup - cold, gs=gs, fuse=fuse)
     torch.cuda.synchronize()
     warm = gs.gs_profile_query()
     kernel_ms = {k: ms / max(args.warmup - cold, 1) for k, (cnt, ms) in warm.items()}
@@ -249,7 +271,7 @@ def main():
     gs.gs_profile_enable(True, dominant)
     timer = StageTimer(torch, args.steps)
     t0 = time.perf_counter()
-    run_steps(pl, cams, targets, args.warmup, args.steps, timer=timer, gs=gs)
+    run_steps(pl, cams, targets, args.warmup, args.steps, timer=timer, gs=gs, fuse=fuse)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     live = gs.gs_profile_query()[dominant]
@@ -260,10 +282,10 @@ def main():
     # evaluation counts: replay the same cameras from the same starting state, untimed
     params2 = torch.from_numpy(wl.scene.params).cuda()
     pl2 = Pipeline(params2, deg, cam0.width, cam0.height)
-    run_steps(pl2, cams, targets, 0, args.warmup, gs=gs)
+    run_steps(pl2, cams, targets, 0, args.warmup, gs=gs, fuse=fuse)
     ev_f = ev_b = 0
     for s in range(args.steps):
-        run_steps(pl2, cams, targets, args.warmup + s, 1, gs=gs)
+        run_steps(pl2, cams, targets, args.warmup + s, 1, gs=gs, fuse=fuse)
         f, b = count_evals(pl2, torch)
         ev_f += f
         ev_b += b
@@ -273,7 +295,7 @@ def main():
     # roofline of the dominant kernel from its live launch times
     dom_launches, dom_ms = live
     dom_avg_ms = dom_ms / dom_launches
-    dom_bytes = kernel_bytes(dominant, n, deg, P)
+    dom_bytes = kernel_bytes(dominant, n, deg, P, fuse)
     if dom_bytes is not None:
         achieved = dom_bytes / (dom_avg_ms / 1000.0) / 1e9
         roof = {"kernel": dominant + "_kernel", "bound": "hbm", "achieved": round(achieved, 1),
@@ -297,7 +319,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "gaussians": n, "sh_degree": deg, "image": [cam0.width, cam0.height],
-                   "cameras": len(cams), "step": "preprocess+sort+fwd+loss+bwd+chain+adam (fused)", "parallelism": "none",
+                   "cameras": len(cams), "step": ("sort+fwd+loss+bwd+chain+adam+projection of the next camera (fused; one projection per step)"
+                            if fuse else "preprocess+sort+fwd+loss+bwd+chain+adam (fused)"), "parallelism": "none",
                    "blend_split": split},
         "evals_per_s": round((ev_f + ev_b) / t_fb, 1),
         "evals_per_step": {"fwd": ev_f // args.steps, "bwd": ev_b // args.steps},

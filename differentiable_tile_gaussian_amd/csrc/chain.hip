@@ -14,6 +14,11 @@
 // waves through LDS; every parameter, moment and screen-gradient byte crosses HBM once.
 // gscreen: [n][9] per Gaussian: 0 u, 1 v, 2 A, 3 B, 4 C, 5 opacity, 6-8 colour (read only).
 //
+// With PROJ the block then projects its 64 updated Gaussians for the next camera, from
+// the values it has just written (so they are not read back): wave 3 the geometry and
+// view direction, waves 0-2 the colour of one channel each, wave 3 the record, as the
+// projection kernel does (the same device functions).
+//
 // Compiled without floating-point contraction, like the forward projection, so the
 // recomputed projection is the forward's bit for bit.
 #include "adam_math.h"
@@ -28,106 +33,13 @@ using namespace proj;
 // Plane of colour coefficient k (0 = DC, 1.. = bands) of channel ch.
 __device__ inline int colour_plane(int k, int ch) { return k == 0 ? 11 + ch : 14 + 3 * (k - 1) + ch; }
 
-template <int DEG, bool ADAM>
-__global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, int n, gs_camera cam,
-                                                     const uint32_t* __restrict__ tiles,
-                                                     const float* __restrict__ gscreen, float* __restrict__ gparams,
-                                                     float* __restrict__ m, float* __restrict__ v, AdamArgs a) {
-  constexpr int K = (DEG + 1) * (DEG + 1) - 1;
-  constexpr int P = 11 + 3 * (K + 1);
-  __shared__ float s_gdir[3][3][64];   // view-direction partials of each colour channel
-  __shared__ float s_mean[3][64];
-  __shared__ uint32_t s_tile[64];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int i = blockIdx.x * 64 + lane;
-  const bool valid = i < n;
-  // This block's 64 Gaussians are one group of the blocked layout: each plane is a
-  // contiguous 256-byte row.  Waves 0-2 take the colour planes of one channel each,
-  // wave 3 the eleven geometry planes.  Every load of a lane is issued before any
-  // arithmetic (the pass is a stream; a load that waited on another would add a
-  // memory round trip).  (Separate code paths per wave kind, with the barriers
-  // inside each, use fewer registers but ran slower.)
-  const size_t gb = size_t(blockIdx.x) * P * kGB + lane;
-  const int ch = wv;   // colour waves
-  uint32_t ntile = 0;
-  float th[11], gs6[6], mo[ADAM ? 11 : 1], vo[ADAM ? 11 : 1];
-  float coef[K + 1], cmo[ADAM ? K + 1 : 1], cvo[ADAM ? K + 1 : 1];
-  float gcol = 0.0f;
-  if (wv == 3) {
-    if (valid) {
-      ntile = tiles[i];
-#pragma unroll
-      for (int k = 0; k < 11; ++k) th[k] = __builtin_nontemporal_load(params + gb + k * kGB);
-#pragma unroll
-      for (int k = 0; k < 6; ++k) gs6[k] = gscreen[size_t(i) * 9 + k];
-      if (ADAM) {
-#pragma unroll
-        for (int k = 0; k < 11; ++k) {
-          mo[k] = __builtin_nontemporal_load(m + gb + k * kGB);
-          vo[k] = __builtin_nontemporal_load(v + gb + k * kGB);
-        }
-      }
-    }
-    s_tile[lane] = ntile;
-#pragma unroll
-    for (int c = 0; c < 3; ++c) s_mean[c][lane] = valid ? th[c] : 0.0f;
-  } else if (valid) {
-#pragma unroll
-    for (int k = 0; k <= K; ++k) coef[k] = __builtin_nontemporal_load(params + gb + colour_plane(k, ch) * kGB);
-    gcol = gscreen[size_t(i) * 9 + 6 + ch];
-    if (ADAM) {
-#pragma unroll
-      for (int k = 0; k <= K; ++k) {
-        const size_t o = gb + colour_plane(k, ch) * kGB;
-        cmo[k] = __builtin_nontemporal_load(m + o);
-        cvo[k] = __builtin_nontemporal_load(v + o);
-      }
-    }
-  }
-  __syncthreads();   // tile counts and means
-  if (wv < 3) {
-    const bool vis = valid && s_tile[lane] != 0u;
-    float dir[3] = {0.f, 0.f, 0.f};
-    float Y[16];
-    if (K > 0 && vis) {
-      view_dir_from(s_mean[0][lane], s_mean[1][lane], s_mean[2][lane], cam, dir);
-      sh_eval(dir[0], dir[1], dir[2], Y);
-    }
-    float gc = 0.0f;
-    if (vis) {
-      float raw = coef[0];
-#pragma unroll
-      for (int k = 1; k <= K; ++k) raw = raw + coef[k] * Y[k];
-      gc = raw < 0.0f ? 0.0f : gcol;
-    }
-    if (K > 0) {
-      float gd[3] = {0.f, 0.f, 0.f};
-      if (vis) {
-        float wk[16];
-#pragma unroll
-        for (int k = 1; k <= K; ++k) wk[k] = gc * coef[k];
-        sh_grad_dot(dir[0], dir[1], dir[2], wk, K, gd);
-      }
-#pragma unroll
-      for (int c = 0; c < 3; ++c) s_gdir[ch][c][lane] = gd[c];
-    }
-    if (valid) {
-#pragma unroll
-      for (int k = 0; k <= K; ++k) {
-        const float g = k == 0 ? gc : (vis ? gc * Y[k] : 0.0f);
-        const size_t o = gb + colour_plane(k, ch) * kGB;
-        if (ADAM) {
-          __builtin_nontemporal_store(adam_update(coef[k], g, cmo[k], cvo[k], a.lr[4], a), params + o);
-          __builtin_nontemporal_store(cmo[k], m + o);
-          __builtin_nontemporal_store(cvo[k], v + o);
-        } else {
-          gparams[o] = g;
-        }
-      }
-    }
-  }
-  __syncthreads();   // view-direction partials of the three channels
-  if (wv != 3 || !valid) return;
+// Wave 3's part after the colour waves: the geometry gradients and their Adam update
+// (th returns the updated values).
+template <int K, bool ADAM>
+__device__ inline void geometry_tail(float* th, const float* gs6, float* mo, float* vo, uint32_t ntile, int lane,
+                                     size_t gb, const gs_camera& cam, const float (*s_gdir)[3][64],
+                                     float* __restrict__ params, float* __restrict__ gparams, float* __restrict__ m,
+                                     float* __restrict__ v, const AdamArgs& a) {
   float gp[11];
 #pragma unroll
   for (int k = 0; k < 11; ++k) gp[k] = 0.0f;
@@ -215,7 +127,8 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
   for (int pl = 0; pl < 11; ++pl) {
     const size_t o = gb + pl * kGB;
     if (ADAM) {
-      __builtin_nontemporal_store(adam_update(th[pl], gp[pl], mo[pl], vo[pl], a.lr[adam_group(pl)], a), params + o);
+      th[pl] = adam_update(th[pl], gp[pl], mo[pl], vo[pl], a.lr[adam_group(pl)], a);
+      __builtin_nontemporal_store(th[pl], params + o);
       __builtin_nontemporal_store(mo[pl], m + o);
       __builtin_nontemporal_store(vo[pl], v + o);
     } else {
@@ -225,21 +138,166 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
 }
 
 
-template <int DEG, bool ADAM>
-void launch_chain_deg(float* params, int n, const gs_camera& cam, const uint32_t* tiles, const float* gscreen,
-                      float* gparams, float* m, float* v, const AdamArgs& a, hipStream_t s) {
-  GSK_PROF("chain", s);
-  chain_kernel<DEG, ADAM><<<div_up(n, 64), 256, 0, s>>>(params, n, cam, tiles, gscreen, gparams, m, v, a);
+template <int DEG, bool ADAM, bool PROJ>
+__global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, int n, gs_camera cam,
+                                                     const uint32_t* tiles,   // may be np.tiles
+                                                     const float* __restrict__ gscreen, float* __restrict__ gparams,
+                                                     float* __restrict__ m, float* __restrict__ v, AdamArgs a,
+                                                     NextProj np) {
+  constexpr int K = (DEG + 1) * (DEG + 1) - 1;
+  constexpr int P = 11 + 3 * (K + 1);
+  __shared__ float s_gdir[3][3][64];   // view-direction partials of each colour channel
+  __shared__ float s_mean[3][64];
+  __shared__ uint32_t s_tile[64];
+  __shared__ float s_ndir[PROJ ? 3 : 1][64];   // next camera: view direction, colour before the clamp
+  __shared__ float s_nraw[PROJ ? 3 : 1][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + lane;
+  const bool valid = i < n;
+  // This block's 64 Gaussians are one group of the blocked layout: each plane is a
+  // contiguous 256-byte row.  Waves 0-2 take the colour planes of one channel each,
+  // wave 3 the eleven geometry planes.  Every load of a lane is issued before any
+  // arithmetic (the pass is a stream; a load that waited on another would add a
+  // memory round trip).  (Separate code paths per wave kind, with the barriers
+  // inside each, use fewer registers but ran slower.)
+  const size_t gb = size_t(blockIdx.x) * P * kGB + lane;
+  const int ch = wv;   // colour waves
+  uint32_t ntile = 0;
+  float th[11], gs6[6], mo[ADAM ? 11 : 1], vo[ADAM ? 11 : 1];
+  float coef[K + 1], cmo[ADAM ? K + 1 : 1], cvo[ADAM ? K + 1 : 1];
+  float gcol = 0.0f;
+  if (wv == 3) {
+    if (valid) {
+      ntile = tiles[i];
+#pragma unroll
+      for (int k = 0; k < 11; ++k) th[k] = __builtin_nontemporal_load(params + gb + k * kGB);
+#pragma unroll
+      for (int k = 0; k < 6; ++k) gs6[k] = gscreen[size_t(i) * 9 + k];
+      if (ADAM) {
+#pragma unroll
+        for (int k = 0; k < 11; ++k) {
+          mo[k] = __builtin_nontemporal_load(m + gb + k * kGB);
+          vo[k] = __builtin_nontemporal_load(v + gb + k * kGB);
+        }
+      }
+    }
+    s_tile[lane] = ntile;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) s_mean[c][lane] = valid ? th[c] : 0.0f;
+  } else if (valid) {
+#pragma unroll
+    for (int k = 0; k <= K; ++k) coef[k] = __builtin_nontemporal_load(params + gb + colour_plane(k, ch) * kGB);
+    gcol = gscreen[size_t(i) * 9 + 6 + ch];
+    if (ADAM) {
+#pragma unroll
+      for (int k = 0; k <= K; ++k) {
+        const size_t o = gb + colour_plane(k, ch) * kGB;
+        cmo[k] = __builtin_nontemporal_load(m + o);
+        cvo[k] = __builtin_nontemporal_load(v + o);
+      }
+    }
+  }
+  __syncthreads();   // tile counts and means
+  if (wv < 3) {
+    const bool vis = valid && s_tile[lane] != 0u;
+    float dir[3] = {0.f, 0.f, 0.f};
+    float Y[16];
+    if (K > 0 && vis) {
+      view_dir_from(s_mean[0][lane], s_mean[1][lane], s_mean[2][lane], cam, dir);
+      sh_eval(dir[0], dir[1], dir[2], Y);
+    }
+    float gc = 0.0f;
+    if (vis) {
+      float raw = coef[0];
+#pragma unroll
+      for (int k = 1; k <= K; ++k) raw = raw + coef[k] * Y[k];
+      gc = raw < 0.0f ? 0.0f : gcol;
+    }
+    if (K > 0) {
+      float gd[3] = {0.f, 0.f, 0.f};
+      if (vis) {
+        float wk[16];
+#pragma unroll
+        for (int k = 1; k <= K; ++k) wk[k] = gc * coef[k];
+        sh_grad_dot(dir[0], dir[1], dir[2], wk, K, gd);
+      }
+#pragma unroll
+      for (int c = 0; c < 3; ++c) s_gdir[ch][c][lane] = gd[c];
+    }
+    if (valid) {
+#pragma unroll
+      for (int k = 0; k <= K; ++k) {
+        const float g = k == 0 ? gc : (vis ? gc * Y[k] : 0.0f);
+        const size_t o = gb + colour_plane(k, ch) * kGB;
+        if (ADAM) {
+          coef[k] = adam_update(coef[k], g, cmo[k], cvo[k], a.lr[4], a);
+          __builtin_nontemporal_store(coef[k], params + o);
+          __builtin_nontemporal_store(cmo[k], m + o);
+          __builtin_nontemporal_store(cvo[k], v + o);
+        } else {
+          gparams[o] = g;
+        }
+      }
+    }
+  }
+  __syncthreads();   // view-direction partials of the three channels
+  if (wv == 3 && valid) geometry_tail<K, ADAM>(th, gs6, mo, vo, ntile, lane, gb, cam, s_gdir, params, gparams, m, v, a);
+  if (!PROJ) return;
+  // ---- projection of the updated Gaussians for the next camera
+  Proj g;
+  bool geom = false;
+  if (wv == 3) {
+    if (valid) {
+      geom = project_geometry_from(th, np.cam, g);
+      if (K > 0) {
+        float dir[3];
+        view_dir_from(th[0], th[1], th[2], np.cam, dir);
+#pragma unroll
+        for (int c = 0; c < 3; ++c) s_ndir[c][lane] = dir[c];
+      }
+    }
+  }
+  __syncthreads();   // next view directions
+  if (wv < 3 && valid) {
+    float Y[16];
+    if (K > 0) sh_eval(s_ndir[0][lane], s_ndir[1][lane], s_ndir[2][lane], Y);
+    float raw = coef[0];
+#pragma unroll
+    for (int k = 1; k <= K; ++k) raw = raw + coef[k] * Y[k];
+    s_nraw[ch][lane] = raw;
+  }
+  __syncthreads();   // next colours
+  if (wv != 3) return;
+  Record r;
+  uint32_t cnt = 0u;
+  if (valid) {
+    const float raw[3] = {s_nraw[0][lane], s_nraw[1][lane], s_nraw[2][lane]};
+    make_record(geom, g, raw, np.tx, np.ty, r);
+    store_record(r, i, np.splat, np.depth, np.rect, np.tiles);
+    cnt = r.tiles;
+  }
+  // this block's tile count (the pair count is the sum over blocks)
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) cnt += __shfl_xor(cnt, d, 64);
+  if (lane == 0) np.block_tiles[blockIdx.x] = cnt;
+  if (blockIdx.x == 0 && lane == 0) *np.total = 0u;   // the per-block sums are added after this kernel
 }
 
-template <bool ADAM>
+template <int DEG, bool ADAM, bool PROJ>
+void launch_chain_deg(float* params, int n, const gs_camera& cam, const uint32_t* tiles, const float* gscreen,
+                      float* gparams, float* m, float* v, const AdamArgs& a, const NextProj& np, hipStream_t s) {
+  GSK_PROF("chain", s);
+  chain_kernel<DEG, ADAM, PROJ><<<div_up(n, 64), 256, 0, s>>>(params, n, cam, tiles, gscreen, gparams, m, v, a, np);
+}
+
+template <bool ADAM, bool PROJ>
 void launch_chain_mode(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles, const float* gscreen,
-                       float* gparams, float* m, float* v, const AdamArgs& a, hipStream_t s) {
+                       float* gparams, float* m, float* v, const AdamArgs& a, const NextProj& np, hipStream_t s) {
   switch (deg) {
-    case 0: launch_chain_deg<0, ADAM>(params, n, cam, tiles, gscreen, gparams, m, v, a, s); break;
-    case 1: launch_chain_deg<1, ADAM>(params, n, cam, tiles, gscreen, gparams, m, v, a, s); break;
-    case 2: launch_chain_deg<2, ADAM>(params, n, cam, tiles, gscreen, gparams, m, v, a, s); break;
-    default: launch_chain_deg<3, ADAM>(params, n, cam, tiles, gscreen, gparams, m, v, a, s); break;
+    case 0: launch_chain_deg<0, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, s); break;
+    case 1: launch_chain_deg<1, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, s); break;
+    case 2: launch_chain_deg<2, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, s); break;
+    default: launch_chain_deg<3, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, s); break;
   }
 }
 
@@ -248,16 +306,26 @@ void launch_chain_mode(float* params, int n, int deg, const gs_camera& cam, cons
 hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_camera& cam,
                                  const uint32_t* tiles, const float* gscreen, float* gparams, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  launch_chain_mode<false>(const_cast<float*>(params), n, deg, cam, tiles, gscreen, gparams, nullptr, nullptr,
-                           AdamArgs{}, s);
+  launch_chain_mode<false, false>(const_cast<float*>(params), n, deg, cam, tiles, gscreen, gparams, nullptr, nullptr,
+                                  AdamArgs{}, NextProj{}, s);
   return hipGetLastError();
 }
 
 hipError_t launch_chain_adam(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
                              const float* gscreen, float* m, float* v, const AdamArgs& a, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  launch_chain_mode<true>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, s);
+  launch_chain_mode<true, false>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, NextProj{}, s);
   return hipGetLastError();
+}
+
+hipError_t launch_chain_adam_project(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
+                                     const float* gscreen, float* m, float* v, const AdamArgs& a,
+                                     const NextProj& np, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  launch_chain_mode<true, true>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, np, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_tile_count_total(np.block_tiles, int(div_up(n, 64)), np.total, s);
 }
 
 }  // namespace gsk

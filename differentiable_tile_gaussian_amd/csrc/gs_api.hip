@@ -59,25 +59,31 @@ int32_t check_proj(const gs_proj* p, int64_t n, bool need_order) {
 
 inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
-// Preprocess workspace: pair count, per-block tile sums, depth-order state.
+// Preprocess workspace: pair count, per-block tile sums (one per 64 Gaussians: the
+// projection kernel uses one per 256, the chain with projection one per 64),
+// depth-order state.
 struct PreWs {
   uint64_t* total64;
   uint32_t* block_tiles;
   void* depth_ws;
 };
 
-size_t pre_ws_bytes(int64_t n) {
-  return 256 + align256(size_t(gsk::div_up(n > 0 ? n : 1, 256)) * 4) + gsk::depth_order_ws_bytes(n);
-}
+size_t block_sum_bytes(int64_t n) { return align256(size_t(gsk::div_up(n > 0 ? n : 1, 64)) * 4); }
+
+size_t pre_ws_bytes(int64_t n) { return 256 + block_sum_bytes(n) + gsk::depth_order_ws_bytes(n); }
 
 PreWs carve_pre(void* ws, int64_t n) {
   char* p = static_cast<char*>(ws);
   PreWs w;
   w.total64 = reinterpret_cast<uint64_t*>(p);
   w.block_tiles = reinterpret_cast<uint32_t*>(p + 256);
-  w.depth_ws = p + 256 + align256(size_t(gsk::div_up(n > 0 ? n : 1, 256)) * 4);
+  w.depth_ws = p + 256 + block_sum_bytes(n);
   return w;
 }
+
+// The part of gs_preprocess after the projection kernels: the pair count to the host
+// while the depth order is computed.
+int32_t finish_preprocess(gs_proj* out, int n, const PreWs& w, uint32_t* total_pairs, hipStream_t s);
 
 // Pinned host word the pair count is copied into, and the event that marks the copy,
 // one per device and host thread, created on first use and kept for the process.
@@ -170,6 +176,15 @@ int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out,
   hipError_t e = gsk::launch_preprocess_fwd(scene->params, n, scene->sh_degree, *cam, *out, w.block_tiles,
                                             w.total64, s);
   if (e != hipSuccess) return hip_fail(e, "preprocess_fwd");
+  return finish_preprocess(out, n, w, total_pairs, s);
+}
+
+}  // extern "C"
+
+namespace {
+
+int32_t finish_preprocess(gs_proj* out, int n, const PreWs& w, uint32_t* total_pairs, hipStream_t s) {
+  hipError_t e;
   // the pair count goes to the host while the depth order is computed
   HostSlot* hs = host_slot();
   if (!hs) return fail(GS_ERR_HIP, "cannot set up the pinned pair-count buffer");
@@ -191,6 +206,10 @@ int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out,
   *total_pairs = uint32_t(host_total);
   return GS_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32_t total_pairs, uint32_t* keys,
                     uint32_t* vals, uint32_t capacity, uint32_t* ranges, void* ws, size_t ws_bytes, void* stream) {
@@ -319,6 +338,52 @@ int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs
                              adam_args(lr, beta1, beta2, eps, step), s);
   if (e != hipSuccess) return hip_fail(e, "chain_adam");
   return GS_OK;
+}
+
+int32_t gs_render_bwd_adam_project(float* params, int64_t n, int32_t sh_degree, const gs_proj* proj,
+                                   const uint32_t* vals, const uint32_t* ranges, uint32_t total_pairs,
+                                   const gs_camera* cam, const float* T_final, const uint32_t* n_contrib,
+                                   const float* dL_dimg, float* gscreen, float* m, float* v, const float* lr,
+                                   double beta1, double beta2, double eps, int32_t step, void* ws, size_t ws_bytes,
+                                   const gs_camera* next_cam, gs_proj* next_out, uint32_t* next_total_pairs,
+                                   void* pre_ws, size_t pre_ws_bytes_, void* stream) {
+  g_err[0] = 0;
+  int32_t st;
+  const gs_scene scene{n, sh_degree, params};
+  if ((st = check_scene(&scene)) != GS_OK) return st;
+  if ((st = check_adam(n, sh_degree, lr, beta1, beta2, eps, step)) != GS_OK) return st;
+  if ((st = check_camera(cam)) != GS_OK) return st;
+  if ((st = check_camera(next_cam)) != GS_OK) return st;
+  if ((st = check_proj(proj, n, false)) != GS_OK) return st;
+  if ((st = check_proj(next_out, n, true)) != GS_OK) return st;
+  if (!next_total_pairs) return fail(GS_ERR_INVALID_ARG, "next_total_pairs is null");
+  if (!ranges || !T_final || !n_contrib || !dL_dimg) return fail(GS_ERR_INVALID_ARG, "a render input is null");
+  if (n > 0 && (!gscreen || !m || !v)) return fail(GS_ERR_INVALID_ARG, "gscreen, m or v is null");
+  if (total_pairs > 0 && !vals) return fail(GS_ERR_INVALID_ARG, "vals is null");
+  const size_t need = gs_workspace_bytes(GS_WS_RENDER, n, total_pairs, cam->width, cam->height);
+  if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "render workspace needs %zu bytes", need);
+  const size_t need_pre = gs_workspace_bytes(GS_WS_PREPROCESS, n, 0, 0, 0);
+  if (!pre_ws || pre_ws_bytes_ < need_pre)
+    return fail(GS_ERR_CAPACITY, "preprocess workspace needs %zu bytes", need_pre);
+  hipStream_t s = as_stream(stream);
+  hipError_t e = gsk::launch_render_bwd(*proj, int(n), vals, ranges, *cam, total_pairs, T_final, n_contrib,
+                                        dL_dimg, gscreen, ws, s);
+  if (e != hipSuccess) return hip_fail(e, "render_bwd");
+  PreWs w = carve_pre(pre_ws, n);
+  gsk::NextProj np;
+  np.cam = *next_cam;
+  np.tx = gsk::tiles_x(*next_cam);
+  np.ty = gsk::tiles_y(*next_cam);
+  np.splat = reinterpret_cast<float4*>(next_out->splat);
+  np.depth = next_out->depth;
+  np.rect = reinterpret_cast<uint2*>(next_out->rect);
+  np.tiles = next_out->tiles;
+  np.block_tiles = w.block_tiles;
+  np.total = w.total64;
+  e = gsk::launch_chain_adam_project(params, int(n), sh_degree, *cam, proj->tiles, gscreen, m, v,
+                                     adam_args(lr, beta1, beta2, eps, step), np, s);
+  if (e != hipSuccess) return hip_fail(e, "chain_adam_project");
+  return finish_preprocess(next_out, int(n), w, next_total_pairs, s);
 }
 
 int32_t gs_adam_step(float* params, const float* grads, float* m, float* v, int64_t n, int32_t sh_degree,

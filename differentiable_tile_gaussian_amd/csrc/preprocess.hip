@@ -21,35 +21,6 @@ namespace {
 
 using namespace proj;
 
-// Half-widths of a box around (u, v) outside which no pixel centre can get
-// alpha >= 1/255 from this Gaussian, for the blend's per-quadrant skipping.  The
-// blend tests o exp(-e) >= 1/255 with e from the fp32 conic (A, B, C), so the box
-// bounds the ellipse e <= ln(255 o) of that conic: |dx| <= sqrt(2 t C / (A C - B^2)),
-// |dy| <= sqrt(2 t A / (A C - B^2)), evaluated in fp64 from the fp32 conic and widened
-// to cover the blend's fp32 evaluation of e: t by 1 % + 0.01 (the widened value is
-// returned in tm, for the blend's finer per-quadrant test of e itself), the half-widths
-// by 1 % + 0.05 px.  With A C / (A C - B^2) <= 1000 the rounding error of e stays below
-// 0.2 % of e (about 0.01 at the box), inside the margin; more elongated conics get an
-// unbounded box.  Negative when o < e^-0.001 / 255 (no pixel can reach 1/255);
-// infinite (box and tm) when the fp32 conic is not positive definite.
-__device__ inline void blend_box(const Proj& g, float& hx, float& hy, float& tm_out) {
-  const double t = log(double(g.o) * 255.0);
-  if (!(t > -1e-3)) {
-    hx = hy = tm_out = -1.0f;
-    return;
-  }
-  const double A = g.A, B = g.B, C = g.C;
-  const double det = A * C - B * B;
-  if (!(det > 0.0) || !(A > 0.0) || !(C > 0.0) || !(A * C <= 1000.0 * det)) {
-    hx = hy = tm_out = __builtin_inff();
-    return;
-  }
-  const double tm = t + 0.01 + 0.01 * fabs(t);
-  hx = float(sqrt(2.0 * tm * C / det) * 1.01 + 0.05);
-  hy = float(sqrt(2.0 * tm * A / det) * 1.01 + 0.05);
-  tm_out = float(tm);
-}
-
 // One Gaussian: writes its projected record and returns its tile count.
 template <int DEG>
 __device__ inline uint32_t project_one(const float* __restrict__ params, int i, const gs_camera& cam, int tx, int ty,
@@ -59,67 +30,21 @@ __device__ inline uint32_t project_one(const float* __restrict__ params, int i, 
   constexpr int P = 11 + 3 * (K + 1);
   const float* g0 = gaussian_base(params, i, P);
   Proj g;
-  bool vis = project_geometry(g0, cam, g);
-  float rgb[3] = {0.f, 0.f, 0.f};
-  uint32_t x0 = 0, y0 = 0, x1 = 0, y1 = 0, cnt = 0;
-  if (vis) {
+  const bool geom = project_geometry(g0, cam, g);
+  float raw[3] = {0.f, 0.f, 0.f};
+  if (geom) {
     float Y[16];
     if (K > 0) {
       float dir[3];
       view_dir(g0, cam, dir);
       sh_eval(dir[0], dir[1], dir[2], Y);
     }
-    float raw[3];
     sh_colour(g0, K, Y, raw);
-    bool finite = __builtin_isfinite(g.u) && __builtin_isfinite(g.v) && __builtin_isfinite(g.A) &&
-                  __builtin_isfinite(g.B) && __builtin_isfinite(g.C) && __builtin_isfinite(g.o);
-    for (int ch = 0; ch < 3; ++ch) {
-      rgb[ch] = fmaxf(raw[ch], 0.0f);
-      finite = finite && __builtin_isfinite(rgb[ch]);
-    }
-    vis = finite;
-    if (vis) {
-      // opacity-aware extent ([GSG] "Why tiling"): rad = sqrt(2 eMax) sqrt(lambda_max)
-      const float mid = 0.5f * (g.a + g.c);
-      const float disc = sqrtf(fmaxf(mid * mid - g.det, 0.0f));
-      const float lmax = mid + disc;
-      const float emax = float(fmin(4.5, log(fmax(double(g.o) * 255.0, 1.0001))));
-      const float rad = sqrtf(2.0f * emax) * sqrtf(lmax);
-      vis = __builtin_isfinite(rad);
-      if (vis) {
-        const float fx0 = floorf((g.u - rad) / 16.0f), fx1 = floorf((g.u + rad) / 16.0f);
-        const float fy0 = floorf((g.v - rad) / 16.0f), fy1 = floorf((g.v + rad) / 16.0f);
-        if (fx1 < 0.0f || fx0 > float(tx - 1) || fy1 < 0.0f || fy0 > float(ty - 1)) {
-          vis = false;
-        } else {
-          x0 = uint32_t(fmaxf(fx0, 0.0f));
-          y0 = uint32_t(fmaxf(fy0, 0.0f));
-          x1 = uint32_t(fminf(fx1, float(tx - 1)));
-          y1 = uint32_t(fminf(fy1, float(ty - 1)));
-          cnt = (x1 - x0 + 1) * (y1 - y0 + 1);
-        }
-      }
-    }
   }
-  if (vis) {
-    splat[3 * i + 0] = make_float4(g.u, g.v, g.A, g.B);
-    splat[3 * i + 1] = make_float4(g.C, g.o, rgb[0], rgb[1]);
-    float hx, hy, tm;
-    blend_box(g, hx, hy, tm);
-    splat[3 * i + 2] = make_float4(rgb[2], hx, hy, tm);
-    depth[i] = g.p[2];
-    rect[i] = make_uint2(x0 | (y0 << 16), x1 | (y1 << 16));
-    tiles[i] = cnt;
-  } else {
-    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-    splat[3 * i + 0] = z;
-    splat[3 * i + 1] = z;
-    splat[3 * i + 2] = z;
-    depth[i] = 0.0f;
-    rect[i] = make_uint2(0u, 0u);
-    tiles[i] = 0u;
-  }
-  return vis ? cnt : 0u;
+  Record r;
+  make_record(geom, g, raw, tx, ty, r);
+  store_record(r, i, splat, depth, rect, tiles);
+  return r.tiles;
 }
 
 template <int DEG>
@@ -178,8 +103,12 @@ hipError_t launch_preprocess_fwd(const float* params, int n, int deg, const gs_c
       default: preprocess_fwd_kernel<3><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles, total_pairs); break;
     }
   }
+  return launch_tile_count_total(block_tiles, int(grid.x), total_pairs, s);
+}
+
+hipError_t launch_tile_count_total(const uint32_t* block_tiles, int nb, uint64_t* total, hipStream_t s) {
   GSK_PROF("sum_counts", s);
-  sum_counts_kernel<<<div_up(grid.x, 1024), 1024, 0, s>>>(block_tiles, int(grid.x), total_pairs);
+  sum_counts_kernel<<<div_up(nb, 1024), 1024, 0, s>>>(block_tiles, nb, total);
   return hipGetLastError();
 }
 

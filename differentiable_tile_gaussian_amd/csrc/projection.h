@@ -204,5 +204,107 @@ __device__ inline void sh_colour(const float* __restrict__ g0, int K, const floa
   }
 }
 
+// Half-widths of a box around (u, v) outside which no pixel centre can get
+// alpha >= 1/255 from this Gaussian, for the blend's per-quadrant skipping.  The
+// blend tests o exp(-e) >= 1/255 with e from the fp32 conic (A, B, C), so the box
+// bounds the ellipse e <= ln(255 o) of that conic: |dx| <= sqrt(2 t C / (A C - B^2)),
+// |dy| <= sqrt(2 t A / (A C - B^2)), evaluated in fp64 from the fp32 conic and widened
+// to cover the blend's fp32 evaluation of e: t by 1 % + 0.01 (the widened value is
+// returned in tm, for the blend's finer per-quadrant test of e itself), the half-widths
+// by 1 % + 0.05 px.  With A C / (A C - B^2) <= 1000 the rounding error of e stays below
+// 0.2 % of e (about 0.01 at the box), inside the margin; more elongated conics get an
+// unbounded box.  Negative when o < e^-0.001 / 255 (no pixel can reach 1/255);
+// infinite (box and tm) when the fp32 conic is not positive definite.
+__device__ inline void blend_box(const Proj& g, float& hx, float& hy, float& tm_out) {
+  const double t = log(double(g.o) * 255.0);
+  if (!(t > -1e-3)) {
+    hx = hy = tm_out = -1.0f;
+    return;
+  }
+  const double A = g.A, B = g.B, C = g.C;
+  const double det = A * C - B * B;
+  if (!(det > 0.0) || !(A > 0.0) || !(C > 0.0) || !(A * C <= 1000.0 * det)) {
+    hx = hy = tm_out = __builtin_inff();
+    return;
+  }
+  const double tm = t + 0.01 + 0.01 * fabs(t);
+  hx = float(sqrt(2.0 * tm * C / det) * 1.01 + 0.05);
+  hy = float(sqrt(2.0 * tm * A / det) * 1.01 + 0.05);
+  tm_out = float(tm);
+}
+
+// A Gaussian's projected record (the gs_proj entries), zero when culled.
+struct Record {
+  float4 r0, r1, r2;   // u, v, A, B | C, o, r, g | b, hx, hy, tm
+  float depth;
+  uint2 rect;          // x0 | y0 << 16, x1 | y1 << 16
+  uint32_t tiles;
+};
+
+// The record from the geometry (geom: project_geometry_from succeeded) and the colour
+// before the clamp: clamped colour, culling of non-finite values, the opacity-aware
+// extent and tile rectangle ([GSG] "Why tiling": rad = sqrt(2 eMax) sqrt(lambda_max)),
+// and the blend box.
+__device__ inline void make_record(bool geom, const Proj& g, const float* raw, int tx, int ty, Record& out) {
+  bool vis = geom;
+  float rgb[3] = {0.f, 0.f, 0.f};
+  uint32_t x0 = 0, y0 = 0, x1 = 0, y1 = 0, cnt = 0;
+  if (vis) {
+    bool finite = __builtin_isfinite(g.u) && __builtin_isfinite(g.v) && __builtin_isfinite(g.A) &&
+                  __builtin_isfinite(g.B) && __builtin_isfinite(g.C) && __builtin_isfinite(g.o);
+    for (int ch = 0; ch < 3; ++ch) {
+      rgb[ch] = fmaxf(raw[ch], 0.0f);
+      finite = finite && __builtin_isfinite(rgb[ch]);
+    }
+    vis = finite;
+    if (vis) {
+      const float mid = 0.5f * (g.a + g.c);
+      const float disc = sqrtf(fmaxf(mid * mid - g.det, 0.0f));
+      const float lmax = mid + disc;
+      const float emax = float(fmin(4.5, log(fmax(double(g.o) * 255.0, 1.0001))));
+      const float rad = sqrtf(2.0f * emax) * sqrtf(lmax);
+      vis = __builtin_isfinite(rad);
+      if (vis) {
+        const float fx0 = floorf((g.u - rad) / 16.0f), fx1 = floorf((g.u + rad) / 16.0f);
+        const float fy0 = floorf((g.v - rad) / 16.0f), fy1 = floorf((g.v + rad) / 16.0f);
+        if (fx1 < 0.0f || fx0 > float(tx - 1) || fy1 < 0.0f || fy0 > float(ty - 1)) {
+          vis = false;
+        } else {
+          x0 = uint32_t(fmaxf(fx0, 0.0f));
+          y0 = uint32_t(fmaxf(fy0, 0.0f));
+          x1 = uint32_t(fminf(fx1, float(tx - 1)));
+          y1 = uint32_t(fminf(fy1, float(ty - 1)));
+          cnt = (x1 - x0 + 1) * (y1 - y0 + 1);
+        }
+      }
+    }
+  }
+  if (vis) {
+    out.r0 = make_float4(g.u, g.v, g.A, g.B);
+    out.r1 = make_float4(g.C, g.o, rgb[0], rgb[1]);
+    float hx, hy, tm;
+    blend_box(g, hx, hy, tm);
+    out.r2 = make_float4(rgb[2], hx, hy, tm);
+    out.depth = g.p[2];
+    out.rect = make_uint2(x0 | (y0 << 16), x1 | (y1 << 16));
+    out.tiles = cnt;
+  } else {
+    out.r0 = out.r1 = out.r2 = make_float4(0.f, 0.f, 0.f, 0.f);
+    out.depth = 0.0f;
+    out.rect = make_uint2(0u, 0u);
+    out.tiles = 0u;
+  }
+}
+
+__device__ inline void store_record(const Record& r, int i, float4* __restrict__ splat, float* __restrict__ depth,
+                                    uint2* __restrict__ rect, uint32_t* __restrict__ tiles) {
+  splat[3 * i + 0] = r.r0;
+  splat[3 * i + 1] = r.r1;
+  splat[3 * i + 2] = r.r2;
+  depth[i] = r.depth;
+  rect[i] = r.rect;
+  tiles[i] = r.tiles;
+}
+
 }  // namespace proj
 }  // namespace gsk

@@ -21,7 +21,7 @@ GS_WS_PREPROCESS, GS_WS_BIN_SORT, GS_WS_LOSS, GS_WS_RENDER = 0, 1, 2, 3
 GS_TUNE_SPLIT_FIRST, GS_TUNE_SPLIT_CHUNK = 0, 1
 
 EXPORTED = ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
-            "gs_adam_step", "gs_render_bwd_adam", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
+            "gs_adam_step", "gs_render_bwd_adam", "gs_render_bwd_adam_project", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
             "gs_profile_enable", "gs_profile_query", "gs_param_floats", "gs_params_to_blocked",
             "gs_params_from_blocked", "gs_last_error")
 
@@ -60,6 +60,10 @@ def _load():
     lib.gs_render_bwd_adam.argtypes = [P, I64, I32, P, P, P, U32, P, P, P, P, P, P, P, P, C.c_double, C.c_double,
                                        C.c_double, I32, P, C.c_size_t, P]
     lib.gs_render_bwd_adam.restype = I32
+    lib.gs_render_bwd_adam_project.argtypes = [P, I64, I32, P, P, P, U32, P, P, P, P, P, P, P, P, C.c_double,
+                                               C.c_double, C.c_double, I32, P, C.c_size_t, P, P, P, P, C.c_size_t,
+                                               P]
+    lib.gs_render_bwd_adam_project.restype = I32
     lib.gs_set_tuning.argtypes = [I32, I64]
     lib.gs_set_tuning.restype = I32
     lib.gs_get_tuning.argtypes = [I32]
@@ -242,6 +246,24 @@ def gs_render_bwd_adam(params, sh_degree, proj: Proj, vals, ranges, total_pairs,
                                    total_pairs, C.byref(cam), _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimg),
                                    _ptr(gscreen), _ptr(m), _ptr(v), lr_arr, float(beta1), float(beta2),
                                    float(eps), int(step), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def gs_render_bwd_adam_project(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam: GsCamera, T_final,
+                               n_contrib, dL_dimg, gscreen, m, v, lr, beta1, beta2, eps, step, ws,
+                               next_cam: GsCamera, next_proj: Proj, pre_ws, stream=None) -> int:
+    """gs_render_bwd_adam, then the projection of the updated scene for next_cam into
+    next_proj (may be proj); returns the next pair count (synchronises once)."""
+    for t in (params, m, v):
+        _blocked(t, proj.n, sh_degree)
+    assert next_proj.n == proj.n
+    lr_arr = (C.c_float * 5)(*[float(x) for x in lr])
+    total = C.c_uint32(0)
+    _check(_lib.gs_render_bwd_adam_project(
+        _ptr(params), proj.n, sh_degree, C.byref(proj.struct), _ptr(vals), _ptr(ranges), total_pairs, C.byref(cam),
+        _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimg), _ptr(gscreen), _ptr(m), _ptr(v), lr_arr, float(beta1),
+        float(beta2), float(eps), int(step), _ptr(ws), ws.numel(), C.byref(next_cam), C.byref(next_proj.struct),
+        C.byref(total), _ptr(pre_ws), pre_ws.numel(), _stream(stream)))
+    return int(total.value)
 
 
 def gs_set_tuning(key, value):

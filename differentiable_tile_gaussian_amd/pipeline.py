@@ -45,6 +45,7 @@ class Pipeline:
         self.v = gs.empty_blocked(self.n, sh_degree, dev, zero=True)
         self.t = 0
         self.pairs = 0
+        self.projected_for = None   # set by a fused update that projected for the next step's camera
 
     def planar(self, blocked: torch.Tensor) -> torch.Tensor:
         """[P][n] copy of one of the blocked arrays (params, grads, m, v)."""
@@ -53,6 +54,7 @@ class Pipeline:
     def set_planar(self, blocked: torch.Tensor, planar: torch.Tensor):
         """Overwrite one of the blocked arrays from a [P][n] tensor."""
         gs.to_blocked(planar.to(blocked.device).contiguous(), self.deg, out=blocked)
+        self.projected_for = None
 
     def _reserve(self, pairs):
         if self.keys.numel() < pairs:
@@ -67,7 +69,9 @@ class Pipeline:
             self.ws_render = torch.empty(int(need * 1.25) + 4096, dtype=torch.uint8, device=self.params.device)
 
     def forward(self, cam: gs.GsCamera):
-        self.pairs = gs.gs_preprocess(self.params, self.deg, cam, self.proj, self.ws_pre)
+        if self.projected_for is not cam:
+            self.pairs = gs.gs_preprocess(self.params, self.deg, cam, self.proj, self.ws_pre)
+        self.projected_for = None
         self._reserve(self.pairs)
         gs.gs_bin_sort(self.proj, cam, self.pairs, self.keys, self.vals, self.ranges, self.ws_sort)
         gs.gs_render_fwd(self.proj, self.vals, self.ranges, self.pairs, cam, self.rgb, self.T, self.nc,
@@ -85,18 +89,30 @@ class Pipeline:
         gs.gs_adam_step(self.params, self.grads, self.m, self.v, self.n, self.deg, self.lr, self.betas[0],
                         self.betas[1], self.eps, self.t)
 
-    def backward_adam(self, cam: gs.GsCamera, target: torch.Tensor):
-        """Loss, backward and Adam with the chain and Adam fused (no gradient written)."""
+    def backward_adam(self, cam: gs.GsCamera, target: torch.Tensor, next_cam: gs.GsCamera = None):
+        """Loss, backward and Adam with the chain and Adam fused (no gradient written).
+        With next_cam, the update also projects the scene for next_cam, and the next
+        forward(next_cam) (the same camera object) uses that projection."""
         gs.gs_loss_l1_dssim(self.rgb, target, self.lam, self.loss, self.dLdI, self.ws_loss)
         self.t += 1
-        gs.gs_render_bwd_adam(self.params, self.deg, self.proj, self.vals, self.ranges, self.pairs, cam, self.T,
-                              self.nc, self.dLdI, self.gscreen, self.m, self.v, self.lr, self.betas[0],
-                              self.betas[1], self.eps, self.t, self.ws_render)
+        if next_cam is None:
+            gs.gs_render_bwd_adam(self.params, self.deg, self.proj, self.vals, self.ranges, self.pairs, cam, self.T,
+                                  self.nc, self.dLdI, self.gscreen, self.m, self.v, self.lr, self.betas[0],
+                                  self.betas[1], self.eps, self.t, self.ws_render)
+            return
+        self.pairs = gs.gs_render_bwd_adam_project(self.params, self.deg, self.proj, self.vals, self.ranges,
+                                                   self.pairs, cam, self.T, self.nc, self.dLdI, self.gscreen, self.m,
+                                                   self.v, self.lr, self.betas[0], self.betas[1], self.eps, self.t,
+                                                   self.ws_render, next_cam, self.proj, self.ws_pre)
+        self.projected_for = next_cam
 
-    def step(self, cam: gs.GsCamera, target: torch.Tensor, adam: bool = True, fused: bool = True):
+    def step(self, cam: gs.GsCamera, target: torch.Tensor, adam: bool = True, fused: bool = True,
+             next_cam: gs.GsCamera = None):
+        """One training step; with next_cam (fused Adam only) the update also projects
+        the scene for the camera of the following step."""
         self.forward(cam)
         if adam and fused:
-            self.backward_adam(cam, target)
+            self.backward_adam(cam, target, next_cam)
             return self.loss
         self.backward(cam, target)
         if adam:

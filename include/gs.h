@@ -217,6 +217,24 @@ int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs
                            float* m, float* v, const float* lr, double beta1, double beta2, double eps,
                            int32_t step, void* ws, size_t ws_bytes, void* stream);
 
+/* gs_render_bwd_adam followed by gs_preprocess of the updated scene for the camera of the
+ * next step ([GSG] training loop: pick a view, render, compare, backpropagate, update;
+ * the next view is known when this one's update runs).  The chain projects each
+ * Gaussian for next_cam from the parameters it has just computed, in the same kernel,
+ * so they are not read back from memory; the projection, depth order, pair offsets
+ * and pair count are those gs_preprocess(scene, next_cam, next_out, next_total_pairs,
+ * pre_ws) would produce from the updated params, bit for bit.  next_out may be proj
+ * itself (each Gaussian's tile count is read before its new record is written).
+ * pre_ws: gs_workspace_bytes(GS_WS_PREPROCESS, n, 0, 0, 0) bytes.  Waits for the next
+ * pair count as gs_preprocess does; errors as gs_render_bwd_adam and gs_preprocess. */
+int32_t gs_render_bwd_adam_project(float* params, int64_t n, int32_t sh_degree, const gs_proj* proj,
+                                   const uint32_t* vals, const uint32_t* ranges, uint32_t total_pairs,
+                                   const gs_camera* cam, const float* T_final, const uint32_t* n_contrib,
+                                   const float* dL_dimg, float* gscreen, float* m, float* v, const float* lr,
+                                   double beta1, double beta2, double eps, int32_t step, void* ws, size_t ws_bytes,
+                                   const gs_camera* next_cam, gs_proj* next_out, uint32_t* next_total_pairs,
+                                   void* pre_ws, size_t pre_ws_bytes, void* stream);
+
 /* Layout of the per-Gaussian parameter arrays (see the blocked layout above).
  * gs_param_floats: floats in a blocked array for n Gaussians (0 for bad arguments).
  * gs_params_to_blocked: planar [P][n] -> blocked, padding zeroed; gs_params_from_blocked:

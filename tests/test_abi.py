@@ -75,6 +75,19 @@ def test_argument_errors_without_gpu(gs):
                            None) == gs.GS_ERR_INVALID_ARG
     # render without its workspace
     assert L.gs_render_fwd(C.byref(proj), 10, 1, 1, 100, C.byref(cam), 1, 1, 1, None, 0, None) == gs.GS_ERR_CAPACITY
+    # backward + Adam + next projection: the next camera, its pair-count output and the
+    # preprocess workspace are checked before anything is enqueued
+    nxt = gs.GsCamera.from_buffer_copy(cam)
+    nt = C.c_uint32(0)
+
+    def bwd_project(next_cam, next_total, pre_ws, pre_bytes):
+        return L.gs_render_bwd_adam_project(1, 10, 0, C.byref(proj), 1, 1, 100, C.byref(cam), 1, 1, 1, 1, 1, 1, lr,
+                                            0.9, 0.999, 1e-8, 1, 1, 1 << 40, next_cam, C.byref(proj), next_total,
+                                            pre_ws, pre_bytes, None)
+    assert bwd_project(None, C.byref(nt), 1, 1 << 40) == gs.GS_ERR_INVALID_ARG
+    assert bwd_project(C.byref(nxt), None, 1, 1 << 40) == gs.GS_ERR_INVALID_ARG
+    assert bwd_project(C.byref(nxt), C.byref(nt), None, 0) == gs.GS_ERR_CAPACITY
+    assert "preprocess workspace" in gs.gs_last_error()
     # tuning values are checked
     assert L.gs_set_tuning(gs.GS_TUNE_SPLIT_CHUNK, 6) == gs.GS_ERR_INVALID_ARG
     assert L.gs_set_tuning(77, 1024) == gs.GS_ERR_INVALID_ARG

@@ -449,3 +449,59 @@ def test_workload_full_step(torch_cuda, oracle, cfg):
         tol = 2e-3 * lr + 2e-7 * np.abs(th0[sl])
         assert np.all(np.abs(st - pred)[firm] <= tol[firm]), f"fused update {name}"
         assert np.all(np.abs(st) <= 1.01 * lr + 2e-7 * np.abs(th0[sl])), f"fused update bound {name}"
+
+
+# ------------------------------------ update fused with the next camera's projection
+def _proj_arrays(proj, n):
+    nv = int(proj.n_visible.cpu().numpy().view(np.uint32)[0])
+    return dict(splat=proj.splat[:n].cpu().numpy().view(np.uint32), depth=proj.depth[:n].cpu().numpy().view(np.uint32),
+                rect=proj.rect[:n].cpu().numpy(), tiles=proj.tiles[:n].cpu().numpy(), n_visible=np.array([nv]),
+                order=proj.order[:nv].cpu().numpy(), rect_order=proj.rect_order[:nv].cpu().numpy(),
+                offs=proj.offs[:nv + 1].cpu().numpy())
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("case", ["small1", "small3", "small4", "cfg5"])
+def test_update_with_next_projection(torch_cuda, case):
+    """gs_render_bwd_adam_project (in place, as the benchmark calls it): the next camera's
+    records, depths, rectangles, tile counts, depth order, rectangles in that order, pair
+    offsets and pair count equal gs_preprocess of the parameters it wrote, bit for bit
+    (the same contraction-free fp32 code, fed from registers instead of memory); and the
+    update equals gs_render_bwd_adam's up to the order of the gradient atomics."""
+    torch = torch_cuda
+    from differentiable_tile_gaussian_amd import gs
+    if case == "cfg5":
+        wl = scenes.CONFIGS[5]()
+        s, cam, cam2 = wl.scene, wl.cameras[0], wl.cameras[1]
+    else:
+        args = _small_cases()[int(case[-1])]
+        s, cam = _scene_and_camera(*args)
+        cam2 = _scene_and_camera(args[0] + 3, *args[1:])[1]   # the same image size, another orbit angle
+    deg, n = s.sh_degree, s.n
+    print(f"case {case}: n={n} {cam.width}x{cam.height}", flush=True)
+    dLdI = (np.random.default_rng(5).standard_normal((3, cam.height, cam.width)) * 1e-3).astype(np.float32)
+    c2 = gs.make_camera(cam2)
+    pl, c = pu.gpu_forward(s.params, deg, cam)
+    pl.dLdI.copy_(torch.from_numpy(dLdI))
+    pairs = gs.gs_render_bwd_adam_project(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc,
+                                          pl.dLdI, pl.gscreen, pl.m, pl.v, pl.lr, 0.9, 0.999, 1e-8, 1,
+                                          pl.ws_render, c2, pl.proj, pl.ws_pre)
+    torch.cuda.synchronize()
+    fused = _proj_arrays(pl.proj, n)
+    proj_b = gs.Proj(n)
+    pairs_b = gs.gs_preprocess(pl.params, deg, c2, proj_b, gs.workspace(gs.GS_WS_PREPROCESS, n=n))
+    torch.cuda.synchronize()
+    ref = _proj_arrays(proj_b, n)
+    assert pairs == pairs_b
+    for k in ref:
+        np.testing.assert_array_equal(fused[k], ref[k], err_msg=k)
+    # the update against the call without the projection
+    pl2, c_ = pu.gpu_forward(s.params, deg, cam)
+    pl2.dLdI.copy_(torch.from_numpy(dLdI))
+    gs.gs_render_bwd_adam(pl2.params, deg, pl2.proj, pl2.vals, pl2.ranges, pl2.pairs, c_, pl2.T, pl2.nc, pl2.dLdI,
+                          pl2.gscreen, pl2.m, pl2.v, pl2.lr, 0.9, 0.999, 1e-8, 1, pl2.ws_render)
+    torch.cuda.synchronize()
+    for name, a, b in (("params", pl.params, pl2.params), ("m", pl.m, pl2.m), ("v", pl.v, pl2.v)):
+        x, y = pl.planar(a).cpu().numpy(), pl2.planar(b).cpu().numpy()
+        scale = np.abs(y).max() + 1e-30
+        np.testing.assert_allclose(x, y, rtol=1e-5, atol=1e-5 * scale if name != "params" else 1e-5, err_msg=name)
