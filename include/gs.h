@@ -218,8 +218,9 @@ int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs
                            int32_t step, void* ws, size_t ws_bytes, void* stream);
 
 /* gs_render_bwd_adam followed by gs_preprocess of the updated scene for the camera of the
- * next step ([GSG] training loop: pick a view, render, compare, backpropagate, update;
- * the next view is known when this one's update runs).  The chain projects each
+ * next step ([GSG] "Putting every stage together": per step, pick a view, project, tile,
+ * composite, loss, backward, Adam; here the next step's view is picked before this step's
+ * update, which changes no result).  The chain projects each
  * Gaussian for next_cam from the parameters it has just computed, in the same kernel,
  * so they are not read back from memory; the projection, depth order, pair offsets
  * and pair count are those gs_preprocess(scene, next_cam, next_out, next_total_pairs,
