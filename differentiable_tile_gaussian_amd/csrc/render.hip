@@ -16,9 +16,13 @@
 // pairs form chunks of `chunk` pairs that separate blocks walk at the same time.
 //   chunk 0   continues the exact walk from the carried state;
 //   chunk c>0 walks from T = 1 (the local transmittance and colour of the chunk),
-//             stops a pixel once its local T drops below 1e-4 (then the overall T
-//             has too) and drops pixels that an earlier chunk has already
-//             saturated (a per-pixel "first saturating chunk" marker, polled);
+//             stops a pixel once T_first T_local < 1e-4, T_first being its
+//             transmittance after the first segment (it bounds the transmittance in
+//             front of the chunk from above, also in fp32, where every later factor
+//             is at most 1: so the overall T has dropped below 1e-4 by then too, and
+//             the combine finds the stop in this chunk or an earlier one), and drops
+//             pixels that an earlier chunk has already saturated (a per-pixel "first
+//             saturating chunk" marker, polled);
 //   combine   per pixel, chains the chunks: T_front(c+1) = T_front(c) T_c and
 //             colour += T_front(c) C_c, until the product falls below 1e-4;
 //   re-walk   the chunk where that happens is walked again from T_front with the
@@ -476,13 +480,14 @@ __global__ void __launch_bounds__(256) split_chunk_kernel(const float4* __restri
   const int lo = first + int(c) * chunk, hi = min(lo + chunk, n);
   const size_t so = size_t(slot) * 256 + tid;
   const bool done0 = (ws.stl[so] & kFlag) != 0u;
-  PixelFwd s{c == 0 ? ws.st4[so].x : 1.0f, 0.0f, 0.0f, 0.0f, 0u, done0};
+  const float T_first = ws.st4[so].x;   // transmittance after the first segment
+  PixelFwd s{c == 0 ? T_first : 1.0f, 0.0f, 0.0f, 0.0f, 0u, done0};
   if (c == 0)
     fwd_walk<false>(L, splat, vals, start, lo, hi, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f,
                     float(py) + 0.5f, 1.0f, s, nullptr, 0u);
-  else
+  else   // T_first bounds the transmittance in front of this chunk from above
     fwd_walk<true>(L, splat, vals, start, lo, hi, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f,
-                   float(py) + 0.5f, 1.0f, s, ws.sat + size_t(slot) * 256, c);
+                   float(py) + 0.5f, T_first, s, ws.sat + size_t(slot) * 256, c);
   const size_t io = size_t(item) * 256 + tid;
   ws.part4[io] = make_float4(s.T, s.c0, s.c1, s.c2);
   // chunk 0 continues the exact walk: its flag means "stopped here"
