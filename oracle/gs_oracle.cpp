@@ -720,6 +720,121 @@ void smooth_order(int64_t n, const R* depth, const uint8_t* visible, std::vector
 
 // ===================================================================== C ABI
 // Plain entry points for ctypes.  Arrays are planar ([plane][n] or [ch][H][W]).
+
+// ---------------------------------------------------------- density control
+// [GST] density-control slide ("Original 3DGS periodically changes the number of
+// primitives"): the screen-space centre gradient magnitude of every visible
+// observation is accumulated and averaged over the observations; small Gaussians with a
+// large average are cloned (an exact copy), large ones split into two children
+// sampled around the parent with smaller scales, very transparent or oversized ones
+// pruned; an opacity reset clamps opacity to at most a cap.  [GSG] "Densification":
+// split halves shrink by 1.6 and a reshaped Gaussian starts with zero Adam moments.
+// Thresholds the pages leave open are arguments; decisions are taken on the stored
+// logit and log-scales against thresholds rounded once from double (reading R34).
+
+// One step's observations: a Gaussian with tiles > 0 adds |(du, dv)| and 1.
+void densify_accumulate(int64_t n, const uint32_t* tiles, const float* gscreen, float* stats) {
+  for (int64_t i = 0; i < n; ++i) {
+    if (tiles[i] == 0u) continue;
+    const float du = gscreen[i], dv = gscreen[n + i];
+    stats[2 * i] += std::sqrt(du * du + dv * dv);
+    stats[2 * i + 1] += 1.0f;
+  }
+}
+
+enum DensAct { kPrune = 0, kKeep = 1, kClone = 2, kSplit = 3 };
+
+int densify_action(const float* params, int64_t n, int64_t i, const float* stats, float grad_thr, float logit_prune,
+                   float lscale_prune, float lscale_split) {
+  auto P = [&](int k) { return params[k * n + i]; };
+  const float lsmax = std::max(std::max(P(3), P(4)), P(5));
+  if (P(10) < logit_prune || lsmax > lscale_prune) return kPrune;
+  const float cnt = stats[2 * i + 1];
+  const float avg = cnt > 0.0f ? stats[2 * i] / cnt : 0.0f;
+  if (!(avg >= grad_thr)) return kKeep;
+  return lsmax > lscale_split ? kSplit : kClone;
+}
+
+// Mean of split child c of Gaussian i: mean + Rq (s * eps), eps = rand[i][c][0..2] standard
+// normals drawn by the caller, Rq from the normalised quaternion (identity for a zero one).
+void split_child_mean(const float* params, int64_t n, int64_t i, const float* eps, float* out) {
+  auto P = [&](int k) { return params[k * n + i]; };
+  float s[3];
+  for (int k = 0; k < 3; ++k) s[k] = exp_r(P(3 + k));
+  float Rq[3][3] = {{1.f, 0.f, 0.f}, {0.f, 1.f, 0.f}, {0.f, 0.f, 1.f}};
+  const float n2 = ((P(6) * P(6) + P(7) * P(7)) + P(8) * P(8)) + P(9) * P(9);
+  if (n2 > 0.0f) {
+    const float ql = std::sqrt(n2);
+    const float w = P(6) / ql, x = P(7) / ql, y = P(8) / ql, z = P(9) / ql;
+    Rq[0][0] = 1.0f - 2.0f * (y * y + z * z);
+    Rq[0][1] = 2.0f * (x * y - w * z);
+    Rq[0][2] = 2.0f * (x * z + w * y);
+    Rq[1][0] = 2.0f * (x * y + w * z);
+    Rq[1][1] = 1.0f - 2.0f * (x * x + z * z);
+    Rq[1][2] = 2.0f * (y * z - w * x);
+    Rq[2][0] = 2.0f * (x * z - w * y);
+    Rq[2][1] = 2.0f * (y * z + w * x);
+    Rq[2][2] = 1.0f - 2.0f * (x * x + y * y);
+  }
+  const float d[3] = {s[0] * eps[0], s[1] * eps[1], s[2] * eps[2]};
+  for (int r = 0; r < 3; ++r) out[r] = P(r) + ((Rq[r][0] * d[0] + Rq[r][1] * d[1]) + Rq[r][2] * d[2]);
+}
+
+// The new population, in the order: kept Gaussians, clones, first split children, second
+// split children (each group in the order of its parents).  Returns its size; the
+// outputs ([P][cap] planar; stats_out [cap][2], zeroed) are written only if it fits.
+int64_t densify(int64_t n, int deg, const float* params, const float* m, const float* v, const float* stats,
+                const float* rand, float grad_thr, float logit_prune, float lscale_prune, float lscale_split,
+                float lscale_shrink, int reset, float logit_cap, int64_t cap, float* params_out, float* m_out,
+                float* v_out, float* stats_out, int64_t* counts) {
+  const int P = num_planes(deg);
+  std::vector<int> act(static_cast<size_t>(n), 0);
+  int64_t kept = 0, clones = 0, splits = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    act[size_t(i)] = densify_action(params, n, i, stats, grad_thr, logit_prune, lscale_prune, lscale_split);
+    kept += act[size_t(i)] == kKeep || act[size_t(i)] == kClone;
+    clones += act[size_t(i)] == kClone;
+    splits += act[size_t(i)] == kSplit;
+  }
+  counts[0] = kept;
+  counts[1] = clones;
+  counts[2] = splits;
+  const int64_t total = kept + clones + 2 * splits;
+  if (total > cap) return total;
+  // writes Gaussian i as output d; fresh: zero moments; mean / lscale_delta: child changes
+  auto put = [&](int64_t i, int64_t d, bool fresh, const float* mean, bool shrink) {
+    for (int k = 0; k < P; ++k) {
+      float th = params[k * n + i];
+      if (mean && k < 3) th = mean[k];
+      if (shrink && k >= 3 && k < 6) th = th - lscale_shrink;
+      float mo = fresh ? 0.0f : m[k * n + i], vo = fresh ? 0.0f : v[k * n + i];
+      if (reset && k == 10) {
+        th = std::min(th, logit_cap);
+        mo = vo = 0.0f;
+      }
+      params_out[k * cap + d] = th;
+      m_out[k * cap + d] = mo;
+      v_out[k * cap + d] = vo;
+    }
+    stats_out[2 * d] = stats_out[2 * d + 1] = 0.0f;
+  };
+  int64_t dk = 0, dc = kept, ds = kept + clones;
+  for (int64_t i = 0; i < n; ++i) {
+    const int a = act[size_t(i)];
+    if (a == kKeep || a == kClone) put(i, dk++, false, nullptr, false);
+    if (a == kClone) put(i, dc++, true, nullptr, false);
+    if (a == kSplit) {
+      for (int c = 0; c < 2; ++c) {
+        float mean[3];
+        split_child_mean(params, n, i, rand + (2 * i + c) * 3, mean);
+        put(i, ds + c * splits, true, mean, true);
+      }
+      ++ds;
+    }
+  }
+  return total;
+}
+
 extern "C" {
 
 int or_num_planes(int deg) { return num_planes(deg); }
@@ -1010,6 +1125,18 @@ void or_adam_f64(double* params, const double* grads, double* m, double* v, int6
 void or_adam_f32(float* params, const float* grads, float* m, float* v, int64_t n, int deg, const double* lr,
                  double b1, double b2, double eps, int step) {
   adam<float>(params, grads, m, v, n, deg, lr, b1, b2, eps, step);
+}
+
+void or_densify_accumulate_f32(int64_t n, const uint32_t* tiles, const float* gscreen, float* stats) {
+  densify_accumulate(n, tiles, gscreen, stats);
+}
+
+int64_t or_densify_f32(int64_t n, int deg, const float* params, const float* m, const float* v, const float* stats,
+                       const float* rand, float grad_thr, float logit_prune, float lscale_prune, float lscale_split,
+                       float lscale_shrink, int reset, float logit_cap, int64_t cap, float* params_out, float* m_out,
+                       float* v_out, float* stats_out, int64_t* counts) {
+  return densify(n, deg, params, m, v, stats, rand, grad_thr, logit_prune, lscale_prune, lscale_split, lscale_shrink,
+                 reset, logit_cap, cap, params_out, m_out, v_out, stats_out, counts);
 }
 
 }  // extern "C"

@@ -78,6 +78,10 @@ def _declare(L):
     L.or_render_bwd_f64.argtypes = [I64] + [P] * 6 + [P] + [P] * 4
     L.or_flip_risk_f32.argtypes = [I64] + [P] * 6 + [P, P, C.c_double, P, P, P, P]
     L.or_flip_risk_f32.restype = I64
+    L.or_densify_accumulate_f32.argtypes = [I64, P, P, P]
+    F = C.c_float
+    L.or_densify_f32.argtypes = [I64, I32, P, P, P, P, P, F, F, F, F, F, I32, F, I64, P, P, P, P, P]
+    L.or_densify_f32.restype = I64
 
 
 def _p(a):
@@ -327,3 +331,52 @@ def train_step_grads(scene_params, sh_degree, cam, target, lam=0.2):
     out["risk"] = flip_risk(out["pre"], out["vals"], out["ranges"], cam, out["dLdI"].astype(np.float32))
     out["slack"] = rounding_slack(out.pop("mass"), out.pop("count"))
     return out
+
+
+# ---------------------------------------------------------- density control
+def densify_thresholds(prune_opacity, prune_scale, split_scale, opacity_cap, shrink=1.6):
+    """The thresholds in the domains the parameters are stored in, each formed in fp64
+    and rounded once to fp32: logit of the prune opacity and of the reset cap, log of the
+    prune and split scales and of the split shrink factor."""
+    import math
+
+    def logit(p):
+        return math.log(p / (1.0 - p))
+
+    def log_or_inf(x):
+        return math.inf if math.isinf(x) else math.log(x)
+    return dict(logit_prune=np.float32(logit(prune_opacity)), lscale_prune=np.float32(log_or_inf(prune_scale)),
+                lscale_split=np.float32(math.log(split_scale)), logit_cap=np.float32(logit(opacity_cap)),
+                lscale_shrink=np.float32(math.log(shrink)))
+
+
+def densify_accumulate(tiles, gscreen, stats):
+    """One step's observations added to stats [n][2] (a new array): a Gaussian with a
+    nonzero tile count adds the length of its screen-position gradient (du, dv) and 1."""
+    stats = np.array(stats, dtype=np.float32, copy=True)
+    n = stats.shape[0]
+    lib().or_densify_accumulate_f32(n, _p(_c(tiles, np.uint32)), _p(_c(gscreen, np.float32)), _p(stats))
+    return stats
+
+
+def densify(params, m, v, stats, rand, sh_degree, grad_threshold, prune_opacity, prune_scale, split_scale,
+            reset_opacity=False, opacity_cap=0.01, shrink=1.6):
+    """One densification of the planar [P][n] population (see gs_oracle.cpp): returns the
+    new params, m, v ([P][n_new]), zeroed stats [n_new][2] and the counts (kept, cloned,
+    split).  rand [n][2][3]: the standard normals of each Gaussian's two split children."""
+    params = _c(params, np.float32)
+    m = _c(m, np.float32)
+    v = _c(v, np.float32)
+    stats = _c(stats, np.float32)
+    rand = _c(rand, np.float32)
+    P, n = params.shape
+    t = densify_thresholds(prune_opacity, prune_scale, split_scale, opacity_cap, shrink)
+    counts = np.zeros(3, np.int64)
+    args = (n, sh_degree, _p(params), _p(m), _p(v), _p(stats), _p(rand), float(np.float32(grad_threshold)),
+            float(t["logit_prune"]), float(t["lscale_prune"]), float(t["lscale_split"]), float(t["lscale_shrink"]),
+            int(bool(reset_opacity)), float(t["logit_cap"]))
+    total = lib().or_densify_f32(*args, 0, None, None, None, None, _p(counts))
+    po, mo, vo = (np.zeros((P, total), np.float32) for _ in range(3))
+    so = np.zeros((total, 2), np.float32)
+    lib().or_densify_f32(*args, total, _p(po), _p(mo), _p(vo), _p(so), _p(counts))
+    return dict(params=po, m=mo, v=vo, stats=so, counts=counts)
