@@ -60,6 +60,7 @@ def parse():
                     help="FIRST,CHUNK: pairs every tile walks in one block, and the chunk size of the "
                          "parallel walk of longer lists (library defaults if omitted)")
     ap.add_argument("--stage-report", action="store_true", help="also print per-stage times to stderr")
+    ap.add_argument("--no-densify", action="store_true", help="skip the density-control measurement")
     ap.add_argument("--no-fuse-projection", action="store_true",
                     help="project each step's camera in its own preprocess call instead of in the previous "
                          "step's update")
@@ -125,13 +126,55 @@ def run_steps(pl, cams, targets, first, count, timer=None, gs=None, fuse=True):
             pl.pairs = gs.gs_render_bwd_adam_project(pl.params, pl.deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c,
                                                      pl.T, pl.nc, pl.dLdI, pl.gscreen, pl.m, pl.v, pl.lr,
                                                      pl.betas[0], pl.betas[1], pl.eps, pl.t, pl.ws_render,
-                                                     cams[nxt], pl.proj, pl.ws_pre)
+                                                     cams[nxt], pl.proj, pl.ws_pre, pl.dstats)
             pl.projected_for = cams[nxt]
         else:
             gs.gs_render_bwd_adam(pl.params, pl.deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc,
                                   pl.dLdI, pl.gscreen, pl.m, pl.v, pl.lr, pl.betas[0], pl.betas[1], pl.eps, pl.t,
                                   pl.ws_render)
         if timer: timer.mark(s, 5)
+
+
+def measure_densify(pl, cams, targets, first, torch, gs, steps=3):
+    """Density control on the benchmark's population (untimed by the step clock): the
+    statistics of `steps` training steps (added by the projecting update), then one
+    densification (gs_densify: count, then write) timed with HIP events.  The gradient
+    threshold is the 95th percentile of the observed averages, so that about one
+    Gaussian in twenty observed is cloned or split; prune opacity 0.005, prune scale 1,
+    split scale 0.05 (world units)."""
+    pl.enable_density_stats()
+    run_steps(pl, cams, targets, first, steps, gs=gs, fuse=True)
+    st = pl.dstats[:pl.n]
+    seen = st[:, 1] > 0
+    avg = st[seen, 0] / st[seen, 1]
+    thr = float(torch.quantile(avg[:1 << 24], 0.95)) if avg.numel() else 1.0
+    n, deg = pl.n, pl.deg
+    gen = torch.Generator(device=pl.params.device).manual_seed(5)
+    rand = torch.randn((max(n, 1), 2, 3), dtype=torch.float32, device=pl.params.device, generator=gen)
+    ws = gs.workspace(gs.GS_WS_DENSIFY, n=n)
+    thr_args = dict(grad_threshold=thr, prune_opacity=0.005, prune_scale=1.0, split_scale=0.05)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    n_new, counts = gs.gs_densify(pl.params, pl.m, pl.v, pl.dstats, rand, n, deg, ws=ws, **thr_args)
+    ev[1].record()
+    outs = [gs.empty_blocked(n_new, deg) for _ in range(3)]
+    so = torch.empty((max(n_new, 1), 2), dtype=torch.float32, device=pl.params.device)
+    torch.cuda.synchronize()
+    ev[2].record()
+    gs.gs_densify(pl.params, pl.m, pl.v, pl.dstats, rand, n, deg, ws=ws, params_out=outs[0], m_out=outs[1],
+                  v_out=outs[2], stats_out=so, capacity=n_new, **thr_args)
+    end = torch.cuda.Event(enable_timing=True)
+    end.record()
+    torch.cuda.synchronize()
+    count_ms, write_ms = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(end)
+    P = 11 + 3 * (deg + 1) ** 2
+    # the write phase reads theta, m, v of every source Gaussian, its flags and prefix sums,
+    # and a split parent's normals; it writes theta, m, v and the zeroed statistics of every output
+    wbytes = (12 * P + 24) * n + 24 * counts[2] + (12 * P + 8) * n_new
+    return {"steps_of_statistics": steps, "grad_threshold": thr, "n_in": n, "n_out": n_new,
+            "kept_cloned_split": list(counts), "count_ms": round(count_ms, 4), "write_ms": round(write_ms, 4),
+            "write_bytes": wbytes, "write_GBps": round(wbytes / (write_ms / 1000.0) / 1e9, 1)}
 
 
 def count_evals(pl, torch):
@@ -290,6 +333,7 @@ def main():
         ev_f += f
         ev_b += b
     del pl2, params2
+    densify = measure_densify(pl, cams, targets, args.warmup + args.steps, torch, gs) if not args.no_densify else None
     t_fb = (stage[:, 2].sum() + stage[:, 4].sum()) / 1000.0
 
     # roofline of the dominant kernel from its live launch times
@@ -329,6 +373,7 @@ def main():
         "kernel_ms_per_step": {k: round(v, 4) for k, v in sorted(kernel_ms.items(), key=lambda kv: -kv[1])},
         "blend_valu": {"bound": "alu", "peak": VALU_PEAK, "unit": "wave instr/s", "kernels": measured_valu()},
         "roofline": roof,
+        "densify": densify,
         "setup_s": round(setup_s, 2),
     }
     if not args.no_cpu_baseline and args.workload == WORKLOAD_CFG:

@@ -18,8 +18,10 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libgs.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["preprocess.hip", "chain.hip", "scan.hip", "sort.hip", "render.hip", "loss.hip", "adam.hip", "layout.hip", "profile.hip", "gs_api.hip"]
-PER_FILE_FLAGS = {"preprocess.hip": ["-ffp-contract=off"], "chain.hip": ["-ffp-contract=off"]}
+SOURCES = ["preprocess.hip", "chain.hip", "scan.hip", "sort.hip", "render.hip", "loss.hip", "adam.hip", "layout.hip",
+           "densify.hip", "profile.hip", "gs_api.hip"]
+PER_FILE_FLAGS = {"preprocess.hip": ["-ffp-contract=off"], "chain.hip": ["-ffp-contract=off"],
+                  "densify.hip": ["-ffp-contract=off"]}
 ARCH = os.environ.get("GS_OFFLOAD_ARCH", "gfx950")
 
 

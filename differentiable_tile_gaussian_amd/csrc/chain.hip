@@ -143,7 +143,7 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
                                                      const uint32_t* tiles,   // may be np.tiles
                                                      const float* __restrict__ gscreen, float* __restrict__ gparams,
                                                      float* __restrict__ m, float* __restrict__ v, AdamArgs a,
-                                                     NextProj np) {
+                                                     NextProj np, float2* __restrict__ dstats) {
   constexpr int K = (DEG + 1) * (DEG + 1) - 1;
   constexpr int P = 11 + 3 * (K + 1);
   __shared__ float s_gdir[3][3][64];   // view-direction partials of each colour channel
@@ -241,7 +241,15 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
     }
   }
   __syncthreads();   // view-direction partials of the three channels
-  if (wv == 3 && valid) geometry_tail<K, ADAM>(th, gs6, mo, vo, ntile, lane, gb, cam, s_gdir, params, gparams, m, v, a);
+  if (wv == 3 && valid) {
+    if (dstats && ntile != 0u) {   // density statistics: this observation's |(du, dv)| and 1
+      float2 st = dstats[i];
+      st.x += sqrtf(gs6[0] * gs6[0] + gs6[1] * gs6[1]);
+      st.y += 1.0f;
+      dstats[i] = st;
+    }
+    geometry_tail<K, ADAM>(th, gs6, mo, vo, ntile, lane, gb, cam, s_gdir, params, gparams, m, v, a);
+  }
   if (!PROJ) return;
   // ---- projection of the updated Gaussians for the next camera
   Proj g;
@@ -285,19 +293,22 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
 
 template <int DEG, bool ADAM, bool PROJ>
 void launch_chain_deg(float* params, int n, const gs_camera& cam, const uint32_t* tiles, const float* gscreen,
-                      float* gparams, float* m, float* v, const AdamArgs& a, const NextProj& np, hipStream_t s) {
+                      float* gparams, float* m, float* v, const AdamArgs& a, const NextProj& np, float* dstats,
+                      hipStream_t s) {
   GSK_PROF("chain", s);
-  chain_kernel<DEG, ADAM, PROJ><<<div_up(n, 64), 256, 0, s>>>(params, n, cam, tiles, gscreen, gparams, m, v, a, np);
+  chain_kernel<DEG, ADAM, PROJ><<<div_up(n, 64), 256, 0, s>>>(params, n, cam, tiles, gscreen, gparams, m, v, a, np,
+                                                              reinterpret_cast<float2*>(dstats));
 }
 
 template <bool ADAM, bool PROJ>
 void launch_chain_mode(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles, const float* gscreen,
-                       float* gparams, float* m, float* v, const AdamArgs& a, const NextProj& np, hipStream_t s) {
+                       float* gparams, float* m, float* v, const AdamArgs& a, const NextProj& np, float* dstats,
+                       hipStream_t s) {
   switch (deg) {
-    case 0: launch_chain_deg<0, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, s); break;
-    case 1: launch_chain_deg<1, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, s); break;
-    case 2: launch_chain_deg<2, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, s); break;
-    default: launch_chain_deg<3, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, s); break;
+    case 0: launch_chain_deg<0, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, s); break;
+    case 1: launch_chain_deg<1, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, s); break;
+    case 2: launch_chain_deg<2, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, s); break;
+    default: launch_chain_deg<3, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, s); break;
   }
 }
 
@@ -307,22 +318,22 @@ hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_c
                                  const uint32_t* tiles, const float* gscreen, float* gparams, hipStream_t s) {
   if (n == 0) return hipSuccess;
   launch_chain_mode<false, false>(const_cast<float*>(params), n, deg, cam, tiles, gscreen, gparams, nullptr, nullptr,
-                                  AdamArgs{}, NextProj{}, s);
+                                  AdamArgs{}, NextProj{}, nullptr, s);
   return hipGetLastError();
 }
 
 hipError_t launch_chain_adam(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
                              const float* gscreen, float* m, float* v, const AdamArgs& a, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  launch_chain_mode<true, false>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, NextProj{}, s);
+  launch_chain_mode<true, false>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, NextProj{}, nullptr, s);
   return hipGetLastError();
 }
 
 hipError_t launch_chain_adam_project(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
                                      const float* gscreen, float* m, float* v, const AdamArgs& a,
-                                     const NextProj& np, hipStream_t s) {
+                                     const NextProj& np, float* dstats, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  launch_chain_mode<true, true>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, np, s);
+  launch_chain_mode<true, true>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, np, dstats, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_tile_count_total(np.block_tiles, int(div_up(n, 64)), np.total, s);

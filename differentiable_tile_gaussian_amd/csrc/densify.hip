@@ -1,0 +1,210 @@
+// Density control: per-step gradient statistics and one densification (clone, split,
+// prune, opacity reset) of the blocked population.
+//
+// [GST] density-control slide: the screen-space centre gradient magnitude of every visible
+// observation is accumulated and averaged over the observations; small Gaussians with a
+// large average are cloned (an exact copy), large ones split into two children sampled
+// around the parent with smaller scales, very transparent or oversized ones pruned; an
+// opacity reset clamps opacity to at most a cap.  [GSG] "Densification": split halves
+// shrink by 1.6 and a reshaped Gaussian starts with zero Adam moments.
+//
+// The new population is: the kept Gaussians in their order, then the clones, then the
+// first and then the second children of the split ones (each group in the order of its
+// parents).  A Gaussian's destination is a prefix sum of per-Gaussian flags, so the
+// result does not depend on scheduling.  Decisions compare the stored logit and
+// log-scales against thresholds rounded once from double on the host.
+//
+// Compiled without floating-point contraction: the split children's means are the
+// written sequence of fp32 roundings.
+#include "gs_internal.h"
+#include "profile.h"
+
+namespace gsk {
+namespace {
+
+// The std::max / std::min of the C++ library (NaN handling included).
+__device__ inline float max_of(float a, float b) { return a < b ? b : a; }
+__device__ inline float min_of(float a, float b) { return b < a ? b : a; }
+
+enum : uint32_t { kPrune = 0, kKeep = 1, kClone = 2, kSplit = 3 };
+
+__device__ inline uint32_t action(const float* g0, float2 st, const DensifyArgs& a) {
+  const float lsmax = max_of(max_of(g0[3 * kGB], g0[4 * kGB]), g0[5 * kGB]);
+  if (g0[10 * kGB] < a.logit_prune || lsmax > a.lscale_prune) return kPrune;
+  const float avg = st.y > 0.0f ? st.x / st.y : 0.0f;
+  if (!(avg >= a.grad_thr)) return kKeep;
+  return lsmax > a.lscale_split ? kSplit : kClone;
+}
+
+__global__ void __launch_bounds__(256) densify_accumulate_kernel(int n, const uint32_t* __restrict__ tiles,
+                                                                  const float* __restrict__ gscreen,
+                                                                  float2* __restrict__ stats) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n || tiles[i] == 0u) return;
+  const float du = gscreen[size_t(i) * 9], dv = gscreen[size_t(i) * 9 + 1];
+  float2 s = stats[i];
+  s.x += sqrtf(du * du + dv * dv);
+  s.y += 1.0f;
+  stats[i] = s;
+}
+
+// Flags of each Gaussian for the three prefix sums: kept, cloned, split.
+__global__ void __launch_bounds__(256) densify_classify_kernel(const float* __restrict__ params, int n, int P,
+                                                                const float2* __restrict__ stats, DensifyArgs a,
+                                                                uint32_t* __restrict__ fkeep,
+                                                                uint32_t* __restrict__ fclone,
+                                                                uint32_t* __restrict__ fsplit) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t act = action(gaussian_base(params, i, P), stats[i], a);
+  fkeep[i] = act == kKeep || act == kClone;
+  fclone[i] = act == kClone;
+  fsplit[i] = act == kSplit;
+}
+
+// Mean of a split child: mean + Rq (s * eps), Rq from the normalised quaternion (the
+// identity for a zero one), s = exp(log-scales) rounded once from double.
+__device__ inline void child_mean(const float* g0, const float* eps, float* out) {
+  float s[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) s[k] = float(exp(double(g0[(3 + k) * kGB])));
+  float R[3][3] = {{1.f, 0.f, 0.f}, {0.f, 1.f, 0.f}, {0.f, 0.f, 1.f}};
+  const float q0 = g0[6 * kGB], q1 = g0[7 * kGB], q2 = g0[8 * kGB], q3 = g0[9 * kGB];
+  const float n2 = ((q0 * q0 + q1 * q1) + q2 * q2) + q3 * q3;
+  if (n2 > 0.0f) {
+    const float ql = sqrtf(n2);
+    const float w = q0 / ql, x = q1 / ql, y = q2 / ql, z = q3 / ql;
+    R[0][0] = 1.0f - 2.0f * (y * y + z * z);
+    R[0][1] = 2.0f * (x * y - w * z);
+    R[0][2] = 2.0f * (x * z + w * y);
+    R[1][0] = 2.0f * (x * y + w * z);
+    R[1][1] = 1.0f - 2.0f * (x * x + z * z);
+    R[1][2] = 2.0f * (y * z - w * x);
+    R[2][0] = 2.0f * (x * z - w * y);
+    R[2][1] = 2.0f * (y * z + w * x);
+    R[2][2] = 1.0f - 2.0f * (x * x + y * y);
+  }
+  const float d[3] = {s[0] * eps[0], s[1] * eps[1], s[2] * eps[2]};
+#pragma unroll
+  for (int r = 0; r < 3; ++r) out[r] = g0[r * kGB] + ((R[r][0] * d[0] + R[r][1] * d[1]) + R[r][2] * d[2]);
+}
+
+// Writes Gaussian g0 (its theta, m, v rows) as output d: fresh ones get zero moments;
+// a child gets its own mean and the log-scales lowered by the shrink.
+__device__ inline void put(const float* g0, const float* m0, const float* v0, float* params_out, float* m_out,
+                           float* v_out, float2* stats_out, int d, int P, bool fresh, const float* mean,
+                           const DensifyArgs& a) {
+  float* gp = gaussian_base(params_out, d, P);
+  float* gm = gaussian_base(m_out, d, P);
+  float* gv = gaussian_base(v_out, d, P);
+  for (int k = 0; k < P; ++k) {
+    float th = g0[k * kGB];
+    if (mean && k < 3) th = mean[k];
+    if (mean && k >= 3 && k < 6) th = th - a.lscale_shrink;
+    float mo = fresh ? 0.0f : m0[k * kGB], vo = fresh ? 0.0f : v0[k * kGB];
+    if (a.reset && k == 10) {
+      th = min_of(th, a.logit_cap);
+      mo = vo = 0.0f;
+    }
+    gp[k * kGB] = th;
+    gm[k * kGB] = mo;
+    gv[k * kGB] = vo;
+  }
+  stats_out[d] = make_float2(0.0f, 0.0f);
+}
+
+// One thread per source Gaussian; its outputs' places are the prefix sums of the flags
+// (offs_keep[n] = kept, offs_clone[n] = cloned).
+__global__ void __launch_bounds__(256) densify_scatter_kernel(
+    const float* __restrict__ params, const float* __restrict__ m, const float* __restrict__ v, int n, int P,
+    const float* __restrict__ rand, const uint32_t* __restrict__ fkeep, const uint32_t* __restrict__ fclone,
+    const uint32_t* __restrict__ fsplit, const uint32_t* __restrict__ offs_keep,
+    const uint32_t* __restrict__ offs_clone, const uint32_t* __restrict__ offs_split, DensifyArgs a,
+    float* __restrict__ params_out, float* __restrict__ m_out, float* __restrict__ v_out,
+    float2* __restrict__ stats_out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float* g0 = gaussian_base(params, i, P);
+  const float* m0 = gaussian_base(m, i, P);
+  const float* v0 = gaussian_base(v, i, P);
+  const int kept = int(offs_keep[n]), cloned = int(offs_clone[n]), splits = int(offs_split[n]);
+  if (fkeep[i]) put(g0, m0, v0, params_out, m_out, v_out, stats_out, int(offs_keep[i]), P, false, nullptr, a);
+  if (fclone[i])
+    put(g0, m0, v0, params_out, m_out, v_out, stats_out, kept + int(offs_clone[i]), P, true, nullptr, a);
+  if (fsplit[i]) {
+    for (int c = 0; c < 2; ++c) {
+      float mean[3];
+      child_mean(g0, rand + (size_t(2) * i + c) * 3, mean);
+      put(g0, m0, v0, params_out, m_out, v_out, stats_out, kept + cloned + c * splits + int(offs_split[i]), P,
+          true, mean, a);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_densify_accumulate(const uint32_t* tiles, int n, const float* gscreen, float* stats,
+                                     hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  GSK_PROF("densify_accumulate", s);
+  densify_accumulate_kernel<<<div_up(n, 256), 256, 0, s>>>(n, tiles, gscreen, reinterpret_cast<float2*>(stats));
+  return hipGetLastError();
+}
+
+size_t densify_ws_bytes(int64_t n) {
+  const size_t flags = (size_t(n > 0 ? n : 1) * 4 + 255) & ~size_t(255);
+  const size_t offs = (size_t(n + 1) * 4 + 255) & ~size_t(255);
+  return 3 * flags + 3 * offs + 256 + 3 * ((scan_ws_bytes(n) + 255) & ~size_t(255));
+}
+
+hipError_t launch_densify_count(const float* params, int n, int deg, const float* stats, const DensifyArgs& a,
+                                void* ws, hipStream_t s) {
+  DensifyWs w = carve_densify(ws, n);
+  const int P = num_planes(deg);
+  {
+    GSK_PROF("densify_classify", s);
+    densify_classify_kernel<<<div_up(n, 256), 256, 0, s>>>(params, n, P, reinterpret_cast<const float2*>(stats), a,
+                                                           w.flag[0], w.flag[1], w.flag[2]);
+  }
+  hipError_t e = hipGetLastError();
+  for (int k = 0; k < 3 && e == hipSuccess; ++k)
+    e = launch_scan_u32(w.flag[k], w.offs[k], n, w.totals + k, w.scan_ws[k], s);
+  return e;
+}
+
+hipError_t launch_densify_write(const float* params, const float* m, const float* v, int n, int deg,
+                                const float* rand, const DensifyArgs& a, void* ws, float* params_out, float* m_out,
+                                float* v_out, float* stats_out, hipStream_t s) {
+  DensifyWs w = carve_densify(ws, n);
+  GSK_PROF("densify_scatter", s);
+  densify_scatter_kernel<<<div_up(n, 256), 256, 0, s>>>(params, m, v, n, num_planes(deg), rand, w.flag[0],
+                                                        w.flag[1], w.flag[2], w.offs[0], w.offs[1], w.offs[2], a,
+                                                        params_out, m_out, v_out,
+                                                        reinterpret_cast<float2*>(stats_out));
+  return hipGetLastError();
+}
+
+DensifyWs carve_densify(void* ws, int64_t n) {
+  char* p = static_cast<char*>(ws);
+  DensifyWs w;
+  const size_t flags = (size_t(n > 0 ? n : 1) * 4 + 255) & ~size_t(255);
+  const size_t offs = (size_t(n + 1) * 4 + 255) & ~size_t(255);
+  const size_t sw = (scan_ws_bytes(n) + 255) & ~size_t(255);
+  for (int k = 0; k < 3; ++k) {
+    w.flag[k] = reinterpret_cast<uint32_t*>(p);
+    p += flags;
+  }
+  for (int k = 0; k < 3; ++k) {
+    w.offs[k] = reinterpret_cast<uint32_t*>(p);
+    p += offs;
+  }
+  w.totals = reinterpret_cast<uint64_t*>(p);
+  p += 256;
+  for (int k = 0; k < 3; ++k) {
+    w.scan_ws[k] = p;
+    p += sw;
+  }
+  return w;
+}
+
+}  // namespace gsk

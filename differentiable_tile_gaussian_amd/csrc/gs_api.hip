@@ -99,7 +99,7 @@ HostSlot* host_slot() {
   HostSlot& h = slots[dev];
   if (!h.pinned) {
     void* p = nullptr;
-    if (hipHostMalloc(&p, sizeof(uint64_t), hipHostMallocDefault) != hipSuccess) return nullptr;
+    if (hipHostMalloc(&p, 4 * sizeof(uint64_t), hipHostMallocDefault) != hipSuccess) return nullptr;
     if (hipEventCreateWithFlags(&h.copied, hipEventDisableTiming) != hipSuccess) {
       (void)hipHostFree(p);
       return nullptr;
@@ -156,6 +156,7 @@ size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t
     case GS_WS_BIN_SORT: return gsk::bin_sort_ws_bytes(pairs);
     case GS_WS_LOSS: return (W > 0 && H > 0) ? gsk::loss_ws_bytes(H, W) : 0;
     case GS_WS_RENDER: return (W > 0 && H > 0) ? gsk::render_ws_bytes(W, H, pairs) : 0;
+    case GS_WS_DENSIFY: return gsk::densify_ws_bytes(n < 0 ? 0 : n);
     default: return 0;
   }
 }
@@ -346,7 +347,7 @@ int32_t gs_render_bwd_adam_project(float* params, int64_t n, int32_t sh_degree, 
                                    const float* dL_dimg, float* gscreen, float* m, float* v, const float* lr,
                                    double beta1, double beta2, double eps, int32_t step, void* ws, size_t ws_bytes,
                                    const gs_camera* next_cam, gs_proj* next_out, uint32_t* next_total_pairs,
-                                   void* pre_ws, size_t pre_ws_bytes_, void* stream) {
+                                   void* pre_ws, size_t pre_ws_bytes_, float* densify_stats, void* stream) {
   g_err[0] = 0;
   int32_t st;
   const gs_scene scene{n, sh_degree, params};
@@ -381,7 +382,7 @@ int32_t gs_render_bwd_adam_project(float* params, int64_t n, int32_t sh_degree, 
   np.block_tiles = w.block_tiles;
   np.total = w.total64;
   e = gsk::launch_chain_adam_project(params, int(n), sh_degree, *cam, proj->tiles, gscreen, m, v,
-                                     adam_args(lr, beta1, beta2, eps, step), np, s);
+                                     adam_args(lr, beta1, beta2, eps, step), np, densify_stats, s);
   if (e != hipSuccess) return hip_fail(e, "chain_adam_project");
   return finish_preprocess(next_out, int(n), w, next_total_pairs, s);
 }
@@ -437,6 +438,81 @@ int32_t gs_params_from_blocked(const float* blocked, float* planar, int64_t n, i
   if ((st = check_layout(blocked, planar, n, sh_degree)) != GS_OK) return st;
   hipError_t e = gsk::launch_from_blocked(blocked, planar, int(n), gsk::num_planes(sh_degree), as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "from_blocked");
+  return GS_OK;
+}
+
+int32_t gs_densify_accumulate(const gs_proj* proj, int64_t n, const float* gscreen, float* stats, void* stream) {
+  g_err[0] = 0;
+  if (n < 0 || n >= (int64_t(1) << 31)) return fail(GS_ERR_INVALID_ARG, "n out of range");
+  if (n == 0) return GS_OK;
+  if (!proj || !proj->tiles) return fail(GS_ERR_INVALID_ARG, "proj or proj.tiles is null");
+  if (!gscreen || !stats) return fail(GS_ERR_INVALID_ARG, "gscreen or stats is null");
+  const hipError_t e = gsk::launch_densify_accumulate(proj->tiles, int(n), gscreen, stats, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "densify_accumulate");
+  return GS_OK;
+}
+
+int32_t gs_densify(const float* params, const float* m, const float* v, const float* stats, const float* rand,
+                   int64_t n, int32_t sh_degree, double grad_threshold, double prune_opacity, double prune_scale,
+                   double split_scale, int32_t reset_opacity, double opacity_cap, float* params_out, float* m_out,
+                   float* v_out, float* stats_out, int64_t capacity, int64_t* n_out, int64_t* counts, void* ws,
+                   size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (n < 0 || n >= (int64_t(1) << 31)) return fail(GS_ERR_INVALID_ARG, "n out of range");
+  if (sh_degree < 0 || sh_degree > 3) return fail(GS_ERR_UNSUPPORTED, "SH degree must be 0..3");
+  if (!n_out) return fail(GS_ERR_INVALID_ARG, "n_out is null");
+  if (n > 0 && (!params || !m || !v || !stats || !rand)) return fail(GS_ERR_INVALID_ARG, "an input is null");
+  if (!(grad_threshold >= 0.0) || !(prune_opacity >= 0.0 && prune_opacity < 1.0) || !(prune_scale > 0.0) ||
+      !(split_scale > 0.0) || !std::isfinite(split_scale) ||
+      (reset_opacity && !(opacity_cap > 0.0 && opacity_cap < 1.0)))
+    return fail(GS_ERR_INVALID_ARG, "bad density-control thresholds");
+  const bool write = params_out != nullptr;
+  if (write) {
+    if (!m_out || !v_out || !stats_out) return fail(GS_ERR_INVALID_ARG, "an output is null");
+    if (capacity < 0 || gsk::param_floats(capacity, gsk::num_planes(sh_degree)) >= (size_t(1) << 31))
+      return fail(GS_ERR_INVALID_ARG, "capacity out of range");
+    const void* ins[5] = {params, m, v, stats, rand};
+    const void* outs[4] = {params_out, m_out, v_out, stats_out};
+    for (const void* o : outs)
+      for (const void* x : ins)
+        if (o == x) return fail(GS_ERR_INVALID_ARG, "an output is one of the inputs");
+  }
+  const size_t need = gs_workspace_bytes(GS_WS_DENSIFY, n, 0, 0, 0);
+  if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "densify workspace needs %zu bytes", need);
+  gsk::DensifyArgs a;
+  a.grad_thr = float(grad_threshold);
+  a.logit_prune = float(std::log(prune_opacity / (1.0 - prune_opacity)));
+  a.lscale_prune = std::isinf(prune_scale) ? __builtin_inff() : float(std::log(prune_scale));
+  a.lscale_split = float(std::log(split_scale));
+  a.lscale_shrink = float(std::log(1.6));
+  a.logit_cap = reset_opacity ? float(std::log(opacity_cap / (1.0 - opacity_cap))) : 0.0f;
+  a.reset = reset_opacity ? 1 : 0;
+  hipStream_t s = as_stream(stream);
+  uint64_t tot[3] = {0, 0, 0};
+  if (n > 0) {
+    hipError_t e = gsk::launch_densify_count(params, int(n), sh_degree, stats, a, ws, s);
+    if (e != hipSuccess) return hip_fail(e, "densify_count");
+    HostSlot* hs = host_slot();
+    if (!hs) return fail(GS_ERR_HIP, "cannot set up the pinned count buffer");
+    e = hipMemcpyAsync(hs->pinned, gsk::carve_densify(ws, n).totals, 3 * sizeof(uint64_t), hipMemcpyDeviceToHost,
+                       s);
+    if (e != hipSuccess) return hip_fail(e, "densify count copy");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "densify sync");
+    for (int k = 0; k < 3; ++k) tot[k] = hs->pinned[k];
+  }
+  const int64_t total = int64_t(tot[0] + tot[1] + 2 * tot[2]);
+  *n_out = total;
+  if (counts)
+    for (int k = 0; k < 3; ++k) counts[k] = int64_t(tot[k]);
+  if (!write) return GS_OK;
+  if (total > capacity) return fail(GS_ERR_CAPACITY, "the new population (%lld) exceeds capacity (%lld)",
+                                    (long long)total, (long long)capacity);
+  if (n > 0) {
+    const hipError_t e = gsk::launch_densify_write(params, m, v, int(n), sh_degree, rand, a, ws, params_out, m_out,
+                                                   v_out, stats_out, s);
+    if (e != hipSuccess) return hip_fail(e, "densify_write");
+  }
   return GS_OK;
 }
 

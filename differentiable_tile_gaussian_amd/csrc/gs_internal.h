@@ -54,10 +54,11 @@ hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_c
 hipError_t launch_chain_adam(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
                              const float* gscreen, float* m, float* v, const AdamArgs& a, hipStream_t s);
 // The same, then the projection of the updated Gaussians into np (may alias tiles: each
-// Gaussian's count is read before its new record is written) and np's pair count.
+// Gaussian's count is read before its new record is written) and np's pair count; with
+// dstats ([n][2], nullable) also the density statistics of this step's observations.
 hipError_t launch_chain_adam_project(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
                                      const float* gscreen, float* m, float* v, const AdamArgs& a,
-                                     const NextProj& np, hipStream_t s);
+                                     const NextProj& np, float* dstats, hipStream_t s);
 
 // ---- scan.hip: exclusive prefix sum of n u32 values into out[0..n], out[n] = total.
 // The total is also written as u64 to *total64 (device) so that overflow of 32 bits is seen.
@@ -73,6 +74,30 @@ hipError_t launch_depth_order(const gs_proj& proj, int n, void* ws, hipStream_t 
 size_t bin_sort_ws_bytes(uint32_t pairs);
 hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uint32_t pairs, uint32_t* keys,
                            uint32_t* vals, uint32_t* ranges, void* ws, hipStream_t s);
+
+// ---- densify.hip
+// Thresholds in the stored domains (logit, log-scale), rounded once from double.
+struct DensifyArgs {
+  float grad_thr, logit_prune, lscale_prune, lscale_split, lscale_shrink, logit_cap;
+  int reset;
+};
+// Workspace: per-Gaussian flags (kept, cloned, split), their exclusive prefix sums
+// (n + 1 entries each), the three totals (u64) and the scans' block sums.
+struct DensifyWs {
+  uint32_t* flag[3];
+  uint32_t* offs[3];
+  uint64_t* totals;
+  void* scan_ws[3];
+};
+size_t densify_ws_bytes(int64_t n);
+DensifyWs carve_densify(void* ws, int64_t n);
+hipError_t launch_densify_accumulate(const uint32_t* tiles, int n, const float* gscreen, float* stats,
+                                     hipStream_t s);
+hipError_t launch_densify_count(const float* params, int n, int deg, const float* stats, const DensifyArgs& a,
+                                void* ws, hipStream_t s);
+hipError_t launch_densify_write(const float* params, const float* m, const float* v, int n, int deg,
+                                const float* rand, const DensifyArgs& a, void* ws, float* params_out, float* m_out,
+                                float* v_out, float* stats_out, hipStream_t s);
 
 // ---- render.hip
 int32_t set_render_split(int first, int chunk);

@@ -17,11 +17,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgs.so")
 
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_UNSUPPORTED, GS_ERR_HIP = 0, -1, -2, -3, -4
-GS_WS_PREPROCESS, GS_WS_BIN_SORT, GS_WS_LOSS, GS_WS_RENDER = 0, 1, 2, 3
+GS_WS_PREPROCESS, GS_WS_BIN_SORT, GS_WS_LOSS, GS_WS_RENDER, GS_WS_DENSIFY = 0, 1, 2, 3, 4
 GS_TUNE_SPLIT_FIRST, GS_TUNE_SPLIT_CHUNK = 0, 1
 
 EXPORTED = ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
-            "gs_adam_step", "gs_render_bwd_adam", "gs_render_bwd_adam_project", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
+            "gs_adam_step", "gs_render_bwd_adam", "gs_render_bwd_adam_project", "gs_densify_accumulate",
+            "gs_densify", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
             "gs_profile_enable", "gs_profile_query", "gs_param_floats", "gs_params_to_blocked",
             "gs_params_from_blocked", "gs_last_error")
 
@@ -62,8 +63,13 @@ def _load():
     lib.gs_render_bwd_adam.restype = I32
     lib.gs_render_bwd_adam_project.argtypes = [P, I64, I32, P, P, P, U32, P, P, P, P, P, P, P, P, C.c_double,
                                                C.c_double, C.c_double, I32, P, C.c_size_t, P, P, P, P, C.c_size_t,
-                                               P]
+                                               P, P]
     lib.gs_render_bwd_adam_project.restype = I32
+    lib.gs_densify_accumulate.argtypes = [P, I64, P, P, P]
+    lib.gs_densify_accumulate.restype = I32
+    D = C.c_double
+    lib.gs_densify.argtypes = [P, P, P, P, P, I64, I32, D, D, D, D, I32, D, P, P, P, P, I64, P, P, P, C.c_size_t, P]
+    lib.gs_densify.restype = I32
     lib.gs_set_tuning.argtypes = [I32, I64]
     lib.gs_set_tuning.restype = I32
     lib.gs_get_tuning.argtypes = [I32]
@@ -250,9 +256,10 @@ def gs_render_bwd_adam(params, sh_degree, proj: Proj, vals, ranges, total_pairs,
 
 def gs_render_bwd_adam_project(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam: GsCamera, T_final,
                                n_contrib, dL_dimg, gscreen, m, v, lr, beta1, beta2, eps, step, ws,
-                               next_cam: GsCamera, next_proj: Proj, pre_ws, stream=None) -> int:
+                               next_cam: GsCamera, next_proj: Proj, pre_ws, densify_stats=None, stream=None) -> int:
     """gs_render_bwd_adam, then the projection of the updated scene for next_cam into
-    next_proj (may be proj); returns the next pair count (synchronises once)."""
+    next_proj (may be proj); returns the next pair count (synchronises once).  With
+    densify_stats ([n][2]), this step's observations are added to it."""
     for t in (params, m, v):
         _blocked(t, proj.n, sh_degree)
     assert next_proj.n == proj.n
@@ -262,8 +269,28 @@ def gs_render_bwd_adam_project(params, sh_degree, proj: Proj, vals, ranges, tota
         _ptr(params), proj.n, sh_degree, C.byref(proj.struct), _ptr(vals), _ptr(ranges), total_pairs, C.byref(cam),
         _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimg), _ptr(gscreen), _ptr(m), _ptr(v), lr_arr, float(beta1),
         float(beta2), float(eps), int(step), _ptr(ws), ws.numel(), C.byref(next_cam), C.byref(next_proj.struct),
-        C.byref(total), _ptr(pre_ws), pre_ws.numel(), _stream(stream)))
+        C.byref(total), _ptr(pre_ws), pre_ws.numel(), _ptr(densify_stats), _stream(stream)))
     return int(total.value)
+
+
+def gs_densify_accumulate(proj: Proj, gscreen, stats, stream=None):
+    """Adds one step's screen-position gradient lengths and observation counts to stats [n][2]."""
+    _check(_lib.gs_densify_accumulate(C.byref(proj.struct), proj.n, _ptr(gscreen), _ptr(stats), _stream(stream)))
+
+
+def gs_densify(params, m, v, stats, rand, n, sh_degree, grad_threshold, prune_opacity, prune_scale, split_scale,
+               ws, reset_opacity=False, opacity_cap=0.01, params_out=None, m_out=None, v_out=None, stats_out=None,
+               capacity=0, stream=None):
+    """One densification; returns (new count, (kept, cloned, split)).  Without params_out
+    only the counts are computed."""
+    n_out = C.c_int64(0)
+    counts = (C.c_int64 * 3)()
+    _check(_lib.gs_densify(_ptr(params), _ptr(m), _ptr(v), _ptr(stats), _ptr(rand), n, sh_degree,
+                           float(grad_threshold), float(prune_opacity), float(prune_scale), float(split_scale),
+                           1 if reset_opacity else 0, float(opacity_cap), _ptr(params_out), _ptr(m_out),
+                           _ptr(v_out), _ptr(stats_out), int(capacity), C.byref(n_out), counts, _ptr(ws),
+                           ws.numel() if ws is not None else 0, _stream(stream)))
+    return int(n_out.value), tuple(int(c) for c in counts)
 
 
 def gs_set_tuning(key, value):

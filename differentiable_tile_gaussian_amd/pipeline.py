@@ -46,6 +46,7 @@ class Pipeline:
         self.t = 0
         self.pairs = 0
         self.projected_for = None   # set by a fused update that projected for the next step's camera
+        self.dstats = None          # [n][2] density statistics, once enable_density_stats() is called
 
     def planar(self, blocked: torch.Tensor) -> torch.Tensor:
         """[P][n] copy of one of the blocked arrays (params, grads, m, v)."""
@@ -103,18 +104,65 @@ class Pipeline:
         self.pairs = gs.gs_render_bwd_adam_project(self.params, self.deg, self.proj, self.vals, self.ranges,
                                                    self.pairs, cam, self.T, self.nc, self.dLdI, self.gscreen, self.m,
                                                    self.v, self.lr, self.betas[0], self.betas[1], self.eps, self.t,
-                                                   self.ws_render, next_cam, self.proj, self.ws_pre)
+                                                   self.ws_render, next_cam, self.proj, self.ws_pre, self.dstats)
         self.projected_for = next_cam
 
     def step(self, cam: gs.GsCamera, target: torch.Tensor, adam: bool = True, fused: bool = True,
              next_cam: gs.GsCamera = None):
         """One training step; with next_cam (fused Adam only) the update also projects
-        the scene for the camera of the following step."""
+        the scene for the camera of the following step.  With density statistics enabled,
+        the step's observations are added to them (from this step's projection and
+        screen gradients, before any projection for the next camera replaces them)."""
         self.forward(cam)
         if adam and fused:
-            self.backward_adam(cam, target, next_cam)
+            self.backward_adam(cam, target, next_cam)   # accumulates the statistics when projecting
+            if self.dstats is not None and next_cam is None:
+                gs.gs_densify_accumulate(self.proj, self.gscreen, self.dstats)
             return self.loss
         self.backward(cam, target)
+        if self.dstats is not None:
+            gs.gs_densify_accumulate(self.proj, self.gscreen, self.dstats)
         if adam:
             self.adam()
         return self.loss
+
+    # ------------------------------------------------------------ density control
+    def enable_density_stats(self):
+        """Start accumulating each step's screen-position gradient lengths and observation
+        counts (zeroed)."""
+        self.dstats = torch.zeros((max(self.n, 1), 2), dtype=torch.float32, device=self.params.device)
+
+    def densify(self, grad_threshold, prune_opacity, prune_scale, split_scale, reset_opacity=False,
+                opacity_cap=0.01, generator=None):
+        """One densification (gs_densify): the population, its Adam moments and the
+        statistics are replaced by arrays of the new size.  Split children are sampled
+        with standard normals drawn on the device from `generator`.  Returns the counts
+        (kept, cloned, split)."""
+        dev = self.params.device
+        if self.dstats is None:
+            self.enable_density_stats()
+        rand = torch.randn((max(self.n, 1), 2, 3), dtype=torch.float32, device=dev, generator=generator)
+        ws = gs.workspace(gs.GS_WS_DENSIFY, n=self.n, device=dev)
+        args = (self.params, self.m, self.v, self.dstats, rand, self.n, self.deg, grad_threshold, prune_opacity,
+                prune_scale, split_scale, ws)
+        n_new, _ = gs.gs_densify(*args, reset_opacity=reset_opacity, opacity_cap=opacity_cap)
+        params = gs.empty_blocked(n_new, self.deg, dev, zero=True)
+        m = gs.empty_blocked(n_new, self.deg, dev, zero=True)
+        v = gs.empty_blocked(n_new, self.deg, dev, zero=True)
+        stats = torch.zeros((max(n_new, 1), 2), dtype=torch.float32, device=dev)
+        n_chk, counts = gs.gs_densify(*args, reset_opacity=reset_opacity, opacity_cap=opacity_cap, params_out=params,
+                                      m_out=m, v_out=v, stats_out=stats, capacity=n_new)
+        assert n_chk == n_new
+        self.params, self.m, self.v, self.dstats = params, m, v, stats
+        self._resize(n_new)
+        return counts
+
+    def _resize(self, n):
+        """Buffers sized by the Gaussian count, after the population changed."""
+        dev = self.params.device
+        self.n = n
+        self.proj = gs.Proj(n, dev)
+        self.ws_pre = gs.workspace(gs.GS_WS_PREPROCESS, n=n, device=dev)
+        self.gscreen = torch.empty((max(n, 1), 9), dtype=torch.float32, device=dev)
+        self.grads = gs.empty_blocked(n, self.deg, dev, zero=True)
+        self.projected_for = None

@@ -226,15 +226,18 @@ int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs
  * and pair count are those gs_preprocess(scene, next_cam, next_out, next_total_pairs,
  * pre_ws) would produce from the updated params, bit for bit.  next_out may be proj
  * itself (each Gaussian's tile count is read before its new record is written).
- * pre_ws: gs_workspace_bytes(GS_WS_PREPROCESS, n, 0, 0, 0) bytes.  Waits for the next
- * pair count as gs_preprocess does; errors as gs_render_bwd_adam and gs_preprocess. */
+ * pre_ws: gs_workspace_bytes(GS_WS_PREPROCESS, n, 0, 0, 0) bytes.  densify_stats (device
+ * float [n][2], nullable): when given, this step's observations are added to it as
+ * gs_densify_accumulate would (from this step's tile counts, before they are replaced).
+ * Waits for the next pair count as gs_preprocess does; errors as gs_render_bwd_adam and
+ * gs_preprocess. */
 int32_t gs_render_bwd_adam_project(float* params, int64_t n, int32_t sh_degree, const gs_proj* proj,
                                    const uint32_t* vals, const uint32_t* ranges, uint32_t total_pairs,
                                    const gs_camera* cam, const float* T_final, const uint32_t* n_contrib,
                                    const float* dL_dimg, float* gscreen, float* m, float* v, const float* lr,
                                    double beta1, double beta2, double eps, int32_t step, void* ws, size_t ws_bytes,
                                    const gs_camera* next_cam, gs_proj* next_out, uint32_t* next_total_pairs,
-                                   void* pre_ws, size_t pre_ws_bytes, void* stream);
+                                   void* pre_ws, size_t pre_ws_bytes, float* densify_stats, void* stream);
 
 /* Layout of the per-Gaussian parameter arrays (see the blocked layout above).
  * gs_param_floats: floats in a blocked array for n Gaussians (0 for bad arguments).
@@ -246,7 +249,43 @@ int32_t gs_params_to_blocked(const float* planar, float* blocked, int64_t n, int
 int32_t gs_params_from_blocked(const float* blocked, float* planar, int64_t n, int32_t sh_degree, void* stream);
 
 /* Workspace sizes, in bytes, for the calls that take one. */
-enum { GS_WS_PREPROCESS = 0, GS_WS_BIN_SORT = 1, GS_WS_LOSS = 2, GS_WS_RENDER = 3 };
+/* Density control, statistics ([GST] density-control slide: screen-space centre gradient
+ * magnitudes accumulated per visible observation).  After a step's backward (gs_render_bwd or
+ * the fused calls), for every Gaussian with proj->tiles[i] > 0:
+ *   stats[i][0] += |(du, dv)| (from gscreen[i][0..1]);  stats[i][1] += 1.
+ * stats: device float [n][2], updated in place (zero it when a population starts).
+ * gscreen, proj: as the backward left them.  Enqueues only. */
+int32_t gs_densify_accumulate(const gs_proj* proj, int64_t n, const float* gscreen, float* stats, void* stream);
+
+/* Density control, one densification ([GST] density-control slide; [GSG] "Densification").
+ * For Gaussian i, with average a = stats[i][0] / stats[i][1] (0 when never observed) and s
+ * its largest scale:
+ *   pruned   if opacity < prune_opacity or s > prune_scale;
+ *   else, if a >= grad_threshold: split if s > split_scale, else cloned;
+ *   else kept.
+ * The comparisons are taken on the stored logit and log-scales against the thresholds'
+ * logit / log formed in double and rounded once to float (a prune_scale of +infinity
+ * prunes by opacity only).  New population: the kept and cloned Gaussians in their order,
+ * then the clones (exact copies), then the first and then the second children of the split
+ * ones; the child of Gaussian i with c = 0, 1 has mean + Rq (s * eps), eps = rand[i][c][0..2]
+ * (caller-drawn standard normals; Rq from the normalised quaternion, the identity for a zero
+ * one; s the scales exp(log-scales)) and log-scales lowered by ln 1.6 ([GSG]: halves shrink by
+ * 1.6), everything else copied.  Clones and children start with zero m and v; kept Gaussians
+ * keep theirs.  With reset_opacity, every output's logit becomes min(logit, logit(opacity_cap))
+ * and its opacity moments zero.  stats_out is zeroed for the outputs.
+ * params, m, v: blocked layout for n; stats [n][2]; rand [n][2][3] (device).  Outputs: blocked
+ * for capacity Gaussians (padding untouched), stats_out [capacity][2], none overlapping an
+ * input.  *n_out (host) receives the new count and counts (host int64[3], nullable) the numbers
+ * kept, cloned and split; with params_out == NULL only these are computed.  GS_ERR_CAPACITY
+ * (nothing written) if the new count exceeds capacity.  ws: gs_workspace_bytes(GS_WS_DENSIFY,
+ * n, 0, 0, 0).  Waits for the counts (one copy to a pinned host word). */
+int32_t gs_densify(const float* params, const float* m, const float* v, const float* stats, const float* rand,
+                   int64_t n, int32_t sh_degree, double grad_threshold, double prune_opacity, double prune_scale,
+                   double split_scale, int32_t reset_opacity, double opacity_cap, float* params_out, float* m_out,
+                   float* v_out, float* stats_out, int64_t capacity, int64_t* n_out, int64_t* counts, void* ws,
+                   size_t ws_bytes, void* stream);
+
+enum { GS_WS_PREPROCESS = 0, GS_WS_BIN_SORT = 1, GS_WS_LOSS = 2, GS_WS_RENDER = 3, GS_WS_DENSIFY = 4 };
 size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H);
 
 /* Tuning of the blend's work split (process-wide; set before sizing workspaces, and not between a

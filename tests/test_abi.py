@@ -83,11 +83,28 @@ def test_argument_errors_without_gpu(gs):
     def bwd_project(next_cam, next_total, pre_ws, pre_bytes):
         return L.gs_render_bwd_adam_project(1, 10, 0, C.byref(proj), 1, 1, 100, C.byref(cam), 1, 1, 1, 1, 1, 1, lr,
                                             0.9, 0.999, 1e-8, 1, 1, 1 << 40, next_cam, C.byref(proj), next_total,
-                                            pre_ws, pre_bytes, None)
+                                            pre_ws, pre_bytes, None, None)
     assert bwd_project(None, C.byref(nt), 1, 1 << 40) == gs.GS_ERR_INVALID_ARG
     assert bwd_project(C.byref(nxt), None, 1, 1 << 40) == gs.GS_ERR_INVALID_ARG
     assert bwd_project(C.byref(nxt), C.byref(nt), None, 0) == gs.GS_ERR_CAPACITY
     assert "preprocess workspace" in gs.gs_last_error()
+    # density control: arguments are checked before anything is enqueued
+    n_out = C.c_int64(-1)
+    big = 1 << 40
+
+    def densify(n_ptr, thr=(2e-4, 0.005, 5.0, 0.05), outs=(None, None, None, None), ws=1, ws_bytes=big):
+        return L.gs_densify(1, 2, 3, 4, 5, 10, 0, *thr, 0, 0.01, *outs, 100, n_ptr, None, ws, ws_bytes, None)
+    assert densify(None) == gs.GS_ERR_INVALID_ARG                                  # n_out
+    assert densify(C.byref(n_out), thr=(2e-4, 1.5, 5.0, 0.05)) == gs.GS_ERR_INVALID_ARG   # opacity >= 1
+    assert densify(C.byref(n_out), thr=(2e-4, 0.005, 5.0, 0.0)) == gs.GS_ERR_INVALID_ARG  # split scale 0
+    assert densify(C.byref(n_out), thr=(-1.0, 0.005, 5.0, 0.05)) == gs.GS_ERR_INVALID_ARG # negative threshold
+    assert densify(C.byref(n_out), outs=(1, 7, 8, 9)) == gs.GS_ERR_INVALID_ARG          # output aliases params
+    assert "output" in gs.gs_last_error()
+    assert densify(C.byref(n_out), ws=None, ws_bytes=0) == gs.GS_ERR_CAPACITY
+    assert "densify workspace" in gs.gs_last_error()
+    assert n_out.value == -1                                                          # nothing written
+    assert L.gs_densify_accumulate(C.byref(proj), 10, None, 1, None) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_densify_accumulate(None, 0, None, None, None) == gs.GS_OK            # empty: nothing to do
     # tuning values are checked
     assert L.gs_set_tuning(gs.GS_TUNE_SPLIT_CHUNK, 6) == gs.GS_ERR_INVALID_ARG
     assert L.gs_set_tuning(77, 1024) == gs.GS_ERR_INVALID_ARG
@@ -102,6 +119,8 @@ def test_workspace_sizes_grow_with_the_problem(gs):
     small = gs.gs_workspace_bytes(gs.GS_WS_LOSS, 0, 0, 128, 128)
     assert gs.gs_workspace_bytes(gs.GS_WS_LOSS, 0, 0, 1920, 1080) > small >= 8
     assert gs.gs_workspace_bytes(gs.GS_WS_PREPROCESS, 6_000_000, 0, 0, 0) > 0
+    # density control: three flags and three prefix sums per Gaussian
+    assert gs.gs_workspace_bytes(gs.GS_WS_DENSIFY, 1_000_000, 0, 0, 0) >= 24 * 1_000_000
     assert gs.gs_workspace_bytes(99, 1, 1, 1, 1) == 0
 
 
