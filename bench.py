@@ -153,17 +153,22 @@ def measure_densify(pl, cams, targets, first, torch, gs, steps=3):
     rand = torch.randn((max(n, 1), 2, 3), dtype=torch.float32, device=pl.params.device, generator=gen)
     ws = gs.workspace(gs.GS_WS_DENSIFY, n=n)
     thr_args = dict(grad_threshold=thr, prune_opacity=0.005, prune_scale=1.0, split_scale=0.05)
+    n_new, counts = gs.gs_densify(pl.params, pl.m, pl.v, pl.dstats, rand, n, deg, ws=ws, **thr_args)
+    outs = [gs.empty_blocked(n_new, deg) for _ in range(3)]
+    so = torch.empty((max(n_new, 1), 2), dtype=torch.float32, device=pl.params.device)
+
+    def write():
+        gs.gs_densify(pl.params, pl.m, pl.v, pl.dstats, rand, n, deg, ws=ws, params_out=outs[0], m_out=outs[1],
+                      v_out=outs[2], stats_out=so, capacity=n_new, **thr_args)
+    write()   # untimed: the kernels' first launch (the inputs are not modified, so it can be repeated)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     torch.cuda.synchronize()
     ev[0].record()
-    n_new, counts = gs.gs_densify(pl.params, pl.m, pl.v, pl.dstats, rand, n, deg, ws=ws, **thr_args)
+    gs.gs_densify(pl.params, pl.m, pl.v, pl.dstats, rand, n, deg, ws=ws, **thr_args)
     ev[1].record()
-    outs = [gs.empty_blocked(n_new, deg) for _ in range(3)]
-    so = torch.empty((max(n_new, 1), 2), dtype=torch.float32, device=pl.params.device)
     torch.cuda.synchronize()
     ev[2].record()
-    gs.gs_densify(pl.params, pl.m, pl.v, pl.dstats, rand, n, deg, ws=ws, params_out=outs[0], m_out=outs[1],
-                  v_out=outs[2], stats_out=so, capacity=n_new, **thr_args)
+    write()
     end = torch.cuda.Event(enable_timing=True)
     end.record()
     torch.cuda.synchronize()
