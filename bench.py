@@ -61,6 +61,8 @@ def parse():
                          "parallel walk of longer lists (library defaults if omitted)")
     ap.add_argument("--stage-report", action="store_true", help="also print per-stage times to stderr")
     ap.add_argument("--no-densify", action="store_true", help="skip the density-control measurement")
+    ap.add_argument("--fixed-sums", action="store_true",
+                    help="sum the backward's gradients in fixed point (reproducible; gs_set_grad_sums)")
     ap.add_argument("--no-fuse-projection", action="store_true",
                     help="project each step's camera in its own preprocess call instead of in the previous "
                          "step's update")
@@ -292,6 +294,8 @@ def main():
         gs.gs_set_tuning(gs.GS_TUNE_SPLIT_CHUNK, chunk)
     split = [gs.gs_get_tuning(gs.GS_TUNE_SPLIT_FIRST), gs.gs_get_tuning(gs.GS_TUNE_SPLIT_CHUNK)]
     fuse = not args.no_fuse_projection
+    if args.fixed_sums:
+        gs.gs_set_grad_sums(gs.GS_GRAD_SUMS_FIXED)
     t_setup = time.perf_counter()
     wl = scenes.CONFIGS[args.workload]()
     cams = [gs.make_camera(c) for c in wl.cameras]
@@ -370,7 +374,7 @@ def main():
         "config": {"workload": wl.name, "gaussians": n, "sh_degree": deg, "image": [cam0.width, cam0.height],
                    "cameras": len(cams), "step": ("sort+fwd+loss+bwd+chain+adam+projection of the next camera (fused; one projection per step)"
                             if fuse else "preprocess+sort+fwd+loss+bwd+chain+adam (fused)"), "parallelism": "none",
-                   "blend_split": split},
+                   "blend_split": split, "grad_sums": "fixed" if args.fixed_sums else "float"},
         "evals_per_s": round((ev_f + ev_b) / t_fb, 1),
         "evals_per_step": {"fwd": ev_f // args.steps, "bwd": ev_b // args.steps},
         "stage_ms": {k: round(float(stage[:, i].mean()), 4) for i, k in enumerate(StageTimer.NAMES)},

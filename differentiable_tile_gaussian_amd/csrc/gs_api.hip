@@ -1,5 +1,6 @@
 // The C ABI declared in include/gs.h: argument checks, workspace carving and the
 // launches of the kernels in the other translation units.  No call allocates.
+#include <atomic>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -9,6 +10,9 @@
 #include "profile.h"
 
 namespace {
+
+// Gradient-sum mode of the backward blend (gs_set_grad_sums), for the whole process.
+std::atomic<int> g_fixed_sums{0};
 
 thread_local char g_err[512] = "";
 
@@ -114,6 +118,16 @@ HostSlot* host_slot() {
 extern "C" {
 
 const char* gs_last_error(void) { return g_err; }
+
+int32_t gs_set_grad_sums(int32_t mode) {
+  g_err[0] = 0;
+  if (mode != GS_GRAD_SUMS_FLOAT && mode != GS_GRAD_SUMS_FIXED)
+    return fail(GS_ERR_INVALID_ARG, "unknown gradient-sum mode %d", mode);
+  g_fixed_sums = mode == GS_GRAD_SUMS_FIXED ? 1 : 0;
+  return GS_OK;
+}
+
+int32_t gs_get_grad_sums(void) { return g_fixed_sums ? GS_GRAD_SUMS_FIXED : GS_GRAD_SUMS_FLOAT; }
 
 int32_t gs_set_tuning(int32_t key, int64_t value) {
   g_err[0] = 0;
@@ -281,7 +295,7 @@ int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t
   hipStream_t s = as_stream(stream);
   const int n = int(scene->n);
   hipError_t e = gsk::launch_render_bwd(*proj, n, vals, ranges, *cam, total_pairs, T_final, n_contrib, dL_dimg,
-                                        gscreen, ws, s);
+                                        gscreen, ws, g_fixed_sums != 0, s);
   if (e != hipSuccess) return hip_fail(e, "render_bwd");
   e = gsk::launch_preprocess_bwd(scene->params, n, scene->sh_degree, *cam, proj->tiles, gscreen, gparams, s);
   if (e != hipSuccess) return hip_fail(e, "preprocess_bwd");
@@ -333,7 +347,7 @@ int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "render workspace needs %zu bytes", need);
   hipStream_t s = as_stream(stream);
   hipError_t e = gsk::launch_render_bwd(*proj, int(n), vals, ranges, *cam, total_pairs, T_final, n_contrib,
-                                        dL_dimg, gscreen, ws, s);
+                                        dL_dimg, gscreen, ws, g_fixed_sums != 0, s);
   if (e != hipSuccess) return hip_fail(e, "render_bwd");
   e = gsk::launch_chain_adam(params, int(n), sh_degree, *cam, proj->tiles, gscreen, m, v,
                              adam_args(lr, beta1, beta2, eps, step), s);
@@ -368,7 +382,7 @@ int32_t gs_render_bwd_adam_project(float* params, int64_t n, int32_t sh_degree, 
     return fail(GS_ERR_CAPACITY, "preprocess workspace needs %zu bytes", need_pre);
   hipStream_t s = as_stream(stream);
   hipError_t e = gsk::launch_render_bwd(*proj, int(n), vals, ranges, *cam, total_pairs, T_final, n_contrib,
-                                        dL_dimg, gscreen, ws, s);
+                                        dL_dimg, gscreen, ws, g_fixed_sums != 0, s);
   if (e != hipSuccess) return hip_fail(e, "render_bwd");
   PreWs w = carve_pre(pre_ws, n);
   gsk::NextProj np;

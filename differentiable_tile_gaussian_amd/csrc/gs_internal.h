@@ -107,10 +107,12 @@ size_t render_ws_bytes(int W, int H, uint32_t pairs);
 hipError_t launch_render_fwd(const gs_proj& proj, const uint32_t* vals, const uint32_t* ranges,
                              const gs_camera& cam, uint32_t pairs, float* rgb, float* T_final,
                              uint32_t* n_contrib, void* ws, hipStream_t s);
+// fixed: gradient sums in fixed point (reproducible bit for bit); gscreen holds the float
+// partials on return either way.
 hipError_t launch_render_bwd(const gs_proj& proj, int n, const uint32_t* vals, const uint32_t* ranges,
                              const gs_camera& cam, uint32_t pairs, const float* T_final,
                              const uint32_t* n_contrib, const float* dL_dimg, float* gscreen, void* ws,
-                             hipStream_t s);
+                             bool fixed, hipStream_t s);
 
 // ---- loss.hip
 size_t loss_ws_bytes(int H, int W);

@@ -702,6 +702,24 @@ __device__ inline void wave_sum9(float* v) {
   v[8] += dpp<kQuadXor1>(v[8]);
 }
 
+// Fixed-point gradient sums ([GSG] "Making the parallel sums exact": integers add in any
+// order, so the sums are reproducible bit for bit; a blame is multiplied by 16384 and
+// rounded, the second moments of a large footprint divided by a size factor first).
+constexpr float kFixedUnit = 16384.0f;
+
+// Size factor of a pair's footprint: 1 + the trace of its screen covariance (the inverse
+// of the conic; the trace bounds the largest eigenvalue within a factor 2).  Explicit
+// roundings, so that the walk and the decode compute the identical value; 1 when the
+// conic is not positive definite.
+__device__ inline float fixed_size_factor(float A, float B, float C) {
+  const float det = __fsub_rn(__fmul_rn(A, C), __fmul_rn(B, B));
+  const float tr = __fdiv_rn(__fadd_rn(A, C), det);
+  return (det > 0.0f && tr >= 0.0f && tr < 1e30f) ? __fadd_rn(1.0f, tr) : 1.0f;
+}
+
+// Clamped to +-1e9 (the pages' bound) and rounded to the nearest integer.
+__device__ inline int to_fixed(float x) { return int(rintf(fminf(fmaxf(x, -1e9f), 1e9f))); }
+
 // The backward stages batches of kBwdBatch pairs (half the forward's, so that more
 // blocks fit in a CU's LDS: 0.61 -> 0.56 ms on the 6M-Gaussian 1080p step; 64 is no faster).
 constexpr int kBwdBatch = 128;
@@ -712,16 +730,19 @@ struct BwdLds {
   float c[2][kBwdBatch];      // b
   uint32_t id[2][kBwdBatch];
   uint32_t m[2][kBwdBatch];   // quadrant masks
+  float inv_f[2][kBwdBatch];  // fixed-point sums: 1 / the pair's size factor
   float acc[kBwdBatch][9];    // per-entry sums over the block's waves (entry-major, as gscreen)
   uint16_t list[4][kBwdBatch + 4];
   uint32_t top;
 };
 
+template <bool FIXED>
 __device__ inline void stage_bwd(const float4* __restrict__ splat, uint32_t g, float ox, float oy, float4& a,
-                                 float4& b, float& c, uint32_t& m) {
+                                 float4& b, float& c, uint32_t& m, float& inv_f) {
   const float4 r0 = splat[3 * g], r1 = splat[3 * g + 1], r2 = splat[3 * g + 2];
   stage_coeffs(r0, r1, a, b);
   c = r2.x;
+  if (FIXED) inv_f = __fdiv_rn(1.0f, fixed_size_factor(r0.z, r0.w, r1.x));
   m = ellipse_mask(quad_mask(r0.x, r0.y, r2.y, r2.z, ox, oy), r0.x, r0.y, r0.z, r0.w, r1.x, r2.w, ox, oy);
 }
 
@@ -732,10 +753,16 @@ struct PixelBwd {
 };
 
 // Walks pairs top-1 .. lo (top per pixel, at most hi) of a tile list, adding
-// each pair's partials to gscreen.  Must be called by all 256 threads.
+// each pair's partials to gscreen.  Must be called by all 256 threads.  With FIXED the
+// sums are integers ([GSG] "Making the parallel sums exact"): every wave-reduced moment,
+// times `unit` (16384 times the loss's element count, so that the unit is that of the
+// summed loss) and, for the three second moments, the pair's 1 / size factor, is rounded
+// to an i32 and added with integer atomics, in LDS and then into gscreen, whose words then
+// hold i32 moment sums for the decode kernel; the order of the additions does not matter.
+template <bool FIXED>
 __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint32_t* __restrict__ vals,
                          uint32_t start, int lo, float ox, float oy, float fx, float fy, PixelBwd& s,
-                         float* __restrict__ gscreen) {
+                         float* __restrict__ gscreen, float unit) {
   const int tid = threadIdx.x;
   const int lane = __lane_id();
   if (tid == 0) L.top = 0u;
@@ -754,13 +781,14 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
   if (tid < kBwdBatch) {
     const int blo = max(hi - kBwdBatch, lo);
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = make_float4(0.f, kNoOpacity, 0.f, 0.f);
-    float c = 0.f;
+    float c = 0.f, f = 1.f;
     uint32_t g = 0, m = 0u;
     if (blo + tid < hi) {
       g = vals[start + uint32_t(blo + tid)];
-      stage_bwd(splat, g, ox, oy, a, b, c, m);
+      stage_bwd<FIXED>(splat, g, ox, oy, a, b, c, m, f);
     }
     L.a[0][tid] = a; L.b[0][tid] = b; L.c[0][tid] = c; L.id[0][tid] = g; L.m[0][tid] = m;
+    if (FIXED) L.inv_f[0][tid] = f;
   }
   __syncthreads();
   uint16_t* list = L.list[tid >> 6];
@@ -769,11 +797,11 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
     const int blo = max(hi - kBwdBatch, lo);
     const int nhi = blo, nlo = max(nhi - kBwdBatch, lo);
     float4 na = make_float4(0.f, 0.f, 0.f, 0.f), nb = make_float4(0.f, kNoOpacity, 0.f, 0.f);
-    float ncr = 0.f;
+    float ncr = 0.f, nf = 1.f;
     uint32_t ng = 0, nm = 0u;
     if (tid < kBwdBatch && nlo + tid < nhi) {
       ng = vals[start + uint32_t(nlo + tid)];
-      stage_bwd(splat, ng, ox, oy, na, nb, ncr, nm);
+      stage_bwd<FIXED>(splat, ng, ox, oy, na, nb, ncr, nm, nf);
     }
     // entries 0 .. etop of the batch whose quadrant bit is set, last to first
     const int etop = min(hi, wave_top) - 1 - blo;
@@ -817,15 +845,24 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
       s.S2 += cb * w;
       s.T = Tn;
       wave_sum9(v);
-      if ((lane & 7) == 0) atomicAdd(&L.acc[e][lane >> 3], v[0]);
-      if (lane == 0) atomicAdd(&L.acc[e][8], v[8]);
+      if (FIXED) {
+        int* acc = reinterpret_cast<int*>(&L.acc[e][0]);
+        const int k = lane >> 3;
+        const float sc = (k >= 2 && k <= 4) ? unit * L.inv_f[buf][e] : unit;
+        if ((lane & 7) == 0) atomicAdd(&acc[k], to_fixed(v[0] * sc));
+        if (lane == 0) atomicAdd(&acc[8], to_fixed(v[8] * unit));
+      } else {
+        if ((lane & 7) == 0) atomicAdd(&L.acc[e][lane >> 3], v[0]);
+        if (lane == 0) atomicAdd(&L.acc[e][8], v[8]);
+      }
     }
     if (tid < kBwdBatch && nlo < nhi) {
       L.a[buf ^ 1][tid] = na; L.b[buf ^ 1][tid] = nb; L.c[buf ^ 1][tid] = ncr; L.id[buf ^ 1][tid] = ng;
       L.m[buf ^ 1][tid] = nm;
+      if (FIXED) L.inv_f[buf ^ 1][tid] = nf;
     }
     __syncthreads();
-    if (tid < hi - blo) {
+    if (!FIXED && tid < hi - blo) {
       // e = (A dx^2 + C dy^2) / 2 + B dx dy: du = -(A M_x + B M_y), dv = -(B M_x + C M_y),
       // dA = M_xx / 2, dB = M_xy, dC = M_yy / 2 for the moments M of dL/de
       // (the unscaled conic back from the staged coefficients: a' = -log2(e) A / 2, ...)
@@ -840,17 +877,23 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
       const float so = L.acc[tid][5];
       if (so != 0.0f) L.acc[tid][5] = so * fast_exp2(-L.b[buf][tid].y);
     }
-    __syncthreads();
+    if (!FIXED) __syncthreads();
     {
       // one thread per (entry, partial) in gscreen's own order, so that the atomics of a
       // wave land on a few cache lines (about 7 entries of 36 bytes) instead of 64
-      const float* flat = &L.acc[0][0];
+      float* flat = &L.acc[0][0];
       const int cnt9 = (hi - blo) * 9;
       for (int idx = tid; idx < cnt9; idx += kBlock) {
         const int e = idx / 9;
-        const float x = flat[idx];
-        if (x != 0.0f) atomicAdd(&gscreen[size_t(L.id[buf][e]) * 9 + (idx - 9 * e)], x);
-        (&L.acc[0][0])[idx] = 0.0f;
+        float* dst = &gscreen[size_t(L.id[buf][e]) * 9 + (idx - 9 * e)];
+        if (FIXED) {
+          const int x = __float_as_int(flat[idx]);
+          if (x != 0) atomicAdd(reinterpret_cast<int*>(dst), x);
+        } else {
+          const float x = flat[idx];
+          if (x != 0.0f) atomicAdd(dst, x);
+        }
+        flat[idx] = 0.0f;
       }
     }
     __syncthreads();
@@ -871,9 +914,11 @@ struct BwdArgs {
   const float* dL_dimg;
   int n;
   float* gscreen;
+  float unit;   // fixed-point sums: 16384 times the loss's element count
 };
 
 // A tile's first segment (the whole list for tiles that were not split).
+template <bool FIXED>
 __device__ void bwd_tile(BwdLds& L, const BwdArgs& A, const SplitWs& ws, int tile) {
   const float4* __restrict__ splat = A.splat;
   const uint32_t* __restrict__ vals = A.vals;
@@ -907,10 +952,12 @@ __device__ void bwd_tile(BwdLds& L, const BwdArgs& A, const SplitWs& ws, int til
       s.top = int(n_contrib[p]);
     }
   }
-  bwd_walk(L, splat, vals, start, 0, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f, float(py) + 0.5f, s, gscreen);
+  bwd_walk<FIXED>(L, splat, vals, start, 0, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f, float(py) + 0.5f,
+                  s, gscreen, A.unit);
 }
 
 // One chunk of a split tile.
+template <bool FIXED>
 __device__ void bwd_chunk(BwdLds& L, const BwdArgs& A, const SplitWs& ws, uint32_t item) {
   const float4* __restrict__ splat = A.splat;
   const uint32_t* __restrict__ vals = A.vals;
@@ -949,7 +996,8 @@ __device__ void bwd_chunk(BwdLds& L, const BwdArgs& A, const SplitWs& ws, uint32
       s.top = hi;
     }
   }
-  bwd_walk(L, splat, vals, start, lo, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f, float(py) + 0.5f, s, gscreen);
+  bwd_walk<FIXED>(L, splat, vals, start, lo, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f, float(py) + 0.5f,
+                  s, gscreen, A.unit);
 }
 
 // The backward of every tile's first segment and of every chunk of the split tiles,
@@ -957,16 +1005,45 @@ __device__ void bwd_chunk(BwdLds& L, const BwdArgs& A, const SplitWs& ws, uint32
 // after them the chunks, which are independent of the first segments (each starts
 // from the state the forward left at its end) and so fill the CUs that the last
 // long first segments leave idle.
+template <bool FIXED>
 __global__ void __launch_bounds__(256) render_bwd_kernel(BwdArgs A, SplitWs ws) {
   __shared__ BwdLds L;
   const uint32_t b = blockIdx.x;
   if (b < uint32_t(A.num_tiles)) {
-    bwd_tile(L, A, ws, int(ws.order[b]));
+    bwd_tile<FIXED>(L, A, ws, int(ws.order[b]));
   } else {
     const uint32_t item = b - uint32_t(A.num_tiles);
     if (item >= ws.counters[1]) return;
-    bwd_chunk(L, A, ws, item);
+    bwd_chunk<FIXED>(L, A, ws, item);
   }
+}
+
+// Fixed-point sums back to the partials: gscreen[i] holds the i32 sums of the moments
+// M_x, M_y, M_xx, M_xy, M_yy (the second moments divided by the size factor), of o dL/do
+// and of the colour partials, all times `unit`; with the record's own conic and opacity
+// (the values the walks used): du = -(A M_x + B M_y), dv = -(B M_x + C M_y), dA = M_xx / 2,
+// dB = M_xy, dC = M_yy / 2, d opacity = (o dL/do) / o.
+__global__ void __launch_bounds__(256) fixed_decode_kernel(int n, const float4* __restrict__ splat,
+                                                            float* __restrict__ gscreen, float unit) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float* g = gscreen + size_t(i) * 9;
+  int q[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) q[k] = __float_as_int(g[k]);
+  const float4 r0 = splat[3 * i], r1 = splat[3 * i + 1];
+  const float A = r0.z, B = r0.w, C = r1.x, o = r1.y;
+  const float f = fixed_size_factor(A, B, C);
+  const float mx = float(q[0]) / unit, my = float(q[1]) / unit;
+  const float mxx = float(q[2]) * f / unit, mxy = float(q[3]) * f / unit, myy = float(q[4]) * f / unit;
+  g[0] = -(A * mx + B * my);
+  g[1] = -(B * mx + C * my);
+  g[2] = 0.5f * mxx;
+  g[3] = mxy;
+  g[4] = 0.5f * myy;
+  g[5] = q[5] != 0 ? (float(q[5]) / unit) / o : 0.0f;
+#pragma unroll
+  for (int k = 6; k < 9; ++k) g[k] = float(q[k]) / unit;
 }
 
 __global__ void zero_f32_kernel(float* __restrict__ p, int64_t count) {
@@ -1047,7 +1124,7 @@ hipError_t launch_render_fwd(const gs_proj& proj, const uint32_t* vals, const ui
 
 hipError_t launch_render_bwd(const gs_proj& proj, int n, const uint32_t* vals, const uint32_t* ranges,
                              const gs_camera& cam, uint32_t pairs, const float* T_final, const uint32_t* n_contrib,
-                             const float* dL_dimg, float* gscreen, void* wsp, hipStream_t s) {
+                             const float* dL_dimg, float* gscreen, void* wsp, bool fixed, hipStream_t s) {
   const int tx = tiles_x(cam), ty = tiles_y(cam);
   const int num_tiles = tx * ty;
   const SplitDims d = split_dims(cam.width, cam.height, pairs, g_first, g_chunk);
@@ -1063,12 +1140,20 @@ hipError_t launch_render_bwd(const gs_proj& proj, int n, const uint32_t* vals, c
       zero_f32_kernel<<<div_up(count, 256), 256, 0, s>>>(gscreen, count);
     }
   }
+  const float unit = kFixedUnit * 3.0f * float(cam.width) * float(cam.height);
   const BwdArgs A{splat, vals, ranges, num_tiles, tx, cam.width, cam.height, cam.bg[0], cam.bg[1], cam.bg[2],
-                  g_first, g_chunk, T_final, n_contrib, dL_dimg, n, gscreen};
+                  g_first, g_chunk, T_final, n_contrib, dL_dimg, n, gscreen, unit};
   const unsigned blocks = unsigned(num_tiles) + (pairs > uint32_t(g_first) ? unsigned(d.I) : 0u);
   {
     GSK_PROF("render_bwd", s);
-    render_bwd_kernel<<<blocks, 256, 0, s>>>(A, ws);
+    if (fixed)
+      render_bwd_kernel<true><<<blocks, 256, 0, s>>>(A, ws);
+    else
+      render_bwd_kernel<false><<<blocks, 256, 0, s>>>(A, ws);
+  }
+  if (fixed && n > 0) {
+    GSK_PROF("fixed_decode", s);
+    fixed_decode_kernel<<<div_up(n, 256), 256, 0, s>>>(n, splat, gscreen, unit);
   }
   return hipGetLastError();
 }

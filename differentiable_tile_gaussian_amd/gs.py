@@ -19,10 +19,11 @@ LIB_PATH = os.path.join(_HERE, "libgs.so")
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_UNSUPPORTED, GS_ERR_HIP = 0, -1, -2, -3, -4
 GS_WS_PREPROCESS, GS_WS_BIN_SORT, GS_WS_LOSS, GS_WS_RENDER, GS_WS_DENSIFY = 0, 1, 2, 3, 4
 GS_TUNE_SPLIT_FIRST, GS_TUNE_SPLIT_CHUNK = 0, 1
+GS_GRAD_SUMS_FLOAT, GS_GRAD_SUMS_FIXED = 0, 1
 
 EXPORTED = ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
             "gs_adam_step", "gs_render_bwd_adam", "gs_render_bwd_adam_project", "gs_densify_accumulate",
-            "gs_densify", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
+            "gs_densify", "gs_set_grad_sums", "gs_get_grad_sums", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
             "gs_profile_enable", "gs_profile_query", "gs_param_floats", "gs_params_to_blocked",
             "gs_params_from_blocked", "gs_last_error")
 
@@ -65,6 +66,10 @@ def _load():
                                                C.c_double, C.c_double, I32, P, C.c_size_t, P, P, P, P, C.c_size_t,
                                                P, P]
     lib.gs_render_bwd_adam_project.restype = I32
+    lib.gs_set_grad_sums.argtypes = [I32]
+    lib.gs_set_grad_sums.restype = I32
+    lib.gs_get_grad_sums.argtypes = []
+    lib.gs_get_grad_sums.restype = I32
     lib.gs_densify_accumulate.argtypes = [P, I64, P, P, P]
     lib.gs_densify_accumulate.restype = I32
     D = C.c_double
@@ -291,6 +296,15 @@ def gs_densify(params, m, v, stats, rand, n, sh_degree, grad_threshold, prune_op
                            _ptr(v_out), _ptr(stats_out), int(capacity), C.byref(n_out), counts, _ptr(ws),
                            ws.numel() if ws is not None else 0, _stream(stream)))
     return int(n_out.value), tuple(int(c) for c in counts)
+
+
+def gs_set_grad_sums(mode):
+    """GS_GRAD_SUMS_FLOAT (fp32 atomics) or GS_GRAD_SUMS_FIXED (integer sums, reproducible)."""
+    _check(_lib.gs_set_grad_sums(int(mode)))
+
+
+def gs_get_grad_sums():
+    return int(_lib.gs_get_grad_sums())
 
 
 def gs_set_tuning(key, value):

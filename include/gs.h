@@ -286,6 +286,22 @@ int32_t gs_densify(const float* params, const float* m, const float* v, const fl
                    size_t ws_bytes, void* stream);
 
 enum { GS_WS_PREPROCESS = 0, GS_WS_BIN_SORT = 1, GS_WS_LOSS = 2, GS_WS_RENDER = 3, GS_WS_DENSIFY = 4 };
+
+/* How the backward blend sums the per-pixel gradient contributions of a Gaussian (for the
+ * whole process, every backward call enqueued after it; default GS_GRAD_SUMS_FLOAT).
+ *   GS_GRAD_SUMS_FLOAT: fp32 atomics; the order of the additions varies from run to run.
+ *   GS_GRAD_SUMS_FIXED: [GSG] "Making the parallel sums exact": every wave-summed moment
+ *     (position moments, the three second moments divided by a footprint size factor
+ *     1 + trace of the screen covariance, opacity, colour), times 16384 and times the
+ *     loss's element count 3 W H (so that the unit is that of the summed loss), clamped to
+ *     +-1e9, rounded to the nearest integer and added with i32 atomics; a decode pass then
+ *     turns the sums into the same partials as the float mode.  Results are identical bit
+ *     for bit from run to run; each addition is exact to 0.5 / (16384 * 3 W H), and a
+ *     partial's total must stay within 2^31 units (it wraps beyond).
+ * GS_ERR_INVALID_ARG for another mode. */
+enum { GS_GRAD_SUMS_FLOAT = 0, GS_GRAD_SUMS_FIXED = 1 };
+int32_t gs_set_grad_sums(int32_t mode);
+int32_t gs_get_grad_sums(void);
 size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H);
 
 /* Tuning of the blend's work split (process-wide; set before sizing workspaces, and not between a

@@ -105,6 +105,10 @@ def test_argument_errors_without_gpu(gs):
     assert n_out.value == -1                                                          # nothing written
     assert L.gs_densify_accumulate(C.byref(proj), 10, None, 1, None) == gs.GS_ERR_INVALID_ARG
     assert L.gs_densify_accumulate(None, 0, None, None, None) == gs.GS_OK            # empty: nothing to do
+    # gradient-sum modes
+    assert L.gs_get_grad_sums() == gs.GS_GRAD_SUMS_FLOAT
+    assert L.gs_set_grad_sums(7) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_get_grad_sums() == gs.GS_GRAD_SUMS_FLOAT
     # tuning values are checked
     assert L.gs_set_tuning(gs.GS_TUNE_SPLIT_CHUNK, 6) == gs.GS_ERR_INVALID_ARG
     assert L.gs_set_tuning(77, 1024) == gs.GS_ERR_INVALID_ARG
