@@ -721,6 +721,31 @@ void smooth_order(int64_t n, const R* depth, const uint8_t* visible, std::vector
 // ===================================================================== C ABI
 // Plain entry points for ctypes.  Arrays are planar ([plane][n] or [ch][H][W]).
 
+// ------------------------------------------------ Charbonnier loss with exposure
+// [GSG] the trainer's loss (the code after "The painting itself"): per element
+// err = gain C + bias - target, root = sqrt(err^2 + delta^2), loss term root - delta, slope
+// gain err / root; "Forgiving the camera and the light": one gain (stored as its log) and
+// one bias per image, d/d(log gain) = sum (err / root) C gain, d/d bias = sum err / root.
+// Reading: the loss is the mean over the 3HW elements (as the L1 term is).
+template <class R>
+void loss_charbonnier(const R* img, const R* tgt, int64_t count, R delta, R log_gain, R bias, R* out3, R* grad) {
+  const R gain = R(std::exp(double(log_gain)));
+  double sl = 0.0, sg = 0.0, sb = 0.0;
+  const R inv = R(1.0 / double(count));
+  for (int64_t i = 0; i < count; ++i) {
+    const R err = gain * img[i] + bias - tgt[i];
+    const R root = std::sqrt(err * err + delta * delta);
+    const R eg = err / root;
+    sl += double(root - delta);
+    sg += double(eg * img[i] * gain);
+    sb += double(eg);
+    grad[i] = gain * eg * inv;
+  }
+  out3[0] = R(sl / double(count));
+  out3[1] = R(sg / double(count));
+  out3[2] = R(sb / double(count));
+}
+
 // ---------------------------------------------------------- density control
 // [GST] density-control slide ("Original 3DGS periodically changes the number of
 // primitives"): the screen-space centre gradient magnitude of every visible
@@ -1125,6 +1150,15 @@ void or_adam_f64(double* params, const double* grads, double* m, double* v, int6
 void or_adam_f32(float* params, const float* grads, float* m, float* v, int64_t n, int deg, const double* lr,
                  double b1, double b2, double eps, int step) {
   adam<float>(params, grads, m, v, n, deg, lr, b1, b2, eps, step);
+}
+
+void or_loss_charbonnier_f32(const float* img, const float* tgt, int64_t count, float delta, float log_gain,
+                             float bias, float* out3, float* grad) {
+  loss_charbonnier<float>(img, tgt, count, delta, log_gain, bias, out3, grad);
+}
+void or_loss_charbonnier_f64(const double* img, const double* tgt, int64_t count, double delta, double log_gain,
+                             double bias, double* out3, double* grad) {
+  loss_charbonnier<double>(img, tgt, count, delta, log_gain, bias, out3, grad);
 }
 
 void or_densify_accumulate_f32(int64_t n, const uint32_t* tiles, const float* gscreen, float* stats) {

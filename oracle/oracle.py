@@ -79,6 +79,8 @@ def _declare(L):
     L.or_flip_risk_f32.argtypes = [I64] + [P] * 6 + [P, P, C.c_double, P, P, P, P]
     L.or_flip_risk_f32.restype = I64
     L.or_densify_accumulate_f32.argtypes = [I64, P, P, P]
+    L.or_loss_charbonnier_f32.argtypes = [P, P, I64, C.c_float, C.c_float, C.c_float, P, P]
+    L.or_loss_charbonnier_f64.argtypes = [P, P, I64, C.c_double, C.c_double, C.c_double, P, P]
     F = C.c_float
     L.or_densify_f32.argtypes = [I64, I32, P, P, P, P, P, F, F, F, F, F, I32, F, I64, P, P, P, P, P]
     L.or_densify_f32.restype = I64
@@ -380,3 +382,16 @@ def densify(params, m, v, stats, rand, sh_degree, grad_threshold, prune_opacity,
     so = np.zeros((total, 2), np.float32)
     lib().or_densify_f32(*args, total, _p(po), _p(mo), _p(vo), _p(so), _p(counts))
     return dict(params=po, m=mo, v=vo, stats=so, counts=counts)
+
+
+# ------------------------------------------- Charbonnier loss with exposure
+def loss_charbonnier(img, tgt, delta=0.03, log_gain=0.0, bias=0.0, dtype=np.float64):
+    """Mean over the elements of sqrt((gain img + bias - tgt)^2 + delta^2) - delta, gain =
+    exp(log_gain); returns (loss, dL/dimg, dL/dlog_gain, dL/dbias)."""
+    img = _c(img, dtype)
+    tgt = _c(tgt, dtype)
+    out = np.zeros(3, dtype)
+    grad = np.zeros_like(img)
+    fn = lib().or_loss_charbonnier_f64 if dtype == np.float64 else lib().or_loss_charbonnier_f32
+    fn(_p(img), _p(tgt), img.size, delta, log_gain, bias, _p(out), _p(grad))
+    return out[0], grad, out[1], out[2]
