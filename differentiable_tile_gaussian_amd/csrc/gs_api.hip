@@ -171,6 +171,7 @@ size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t
     case GS_WS_LOSS: return (W > 0 && H > 0) ? gsk::loss_ws_bytes(H, W) : 0;
     case GS_WS_RENDER: return (W > 0 && H > 0) ? gsk::render_ws_bytes(W, H, pairs) : 0;
     case GS_WS_DENSIFY: return gsk::densify_ws_bytes(n < 0 ? 0 : n);
+    case GS_WS_LOSS_CHARBONNIER: return (W > 0 && H > 0) ? gsk::charbonnier_ws_bytes(H, W) : 0;
     default: return 0;
   }
 }
@@ -527,6 +528,21 @@ int32_t gs_densify(const float* params, const float* m, const float* v, const fl
                                                    v_out, stats_out, s);
     if (e != hipSuccess) return hip_fail(e, "densify_write");
   }
+  return GS_OK;
+}
+
+int32_t gs_loss_charbonnier(const float* img, const float* target, int32_t H, int32_t W, float delta,
+                            const float* exposure, float* loss_out, float* dL_dimg, float* dL_dexposure, void* ws,
+                            size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (H <= 0 || W <= 0 || int64_t(H) * W > (int64_t(1) << 29)) return fail(GS_ERR_INVALID_ARG, "bad image size");
+  if (!img || !target || !exposure || !loss_out || !dL_dimg) return fail(GS_ERR_INVALID_ARG, "an argument is null");
+  if (!(delta > 0.0f) || !std::isfinite(delta)) return fail(GS_ERR_INVALID_ARG, "delta must be positive");
+  const size_t need = gs_workspace_bytes(GS_WS_LOSS_CHARBONNIER, 0, 0, W, H);
+  if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "Charbonnier workspace needs %zu bytes", need);
+  const hipError_t e = gsk::launch_charbonnier(img, target, H, W, delta, exposure, loss_out, dL_dimg, dL_dexposure,
+                                               ws, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "loss_charbonnier");
   return GS_OK;
 }
 

@@ -118,6 +118,9 @@ hipError_t launch_render_bwd(const gs_proj& proj, int n, const uint32_t* vals, c
 size_t loss_ws_bytes(int H, int W);
 hipError_t launch_loss(const float* img, const float* target, int H, int W, float lambda, float* loss_out,
                        float* grad, void* ws, hipStream_t s);
+size_t charbonnier_ws_bytes(int H, int W);
+hipError_t launch_charbonnier(const float* img, const float* target, int H, int W, float delta, const float* exposure,
+                              float* loss_out, float* grad, float* dexp, void* ws, hipStream_t s);
 
 // ---- layout.hip: planar [P][n] <-> blocked (padding written as zero)
 hipError_t launch_to_blocked(const float* planar, float* blocked, int n, int P, hipStream_t s);

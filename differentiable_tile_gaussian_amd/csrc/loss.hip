@@ -234,9 +234,132 @@ __global__ void __launch_bounds__(256) loss_finalize_kernel(const float* __restr
   }
 }
 
+// ------------------------------------------------ Charbonnier loss with exposure
+// [GSG] the trainer's loss (the code after "The painting itself") and "Forgiving the
+// camera and the light": err = gain x + bias - y, root = sqrt(err^2 + delta^2); the loss is
+// the mean of root - delta over the 3HW elements, dL/dx = gain (err / root) / 3HW, and the
+// exposure gradients are the means of (err / root) x gain (log gain) and err / root (bias).
+// One pass: 16 elements per thread (four 16-byte loads when the arrays allow), the
+// block's three partial sums in fp32, then one block adds the partials in fp64 in a fixed
+// order (so the result does not depend on scheduling).
+constexpr int kCbThreads = 256;
+constexpr int kCbItems = 16;
+constexpr int kCbTile = kCbThreads * kCbItems;
+
+__global__ void __launch_bounds__(kCbThreads) charbonnier_kernel(const float* __restrict__ img,
+                                                                  const float* __restrict__ tgt, int64_t count,
+                                                                  float delta, const float* __restrict__ exposure,
+                                                                  float inv_count, bool vec, float* __restrict__ grad,
+                                                                  float* __restrict__ partial) {
+  __shared__ float s_part[3][kCbThreads / 64];
+  const float gain = float(exp(double(exposure[0]))), bias = exposure[1];
+  const int64_t base = int64_t(blockIdx.x) * kCbTile + int64_t(threadIdx.x) * 4;
+  float sl = 0.0f, sg = 0.0f, sb = 0.0f;
+#pragma unroll
+  for (int r = 0; r < kCbItems / 4; ++r) {
+    const int64_t i0 = base + int64_t(r) * kCbThreads * 4;
+    float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
+    const bool full = vec && i0 + 4 <= count;
+    if (full) {
+      const float4 a = *reinterpret_cast<const float4*>(img + i0), b = *reinterpret_cast<const float4*>(tgt + i0);
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+      y[0] = b.x; y[1] = b.y; y[2] = b.z; y[3] = b.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (i0 + k < count) { x[k] = img[i0 + k]; y[k] = tgt[i0 + k]; }
+    }
+    float g[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool in = i0 + k < count;
+      const float err = gain * x[k] + bias - y[k];
+      const float root = sqrtf(err * err + delta * delta);
+      const float eg = err / root;
+      g[k] = gain * eg * inv_count;
+      if (in) {
+        sl += root - delta;
+        sg += eg * x[k] * gain;
+        sb += eg;
+      }
+    }
+    if (full) {
+      *reinterpret_cast<float4*>(grad + i0) = make_float4(g[0], g[1], g[2], g[3]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (i0 + k < count) grad[i0 + k] = g[k];
+    }
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    sl += __shfl_xor(sl, d, 64);
+    sg += __shfl_xor(sg, d, 64);
+    sb += __shfl_xor(sb, d, 64);
+  }
+  if (__lane_id() == 0) {
+    s_part[0][threadIdx.x >> 6] = sl;
+    s_part[1][threadIdx.x >> 6] = sg;
+    s_part[2][threadIdx.x >> 6] = sb;
+  }
+  __syncthreads();
+  if (threadIdx.x < 3) {
+    float t = 0.0f;
+    for (int w = 0; w < kCbThreads / 64; ++w) t += s_part[threadIdx.x][w];
+    partial[3 * blockIdx.x + threadIdx.x] = t;
+  }
+}
+
+__global__ void __launch_bounds__(256) charbonnier_finalize_kernel(const float* __restrict__ partial, int nblocks,
+                                                                    double inv_n, float* __restrict__ loss_out,
+                                                                    float* __restrict__ dexp) {
+  __shared__ double s[3][256];
+  double a[3] = {0.0, 0.0, 0.0};
+  for (int k = threadIdx.x; k < nblocks; k += 256)
+    for (int j = 0; j < 3; ++j) a[j] += double(partial[3 * k + j]);
+  for (int j = 0; j < 3; ++j) s[j][threadIdx.x] = a[j];
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (threadIdx.x < h)
+      for (int j = 0; j < 3; ++j) s[j][threadIdx.x] += s[j][threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    loss_out[0] = float(s[0][0] * inv_n);
+    if (dexp) {
+      dexp[0] = float(s[1][0] * inv_n);
+      dexp[1] = float(s[2][0] * inv_n);
+    }
+  }
+}
+
 inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 }  // namespace
+
+size_t charbonnier_ws_bytes(int H, int W) {
+  const int64_t count = int64_t(3) * H * W;
+  return align256(size_t(div_up(count, kCbTile)) * 3 * 4);
+}
+
+hipError_t launch_charbonnier(const float* img, const float* target, int H, int W, float delta, const float* exposure,
+                              float* loss_out, float* grad, float* dexp, void* ws, hipStream_t s) {
+  const int64_t count = int64_t(3) * H * W;
+  const int nb = int(div_up(count, kCbTile));
+  float* partial = static_cast<float*>(ws);
+  const bool vec = reinterpret_cast<uintptr_t>(img) % 16 == 0 && reinterpret_cast<uintptr_t>(target) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(grad) % 16 == 0;
+  {
+    GSK_PROF("charbonnier", s);
+    charbonnier_kernel<<<nb, kCbThreads, 0, s>>>(img, target, count, delta, exposure, float(1.0 / double(count)),
+                                                 vec, grad, partial);
+  }
+  {
+    GSK_PROF("charbonnier_finalize", s);
+    charbonnier_finalize_kernel<<<1, 256, 0, s>>>(partial, nb, 1.0 / double(count), loss_out, dexp);
+  }
+  return hipGetLastError();
+}
 
 size_t loss_ws_bytes(int H, int W) {
   const size_t nb = size_t(div_up(W, kSO)) * div_up(H, kSR) * 3;

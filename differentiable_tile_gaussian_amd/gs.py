@@ -17,13 +17,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgs.so")
 
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_UNSUPPORTED, GS_ERR_HIP = 0, -1, -2, -3, -4
-GS_WS_PREPROCESS, GS_WS_BIN_SORT, GS_WS_LOSS, GS_WS_RENDER, GS_WS_DENSIFY = 0, 1, 2, 3, 4
+GS_WS_PREPROCESS, GS_WS_BIN_SORT, GS_WS_LOSS, GS_WS_RENDER, GS_WS_DENSIFY, GS_WS_LOSS_CHARBONNIER = 0, 1, 2, 3, 4, 5
 GS_TUNE_SPLIT_FIRST, GS_TUNE_SPLIT_CHUNK = 0, 1
 GS_GRAD_SUMS_FLOAT, GS_GRAD_SUMS_FIXED = 0, 1
 
 EXPORTED = ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
             "gs_adam_step", "gs_render_bwd_adam", "gs_render_bwd_adam_project", "gs_densify_accumulate",
-            "gs_densify", "gs_set_grad_sums", "gs_get_grad_sums", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
+            "gs_densify", "gs_set_grad_sums", "gs_get_grad_sums", "gs_loss_charbonnier", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
             "gs_profile_enable", "gs_profile_query", "gs_param_floats", "gs_params_to_blocked",
             "gs_params_from_blocked", "gs_last_error")
 
@@ -66,6 +66,8 @@ def _load():
                                                C.c_double, C.c_double, I32, P, C.c_size_t, P, P, P, P, C.c_size_t,
                                                P, P]
     lib.gs_render_bwd_adam_project.restype = I32
+    lib.gs_loss_charbonnier.argtypes = [P, P, I32, I32, C.c_float, P, P, P, P, P, C.c_size_t, P]
+    lib.gs_loss_charbonnier.restype = I32
     lib.gs_set_grad_sums.argtypes = [I32]
     lib.gs_set_grad_sums.restype = I32
     lib.gs_get_grad_sums.argtypes = []
@@ -296,6 +298,13 @@ def gs_densify(params, m, v, stats, rand, n, sh_degree, grad_threshold, prune_op
                            _ptr(v_out), _ptr(stats_out), int(capacity), C.byref(n_out), counts, _ptr(ws),
                            ws.numel() if ws is not None else 0, _stream(stream)))
     return int(n_out.value), tuple(int(c) for c in counts)
+
+
+def gs_loss_charbonnier(img, target, exposure, loss_out, dL_dimg, ws, delta=0.03, dL_dexposure=None, stream=None):
+    """Charbonnier loss with exposure (log gain, bias): mean of sqrt(err^2 + delta^2) - delta."""
+    _, H, W = img.shape
+    _check(_lib.gs_loss_charbonnier(_ptr(img), _ptr(target), H, W, float(delta), _ptr(exposure), _ptr(loss_out),
+                                    _ptr(dL_dimg), _ptr(dL_dexposure), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def gs_set_grad_sums(mode):

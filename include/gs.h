@@ -174,6 +174,19 @@ int32_t gs_render_fwd(const gs_proj* proj, int64_t n, const uint32_t* vals, cons
 int32_t gs_loss_l1_dssim(const float* img, const float* target, int32_t H, int32_t W, float lambda_dssim,
                          float* loss_out, float* dL_dimg, void* ws, size_t ws_bytes, void* stream);
 
+/* The trainer's other loss: Charbonnier with per-image exposure ([GSG] the loss code after
+ * "The painting itself"; "Forgiving the camera and the light").  Per element
+ *   err = gain img + bias - target,  root = sqrt(err^2 + delta^2),
+ * gain = exp(exposure[0]), bias = exposure[1]; the loss is the mean of root - delta over the
+ * 3HW elements, dL/dimg = gain err / root / 3HW, and dL_dexposure (nullable) receives the
+ * means of (err / root) img gain (the log gain's gradient) and err / root (the bias's).
+ * img, target, dL_dimg: [3][H][W]; exposure, dL_dexposure: device float[2]; loss_out: device
+ * float[1]; delta > 0 (0.03 on the page).  The sums are formed in a fixed order (the result
+ * is reproducible).  ws: gs_workspace_bytes(GS_WS_LOSS_CHARBONNIER, 0, 0, W, H). */
+int32_t gs_loss_charbonnier(const float* img, const float* target, int32_t H, int32_t W, float delta,
+                            const float* exposure, float* loss_out, float* dL_dimg, float* dL_dexposure, void* ws,
+                            size_t ws_bytes, void* stream);
+
 /* Backward pass.  Part 1, the blend: [DR] "The trick: recompute the blend state instead of
  * storing it"; [GSG] "The clever bit: a single backward sweep through the blend" and "From a
  * pixel's blame to the oval's shape and place"; [GST] compositing-derivative slide.  Each
@@ -285,7 +298,8 @@ int32_t gs_densify(const float* params, const float* m, const float* v, const fl
                    float* v_out, float* stats_out, int64_t capacity, int64_t* n_out, int64_t* counts, void* ws,
                    size_t ws_bytes, void* stream);
 
-enum { GS_WS_PREPROCESS = 0, GS_WS_BIN_SORT = 1, GS_WS_LOSS = 2, GS_WS_RENDER = 3, GS_WS_DENSIFY = 4 };
+enum { GS_WS_PREPROCESS = 0, GS_WS_BIN_SORT = 1, GS_WS_LOSS = 2, GS_WS_RENDER = 3, GS_WS_DENSIFY = 4,
+       GS_WS_LOSS_CHARBONNIER = 5 };
 
 /* How the backward blend sums the per-pixel gradient contributions of a Gaussian (for the
  * whole process, every backward call enqueued after it; default GS_GRAD_SUMS_FLOAT).

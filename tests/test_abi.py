@@ -105,6 +105,11 @@ def test_argument_errors_without_gpu(gs):
     assert n_out.value == -1                                                          # nothing written
     assert L.gs_densify_accumulate(C.byref(proj), 10, None, 1, None) == gs.GS_ERR_INVALID_ARG
     assert L.gs_densify_accumulate(None, 0, None, None, None) == gs.GS_OK            # empty: nothing to do
+    # Charbonnier loss: sizes, delta and the workspace are checked first
+    assert L.gs_loss_charbonnier(1, 1, 8, 8, C.c_float(0.0), 1, 1, 1, None, 1, big, None) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_loss_charbonnier(1, 1, 0, 8, C.c_float(0.03), 1, 1, 1, None, 1, big, None) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_loss_charbonnier(1, None, 8, 8, C.c_float(0.03), 1, 1, 1, None, 1, big, None) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_loss_charbonnier(1, 1, 8, 8, C.c_float(0.03), 1, 1, 1, None, None, 0, None) == gs.GS_ERR_CAPACITY
     # gradient-sum modes
     assert L.gs_get_grad_sums() == gs.GS_GRAD_SUMS_FLOAT
     assert L.gs_set_grad_sums(7) == gs.GS_ERR_INVALID_ARG
