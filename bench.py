@@ -184,6 +184,28 @@ def measure_densify(pl, cams, targets, first, torch, gs, steps=3):
             "write_bytes": wbytes, "write_GBps": round(wbytes / (write_ms / 1000.0) / 1e9, 1)}
 
 
+def measure_charbonnier(pl, targets, torch, gs, reps=20):
+    """The Charbonnier loss with exposure on the benchmark's image (an alternative to the
+    L1 + D-SSIM loss, not part of the step): average of `reps` calls, HIP events."""
+    dev = pl.params.device
+    exposure = torch.tensor([0.05, -0.01], dtype=torch.float32, device=dev)
+    loss = torch.zeros(1, device=dev)
+    dexp = torch.zeros(2, device=dev)
+    grad = torch.empty_like(pl.rgb)
+    ws = gs.workspace(gs.GS_WS_LOSS_CHARBONNIER, W=pl.W, H=pl.H)
+    gs.gs_loss_charbonnier(pl.rgb, targets[0], exposure, loss, grad, ws, dL_dexposure=dexp)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(reps):
+        gs.gs_loss_charbonnier(pl.rgb, targets[0], exposure, loss, grad, ws, dL_dexposure=dexp)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    nbytes = 3 * pl.H * pl.W * 12   # image and target read, gradient written
+    return {"ms": round(ms, 4), "bytes": nbytes, "GBps": round(nbytes / (ms / 1000.0) / 1e9, 1)}
+
+
 def count_evals(pl, torch):
     """Gaussian-pixel evaluations of the last forward/backward: the forward examines
     entries up to the stopping one (n_contrib for stopped pixels, the whole tile list
@@ -343,6 +365,7 @@ def main():
         ev_b += b
     del pl2, params2
     densify = measure_densify(pl, cams, targets, args.warmup + args.steps, torch, gs) if not args.no_densify else None
+    charbonnier = measure_charbonnier(pl, targets, torch, gs)
     t_fb = (stage[:, 2].sum() + stage[:, 4].sum()) / 1000.0
 
     # roofline of the dominant kernel from its live launch times
@@ -383,6 +406,7 @@ def main():
         "blend_valu": {"bound": "alu", "peak": VALU_PEAK, "unit": "wave instr/s", "kernels": measured_valu()},
         "roofline": roof,
         "densify": densify,
+        "charbonnier_loss": charbonnier,
         "setup_s": round(setup_s, 2),
     }
     if not args.no_cpu_baseline and args.workload == WORKLOAD_CFG:
