@@ -134,6 +134,15 @@ void sh_basis(const R d[3], R Y[16], R dY[16][3]) {
 
 inline int num_planes(int deg) { return 11 + 3 * (deg + 1) * (deg + 1); }
 
+// SH degree ramp ([GSG] "Spherical harmonics": only the first activeK = (activeDeg + 1)^2 - 1
+// band weights are summed, and the inactive ones receive no gradient until their band
+// switches on).  -1: every stored band.  Set by or_set_active_sh_degree.
+int g_active_deg = -1;
+inline int active_bands(int deg) {
+  const int d = (g_active_deg < 0 || g_active_deg > deg) ? deg : g_active_deg;
+  return (d + 1) * (d + 1) - 1;
+}
+
 // --------------------------------------------------------------- preprocess
 // Everything the forward projection computes for one Gaussian, kept so the
 // backward chain can reuse it.  Sources:
@@ -238,8 +247,8 @@ Fwd<R> project(const R* params, int64_t n, int64_t i, int deg, const Camera& cam
   f.B = -f.b / f.det;
   f.C = f.a / f.det;
   f.o = sigmoid_r(P(10));
-  // colour: DC plus the higher bands along dir = normalize(m - campos)
-  const int K = (deg + 1) * (deg + 1) - 1;
+  // colour: DC plus the (active) higher bands along dir = normalize(m - campos)
+  const int K = active_bands(deg);
   for (int k = 0; k < 3; ++k) f.dvec[k] = f.m[k] - R(cam.campos[k]);
   f.dlen = std::sqrt((f.dvec[0] * f.dvec[0] + f.dvec[1] * f.dvec[1]) + f.dvec[2] * f.dvec[2]);
   for (int k = 0; k < 3; ++k) f.dir[k] = f.dvec[k] / f.dlen;
@@ -468,8 +477,8 @@ void chain_one(const R* params, int64_t n, int64_t i, int deg, const Camera& cam
   const R gu = GS(0), gv = GS(1), gA = GS(2), gB = GS(3), gC = GS(4), go = GS(5);
   // opacity logit
   GP(10) = go * f.o * (R(1) - f.o);
-  // colour -> DC, higher bands, view direction
-  const int K = (deg + 1) * (deg + 1) - 1;
+  // colour -> DC, the active higher bands (the others get none), view direction
+  const int K = active_bands(deg);
   R gc[3];
   for (int ch = 0; ch < 3; ++ch) gc[ch] = (!smooth && f.raw[ch] < R(0)) ? R(0) : GS(6 + ch);
   R gdir[3] = {R(0), R(0), R(0)};
@@ -863,6 +872,7 @@ int64_t densify(int64_t n, int deg, const float* params, const float* m, const f
 extern "C" {
 
 int or_num_planes(int deg) { return num_planes(deg); }
+void or_set_active_sh_degree(int d) { g_active_deg = d; }
 
 // Scalar helpers for the SH pins.
 double or_sh_norm(int l, int m) { return sh_norm(l, m); }

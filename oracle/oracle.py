@@ -56,6 +56,7 @@ I32 = C.c_int
 
 def _declare(L):
     L.or_num_planes.argtypes = [I32]
+    L.or_set_active_sh_degree.argtypes = [I32]
     L.or_num_planes.restype = I32
     L.or_sh_norm.argtypes = [I32, I32]
     L.or_sh_norm.restype = C.c_double
@@ -96,6 +97,11 @@ def _c(a, dtype):
 
 def num_planes(deg):
     return lib().or_num_planes(deg)
+
+
+def set_active_sh_degree(d):
+    """SH degree ramp: only bands up to d are evaluated and receive gradients (-1: all)."""
+    lib().or_set_active_sh_degree(int(d))
 
 
 # ----------------------------------------------------------------- forward
