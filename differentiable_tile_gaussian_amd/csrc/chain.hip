@@ -143,7 +143,7 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
                                                      const uint32_t* tiles,   // may be np.tiles
                                                      const float* __restrict__ gscreen, float* __restrict__ gparams,
                                                      float* __restrict__ m, float* __restrict__ v, AdamArgs a,
-                                                     NextProj np, float2* __restrict__ dstats) {
+                                                     NextProj np, float2* __restrict__ dstats, int kact) {
   constexpr int K = (DEG + 1) * (DEG + 1) - 1;
   constexpr int P = 11 + 3 * (K + 1);
   __shared__ float s_gdir[3][3][64];   // view-direction partials of each colour channel
@@ -210,7 +210,8 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
     if (vis) {
       float raw = coef[0];
 #pragma unroll
-      for (int k = 1; k <= K; ++k) raw = raw + coef[k] * Y[k];
+      for (int k = 1; k <= K; ++k)
+        if (k <= kact) raw = raw + coef[k] * Y[k];
       gc = raw < 0.0f ? 0.0f : gcol;
     }
     if (K > 0) {
@@ -219,7 +220,7 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
         float wk[16];
 #pragma unroll
         for (int k = 1; k <= K; ++k) wk[k] = gc * coef[k];
-        sh_grad_dot(dir[0], dir[1], dir[2], wk, K, gd);
+        sh_grad_dot(dir[0], dir[1], dir[2], wk, kact, gd);   // the active bands only
       }
 #pragma unroll
       for (int c = 0; c < 3; ++c) s_gdir[ch][c][lane] = gd[c];
@@ -227,7 +228,7 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
     if (valid) {
 #pragma unroll
       for (int k = 0; k <= K; ++k) {
-        const float g = k == 0 ? gc : (vis ? gc * Y[k] : 0.0f);
+        const float g = k == 0 ? gc : (vis && k <= kact ? gc * Y[k] : 0.0f);
         const size_t o = gb + colour_plane(k, ch) * kGB;
         if (ADAM) {
           coef[k] = adam_update(coef[k], g, cmo[k], cvo[k], a.lr[4], a);
@@ -271,7 +272,8 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
     if (K > 0) sh_eval(s_ndir[0][lane], s_ndir[1][lane], s_ndir[2][lane], Y);
     float raw = coef[0];
 #pragma unroll
-    for (int k = 1; k <= K; ++k) raw = raw + coef[k] * Y[k];
+    for (int k = 1; k <= K; ++k)
+      if (k <= kact) raw = raw + coef[k] * Y[k];
     s_nraw[ch][lane] = raw;
   }
   __syncthreads();   // next colours
@@ -294,46 +296,48 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
 template <int DEG, bool ADAM, bool PROJ>
 void launch_chain_deg(float* params, int n, const gs_camera& cam, const uint32_t* tiles, const float* gscreen,
                       float* gparams, float* m, float* v, const AdamArgs& a, const NextProj& np, float* dstats,
-                      hipStream_t s) {
+                      int kact, hipStream_t s) {
   GSK_PROF("chain", s);
   chain_kernel<DEG, ADAM, PROJ><<<div_up(n, 64), 256, 0, s>>>(params, n, cam, tiles, gscreen, gparams, m, v, a, np,
-                                                              reinterpret_cast<float2*>(dstats));
+                                                              reinterpret_cast<float2*>(dstats), kact);
 }
 
 template <bool ADAM, bool PROJ>
 void launch_chain_mode(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles, const float* gscreen,
                        float* gparams, float* m, float* v, const AdamArgs& a, const NextProj& np, float* dstats,
-                       hipStream_t s) {
+                       int kact, hipStream_t s) {
   switch (deg) {
-    case 0: launch_chain_deg<0, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, s); break;
-    case 1: launch_chain_deg<1, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, s); break;
-    case 2: launch_chain_deg<2, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, s); break;
-    default: launch_chain_deg<3, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, s); break;
+    case 0: launch_chain_deg<0, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, kact, s); break;
+    case 1: launch_chain_deg<1, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, kact, s); break;
+    case 2: launch_chain_deg<2, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, kact, s); break;
+    default: launch_chain_deg<3, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, kact, s); break;
   }
 }
 
 }  // namespace
 
 hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_camera& cam,
-                                 const uint32_t* tiles, const float* gscreen, float* gparams, hipStream_t s) {
+                                 const uint32_t* tiles, const float* gscreen, float* gparams, int kact,
+                                 hipStream_t s) {
   if (n == 0) return hipSuccess;
   launch_chain_mode<false, false>(const_cast<float*>(params), n, deg, cam, tiles, gscreen, gparams, nullptr, nullptr,
-                                  AdamArgs{}, NextProj{}, nullptr, s);
+                                  AdamArgs{}, NextProj{}, nullptr, kact, s);
   return hipGetLastError();
 }
 
 hipError_t launch_chain_adam(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
-                             const float* gscreen, float* m, float* v, const AdamArgs& a, hipStream_t s) {
+                             const float* gscreen, float* m, float* v, const AdamArgs& a, int kact, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  launch_chain_mode<true, false>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, NextProj{}, nullptr, s);
+  launch_chain_mode<true, false>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, NextProj{}, nullptr, kact,
+                                 s);
   return hipGetLastError();
 }
 
 hipError_t launch_chain_adam_project(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
                                      const float* gscreen, float* m, float* v, const AdamArgs& a,
-                                     const NextProj& np, float* dstats, hipStream_t s) {
+                                     const NextProj& np, float* dstats, int kact, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  launch_chain_mode<true, true>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, np, dstats, s);
+  launch_chain_mode<true, true>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, np, dstats, kact, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_tile_count_total(np.block_tiles, int(div_up(n, 64)), np.total, s);

@@ -14,6 +14,16 @@ namespace {
 // Gradient-sum mode of the backward blend (gs_set_grad_sums), for the whole process.
 std::atomic<int> g_fixed_sums{0};
 
+// SH degree ramp (gs_set_active_sh_degree), for the whole process: -1 = every stored band.
+std::atomic<int> g_active_deg{-1};
+
+// The active higher bands for a stored degree: (d + 1)^2 - 1 with d the smaller of the two.
+int active_bands(int deg) {
+  const int a = g_active_deg.load();
+  const int d = (a < 0 || a > deg) ? deg : a;
+  return (d + 1) * (d + 1) - 1;
+}
+
 thread_local char g_err[512] = "";
 
 int32_t fail(int32_t code, const char* fmt, ...) {
@@ -129,6 +139,15 @@ int32_t gs_set_grad_sums(int32_t mode) {
 
 int32_t gs_get_grad_sums(void) { return g_fixed_sums ? GS_GRAD_SUMS_FIXED : GS_GRAD_SUMS_FLOAT; }
 
+int32_t gs_set_active_sh_degree(int32_t degree) {
+  g_err[0] = 0;
+  if (degree < -1 || degree > 3) return fail(GS_ERR_INVALID_ARG, "active SH degree must be -1..3");
+  g_active_deg = degree;
+  return GS_OK;
+}
+
+int32_t gs_get_active_sh_degree(void) { return g_active_deg.load(); }
+
 int32_t gs_set_tuning(int32_t key, int64_t value) {
   g_err[0] = 0;
   if (value < 4 || value > (int64_t(1) << 24) || (value & 3))
@@ -190,7 +209,7 @@ int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out,
   const int n = int(scene->n);
   PreWs w = carve_pre(ws, n);
   hipError_t e = gsk::launch_preprocess_fwd(scene->params, n, scene->sh_degree, *cam, *out, w.block_tiles,
-                                            w.total64, s);
+                                            w.total64, active_bands(scene->sh_degree), s);
   if (e != hipSuccess) return hip_fail(e, "preprocess_fwd");
   return finish_preprocess(out, n, w, total_pairs, s);
 }
@@ -298,7 +317,8 @@ int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t
   hipError_t e = gsk::launch_render_bwd(*proj, n, vals, ranges, *cam, total_pairs, T_final, n_contrib, dL_dimg,
                                         gscreen, ws, g_fixed_sums != 0, s);
   if (e != hipSuccess) return hip_fail(e, "render_bwd");
-  e = gsk::launch_preprocess_bwd(scene->params, n, scene->sh_degree, *cam, proj->tiles, gscreen, gparams, s);
+  e = gsk::launch_preprocess_bwd(scene->params, n, scene->sh_degree, *cam, proj->tiles, gscreen, gparams,
+                                 active_bands(scene->sh_degree), s);
   if (e != hipSuccess) return hip_fail(e, "preprocess_bwd");
   return GS_OK;
 }
@@ -351,7 +371,7 @@ int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs
                                         dL_dimg, gscreen, ws, g_fixed_sums != 0, s);
   if (e != hipSuccess) return hip_fail(e, "render_bwd");
   e = gsk::launch_chain_adam(params, int(n), sh_degree, *cam, proj->tiles, gscreen, m, v,
-                             adam_args(lr, beta1, beta2, eps, step), s);
+                             adam_args(lr, beta1, beta2, eps, step), active_bands(sh_degree), s);
   if (e != hipSuccess) return hip_fail(e, "chain_adam");
   return GS_OK;
 }
@@ -397,7 +417,8 @@ int32_t gs_render_bwd_adam_project(float* params, int64_t n, int32_t sh_degree, 
   np.block_tiles = w.block_tiles;
   np.total = w.total64;
   e = gsk::launch_chain_adam_project(params, int(n), sh_degree, *cam, proj->tiles, gscreen, m, v,
-                                     adam_args(lr, beta1, beta2, eps, step), np, densify_stats, s);
+                                     adam_args(lr, beta1, beta2, eps, step), np, densify_stats,
+                                     active_bands(sh_degree), s);
   if (e != hipSuccess) return hip_fail(e, "chain_adam_project");
   return finish_preprocess(next_out, int(n), w, next_total_pairs, s);
 }

@@ -23,7 +23,8 @@ GS_GRAD_SUMS_FLOAT, GS_GRAD_SUMS_FIXED = 0, 1
 
 EXPORTED = ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
             "gs_adam_step", "gs_render_bwd_adam", "gs_render_bwd_adam_project", "gs_densify_accumulate",
-            "gs_densify", "gs_set_grad_sums", "gs_get_grad_sums", "gs_loss_charbonnier", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
+            "gs_densify", "gs_set_grad_sums", "gs_get_grad_sums", "gs_set_active_sh_degree",
+            "gs_get_active_sh_degree", "gs_loss_charbonnier", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
             "gs_profile_enable", "gs_profile_query", "gs_param_floats", "gs_params_to_blocked",
             "gs_params_from_blocked", "gs_last_error")
 
@@ -68,6 +69,10 @@ def _load():
     lib.gs_render_bwd_adam_project.restype = I32
     lib.gs_loss_charbonnier.argtypes = [P, P, I32, I32, C.c_float, P, P, P, P, P, C.c_size_t, P]
     lib.gs_loss_charbonnier.restype = I32
+    lib.gs_set_active_sh_degree.argtypes = [I32]
+    lib.gs_set_active_sh_degree.restype = I32
+    lib.gs_get_active_sh_degree.argtypes = []
+    lib.gs_get_active_sh_degree.restype = I32
     lib.gs_set_grad_sums.argtypes = [I32]
     lib.gs_set_grad_sums.restype = I32
     lib.gs_get_grad_sums.argtypes = []
@@ -305,6 +310,15 @@ def gs_loss_charbonnier(img, target, exposure, loss_out, dL_dimg, ws, delta=0.03
     _, H, W = img.shape
     _check(_lib.gs_loss_charbonnier(_ptr(img), _ptr(target), H, W, float(delta), _ptr(exposure), _ptr(loss_out),
                                     _ptr(dL_dimg), _ptr(dL_dexposure), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def gs_set_active_sh_degree(degree):
+    """SH degree ramp: bands up to `degree` are evaluated and trained (-1: every stored band)."""
+    _check(_lib.gs_set_active_sh_degree(int(degree)))
+
+
+def gs_get_active_sh_degree():
+    return int(_lib.gs_get_active_sh_degree())
 
 
 def gs_set_grad_sums(mode):

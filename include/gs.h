@@ -316,6 +316,16 @@ enum { GS_WS_PREPROCESS = 0, GS_WS_BIN_SORT = 1, GS_WS_LOSS = 2, GS_WS_RENDER = 
 enum { GS_GRAD_SUMS_FLOAT = 0, GS_GRAD_SUMS_FIXED = 1 };
 int32_t gs_set_grad_sums(int32_t mode);
 int32_t gs_get_grad_sums(void);
+
+/* SH degree ramp ([GSG] "Spherical harmonics": only the first activeK = (activeDeg + 1)^2 - 1
+ * band weights are summed, the active degree stepping up about every thousand steps; the
+ * inactive ones contribute nothing and receive no gradient until their band switches on).
+ * For the whole process, every projection and chain enqueued after it: the colour sums
+ * the bands up to min(degree, the scene's SH degree), and the other bands' gradients are
+ * zero (with the fused Adam their parameters stay unchanged while their moments are zero).
+ * -1 (the default): every stored band.  GS_ERR_INVALID_ARG outside -1..3. */
+int32_t gs_set_active_sh_degree(int32_t degree);
+int32_t gs_get_active_sh_degree(void);
 size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H);
 
 /* Tuning of the blend's work split (process-wide; set before sizing workspaces, and not between a

@@ -110,6 +110,11 @@ def test_argument_errors_without_gpu(gs):
     assert L.gs_loss_charbonnier(1, 1, 0, 8, C.c_float(0.03), 1, 1, 1, None, 1, big, None) == gs.GS_ERR_INVALID_ARG
     assert L.gs_loss_charbonnier(1, None, 8, 8, C.c_float(0.03), 1, 1, 1, None, 1, big, None) == gs.GS_ERR_INVALID_ARG
     assert L.gs_loss_charbonnier(1, 1, 8, 8, C.c_float(0.03), 1, 1, 1, None, None, 0, None) == gs.GS_ERR_CAPACITY
+    # SH degree ramp
+    assert L.gs_get_active_sh_degree() == -1
+    assert L.gs_set_active_sh_degree(4) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_set_active_sh_degree(-2) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_get_active_sh_degree() == -1
     # gradient-sum modes
     assert L.gs_get_grad_sums() == gs.GS_GRAD_SUMS_FLOAT
     assert L.gs_set_grad_sums(7) == gs.GS_ERR_INVALID_ARG

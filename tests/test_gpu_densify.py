@@ -167,3 +167,42 @@ def test_projecting_update_accumulates_this_steps_observations(torch_cuda):
     np.testing.assert_array_equal(res[0][:, 1], res[1][:, 1])
     np.testing.assert_allclose(res[0][:, 0], res[1][:, 0], rtol=1e-4, atol=1e-12)
     assert (res[0][:, 1] > 0).sum() > 1000
+
+
+def test_training_loop_with_density_control(torch_cuda):
+    """Pipeline: fused steps that accumulate statistics, a densification, and fused steps
+    on the new population; after it, the projection the last update made for the next
+    camera equals gs_preprocess of the parameters it wrote."""
+    torch = torch_cuda
+    from differentiable_tile_gaussian_amd import gs
+    from differentiable_tile_gaussian_amd.pipeline import Pipeline
+    wl = scenes.CONFIGS[2]()
+    cams = [gs.make_camera(c) for c in (wl.cameras[0],
+                                        scenes.look_at_origin((3.0, 0.5, -2.5), 800, 800, 1100.0),
+                                        scenes.look_at_origin((-3.5, -0.4, -2.0), 800, 800, 1100.0))]
+    rng = np.random.default_rng(6)
+    targets = [torch.from_numpy(rng.random((3, 800, 800), dtype=np.float32)).cuda() for _ in cams]
+    pl = Pipeline(torch.from_numpy(wl.scene.params).cuda(), 3, 800, 800)
+    pl.enable_density_stats()
+    for k in range(6):
+        pl.step(cams[k % 3], targets[k % 3], next_cam=cams[(k + 1) % 3])
+    torch.cuda.synchronize()
+    st = pl.dstats[:pl.n].cpu().numpy()
+    assert st[:, 1].max() <= 6 and (st[:, 1] > 0).sum() > 1000
+    thr = float(np.quantile(st[st[:, 1] > 0, 0] / st[st[:, 1] > 0, 1], 0.9))
+    n0 = pl.n
+    counts = pl.densify(thr, 0.005, 1.0, 0.01, generator=torch.Generator(device="cuda").manual_seed(1))
+    kept, cloned, split = counts
+    assert pl.n == kept + cloned + 2 * split and cloned + split > 0 and kept <= n0
+    for k in range(3):
+        loss = pl.step(cams[k], targets[k], next_cam=cams[(k + 1) % 3])
+    torch.cuda.synchronize()
+    assert np.isfinite(loss.cpu().numpy()).all()
+    ref = gs.Proj(pl.n)
+    pairs = gs.gs_preprocess(pl.params, 3, cams[0], ref, gs.workspace(gs.GS_WS_PREPROCESS, n=pl.n))
+    torch.cuda.synchronize()
+    assert pairs == pl.pairs
+    for name in ("splat", "depth", "rect", "tiles"):
+        a = getattr(pl.proj, name)[:pl.n].cpu().numpy()
+        b = getattr(ref, name)[:pl.n].cpu().numpy()
+        np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32), err_msg=name)
