@@ -458,6 +458,37 @@ void blend_pixel_bwd(R px, R py, const uint32_t* list, int64_t n_walk, const R* 
   }
 }
 
+// [GSG] "Forgiving the camera and the light": the render depends on the camera pose, so
+// backpropagation yields its gradient.  Pose W, t (p = W m + t; the camera centre is
+// -W^T t), rotation perturbed on the left, W <- (I + [w]x) W.  One Gaussian's terms of
+// dL/dW: the covariance path J^T dT (T = J W), the position path dp m^T, and the view
+// direction's path through the centre, t gm_sh^T (dL/dcentre = -gm_sh); of dL/dt: dp and
+// W gm_sh.  With G = dL/dW and M = G W^T the rotation gradient is (M21 - M12, M02 - M20,
+// M10 - M01); for the position path alone that is (p - t) x dp, the pages' torque.
+// out[0..2] += rotation gradient, out[3..5] += translation gradient.
+template <class R>
+void camera_grad_terms(const Fwd<R>& f, const Camera& cam, const R dT[2][3], const R dp[3], const R gm_sh[3],
+                       double* out) {
+  const double fx = cam.fx, fy = cam.fy, pz = f.p[2];
+  const double J[2][3] = {{fx / pz, 0.0, -fx * double(f.p[0]) / (pz * pz)},
+                          {0.0, fy / pz, -fy * double(f.p[1]) / (pz * pz)}};
+  double W[3][3], G[3][3];
+  for (int r = 0; r < 3; ++r)
+    for (int c = 0; c < 3; ++c) W[r][c] = cam.R[3 * r + c];
+  for (int r = 0; r < 3; ++r)
+    for (int c = 0; c < 3; ++c)
+      G[r][c] = J[0][r] * double(dT[0][c]) + J[1][r] * double(dT[1][c]) + double(dp[r]) * double(f.m[c]) +
+                double(cam.t[r]) * double(gm_sh[c]);
+  double M[3][3];
+  for (int r = 0; r < 3; ++r)
+    for (int c = 0; c < 3; ++c) M[r][c] = G[r][0] * W[c][0] + G[r][1] * W[c][1] + G[r][2] * W[c][2];
+  out[0] += M[2][1] - M[1][2];
+  out[1] += M[0][2] - M[2][0];
+  out[2] += M[1][0] - M[0][1];
+  for (int r = 0; r < 3; ++r)
+    out[3 + r] += double(dp[r]) + W[r][0] * double(gm_sh[0]) + W[r][1] * double(gm_sh[1]) + W[r][2] * double(gm_sh[2]);
+}
+
 // --------------------------------------------------------- backward chain
 // Per Gaussian: screen gradients -> parameter gradients.  Sources:
 //   [GSG] "From a pixel's blame to the oval's shape and place": opacity logit factor;
@@ -465,9 +496,11 @@ void blend_pixel_bwd(R px, R py, const uint32_t* list, int64_t n_walk, const R* 
 //         Sigma -> M (dM = 2 dSigma M), scale and quaternion, projection off |q|;
 //   [GSG] "Where the position gradient comes from" and [GST] Jacobian slide: both position paths;
 //   [GSG] "Spherical harmonics": dL/dsh_k = dRGB Y_k and the view-direction term.
+// With camg, the Gaussian's part of the camera-pose gradient is added to it (double[6]):
+// see camera_grad_terms.
 template <class R>
 void chain_one(const R* params, int64_t n, int64_t i, int deg, const Camera& cam, bool smooth,
-               const R* gscreen, R* gparams) {
+               const R* gscreen, R* gparams, double* camg = nullptr) {
   const int P = num_planes(deg);
   for (int pl = 0; pl < P; ++pl) gparams[int64_t(pl) * n + i] = R(0);
   Fwd<R> f = project<R>(params, n, i, deg, cam, smooth);
@@ -495,6 +528,7 @@ void chain_one(const R* params, int64_t n, int64_t i, int deg, const Camera& cam
     const R dd = f.dir[0] * gdir[0] + f.dir[1] * gdir[1] + f.dir[2] * gdir[2];
     for (int a = 0; a < 3; ++a) gm[a] += (gdir[a] - f.dir[a] * dd) / f.dlen;
   }
+  const R gm_sh[3] = {gm[0], gm[1], gm[2]};   // the view-direction part (dL/dcampos = -gm_sh)
   // conic -> dilated covariance: dL/dV' = -K G K, with G the symmetric conic gradient
   const R Km[2][2] = {{f.A, f.B}, {f.B, f.C}};
   const R Gm[2][2] = {{gA, R(0.5) * gB}, {R(0.5) * gB, gC}};
@@ -547,6 +581,7 @@ void chain_one(const R* params, int64_t n, int64_t i, int deg, const Camera& cam
   for (int c = 0; c < 3; ++c)
     for (int r = 0; r < 3; ++r) gm[c] += cam_R<R>(cam, r, c) * dp[r];
   for (int c = 0; c < 3; ++c) GP(c) = gm[c];
+  if (camg) camera_grad_terms<R>(f, cam, dT, dp, gm_sh, camg);
   // Sigma = M M^T -> dM = 2 dSigma M
   R dM[3][3];
   for (int r = 0; r < 3; ++r)
@@ -1145,6 +1180,17 @@ OR_SMOOTH(double, f64)
   }
 OR_CHAIN(float, f32)
 OR_CHAIN(double, f64)
+
+#define OR_CAMERA_GRAD(R, SUF)                                                                                  \
+  void or_camera_grad_##SUF(int64_t n, int deg, const R* params, const Camera* cam, int smooth, const R* gscreen, \
+                            double* out6) {                                                                     \
+    std::vector<R> scratch(size_t(num_planes(deg)) * size_t(n));                                              \
+    for (int k = 0; k < 6; ++k) out6[k] = 0.0;                                                                \
+    for (int64_t i = 0; i < n; ++i)                                                                           \
+      chain_one<R>(params, n, i, deg, *cam, smooth != 0, gscreen, scratch.data(), out6);                      \
+  }
+OR_CAMERA_GRAD(float, f32)
+OR_CAMERA_GRAD(double, f64)
 
 #define OR_LOSS(R, SUF)                                                                                      \
   void or_loss_##SUF(const R* img, const R* tgt, int H, int W, R lambda, R* out3, R* grad) {                  \

@@ -57,6 +57,8 @@ I32 = C.c_int
 def _declare(L):
     L.or_num_planes.argtypes = [I32]
     L.or_set_active_sh_degree.argtypes = [I32]
+    for suf in ("f32", "f64"):
+        getattr(L, f"or_camera_grad_{suf}").argtypes = [I64, I32, P, P, I32, P, P]
     L.or_num_planes.restype = I32
     L.or_sh_norm.argtypes = [I32, I32]
     L.or_sh_norm.restype = C.c_double
@@ -401,3 +403,17 @@ def loss_charbonnier(img, tgt, delta=0.03, log_gain=0.0, bias=0.0, dtype=np.floa
     fn = lib().or_loss_charbonnier_f64 if dtype == np.float64 else lib().or_loss_charbonnier_f32
     fn(_p(img), _p(tgt), img.size, delta, log_gain, bias, _p(out), _p(grad))
     return out[0], grad, out[1], out[2]
+
+
+# ------------------------------------------------------ camera-pose gradient
+def camera_grad(params, sh_degree, cam, gscreen, smooth=False, dtype=np.float32):
+    """Gradient of the loss with respect to the camera pose from the screen partials
+    ([9][n]): (rotation, perturbed on the left as W <- (I + [w]x) W; translation), summed
+    over the visible Gaussians in fp64 (see camera_grad_terms in gs_oracle.cpp)."""
+    params = _c(params, dtype)
+    gscreen = _c(gscreen, dtype)
+    out = np.zeros(6, np.float64)
+    c = make_camera(cam)
+    fn = lib().or_camera_grad_f64 if dtype == np.float64 else lib().or_camera_grad_f32
+    fn(params.shape[1], sh_degree, _p(params), C.byref(c), int(smooth), _p(gscreen), _p(out))
+    return out
