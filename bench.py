@@ -206,6 +206,28 @@ def measure_charbonnier(pl, targets, torch, gs, reps=20):
     return {"ms": round(ms, 4), "bytes": nbytes, "GBps": round(nbytes / (ms / 1000.0) / 1e9, 1)}
 
 
+def measure_camera_grad(pl, cam, torch, gs, reps=20):
+    """The camera-pose gradient (optional, not part of the step) over the benchmark's
+    population, on the screen partials and tile counts the last step left: average of `reps`
+    calls, HIP events.  Algorithmic bytes: every Gaussian's tile count, eleven geometry
+    planes and six screen partials; a visible one's colour planes and colour partials too."""
+    dev = pl.params.device
+    out = torch.zeros(6, dtype=torch.float64, device=dev)
+    ws = gs.workspace(gs.GS_WS_CAMERA_GRAD, n=pl.n)
+    gs.gs_camera_grad(pl.params, pl.deg, pl.proj, cam, pl.gscreen, out, ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(reps):
+        gs.gs_camera_grad(pl.params, pl.deg, pl.proj, cam, pl.gscreen, out, ws)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    n_vis = int((pl.proj.tiles[:pl.n] != 0).sum().item())
+    nbytes = pl.n * (4 + 11 * 4 + 6 * 4) + n_vis * (3 * (pl.deg + 1) ** 2 * 4 + 3 * 4)
+    return {"ms": round(ms, 4), "bytes": nbytes, "GBps": round(nbytes / (ms / 1000.0) / 1e9, 1)}
+
+
 def count_evals(pl, torch):
     """Gaussian-pixel evaluations of the last forward/backward: the forward examines
     entries up to the stopping one (n_contrib for stopped pixels, the whole tile list
@@ -366,6 +388,7 @@ def main():
     del pl2, params2
     densify = measure_densify(pl, cams, targets, args.warmup + args.steps, torch, gs) if not args.no_densify else None
     charbonnier = measure_charbonnier(pl, targets, torch, gs)
+    camera_grad = measure_camera_grad(pl, cams[0], torch, gs)
     t_fb = (stage[:, 2].sum() + stage[:, 4].sum()) / 1000.0
 
     # roofline of the dominant kernel from its live launch times
@@ -407,6 +430,7 @@ def main():
         "roofline": roof,
         "densify": densify,
         "charbonnier_loss": charbonnier,
+        "camera_grad": camera_grad,
         "setup_s": round(setup_s, 2),
     }
     if not args.no_cpu_baseline and args.workload == WORKLOAD_CFG:

@@ -33,16 +33,28 @@ using namespace proj;
 // Plane of colour coefficient k (0 = DC, 1.. = bands) of channel ch.
 __device__ inline int colour_plane(int k, int ch) { return k == 0 ? 11 + ch : 14 + 3 * (k - 1) + ch; }
 
-// Wave 3's part after the colour waves: the geometry gradients and their Adam update
-// (th returns the updated values).
-template <int K, bool ADAM>
-__device__ inline void geometry_tail(float* th, const float* gs6, float* mo, float* vo, uint32_t ntile, int lane,
-                                     size_t gb, const gs_camera& cam, const float (*s_gdir)[3][64],
-                                     float* __restrict__ params, float* __restrict__ gparams, float* __restrict__ m,
-                                     float* __restrict__ v, const AdamArgs& a) {
-  float gp[11];
+// What the camera-pose gradient needs of one Gaussian's chain: the gradients of T = J W
+// (rows dT0, dT1), of the camera-space centre p, and the view-direction part of the mean's
+// gradient; zero, with geom false, when the Gaussian is not visible.
+struct CamPart {
+  float p[3], dT0[3], dT1[3], dp[3], gsh[3];
+  bool geom;
+};
+
+// The eleven geometry gradients of one Gaussian (mean, log-scales, quaternion, opacity
+// logit) from its screen partials gs6 and the colour waves' view-direction partials; with
+// cp, also what the camera-pose gradient needs.
+template <int K>
+__device__ inline void geometry_grads(const float* th, const float* gs6, uint32_t ntile, int lane,
+                                      const gs_camera& cam, const float (*s_gdir)[3][64], float* gp,
+                                      CamPart* cp) {
 #pragma unroll
   for (int k = 0; k < 11; ++k) gp[k] = 0.0f;
+  if (cp) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) cp->p[k] = cp->dT0[k] = cp->dT1[k] = cp->dp[k] = cp->gsh[k] = 0.0f;
+    cp->geom = false;
+  }
   if (K > 0 && ntile != 0u) {
     // the colour's view-direction term, projected off the unit direction
     float dir[3];
@@ -53,6 +65,8 @@ __device__ inline void geometry_tail(float* th, const float* gs6, float* mo, flo
     const float dd = dir[0] * gt[0] + dir[1] * gt[1] + dir[2] * gt[2];
 #pragma unroll
     for (int c = 0; c < 3; ++c) gp[c] = (gt[c] - dir[c] * dd) / dlen;
+    if (cp)
+      for (int c = 0; c < 3; ++c) cp->gsh[c] = gp[c];
   }
   Proj g;
   if (ntile != 0u && project_geometry_from(th, cam, g)) {
@@ -99,6 +113,17 @@ __device__ inline void geometry_tail(float* th, const float* gs6, float* mo, flo
                       dJ12 * (2.0f * fy * g.p[1] / pz3) - gu * fx * g.p[0] / pz2 - gv * fy * g.p[1] / pz2;
     // p = W m + t: dm = W^T dp
     for (int c = 0; c < 3; ++c) gp[c] += cam.R[c] * dp0 + cam.R[3 + c] * dp1 + cam.R[6 + c] * dp2;
+    if (cp) {
+      cp->geom = true;
+      for (int c = 0; c < 3; ++c) {
+        cp->p[c] = g.p[c];
+        cp->dT0[c] = dT0[c];
+        cp->dT1[c] = dT1[c];
+      }
+      cp->dp[0] = dp0;
+      cp->dp[1] = dp1;
+      cp->dp[2] = dp2;
+    }
     // Sigma = M M^T: dM = 2 dSigma M
     float dM[3][3];
     for (int r = 0; r < 3; ++r)
@@ -123,6 +148,17 @@ __device__ inline void geometry_tail(float* th, const float* gs6, float* mo, flo
     const float qd = (w * gq[0] + x * gq[1]) + (y * gq[2] + z * gq[3]);
     for (int k = 0; k < 4; ++k) gp[6 + k] = (gq[k] - g.q[k] * qd) / g.ql;
   }
+}
+
+// Wave 3's part after the colour waves: the geometry gradients and their Adam update
+// (th returns the updated values).
+template <int K, bool ADAM>
+__device__ inline void geometry_tail(float* th, const float* gs6, float* mo, float* vo, uint32_t ntile, int lane,
+                                     size_t gb, const gs_camera& cam, const float (*s_gdir)[3][64],
+                                     float* __restrict__ params, float* __restrict__ gparams, float* __restrict__ m,
+                                     float* __restrict__ v, const AdamArgs& a) {
+  float gp[11];
+  geometry_grads<K>(th, gs6, ntile, lane, cam, s_gdir, gp, nullptr);
 #pragma unroll
   for (int pl = 0; pl < 11; ++pl) {
     const size_t o = gb + pl * kGB;
@@ -314,7 +350,154 @@ void launch_chain_mode(float* params, int n, int deg, const gs_camera& cam, cons
   }
 }
 
+// ---------------------------------------------------------------- camera-pose gradient
+// [GSG] "Forgiving the camera and the light": the loss's gradient with respect to the
+// camera pose, the rotation W perturbed on the left (W <- (I + [w]x) W) and the translation
+// t.  Every Gaussian reaches the pose three ways: through T = J W of its covariance, through
+// its camera-space centre p = W m + t, and through the view direction of its colour (the
+// camera centre is -W^T t).  With G = J^T dT + dp m^T + t gsh^T (gsh: the view-direction
+// part of the mean's gradient, so the centre's gradient is -gsh), dL/dW = G and
+//   dL/dw = (M21 - M12, M02 - M20, M10 - M01) with M = G W^T,   dL/dt = dp + W gsh.
+// The per-Gaussian terms are formed in double from the fp32 chain quantities and summed in
+// double, per wave with a fixed butterfly and over blocks in a fixed order, so the result
+// is reproducible.
+__device__ inline void camera_terms(const CamPart& c, const float* mean, const gs_camera& cam, double* out) {
+  const double fx = cam.fx, fy = cam.fy, pz = c.p[2];
+  const double J[2][3] = {{fx / pz, 0.0, -fx * double(c.p[0]) / (pz * pz)},
+                          {0.0, fy / pz, -fy * double(c.p[1]) / (pz * pz)}};
+  double G[3][3];
+  for (int r = 0; r < 3; ++r)
+    for (int k = 0; k < 3; ++k)
+      G[r][k] = J[0][r] * double(c.dT0[k]) + J[1][r] * double(c.dT1[k]) + double(c.dp[r]) * double(mean[k]) +
+                double(cam.t[r]) * double(c.gsh[k]);
+  double M[3][3];
+  for (int r = 0; r < 3; ++r)
+    for (int k = 0; k < 3; ++k)
+      M[r][k] = G[r][0] * double(cam.R[3 * k]) + G[r][1] * double(cam.R[3 * k + 1]) + G[r][2] * double(cam.R[3 * k + 2]);
+  out[0] = M[2][1] - M[1][2];
+  out[1] = M[0][2] - M[2][0];
+  out[2] = M[1][0] - M[0][1];
+  for (int r = 0; r < 3; ++r)
+    out[3 + r] = double(c.dp[r]) + double(cam.R[3 * r]) * double(c.gsh[0]) +
+                 double(cam.R[3 * r + 1]) * double(c.gsh[1]) + double(cam.R[3 * r + 2]) * double(c.gsh[2]);
+}
+
+// One block per group of 64 Gaussians, the chain kernel's split: waves 0-2 the view-direction
+// partial of one colour channel each, wave 3 the geometry path and the six terms.  Writes
+// the block's sums to part[k * nb + block].
+template <int DEG>
+__global__ void __launch_bounds__(256) camera_grad_kernel(const float* __restrict__ params, int n, gs_camera cam,
+                                                           const uint32_t* __restrict__ tiles,
+                                                           const float* __restrict__ gscreen,
+                                                           double* __restrict__ part, int kact) {
+  constexpr int K = (DEG + 1) * (DEG + 1) - 1;
+  constexpr int P = 11 + 3 * (K + 1);
+  __shared__ float s_gdir[3][3][64];
+  __shared__ float s_mean[3][64];
+  __shared__ uint32_t s_tile[64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + lane;
+  const bool valid = i < n;
+  const size_t gb = size_t(blockIdx.x) * P * kGB + lane;
+  float th[11], gs6[6];
+  uint32_t ntile = 0;
+  if (wv == 3) {
+    if (valid) {
+      ntile = tiles[i];
+#pragma unroll
+      for (int k = 0; k < 11; ++k) th[k] = params[gb + k * kGB];
+#pragma unroll
+      for (int k = 0; k < 6; ++k) gs6[k] = gscreen[size_t(i) * 9 + k];
+    }
+    s_tile[lane] = ntile;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) s_mean[c][lane] = valid ? th[c] : 0.0f;
+  }
+  __syncthreads();
+  if (K > 0 && wv < 3) {
+    const int ch = wv;
+    float gd[3] = {0.f, 0.f, 0.f};
+    if (valid && s_tile[lane] != 0u) {
+      float coef[K + 1];
+#pragma unroll
+      for (int k = 0; k <= K; ++k) coef[k] = params[gb + colour_plane(k, ch) * kGB];
+      float dir[3], Y[16];
+      view_dir_from(s_mean[0][lane], s_mean[1][lane], s_mean[2][lane], cam, dir);
+      sh_eval(dir[0], dir[1], dir[2], Y);
+      float raw = coef[0];
+#pragma unroll
+      for (int k = 1; k <= K; ++k)
+        if (k <= kact) raw = raw + coef[k] * Y[k];
+      const float gc = raw < 0.0f ? 0.0f : gscreen[size_t(i) * 9 + 6 + ch];
+      float wk[16];
+#pragma unroll
+      for (int k = 1; k <= K; ++k) wk[k] = gc * coef[k];
+      sh_grad_dot(dir[0], dir[1], dir[2], wk, kact, gd);
+    }
+#pragma unroll
+    for (int c = 0; c < 3; ++c) s_gdir[ch][c][lane] = gd[c];
+  }
+  __syncthreads();
+  if (wv != 3) return;
+  double t6[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  if (valid && ntile != 0u) {
+    float gp[11];
+    CamPart cp;
+    geometry_grads<K>(th, gs6, ntile, lane, cam, s_gdir, gp, &cp);
+    if (cp.geom) camera_terms(cp, th, cam, t6);
+  }
+#pragma unroll
+  for (int k = 0; k < 6; ++k)
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) t6[k] += __shfl_xor(t6[k], d, 64);
+  if (lane == 0)
+#pragma unroll
+    for (int k = 0; k < 6; ++k) part[size_t(k) * gridDim.x + blockIdx.x] = t6[k];
+}
+
+// out[k] = sum over the nb block sums of component k, one block per component, each
+// thread a fixed stride of them, then a fixed tree.
+__global__ void __launch_bounds__(1024) camera_grad_finalize_kernel(const double* __restrict__ part, int nb,
+                                                                    double* __restrict__ out) {
+  __shared__ double s[1024];
+  const int k = blockIdx.x, t = threadIdx.x;
+  double acc = 0.0;
+  for (int b = t; b < nb; b += 1024) acc += part[size_t(k) * nb + b];
+  s[t] = acc;
+  __syncthreads();
+  for (int w = 512; w >= 1; w >>= 1) {
+    if (t < w) s[t] += s[t + w];
+    __syncthreads();
+  }
+  if (t == 0) out[k] = s[0];
+}
+
 }  // namespace
+
+size_t camera_grad_ws_bytes(int64_t n) { return size_t(div_up(n, 64)) * 6 * sizeof(double); }
+
+hipError_t launch_camera_grad(const float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
+                              const float* gscreen, double* out, void* ws, int kact, hipStream_t s) {
+  double* part = static_cast<double*>(ws);
+  if (n == 0) {
+    camera_grad_finalize_kernel<<<6, 1024, 0, s>>>(part, 0, out);
+    return hipGetLastError();
+  }
+  const int nb = int(div_up(n, 64));
+  {
+    GSK_PROF("camera_grad", s);
+    switch (deg) {
+      case 0: camera_grad_kernel<0><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, kact); break;
+      case 1: camera_grad_kernel<1><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, kact); break;
+      case 2: camera_grad_kernel<2><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, kact); break;
+      default: camera_grad_kernel<3><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, kact); break;
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  camera_grad_finalize_kernel<<<6, 1024, 0, s>>>(part, nb, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_camera& cam,
                                  const uint32_t* tiles, const float* gscreen, float* gparams, int kact,

@@ -191,6 +191,7 @@ size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t
     case GS_WS_RENDER: return (W > 0 && H > 0) ? gsk::render_ws_bytes(W, H, pairs) : 0;
     case GS_WS_DENSIFY: return gsk::densify_ws_bytes(n < 0 ? 0 : n);
     case GS_WS_LOSS_CHARBONNIER: return (W > 0 && H > 0) ? gsk::charbonnier_ws_bytes(H, W) : 0;
+    case GS_WS_CAMERA_GRAD: return gsk::camera_grad_ws_bytes(n < 0 ? 0 : n);
     default: return 0;
   }
 }
@@ -320,6 +321,25 @@ int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t
   e = gsk::launch_preprocess_bwd(scene->params, n, scene->sh_degree, *cam, proj->tiles, gscreen, gparams,
                                  active_bands(scene->sh_degree), s);
   if (e != hipSuccess) return hip_fail(e, "preprocess_bwd");
+  return GS_OK;
+}
+
+int32_t gs_camera_grad(const gs_scene* scene, const gs_proj* proj, const gs_camera* cam, const float* gscreen,
+                       double* grad_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int32_t st;
+  if ((st = check_scene(scene)) != GS_OK) return st;
+  if ((st = check_camera(cam)) != GS_OK) return st;
+  if ((st = check_proj(proj, scene->n, false)) != GS_OK) return st;
+  if (!grad_out) return fail(GS_ERR_INVALID_ARG, "grad_out is null");
+  if (scene->n > 0 && !gscreen) return fail(GS_ERR_INVALID_ARG, "gscreen is null");
+  const size_t need = gs_workspace_bytes(GS_WS_CAMERA_GRAD, scene->n, 0, 0, 0);
+  if (scene->n > 0 && (!ws || ws_bytes < need))
+    return fail(GS_ERR_CAPACITY, "camera-gradient workspace needs %zu bytes", need);
+  const hipError_t e = gsk::launch_camera_grad(scene->params, int(scene->n), scene->sh_degree, *cam, proj->tiles,
+                                               gscreen, grad_out, ws, active_bands(scene->sh_degree),
+                                               as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "camera_grad");
   return GS_OK;
 }
 

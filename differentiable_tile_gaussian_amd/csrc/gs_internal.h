@@ -53,6 +53,11 @@ struct NextProj {
 hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_camera& cam,
                                  const uint32_t* tiles, const float* gscreen, float* gparams, int kact,
                                  hipStream_t s);
+// Camera-pose gradient: out (device double[6]) = (rotation, translation); ws holds
+// camera_grad_ws_bytes(n) bytes of per-block sums.
+size_t camera_grad_ws_bytes(int64_t n);
+hipError_t launch_camera_grad(const float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
+                              const float* gscreen, double* out, void* ws, int kact, hipStream_t s);
 hipError_t launch_chain_adam(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
                              const float* gscreen, float* m, float* v, const AdamArgs& a, int kact, hipStream_t s);
 // The same, then the projection of the updated Gaussians into np (may alias tiles: each

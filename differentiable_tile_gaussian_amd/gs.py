@@ -18,11 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libgs.so")
 
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_UNSUPPORTED, GS_ERR_HIP = 0, -1, -2, -3, -4
 GS_WS_PREPROCESS, GS_WS_BIN_SORT, GS_WS_LOSS, GS_WS_RENDER, GS_WS_DENSIFY, GS_WS_LOSS_CHARBONNIER = 0, 1, 2, 3, 4, 5
+GS_WS_CAMERA_GRAD = 6
 GS_TUNE_SPLIT_FIRST, GS_TUNE_SPLIT_CHUNK = 0, 1
 GS_GRAD_SUMS_FLOAT, GS_GRAD_SUMS_FIXED = 0, 1
 
 EXPORTED = ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
-            "gs_adam_step", "gs_render_bwd_adam", "gs_render_bwd_adam_project", "gs_densify_accumulate",
+            "gs_adam_step", "gs_render_bwd_adam", "gs_render_bwd_adam_project", "gs_camera_grad", "gs_densify_accumulate",
             "gs_densify", "gs_set_grad_sums", "gs_get_grad_sums", "gs_set_active_sh_degree",
             "gs_get_active_sh_degree", "gs_loss_charbonnier", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
             "gs_profile_enable", "gs_profile_query", "gs_param_floats", "gs_params_to_blocked",
@@ -77,6 +78,8 @@ def _load():
     lib.gs_set_grad_sums.restype = I32
     lib.gs_get_grad_sums.argtypes = []
     lib.gs_get_grad_sums.restype = I32
+    lib.gs_camera_grad.argtypes = [P, P, P, P, P, P, C.c_size_t, P]
+    lib.gs_camera_grad.restype = I32
     lib.gs_densify_accumulate.argtypes = [P, I64, P, P, P]
     lib.gs_densify_accumulate.restype = I32
     D = C.c_double
@@ -245,6 +248,17 @@ def gs_render_bwd(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam:
                               C.byref(cam),
                               _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimg), _ptr(gscreen), _ptr(gparams),
                               _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def gs_camera_grad(params, sh_degree, proj: Proj, cam: GsCamera, gscreen, grad_out, ws, stream=None):
+    """grad_out: device float64[6] = (rotation, translation) gradient of the camera pose."""
+    n = proj.n
+    _blocked(params, n, sh_degree)
+    if grad_out.dtype != torch.float64 or grad_out.numel() < 6:
+        raise ValueError("grad_out must hold 6 float64 values")
+    scene = GsScene(n, sh_degree, params.data_ptr() if n else None)
+    _check(_lib.gs_camera_grad(C.byref(scene), C.byref(proj.struct), C.byref(cam), _ptr(gscreen), _ptr(grad_out),
+                               _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def gs_adam_step(params, grads, m, v, n, sh_degree, lr, beta1, beta2, eps, step, stream=None):

@@ -208,6 +208,21 @@ int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t
                       const uint32_t* n_contrib, const float* dL_dimg, float* gscreen, float* gparams, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* Camera-pose gradient ([GSG] "Forgiving the camera and the light": the pose receives the
+ * loss's gradient like any other parameter).  With the rotation perturbed on the left,
+ * W <- (I + [w]x) W, and the translation t (the camera centre is -W^T t), every visible
+ * Gaussian (proj->tiles[i] > 0) contributes through T = J W of its covariance, through its
+ * camera-space centre p = W m + t and through its colour's view direction:
+ *   G = J^T dT + dp m^T + t gsh^T  (= dL/dW; gsh the view-direction part of dL/dm),
+ *   dL/dw = (M21 - M12, M02 - M20, M10 - M01) with M = G W^T,   dL/dt = dp + W gsh.
+ * grad_out: device double[6] = (dL/dw, dL/dt), overwritten.  scene, proj, cam and gscreen as
+ * gs_render_bwd read and left them: the parameters before any update of this step (the fused
+ * update calls overwrite them, so pose optimisation takes gs_render_bwd and gs_adam).  The
+ * per-Gaussian terms are formed in double and summed in a fixed order (the result is
+ * reproducible).  ws: gs_workspace_bytes(GS_WS_CAMERA_GRAD, n, 0, 0, 0).  Enqueues only. */
+int32_t gs_camera_grad(const gs_scene* scene, const gs_proj* proj, const gs_camera* cam, const float* gscreen,
+                       double* grad_out, void* ws, size_t ws_bytes, void* stream);
+
 /* Adam, [GSG] Adam section; per-group rates [DR] "From a pixel error back to a quaternion".
  *   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
  *   theta -= lr_group (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
@@ -299,7 +314,7 @@ int32_t gs_densify(const float* params, const float* m, const float* v, const fl
                    size_t ws_bytes, void* stream);
 
 enum { GS_WS_PREPROCESS = 0, GS_WS_BIN_SORT = 1, GS_WS_LOSS = 2, GS_WS_RENDER = 3, GS_WS_DENSIFY = 4,
-       GS_WS_LOSS_CHARBONNIER = 5 };
+       GS_WS_LOSS_CHARBONNIER = 5, GS_WS_CAMERA_GRAD = 6 };
 
 /* How the backward blend sums the per-pixel gradient contributions of a Gaussian (for the
  * whole process, every backward call enqueued after it; default GS_GRAD_SUMS_FLOAT).

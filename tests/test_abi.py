@@ -110,6 +110,15 @@ def test_argument_errors_without_gpu(gs):
     assert L.gs_loss_charbonnier(1, 1, 0, 8, C.c_float(0.03), 1, 1, 1, None, 1, big, None) == gs.GS_ERR_INVALID_ARG
     assert L.gs_loss_charbonnier(1, None, 8, 8, C.c_float(0.03), 1, 1, 1, None, 1, big, None) == gs.GS_ERR_INVALID_ARG
     assert L.gs_loss_charbonnier(1, 1, 8, 8, C.c_float(0.03), 1, 1, 1, None, None, 0, None) == gs.GS_ERR_CAPACITY
+    # camera-pose gradient: scene, output, gscreen and workspace are checked first
+    sc = gs.GsScene(10, 1, 1234)
+    assert L.gs_camera_grad(None, C.byref(proj), C.byref(cam), 1, 1, 1, big, None) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_camera_grad(C.byref(sc), C.byref(proj), C.byref(cam), 1, None, 1, big, None) == gs.GS_ERR_INVALID_ARG
+    assert "grad_out" in gs.gs_last_error()
+    assert L.gs_camera_grad(C.byref(sc), C.byref(proj), C.byref(cam), None, 1, 1, big, None) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_camera_grad(C.byref(sc), None, C.byref(cam), 1, 1, 1, big, None) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_camera_grad(C.byref(sc), C.byref(proj), C.byref(cam), 1, 1, 1, 47, None) == gs.GS_ERR_CAPACITY
+    assert "camera-gradient workspace" in gs.gs_last_error()
     # SH degree ramp
     assert L.gs_get_active_sh_degree() == -1
     assert L.gs_set_active_sh_degree(4) == gs.GS_ERR_INVALID_ARG
@@ -135,6 +144,8 @@ def test_workspace_sizes_grow_with_the_problem(gs):
     assert gs.gs_workspace_bytes(gs.GS_WS_PREPROCESS, 6_000_000, 0, 0, 0) > 0
     # density control: three flags and three prefix sums per Gaussian
     assert gs.gs_workspace_bytes(gs.GS_WS_DENSIFY, 1_000_000, 0, 0, 0) >= 24 * 1_000_000
+    # camera-pose gradient: six double sums per group of 64 Gaussians
+    assert gs.gs_workspace_bytes(gs.GS_WS_CAMERA_GRAD, 1_000_000, 0, 0, 0) == 15625 * 48
     assert gs.gs_workspace_bytes(99, 1, 1, 1, 1) == 0
 
 
