@@ -138,6 +138,15 @@ inline int num_planes(int deg) { return 11 + 3 * (deg + 1) * (deg + 1); }
 // band weights are summed, and the inactive ones receive no gradient until their band
 // switches on).  -1: every stored band.  Set by or_set_active_sh_degree.
 int g_active_deg = -1;
+// Mip-Splatting opacity compensation ([GSG] "Flattening a 3D blob into a 2D oval": a small
+// factor keeps tiny blobs from adding spurious energy; the code there multiplies the
+// opacity by comp in the extent and in alpha).  Off (0) by default; set by
+// or_set_mip_compensation.  The factor is not printed on the pages; the reading taken is
+// the one that removes exactly the energy the 0.3 px^2 dilation adds: the footprint
+// o exp(-d^T V^-1 d / 2) integrates to o 2 pi sqrt(det V), so the dilated footprint keeps
+// that integral with comp = sqrt(det V / det(V + 0.3 I)) (0 when det V <= 0).
+int g_mip = 0;
+
 inline int active_bands(int deg) {
   const int d = (g_active_deg < 0 || g_active_deg > deg) ? deg : g_active_deg;
   return (d + 1) * (d + 1) - 1;
@@ -167,7 +176,9 @@ struct Fwd {
   R t0[3], t1[3];        // rows of T = J W
   R a, b, c, det;        // dilated screen covariance [[a, b], [b, c]] and its determinant
   R A, B, C;             // conic
-  R o;                   // opacity
+  R o;                   // opacity of the record (ob comp with the Mip compensation, else ob)
+  R ob, comp;            // sigmoid of the logit; the compensation factor (1 when off)
+  R va, vb, vc, detv;    // undilated screen covariance and its determinant
   R dvec[3], dlen, dir[3];
   R Y[16], dY[16][3];
   R raw[3], rgb[3];      // colour before / after the clamp at zero
@@ -246,7 +257,17 @@ Fwd<R> project(const R* params, int64_t n, int64_t i, int deg, const Camera& cam
   f.A = f.c / f.det;
   f.B = -f.b / f.det;
   f.C = f.a / f.det;
-  f.o = sigmoid_r(P(10));
+  f.ob = sigmoid_r(P(10));
+  f.va = V00;
+  f.vb = V01;
+  f.vc = V11;
+  f.detv = V00 * V11 - V01 * V01;
+  f.comp = R(1);
+  f.o = f.ob;
+  if (g_mip) {
+    f.comp = std::sqrt(std::max(f.detv, R(0)) / f.det);
+    f.o = f.ob * f.comp;
+  }
   // colour: DC plus the (active) higher bands along dir = normalize(m - campos)
   const int K = active_bands(deg);
   for (int k = 0; k < 3; ++k) f.dvec[k] = f.m[k] - R(cam.campos[k]);
@@ -508,8 +529,8 @@ void chain_one(const R* params, int64_t n, int64_t i, int deg, const Camera& cam
   auto GS = [&](int k) { return gscreen[int64_t(k) * n + i]; };
   auto GP = [&](int plane) -> R& { return gparams[int64_t(plane) * n + i]; };
   const R gu = GS(0), gv = GS(1), gA = GS(2), gB = GS(3), gC = GS(4), go = GS(5);
-  // opacity logit
-  GP(10) = go * f.o * (R(1) - f.o);
+  // opacity logit (through the compensation factor when it is on)
+  GP(10) = g_mip ? go * f.comp * f.ob * (R(1) - f.ob) : go * f.o * (R(1) - f.o);
   // colour -> DC, the active higher bands (the others get none), view direction
   const int K = active_bands(deg);
   R gc[3];
@@ -537,7 +558,17 @@ void chain_one(const R* params, int64_t n, int64_t i, int deg, const Camera& cam
     for (int c = 0; c < 2; ++c) KG[r][c] = Km[r][0] * Gm[0][c] + Km[r][1] * Gm[1][c];
   for (int r = 0; r < 2; ++r)
     for (int c = 0; c < 2; ++c) KGK[r][c] = KG[r][0] * Km[0][c] + KG[r][1] * Km[1][c];
-  const R gV00 = -KGK[0][0], gV01 = -(KGK[0][1] + KGK[1][0]), gV11 = -KGK[1][1];
+  R gV00 = -KGK[0][0], gV01 = -(KGK[0][1] + KGK[1][0]), gV11 = -KGK[1][1];
+  // the compensation factor comp = sqrt(det V / det V') with V' = V + 0.3 I:
+  //   d comp = comp / 2 (d det V / det V - d det V' / det V'),
+  //   d det V = (vc, -2 vb, va) . (d va, d vb, d vc), and the same for V' with (c, b, a)
+  if (g_mip && f.detv > R(0)) {
+    const R gcomp = go * f.ob;
+    const R h = R(0.5) * f.comp;
+    gV00 += gcomp * h * (f.vc / f.detv - f.c / f.det);
+    gV11 += gcomp * h * (f.va / f.detv - f.a / f.det);
+    gV01 += gcomp * h * (R(2) * f.b / f.det - R(2) * f.vb / f.detv);
+  }
   // V = T Sigma T^T:  dSigma = T^T H T,  dT = 2 H T Sigma
   const R H[2][2] = {{gV00, R(0.5) * gV01}, {R(0.5) * gV01, gV11}};
   const R* Tr[2] = {f.t0, f.t1};
@@ -908,6 +939,7 @@ extern "C" {
 
 int or_num_planes(int deg) { return num_planes(deg); }
 void or_set_active_sh_degree(int d) { g_active_deg = d; }
+void or_set_mip_compensation(int on) { g_mip = on ? 1 : 0; }
 
 // Scalar helpers for the SH pins.
 double or_sh_norm(int l, int m) { return sh_norm(l, m); }

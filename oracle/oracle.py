@@ -57,6 +57,7 @@ I32 = C.c_int
 def _declare(L):
     L.or_num_planes.argtypes = [I32]
     L.or_set_active_sh_degree.argtypes = [I32]
+    L.or_set_mip_compensation.argtypes = [I32]
     for suf in ("f32", "f64"):
         getattr(L, f"or_camera_grad_{suf}").argtypes = [I64, I32, P, P, I32, P, P]
     L.or_num_planes.restype = I32
@@ -104,6 +105,12 @@ def num_planes(deg):
 def set_active_sh_degree(d):
     """SH degree ramp: only bands up to d are evaluated and receive gradients (-1: all)."""
     lib().or_set_active_sh_degree(int(d))
+
+
+def set_mip_compensation(on):
+    """Mip-Splatting opacity compensation: the record's opacity becomes
+    sigmoid(logit) sqrt(det V / det(V + 0.3 I)) (off by default)."""
+    lib().or_set_mip_compensation(int(bool(on)))
 
 
 # ----------------------------------------------------------------- forward
