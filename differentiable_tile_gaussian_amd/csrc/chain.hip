@@ -46,7 +46,7 @@ struct CamPart {
 // cp, also what the camera-pose gradient needs.
 template <int K>
 __device__ inline void geometry_grads(const float* th, const float* gs6, uint32_t ntile, int lane,
-                                      const gs_camera& cam, const float (*s_gdir)[3][64], float* gp,
+                                      const gs_camera& cam, int mip, const float (*s_gdir)[3][64], float* gp,
                                       CamPart* cp) {
 #pragma unroll
   for (int k = 0; k < 11; ++k) gp[k] = 0.0f;
@@ -69,17 +69,26 @@ __device__ inline void geometry_grads(const float* th, const float* gs6, uint32_
       for (int c = 0; c < 3; ++c) cp->gsh[c] = gp[c];
   }
   Proj g;
-  if (ntile != 0u && project_geometry_from(th, cam, g)) {
+  if (ntile != 0u && project_geometry_from(th, cam, mip, g)) {
     const float gu = gs6[0], gv = gs6[1], gA = gs6[2], gB = gs6[3], gC = gs6[4], go = gs6[5];
-    // opacity logit through the sigmoid
-    gp[10] = go * g.o * (1.0f - g.o);
+    // opacity logit through the sigmoid (and the compensation factor when it is on)
+    gp[10] = mip ? go * g.comp * g.ob * (1.0f - g.ob) : go * g.o * (1.0f - g.o);
     // conic -> dilated covariance: dV' = -K Gk K with Gk = [[gA, gB/2], [gB/2, gC]]
     const float hB = 0.5f * gB;
     const float kg00 = g.A * gA + g.B * hB, kg01 = g.A * hB + g.B * gC;
     const float kg10 = g.B * gA + g.C * hB, kg11 = g.B * hB + g.C * gC;
     const float p00 = kg00 * g.A + kg01 * g.B, p01 = kg00 * g.B + kg01 * g.C;
     const float p10 = kg10 * g.A + kg11 * g.B, p11 = kg10 * g.B + kg11 * g.C;
-    const float gV00 = -p00, gV01 = -(p01 + p10), gV11 = -p11;
+    float gV00 = -p00, gV01 = -(p01 + p10), gV11 = -p11;
+    if (mip && g.detv > 0.0f) {
+      // comp = sqrt(det V / det V'), V' = V + 0.3 I: d comp = comp / 2 (d det V / det V -
+      // d det V' / det V'), d det V = (v11, -2 b, v00) . (d v00, d b, d v11), and for V' (c, -2 b, a)
+      const float gcomp = go * g.ob;
+      const float h = 0.5f * g.comp;
+      gV00 += gcomp * h * (g.v11 / g.detv - g.c / g.det);
+      gV11 += gcomp * h * (g.v00 / g.detv - g.a / g.det);
+      gV01 += gcomp * h * (2.0f * g.b / g.det - 2.0f * g.b / g.detv);
+    }
     // V = T Sigma T^T: H = [[gV00, gV01/2], [gV01/2, gV11]]
     const float h00 = gV00, h01 = 0.5f * gV01, h11 = gV11;
     // U = H T (rows u0, u1)
@@ -154,11 +163,11 @@ __device__ inline void geometry_grads(const float* th, const float* gs6, uint32_
 // (th returns the updated values).
 template <int K, bool ADAM>
 __device__ inline void geometry_tail(float* th, const float* gs6, float* mo, float* vo, uint32_t ntile, int lane,
-                                     size_t gb, const gs_camera& cam, const float (*s_gdir)[3][64],
+                                     size_t gb, const gs_camera& cam, int mip, const float (*s_gdir)[3][64],
                                      float* __restrict__ params, float* __restrict__ gparams, float* __restrict__ m,
                                      float* __restrict__ v, const AdamArgs& a) {
   float gp[11];
-  geometry_grads<K>(th, gs6, ntile, lane, cam, s_gdir, gp, nullptr);
+  geometry_grads<K>(th, gs6, ntile, lane, cam, mip, s_gdir, gp, nullptr);
 #pragma unroll
   for (int pl = 0; pl < 11; ++pl) {
     const size_t o = gb + pl * kGB;
@@ -179,7 +188,7 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
                                                      const uint32_t* tiles,   // may be np.tiles
                                                      const float* __restrict__ gscreen, float* __restrict__ gparams,
                                                      float* __restrict__ m, float* __restrict__ v, AdamArgs a,
-                                                     NextProj np, float2* __restrict__ dstats, int kact) {
+                                                     NextProj np, float2* __restrict__ dstats, Shade shade) {
   constexpr int K = (DEG + 1) * (DEG + 1) - 1;
   constexpr int P = 11 + 3 * (K + 1);
   __shared__ float s_gdir[3][3][64];   // view-direction partials of each colour channel
@@ -247,7 +256,7 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
       float raw = coef[0];
 #pragma unroll
       for (int k = 1; k <= K; ++k)
-        if (k <= kact) raw = raw + coef[k] * Y[k];
+        if (k <= shade.kact) raw = raw + coef[k] * Y[k];
       gc = raw < 0.0f ? 0.0f : gcol;
     }
     if (K > 0) {
@@ -256,7 +265,7 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
         float wk[16];
 #pragma unroll
         for (int k = 1; k <= K; ++k) wk[k] = gc * coef[k];
-        sh_grad_dot(dir[0], dir[1], dir[2], wk, kact, gd);   // the active bands only
+        sh_grad_dot(dir[0], dir[1], dir[2], wk, shade.kact, gd);   // the active bands only
       }
 #pragma unroll
       for (int c = 0; c < 3; ++c) s_gdir[ch][c][lane] = gd[c];
@@ -264,7 +273,7 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
     if (valid) {
 #pragma unroll
       for (int k = 0; k <= K; ++k) {
-        const float g = k == 0 ? gc : (vis && k <= kact ? gc * Y[k] : 0.0f);
+        const float g = k == 0 ? gc : (vis && k <= shade.kact ? gc * Y[k] : 0.0f);
         const size_t o = gb + colour_plane(k, ch) * kGB;
         if (ADAM) {
           coef[k] = adam_update(coef[k], g, cmo[k], cvo[k], a.lr[4], a);
@@ -285,7 +294,7 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
       st.y += 1.0f;
       dstats[i] = st;
     }
-    geometry_tail<K, ADAM>(th, gs6, mo, vo, ntile, lane, gb, cam, s_gdir, params, gparams, m, v, a);
+    geometry_tail<K, ADAM>(th, gs6, mo, vo, ntile, lane, gb, cam, shade.mip, s_gdir, params, gparams, m, v, a);
   }
   if (!PROJ) return;
   // ---- projection of the updated Gaussians for the next camera
@@ -293,7 +302,7 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
   bool geom = false;
   if (wv == 3) {
     if (valid) {
-      geom = project_geometry_from(th, np.cam, g);
+      geom = project_geometry_from(th, np.cam, shade.mip, g);
       if (K > 0) {
         float dir[3];
         view_dir_from(th[0], th[1], th[2], np.cam, dir);
@@ -309,7 +318,7 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
     float raw = coef[0];
 #pragma unroll
     for (int k = 1; k <= K; ++k)
-      if (k <= kact) raw = raw + coef[k] * Y[k];
+      if (k <= shade.kact) raw = raw + coef[k] * Y[k];
     s_nraw[ch][lane] = raw;
   }
   __syncthreads();   // next colours
@@ -332,21 +341,21 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
 template <int DEG, bool ADAM, bool PROJ>
 void launch_chain_deg(float* params, int n, const gs_camera& cam, const uint32_t* tiles, const float* gscreen,
                       float* gparams, float* m, float* v, const AdamArgs& a, const NextProj& np, float* dstats,
-                      int kact, hipStream_t s) {
+                      Shade shade, hipStream_t s) {
   GSK_PROF("chain", s);
   chain_kernel<DEG, ADAM, PROJ><<<div_up(n, 64), 256, 0, s>>>(params, n, cam, tiles, gscreen, gparams, m, v, a, np,
-                                                              reinterpret_cast<float2*>(dstats), kact);
+                                                              reinterpret_cast<float2*>(dstats), shade);
 }
 
 template <bool ADAM, bool PROJ>
 void launch_chain_mode(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles, const float* gscreen,
                        float* gparams, float* m, float* v, const AdamArgs& a, const NextProj& np, float* dstats,
-                       int kact, hipStream_t s) {
+                       Shade shade, hipStream_t s) {
   switch (deg) {
-    case 0: launch_chain_deg<0, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, kact, s); break;
-    case 1: launch_chain_deg<1, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, kact, s); break;
-    case 2: launch_chain_deg<2, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, kact, s); break;
-    default: launch_chain_deg<3, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, kact, s); break;
+    case 0: launch_chain_deg<0, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, shade, s); break;
+    case 1: launch_chain_deg<1, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, shade, s); break;
+    case 2: launch_chain_deg<2, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, shade, s); break;
+    default: launch_chain_deg<3, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, shade, s); break;
   }
 }
 
@@ -389,7 +398,7 @@ template <int DEG>
 __global__ void __launch_bounds__(256) camera_grad_kernel(const float* __restrict__ params, int n, gs_camera cam,
                                                            const uint32_t* __restrict__ tiles,
                                                            const float* __restrict__ gscreen,
-                                                           double* __restrict__ part, int kact) {
+                                                           double* __restrict__ part, Shade shade) {
   constexpr int K = (DEG + 1) * (DEG + 1) - 1;
   constexpr int P = 11 + 3 * (K + 1);
   __shared__ float s_gdir[3][3][64];
@@ -427,12 +436,12 @@ __global__ void __launch_bounds__(256) camera_grad_kernel(const float* __restric
       float raw = coef[0];
 #pragma unroll
       for (int k = 1; k <= K; ++k)
-        if (k <= kact) raw = raw + coef[k] * Y[k];
+        if (k <= shade.kact) raw = raw + coef[k] * Y[k];
       const float gc = raw < 0.0f ? 0.0f : gscreen[size_t(i) * 9 + 6 + ch];
       float wk[16];
 #pragma unroll
       for (int k = 1; k <= K; ++k) wk[k] = gc * coef[k];
-      sh_grad_dot(dir[0], dir[1], dir[2], wk, kact, gd);
+      sh_grad_dot(dir[0], dir[1], dir[2], wk, shade.kact, gd);
     }
 #pragma unroll
     for (int c = 0; c < 3; ++c) s_gdir[ch][c][lane] = gd[c];
@@ -443,7 +452,7 @@ __global__ void __launch_bounds__(256) camera_grad_kernel(const float* __restric
   if (valid && ntile != 0u) {
     float gp[11];
     CamPart cp;
-    geometry_grads<K>(th, gs6, ntile, lane, cam, s_gdir, gp, &cp);
+    geometry_grads<K>(th, gs6, ntile, lane, cam, shade.mip, s_gdir, gp, &cp);
     if (cp.geom) camera_terms(cp, th, cam, t6);
   }
 #pragma unroll
@@ -477,7 +486,7 @@ __global__ void __launch_bounds__(1024) camera_grad_finalize_kernel(const double
 size_t camera_grad_ws_bytes(int64_t n) { return size_t(div_up(n, 64)) * 6 * sizeof(double); }
 
 hipError_t launch_camera_grad(const float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
-                              const float* gscreen, double* out, void* ws, int kact, hipStream_t s) {
+                              const float* gscreen, double* out, void* ws, Shade shade, hipStream_t s) {
   double* part = static_cast<double*>(ws);
   if (n == 0) {
     camera_grad_finalize_kernel<<<6, 1024, 0, s>>>(part, 0, out);
@@ -487,10 +496,10 @@ hipError_t launch_camera_grad(const float* params, int n, int deg, const gs_came
   {
     GSK_PROF("camera_grad", s);
     switch (deg) {
-      case 0: camera_grad_kernel<0><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, kact); break;
-      case 1: camera_grad_kernel<1><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, kact); break;
-      case 2: camera_grad_kernel<2><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, kact); break;
-      default: camera_grad_kernel<3><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, kact); break;
+      case 0: camera_grad_kernel<0><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, shade); break;
+      case 1: camera_grad_kernel<1><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, shade); break;
+      case 2: camera_grad_kernel<2><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, shade); break;
+      default: camera_grad_kernel<3><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, shade); break;
     }
   }
   hipError_t e = hipGetLastError();
@@ -500,27 +509,27 @@ hipError_t launch_camera_grad(const float* params, int n, int deg, const gs_came
 }
 
 hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_camera& cam,
-                                 const uint32_t* tiles, const float* gscreen, float* gparams, int kact,
+                                 const uint32_t* tiles, const float* gscreen, float* gparams, Shade shade,
                                  hipStream_t s) {
   if (n == 0) return hipSuccess;
   launch_chain_mode<false, false>(const_cast<float*>(params), n, deg, cam, tiles, gscreen, gparams, nullptr, nullptr,
-                                  AdamArgs{}, NextProj{}, nullptr, kact, s);
+                                  AdamArgs{}, NextProj{}, nullptr, shade, s);
   return hipGetLastError();
 }
 
 hipError_t launch_chain_adam(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
-                             const float* gscreen, float* m, float* v, const AdamArgs& a, int kact, hipStream_t s) {
+                             const float* gscreen, float* m, float* v, const AdamArgs& a, Shade shade, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  launch_chain_mode<true, false>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, NextProj{}, nullptr, kact,
+  launch_chain_mode<true, false>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, NextProj{}, nullptr, shade,
                                  s);
   return hipGetLastError();
 }
 
 hipError_t launch_chain_adam_project(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
                                      const float* gscreen, float* m, float* v, const AdamArgs& a,
-                                     const NextProj& np, float* dstats, int kact, hipStream_t s) {
+                                     const NextProj& np, float* dstats, Shade shade, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  launch_chain_mode<true, true>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, np, dstats, kact, s);
+  launch_chain_mode<true, true>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, np, dstats, shade, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_tile_count_total(np.block_tiles, int(div_up(n, 64)), np.total, s);

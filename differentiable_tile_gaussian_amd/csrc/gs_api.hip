@@ -17,11 +17,16 @@ std::atomic<int> g_fixed_sums{0};
 // SH degree ramp (gs_set_active_sh_degree), for the whole process: -1 = every stored band.
 std::atomic<int> g_active_deg{-1};
 
-// The active higher bands for a stored degree: (d + 1)^2 - 1 with d the smaller of the two.
-int active_bands(int deg) {
+// Mip-Splatting opacity compensation (gs_set_mip_compensation), for the whole process.
+std::atomic<int> g_mip{0};
+
+// How the kernels shade a scene of a stored degree: the active higher bands,
+// (d + 1)^2 - 1 with d the smaller of the stored and the active degree, and the
+// compensation switch.
+gsk::Shade shade_of(int deg) {
   const int a = g_active_deg.load();
   const int d = (a < 0 || a > deg) ? deg : a;
-  return (d + 1) * (d + 1) - 1;
+  return gsk::Shade{(d + 1) * (d + 1) - 1, g_mip.load()};
 }
 
 thread_local char g_err[512] = "";
@@ -148,6 +153,15 @@ int32_t gs_set_active_sh_degree(int32_t degree) {
 
 int32_t gs_get_active_sh_degree(void) { return g_active_deg.load(); }
 
+int32_t gs_set_mip_compensation(int32_t on) {
+  g_err[0] = 0;
+  if (on != 0 && on != 1) return fail(GS_ERR_INVALID_ARG, "Mip compensation switch must be 0 or 1");
+  g_mip = on;
+  return GS_OK;
+}
+
+int32_t gs_get_mip_compensation(void) { return g_mip.load(); }
+
 int32_t gs_set_tuning(int32_t key, int64_t value) {
   g_err[0] = 0;
   if (value < 4 || value > (int64_t(1) << 24) || (value & 3))
@@ -210,7 +224,7 @@ int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out,
   const int n = int(scene->n);
   PreWs w = carve_pre(ws, n);
   hipError_t e = gsk::launch_preprocess_fwd(scene->params, n, scene->sh_degree, *cam, *out, w.block_tiles,
-                                            w.total64, active_bands(scene->sh_degree), s);
+                                            w.total64, shade_of(scene->sh_degree), s);
   if (e != hipSuccess) return hip_fail(e, "preprocess_fwd");
   return finish_preprocess(out, n, w, total_pairs, s);
 }
@@ -319,7 +333,7 @@ int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t
                                         gscreen, ws, g_fixed_sums != 0, s);
   if (e != hipSuccess) return hip_fail(e, "render_bwd");
   e = gsk::launch_preprocess_bwd(scene->params, n, scene->sh_degree, *cam, proj->tiles, gscreen, gparams,
-                                 active_bands(scene->sh_degree), s);
+                                 shade_of(scene->sh_degree), s);
   if (e != hipSuccess) return hip_fail(e, "preprocess_bwd");
   return GS_OK;
 }
@@ -337,7 +351,7 @@ int32_t gs_camera_grad(const gs_scene* scene, const gs_proj* proj, const gs_came
   if (scene->n > 0 && (!ws || ws_bytes < need))
     return fail(GS_ERR_CAPACITY, "camera-gradient workspace needs %zu bytes", need);
   const hipError_t e = gsk::launch_camera_grad(scene->params, int(scene->n), scene->sh_degree, *cam, proj->tiles,
-                                               gscreen, grad_out, ws, active_bands(scene->sh_degree),
+                                               gscreen, grad_out, ws, shade_of(scene->sh_degree),
                                                as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "camera_grad");
   return GS_OK;
@@ -391,7 +405,7 @@ int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs
                                         dL_dimg, gscreen, ws, g_fixed_sums != 0, s);
   if (e != hipSuccess) return hip_fail(e, "render_bwd");
   e = gsk::launch_chain_adam(params, int(n), sh_degree, *cam, proj->tiles, gscreen, m, v,
-                             adam_args(lr, beta1, beta2, eps, step), active_bands(sh_degree), s);
+                             adam_args(lr, beta1, beta2, eps, step), shade_of(sh_degree), s);
   if (e != hipSuccess) return hip_fail(e, "chain_adam");
   return GS_OK;
 }
@@ -438,7 +452,7 @@ int32_t gs_render_bwd_adam_project(float* params, int64_t n, int32_t sh_degree, 
   np.total = w.total64;
   e = gsk::launch_chain_adam_project(params, int(n), sh_degree, *cam, proj->tiles, gscreen, m, v,
                                      adam_args(lr, beta1, beta2, eps, step), np, densify_stats,
-                                     active_bands(sh_degree), s);
+                                     shade_of(sh_degree), s);
   if (e != hipSuccess) return hip_fail(e, "chain_adam_project");
   return finish_preprocess(next_out, int(n), w, next_total_pairs, s);
 }

@@ -28,11 +28,18 @@ __host__ __device__ inline T* gaussian_base(T* params, int i, int P) {
   return params + size_t(i / kGB) * size_t(P) * kGB + (i % kGB);
 }
 
+// How a Gaussian is shaded, for the projection and its gradient: kact, the active SH
+// bands ((d + 1)^2 - 1 for an active degree d; the degree ramp), and mip, whether the
+// Mip-Splatting compensation sqrt(det V / det(V + 0.3 I)) multiplies the opacity.
+struct Shade {
+  int kact;
+  int mip;
+};
+
 // ---- preprocess.hip
 // block_tiles: div_up(n, 256) per-block sums of the tile counts; *total_pairs their sum.
-// kact (here and in the chain): the active SH bands, (d + 1)^2 - 1 for an active degree d.
 hipError_t launch_preprocess_fwd(const float* params, int n, int deg, const gs_camera& cam, const gs_proj& out,
-                                 uint32_t* block_tiles, uint64_t* total_pairs, int kact, hipStream_t s);
+                                 uint32_t* block_tiles, uint64_t* total_pairs, Shade shade, hipStream_t s);
 // *total += the sum of block_tiles[0 .. nb) (the caller's kernel zeroed *total).
 hipError_t launch_tile_count_total(const uint32_t* block_tiles, int nb, uint64_t* total, hipStream_t s);
 
@@ -51,21 +58,21 @@ struct NextProj {
   uint64_t* total;
 };
 hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_camera& cam,
-                                 const uint32_t* tiles, const float* gscreen, float* gparams, int kact,
+                                 const uint32_t* tiles, const float* gscreen, float* gparams, Shade shade,
                                  hipStream_t s);
 // Camera-pose gradient: out (device double[6]) = (rotation, translation); ws holds
 // camera_grad_ws_bytes(n) bytes of per-block sums.
 size_t camera_grad_ws_bytes(int64_t n);
 hipError_t launch_camera_grad(const float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
-                              const float* gscreen, double* out, void* ws, int kact, hipStream_t s);
+                              const float* gscreen, double* out, void* ws, Shade shade, hipStream_t s);
 hipError_t launch_chain_adam(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
-                             const float* gscreen, float* m, float* v, const AdamArgs& a, int kact, hipStream_t s);
+                             const float* gscreen, float* m, float* v, const AdamArgs& a, Shade shade, hipStream_t s);
 // The same, then the projection of the updated Gaussians into np (may alias tiles: each
 // Gaussian's count is read before its new record is written) and np's pair count; with
 // dstats ([n][2], nullable) also the density statistics of this step's observations.
 hipError_t launch_chain_adam_project(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
                                      const float* gscreen, float* m, float* v, const AdamArgs& a,
-                                     const NextProj& np, float* dstats, int kact, hipStream_t s);
+                                     const NextProj& np, float* dstats, Shade shade, hipStream_t s);
 
 // ---- scan.hip: exclusive prefix sum of n u32 values into out[0..n], out[n] = total.
 // The total is also written as u64 to *total64 (device) so that overflow of 32 bits is seen.

@@ -21,26 +21,25 @@ namespace {
 
 using namespace proj;
 
-// One Gaussian: writes its projected record and returns its tile count.  kact: the
-// active bands (the SH degree ramp; K for every stored band).
+// One Gaussian: writes its projected record and returns its tile count.
 template <int DEG>
 __device__ inline uint32_t project_one(const float* __restrict__ params, int i, const gs_camera& cam, int tx, int ty,
-                                       int kact, float4* __restrict__ splat, float* __restrict__ depth,
+                                       Shade shade, float4* __restrict__ splat, float* __restrict__ depth,
                                        uint2* __restrict__ rect, uint32_t* __restrict__ tiles) {
   constexpr int K = (DEG + 1) * (DEG + 1) - 1;
   constexpr int P = 11 + 3 * (K + 1);
   const float* g0 = gaussian_base(params, i, P);
   Proj g;
-  const bool geom = project_geometry(g0, cam, g);
+  const bool geom = project_geometry(g0, cam, shade.mip, g);
   float raw[3] = {0.f, 0.f, 0.f};
   if (geom) {
     float Y[16];
-    if (kact > 0) {
+    if (shade.kact > 0) {
       float dir[3];
       view_dir(g0, cam, dir);
       sh_eval(dir[0], dir[1], dir[2], Y);
     }
-    sh_colour(g0, kact, Y, raw);
+    sh_colour(g0, shade.kact, Y, raw);
   }
   Record r;
   make_record(geom, g, raw, tx, ty, r);
@@ -54,11 +53,11 @@ __global__ void __launch_bounds__(256) preprocess_fwd_kernel(const float* __rest
                                                               float* __restrict__ depth, uint2* __restrict__ rect,
                                                               uint32_t* __restrict__ tiles,
                                                               uint32_t* __restrict__ block_tiles,
-                                                              uint64_t* __restrict__ total, int kact) {
+                                                              uint64_t* __restrict__ total, Shade shade) {
   __shared__ uint32_t s_wave[4];
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i == 0) *total = 0u;   // sum_counts_kernel adds into it after this kernel
-  const uint32_t cnt = i < n ? project_one<DEG>(params, i, cam, tx, ty, kact, splat, depth, rect, tiles) : 0u;
+  const uint32_t cnt = i < n ? project_one<DEG>(params, i, cam, tx, ty, shade, splat, depth, rect, tiles) : 0u;
   // the block's total of tile counts (the pair count is the sum over blocks)
   uint32_t v = cnt;
 #pragma unroll
@@ -89,7 +88,7 @@ __global__ void __launch_bounds__(1024) sum_counts_kernel(const uint32_t* __rest
 }  // namespace
 
 hipError_t launch_preprocess_fwd(const float* params, int n, int deg, const gs_camera& cam, const gs_proj& out,
-                                 uint32_t* block_tiles, uint64_t* total_pairs, int kact, hipStream_t s) {
+                                 uint32_t* block_tiles, uint64_t* total_pairs, Shade shade, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const dim3 grid(div_up(n, 256)), block(256);
   const int tx = tiles_x(cam), ty = tiles_y(cam);
@@ -98,10 +97,10 @@ hipError_t launch_preprocess_fwd(const float* params, int n, int deg, const gs_c
   {
     GSK_PROF("preprocess_fwd", s);
     switch (deg) {
-      case 0: preprocess_fwd_kernel<0><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles, total_pairs, kact); break;
-      case 1: preprocess_fwd_kernel<1><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles, total_pairs, kact); break;
-      case 2: preprocess_fwd_kernel<2><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles, total_pairs, kact); break;
-      default: preprocess_fwd_kernel<3><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles, total_pairs, kact); break;
+      case 0: preprocess_fwd_kernel<0><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles, total_pairs, shade); break;
+      case 1: preprocess_fwd_kernel<1><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles, total_pairs, shade); break;
+      case 2: preprocess_fwd_kernel<2><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles, total_pairs, shade); break;
+      default: preprocess_fwd_kernel<3><<<grid, block, 0, s>>>(params, n, cam, tx, ty, splat, out.depth, rect, out.tiles, block_tiles, total_pairs, shade); break;
     }
   }
   return launch_tile_count_total(block_tiles, int(grid.x), total_pairs, s);

@@ -99,14 +99,19 @@ struct Proj {
   float t0[3], t1[3];    // rows of T = J W
   float a, b, c, det;    // dilated screen covariance
   float A, B, C;         // conic
-  float o;
+  float o;               // the record's opacity: ob comp with the Mip compensation, else ob
+  float ob, comp;        // sigmoid of the logit; the compensation factor (1 when off)
+  float v00, v11, detv;  // undilated screen covariance (its off-diagonal is b) and determinant
 };
 
 // Geometry of one Gaussian ([GST] parameter and Jacobian slides; [DR] "Forward";
 // [GSG] "Flattening a 3D blob into a 2D oval").  Returns false when culled (behind the
 // near plane, zero quaternion, non-positive determinant).
 // th: the 11 geometry parameters (mean 0-2, log-scales 3-5, quaternion 6-9, logit 10).
-__device__ inline bool project_geometry_from(const float* th, const gs_camera& cam, Proj& g) {
+// mip: the opacity is multiplied by comp = sqrt(det V / det(V + 0.3 I)) ([GSG] same section:
+// the Mip-Splatting factor that keeps tiny blobs from adding energy; this ratio gives the
+// dilated footprint exactly the integral of the undilated one), 0 when det V <= 0.
+__device__ inline bool project_geometry_from(const float* th, const gs_camera& cam, int mip, Proj& g) {
   const float mx = th[0], my = th[1], mz = th[2];
   for (int r = 0; r < 3; ++r)
     g.p[r] = ((cam.R[3 * r] * mx + cam.R[3 * r + 1] * my) + cam.R[3 * r + 2] * mz) + cam.t[r];
@@ -169,16 +174,25 @@ __device__ inline bool project_geometry_from(const float* th, const gs_camera& c
   g.A = g.c / g.det;
   g.B = -g.b / g.det;
   g.C = g.a / g.det;
-  g.o = float(1.0 / (1.0 + exp(-double(th[10]))));
+  g.ob = float(1.0 / (1.0 + exp(-double(th[10]))));
+  g.v00 = V00;
+  g.v11 = V11;
+  g.detv = V00 * V11 - V01 * V01;
+  g.comp = 1.0f;
+  g.o = g.ob;
+  if (mip) {
+    g.comp = sqrtf(fmaxf(g.detv, 0.0f) / g.det);
+    g.o = g.ob * g.comp;
+  }
   return true;
 }
 
 // The same, reading the 11 geometry planes of one Gaussian; g0 = gaussian_base(params, i, P).
-__device__ inline bool project_geometry(const float* __restrict__ g0, const gs_camera& cam, Proj& g) {
+__device__ inline bool project_geometry(const float* __restrict__ g0, const gs_camera& cam, int mip, Proj& g) {
   float th[11];
 #pragma unroll
   for (int k = 0; k < 11; ++k) th[k] = g0[k * kGB];
-  return project_geometry_from(th, cam, g);
+  return project_geometry_from(th, cam, mip, g);
 }
 
 // View direction dir = normalize(mean - campos) and its length ([GSG] "Spherical harmonics").

@@ -25,7 +25,8 @@ GS_GRAD_SUMS_FLOAT, GS_GRAD_SUMS_FIXED = 0, 1
 EXPORTED = ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
             "gs_adam_step", "gs_render_bwd_adam", "gs_render_bwd_adam_project", "gs_camera_grad", "gs_densify_accumulate",
             "gs_densify", "gs_set_grad_sums", "gs_get_grad_sums", "gs_set_active_sh_degree",
-            "gs_get_active_sh_degree", "gs_loss_charbonnier", "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
+            "gs_get_active_sh_degree", "gs_set_mip_compensation", "gs_get_mip_compensation", "gs_loss_charbonnier",
+            "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
             "gs_profile_enable", "gs_profile_query", "gs_param_floats", "gs_params_to_blocked",
             "gs_params_from_blocked", "gs_last_error")
 
@@ -74,6 +75,10 @@ def _load():
     lib.gs_set_active_sh_degree.restype = I32
     lib.gs_get_active_sh_degree.argtypes = []
     lib.gs_get_active_sh_degree.restype = I32
+    lib.gs_set_mip_compensation.argtypes = [I32]
+    lib.gs_set_mip_compensation.restype = I32
+    lib.gs_get_mip_compensation.argtypes = []
+    lib.gs_get_mip_compensation.restype = I32
     lib.gs_set_grad_sums.argtypes = [I32]
     lib.gs_set_grad_sums.restype = I32
     lib.gs_get_grad_sums.argtypes = []
@@ -333,6 +338,15 @@ def gs_set_active_sh_degree(degree):
 
 def gs_get_active_sh_degree():
     return int(_lib.gs_get_active_sh_degree())
+
+
+def gs_set_mip_compensation(on):
+    """Mip-Splatting opacity compensation for every later projection and chain (off by default)."""
+    _check(_lib.gs_set_mip_compensation(int(bool(on))))
+
+
+def gs_get_mip_compensation():
+    return bool(_lib.gs_get_mip_compensation())
 
 
 def gs_set_grad_sums(mode):

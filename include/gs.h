@@ -341,6 +341,19 @@ int32_t gs_get_grad_sums(void);
  * -1 (the default): every stored band.  GS_ERR_INVALID_ARG outside -1..3. */
 int32_t gs_set_active_sh_degree(int32_t degree);
 int32_t gs_get_active_sh_degree(void);
+
+/* Mip-Splatting opacity compensation ([GSG] "Flattening a 3D blob into a 2D oval": a small
+ * factor keeps very tiny blobs from adding spurious energy; the trainer's code multiplies the
+ * opacity by it in the extent and in alpha).  With on = 1, for the whole process, every
+ * projection and chain enqueued after it: the record's opacity is
+ *   sigmoid(logit) comp,  comp = sqrt(max(det V, 0) / det(V + 0.3 I)),
+ * V the undilated screen covariance (the factor that gives the dilated footprint exactly the
+ * integral of the undilated one), so it also enters the extent, alpha and the skip boxes;
+ * the chain adds comp's gradient to the covariance's and scales the logit's by comp.  The
+ * blend is unchanged (it differentiates the record's opacity).  0 (the default): off.
+ * GS_ERR_INVALID_ARG for another value. */
+int32_t gs_set_mip_compensation(int32_t on);
+int32_t gs_get_mip_compensation(void);
 size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H);
 
 /* Tuning of the blend's work split (process-wide; set before sizing workspaces, and not between a

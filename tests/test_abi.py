@@ -124,6 +124,10 @@ def test_argument_errors_without_gpu(gs):
     assert L.gs_set_active_sh_degree(4) == gs.GS_ERR_INVALID_ARG
     assert L.gs_set_active_sh_degree(-2) == gs.GS_ERR_INVALID_ARG
     assert L.gs_get_active_sh_degree() == -1
+    # Mip-Splatting compensation switch
+    assert L.gs_get_mip_compensation() == 0
+    assert L.gs_set_mip_compensation(2) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_get_mip_compensation() == 0
     # gradient-sum modes
     assert L.gs_get_grad_sums() == gs.GS_GRAD_SUMS_FLOAT
     assert L.gs_set_grad_sums(7) == gs.GS_ERR_INVALID_ARG
