@@ -159,13 +159,19 @@ __device__ inline void geometry_grads(const float* th, const float* gs6, uint32_
   }
 }
 
+// A gradient written without Adam: gw g, or added to what is there (several views of one
+// step summed into one gradient).  With gw = 1 and no accumulation the value itself.
+__device__ inline void put_grad(float* __restrict__ gparams, size_t o, float g, float gw, int gacc) {
+  gparams[o] = gacc ? gparams[o] + gw * g : gw * g;
+}
+
 // Wave 3's part after the colour waves: the geometry gradients and their Adam update
 // (th returns the updated values).
 template <int K, bool ADAM>
 __device__ inline void geometry_tail(float* th, const float* gs6, float* mo, float* vo, uint32_t ntile, int lane,
                                      size_t gb, const gs_camera& cam, int mip, const float (*s_gdir)[3][64],
-                                     float* __restrict__ params, float* __restrict__ gparams, float* __restrict__ m,
-                                     float* __restrict__ v, const AdamArgs& a) {
+                                     float* __restrict__ params, float* __restrict__ gparams, float gw, int gacc,
+                                     float* __restrict__ m, float* __restrict__ v, const AdamArgs& a) {
   float gp[11];
   geometry_grads<K>(th, gs6, ntile, lane, cam, mip, s_gdir, gp, nullptr);
 #pragma unroll
@@ -177,7 +183,7 @@ __device__ inline void geometry_tail(float* th, const float* gs6, float* mo, flo
       __builtin_nontemporal_store(mo[pl], m + o);
       __builtin_nontemporal_store(vo[pl], v + o);
     } else {
-      gparams[o] = gp[pl];
+      put_grad(gparams, o, gp[pl], gw, gacc);
     }
   }
 }
@@ -187,6 +193,7 @@ template <int DEG, bool ADAM, bool PROJ>
 __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, int n, gs_camera cam,
                                                      const uint32_t* tiles,   // may be np.tiles
                                                      const float* __restrict__ gscreen, float* __restrict__ gparams,
+                                                     float gw, int gacc,
                                                      float* __restrict__ m, float* __restrict__ v, AdamArgs a,
                                                      NextProj np, float2* __restrict__ dstats, Shade shade) {
   constexpr int K = (DEG + 1) * (DEG + 1) - 1;
@@ -281,7 +288,7 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
           __builtin_nontemporal_store(cmo[k], m + o);
           __builtin_nontemporal_store(cvo[k], v + o);
         } else {
-          gparams[o] = g;
+          put_grad(gparams, o, g, gw, gacc);
         }
       }
     }
@@ -294,7 +301,8 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
       st.y += 1.0f;
       dstats[i] = st;
     }
-    geometry_tail<K, ADAM>(th, gs6, mo, vo, ntile, lane, gb, cam, shade.mip, s_gdir, params, gparams, m, v, a);
+    geometry_tail<K, ADAM>(th, gs6, mo, vo, ntile, lane, gb, cam, shade.mip, s_gdir, params, gparams, gw, gacc, m, v,
+                           a);
   }
   if (!PROJ) return;
   // ---- projection of the updated Gaussians for the next camera
@@ -340,22 +348,25 @@ __global__ void __launch_bounds__(256) chain_kernel(float* __restrict__ params, 
 
 template <int DEG, bool ADAM, bool PROJ>
 void launch_chain_deg(float* params, int n, const gs_camera& cam, const uint32_t* tiles, const float* gscreen,
-                      float* gparams, float* m, float* v, const AdamArgs& a, const NextProj& np, float* dstats,
-                      Shade shade, hipStream_t s) {
+                      float* gparams, float gw, int gacc, float* m, float* v, const AdamArgs& a, const NextProj& np,
+                      float* dstats, Shade shade, hipStream_t s) {
   GSK_PROF("chain", s);
-  chain_kernel<DEG, ADAM, PROJ><<<div_up(n, 64), 256, 0, s>>>(params, n, cam, tiles, gscreen, gparams, m, v, a, np,
-                                                              reinterpret_cast<float2*>(dstats), shade);
+  chain_kernel<DEG, ADAM, PROJ><<<div_up(n, 64), 256, 0, s>>>(params, n, cam, tiles, gscreen, gparams, gw, gacc, m,
+                                                              v, a, np, reinterpret_cast<float2*>(dstats), shade);
 }
 
 template <bool ADAM, bool PROJ>
 void launch_chain_mode(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles, const float* gscreen,
-                       float* gparams, float* m, float* v, const AdamArgs& a, const NextProj& np, float* dstats,
-                       Shade shade, hipStream_t s) {
+                       float* gparams, float gw, int gacc, float* m, float* v, const AdamArgs& a, const NextProj& np,
+                       float* dstats, Shade shade, hipStream_t s) {
   switch (deg) {
-    case 0: launch_chain_deg<0, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, shade, s); break;
-    case 1: launch_chain_deg<1, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, shade, s); break;
-    case 2: launch_chain_deg<2, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, shade, s); break;
-    default: launch_chain_deg<3, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, m, v, a, np, dstats, shade, s); break;
+#define GSK_CHAIN_CASE(D) \
+    launch_chain_deg<D, ADAM, PROJ>(params, n, cam, tiles, gscreen, gparams, gw, gacc, m, v, a, np, dstats, shade, s)
+    case 0: GSK_CHAIN_CASE(0); break;
+    case 1: GSK_CHAIN_CASE(1); break;
+    case 2: GSK_CHAIN_CASE(2); break;
+    default: GSK_CHAIN_CASE(3); break;
+#undef GSK_CHAIN_CASE
   }
 }
 
@@ -510,18 +521,18 @@ hipError_t launch_camera_grad(const float* params, int n, int deg, const gs_came
 
 hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_camera& cam,
                                  const uint32_t* tiles, const float* gscreen, float* gparams, Shade shade,
-                                 hipStream_t s) {
+                                 hipStream_t s, float weight, int accumulate) {
   if (n == 0) return hipSuccess;
-  launch_chain_mode<false, false>(const_cast<float*>(params), n, deg, cam, tiles, gscreen, gparams, nullptr, nullptr,
-                                  AdamArgs{}, NextProj{}, nullptr, shade, s);
+  launch_chain_mode<false, false>(const_cast<float*>(params), n, deg, cam, tiles, gscreen, gparams, weight,
+                                  accumulate, nullptr, nullptr, AdamArgs{}, NextProj{}, nullptr, shade, s);
   return hipGetLastError();
 }
 
 hipError_t launch_chain_adam(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
                              const float* gscreen, float* m, float* v, const AdamArgs& a, Shade shade, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  launch_chain_mode<true, false>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, NextProj{}, nullptr, shade,
-                                 s);
+  launch_chain_mode<true, false>(params, n, deg, cam, tiles, gscreen, nullptr, 1.0f, 0, m, v, a, NextProj{}, nullptr,
+                                 shade, s);
   return hipGetLastError();
 }
 
@@ -529,7 +540,8 @@ hipError_t launch_chain_adam_project(float* params, int n, int deg, const gs_cam
                                      const float* gscreen, float* m, float* v, const AdamArgs& a,
                                      const NextProj& np, float* dstats, Shade shade, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  launch_chain_mode<true, true>(params, n, deg, cam, tiles, gscreen, nullptr, m, v, a, np, dstats, shade, s);
+  launch_chain_mode<true, true>(params, n, deg, cam, tiles, gscreen, nullptr, 1.0f, 0, m, v, a, np, dstats, shade,
+                                s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_tile_count_total(np.block_tiles, int(div_up(n, 64)), np.total, s);

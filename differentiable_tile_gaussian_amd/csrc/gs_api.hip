@@ -313,11 +313,11 @@ int32_t gs_loss_l1_dssim(const float* img, const float* target, int32_t H, int32
   return GS_OK;
 }
 
-int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t* vals, const uint32_t* ranges,
-                      uint32_t total_pairs, const gs_camera* cam, const float* T_final,
-                      const uint32_t* n_contrib, const float* dL_dimg, float* gscreen, float* gparams, void* ws,
-                      size_t ws_bytes, void* stream) {
-  g_err[0] = 0;
+static int32_t render_bwd_common(const gs_scene* scene, const gs_proj* proj, const uint32_t* vals,
+                                 const uint32_t* ranges, uint32_t total_pairs, const gs_camera* cam,
+                                 const float* T_final, const uint32_t* n_contrib, const float* dL_dimg,
+                                 float* gscreen, float* gparams, float weight, int accumulate, void* ws,
+                                 size_t ws_bytes, void* stream) {
   int32_t st;
   if ((st = check_scene(scene)) != GS_OK) return st;
   if ((st = check_camera(cam)) != GS_OK) return st;
@@ -333,9 +333,30 @@ int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t
                                         gscreen, ws, g_fixed_sums != 0, s);
   if (e != hipSuccess) return hip_fail(e, "render_bwd");
   e = gsk::launch_preprocess_bwd(scene->params, n, scene->sh_degree, *cam, proj->tiles, gscreen, gparams,
-                                 shade_of(scene->sh_degree), s);
+                                 shade_of(scene->sh_degree), s, weight, accumulate);
   if (e != hipSuccess) return hip_fail(e, "preprocess_bwd");
   return GS_OK;
+}
+
+int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t* vals, const uint32_t* ranges,
+                      uint32_t total_pairs, const gs_camera* cam, const float* T_final,
+                      const uint32_t* n_contrib, const float* dL_dimg, float* gscreen, float* gparams, void* ws,
+                      size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  return render_bwd_common(scene, proj, vals, ranges, total_pairs, cam, T_final, n_contrib, dL_dimg, gscreen, gparams,
+                           1.0f, 0, ws, ws_bytes, stream);
+}
+
+int32_t gs_render_bwd_weighted(const gs_scene* scene, const gs_proj* proj, const uint32_t* vals,
+                               const uint32_t* ranges, uint32_t total_pairs, const gs_camera* cam,
+                               const float* T_final, const uint32_t* n_contrib, const float* dL_dimg,
+                               float* gscreen, float* gparams, float weight, int32_t accumulate, void* ws,
+                               size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!std::isfinite(weight)) return fail(GS_ERR_INVALID_ARG, "weight must be finite");
+  if (accumulate != 0 && accumulate != 1) return fail(GS_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  return render_bwd_common(scene, proj, vals, ranges, total_pairs, cam, T_final, n_contrib, dL_dimg, gscreen, gparams,
+                           weight, accumulate, ws, ws_bytes, stream);
 }
 
 int32_t gs_camera_grad(const gs_scene* scene, const gs_proj* proj, const gs_camera* cam, const float* gscreen,

@@ -57,9 +57,10 @@ struct NextProj {
   uint32_t* block_tiles;
   uint64_t* total;
 };
+// The chain without Adam: gparams = weight g, or += weight g with accumulate.
 hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_camera& cam,
                                  const uint32_t* tiles, const float* gscreen, float* gparams, Shade shade,
-                                 hipStream_t s);
+                                 hipStream_t s, float weight = 1.0f, int accumulate = 0);
 // Camera-pose gradient: out (device double[6]) = (rotation, translation); ws holds
 // camera_grad_ws_bytes(n) bytes of per-block sums.
 size_t camera_grad_ws_bytes(int64_t n);

@@ -23,7 +23,7 @@ GS_TUNE_SPLIT_FIRST, GS_TUNE_SPLIT_CHUNK = 0, 1
 GS_GRAD_SUMS_FLOAT, GS_GRAD_SUMS_FIXED = 0, 1
 
 EXPORTED = ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
-            "gs_adam_step", "gs_render_bwd_adam", "gs_render_bwd_adam_project", "gs_camera_grad", "gs_densify_accumulate",
+            "gs_adam_step", "gs_render_bwd_adam", "gs_render_bwd_adam_project", "gs_render_bwd_weighted", "gs_camera_grad", "gs_densify_accumulate",
             "gs_densify", "gs_set_grad_sums", "gs_get_grad_sums", "gs_set_active_sh_degree",
             "gs_get_active_sh_degree", "gs_set_mip_compensation", "gs_get_mip_compensation", "gs_loss_charbonnier",
             "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
@@ -83,6 +83,8 @@ def _load():
     lib.gs_set_grad_sums.restype = I32
     lib.gs_get_grad_sums.argtypes = []
     lib.gs_get_grad_sums.restype = I32
+    lib.gs_render_bwd_weighted.argtypes = [P, P, P, P, U32, P, P, P, P, P, P, C.c_float, I32, P, C.c_size_t, P]
+    lib.gs_render_bwd_weighted.restype = I32
     lib.gs_camera_grad.argtypes = [P, P, P, P, P, P, C.c_size_t, P]
     lib.gs_camera_grad.restype = I32
     lib.gs_densify_accumulate.argtypes = [P, I64, P, P, P]
@@ -253,6 +255,18 @@ def gs_render_bwd(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam:
                               C.byref(cam),
                               _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimg), _ptr(gscreen), _ptr(gparams),
                               _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def gs_render_bwd_weighted(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam: GsCamera, T_final,
+                           n_contrib, dL_dimg, gscreen, gparams, ws, weight, accumulate, stream=None):
+    n = proj.n
+    _blocked(params, n, sh_degree)
+    _blocked(gparams, n, sh_degree)
+    scene = GsScene(n, sh_degree, params.data_ptr() if n else None)
+    _check(_lib.gs_render_bwd_weighted(C.byref(scene), C.byref(proj.struct), _ptr(vals), _ptr(ranges), total_pairs,
+                                       C.byref(cam), _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimg), _ptr(gscreen),
+                                       _ptr(gparams), float(weight), int(bool(accumulate)), _ptr(ws), ws.numel(),
+                                       _stream(stream)))
 
 
 def gs_camera_grad(params, sh_degree, proj: Proj, cam: GsCamera, gscreen, grad_out, ws, stream=None):

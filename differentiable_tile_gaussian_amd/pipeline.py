@@ -126,6 +126,25 @@ class Pipeline:
             self.adam()
         return self.loss
 
+    def step_views(self, cams, targets):
+        """One training step over several views: each view is rendered and differentiated
+        in turn, its parameter gradients added into one buffer with weight 1/B (the mean
+        over the B views), then one Adam update.  Returns the losses of the views
+        ([B][3]: total, L1, SSIM).  With density statistics enabled, every view's
+        observations are added to them."""
+        B = len(cams)
+        assert B == len(targets) and B > 0
+        losses = torch.empty((B, 3), dtype=torch.float32, device=self.params.device)
+        for k, (cam, target) in enumerate(zip(cams, targets)):
+            self.forward(cam)
+            gs.gs_loss_l1_dssim(self.rgb, target, self.lam, losses[k], self.dLdI, self.ws_loss)
+            gs.gs_render_bwd_weighted(self.params, self.deg, self.proj, self.vals, self.ranges, self.pairs, cam, self.T,
+                                      self.nc, self.dLdI, self.gscreen, self.grads, self.ws_render, 1.0 / B, k > 0)
+            if self.dstats is not None:
+                gs.gs_densify_accumulate(self.proj, self.gscreen, self.dstats)
+        self.adam()
+        return losses
+
     # ------------------------------------------------------------ density control
     def enable_density_stats(self):
         """Start accumulating each step's screen-position gradient lengths and observation

@@ -208,6 +208,20 @@ int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t
                       const uint32_t* n_contrib, const float* dL_dimg, float* gscreen, float* gparams, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* gs_render_bwd for a step over several views (the trainer's loop renders one view per step;
+ * a batch of views is the same loop with their gradients summed before one Adam update).
+ * Every Gaussian's P parameter gradients g of this view are written as
+ *   gparams = weight g            (accumulate = 0), or
+ *   gparams = gparams + weight g  (accumulate = 1, each entry read and rounded once more),
+ * e.g. weight 1/B for the mean over B views, the first with accumulate = 0.  weight 1 with
+ * accumulate 0 is gs_render_bwd exactly.  Other arguments, and errors, as gs_render_bwd;
+ * GS_ERR_INVALID_ARG for a non-finite weight or accumulate other than 0 or 1. */
+int32_t gs_render_bwd_weighted(const gs_scene* scene, const gs_proj* proj, const uint32_t* vals,
+                               const uint32_t* ranges, uint32_t total_pairs, const gs_camera* cam,
+                               const float* T_final, const uint32_t* n_contrib, const float* dL_dimg,
+                               float* gscreen, float* gparams, float weight, int32_t accumulate, void* ws,
+                               size_t ws_bytes, void* stream);
+
 /* Camera-pose gradient ([GSG] "Forgiving the camera and the light": the pose receives the
  * loss's gradient like any other parameter).  With the rotation perturbed on the left,
  * W <- (I + [w]x) W, and the translation t (the camera centre is -W^T t), every visible

@@ -124,6 +124,14 @@ def test_argument_errors_without_gpu(gs):
     assert L.gs_set_active_sh_degree(4) == gs.GS_ERR_INVALID_ARG
     assert L.gs_set_active_sh_degree(-2) == gs.GS_ERR_INVALID_ARG
     assert L.gs_get_active_sh_degree() == -1
+    # several views per step: the weight and the accumulate flag are checked first
+    def weighted(weight, acc):
+        return L.gs_render_bwd_weighted(C.byref(sc), C.byref(proj), 1, 1, 100, C.byref(cam), 1, 1, 1, 1, 1,
+                                        C.c_float(weight), acc, 1, big, None)
+    assert weighted(float("nan"), 0) == gs.GS_ERR_INVALID_ARG
+    assert weighted(float("inf"), 1) == gs.GS_ERR_INVALID_ARG
+    assert weighted(0.5, 2) == gs.GS_ERR_INVALID_ARG
+    assert "accumulate" in gs.gs_last_error()
     # Mip-Splatting compensation switch
     assert L.gs_get_mip_compensation() == 0
     assert L.gs_set_mip_compensation(2) == gs.GS_ERR_INVALID_ARG
