@@ -210,7 +210,9 @@ def measure_camera_grad(pl, cam, torch, gs, reps=20):
     """The camera-pose gradient (optional, not part of the step) over the benchmark's
     population, on the screen partials and tile counts the last step left: average of `reps`
     calls, HIP events.  Algorithmic bytes: every Gaussian's tile count, eleven geometry
-    planes and six screen partials; a visible one's colour planes and colour partials too."""
+    planes and six screen partials; and, in every 64-Gaussian group with a visible member,
+    the colour planes and colour partials of the whole group (a wave reads a plane's
+    256-byte row when any of its lanes needs it, as the projection does)."""
     dev = pl.params.device
     out = torch.zeros(6, dtype=torch.float64, device=dev)
     ws = gs.workspace(gs.GS_WS_CAMERA_GRAD, n=pl.n)
@@ -223,8 +225,10 @@ def measure_camera_grad(pl, cam, torch, gs, reps=20):
     ev[1].record()
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[1]) / reps
-    n_vis = int((pl.proj.tiles[:pl.n] != 0).sum().item())
-    nbytes = pl.n * (4 + 11 * 4 + 6 * 4) + n_vis * (3 * (pl.deg + 1) ** 2 * 4 + 3 * 4)
+    vis = (pl.proj.tiles[:pl.n] != 0).int()
+    pad = (-pl.n) % 64
+    groups_vis = int((torch.nn.functional.pad(vis, (0, pad)).view(-1, 64).sum(1) > 0).sum().item())
+    nbytes = pl.n * (4 + 11 * 4 + 6 * 4) + groups_vis * 64 * (3 * (pl.deg + 1) ** 2 * 4 + 3 * 4)
     return {"ms": round(ms, 4), "bytes": nbytes, "GBps": round(nbytes / (ms / 1000.0) / 1e9, 1)}
 
 

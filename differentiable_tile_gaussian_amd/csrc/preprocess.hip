@@ -34,12 +34,12 @@ __device__ inline uint32_t project_one(const float* __restrict__ params, int i, 
   float raw[3] = {0.f, 0.f, 0.f};
   if (geom) {
     float Y[16];
-    if (shade.kact > 0) {
+    if (K > 0) {
       float dir[3];
       view_dir(g0, cam, dir);
       sh_eval(dir[0], dir[1], dir[2], Y);
     }
-    sh_colour(g0, shade.kact, Y, raw);
+    sh_colour<K>(g0, shade.kact, Y, raw);
   }
   Record r;
   make_record(geom, g, raw, tx, ty, r);

@@ -209,11 +209,20 @@ __device__ inline float view_dir(const float* __restrict__ g0, const gs_camera& 
   return view_dir_from(g0[0], g0[kGB], g0[2 * kGB], cam, dir);
 }
 
-// Colour before the clamp: DC + sum_k sh_k Y_k.
-__device__ inline void sh_colour(const float* __restrict__ g0, int K, const float* Y, float* raw) {
+// Colour before the clamp: DC + sum_k sh_k Y_k over the active bands k <= kact of the K
+// stored ones.  The loop runs over the stored bands (unrolled, every load issued up
+// front) and an inactive band's term is dropped by a select, so the sum is formed with
+// the same roundings as a loop over the active bands alone.
+template <int K>
+__device__ inline void sh_colour(const float* __restrict__ g0, int kact, const float* Y, float* raw) {
+#pragma unroll
   for (int ch = 0; ch < 3; ++ch) {
     float col = g0[(11 + ch) * kGB];
-    for (int k = 1; k <= K; ++k) col = col + g0[(14 + 3 * (k - 1) + ch) * kGB] * Y[k];
+#pragma unroll
+    for (int k = 1; k <= K; ++k) {
+      const float t = g0[(14 + 3 * (k - 1) + ch) * kGB] * Y[k];
+      col = k <= kact ? col + t : col;
+    }
     raw[ch] = col;
   }
 }
