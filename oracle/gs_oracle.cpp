@@ -26,6 +26,7 @@
 // Build: g++ -O2 -std=c++17 -ffp-contract=off -fno-fast-math -shared -fPIC.
 
 #include <algorithm>
+#include <utility>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -935,6 +936,51 @@ int64_t densify(int64_t n, int deg, const float* params, const float* m, const f
   return total;
 }
 
+// Relocation of the dead ([GSG] "Densification", the MCMC-style pass): a Gaussian whose
+// opacity is below the dead threshold is dead, one above the donor threshold a donor
+// (decisions on the stored logit against the thresholds' logit, rounded once to float;
+// a donor's largest log-scale must not be NaN).  The donors are ranked by their largest
+// log-scale, largest first, equal sizes in index order; the k-th dead Gaussian in index
+// order moves to the k-th ranked donor, for k below the smaller count and max_moves.  A
+// moved Gaussian takes the donor's parameters with its mean placed at mean + Rq (s eps)
+// (eps: its own three caller-drawn normals, as a split child's) and the log-scales
+// lowered by the shrink; the donor's log-scales are lowered too; both restart with zero
+// moments.  Everything else is unchanged, and so is the count.  In place; returns the
+// number of moves.
+int64_t relocate(int64_t n, int deg, float* params, float* m, float* v, const float* rand, float logit_dead,
+                 float logit_donor, float lscale_shrink, int64_t max_moves) {
+  const int P = num_planes(deg);
+  std::vector<int64_t> dead;
+  std::vector<std::pair<float, int64_t>> donors;
+  for (int64_t i = 0; i < n; ++i) {
+    const float logit = params[10 * n + i];
+    const float lsmax = std::max(std::max(params[3 * n + i], params[4 * n + i]), params[5 * n + i]);
+    if (logit < logit_dead) dead.push_back(i);
+    else if (logit > logit_donor && !std::isnan(lsmax)) donors.push_back({lsmax, i});
+  }
+  std::stable_sort(donors.begin(), donors.end(),
+                   [](const std::pair<float, int64_t>& a, const std::pair<float, int64_t>& b) {
+                     return a.first > b.first;
+                   });
+  int64_t moves = std::min<int64_t>(int64_t(dead.size()), int64_t(donors.size()));
+  if (max_moves >= 0) moves = std::min(moves, max_moves);
+  for (int64_t k = 0; k < moves; ++k) {
+    const int64_t bi = dead[size_t(k)], bd = donors[size_t(k)].second;
+    float mean[3];
+    split_child_mean(params, n, bd, rand + 3 * bi, mean);
+    for (int pl = 0; pl < P; ++pl) {
+      float th = params[pl * n + bd];
+      if (pl < 3) th = mean[pl];
+      if (pl >= 3 && pl < 6) th = th - lscale_shrink;
+      params[pl * n + bi] = th;
+      m[pl * n + bi] = v[pl * n + bi] = 0.0f;
+      m[pl * n + bd] = v[pl * n + bd] = 0.0f;
+    }
+    for (int pl = 3; pl < 6; ++pl) params[pl * n + bd] = params[pl * n + bd] - lscale_shrink;
+  }
+  return moves;
+}
+
 extern "C" {
 
 int or_num_planes(int deg) { return num_planes(deg); }
@@ -1251,6 +1297,11 @@ void or_loss_charbonnier_f64(const double* img, const double* tgt, int64_t count
 
 void or_densify_accumulate_f32(int64_t n, const uint32_t* tiles, const float* gscreen, float* stats) {
   densify_accumulate(n, tiles, gscreen, stats);
+}
+
+int64_t or_relocate_f32(int64_t n, int deg, float* params, float* m, float* v, const float* rand, float logit_dead,
+                        float logit_donor, float lscale_shrink, int64_t max_moves) {
+  return relocate(n, deg, params, m, v, rand, logit_dead, logit_donor, lscale_shrink, max_moves);
 }
 
 int64_t or_densify_f32(int64_t n, int deg, const float* params, const float* m, const float* v, const float* stats,

@@ -88,6 +88,8 @@ def _declare(L):
     F = C.c_float
     L.or_densify_f32.argtypes = [I64, I32, P, P, P, P, P, F, F, F, F, F, I32, F, I64, P, P, P, P, P]
     L.or_densify_f32.restype = I64
+    L.or_relocate_f32.argtypes = [I64, I32, P, P, P, P, F, F, F, I64]
+    L.or_relocate_f32.restype = I64
 
 
 def _p(a):
@@ -397,6 +399,22 @@ def densify(params, m, v, stats, rand, sh_degree, grad_threshold, prune_opacity,
     so = np.zeros((total, 2), np.float32)
     lib().or_densify_f32(*args, total, _p(po), _p(mo), _p(vo), _p(so), _p(counts))
     return dict(params=po, m=mo, v=vo, stats=so, counts=counts)
+
+
+def relocate(params, m, v, rand, sh_degree, dead_opacity=0.02, donor_opacity=0.4, shrink=1.6, max_moves=-1):
+    """The MCMC-style relocation of the dead Gaussians to the largest donors (see
+    gs_oracle.cpp): returns new params, m, v ([P][n]) and the number of moves.  rand [n][3]:
+    each Gaussian's normals for the place it would be moved to."""
+    import math
+    params = np.array(params, dtype=np.float32, copy=True, order="C")
+    m = np.array(m, dtype=np.float32, copy=True, order="C")
+    v = np.array(v, dtype=np.float32, copy=True, order="C")
+    rand = _c(rand, np.float32)
+    n = params.shape[1]
+    lg = lambda p: float(np.float32(math.log(p / (1.0 - p))))   # noqa: E731
+    moves = lib().or_relocate_f32(n, sh_degree, _p(params), _p(m), _p(v), _p(rand), lg(dead_opacity),
+                                  lg(donor_opacity), float(np.float32(math.log(shrink))), int(max_moves))
+    return dict(params=params, m=m, v=v, moves=int(moves))
 
 
 # ------------------------------------------- Charbonnier loss with exposure
