@@ -16,6 +16,8 @@
 //
 // Compiled without floating-point contraction: the split children's means are the
 // written sequence of fp32 roundings.
+#include <rocprim/device/device_radix_sort.hpp>
+
 #include "gs_internal.h"
 #include "profile.h"
 
@@ -141,7 +143,155 @@ __global__ void __launch_bounds__(256) densify_scatter_kernel(
   }
 }
 
+// ---- relocation of the dead ([GSG] "Densification", the MCMC-style pass)
+// Dead: logit below logit(dead opacity); donor: not dead, logit above logit(donor
+// opacity) and a largest log-scale that is not NaN.  key: the largest log-scale (-0 made
+// +0) as an unsigned integer in the order of the floats, so that a descending radix sort
+// ranks the donors largest first.
+__global__ void __launch_bounds__(256) relocate_classify_kernel(const float* __restrict__ params, int n, int P,
+                                                                 float logit_dead, float logit_donor,
+                                                                 uint32_t* __restrict__ fdead,
+                                                                 uint32_t* __restrict__ fdonor,
+                                                                 uint32_t* __restrict__ key) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float* g0 = gaussian_base(params, i, P);
+  const float logit = g0[10 * kGB];
+  const float lsmax = max_of(max_of(g0[3 * kGB], g0[4 * kGB]), g0[5 * kGB]);
+  const bool dead = logit < logit_dead;
+  fdead[i] = dead;
+  fdonor[i] = !dead && logit > logit_donor && lsmax == lsmax;
+  const uint32_t u = __float_as_uint(lsmax + 0.0f);
+  key[i] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The dead in index order, and the donors' keys and indices in index order.
+__global__ void __launch_bounds__(256) relocate_compact_kernel(int n, const uint32_t* __restrict__ fdead,
+                                                                const uint32_t* __restrict__ fdonor,
+                                                                const uint32_t* __restrict__ odead,
+                                                                const uint32_t* __restrict__ odonor,
+                                                                const uint32_t* __restrict__ key,
+                                                                uint32_t* __restrict__ dead_list,
+                                                                uint32_t* __restrict__ key_in,
+                                                                uint32_t* __restrict__ idx_in) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  if (fdead[i]) dead_list[odead[i]] = uint32_t(i);
+  if (fdonor[i]) {
+    key_in[odonor[i]] = key[i];
+    idx_in[odonor[i]] = uint32_t(i);
+  }
+}
+
+// Move k: the k-th dead Gaussian takes the k-th ranked donor, placed at mean + Rq (s eps)
+// with its own normals, both log-scales lowered by the shrink, both moments zeroed.  The
+// dead and the donors are disjoint and each is used once, so the moves are independent;
+// a thread reads its donor before it writes the donor's log-scales.
+__global__ void __launch_bounds__(256) relocate_move_kernel(float* __restrict__ params, float* __restrict__ m,
+                                                             float* __restrict__ v, int P,
+                                                             const float* __restrict__ rand,
+                                                             const uint32_t* __restrict__ dead_list,
+                                                             const uint32_t* __restrict__ donor_ranked, int moves,
+                                                             float shrink) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= moves) return;
+  const int bi = int(dead_list[k]), bd = int(donor_ranked[k]);
+  float* gd = gaussian_base(params, bd, P);
+  float* gi = gaussian_base(params, bi, P);
+  float* md = gaussian_base(m, bd, P);
+  float* mi = gaussian_base(m, bi, P);
+  float* vd = gaussian_base(v, bd, P);
+  float* vi = gaussian_base(v, bi, P);
+  float mean[3];
+  child_mean(gd, rand + size_t(3) * bi, mean);
+  for (int pl = 0; pl < P; ++pl) {
+    float th = gd[pl * kGB];
+    if (pl < 3) th = mean[pl];
+    if (pl >= 3 && pl < 6) th = th - shrink;
+    gi[pl * kGB] = th;
+    mi[pl * kGB] = vi[pl * kGB] = 0.0f;
+    md[pl * kGB] = vd[pl * kGB] = 0.0f;
+  }
+  for (int pl = 3; pl < 6; ++pl) gd[pl * kGB] = gd[pl * kGB] - shrink;
+}
+
+size_t radix_temp_bytes(int64_t n) {
+  size_t bytes = 0;
+  rocprim::radix_sort_pairs_desc(nullptr, bytes, static_cast<const uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr),
+                                 static_cast<const uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr),
+                                 size_t(n > 0 ? n : 1), 0, 32);
+  return bytes;
+}
+
 }  // namespace
+
+// Relocation workspace: two flag arrays and their prefix sums and scan space, the two
+// totals, the keys, the dead list, the donors' keys and indices before and after the
+// sort, and the sort's own temporary space.
+RelocateWs carve_relocate(void* ws, int64_t n) {
+  char* base = static_cast<char*>(ws);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* q = base ? base + off : nullptr;
+    off += (bytes + 255) & ~size_t(255);
+    return q;
+  };
+  const size_t items = size_t(n > 0 ? n : 1) * 4;
+  RelocateWs w;
+  w.fdead = reinterpret_cast<uint32_t*>(take(items));
+  w.fdonor = reinterpret_cast<uint32_t*>(take(items));
+  w.odead = reinterpret_cast<uint32_t*>(take(size_t(n + 1) * 4));
+  w.odonor = reinterpret_cast<uint32_t*>(take(size_t(n + 1) * 4));
+  w.totals = reinterpret_cast<uint64_t*>(take(16));
+  w.scan_ws[0] = take(scan_ws_bytes(n));
+  w.scan_ws[1] = take(scan_ws_bytes(n));
+  w.key = reinterpret_cast<uint32_t*>(take(items));
+  w.dead_list = reinterpret_cast<uint32_t*>(take(items));
+  w.key_in = reinterpret_cast<uint32_t*>(take(items));
+  w.idx_in = reinterpret_cast<uint32_t*>(take(items));
+  w.key_out = reinterpret_cast<uint32_t*>(take(items));
+  w.idx_out = reinterpret_cast<uint32_t*>(take(items));
+  w.sort_bytes = radix_temp_bytes(n);
+  w.sort_temp = take(w.sort_bytes);
+  w.bytes = off;
+  return w;
+}
+
+size_t relocate_ws_bytes(int64_t n) { return carve_relocate(nullptr, n).bytes; }
+
+hipError_t launch_relocate_count(const float* params, int n, int deg, float logit_dead, float logit_donor, void* ws,
+                                 hipStream_t s) {
+  RelocateWs w = carve_relocate(ws, n);
+  {
+    GSK_PROF("relocate_classify", s);
+    relocate_classify_kernel<<<div_up(n, 256), 256, 0, s>>>(params, n, num_planes(deg), logit_dead, logit_donor,
+                                                            w.fdead, w.fdonor, w.key);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_scan_u32(w.fdead, w.odead, n, w.totals, w.scan_ws[0], s);
+  if (e != hipSuccess) return e;
+  e = launch_scan_u32(w.fdonor, w.odonor, n, w.totals + 1, w.scan_ws[1], s);
+  if (e != hipSuccess) return e;
+  relocate_compact_kernel<<<div_up(n, 256), 256, 0, s>>>(n, w.fdead, w.fdonor, w.odead, w.odonor, w.key,
+                                                         w.dead_list, w.key_in, w.idx_in);
+  return hipGetLastError();
+}
+
+hipError_t launch_relocate_move(float* params, float* m, float* v, int n, int deg, const float* rand, int donors,
+                                int moves, float shrink, void* ws, hipStream_t s) {
+  RelocateWs w = carve_relocate(ws, n);
+  if (moves <= 0) return hipSuccess;
+  size_t bytes = w.sort_bytes;
+  hipError_t e = rocprim::radix_sort_pairs_desc(w.sort_temp, bytes, static_cast<const uint32_t*>(w.key_in),
+                                                w.key_out, static_cast<const uint32_t*>(w.idx_in), w.idx_out,
+                                                size_t(donors), 0, 32, s);
+  if (e != hipSuccess) return e;
+  GSK_PROF("relocate_move", s);
+  relocate_move_kernel<<<div_up(moves, 256), 256, 0, s>>>(params, m, v, num_planes(deg), rand, w.dead_list,
+                                                          w.idx_out, moves, shrink);
+  return hipGetLastError();
+}
 
 hipError_t launch_densify_accumulate(const uint32_t* tiles, int n, const float* gscreen, float* stats,
                                      hipStream_t s) {

@@ -1,5 +1,6 @@
 // The C ABI declared in include/gs.h: argument checks, workspace carving and the
 // launches of the kernels in the other translation units.  No call allocates.
+#include <algorithm>
 #include <atomic>
 #include <math.h>
 #include <stdarg.h>
@@ -206,6 +207,7 @@ size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t
     case GS_WS_DENSIFY: return gsk::densify_ws_bytes(n < 0 ? 0 : n);
     case GS_WS_LOSS_CHARBONNIER: return (W > 0 && H > 0) ? gsk::charbonnier_ws_bytes(H, W) : 0;
     case GS_WS_CAMERA_GRAD: return gsk::camera_grad_ws_bytes(n < 0 ? 0 : n);
+    case GS_WS_RELOCATE: return gsk::relocate_ws_bytes(n < 0 ? 0 : n);
     default: return 0;
   }
 }
@@ -604,6 +606,45 @@ int32_t gs_densify(const float* params, const float* m, const float* v, const fl
                                                    v_out, stats_out, s);
     if (e != hipSuccess) return hip_fail(e, "densify_write");
   }
+  return GS_OK;
+}
+
+int32_t gs_relocate(float* params, float* m, float* v, int64_t n, int32_t sh_degree, const float* rand,
+                    double dead_opacity, double donor_opacity, int64_t max_moves, int64_t* moves_out, void* ws,
+                    size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (n < 0 || n >= (int64_t(1) << 31)) return fail(GS_ERR_INVALID_ARG, "n out of range");
+  if (sh_degree < 0 || sh_degree > 3) return fail(GS_ERR_UNSUPPORTED, "SH degree must be 0..3");
+  if (!(dead_opacity > 0.0 && dead_opacity < 1.0) || !(donor_opacity > 0.0 && donor_opacity < 1.0) ||
+      !(dead_opacity <= donor_opacity))
+    return fail(GS_ERR_INVALID_ARG, "opacity thresholds must satisfy 0 < dead <= donor < 1");
+  if (n > 0 && (!params || !m || !v || !rand)) return fail(GS_ERR_INVALID_ARG, "an array is null");
+  if (n > 0 && gsk::param_floats(n, gsk::num_planes(sh_degree)) >= (size_t(1) << 31))
+    return fail(GS_ERR_UNSUPPORTED, "gs_param_floats(n, sh_degree) must stay below 2^31");
+  const size_t need = gs_workspace_bytes(GS_WS_RELOCATE, n, 0, 0, 0);
+  if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "relocation workspace needs %zu bytes", need);
+  int64_t moves = 0;
+  if (n > 0) {
+    hipStream_t s = as_stream(stream);
+    const float logit_dead = float(std::log(dead_opacity / (1.0 - dead_opacity)));
+    const float logit_donor = float(std::log(donor_opacity / (1.0 - donor_opacity)));
+    hipError_t e = gsk::launch_relocate_count(params, int(n), sh_degree, logit_dead, logit_donor, ws, s);
+    if (e != hipSuccess) return hip_fail(e, "relocate_count");
+    HostSlot* hs = host_slot();
+    if (!hs) return fail(GS_ERR_HIP, "cannot set up the pinned count buffer");
+    e = hipMemcpyAsync(hs->pinned, gsk::carve_relocate(ws, n).totals, 2 * sizeof(uint64_t), hipMemcpyDeviceToHost,
+                       s);
+    if (e != hipSuccess) return hip_fail(e, "relocate count copy");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "relocate sync");
+    const int64_t dead = int64_t(hs->pinned[0]), donors = int64_t(hs->pinned[1]);
+    moves = std::min(dead, donors);
+    if (max_moves >= 0) moves = std::min(moves, max_moves);
+    e = gsk::launch_relocate_move(params, m, v, int(n), sh_degree, rand, int(donors), int(moves),
+                                  float(std::log(1.6)), ws, s);
+    if (e != hipSuccess) return hip_fail(e, "relocate_move");
+  }
+  if (moves_out) *moves_out = moves;
   return GS_OK;
 }
 

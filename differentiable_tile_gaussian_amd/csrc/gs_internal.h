@@ -106,6 +106,25 @@ struct DensifyWs {
 };
 size_t densify_ws_bytes(int64_t n);
 DensifyWs carve_densify(void* ws, int64_t n);
+// Relocation of the dead to the largest donors: flags, prefix sums and their totals (dead,
+// donors), the donors' size keys, the dead list, the donors' keys and indices before and
+// after the ranking sort, and that sort's temporary space (bytes: the whole workspace).
+struct RelocateWs {
+  uint32_t *fdead, *fdonor, *odead, *odonor;
+  uint64_t* totals;
+  void* scan_ws[2];
+  uint32_t *key, *dead_list, *key_in, *idx_in, *key_out, *idx_out;
+  void* sort_temp;
+  size_t sort_bytes, bytes;
+};
+size_t relocate_ws_bytes(int64_t n);
+RelocateWs carve_relocate(void* ws, int64_t n);
+// Classifies, scans (totals[0] dead, totals[1] donors) and compacts; then, once the host
+// knows the counts, ranks the donors and makes the moves.
+hipError_t launch_relocate_count(const float* params, int n, int deg, float logit_dead, float logit_donor, void* ws,
+                                 hipStream_t s);
+hipError_t launch_relocate_move(float* params, float* m, float* v, int n, int deg, const float* rand, int donors,
+                                int moves, float shrink, void* ws, hipStream_t s);
 hipError_t launch_densify_accumulate(const uint32_t* tiles, int n, const float* gscreen, float* stats,
                                      hipStream_t s);
 hipError_t launch_densify_count(const float* params, int n, int deg, const float* stats, const DensifyArgs& a,

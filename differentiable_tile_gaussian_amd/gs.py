@@ -18,13 +18,13 @@ LIB_PATH = os.path.join(_HERE, "libgs.so")
 
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_UNSUPPORTED, GS_ERR_HIP = 0, -1, -2, -3, -4
 GS_WS_PREPROCESS, GS_WS_BIN_SORT, GS_WS_LOSS, GS_WS_RENDER, GS_WS_DENSIFY, GS_WS_LOSS_CHARBONNIER = 0, 1, 2, 3, 4, 5
-GS_WS_CAMERA_GRAD = 6
+GS_WS_CAMERA_GRAD, GS_WS_RELOCATE = 6, 7
 GS_TUNE_SPLIT_FIRST, GS_TUNE_SPLIT_CHUNK = 0, 1
 GS_GRAD_SUMS_FLOAT, GS_GRAD_SUMS_FIXED = 0, 1
 
 EXPORTED = ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
             "gs_adam_step", "gs_render_bwd_adam", "gs_render_bwd_adam_project", "gs_render_bwd_weighted", "gs_camera_grad", "gs_densify_accumulate",
-            "gs_densify", "gs_set_grad_sums", "gs_get_grad_sums", "gs_set_active_sh_degree",
+            "gs_densify", "gs_relocate", "gs_set_grad_sums", "gs_get_grad_sums", "gs_set_active_sh_degree",
             "gs_get_active_sh_degree", "gs_set_mip_compensation", "gs_get_mip_compensation", "gs_loss_charbonnier",
             "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
             "gs_profile_enable", "gs_profile_query", "gs_param_floats", "gs_params_to_blocked",
@@ -86,6 +86,8 @@ def _load():
     lib.gs_render_bwd_weighted.argtypes = [P, P, P, P, U32, P, P, P, P, P, P, C.c_float, I32, P, C.c_size_t, P]
     lib.gs_render_bwd_weighted.restype = I32
     lib.gs_camera_grad.argtypes = [P, P, P, P, P, P, C.c_size_t, P]
+    lib.gs_relocate.argtypes = [P, P, P, I64, I32, P, C.c_double, C.c_double, I64, P, P, C.c_size_t, P]
+    lib.gs_relocate.restype = I32
     lib.gs_camera_grad.restype = I32
     lib.gs_densify_accumulate.argtypes = [P, I64, P, P, P]
     lib.gs_densify_accumulate.restype = I32
@@ -267,6 +269,18 @@ def gs_render_bwd_weighted(params, sh_degree, proj: Proj, vals, ranges, total_pa
                                        C.byref(cam), _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimg), _ptr(gscreen),
                                        _ptr(gparams), float(weight), int(bool(accumulate)), _ptr(ws), ws.numel(),
                                        _stream(stream)))
+
+
+def gs_relocate(params, m, v, n, sh_degree, rand, ws, dead_opacity=0.02, donor_opacity=0.4, max_moves=-1,
+                stream=None):
+    """Moves the dead Gaussians to the largest donors in place; returns the number of moves."""
+    for t in (params, m, v):
+        _blocked(t, n, sh_degree)
+    moves = C.c_int64(0)
+    _check(_lib.gs_relocate(_ptr(params), _ptr(m), _ptr(v), n, sh_degree, _ptr(rand), float(dead_opacity),
+                            float(donor_opacity), int(max_moves), C.byref(moves), _ptr(ws), ws.numel(),
+                            _stream(stream)))
+    return int(moves.value)
 
 
 def gs_camera_grad(params, sh_degree, proj: Proj, cam: GsCamera, gscreen, grad_out, ws, stream=None):

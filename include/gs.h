@@ -327,8 +327,29 @@ int32_t gs_densify(const float* params, const float* m, const float* v, const fl
                    float* v_out, float* stats_out, int64_t capacity, int64_t* n_out, int64_t* counts, void* ws,
                    size_t ws_bytes, void* stream);
 
+/* Relocation of the dead ([GSG] "Densification", the MCMC-style pass: dead Gaussians are
+ * moved next to healthy donors, biased toward the largest; both halves shrink by 1.6 and a
+ * reshaped Gaussian's Adam moments restart).  Gaussian i is dead when its opacity is below
+ * dead_opacity (about 0.02 on the page), a donor when it is not dead, its opacity is above
+ * donor_opacity (about 0.4) and its largest log-scale is not NaN (the comparisons on the
+ * stored logit against the thresholds' logit formed in double and rounded once to float).
+ * The donors are ranked by their largest log-scale, largest first, equal sizes in index
+ * order; the k-th dead Gaussian in index order is moved to the k-th ranked donor, for k
+ * below min(dead, donors) and below max_moves when max_moves >= 0.  A moved Gaussian takes
+ * all of its donor's parameters, with the mean at donor mean + Rq (s eps) (eps =
+ * rand[i][0..2], caller-drawn standard normals of the moved Gaussian i; Rq and s as for a
+ * split child of gs_densify) and the log-scales lowered by ln 1.6; the donor's log-scales
+ * are lowered by ln 1.6 too; both get zero m and v.  All other Gaussians are unchanged, and
+ * so is the count.  params, m, v: blocked layout for n, updated in place; rand [n][3]
+ * (device).  *moves_out (host, nullable): the number of moves.  ws: gs_workspace_bytes(
+ * GS_WS_RELOCATE, n, 0, 0, 0).  Waits for the two counts (one copy to a pinned host buffer);
+ * the donors are ranked with rocPRIM's stable radix sort. */
+int32_t gs_relocate(float* params, float* m, float* v, int64_t n, int32_t sh_degree, const float* rand,
+                    double dead_opacity, double donor_opacity, int64_t max_moves, int64_t* moves_out, void* ws,
+                    size_t ws_bytes, void* stream);
+
 enum { GS_WS_PREPROCESS = 0, GS_WS_BIN_SORT = 1, GS_WS_LOSS = 2, GS_WS_RENDER = 3, GS_WS_DENSIFY = 4,
-       GS_WS_LOSS_CHARBONNIER = 5, GS_WS_CAMERA_GRAD = 6 };
+       GS_WS_LOSS_CHARBONNIER = 5, GS_WS_CAMERA_GRAD = 6, GS_WS_RELOCATE = 7 };
 
 /* How the backward blend sums the per-pixel gradient contributions of a Gaussian (for the
  * whole process, every backward call enqueued after it; default GS_GRAD_SUMS_FLOAT).

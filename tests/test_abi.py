@@ -132,6 +132,14 @@ def test_argument_errors_without_gpu(gs):
     assert weighted(float("inf"), 1) == gs.GS_ERR_INVALID_ARG
     assert weighted(0.5, 2) == gs.GS_ERR_INVALID_ARG
     assert "accumulate" in gs.gs_last_error()
+    # relocation: thresholds and the workspace are checked before anything is enqueued
+    def relocate(dead, donor, ws_bytes=big):
+        return L.gs_relocate(1, 2, 3, 10, 0, 4, dead, donor, -1, None, 1, ws_bytes, None)
+    assert relocate(0.5, 0.4) == gs.GS_ERR_INVALID_ARG                                  # dead above donor
+    assert relocate(0.0, 0.4) == gs.GS_ERR_INVALID_ARG
+    assert relocate(0.02, 1.0) == gs.GS_ERR_INVALID_ARG
+    assert relocate(0.02, 0.4, ws_bytes=16) == gs.GS_ERR_CAPACITY
+    assert "relocation workspace" in gs.gs_last_error()
     # Mip-Splatting compensation switch
     assert L.gs_get_mip_compensation() == 0
     assert L.gs_set_mip_compensation(2) == gs.GS_ERR_INVALID_ARG
@@ -156,6 +164,8 @@ def test_workspace_sizes_grow_with_the_problem(gs):
     assert gs.gs_workspace_bytes(gs.GS_WS_PREPROCESS, 6_000_000, 0, 0, 0) > 0
     # density control: three flags and three prefix sums per Gaussian
     assert gs.gs_workspace_bytes(gs.GS_WS_DENSIFY, 1_000_000, 0, 0, 0) >= 24 * 1_000_000
+    # relocation: flags, sums, keys and lists per Gaussian, and the sort's space
+    assert gs.gs_workspace_bytes(gs.GS_WS_RELOCATE, 1_000_000, 0, 0, 0) >= 40 * 1_000_000
     # camera-pose gradient: six double sums per group of 64 Gaussians
     assert gs.gs_workspace_bytes(gs.GS_WS_CAMERA_GRAD, 1_000_000, 0, 0, 0) == 15625 * 48
     assert gs.gs_workspace_bytes(99, 1, 1, 1, 1) == 0
