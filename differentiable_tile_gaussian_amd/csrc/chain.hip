@@ -378,28 +378,45 @@ void launch_chain_mode(float* params, int n, int deg, const gs_camera& cam, cons
 // camera centre is -W^T t).  With G = J^T dT + dp m^T + t gsh^T (gsh: the view-direction
 // part of the mean's gradient, so the centre's gradient is -gsh), dL/dW = G and
 //   dL/dw = (M21 - M12, M02 - M20, M10 - M01) with M = G W^T,   dL/dt = dp + W gsh.
+// For the position path alone the rotation term is (p - t) x dp, the pages' torque, and the
+// translation's dp: the trainer's code accumulates exactly those (position_only).
 // The per-Gaussian terms are formed in double from the fp32 chain quantities and summed in
 // double, per wave with a fixed butterfly and over blocks in a fixed order, so the result
 // is reproducible.
-__device__ inline void camera_terms(const CamPart& c, const float* mean, const gs_camera& cam, double* out) {
-  const double fx = cam.fx, fy = cam.fy, pz = c.p[2];
-  const double J[2][3] = {{fx / pz, 0.0, -fx * double(c.p[0]) / (pz * pz)},
-                          {0.0, fy / pz, -fy * double(c.p[1]) / (pz * pz)}};
+__device__ inline void camera_terms(const CamPart& c, const float* mean, const gs_camera& cam, int position_only,
+                                    double* out) {
   double G[3][3];
+#pragma unroll
   for (int r = 0; r < 3; ++r)
-    for (int k = 0; k < 3; ++k)
-      G[r][k] = J[0][r] * double(c.dT0[k]) + J[1][r] * double(c.dT1[k]) + double(c.dp[r]) * double(mean[k]) +
-                double(cam.t[r]) * double(c.gsh[k]);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) G[r][k] = double(c.dp[r]) * double(mean[k]);
+  double tr[3] = {double(c.dp[0]), double(c.dp[1]), double(c.dp[2])};
+  if (!position_only) {
+    const double fx = cam.fx, fy = cam.fy, pz = c.p[2];
+    const double J[2][3] = {{fx / pz, 0.0, -fx * double(c.p[0]) / (pz * pz)},
+                            {0.0, fy / pz, -fy * double(c.p[1]) / (pz * pz)}};
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        G[r][k] = J[0][r] * double(c.dT0[k]) + J[1][r] * double(c.dT1[k]) + G[r][k] +
+                  double(cam.t[r]) * double(c.gsh[k]);
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+      tr[r] = tr[r] + double(cam.R[3 * r]) * double(c.gsh[0]) + double(cam.R[3 * r + 1]) * double(c.gsh[1]) +
+              double(cam.R[3 * r + 2]) * double(c.gsh[2]);
+  }
   double M[3][3];
+#pragma unroll
   for (int r = 0; r < 3; ++r)
+#pragma unroll
     for (int k = 0; k < 3; ++k)
       M[r][k] = G[r][0] * double(cam.R[3 * k]) + G[r][1] * double(cam.R[3 * k + 1]) + G[r][2] * double(cam.R[3 * k + 2]);
   out[0] = M[2][1] - M[1][2];
   out[1] = M[0][2] - M[2][0];
   out[2] = M[1][0] - M[0][1];
-  for (int r = 0; r < 3; ++r)
-    out[3 + r] = double(c.dp[r]) + double(cam.R[3 * r]) * double(c.gsh[0]) +
-                 double(cam.R[3 * r + 1]) * double(c.gsh[1]) + double(cam.R[3 * r + 2]) * double(c.gsh[2]);
+#pragma unroll
+  for (int r = 0; r < 3; ++r) out[3 + r] = tr[r];
 }
 
 // One block per group of 64 Gaussians, the chain kernel's split: waves 0-2 the view-direction
@@ -409,7 +426,8 @@ template <int DEG>
 __global__ void __launch_bounds__(256) camera_grad_kernel(const float* __restrict__ params, int n, gs_camera cam,
                                                            const uint32_t* __restrict__ tiles,
                                                            const float* __restrict__ gscreen,
-                                                           double* __restrict__ part, Shade shade) {
+                                                           double* __restrict__ part, Shade shade,
+                                                           int position_only) {
   constexpr int K = (DEG + 1) * (DEG + 1) - 1;
   constexpr int P = 11 + 3 * (K + 1);
   __shared__ float s_gdir[3][3][64];
@@ -464,7 +482,7 @@ __global__ void __launch_bounds__(256) camera_grad_kernel(const float* __restric
     float gp[11];
     CamPart cp;
     geometry_grads<K>(th, gs6, ntile, lane, cam, shade.mip, s_gdir, gp, &cp);
-    if (cp.geom) camera_terms(cp, th, cam, t6);
+    if (cp.geom) camera_terms(cp, th, cam, position_only, t6);
   }
 #pragma unroll
   for (int k = 0; k < 6; ++k)
@@ -497,7 +515,8 @@ __global__ void __launch_bounds__(1024) camera_grad_finalize_kernel(const double
 size_t camera_grad_ws_bytes(int64_t n) { return size_t(div_up(n, 64)) * 6 * sizeof(double); }
 
 hipError_t launch_camera_grad(const float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
-                              const float* gscreen, double* out, void* ws, Shade shade, hipStream_t s) {
+                              const float* gscreen, int position_only, double* out, void* ws, Shade shade,
+                              hipStream_t s) {
   double* part = static_cast<double*>(ws);
   if (n == 0) {
     camera_grad_finalize_kernel<<<6, 1024, 0, s>>>(part, 0, out);
@@ -507,10 +526,10 @@ hipError_t launch_camera_grad(const float* params, int n, int deg, const gs_came
   {
     GSK_PROF("camera_grad", s);
     switch (deg) {
-      case 0: camera_grad_kernel<0><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, shade); break;
-      case 1: camera_grad_kernel<1><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, shade); break;
-      case 2: camera_grad_kernel<2><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, shade); break;
-      default: camera_grad_kernel<3><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, shade); break;
+      case 0: camera_grad_kernel<0><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, shade, position_only); break;
+      case 1: camera_grad_kernel<1><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, shade, position_only); break;
+      case 2: camera_grad_kernel<2><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, shade, position_only); break;
+      default: camera_grad_kernel<3><<<nb, 256, 0, s>>>(params, n, cam, tiles, gscreen, part, shade, position_only); break;
     }
   }
   hipError_t e = hipGetLastError();

@@ -362,19 +362,20 @@ int32_t gs_render_bwd_weighted(const gs_scene* scene, const gs_proj* proj, const
 }
 
 int32_t gs_camera_grad(const gs_scene* scene, const gs_proj* proj, const gs_camera* cam, const float* gscreen,
-                       double* grad_out, void* ws, size_t ws_bytes, void* stream) {
+                       int32_t position_only, double* grad_out, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   int32_t st;
   if ((st = check_scene(scene)) != GS_OK) return st;
   if ((st = check_camera(cam)) != GS_OK) return st;
   if ((st = check_proj(proj, scene->n, false)) != GS_OK) return st;
   if (!grad_out) return fail(GS_ERR_INVALID_ARG, "grad_out is null");
+  if (position_only != 0 && position_only != 1) return fail(GS_ERR_INVALID_ARG, "position_only must be 0 or 1");
   if (scene->n > 0 && !gscreen) return fail(GS_ERR_INVALID_ARG, "gscreen is null");
   const size_t need = gs_workspace_bytes(GS_WS_CAMERA_GRAD, scene->n, 0, 0, 0);
   if (scene->n > 0 && (!ws || ws_bytes < need))
     return fail(GS_ERR_CAPACITY, "camera-gradient workspace needs %zu bytes", need);
   const hipError_t e = gsk::launch_camera_grad(scene->params, int(scene->n), scene->sh_degree, *cam, proj->tiles,
-                                               gscreen, grad_out, ws, shade_of(scene->sh_degree),
+                                               gscreen, position_only, grad_out, ws, shade_of(scene->sh_degree),
                                                as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "camera_grad");
   return GS_OK;

@@ -65,7 +65,8 @@ hipError_t launch_preprocess_bwd(const float* params, int n, int deg, const gs_c
 // camera_grad_ws_bytes(n) bytes of per-block sums.
 size_t camera_grad_ws_bytes(int64_t n);
 hipError_t launch_camera_grad(const float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
-                              const float* gscreen, double* out, void* ws, Shade shade, hipStream_t s);
+                              const float* gscreen, int position_only, double* out, void* ws, Shade shade,
+                              hipStream_t s);
 hipError_t launch_chain_adam(float* params, int n, int deg, const gs_camera& cam, const uint32_t* tiles,
                              const float* gscreen, float* m, float* v, const AdamArgs& a, Shade shade, hipStream_t s);
 // The same, then the projection of the updated Gaussians into np (may alias tiles: each

@@ -109,8 +109,9 @@ struct Proj {
 // near plane, zero quaternion, non-positive determinant).
 // th: the 11 geometry parameters (mean 0-2, log-scales 3-5, quaternion 6-9, logit 10).
 // mip: the opacity is multiplied by comp = sqrt(det V / det(V + 0.3 I)) ([GSG] same section:
-// the Mip-Splatting factor that keeps tiny blobs from adding energy; this ratio gives the
-// dilated footprint exactly the integral of the undilated one), 0 when det V <= 0.
+// the Mip-Splatting correction against the extra brightness the dilation gives very small
+// Gaussians; this ratio gives the dilated footprint exactly the integral of the undilated
+// one), 0 when det V <= 0.
 __device__ inline bool project_geometry_from(const float* th, const gs_camera& cam, int mip, Proj& g) {
   const float mx = th[0], my = th[1], mz = th[2];
   for (int r = 0; r < 3; ++r)

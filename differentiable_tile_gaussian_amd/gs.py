@@ -85,7 +85,7 @@ def _load():
     lib.gs_get_grad_sums.restype = I32
     lib.gs_render_bwd_weighted.argtypes = [P, P, P, P, U32, P, P, P, P, P, P, C.c_float, I32, P, C.c_size_t, P]
     lib.gs_render_bwd_weighted.restype = I32
-    lib.gs_camera_grad.argtypes = [P, P, P, P, P, P, C.c_size_t, P]
+    lib.gs_camera_grad.argtypes = [P, P, P, P, I32, P, P, C.c_size_t, P]
     lib.gs_relocate.argtypes = [P, P, P, I64, I32, P, C.c_double, C.c_double, I64, P, P, C.c_size_t, P]
     lib.gs_relocate.restype = I32
     lib.gs_camera_grad.restype = I32
@@ -283,15 +283,17 @@ def gs_relocate(params, m, v, n, sh_degree, rand, ws, dead_opacity=0.02, donor_o
     return int(moves.value)
 
 
-def gs_camera_grad(params, sh_degree, proj: Proj, cam: GsCamera, gscreen, grad_out, ws, stream=None):
-    """grad_out: device float64[6] = (rotation, translation) gradient of the camera pose."""
+def gs_camera_grad(params, sh_degree, proj: Proj, cam: GsCamera, gscreen, grad_out, ws, position_only=False,
+                   stream=None):
+    """grad_out: device float64[6] = (rotation, translation) gradient of the camera pose
+    (with position_only, the trainer's position-path terms alone)."""
     n = proj.n
     _blocked(params, n, sh_degree)
     if grad_out.dtype != torch.float64 or grad_out.numel() < 6:
         raise ValueError("grad_out must hold 6 float64 values")
     scene = GsScene(n, sh_degree, params.data_ptr() if n else None)
-    _check(_lib.gs_camera_grad(C.byref(scene), C.byref(proj.struct), C.byref(cam), _ptr(gscreen), _ptr(grad_out),
-                               _ptr(ws), ws.numel(), _stream(stream)))
+    _check(_lib.gs_camera_grad(C.byref(scene), C.byref(proj.struct), C.byref(cam), _ptr(gscreen),
+                               int(bool(position_only)), _ptr(grad_out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def gs_adam_step(params, grads, m, v, n, sh_degree, lr, beta1, beta2, eps, step, stream=None):

@@ -229,13 +229,17 @@ int32_t gs_render_bwd_weighted(const gs_scene* scene, const gs_proj* proj, const
  * camera-space centre p = W m + t and through its colour's view direction:
  *   G = J^T dT + dp m^T + t gsh^T  (= dL/dW; gsh the view-direction part of dL/dm),
  *   dL/dw = (M21 - M12, M02 - M20, M10 - M01) with M = G W^T,   dL/dt = dp + W gsh.
+ * position_only = 1 gives the trainer's own accumulation instead (the same section's
+ * code): only the position path, i.e. the torque sum (p - t) x dp and dL/dt = sum dp, with
+ * dp the camera-space position gradient (its projected-mean and J(z) parts); 0 gives the
+ * exact derivative above.  GS_ERR_INVALID_ARG for another value.
  * grad_out: device double[6] = (dL/dw, dL/dt), overwritten.  scene, proj, cam and gscreen as
  * gs_render_bwd read and left them: the parameters before any update of this step (the fused
  * update calls overwrite them, so pose optimisation takes gs_render_bwd and gs_adam).  The
  * per-Gaussian terms are formed in double and summed in a fixed order (the result is
  * reproducible).  ws: gs_workspace_bytes(GS_WS_CAMERA_GRAD, n, 0, 0, 0).  Enqueues only. */
 int32_t gs_camera_grad(const gs_scene* scene, const gs_proj* proj, const gs_camera* cam, const float* gscreen,
-                       double* grad_out, void* ws, size_t ws_bytes, void* stream);
+                       int32_t position_only, double* grad_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Adam, [GSG] Adam section; per-group rates [DR] "From a pixel error back to a quaternion".
  *   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
@@ -327,9 +331,9 @@ int32_t gs_densify(const float* params, const float* m, const float* v, const fl
                    float* v_out, float* stats_out, int64_t capacity, int64_t* n_out, int64_t* counts, void* ws,
                    size_t ws_bytes, void* stream);
 
-/* Relocation of the dead ([GSG] "Densification", the MCMC-style pass: dead Gaussians are
- * moved next to healthy donors, biased toward the largest; both halves shrink by 1.6 and a
- * reshaped Gaussian's Adam moments restart).  Gaussian i is dead when its opacity is below
+/* Relocation of the dead ([GSG] "Densification", the MCMC-style pass: Gaussians that have
+ * become transparent are reused as copies of well-opaque ones, preferring the biggest; each
+ * pair then shrinks by a factor 1.6 and restarts its Adam moments).  Gaussian i is dead when its opacity is below
  * dead_opacity (about 0.02 on the page), a donor when it is not dead, its opacity is above
  * donor_opacity (about 0.4) and its largest log-scale is not NaN (the comparisons on the
  * stored logit against the thresholds' logit formed in double and rounded once to float).
@@ -377,9 +381,9 @@ int32_t gs_get_grad_sums(void);
 int32_t gs_set_active_sh_degree(int32_t degree);
 int32_t gs_get_active_sh_degree(void);
 
-/* Mip-Splatting opacity compensation ([GSG] "Flattening a 3D blob into a 2D oval": a small
- * factor keeps very tiny blobs from adding spurious energy; the trainer's code multiplies the
- * opacity by it in the extent and in alpha).  With on = 1, for the whole process, every
+/* Mip-Splatting opacity compensation ([GSG] "Flattening a 3D blob into a 2D oval": a
+ * correction so that the dilation does not make very small Gaussians brighter overall; the
+ * trainer's code multiplies the opacity by it in the extent and in alpha).  With on = 1, for the whole process, every
  * projection and chain enqueued after it: the record's opacity is
  *   sigmoid(logit) comp,  comp = sqrt(max(det V, 0) / det(V + 0.3 I)),
  * V the undilated screen covariance (the factor that gives the dilated footprint exactly the

@@ -139,9 +139,10 @@ inline int num_planes(int deg) { return 11 + 3 * (deg + 1) * (deg + 1); }
 // band weights are summed, and the inactive ones receive no gradient until their band
 // switches on).  -1: every stored band.  Set by or_set_active_sh_degree.
 int g_active_deg = -1;
-// Mip-Splatting opacity compensation ([GSG] "Flattening a 3D blob into a 2D oval": a small
-// factor keeps tiny blobs from adding spurious energy; the code there multiplies the
-// opacity by comp in the extent and in alpha).  Off (0) by default; set by
+// Mip-Splatting opacity compensation ([GSG] "Flattening a 3D blob into a 2D oval": a
+// correction from Mip-Splatting so that the dilation does not make very small Gaussians
+// brighter overall; the code there multiplies the opacity by comp in the extent and in
+// alpha).  Off (0) by default; set by
 // or_set_mip_compensation.  The factor is not printed on the pages; the reading taken is
 // the one that removes exactly the energy the 0.3 px^2 dilation adds: the footprint
 // o exp(-d^T V^-1 d / 2) integrates to o 2 pi sqrt(det V), so the dilated footprint keeps
@@ -486,11 +487,13 @@ void blend_pixel_bwd(R px, R py, const uint32_t* list, int64_t n_walk, const R* 
 // dL/dW: the covariance path J^T dT (T = J W), the position path dp m^T, and the view
 // direction's path through the centre, t gm_sh^T (dL/dcentre = -gm_sh); of dL/dt: dp and
 // W gm_sh.  With G = dL/dW and M = G W^T the rotation gradient is (M21 - M12, M02 - M20,
-// M10 - M01); for the position path alone that is (p - t) x dp, the pages' torque.
+// M10 - M01); for the position path alone that is (p - t) x dp, the pages' torque, and
+// the translation's is dp alone: the trainer's code accumulates exactly those two
+// (position_only), the exact derivative adds the other paths.
 // out[0..2] += rotation gradient, out[3..5] += translation gradient.
 template <class R>
 void camera_grad_terms(const Fwd<R>& f, const Camera& cam, const R dT[2][3], const R dp[3], const R gm_sh[3],
-                       double* out) {
+                       bool position_only, double* out) {
   const double fx = cam.fx, fy = cam.fy, pz = f.p[2];
   const double J[2][3] = {{fx / pz, 0.0, -fx * double(f.p[0]) / (pz * pz)},
                           {0.0, fy / pz, -fy * double(f.p[1]) / (pz * pz)}};
@@ -499,8 +502,9 @@ void camera_grad_terms(const Fwd<R>& f, const Camera& cam, const R dT[2][3], con
     for (int c = 0; c < 3; ++c) W[r][c] = cam.R[3 * r + c];
   for (int r = 0; r < 3; ++r)
     for (int c = 0; c < 3; ++c)
-      G[r][c] = J[0][r] * double(dT[0][c]) + J[1][r] * double(dT[1][c]) + double(dp[r]) * double(f.m[c]) +
-                double(cam.t[r]) * double(gm_sh[c]);
+      G[r][c] = position_only ? double(dp[r]) * double(f.m[c])
+                              : J[0][r] * double(dT[0][c]) + J[1][r] * double(dT[1][c]) +
+                                    double(dp[r]) * double(f.m[c]) + double(cam.t[r]) * double(gm_sh[c]);
   double M[3][3];
   for (int r = 0; r < 3; ++r)
     for (int c = 0; c < 3; ++c) M[r][c] = G[r][0] * W[c][0] + G[r][1] * W[c][1] + G[r][2] * W[c][2];
@@ -508,7 +512,9 @@ void camera_grad_terms(const Fwd<R>& f, const Camera& cam, const R dT[2][3], con
   out[1] += M[0][2] - M[2][0];
   out[2] += M[1][0] - M[0][1];
   for (int r = 0; r < 3; ++r)
-    out[3 + r] += double(dp[r]) + W[r][0] * double(gm_sh[0]) + W[r][1] * double(gm_sh[1]) + W[r][2] * double(gm_sh[2]);
+    out[3 + r] += position_only ? double(dp[r])
+                                : double(dp[r]) + W[r][0] * double(gm_sh[0]) + W[r][1] * double(gm_sh[1]) +
+                                      W[r][2] * double(gm_sh[2]);
 }
 
 // --------------------------------------------------------- backward chain
@@ -522,7 +528,7 @@ void camera_grad_terms(const Fwd<R>& f, const Camera& cam, const R dT[2][3], con
 // see camera_grad_terms.
 template <class R>
 void chain_one(const R* params, int64_t n, int64_t i, int deg, const Camera& cam, bool smooth,
-               const R* gscreen, R* gparams, double* camg = nullptr) {
+               const R* gscreen, R* gparams, double* camg = nullptr, bool cam_position_only = false) {
   const int P = num_planes(deg);
   for (int pl = 0; pl < P; ++pl) gparams[int64_t(pl) * n + i] = R(0);
   Fwd<R> f = project<R>(params, n, i, deg, cam, smooth);
@@ -613,7 +619,7 @@ void chain_one(const R* params, int64_t n, int64_t i, int deg, const Camera& cam
   for (int c = 0; c < 3; ++c)
     for (int r = 0; r < 3; ++r) gm[c] += cam_R<R>(cam, r, c) * dp[r];
   for (int c = 0; c < 3; ++c) GP(c) = gm[c];
-  if (camg) camera_grad_terms<R>(f, cam, dT, dp, gm_sh, camg);
+  if (camg) camera_grad_terms<R>(f, cam, dT, dp, gm_sh, cam_position_only, camg);
   // Sigma = M M^T -> dM = 2 dSigma M
   R dM[3][3];
   for (int r = 0; r < 3; ++r)
@@ -1261,11 +1267,11 @@ OR_CHAIN(double, f64)
 
 #define OR_CAMERA_GRAD(R, SUF)                                                                                  \
   void or_camera_grad_##SUF(int64_t n, int deg, const R* params, const Camera* cam, int smooth, const R* gscreen, \
-                            double* out6) {                                                                     \
+                            int position_only, double* out6) {                                                  \
     std::vector<R> scratch(size_t(num_planes(deg)) * size_t(n));                                              \
     for (int k = 0; k < 6; ++k) out6[k] = 0.0;                                                                \
     for (int64_t i = 0; i < n; ++i)                                                                           \
-      chain_one<R>(params, n, i, deg, *cam, smooth != 0, gscreen, scratch.data(), out6);                      \
+      chain_one<R>(params, n, i, deg, *cam, smooth != 0, gscreen, scratch.data(), out6, position_only != 0);  \
   }
 OR_CAMERA_GRAD(float, f32)
 OR_CAMERA_GRAD(double, f64)

@@ -59,7 +59,7 @@ def _declare(L):
     L.or_set_active_sh_degree.argtypes = [I32]
     L.or_set_mip_compensation.argtypes = [I32]
     for suf in ("f32", "f64"):
-        getattr(L, f"or_camera_grad_{suf}").argtypes = [I64, I32, P, P, I32, P, P]
+        getattr(L, f"or_camera_grad_{suf}").argtypes = [I64, I32, P, P, I32, P, I32, P]
     L.or_num_planes.restype = I32
     L.or_sh_norm.argtypes = [I32, I32]
     L.or_sh_norm.restype = C.c_double
@@ -431,14 +431,16 @@ def loss_charbonnier(img, tgt, delta=0.03, log_gain=0.0, bias=0.0, dtype=np.floa
 
 
 # ------------------------------------------------------ camera-pose gradient
-def camera_grad(params, sh_degree, cam, gscreen, smooth=False, dtype=np.float32):
+def camera_grad(params, sh_degree, cam, gscreen, smooth=False, dtype=np.float32, position_only=False):
     """Gradient of the loss with respect to the camera pose from the screen partials
     ([9][n]): (rotation, perturbed on the left as W <- (I + [w]x) W; translation), summed
-    over the visible Gaussians in fp64 (see camera_grad_terms in gs_oracle.cpp)."""
+    over the visible Gaussians in fp64 (see camera_grad_terms in gs_oracle.cpp).  With
+    position_only, the trainer's terms: the torque (p - t) x dp and dp alone."""
     params = _c(params, dtype)
     gscreen = _c(gscreen, dtype)
     out = np.zeros(6, np.float64)
     c = make_camera(cam)
     fn = lib().or_camera_grad_f64 if dtype == np.float64 else lib().or_camera_grad_f32
-    fn(params.shape[1], sh_degree, _p(params), C.byref(c), int(smooth), _p(gscreen), _p(out))
+    fn(params.shape[1], sh_degree, _p(params), C.byref(c), int(smooth), _p(gscreen), int(bool(position_only)),
+       _p(out))
     return out

@@ -112,13 +112,14 @@ def test_argument_errors_without_gpu(gs):
     assert L.gs_loss_charbonnier(1, 1, 8, 8, C.c_float(0.03), 1, 1, 1, None, None, 0, None) == gs.GS_ERR_CAPACITY
     # camera-pose gradient: scene, output, gscreen and workspace are checked first
     sc = gs.GsScene(10, 1, 1234)
-    assert L.gs_camera_grad(None, C.byref(proj), C.byref(cam), 1, 1, 1, big, None) == gs.GS_ERR_INVALID_ARG
-    assert L.gs_camera_grad(C.byref(sc), C.byref(proj), C.byref(cam), 1, None, 1, big, None) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_camera_grad(None, C.byref(proj), C.byref(cam), 1, 0, 1, 1, big, None) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_camera_grad(C.byref(sc), C.byref(proj), C.byref(cam), 1, 0, None, 1, big, None) == gs.GS_ERR_INVALID_ARG
     assert "grad_out" in gs.gs_last_error()
-    assert L.gs_camera_grad(C.byref(sc), C.byref(proj), C.byref(cam), None, 1, 1, big, None) == gs.GS_ERR_INVALID_ARG
-    assert L.gs_camera_grad(C.byref(sc), None, C.byref(cam), 1, 1, 1, big, None) == gs.GS_ERR_INVALID_ARG
-    assert L.gs_camera_grad(C.byref(sc), C.byref(proj), C.byref(cam), 1, 1, 1, 47, None) == gs.GS_ERR_CAPACITY
+    assert L.gs_camera_grad(C.byref(sc), C.byref(proj), C.byref(cam), None, 0, 1, 1, big, None) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_camera_grad(C.byref(sc), None, C.byref(cam), 1, 0, 1, 1, big, None) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_camera_grad(C.byref(sc), C.byref(proj), C.byref(cam), 1, 0, 1, 1, 47, None) == gs.GS_ERR_CAPACITY
     assert "camera-gradient workspace" in gs.gs_last_error()
+    assert L.gs_camera_grad(C.byref(sc), C.byref(proj), C.byref(cam), 1, 2, 1, 1, big, None) == gs.GS_ERR_INVALID_ARG
     # SH degree ramp
     assert L.gs_get_active_sh_degree() == -1
     assert L.gs_set_active_sh_degree(4) == gs.GS_ERR_INVALID_ARG

@@ -42,17 +42,17 @@ def _backward(torch, gs, params, deg, cam, seed, scale=1e-2):
     return pl, c
 
 
-def _camera_grad(torch, gs, pl, deg, c):
+def _camera_grad(torch, gs, pl, deg, c, position_only=False):
     out = torch.full((6,), float("nan"), dtype=torch.float64, device="cuda")
     ws = gs.workspace(gs.GS_WS_CAMERA_GRAD, n=pl.n)
-    gs.gs_camera_grad(pl.params, deg, pl.proj, c, pl.gscreen, out, ws)
+    gs.gs_camera_grad(pl.params, deg, pl.proj, c, pl.gscreen, out, ws, position_only=position_only)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
-def _check_against_oracle(oracle, got, params, deg, cam, gscreen_9n):
-    o32 = oracle.camera_grad(params, deg, cam, gscreen_9n, dtype=np.float32)
-    o64 = oracle.camera_grad(params, deg, cam, gscreen_9n, dtype=np.float64)
+def _check_against_oracle(oracle, got, params, deg, cam, gscreen_9n, position_only=False):
+    o32 = oracle.camera_grad(params, deg, cam, gscreen_9n, dtype=np.float32, position_only=position_only)
+    o64 = oracle.camera_grad(params, deg, cam, gscreen_9n, dtype=np.float64, position_only=position_only)
     for grp in (slice(0, 3), slice(3, 6)):
         e32 = np.abs(o32[grp] - o64[grp]).max()
         tol = 4.0 * e32 + 1e-6 * np.abs(o64[grp]).max()
@@ -88,6 +88,20 @@ def test_camera_grad_matches_oracle(gs_cam, oracle, deg, active):
     # the same call again: the same words (fixed summation order)
     again = _camera_grad(torch, gs, pl, deg, c)
     np.testing.assert_array_equal(got.view(np.uint64), again.view(np.uint64))
+
+
+@pytest.mark.parametrize("deg", [0, 3])
+def test_camera_grad_position_only(gs_cam, oracle, deg):
+    """The trainer's own terms (position path only: torque (p - t) x dp, and dp)."""
+    import torch
+    gs = gs_cam
+    s = _scene(60 + deg, 3000, deg)
+    cam = scenes.look_at_origin((-0.4, 0.5, -4.4), 160, 120, 150.0)
+    pl, c = _backward(torch, gs, s.params, deg, cam, seed=7 + deg)
+    got = _camera_grad(torch, gs, pl, deg, c, position_only=True)
+    _check_against_oracle(oracle, got, s.params, deg, cam, pl.gscreen[:s.n].T.cpu().numpy(), position_only=True)
+    full = _camera_grad(torch, gs, pl, deg, c)
+    assert np.abs(full[:3] - got[:3]).max() > 1e-3 * np.abs(full[:3]).max()
 
 
 def test_camera_grad_ragged_and_empty(gs_cam, oracle):

@@ -42,3 +42,27 @@ def test_camera_grad_matches_central_differences(oracle):
         assert abs(cg[3 + k] - fd_t) <= 1e-3 * scale_t, (k, cg[3 + k], fd_t)
         assert abs(cg[k] - fd_w) <= 1e-3 * scale_w, (k, cg[k], fd_w)
     assert np.abs(cg).min() > 0
+
+
+def test_position_only_is_the_pages_torque(oracle):
+    """The trainer's terms ([GSG] "Forgiving the camera and the light": the torque
+    (p - t) x dp and dp, from each Gaussian's camera-space position gradient).  With SH
+    degree 0 the position gradient is dp_i = W dL/dm_i, so the sums are W sum_i m_i x dL/dm_i
+    and W sum_i dL/dm_i, with dL/dm from the oracle's own parameter gradients."""
+    s = scenes.random_scene(6, 40, 0, spread=1.0, logscale_std=0.5)
+    cam = scenes.look_at_origin((1.0, 0.8, -4.0), 40, 30, 40.0)
+    dLdI = np.random.default_rng(10).standard_normal((3, 30, 40))
+    g, gscreen, _ = oracle.smooth_grad(s.params, 0, cam, dLdI)
+    pos = oracle.camera_grad(s.params, 0, cam, gscreen, smooth=True, dtype=np.float64, position_only=True)
+    full = oracle.camera_grad(s.params, 0, cam, gscreen, smooth=True, dtype=np.float64)
+    W = cam.R.astype(np.float64)
+    m = s.params[0:3].astype(np.float64)
+    gm = g[0:3]
+    want_w = W @ np.cross(m.T, gm.T).sum(axis=0)
+    want_t = W @ gm.sum(axis=1)
+    # (W a) x (W b) = W (a x b) and W W^T = I hold to the rounding of the fp32 rotation (1e-7)
+    np.testing.assert_allclose(pos[:3], want_w, rtol=1e-6, atol=1e-7 * np.abs(want_w).max())
+    np.testing.assert_allclose(pos[3:], want_t, rtol=1e-6, atol=1e-7 * np.abs(want_t).max())
+    # the covariance path is not negligible for these anisotropic Gaussians
+    assert np.abs(full[:3] - pos[:3]).max() > 1e-3 * np.abs(full[:3]).max()
+    np.testing.assert_allclose(full[3:], pos[3:], rtol=1e-12)    # degree 0: no view-direction term

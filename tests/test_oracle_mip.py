@@ -1,6 +1,6 @@
 """Mip-Splatting opacity compensation in the oracle ([GSG] "Flattening a 3D blob into a 2D
-oval": a small factor keeps very tiny blobs from adding spurious energy; the code there
-multiplies the opacity by it in the extent and in alpha).  The factor is not printed; the
+oval": a correction so that the dilation does not make very small Gaussians brighter
+overall; the code there multiplies the opacity by it in the extent and in alpha).  The factor is not printed; the
 reading is comp = sqrt(det V / det(V + 0.3 I)), the one that gives the dilated footprint
 exactly the energy of the undilated one.
 
