@@ -340,6 +340,17 @@ struct Decision {
   int kind;
 };
 
+// FNV-1a step over the eight bytes of v: folds a pixel's decision outcomes into one
+// signature, so that two renders can be compared decision for decision.
+inline uint64_t sig_mix(uint64_t h, uint64_t v) {
+  for (int b = 0; b < 8; ++b) {
+    h ^= (v >> (8 * b)) & 0xffu;
+    h *= 0x100000001b3ull;
+  }
+  return h;
+}
+constexpr uint64_t kSigSeed = 0xcbf29ce484222325ull;
+
 // Front-to-back compositing of one pixel over an ordered list, [GSG] "The
 // painting itself: front-to-back alpha compositing"; weights as in [GST]
 // opacity slide and [TBDR] worked examples.  In smooth mode nothing is capped,
@@ -352,7 +363,7 @@ template <class R>
 void blend_pixel(R px, R py, const uint32_t* list, int64_t len, const R* uv, const R* conic, const R* opac,
                  const R* rgb, int64_t n, const R bg[3], bool smooth, R out[3], R* T_out, PixelTrace* tr,
                  int64_t* evals, const Decision* flip = nullptr, std::vector<Decision>* close = nullptr,
-                 double close_below = 0.0) {
+                 double close_below = 0.0, uint64_t* sig = nullptr) {
   R T = R(1);
   R C[3] = {R(0), R(0), R(0)};
   PixelTrace t{0, 0, std::numeric_limits<double>::infinity()};
@@ -379,6 +390,9 @@ void blend_pixel(R px, R py, const uint32_t* list, int64_t len, const R* uv, con
       }
       bool skip = alpha < alpha_min<R>();
       if (flip && flip->k == k && flip->kind == kDecSkip) skip = !skip;
+      // the outcome of each decision: entry k skipped, or blended with alpha capped (the
+      // backward's test, o G > 0.99, which decides whether the entry passes gradient on)
+      if (sig) *sig = sig_mix(sig_mix(*sig, uint64_t(k)), skip ? 1u : (araw > R(kAlphaCap) ? 2u : 3u));
       if (skip) continue;
       // a capped alpha is exact; closeness to the cap is the backward's concern
       tscale += 1.0 + (capped ? 0.0 : ascale * double(alpha) / (1.0 - double(alpha)));
@@ -398,6 +412,7 @@ void blend_pixel(R px, R py, const uint32_t* list, int64_t len, const R* uv, con
   for (int ch = 0; ch < 3; ++ch) out[ch] = C[ch] + T * bg[ch];
   *T_out = T;
   if (tr) *tr = t;
+  if (sig) *sig = sig_mix(*sig, uint64_t(t.n_contrib) | (uint64_t(t.n_examined) << 32));
 }
 
 // Back-to-front walk of one pixel, recovering the transmittance by division
@@ -798,6 +813,37 @@ void smooth_order(int64_t n, const R* depth, const uint8_t* visible, std::vector
   std::stable_sort(list.begin(), list.end(), [&](uint32_t a, uint32_t b) { return depth[a] < depth[b]; });
 }
 
+// Tiled forward render of all pixels.  Outputs planar rgb [3][H][W], T_final and
+// n_contrib [H][W]; optional n_examined, margin and sig (the decision signature of
+// blend_pixel) [H][W]; returns evals.
+template <class R>
+int64_t render_tiled(int64_t n, const R* uv, const R* conic, const R* opac, const R* rgb, const uint32_t* vals,
+                     const uint32_t* ranges, const Camera* cam, R* out_rgb, R* T_final, uint32_t* n_contrib,
+                     uint32_t* n_examined, double* margin, uint64_t* sig) {
+  const int W = cam->width, H = cam->height, tx = tiles_x(*cam), ty = tiles_y(*cam);
+  const int64_t nt = int64_t(tx) * ty, HW = int64_t(W) * H;
+  const R bg[3] = {R(cam->bg[0]), R(cam->bg[1]), R(cam->bg[2])};
+  int64_t evals = 0;
+  for (int y = 0; y < H; ++y)
+    for (int x = 0; x < W; ++x) {
+      const int64_t t = int64_t(y / kTile) * tx + x / kTile;
+      const uint32_t s = ranges[t], e = ranges[nt + t];
+      const int64_t p = int64_t(y) * W + x;
+      R out[3], T;
+      PixelTrace tr;
+      uint64_t h = kSigSeed;
+      blend_pixel<R>(R(x) + R(0.5), R(y) + R(0.5), vals + s, int64_t(e) - s, uv, conic, opac, rgb, n, bg, false,
+                     out, &T, &tr, &evals, nullptr, nullptr, 0.0, sig ? &h : nullptr);
+      for (int ch = 0; ch < 3; ++ch) out_rgb[ch * HW + p] = out[ch];
+      T_final[p] = T;
+      n_contrib[p] = tr.n_contrib;
+      if (n_examined) n_examined[p] = tr.n_examined;
+      if (margin) margin[p] = tr.margin;
+      if (sig) sig[p] = h;
+    }
+  return evals;
+}
+
 }  // namespace
 
 // ===================================================================== C ABI
@@ -1037,31 +1083,20 @@ void or_bin_sort(int64_t n, const float* depth, const int32_t* rect, const uint3
   bin_sort(n, depth, rect, tiles, tx, ty, keys, vals, ranges);
 }
 
-// Tiled forward render of all pixels.  Outputs planar rgb [3][H][W], T_final and
-// n_contrib [H][W]; optional n_examined and margin [H][W]; returns evals.
 int64_t or_render_fwd_f32(int64_t n, const float* uv, const float* conic, const float* opac, const float* rgb,
                           const uint32_t* vals, const uint32_t* ranges, const Camera* cam, float* out_rgb,
                           float* T_final, uint32_t* n_contrib, uint32_t* n_examined, double* margin) {
-  const int W = cam->width, H = cam->height, tx = tiles_x(*cam), ty = tiles_y(*cam);
-  const int64_t nt = int64_t(tx) * ty, HW = int64_t(W) * H;
-  const float bg[3] = {cam->bg[0], cam->bg[1], cam->bg[2]};
-  int64_t evals = 0;
-  for (int y = 0; y < H; ++y)
-    for (int x = 0; x < W; ++x) {
-      const int64_t t = int64_t(y / kTile) * tx + x / kTile;
-      const uint32_t s = ranges[t], e = ranges[nt + t];
-      float out[3], T;
-      PixelTrace tr;
-      blend_pixel<float>(float(x) + 0.5f, float(y) + 0.5f, vals + s, int64_t(e) - s, uv, conic, opac, rgb, n, bg,
-                         false, out, &T, &tr, &evals);
-      const int64_t p = int64_t(y) * W + x;
-      for (int ch = 0; ch < 3; ++ch) out_rgb[ch * HW + p] = out[ch];
-      T_final[p] = T;
-      n_contrib[p] = tr.n_contrib;
-      if (n_examined) n_examined[p] = tr.n_examined;
-      if (margin) margin[p] = tr.margin;
-    }
-  return evals;
+  return render_tiled<float>(n, uv, conic, opac, rgb, vals, ranges, cam, out_rgb, T_final, n_contrib, n_examined,
+                             margin, nullptr);
+}
+
+// The thresholded tiled forward in double, with every pixel's decision signature (for
+// finite differences that keep only steps which change no decision).
+int64_t or_render_fwd_f64(int64_t n, const double* uv, const double* conic, const double* opac, const double* rgb,
+                          const uint32_t* vals, const uint32_t* ranges, const Camera* cam, double* out_rgb,
+                          double* T_final, uint32_t* n_contrib, uint64_t* sig) {
+  return render_tiled<double>(n, uv, conic, opac, rgb, vals, ranges, cam, out_rgb, T_final, n_contrib, nullptr,
+                              nullptr, sig);
 }
 
 // Thresholded forward render without tiles: every pixel walks every visible

@@ -8,13 +8,16 @@ library ([plane][n] per Gaussian, [ch][H][W] per image).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 import os
 
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liboracle.so")
+# GS_ORACLE_LIB selects another build of the same source (the sanitizer build of the
+# CPU test job); the default is the one oracle/build.py writes.
+LIB_PATH = os.environ.get("GS_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 
 
 class OrCamera(C.Structure):
@@ -76,6 +79,8 @@ def _declare(L):
     L.or_bin_sort.argtypes = [I64, P, P, P, I32, I32, P, P, P]
     L.or_render_fwd_f32.argtypes = [I64] + [P] * 6 + [P] + [P] * 5
     L.or_render_fwd_f32.restype = I64
+    L.or_render_fwd_f64.argtypes = [I64] + [P] * 6 + [P] + [P] * 4
+    L.or_render_fwd_f64.restype = I64
     L.or_render_untiled_f32.argtypes = [I64] + [P] * 6 + [P, P, P]
     L.or_render_pixels_f32.argtypes = [I64] + [P] * 6 + [P, I64, P, P, P, P, P, P]
     L.or_render_bwd_f32.argtypes = [I64] + [P] * 6 + [P] + [P] * 6
@@ -90,6 +95,21 @@ def _declare(L):
     L.or_densify_f32.restype = I64
     L.or_relocate_f32.argtypes = [I64, I32, P, P, P, P, F, F, F, I64]
     L.or_relocate_f32.restype = I64
+
+
+@contextlib.contextmanager
+def library(path):
+    """Run the oracle functions against another build of gs_oracle.cpp (the tests'
+    planted-mistake variants) for the duration of the block."""
+    global _lib
+    saved = lib()
+    alt = C.CDLL(path)
+    _declare(alt)
+    _lib = alt
+    try:
+        yield
+    finally:
+        _lib = saved
 
 
 def _p(a):
@@ -158,6 +178,45 @@ def render_fwd(pre, vals, ranges, cam):
         _p(_c(ranges, np.uint32)), C.byref(c), _p(out["rgb"]), _p(out["T"]), _p(out["n_contrib"]),
         _p(out["n_examined"]), _p(out["margin"])))
     return out
+
+
+def render_thresholded(params, sh_degree, cam):
+    """The thresholded path (cull, tile rectangle, sort, skip, cap, stop, colour clamp) with
+    every operation in fp64: image, T, n_contrib and each pixel's decision signature
+    (`sig`), with the projection, the sorted ids and the ranges it used."""
+    pre = preprocess(params, sh_degree, cam, dtype=np.float64)
+    _, vals, ranges = bin_sort(pre, cam)
+    n = pre["n"]
+    H, W = cam.height, cam.width
+    out = dict(rgb=np.zeros((3, H, W), np.float64), T=np.zeros((H, W), np.float64),
+               n_contrib=np.zeros((H, W), np.uint32), sig=np.zeros((H, W), np.uint64))
+    c = make_camera(cam)
+    lib().or_render_fwd_f64(n, _p(pre["uv"]), _p(pre["conic"]), _p(pre["opac"]), _p(pre["rgb"]), _p(vals),
+                            _p(ranges), C.byref(c), _p(out["rgb"]), _p(out["T"]), _p(out["n_contrib"]),
+                            _p(out["sig"]))
+    out.update(pre=pre, vals=vals, ranges=ranges)
+    return out
+
+
+def decisions(r):
+    """Everything a thresholded render decides, from render_thresholded's result: culls,
+    tile rectangles, clamped colour channels (a clamped channel is exactly 0), the pair
+    order, and per pixel the skip / cap / stop outcomes.  Two renders with equal decisions
+    lie on one smooth piece of the rendering function."""
+    pre = r["pre"]
+    return (pre["visible"], pre["rect"], pre["tiles"], pre["rgb"] == 0.0, r["vals"], r["ranges"], r["sig"])
+
+
+def same_decisions(a, b):
+    return all(np.array_equal(x, y) for x, y in zip(decisions(a), decisions(b)))
+
+
+def thresholded_grad(params, sh_degree, cam, dLdI):
+    """Analytic gradient, in fp64, of sum(dLdI * render_thresholded(params)) with respect
+    to the parameters (the blend's backward walk and the chain with every threshold in place)."""
+    r = render_thresholded(params, sh_degree, cam)
+    gscreen = render_bwd_f64(r["pre"], r["vals"], r["ranges"], cam, r, dLdI)
+    return preprocess_bwd(params, sh_degree, cam, gscreen, dtype=np.float64), gscreen, r
 
 
 def render_untiled(pre, cam):

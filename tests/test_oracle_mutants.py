@@ -1,0 +1,126 @@
+"""Planted mistakes: each pin must be able to fail.
+
+Every case below copies oracle/gs_oracle.cpp, changes one statement into a plausible
+mistake (a comparison, a sign, a dropped term, a mask on the wrong quantity), builds the
+copy with the oracle's own flags into a temporary directory and runs the pins named for
+it against that build.  At least one of them must fail.  Nothing here touches the
+committed oracle or its library, and nothing runs on a GPU.
+"""
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+from tests import test_oracle_pins as pins
+from tests import test_oracle_threshold_pins as tpins
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "gs_oracle.cpp")
+
+
+def _fd_smooth(seeds):
+    def run(O):
+        for s in seeds:
+            pins.test_gradients_finite_difference_smooth(O, s, 1 + s % 8, (0, 1, 3)[s % 3])
+    return run
+
+
+def _fd_thresholded(cases):
+    def run(O):
+        for c in cases:
+            tpins.fd_check_thresholded(O, *c)
+    return run
+
+
+def _pin(fn, *args):
+    return lambda O: fn(O, *args)
+
+
+# name: (statement as written in the oracle, the planted version, pins that must catch it)
+MUTANTS = {
+    "cap_at_or_above": (
+        "capped = araw > R(kAlphaCap);",
+        "capped = araw >= R(kAlphaCap);",
+        [_pin(tpins.test_alpha_exactly_at_cap_passes_gradient)]),
+    "capped_alpha_passes_gradient": (
+        "    if (capped) continue;                // alpha = 0.99 does not depend on opacity or position\n",
+        "",
+        [_pin(tpins.test_capped_alpha_closed_form), _fd_thresholded([tpins.THR_CASES[6]])]),
+    "clamp_mask_on_clamped_colour": (
+        "gc[ch] = (!smooth && f.raw[ch] < R(0)) ? R(0) : GS(6 + ch);",
+        "gc[ch] = (!smooth && f.rgb[ch] <= R(0)) ? R(0) : GS(6 + ch);",
+        [_pin(tpins.test_colour_exactly_zero_passes_gradient)]),
+    "clamp_mask_missing": (
+        "gc[ch] = (!smooth && f.raw[ch] < R(0)) ? R(0) : GS(6 + ch);",
+        "gc[ch] = GS(6 + ch);",
+        [_pin(tpins.test_clamped_channel_closed_form), _fd_thresholded([tpins.THR_CASES[2]])]),
+    "clamp_mask_missing_in_view_direction": (
+        "for (int a = 0; a < 3; ++a) gdir[a] += gc[ch] * coef * f.dY[k][a];",
+        "for (int a = 0; a < 3; ++a) gdir[a] += GS(6 + ch) * coef * f.dY[k][a];",
+        [_pin(tpins.test_clamped_channel_adds_no_view_direction_term), _fd_thresholded([tpins.THR_CASES[2]])]),
+    "view_direction_term_dropped": (
+        "  if (K > 0) {\n",
+        "  if (false) {\n",
+        [_fd_smooth([1, 2])]),
+    "conic_B_sign": (
+        "gscreen[3 * n + g] += ge * dx * dy;",
+        "gscreen[3 * n + g] -= ge * dx * dy;",
+        [_fd_smooth([0, 1])]),
+    "jacobian_depth_path_dropped": (
+        "  dp[0] += dJ[0][2] * (-fx / pz2);\n",
+        "",
+        [_fd_smooth([0, 1])]),
+    "quaternion_sign": (
+        "gq[0] = R(2) * (-z * dR[0][1]",
+        "gq[0] = R(2) * (z * dR[0][1]",
+        [_fd_smooth([0, 1])]),
+    "early_stop_disabled": (
+        "      if (stop) break;\n",
+        "",
+        [_pin(pins.test_early_stop_and_contributor_count)]),
+    "ssim_variance_derivative_sign": (
+        "dsx[idx] = -(A1 * A2) / (B1 * B2 * B2);",
+        "dsx[idx] = (A1 * A2) / (B1 * B2 * B2);",
+        [_pin(pins.test_loss_gradient_finite_difference)]),
+}
+
+
+def _build(name, tmpdir):
+    orig, planted, _ = MUTANTS[name]
+    src = open(ORACLE_SRC).read()
+    assert src.count(orig) == 1, f"{name}: the statement to change is not in the oracle exactly once"
+    path = os.path.join(tmpdir, f"{name}.cpp")
+    with open(path, "w") as f:
+        f.write(src.replace(orig, planted))
+    so = os.path.join(tmpdir, f"lib_{name}.so")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC", path,
+                    "-o", so], check=True, capture_output=True)
+    return so
+
+
+@pytest.fixture(scope="module")
+def mutant_libs(tmp_path_factory):
+    d = str(tmp_path_factory.mktemp("oracle_mutants"))
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        libs = dict(zip(MUTANTS, ex.map(lambda n: _build(n, d), MUTANTS)))
+    return libs
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_planted_mistake_fails_a_pin(oracle, mutant_libs, name):
+    caught = 0
+    with oracle.library(mutant_libs[name]):
+        for check in MUTANTS[name][2]:
+            try:
+                check(oracle)
+            except AssertionError:
+                caught += 1
+    assert caught > 0, f"no pin caught the planted mistake {name}"
+
+
+def test_unplanted_oracle_passes_the_same_pins(oracle):
+    """The checks used above pass on the committed oracle (so a failure above is the
+    planted mistake's doing)."""
+    for _, _, checks in MUTANTS.values():
+        for check in checks:
+            check(oracle)
