@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--stage-report", action="store_true", help="also print per-stage times to stderr")
     ap.add_argument("--no-densify", action="store_true", help="skip the density-control measurement")
     ap.add_argument("--fixed-sums", action="store_true",
-                    help="sum the backward's gradients in fixed point (reproducible; gs_set_grad_sums)")
+                    help="sum the backward's gradients in fixed point (reproducible; gs_config.grad_sums)")
     ap.add_argument("--no-fuse-projection", action="store_true",
                     help="project each step's camera in its own preprocess call instead of in the previous "
                          "step's update")
@@ -112,13 +112,13 @@ def run_steps(pl, cams, targets, first, count, timer=None, gs=None, fuse=True):
         c, tgt = cams[idx], targets[idx]
         if timer: timer.mark(s, 0)
         if not (fuse and pl.projected_for is c):
-            pl.pairs = gs.gs_preprocess(pl.params, pl.deg, c, pl.proj, pl.ws_pre)
+            pl.pairs = gs.gs_preprocess(pl.params, pl.deg, c, pl.proj, pl.ws_pre, cfg=pl.cfg)
         pl.projected_for = None
         pl._reserve(pl.pairs)
         if timer: timer.mark(s, 1)
         gs.gs_bin_sort(pl.proj, c, pl.pairs, pl.keys, pl.vals, pl.ranges, pl.ws_sort)
         if timer: timer.mark(s, 2)
-        gs.gs_render_fwd(pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.rgb, pl.T, pl.nc, pl.ws_render)
+        gs.gs_render_fwd(pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.rgb, pl.T, pl.nc, pl.ws_render, cfg=pl.cfg)
         if timer: timer.mark(s, 3)
         gs.gs_loss_l1_dssim(pl.rgb, tgt, pl.lam, pl.loss, pl.dLdI, pl.ws_loss)
         if timer: timer.mark(s, 4)
@@ -128,12 +128,12 @@ def run_steps(pl, cams, targets, first, count, timer=None, gs=None, fuse=True):
             pl.pairs = gs.gs_render_bwd_adam_project(pl.params, pl.deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c,
                                                      pl.T, pl.nc, pl.dLdI, pl.gscreen, pl.m, pl.v, pl.lr,
                                                      pl.betas[0], pl.betas[1], pl.eps, pl.t, pl.ws_render,
-                                                     cams[nxt], pl.proj, pl.ws_pre, pl.dstats)
+                                                     cams[nxt], pl.proj, pl.ws_pre, pl.dstats, cfg=pl.cfg)
             pl.projected_for = cams[nxt]
         else:
             gs.gs_render_bwd_adam(pl.params, pl.deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc,
                                   pl.dLdI, pl.gscreen, pl.m, pl.v, pl.lr, pl.betas[0], pl.betas[1], pl.eps, pl.t,
-                                  pl.ws_render)
+                                  pl.ws_render, cfg=pl.cfg)
         if timer: timer.mark(s, 5)
 
 
@@ -216,12 +216,12 @@ def measure_camera_grad(pl, cam, torch, gs, reps=20):
     dev = pl.params.device
     out = torch.zeros(6, dtype=torch.float64, device=dev)
     ws = gs.workspace(gs.GS_WS_CAMERA_GRAD, n=pl.n)
-    gs.gs_camera_grad(pl.params, pl.deg, pl.proj, cam, pl.gscreen, out, ws)
+    gs.gs_camera_grad(pl.params, pl.deg, pl.proj, cam, pl.gscreen, out, ws, cfg=pl.cfg)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     ev[0].record()
     for _ in range(reps):
-        gs.gs_camera_grad(pl.params, pl.deg, pl.proj, cam, pl.gscreen, out, ws)
+        gs.gs_camera_grad(pl.params, pl.deg, pl.proj, cam, pl.gscreen, out, ws, cfg=pl.cfg)
     ev[1].record()
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[1]) / reps
@@ -336,14 +336,12 @@ def main():
     from differentiable_tile_gaussian_amd.pipeline import Pipeline
 
     torch.cuda.set_device(0)
+    split = [2048, 512]
     if args.split:
-        first, chunk = (int(x) for x in args.split.split(","))
-        gs.gs_set_tuning(gs.GS_TUNE_SPLIT_FIRST, first)
-        gs.gs_set_tuning(gs.GS_TUNE_SPLIT_CHUNK, chunk)
-    split = [gs.gs_get_tuning(gs.GS_TUNE_SPLIT_FIRST), gs.gs_get_tuning(gs.GS_TUNE_SPLIT_CHUNK)]
+        split = [int(x) for x in args.split.split(",")]
     fuse = not args.no_fuse_projection
-    if args.fixed_sums:
-        gs.gs_set_grad_sums(gs.GS_GRAD_SUMS_FIXED)
+    cfg = gs.GsConfig(grad_sums=gs.GS_GRAD_SUMS_FIXED if args.fixed_sums else gs.GS_GRAD_SUMS_FLOAT,
+                      split_first=split[0], split_chunk=split[1])
     t_setup = time.perf_counter()
     wl = scenes.CONFIGS[args.workload]()
     cams = [gs.make_camera(c) for c in wl.cameras]
@@ -352,7 +350,7 @@ def main():
     params = torch.from_numpy(wl.scene.params).cuda()
     n, deg = wl.scene.n, wl.scene.sh_degree
     P = params.shape[0]
-    pl = Pipeline(params, deg, cam0.width, cam0.height)
+    pl = Pipeline(params, deg, cam0.width, cam0.height, cfg=cfg)
     setup_s = time.perf_counter() - t_setup
 
     # warm-up: the first step untimed (code objects load, caches are cold), then every
@@ -381,7 +379,7 @@ def main():
 
     # evaluation counts: replay the same cameras from the same starting state, untimed
     params2 = torch.from_numpy(wl.scene.params).cuda()
-    pl2 = Pipeline(params2, deg, cam0.width, cam0.height)
+    pl2 = Pipeline(params2, deg, cam0.width, cam0.height, cfg=cfg)
     run_steps(pl2, cams, targets, 0, args.warmup, gs=gs, fuse=fuse)
     ev_f = ev_b = 0
     for s in range(args.steps):

@@ -35,7 +35,7 @@ def hipcc():
 def common_flags():
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics",
-            "-Wall", "-Wno-unused-function"]
+            "-Wall", "-Wno-unused-function", "-Werror"]
 
 
 def _compile(src, verbose):

@@ -16,8 +16,6 @@
 //
 // Compiled without floating-point contraction: the split children's means are the
 // written sequence of fp32 roundings.
-#include <rocprim/device/device_radix_sort.hpp>
-
 #include "gs_internal.h"
 #include "profile.h"
 
@@ -146,8 +144,8 @@ __global__ void __launch_bounds__(256) densify_scatter_kernel(
 // ---- relocation of the dead ([GSG] "Densification", the MCMC-style pass)
 // Dead: logit below logit(dead opacity); donor: not dead, logit above logit(donor
 // opacity) and a largest log-scale that is not NaN.  key: the largest log-scale (-0 made
-// +0) as an unsigned integer in the order of the floats, so that a descending radix sort
-// ranks the donors largest first.
+// +0) as an unsigned integer in the order of the floats, bit-inverted, so that a stable
+// ascending radix sort ranks the donors largest first with equal sizes in index order.
 __global__ void __launch_bounds__(256) relocate_classify_kernel(const float* __restrict__ params, int n, int P,
                                                                  float logit_dead, float logit_donor,
                                                                  uint32_t* __restrict__ fdead,
@@ -162,7 +160,7 @@ __global__ void __launch_bounds__(256) relocate_classify_kernel(const float* __r
   fdead[i] = dead;
   fdonor[i] = !dead && logit > logit_donor && lsmax == lsmax;
   const uint32_t u = __float_as_uint(lsmax + 0.0f);
-  key[i] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  key[i] = ~((u & 0x80000000u) ? ~u : (u | 0x80000000u));
 }
 
 // The dead in index order, and the donors' keys and indices in index order.
@@ -215,19 +213,11 @@ __global__ void __launch_bounds__(256) relocate_move_kernel(float* __restrict__ 
   for (int pl = 3; pl < 6; ++pl) gd[pl * kGB] = gd[pl * kGB] - shrink;
 }
 
-size_t radix_temp_bytes(int64_t n) {
-  size_t bytes = 0;
-  rocprim::radix_sort_pairs_desc(nullptr, bytes, static_cast<const uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr),
-                                 static_cast<const uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr),
-                                 size_t(n > 0 ? n : 1), 0, 32);
-  return bytes;
-}
-
 }  // namespace
 
 // Relocation workspace: two flag arrays and their prefix sums and scan space, the two
-// totals, the keys, the dead list, the donors' keys and indices before and after the
-// sort, and the sort's own temporary space.
+// totals, the keys, the dead list, the donors' keys and indices, and the space of the
+// sort that ranks them.
 RelocateWs carve_relocate(void* ws, int64_t n) {
   char* base = static_cast<char*>(ws);
   size_t off = 0;
@@ -249,10 +239,7 @@ RelocateWs carve_relocate(void* ws, int64_t n) {
   w.dead_list = reinterpret_cast<uint32_t*>(take(items));
   w.key_in = reinterpret_cast<uint32_t*>(take(items));
   w.idx_in = reinterpret_cast<uint32_t*>(take(items));
-  w.key_out = reinterpret_cast<uint32_t*>(take(items));
-  w.idx_out = reinterpret_cast<uint32_t*>(take(items));
-  w.sort_bytes = radix_temp_bytes(n);
-  w.sort_temp = take(w.sort_bytes);
+  w.sort_ws = take(sort_pairs_ws_bytes(n));
   w.bytes = off;
   return w;
 }
@@ -282,14 +269,11 @@ hipError_t launch_relocate_move(float* params, float* m, float* v, int n, int de
                                 int moves, float shrink, void* ws, hipStream_t s) {
   RelocateWs w = carve_relocate(ws, n);
   if (moves <= 0) return hipSuccess;
-  size_t bytes = w.sort_bytes;
-  hipError_t e = rocprim::radix_sort_pairs_desc(w.sort_temp, bytes, static_cast<const uint32_t*>(w.key_in),
-                                                w.key_out, static_cast<const uint32_t*>(w.idx_in), w.idx_out,
-                                                size_t(donors), 0, 32, s);
+  const hipError_t e = launch_sort_pairs_u32(w.key_in, w.idx_in, uint32_t(donors), n, w.sort_ws, s);
   if (e != hipSuccess) return e;
   GSK_PROF("relocate_move", s);
   relocate_move_kernel<<<div_up(moves, 256), 256, 0, s>>>(params, m, v, num_planes(deg), rand, w.dead_list,
-                                                          w.idx_out, moves, shrink);
+                                                          w.idx_in, moves, shrink);
   return hipGetLastError();
 }
 

@@ -12,24 +12,6 @@
 
 namespace {
 
-// Gradient-sum mode of the backward blend (gs_set_grad_sums), for the whole process.
-std::atomic<int> g_fixed_sums{0};
-
-// SH degree ramp (gs_set_active_sh_degree), for the whole process: -1 = every stored band.
-std::atomic<int> g_active_deg{-1};
-
-// Mip-Splatting opacity compensation (gs_set_mip_compensation), for the whole process.
-std::atomic<int> g_mip{0};
-
-// How the kernels shade a scene of a stored degree: the active higher bands,
-// (d + 1)^2 - 1 with d the smaller of the stored and the active degree, and the
-// compensation switch.
-gsk::Shade shade_of(int deg) {
-  const int a = g_active_deg.load();
-  const int d = (a < 0 || a > deg) ? deg : a;
-  return gsk::Shade{(d + 1) * (d + 1) - 1, g_mip.load()};
-}
-
 thread_local char g_err[512] = "";
 
 int32_t fail(int32_t code, const char* fmt, ...) {
@@ -45,6 +27,53 @@ int32_t hip_fail(hipError_t e, const char* where) {
 }
 
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+constexpr int32_t kDefaultSplitFirst = 2048;
+constexpr int32_t kDefaultSplitChunk = 512;
+
+bool split_ok(int32_t v) { return v == 0 || (v >= 4 && v <= (1 << 24) && (v & 3) == 0); }
+
+// The call's settings with the defaults filled in (NULL: every default), or an error.
+int32_t resolve_config(const gs_config* in, gs_config* out) {
+  gs_config c = GS_CONFIG_DEFAULT;
+  if (in) c = *in;
+  if (c.grad_sums != GS_GRAD_SUMS_FLOAT && c.grad_sums != GS_GRAD_SUMS_FIXED)
+    return fail(GS_ERR_INVALID_ARG, "cfg.grad_sums must be GS_GRAD_SUMS_FLOAT or GS_GRAD_SUMS_FIXED");
+  if (c.active_sh_degree < -1 || c.active_sh_degree > 3)
+    return fail(GS_ERR_INVALID_ARG, "cfg.active_sh_degree must be -1..3");
+  if (c.mip_compensation != 0 && c.mip_compensation != 1)
+    return fail(GS_ERR_INVALID_ARG, "cfg.mip_compensation must be 0 or 1");
+  if (!split_ok(c.split_first) || !split_ok(c.split_chunk))
+    return fail(GS_ERR_INVALID_ARG, "cfg.split_first and cfg.split_chunk must be 0 or multiples of 4 in [4, 2^24]");
+  if (c.split_first == 0) c.split_first = kDefaultSplitFirst;
+  if (c.split_chunk == 0) c.split_chunk = kDefaultSplitChunk;
+  *out = c;
+  return GS_OK;
+}
+
+// How the kernels shade a scene of a stored degree: the active higher bands,
+// (d + 1)^2 - 1 with d the smaller of the stored and the active degree, and the
+// compensation switch.
+gsk::Shade shade_of(int deg, const gs_config& c) {
+  const int a = c.active_sh_degree;
+  const int d = (a < 0 || a > deg) ? deg : a;
+  return gsk::Shade{(d + 1) * (d + 1) - 1, c.mip_compensation};
+}
+
+// The backward blend with the call's settings.
+hipError_t launch_bwd_blend(const gs_proj& proj, int n, const uint32_t* vals, const uint32_t* ranges,
+                            const gs_camera& cam, uint32_t pairs, const float* T_final, const uint32_t* n_contrib,
+                            const float* dL_dimg, float* gscreen, void* ws, size_t ws_bytes, const gs_config& c,
+                            hipStream_t s) {
+  return gsk::launch_render_bwd(proj, n, vals, ranges, cam, pairs, T_final, n_contrib, dL_dimg, gscreen, ws,
+                                ws_bytes, c.split_first, c.split_chunk, c.grad_sums == GS_GRAD_SUMS_FIXED, s);
+}
+
+// Render workspace bytes for the resolved settings.
+size_t render_ws(int64_t n, uint32_t pairs, int W, int H, const gs_config& c) {
+  return gsk::render_ws_bytes(W, H, pairs, c.split_first, c.split_chunk,
+                              c.grad_sums == GS_GRAD_SUMS_FIXED ? (n > 0 ? n : 0) : 0);
+}
 
 int32_t check_camera(const gs_camera* cam) {
   if (!cam) return fail(GS_ERR_INVALID_ARG, "camera is null");
@@ -135,48 +164,10 @@ extern "C" {
 
 const char* gs_last_error(void) { return g_err; }
 
-int32_t gs_set_grad_sums(int32_t mode) {
-  g_err[0] = 0;
-  if (mode != GS_GRAD_SUMS_FLOAT && mode != GS_GRAD_SUMS_FIXED)
-    return fail(GS_ERR_INVALID_ARG, "unknown gradient-sum mode %d", mode);
-  g_fixed_sums = mode == GS_GRAD_SUMS_FIXED ? 1 : 0;
-  return GS_OK;
-}
-
-int32_t gs_get_grad_sums(void) { return g_fixed_sums ? GS_GRAD_SUMS_FIXED : GS_GRAD_SUMS_FLOAT; }
-
-int32_t gs_set_active_sh_degree(int32_t degree) {
-  g_err[0] = 0;
-  if (degree < -1 || degree > 3) return fail(GS_ERR_INVALID_ARG, "active SH degree must be -1..3");
-  g_active_deg = degree;
-  return GS_OK;
-}
-
-int32_t gs_get_active_sh_degree(void) { return g_active_deg.load(); }
-
-int32_t gs_set_mip_compensation(int32_t on) {
-  g_err[0] = 0;
-  if (on != 0 && on != 1) return fail(GS_ERR_INVALID_ARG, "Mip compensation switch must be 0 or 1");
-  g_mip = on;
-  return GS_OK;
-}
-
-int32_t gs_get_mip_compensation(void) { return g_mip.load(); }
-
-int32_t gs_set_tuning(int32_t key, int64_t value) {
-  g_err[0] = 0;
-  if (value < 4 || value > (int64_t(1) << 24) || (value & 3))
-    return fail(GS_ERR_INVALID_ARG, "tuning value must be a multiple of 4 in [4, 2^24]");
-  switch (key) {
-    case GS_TUNE_SPLIT_FIRST: gsk::set_render_split(int(value), gsk::render_split_chunk()); return GS_OK;
-    case GS_TUNE_SPLIT_CHUNK: gsk::set_render_split(gsk::render_split_first(), int(value)); return GS_OK;
-    default: return fail(GS_ERR_INVALID_ARG, "unknown tuning key %d", key);
-  }
-}
-
 int32_t gs_profile_enable(int32_t on, const char* only) {
   g_err[0] = 0;
-  gsk::profile_enable(on != 0, only);
+  const hipError_t e = gsk::profile_enable(on != 0, only);
+  if (e != hipSuccess) return hip_fail(e, "gs_profile_enable");
   return GS_OK;
 }
 
@@ -190,20 +181,14 @@ int32_t gs_profile_query(int32_t max_names, char* names, int64_t* launches, doub
   return written;
 }
 
-int64_t gs_get_tuning(int32_t key) {
-  switch (key) {
-    case GS_TUNE_SPLIT_FIRST: return gsk::render_split_first();
-    case GS_TUNE_SPLIT_CHUNK: return gsk::render_split_chunk();
-    default: return -1;
-  }
-}
-
-size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H) {
+size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H, const gs_config* cfg) {
+  gs_config c;
+  if (resolve_config(cfg, &c) != GS_OK) return 0;
   switch (which_call) {
     case GS_WS_PREPROCESS: return pre_ws_bytes(n < 0 ? 0 : n);
     case GS_WS_BIN_SORT: return gsk::bin_sort_ws_bytes(pairs);
     case GS_WS_LOSS: return (W > 0 && H > 0) ? gsk::loss_ws_bytes(H, W) : 0;
-    case GS_WS_RENDER: return (W > 0 && H > 0) ? gsk::render_ws_bytes(W, H, pairs) : 0;
+    case GS_WS_RENDER: return (W > 0 && H > 0) ? render_ws(n, pairs, W, H, c) : 0;
     case GS_WS_DENSIFY: return gsk::densify_ws_bytes(n < 0 ? 0 : n);
     case GS_WS_LOSS_CHARBONNIER: return (W > 0 && H > 0) ? gsk::charbonnier_ws_bytes(H, W) : 0;
     case GS_WS_CAMERA_GRAD: return gsk::camera_grad_ws_bytes(n < 0 ? 0 : n);
@@ -213,20 +198,22 @@ size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t
 }
 
 int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out, uint32_t* total_pairs, void* ws,
-                      size_t ws_bytes, void* stream) {
+                      size_t ws_bytes, const gs_config* cfg, void* stream) {
   g_err[0] = 0;
   int32_t st;
+  gs_config c;
+  if ((st = resolve_config(cfg, &c)) != GS_OK) return st;
   if ((st = check_scene(scene)) != GS_OK) return st;
   if ((st = check_camera(cam)) != GS_OK) return st;
   if ((st = check_proj(out, scene->n, true)) != GS_OK) return st;
   if (!total_pairs) return fail(GS_ERR_INVALID_ARG, "total_pairs is null");
-  const size_t need = gs_workspace_bytes(GS_WS_PREPROCESS, scene->n, 0, 0, 0);
+  const size_t need = pre_ws_bytes(scene->n);
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "preprocess workspace needs %zu bytes", need);
   hipStream_t s = as_stream(stream);
   const int n = int(scene->n);
   PreWs w = carve_pre(ws, n);
   hipError_t e = gsk::launch_preprocess_fwd(scene->params, n, scene->sh_degree, *cam, *out, w.block_tiles,
-                                            w.total64, shade_of(scene->sh_degree), s);
+                                            w.total64, shade_of(scene->sh_degree, c), s);
   if (e != hipSuccess) return hip_fail(e, "preprocess_fwd");
   return finish_preprocess(out, n, w, total_pairs, s);
 }
@@ -275,7 +262,7 @@ int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32
   if (total_pairs > 0 && n == 0) return fail(GS_ERR_INVALID_ARG, "pairs without Gaussians");
   if (capacity < total_pairs)
     return fail(GS_ERR_CAPACITY, "key capacity %u < %u pairs", capacity, total_pairs);
-  const size_t need = gs_workspace_bytes(GS_WS_BIN_SORT, n, total_pairs, cam->width, cam->height);
+  const size_t need = gsk::bin_sort_ws_bytes(total_pairs);
   if (total_pairs > 0 && (!ws || ws_bytes < need))
     return fail(GS_ERR_CAPACITY, "bin_sort workspace needs %zu bytes", need);
   hipError_t e = gsk::launch_bin_sort(*proj, int(n), *cam, total_pairs, keys, vals, ranges, ws, as_stream(stream));
@@ -285,18 +272,20 @@ int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32
 
 int32_t gs_render_fwd(const gs_proj* proj, int64_t n, const uint32_t* vals, const uint32_t* ranges,
                       uint32_t total_pairs, const gs_camera* cam, float* rgb, float* T_final,
-                      uint32_t* n_contrib, void* ws, size_t ws_bytes, void* stream) {
+                      uint32_t* n_contrib, void* ws, size_t ws_bytes, const gs_config* cfg, void* stream) {
   g_err[0] = 0;
   int32_t st;
+  gs_config c;
+  if ((st = resolve_config(cfg, &c)) != GS_OK) return st;
   if (n < 0 || n >= (int64_t(1) << 31)) return fail(GS_ERR_INVALID_ARG, "n out of range");
   if ((st = check_camera(cam)) != GS_OK) return st;
   if ((st = check_proj(proj, n, false)) != GS_OK) return st;
   if (!ranges || !rgb || !T_final || !n_contrib) return fail(GS_ERR_INVALID_ARG, "an output or ranges is null");
   if (total_pairs > 0 && !vals) return fail(GS_ERR_INVALID_ARG, "vals is null");
-  const size_t need = gs_workspace_bytes(GS_WS_RENDER, n, total_pairs, cam->width, cam->height);
+  const size_t need = gsk::render_ws_bytes(cam->width, cam->height, total_pairs, c.split_first, c.split_chunk, 0);
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "render workspace needs %zu bytes", need);
   hipError_t e = gsk::launch_render_fwd(*proj, vals, ranges, *cam, total_pairs, rgb, T_final, n_contrib, ws,
-                                        as_stream(stream));
+                                        c.split_first, c.split_chunk, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "render_fwd");
   return GS_OK;
 }
@@ -308,7 +297,7 @@ int32_t gs_loss_l1_dssim(const float* img, const float* target, int32_t H, int32
   if (H <= 0 || W <= 0) return fail(GS_ERR_INVALID_ARG, "image size must be positive");
   if (int64_t(3) * H * W >= (int64_t(1) << 31)) return fail(GS_ERR_UNSUPPORTED, "image too large");
   if (!(lambda_dssim >= 0.0f && lambda_dssim <= 1.0f)) return fail(GS_ERR_INVALID_ARG, "lambda must be in [0, 1]");
-  const size_t need = gs_workspace_bytes(GS_WS_LOSS, 0, 0, W, H);
+  const size_t need = gsk::loss_ws_bytes(H, W);
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "loss workspace needs %zu bytes", need);
   hipError_t e = gsk::launch_loss(img, target, H, W, lambda_dssim, loss_out, dL_dimg, ws, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "loss");
@@ -319,23 +308,25 @@ static int32_t render_bwd_common(const gs_scene* scene, const gs_proj* proj, con
                                  const uint32_t* ranges, uint32_t total_pairs, const gs_camera* cam,
                                  const float* T_final, const uint32_t* n_contrib, const float* dL_dimg,
                                  float* gscreen, float* gparams, float weight, int accumulate, void* ws,
-                                 size_t ws_bytes, void* stream) {
+                                 size_t ws_bytes, const gs_config* cfg, void* stream) {
   int32_t st;
+  gs_config c;
+  if ((st = resolve_config(cfg, &c)) != GS_OK) return st;
   if ((st = check_scene(scene)) != GS_OK) return st;
   if ((st = check_camera(cam)) != GS_OK) return st;
   if ((st = check_proj(proj, scene->n, false)) != GS_OK) return st;
   if (!ranges || !T_final || !n_contrib || !dL_dimg) return fail(GS_ERR_INVALID_ARG, "a render input is null");
   if (scene->n > 0 && (!gscreen || !gparams)) return fail(GS_ERR_INVALID_ARG, "gscreen or gparams is null");
   if (total_pairs > 0 && !vals) return fail(GS_ERR_INVALID_ARG, "vals is null");
-  const size_t need = gs_workspace_bytes(GS_WS_RENDER, scene->n, total_pairs, cam->width, cam->height);
+  const size_t need = render_ws(scene->n, total_pairs, cam->width, cam->height, c);
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "render workspace needs %zu bytes", need);
   hipStream_t s = as_stream(stream);
   const int n = int(scene->n);
-  hipError_t e = gsk::launch_render_bwd(*proj, n, vals, ranges, *cam, total_pairs, T_final, n_contrib, dL_dimg,
-                                        gscreen, ws, g_fixed_sums != 0, s);
+  hipError_t e = launch_bwd_blend(*proj, n, vals, ranges, *cam, total_pairs, T_final, n_contrib, dL_dimg, gscreen,
+                                  ws, ws_bytes, c, s);
   if (e != hipSuccess) return hip_fail(e, "render_bwd");
   e = gsk::launch_preprocess_bwd(scene->params, n, scene->sh_degree, *cam, proj->tiles, gscreen, gparams,
-                                 shade_of(scene->sh_degree), s, weight, accumulate);
+                                 shade_of(scene->sh_degree, c), s, weight, accumulate);
   if (e != hipSuccess) return hip_fail(e, "preprocess_bwd");
   return GS_OK;
 }
@@ -343,39 +334,42 @@ static int32_t render_bwd_common(const gs_scene* scene, const gs_proj* proj, con
 int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t* vals, const uint32_t* ranges,
                       uint32_t total_pairs, const gs_camera* cam, const float* T_final,
                       const uint32_t* n_contrib, const float* dL_dimg, float* gscreen, float* gparams, void* ws,
-                      size_t ws_bytes, void* stream) {
+                      size_t ws_bytes, const gs_config* cfg, void* stream) {
   g_err[0] = 0;
   return render_bwd_common(scene, proj, vals, ranges, total_pairs, cam, T_final, n_contrib, dL_dimg, gscreen, gparams,
-                           1.0f, 0, ws, ws_bytes, stream);
+                           1.0f, 0, ws, ws_bytes, cfg, stream);
 }
 
 int32_t gs_render_bwd_weighted(const gs_scene* scene, const gs_proj* proj, const uint32_t* vals,
                                const uint32_t* ranges, uint32_t total_pairs, const gs_camera* cam,
                                const float* T_final, const uint32_t* n_contrib, const float* dL_dimg,
                                float* gscreen, float* gparams, float weight, int32_t accumulate, void* ws,
-                               size_t ws_bytes, void* stream) {
+                               size_t ws_bytes, const gs_config* cfg, void* stream) {
   g_err[0] = 0;
   if (!std::isfinite(weight)) return fail(GS_ERR_INVALID_ARG, "weight must be finite");
   if (accumulate != 0 && accumulate != 1) return fail(GS_ERR_INVALID_ARG, "accumulate must be 0 or 1");
   return render_bwd_common(scene, proj, vals, ranges, total_pairs, cam, T_final, n_contrib, dL_dimg, gscreen, gparams,
-                           weight, accumulate, ws, ws_bytes, stream);
+                           weight, accumulate, ws, ws_bytes, cfg, stream);
 }
 
 int32_t gs_camera_grad(const gs_scene* scene, const gs_proj* proj, const gs_camera* cam, const float* gscreen,
-                       int32_t position_only, double* grad_out, void* ws, size_t ws_bytes, void* stream) {
+                       int32_t position_only, double* grad_out, void* ws, size_t ws_bytes, const gs_config* cfg,
+                       void* stream) {
   g_err[0] = 0;
   int32_t st;
+  gs_config c;
+  if ((st = resolve_config(cfg, &c)) != GS_OK) return st;
   if ((st = check_scene(scene)) != GS_OK) return st;
   if ((st = check_camera(cam)) != GS_OK) return st;
   if ((st = check_proj(proj, scene->n, false)) != GS_OK) return st;
   if (!grad_out) return fail(GS_ERR_INVALID_ARG, "grad_out is null");
   if (position_only != 0 && position_only != 1) return fail(GS_ERR_INVALID_ARG, "position_only must be 0 or 1");
   if (scene->n > 0 && !gscreen) return fail(GS_ERR_INVALID_ARG, "gscreen is null");
-  const size_t need = gs_workspace_bytes(GS_WS_CAMERA_GRAD, scene->n, 0, 0, 0);
+  const size_t need = gsk::camera_grad_ws_bytes(scene->n);
   if (scene->n > 0 && (!ws || ws_bytes < need))
     return fail(GS_ERR_CAPACITY, "camera-gradient workspace needs %zu bytes", need);
   const hipError_t e = gsk::launch_camera_grad(scene->params, int(scene->n), scene->sh_degree, *cam, proj->tiles,
-                                               gscreen, position_only, grad_out, ws, shade_of(scene->sh_degree),
+                                               gscreen, position_only, grad_out, ws, shade_of(scene->sh_degree, c),
                                                as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "camera_grad");
   return GS_OK;
@@ -411,9 +405,11 @@ int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs
                            const uint32_t* ranges, uint32_t total_pairs, const gs_camera* cam,
                            const float* T_final, const uint32_t* n_contrib, const float* dL_dimg, float* gscreen,
                            float* m, float* v, const float* lr, double beta1, double beta2, double eps,
-                           int32_t step, void* ws, size_t ws_bytes, void* stream) {
+                           int32_t step, void* ws, size_t ws_bytes, const gs_config* cfg, void* stream) {
   g_err[0] = 0;
   int32_t st;
+  gs_config c;
+  if ((st = resolve_config(cfg, &c)) != GS_OK) return st;
   const gs_scene scene{n, sh_degree, params};
   if ((st = check_scene(&scene)) != GS_OK) return st;
   if ((st = check_adam(n, sh_degree, lr, beta1, beta2, eps, step)) != GS_OK) return st;
@@ -422,14 +418,14 @@ int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs
   if (!ranges || !T_final || !n_contrib || !dL_dimg) return fail(GS_ERR_INVALID_ARG, "a render input is null");
   if (n > 0 && (!gscreen || !m || !v)) return fail(GS_ERR_INVALID_ARG, "gscreen, m or v is null");
   if (total_pairs > 0 && !vals) return fail(GS_ERR_INVALID_ARG, "vals is null");
-  const size_t need = gs_workspace_bytes(GS_WS_RENDER, n, total_pairs, cam->width, cam->height);
+  const size_t need = render_ws(n, total_pairs, cam->width, cam->height, c);
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "render workspace needs %zu bytes", need);
   hipStream_t s = as_stream(stream);
-  hipError_t e = gsk::launch_render_bwd(*proj, int(n), vals, ranges, *cam, total_pairs, T_final, n_contrib,
-                                        dL_dimg, gscreen, ws, g_fixed_sums != 0, s);
+  hipError_t e = launch_bwd_blend(*proj, int(n), vals, ranges, *cam, total_pairs, T_final, n_contrib, dL_dimg,
+                                  gscreen, ws, ws_bytes, c, s);
   if (e != hipSuccess) return hip_fail(e, "render_bwd");
   e = gsk::launch_chain_adam(params, int(n), sh_degree, *cam, proj->tiles, gscreen, m, v,
-                             adam_args(lr, beta1, beta2, eps, step), shade_of(sh_degree), s);
+                             adam_args(lr, beta1, beta2, eps, step), shade_of(sh_degree, c), s);
   if (e != hipSuccess) return hip_fail(e, "chain_adam");
   return GS_OK;
 }
@@ -440,9 +436,12 @@ int32_t gs_render_bwd_adam_project(float* params, int64_t n, int32_t sh_degree, 
                                    const float* dL_dimg, float* gscreen, float* m, float* v, const float* lr,
                                    double beta1, double beta2, double eps, int32_t step, void* ws, size_t ws_bytes,
                                    const gs_camera* next_cam, gs_proj* next_out, uint32_t* next_total_pairs,
-                                   void* pre_ws, size_t pre_ws_bytes_, float* densify_stats, void* stream) {
+                                   void* pre_ws, size_t pre_ws_bytes_, float* densify_stats, const gs_config* cfg,
+                                   void* stream) {
   g_err[0] = 0;
   int32_t st;
+  gs_config c;
+  if ((st = resolve_config(cfg, &c)) != GS_OK) return st;
   const gs_scene scene{n, sh_degree, params};
   if ((st = check_scene(&scene)) != GS_OK) return st;
   if ((st = check_adam(n, sh_degree, lr, beta1, beta2, eps, step)) != GS_OK) return st;
@@ -454,14 +453,14 @@ int32_t gs_render_bwd_adam_project(float* params, int64_t n, int32_t sh_degree, 
   if (!ranges || !T_final || !n_contrib || !dL_dimg) return fail(GS_ERR_INVALID_ARG, "a render input is null");
   if (n > 0 && (!gscreen || !m || !v)) return fail(GS_ERR_INVALID_ARG, "gscreen, m or v is null");
   if (total_pairs > 0 && !vals) return fail(GS_ERR_INVALID_ARG, "vals is null");
-  const size_t need = gs_workspace_bytes(GS_WS_RENDER, n, total_pairs, cam->width, cam->height);
+  const size_t need = render_ws(n, total_pairs, cam->width, cam->height, c);
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "render workspace needs %zu bytes", need);
-  const size_t need_pre = gs_workspace_bytes(GS_WS_PREPROCESS, n, 0, 0, 0);
+  const size_t need_pre = pre_ws_bytes(n);
   if (!pre_ws || pre_ws_bytes_ < need_pre)
     return fail(GS_ERR_CAPACITY, "preprocess workspace needs %zu bytes", need_pre);
   hipStream_t s = as_stream(stream);
-  hipError_t e = gsk::launch_render_bwd(*proj, int(n), vals, ranges, *cam, total_pairs, T_final, n_contrib,
-                                        dL_dimg, gscreen, ws, g_fixed_sums != 0, s);
+  hipError_t e = launch_bwd_blend(*proj, int(n), vals, ranges, *cam, total_pairs, T_final, n_contrib, dL_dimg,
+                                  gscreen, ws, ws_bytes, c, s);
   if (e != hipSuccess) return hip_fail(e, "render_bwd");
   PreWs w = carve_pre(pre_ws, n);
   gsk::NextProj np;
@@ -476,7 +475,7 @@ int32_t gs_render_bwd_adam_project(float* params, int64_t n, int32_t sh_degree, 
   np.total = w.total64;
   e = gsk::launch_chain_adam_project(params, int(n), sh_degree, *cam, proj->tiles, gscreen, m, v,
                                      adam_args(lr, beta1, beta2, eps, step), np, densify_stats,
-                                     shade_of(sh_degree), s);
+                                     shade_of(sh_degree, c), s);
   if (e != hipSuccess) return hip_fail(e, "chain_adam_project");
   return finish_preprocess(next_out, int(n), w, next_total_pairs, s);
 }
@@ -571,7 +570,7 @@ int32_t gs_densify(const float* params, const float* m, const float* v, const fl
       for (const void* x : ins)
         if (o == x) return fail(GS_ERR_INVALID_ARG, "an output is one of the inputs");
   }
-  const size_t need = gs_workspace_bytes(GS_WS_DENSIFY, n, 0, 0, 0);
+  const size_t need = gsk::densify_ws_bytes(n);
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "densify workspace needs %zu bytes", need);
   gsk::DensifyArgs a;
   a.grad_thr = float(grad_threshold);
@@ -622,7 +621,7 @@ int32_t gs_relocate(float* params, float* m, float* v, int64_t n, int32_t sh_deg
   if (n > 0 && (!params || !m || !v || !rand)) return fail(GS_ERR_INVALID_ARG, "an array is null");
   if (n > 0 && gsk::param_floats(n, gsk::num_planes(sh_degree)) >= (size_t(1) << 31))
     return fail(GS_ERR_UNSUPPORTED, "gs_param_floats(n, sh_degree) must stay below 2^31");
-  const size_t need = gs_workspace_bytes(GS_WS_RELOCATE, n, 0, 0, 0);
+  const size_t need = gsk::relocate_ws_bytes(n);
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "relocation workspace needs %zu bytes", need);
   int64_t moves = 0;
   if (n > 0) {
@@ -656,7 +655,7 @@ int32_t gs_loss_charbonnier(const float* img, const float* target, int32_t H, in
   if (H <= 0 || W <= 0 || int64_t(H) * W > (int64_t(1) << 29)) return fail(GS_ERR_INVALID_ARG, "bad image size");
   if (!img || !target || !exposure || !loss_out || !dL_dimg) return fail(GS_ERR_INVALID_ARG, "an argument is null");
   if (!(delta > 0.0f) || !std::isfinite(delta)) return fail(GS_ERR_INVALID_ARG, "delta must be positive");
-  const size_t need = gs_workspace_bytes(GS_WS_LOSS_CHARBONNIER, 0, 0, W, H);
+  const size_t need = gsk::charbonnier_ws_bytes(H, W);
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "Charbonnier workspace needs %zu bytes", need);
   const hipError_t e = gsk::launch_charbonnier(img, target, H, W, delta, exposure, loss_out, dL_dimg, dL_dexposure,
                                                ws, as_stream(stream));

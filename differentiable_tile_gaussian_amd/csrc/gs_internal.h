@@ -88,6 +88,12 @@ hipError_t launch_scan_u32(const uint32_t* in, uint32_t* out, int64_t n, uint64_
 size_t depth_order_ws_bytes(int64_t n);
 hipError_t launch_depth_order(const gs_proj& proj, int n, void* ws, hipStream_t s);
 size_t bin_sort_ws_bytes(uint32_t pairs);
+// Stable ascending sort of count (key, value) pairs by the 32-bit key, in place (the
+// hand-written radix passes of the binning); ws: sort_pairs_ws_bytes(capacity) bytes,
+// capacity >= count.
+size_t sort_pairs_ws_bytes(int64_t capacity);
+hipError_t launch_sort_pairs_u32(uint32_t* keys, uint32_t* vals, uint32_t count, int64_t capacity, void* ws,
+                                 hipStream_t s);
 hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uint32_t pairs, uint32_t* keys,
                            uint32_t* vals, uint32_t* ranges, void* ws, hipStream_t s);
 
@@ -108,15 +114,15 @@ struct DensifyWs {
 size_t densify_ws_bytes(int64_t n);
 DensifyWs carve_densify(void* ws, int64_t n);
 // Relocation of the dead to the largest donors: flags, prefix sums and their totals (dead,
-// donors), the donors' size keys, the dead list, the donors' keys and indices before and
-// after the ranking sort, and that sort's temporary space (bytes: the whole workspace).
+// donors), the donors' rank keys, the dead list, the donors' keys and indices (ranked in
+// place) and the ranking sort's space (bytes: the whole workspace).
 struct RelocateWs {
   uint32_t *fdead, *fdonor, *odead, *odonor;
   uint64_t* totals;
   void* scan_ws[2];
-  uint32_t *key, *dead_list, *key_in, *idx_in, *key_out, *idx_out;
-  void* sort_temp;
-  size_t sort_bytes, bytes;
+  uint32_t *key, *dead_list, *key_in, *idx_in;
+  void* sort_ws;
+  size_t bytes;
 };
 size_t relocate_ws_bytes(int64_t n);
 RelocateWs carve_relocate(void* ws, int64_t n);
@@ -135,19 +141,19 @@ hipError_t launch_densify_write(const float* params, const float* m, const float
                                 float* v_out, float* stats_out, hipStream_t s);
 
 // ---- render.hip
-int32_t set_render_split(int first, int chunk);
-int render_split_first();
-int render_split_chunk();
-size_t render_ws_bytes(int W, int H, uint32_t pairs);
+// Render workspace: a header the forward writes (its split sizes), the split state, and
+// for fixed-point gradient sums 72 bytes per Gaussian (n_fixed Gaussians, else 0).
+size_t render_ws_bytes(int W, int H, uint32_t pairs, int first, int chunk, int64_t n_fixed);
 hipError_t launch_render_fwd(const gs_proj& proj, const uint32_t* vals, const uint32_t* ranges,
                              const gs_camera& cam, uint32_t pairs, float* rgb, float* T_final,
-                             uint32_t* n_contrib, void* ws, hipStream_t s);
+                             uint32_t* n_contrib, void* ws, int first, int chunk, hipStream_t s);
 // fixed: gradient sums in fixed point (reproducible bit for bit); gscreen holds the float
-// partials on return either way.
+// partials on return either way.  first, chunk size the launch (and the fixed-point
+// accumulators' place); the walk takes the forward's split sizes from the header.
 hipError_t launch_render_bwd(const gs_proj& proj, int n, const uint32_t* vals, const uint32_t* ranges,
                              const gs_camera& cam, uint32_t pairs, const float* T_final,
                              const uint32_t* n_contrib, const float* dL_dimg, float* gscreen, void* ws,
-                             bool fixed, hipStream_t s);
+                             size_t ws_bytes, int first, int chunk, bool fixed, hipStream_t s);
 
 // ---- loss.hip
 size_t loss_ws_bytes(int H, int W);

@@ -15,7 +15,7 @@ bool profile_wants(const char* name);
 void profile_record(const char* name, hipEvent_t start, hipEvent_t stop);
 hipEvent_t profile_event();
 // Drops the held records (after waiting for them) and switches recording on or off.
-void profile_enable(bool on, const char* only);
+hipError_t profile_enable(bool on, const char* only);
 // Per kernel name in first-seen order: name (64-byte slots), launches, summed ms.
 hipError_t profile_query(int32_t max_names, char* names, int64_t* launches, double* total_ms, int32_t* written);
 

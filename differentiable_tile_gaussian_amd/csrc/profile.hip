@@ -47,16 +47,19 @@ void profile_record(const char* name, hipEvent_t a, hipEvent_t b) {
   g_recs.push_back(Rec{name, a, b});
 }
 
-void profile_enable(bool on, const char* only) {
+hipError_t profile_enable(bool on, const char* only) {
   std::lock_guard<std::mutex> lk(g_mu);
+  hipError_t first = hipSuccess;
   for (auto& r : g_recs) {
-    hipEventSynchronize(r.b);
+    const hipError_t e = hipEventSynchronize(r.b);
+    if (first == hipSuccess) first = e;
     g_pool.push_back(r.a);
     g_pool.push_back(r.b);
   }
   g_recs.clear();
   g_only = only ? only : "";
   g_on = on;
+  return first;
 }
 
 hipError_t profile_query(int32_t max_names, char* names, int64_t* launches, double* total_ms, int32_t* written) {

@@ -107,21 +107,22 @@ struct SplitWs {
   float4* bnd1;           // [S][256] T and S at the end of the first segment
 };
 
-inline size_t a256(size_t b) { return (b + 255) & ~size_t(255); }
+__host__ __device__ inline size_t a256(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct SplitDims {
   size_t NT, S, I;
 };
 
-SplitDims split_dims(int W, int H, uint32_t pairs, int first, int chunk) {
+__host__ __device__ inline SplitDims split_dims(int W, int H, uint32_t pairs, int first, int chunk) {
   SplitDims d;
   d.NT = size_t((W + kTile - 1) / kTile) * ((H + kTile - 1) / kTile);
-  d.S = std::min(d.NT, size_t(pairs) / size_t(first) + 1);
+  const size_t s = size_t(pairs) / size_t(first) + 1;
+  d.S = s < d.NT ? s : d.NT;
   d.I = size_t(pairs) / size_t(chunk) + d.S + 1;
   return d;
 }
 
-SplitWs carve(void* ws, const SplitDims& d) {
+__host__ __device__ inline SplitWs carve(void* ws, const SplitDims& d) {
   char* p = static_cast<char*>(ws);
   SplitWs w;
   auto take = [&](size_t bytes) { char* q = p; p += a256(bytes); return q; };
@@ -144,10 +145,40 @@ SplitWs carve(void* ws, const SplitDims& d) {
   return w;
 }
 
-size_t carve_bytes(const SplitDims& d) {
+__host__ __device__ inline size_t carve_bytes(const SplitDims& d) {
   return a256(d.NT * 4) + a256(8) + a256(d.NT * 4) + 3 * a256(d.S * 4) + a256(d.I * 8) + a256(d.S * 256 * 16) +
          2 * a256(d.S * 256 * 4) + a256(d.I * 256 * 16) + a256(d.I * 256 * 4) + a256(d.S * 256 * 4) +
          a256(d.S * 256 * 16) + a256(d.S * 256 * 4) + a256(d.S * 256 * 16);
+}
+
+// A render workspace: this header, then the split state (carve), then, for fixed-point
+// gradient sums, the backward's 64-bit accumulators.  The forward writes the header; the
+// backward takes the split sizes and the carve from it, so that it walks the chunks the
+// forward made whatever split sizes its own caller passes.
+struct RenderHeader {
+  uint32_t magic, first, chunk, num_tiles, pairs, W, H, pad;
+  uint64_t split_bytes;
+};
+constexpr uint32_t kHeaderMagic = 0x47535731u;
+constexpr size_t kHeaderBytes = 256;
+
+// What the backward expects of the header: written by a forward of this image and pair
+// count, with split sizes in range and a split state that ends within `avail` bytes.
+struct HeaderCheck {
+  const RenderHeader* h;
+  int num_tiles, W, H;
+  uint32_t pairs;
+  uint64_t avail;
+};
+
+__device__ inline bool header_ok(const HeaderCheck& c, RenderHeader& h) {
+  h = *c.h;
+  if (h.magic != kHeaderMagic || h.num_tiles != uint32_t(c.num_tiles) || h.pairs != c.pairs ||
+      h.W != uint32_t(c.W) || h.H != uint32_t(c.H))
+    return false;
+  if (h.first < 4u || h.chunk < 4u || h.first > (1u << 24) || h.chunk > (1u << 24)) return false;
+  const uint64_t need = carve_bytes(split_dims(c.W, c.H, c.pairs, int(h.first), int(h.chunk)));
+  return h.split_bytes == need && need <= c.avail;
 }
 
 // ---------------------------------------------------------------- tile order
@@ -181,10 +212,11 @@ __global__ void __launch_bounds__(1024) tile_order_kernel(const uint32_t* __rest
 }
 
 __global__ void split_init_kernel(uint32_t* __restrict__ counters, int32_t* __restrict__ slot_of_tile,
-                                  int num_tiles) {
+                                  int num_tiles, RenderHeader* __restrict__ hdr, RenderHeader h) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < 2) counters[i] = 0u;
   if (i < num_tiles) slot_of_tile[i] = -1;
+  if (i == 0) *hdr = h;
 }
 
 // ------------------------------------------------------------ forward walk
@@ -757,12 +789,14 @@ struct PixelBwd {
 // sums are integers ([GSG] "Making the parallel sums exact"): every wave-reduced moment,
 // times `unit` (16384 times the loss's element count, so that the unit is that of the
 // summed loss) and, for the three second moments, the pair's 1 / size factor, is rounded
-// to an i32 and added with integer atomics, in LDS and then into gscreen, whose words then
-// hold i32 moment sums for the decode kernel; the order of the additions does not matter.
+// to an i32 and added with integer atomics, in LDS (i32: one tile's 256 pixels stay far
+// below 2^31 units) and then into acc64 (i64, [n][9]: a Gaussian seen by a whole image
+// can pass 2^31 units), which the decode kernel turns into gscreen; the order of the
+// additions does not matter.
 template <bool FIXED>
 __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint32_t* __restrict__ vals,
                          uint32_t start, int lo, float ox, float oy, float fx, float fy, PixelBwd& s,
-                         float* __restrict__ gscreen, float unit) {
+                         float* __restrict__ gscreen, unsigned long long* __restrict__ acc64, float unit) {
   const int tid = threadIdx.x;
   const int lane = __lane_id();
   if (tid == 0) L.top = 0u;
@@ -885,13 +919,13 @@ __device__ void bwd_walk(BwdLds& L, const float4* __restrict__ splat, const uint
       const int cnt9 = (hi - blo) * 9;
       for (int idx = tid; idx < cnt9; idx += kBlock) {
         const int e = idx / 9;
-        float* dst = &gscreen[size_t(L.id[buf][e]) * 9 + (idx - 9 * e)];
+        const size_t o = size_t(L.id[buf][e]) * 9 + (idx - 9 * e);
         if (FIXED) {
           const int x = __float_as_int(flat[idx]);
-          if (x != 0) atomicAdd(reinterpret_cast<int*>(dst), x);
+          if (x != 0) atomicAdd(&acc64[o], (unsigned long long)(long long)x);
         } else {
           const float x = flat[idx];
-          if (x != 0.0f) atomicAdd(dst, x);
+          if (x != 0.0f) atomicAdd(&gscreen[o], x);
         }
         flat[idx] = 0.0f;
       }
@@ -907,6 +941,7 @@ struct BwdArgs {
   const uint32_t* vals;
   const uint32_t* ranges;
   int num_tiles, tx, W, H;
+  uint32_t pairs;
   float bg0, bg1, bg2;
   int first, chunk;
   const float* T_final;
@@ -914,7 +949,8 @@ struct BwdArgs {
   const float* dL_dimg;
   int n;
   float* gscreen;
-  float unit;   // fixed-point sums: 16384 times the loss's element count
+  unsigned long long* acc64;   // fixed-point sums: [n][9] i64 accumulators
+  float unit;                  // fixed-point sums: 16384 times the loss's element count
 };
 
 // A tile's first segment (the whole list for tiles that were not split).
@@ -923,7 +959,7 @@ __device__ void bwd_tile(BwdLds& L, const BwdArgs& A, const SplitWs& ws, int til
   const float4* __restrict__ splat = A.splat;
   const uint32_t* __restrict__ vals = A.vals;
   const uint32_t* __restrict__ ranges = A.ranges;
-  const int tx = A.tx, W = A.W, H = A.H, first = A.first, n = A.n;
+  const int tx = A.tx, W = A.W, H = A.H, first = A.first;
   const float bg0 = A.bg0, bg1 = A.bg1, bg2 = A.bg2;
   const float* __restrict__ T_final = A.T_final;
   const uint32_t* __restrict__ n_contrib = A.n_contrib;
@@ -953,7 +989,7 @@ __device__ void bwd_tile(BwdLds& L, const BwdArgs& A, const SplitWs& ws, int til
     }
   }
   bwd_walk<FIXED>(L, splat, vals, start, 0, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f, float(py) + 0.5f,
-                  s, gscreen, A.unit);
+                  s, gscreen, A.acc64, A.unit);
 }
 
 // One chunk of a split tile.
@@ -962,7 +998,7 @@ __device__ void bwd_chunk(BwdLds& L, const BwdArgs& A, const SplitWs& ws, uint32
   const float4* __restrict__ splat = A.splat;
   const uint32_t* __restrict__ vals = A.vals;
   const uint32_t* __restrict__ ranges = A.ranges;
-  const int num_tiles = A.num_tiles, tx = A.tx, W = A.W, H = A.H, first = A.first, chunk = A.chunk, n = A.n;
+  const int num_tiles = A.num_tiles, tx = A.tx, W = A.W, H = A.H, first = A.first, chunk = A.chunk;
   const float bg0 = A.bg0, bg1 = A.bg1, bg2 = A.bg2;
   const float* __restrict__ T_final = A.T_final;
   const uint32_t* __restrict__ n_contrib = A.n_contrib;
@@ -997,97 +1033,114 @@ __device__ void bwd_chunk(BwdLds& L, const BwdArgs& A, const SplitWs& ws, uint32
     }
   }
   bwd_walk<FIXED>(L, splat, vals, start, lo, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f, float(py) + 0.5f,
-                  s, gscreen, A.unit);
+                  s, gscreen, A.acc64, A.unit);
 }
 
 // The backward of every tile's first segment and of every chunk of the split tiles,
 // in one launch: blocks [0, num_tiles) take the tiles longest first, the blocks
 // after them the chunks, which are independent of the first segments (each starts
 // from the state the forward left at its end) and so fill the CUs that the last
-// long first segments leave idle.
+// long first segments leave idle.  The split sizes and the split state's layout come
+// from the forward's header; the chunk blocks step through the forward's chunks
+// `chunk_blocks` apart, so every chunk is walked whatever the launch size.  A header
+// that no matching forward wrote makes every block return (the zeroing kernel then
+// wrote NaN partials).
 template <bool FIXED>
-__global__ void __launch_bounds__(256) render_bwd_kernel(BwdArgs A, SplitWs ws) {
+__global__ void __launch_bounds__(256) render_bwd_kernel(BwdArgs A, HeaderCheck hc, char* split_base,
+                                                         uint32_t chunk_blocks) {
   __shared__ BwdLds L;
+  RenderHeader h;
+  if (!header_ok(hc, h)) return;
+  const SplitWs ws = carve(split_base, split_dims(A.W, A.H, A.pairs, int(h.first), int(h.chunk)));
+  A.first = int(h.first);
+  A.chunk = int(h.chunk);
   const uint32_t b = blockIdx.x;
   if (b < uint32_t(A.num_tiles)) {
     bwd_tile<FIXED>(L, A, ws, int(ws.order[b]));
   } else {
-    const uint32_t item = b - uint32_t(A.num_tiles);
-    if (item >= ws.counters[1]) return;
-    bwd_chunk<FIXED>(L, A, ws, item);
+    const uint32_t items = ws.counters[1];
+    for (uint32_t item = b - uint32_t(A.num_tiles); item < items; item += chunk_blocks) {
+      __syncthreads();   // the previous chunk's walk is done with the shared state
+      bwd_chunk<FIXED>(L, A, ws, item);
+    }
   }
 }
 
-// Fixed-point sums back to the partials: gscreen[i] holds the i32 sums of the moments
+// Fixed-point sums back to the partials: acc64[i] holds the i64 sums of the moments
 // M_x, M_y, M_xx, M_xy, M_yy (the second moments divided by the size factor), of o dL/do
 // and of the colour partials, all times `unit`; with the record's own conic and opacity
 // (the values the walks used): du = -(A M_x + B M_y), dv = -(B M_x + C M_y), dA = M_xx / 2,
-// dB = M_xy, dC = M_yy / 2, d opacity = (o dL/do) / o.
+// dB = M_xy, dC = M_yy / 2, d opacity = (o dL/do) / o.  NaN everywhere if the walk did
+// not run (header check failed).
 __global__ void __launch_bounds__(256) fixed_decode_kernel(int n, const float4* __restrict__ splat,
-                                                            float* __restrict__ gscreen, float unit) {
+                                                            const unsigned long long* __restrict__ acc64,
+                                                            float* __restrict__ gscreen, float unit,
+                                                            HeaderCheck hc) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   float* g = gscreen + size_t(i) * 9;
-  int q[9];
+  RenderHeader h;
+  if (!header_ok(hc, h)) {
 #pragma unroll
-  for (int k = 0; k < 9; ++k) q[k] = __float_as_int(g[k]);
+    for (int k = 0; k < 9; ++k) g[k] = __builtin_nanf("");
+    return;
+  }
+  float q[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) q[k] = float((long long)acc64[size_t(i) * 9 + k]);
   const float4 r0 = splat[3 * i], r1 = splat[3 * i + 1];
   const float A = r0.z, B = r0.w, C = r1.x, o = r1.y;
   const float f = fixed_size_factor(A, B, C);
-  const float mx = float(q[0]) / unit, my = float(q[1]) / unit;
-  const float mxx = float(q[2]) * f / unit, mxy = float(q[3]) * f / unit, myy = float(q[4]) * f / unit;
+  const float mx = q[0] / unit, my = q[1] / unit;
+  const float mxx = q[2] * f / unit, mxy = q[3] * f / unit, myy = q[4] * f / unit;
   g[0] = -(A * mx + B * my);
   g[1] = -(B * mx + C * my);
   g[2] = 0.5f * mxx;
   g[3] = mxy;
   g[4] = 0.5f * myy;
-  g[5] = q[5] != 0 ? (float(q[5]) / unit) / o : 0.0f;
+  g[5] = q[5] != 0.0f ? (q[5] / unit) / o : 0.0f;
 #pragma unroll
-  for (int k = 6; k < 9; ++k) g[k] = float(q[k]) / unit;
+  for (int k = 6; k < 9; ++k) g[k] = q[k] / unit;
 }
 
-__global__ void zero_f32_kernel(float* __restrict__ p, int64_t count) {
-  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < count) p[i] = 0.0f;
-}
-
-// 16-byte non-temporal stores over count4 groups of four floats (a pure write stream).
+// gscreen cleared before the walk adds to it, or NaN if the walk will not run (header
+// check failed).  16-byte non-temporal stores over count4 groups of four floats (a pure
+// write stream), then the count % 4 floats left.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-__global__ void zero_f32x4_kernel(f32x4* __restrict__ p, int64_t count4) {
+__global__ void zero_f32x4_kernel(f32x4* __restrict__ p, int64_t count4, float* __restrict__ tail, int ntail,
+                                  HeaderCheck hc) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < count4) __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, p + i);
+  RenderHeader h;
+  const float v = header_ok(hc, h) ? 0.0f : __builtin_nanf("");
+  if (i < count4) __builtin_nontemporal_store(f32x4{v, v, v, v}, p + i);
+  if (i < ntail) tail[i] = v;
 }
 
-int g_first = 2048;
-int g_chunk = 512;
+__global__ void zero_u64_kernel(unsigned long long* __restrict__ p, int64_t count) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = 0ull;
+}
 
 }  // namespace
 
-int render_split_first() { return g_first; }
-int render_split_chunk() { return g_chunk; }
-
-int32_t set_render_split(int first, int chunk) {
-  if (first < 4 || chunk < 4 || (first & 3) || (chunk & 3) || first > (1 << 24) || chunk > (1 << 24)) return -1;
-  g_first = first;
-  g_chunk = chunk;
-  return 0;
-}
-
-size_t render_ws_bytes(int W, int H, uint32_t pairs) {
-  return carve_bytes(split_dims(W, H, pairs, g_first, g_chunk)) + 256;
+size_t render_ws_bytes(int W, int H, uint32_t pairs, int first, int chunk, int64_t n_fixed) {
+  return kHeaderBytes + carve_bytes(split_dims(W, H, pairs, first, chunk)) + a256(size_t(n_fixed) * 9 * 8);
 }
 
 hipError_t launch_render_fwd(const gs_proj& proj, const uint32_t* vals, const uint32_t* ranges,
                              const gs_camera& cam, uint32_t pairs, float* rgb, float* T_final,
-                             uint32_t* n_contrib, void* wsp, hipStream_t s) {
+                             uint32_t* n_contrib, void* wsp, int first, int chunk, hipStream_t s) {
   const int tx = tiles_x(cam), ty = tiles_y(cam);
   const int num_tiles = tx * ty;
-  const SplitDims d = split_dims(cam.width, cam.height, pairs, g_first, g_chunk);
-  const SplitWs ws = carve(wsp, d);
+  const SplitDims d = split_dims(cam.width, cam.height, pairs, first, chunk);
+  const SplitWs ws = carve(static_cast<char*>(wsp) + kHeaderBytes, d);
+  const RenderHeader h{kHeaderMagic, uint32_t(first), uint32_t(chunk), uint32_t(num_tiles), pairs,
+                       uint32_t(cam.width), uint32_t(cam.height), 0u, uint64_t(carve_bytes(d))};
   const float4* splat = reinterpret_cast<const float4*>(proj.splat);
   {
     GSK_PROF("split_init", s);
-    split_init_kernel<<<div_up(num_tiles, 256), 256, 0, s>>>(ws.counters, ws.slot_of_tile, num_tiles);
+    split_init_kernel<<<div_up(num_tiles, 256), 256, 0, s>>>(ws.counters, ws.slot_of_tile, num_tiles,
+                                                             static_cast<RenderHeader*>(wsp), h);
   }
   {
     GSK_PROF("tile_order", s);
@@ -1096,14 +1149,14 @@ hipError_t launch_render_fwd(const gs_proj& proj, const uint32_t* vals, const ui
   {
     GSK_PROF("render_fwd", s);
     render_fwd_kernel<<<num_tiles, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, cam.width, cam.height,
-                                                cam.bg[0], cam.bg[1], cam.bg[2], g_first, g_chunk, rgb, T_final,
+                                                cam.bg[0], cam.bg[1], cam.bg[2], first, chunk, rgb, T_final,
                                                 n_contrib);
   }
-  if (pairs > uint32_t(g_first)) {
+  if (pairs > uint32_t(first)) {
     const unsigned items = unsigned(d.I), slots = unsigned(d.S);
     {
       GSK_PROF("split_chunk", s);
-      split_chunk_kernel<<<items, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, g_first, g_chunk);
+      split_chunk_kernel<<<items, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, first, chunk);
     }
     {
       GSK_PROF("split_combine", s);
@@ -1111,7 +1164,7 @@ hipError_t launch_render_fwd(const gs_proj& proj, const uint32_t* vals, const ui
     }
     {
       GSK_PROF("split_rewalk", s);
-      split_rewalk_kernel<<<items, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, g_first, g_chunk);
+      split_rewalk_kernel<<<items, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, first, chunk);
     }
     {
       GSK_PROF("split_finalize", s);
@@ -1124,36 +1177,52 @@ hipError_t launch_render_fwd(const gs_proj& proj, const uint32_t* vals, const ui
 
 hipError_t launch_render_bwd(const gs_proj& proj, int n, const uint32_t* vals, const uint32_t* ranges,
                              const gs_camera& cam, uint32_t pairs, const float* T_final, const uint32_t* n_contrib,
-                             const float* dL_dimg, float* gscreen, void* wsp, bool fixed, hipStream_t s) {
+                             const float* dL_dimg, float* gscreen, void* wsp, size_t ws_bytes, int first, int chunk,
+                             bool fixed, hipStream_t s) {
   const int tx = tiles_x(cam), ty = tiles_y(cam);
   const int num_tiles = tx * ty;
-  const SplitDims d = split_dims(cam.width, cam.height, pairs, g_first, g_chunk);
-  const SplitWs ws = carve(wsp, d);
+  // the launch is sized with the caller's split sizes; the walk uses the forward's (header)
+  const SplitDims d = split_dims(cam.width, cam.height, pairs, first, chunk);
+  char* base = static_cast<char*>(wsp);
+  // fixed-point accumulators at the end of the workspace (the caller checked that it holds
+  // them after a split state of the caller's split sizes), so that their place does not
+  // depend on the split sizes; the header check keeps the forward's split state before them
+  const size_t acc_off = fixed ? ((ws_bytes - size_t(n) * 9 * 8) & ~size_t(255)) : ws_bytes;
+  unsigned long long* acc64 = fixed ? reinterpret_cast<unsigned long long*>(base + acc_off) : nullptr;
+  const uint64_t avail = acc_off - kHeaderBytes;
+  const HeaderCheck hc{reinterpret_cast<const RenderHeader*>(base), num_tiles, cam.width, cam.height, pairs, avail};
   const float4* splat = reinterpret_cast<const float4*>(proj.splat);
   if (n > 0) {
-    GSK_PROF("zero_f32", s);
-    const int64_t count = 9 * int64_t(n);
-    if (reinterpret_cast<uintptr_t>(gscreen) % 16 == 0) {
-      zero_f32x4_kernel<<<div_up(count / 4, 256), 256, 0, s>>>(reinterpret_cast<f32x4*>(gscreen), count / 4);
-      if (count % 4) zero_f32_kernel<<<1, 4, 0, s>>>(gscreen + (count / 4) * 4, count % 4);
+    if (fixed) {
+      GSK_PROF("zero_u64", s);
+      const int64_t count = 9 * int64_t(n);
+      zero_u64_kernel<<<div_up(count, 256), 256, 0, s>>>(acc64, count);
     } else {
-      zero_f32_kernel<<<div_up(count, 256), 256, 0, s>>>(gscreen, count);
+      GSK_PROF("zero_f32", s);
+      const int64_t count = 9 * int64_t(n);
+      const bool vec = reinterpret_cast<uintptr_t>(gscreen) % 16 == 0;
+      const int64_t count4 = vec ? count / 4 : 0;
+      const int ntail = int(count - 4 * count4);
+      const int64_t threads = count4 > ntail ? count4 : ntail;
+      zero_f32x4_kernel<<<div_up(threads, 256), 256, 0, s>>>(reinterpret_cast<f32x4*>(gscreen), count4,
+                                                             gscreen + 4 * count4, ntail, hc);
     }
   }
   const float unit = kFixedUnit * 3.0f * float(cam.width) * float(cam.height);
-  const BwdArgs A{splat, vals, ranges, num_tiles, tx, cam.width, cam.height, cam.bg[0], cam.bg[1], cam.bg[2],
-                  g_first, g_chunk, T_final, n_contrib, dL_dimg, n, gscreen, unit};
-  const unsigned blocks = unsigned(num_tiles) + (pairs > uint32_t(g_first) ? unsigned(d.I) : 0u);
+  const BwdArgs A{splat, vals, ranges, num_tiles, tx, cam.width, cam.height, pairs, cam.bg[0], cam.bg[1], cam.bg[2],
+                  0, 0, T_final, n_contrib, dL_dimg, n, gscreen, acc64, unit};
+  const uint32_t chunk_blocks = pairs > 0 ? uint32_t(d.I) : 0u;
+  const unsigned blocks = unsigned(num_tiles) + chunk_blocks;
   {
     GSK_PROF("render_bwd", s);
     if (fixed)
-      render_bwd_kernel<true><<<blocks, 256, 0, s>>>(A, ws);
+      render_bwd_kernel<true><<<blocks, 256, 0, s>>>(A, hc, base + kHeaderBytes, chunk_blocks);
     else
-      render_bwd_kernel<false><<<blocks, 256, 0, s>>>(A, ws);
+      render_bwd_kernel<false><<<blocks, 256, 0, s>>>(A, hc, base + kHeaderBytes, chunk_blocks);
   }
   if (fixed && n > 0) {
     GSK_PROF("fixed_decode", s);
-    fixed_decode_kernel<<<div_up(n, 256), 256, 0, s>>>(n, splat, gscreen, unit);
+    fixed_decode_kernel<<<div_up(n, 256), 256, 0, s>>>(n, splat, acc64, gscreen, unit, hc);
   }
   return hipGetLastError();
 }

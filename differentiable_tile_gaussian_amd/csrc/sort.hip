@@ -430,6 +430,33 @@ hipError_t launch_depth_order(const gs_proj& proj, int n, void* ws, hipStream_t 
   return launch_scan_u32(w.counts, proj.offs, n, w.r.total64, w.r.scan_ws, s);
 }
 
+size_t sort_pairs_ws_bytes(int64_t n) {
+  Carver c{nullptr};
+  c.take(size_t(n > 0 ? n : 1) * 4);
+  c.take(size_t(n > 0 ? n : 1) * 4);
+  carve_radix(c, blocks_for(n), 0);
+  return c.off;
+}
+
+hipError_t launch_sort_pairs_u32(uint32_t* keys, uint32_t* vals, uint32_t count, int64_t capacity, void* ws,
+                                 hipStream_t s) {
+  if (count <= 1) return hipSuccess;
+  Carver c{static_cast<char*>(ws)};
+  uint32_t* alt_k = c.take(size_t(capacity) * 4);
+  uint32_t* alt_v = c.take(size_t(capacity) * 4);
+  const RadixWs r = carve_radix(c, blocks_for(capacity), 0);
+  const int nb = blocks_for(count);
+  // four 8-bit passes: keys -> alt -> keys -> alt -> keys
+  for (int pass = 0; pass < 4; ++pass) {
+    const bool even = (pass & 1) == 0;
+    PassIn in{even ? keys : alt_k, even ? vals : alt_v, nullptr, nullptr, count, nullptr};
+    const hipError_t e = radix_pass<kFromKeys>(in, nb, 8 * pass, r, even ? alt_k : keys, even ? alt_v : vals, nullptr,
+                                               nullptr, nullptr, nullptr, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 size_t bin_sort_ws_bytes(uint32_t pairs) { return carve_pairs(nullptr, pairs, nullptr); }
 
 hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uint32_t pairs, uint32_t* keys,

@@ -19,15 +19,12 @@ LIB_PATH = os.path.join(_HERE, "libgs.so")
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_UNSUPPORTED, GS_ERR_HIP = 0, -1, -2, -3, -4
 GS_WS_PREPROCESS, GS_WS_BIN_SORT, GS_WS_LOSS, GS_WS_RENDER, GS_WS_DENSIFY, GS_WS_LOSS_CHARBONNIER = 0, 1, 2, 3, 4, 5
 GS_WS_CAMERA_GRAD, GS_WS_RELOCATE = 6, 7
-GS_TUNE_SPLIT_FIRST, GS_TUNE_SPLIT_CHUNK = 0, 1
 GS_GRAD_SUMS_FLOAT, GS_GRAD_SUMS_FIXED = 0, 1
 
 EXPORTED = ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
-            "gs_adam_step", "gs_render_bwd_adam", "gs_render_bwd_adam_project", "gs_render_bwd_weighted", "gs_camera_grad", "gs_densify_accumulate",
-            "gs_densify", "gs_relocate", "gs_set_grad_sums", "gs_get_grad_sums", "gs_set_active_sh_degree",
-            "gs_get_active_sh_degree", "gs_set_mip_compensation", "gs_get_mip_compensation", "gs_loss_charbonnier",
-            "gs_workspace_bytes", "gs_set_tuning", "gs_get_tuning",
-            "gs_profile_enable", "gs_profile_query", "gs_param_floats", "gs_params_to_blocked",
+            "gs_adam_step", "gs_render_bwd_adam", "gs_render_bwd_adam_project", "gs_render_bwd_weighted",
+            "gs_camera_grad", "gs_densify_accumulate", "gs_densify", "gs_relocate", "gs_loss_charbonnier",
+            "gs_workspace_bytes", "gs_profile_enable", "gs_profile_query", "gs_param_floats", "gs_params_to_blocked",
             "gs_params_from_blocked", "gs_last_error")
 
 
@@ -47,6 +44,22 @@ class GsScene(C.Structure):
     _fields_ = [("n", C.c_int64), ("sh_degree", C.c_int32), ("params", C.c_void_p)]
 
 
+class GsConfig(C.Structure):
+    """gs_config: the per-call settings (defaults: float sums, every SH band, no Mip
+    compensation, the default split sizes)."""
+    _fields_ = [("grad_sums", C.c_int32), ("active_sh_degree", C.c_int32), ("mip_compensation", C.c_int32),
+                ("split_first", C.c_int32), ("split_chunk", C.c_int32)]
+
+    def __init__(self, grad_sums=GS_GRAD_SUMS_FLOAT, active_sh_degree=-1, mip_compensation=False, split_first=0,
+                 split_chunk=0):
+        super().__init__(int(grad_sums), int(active_sh_degree), int(bool(mip_compensation)), int(split_first),
+                         int(split_chunk))
+
+
+def _cfg(cfg):
+    return None if cfg is None else C.byref(cfg)
+
+
 class GsProj(C.Structure):
     _fields_ = [("splat", C.c_void_p), ("depth", C.c_void_p), ("rect", C.c_void_p), ("tiles", C.c_void_p),
                 ("order", C.c_void_p), ("n_visible", C.c_void_p), ("offs", C.c_void_p), ("rect_order", C.c_void_p)]
@@ -57,35 +70,23 @@ def _load():
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
     lib = C.CDLL(LIB_PATH)
     P, I64, I32, U32 = C.c_void_p, C.c_int64, C.c_int32, C.c_uint32
-    lib.gs_preprocess.argtypes = [P, P, P, P, P, C.c_size_t, P]
+    lib.gs_preprocess.argtypes = [P, P, P, P, P, C.c_size_t, P, P]
     lib.gs_bin_sort.argtypes = [P, I64, P, U32, P, P, U32, P, P, C.c_size_t, P]
-    lib.gs_render_fwd.argtypes = [P, I64, P, P, U32, P, P, P, P, P, C.c_size_t, P]
+    lib.gs_render_fwd.argtypes = [P, I64, P, P, U32, P, P, P, P, P, C.c_size_t, P, P]
     lib.gs_loss_l1_dssim.argtypes = [P, P, I32, I32, C.c_float, P, P, P, C.c_size_t, P]
-    lib.gs_render_bwd.argtypes = [P, P, P, P, U32, P, P, P, P, P, P, P, C.c_size_t, P]
+    lib.gs_render_bwd.argtypes = [P, P, P, P, U32, P, P, P, P, P, P, P, C.c_size_t, P, P]
     lib.gs_render_bwd_adam.argtypes = [P, I64, I32, P, P, P, U32, P, P, P, P, P, P, P, P, C.c_double, C.c_double,
-                                       C.c_double, I32, P, C.c_size_t, P]
+                                       C.c_double, I32, P, C.c_size_t, P, P]
     lib.gs_render_bwd_adam.restype = I32
     lib.gs_render_bwd_adam_project.argtypes = [P, I64, I32, P, P, P, U32, P, P, P, P, P, P, P, P, C.c_double,
                                                C.c_double, C.c_double, I32, P, C.c_size_t, P, P, P, P, C.c_size_t,
-                                               P, P]
+                                               P, P, P]
     lib.gs_render_bwd_adam_project.restype = I32
     lib.gs_loss_charbonnier.argtypes = [P, P, I32, I32, C.c_float, P, P, P, P, P, C.c_size_t, P]
     lib.gs_loss_charbonnier.restype = I32
-    lib.gs_set_active_sh_degree.argtypes = [I32]
-    lib.gs_set_active_sh_degree.restype = I32
-    lib.gs_get_active_sh_degree.argtypes = []
-    lib.gs_get_active_sh_degree.restype = I32
-    lib.gs_set_mip_compensation.argtypes = [I32]
-    lib.gs_set_mip_compensation.restype = I32
-    lib.gs_get_mip_compensation.argtypes = []
-    lib.gs_get_mip_compensation.restype = I32
-    lib.gs_set_grad_sums.argtypes = [I32]
-    lib.gs_set_grad_sums.restype = I32
-    lib.gs_get_grad_sums.argtypes = []
-    lib.gs_get_grad_sums.restype = I32
-    lib.gs_render_bwd_weighted.argtypes = [P, P, P, P, U32, P, P, P, P, P, P, C.c_float, I32, P, C.c_size_t, P]
+    lib.gs_render_bwd_weighted.argtypes = [P, P, P, P, U32, P, P, P, P, P, P, C.c_float, I32, P, C.c_size_t, P, P]
     lib.gs_render_bwd_weighted.restype = I32
-    lib.gs_camera_grad.argtypes = [P, P, P, P, I32, P, P, C.c_size_t, P]
+    lib.gs_camera_grad.argtypes = [P, P, P, P, I32, P, P, C.c_size_t, P, P]
     lib.gs_relocate.argtypes = [P, P, P, I64, I32, P, C.c_double, C.c_double, I64, P, P, C.c_size_t, P]
     lib.gs_relocate.restype = I32
     lib.gs_camera_grad.restype = I32
@@ -94,10 +95,6 @@ def _load():
     D = C.c_double
     lib.gs_densify.argtypes = [P, P, P, P, P, I64, I32, D, D, D, D, I32, D, P, P, P, P, I64, P, P, P, C.c_size_t, P]
     lib.gs_densify.restype = I32
-    lib.gs_set_tuning.argtypes = [I32, I64]
-    lib.gs_set_tuning.restype = I32
-    lib.gs_get_tuning.argtypes = [I32]
-    lib.gs_get_tuning.restype = I64
     lib.gs_adam_step.argtypes = [P, P, P, P, I64, I32, P, C.c_double, C.c_double, C.c_double, I32, P]
     lib.gs_profile_enable.argtypes = [I32, C.c_char_p]
     lib.gs_profile_enable.restype = I32
@@ -109,7 +106,7 @@ def _load():
     lib.gs_params_to_blocked.restype = I32
     lib.gs_params_from_blocked.argtypes = [P, P, I64, I32, P]
     lib.gs_params_from_blocked.restype = I32
-    lib.gs_workspace_bytes.argtypes = [I32, I64, U32, I32, I32]
+    lib.gs_workspace_bytes.argtypes = [I32, I64, U32, I32, I32, P]
     lib.gs_workspace_bytes.restype = C.c_size_t
     lib.gs_last_error.restype = C.c_char_p
     for name in ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
@@ -170,13 +167,13 @@ class Proj:
                              self.offs.data_ptr(), self.rect_order.data_ptr())
 
 
-def workspace(which, n=0, pairs=0, W=0, H=0, device="cuda"):
-    nbytes = int(_lib.gs_workspace_bytes(which, n, pairs, W, H))
+def workspace(which, n=0, pairs=0, W=0, H=0, device="cuda", cfg=None):
+    nbytes = int(_lib.gs_workspace_bytes(which, n, pairs, W, H, _cfg(cfg)))
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def gs_workspace_bytes(which, n=0, pairs=0, W=0, H=0):
-    return int(_lib.gs_workspace_bytes(which, n, pairs, W, H))
+def gs_workspace_bytes(which, n=0, pairs=0, W=0, H=0, cfg=None):
+    return int(_lib.gs_workspace_bytes(which, n, pairs, W, H, _cfg(cfg)))
 
 
 def gs_param_floats(n, sh_degree):
@@ -218,7 +215,7 @@ def from_blocked(blocked, n, sh_degree, out=None, stream=None):
     return out
 
 
-def gs_preprocess(params, sh_degree, cam: GsCamera, proj: Proj, ws, stream=None) -> int:
+def gs_preprocess(params, sh_degree, cam: GsCamera, proj: Proj, ws, cfg=None, stream=None) -> int:
     """Projection + tile-count scan; returns the pair count (synchronises the stream once).
     params: blocked layout for proj.n Gaussians."""
     n = proj.n
@@ -226,7 +223,7 @@ def gs_preprocess(params, sh_degree, cam: GsCamera, proj: Proj, ws, stream=None)
     scene = GsScene(n, sh_degree, params.data_ptr() if n else None)
     total = C.c_uint32(0)
     _check(_lib.gs_preprocess(C.byref(scene), C.byref(cam), C.byref(proj.struct), C.byref(total), _ptr(ws),
-                              ws.numel(), _stream(stream)))
+                              ws.numel(), _cfg(cfg), _stream(stream)))
     return int(total.value)
 
 
@@ -236,9 +233,11 @@ def gs_bin_sort(proj: Proj, cam: GsCamera, total_pairs, keys, vals, ranges, ws, 
                             _ptr(ranges), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
-def gs_render_fwd(proj: Proj, vals, ranges, total_pairs, cam: GsCamera, rgb, T_final, n_contrib, ws, stream=None):
+def gs_render_fwd(proj: Proj, vals, ranges, total_pairs, cam: GsCamera, rgb, T_final, n_contrib, ws, cfg=None,
+                  stream=None):
     _check(_lib.gs_render_fwd(C.byref(proj.struct), proj.n, _ptr(vals), _ptr(ranges), total_pairs, C.byref(cam),
-                              _ptr(rgb), _ptr(T_final), _ptr(n_contrib), _ptr(ws), ws.numel(), _stream(stream)))
+                              _ptr(rgb), _ptr(T_final), _ptr(n_contrib), _ptr(ws), ws.numel(), _cfg(cfg),
+                              _stream(stream)))
 
 
 def gs_loss_l1_dssim(img, target, lambda_dssim, loss_out, dL_dimg, ws, stream=None):
@@ -248,7 +247,7 @@ def gs_loss_l1_dssim(img, target, lambda_dssim, loss_out, dL_dimg, ws, stream=No
 
 
 def gs_render_bwd(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam: GsCamera, T_final, n_contrib, dL_dimg,
-                  gscreen, gparams, ws, stream=None):
+                  gscreen, gparams, ws, cfg=None, stream=None):
     n = proj.n
     _blocked(params, n, sh_degree)
     _blocked(gparams, n, sh_degree)
@@ -256,11 +255,11 @@ def gs_render_bwd(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam:
     _check(_lib.gs_render_bwd(C.byref(scene), C.byref(proj.struct), _ptr(vals), _ptr(ranges), total_pairs,
                               C.byref(cam),
                               _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimg), _ptr(gscreen), _ptr(gparams),
-                              _ptr(ws), ws.numel(), _stream(stream)))
+                              _ptr(ws), ws.numel(), _cfg(cfg), _stream(stream)))
 
 
 def gs_render_bwd_weighted(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam: GsCamera, T_final,
-                           n_contrib, dL_dimg, gscreen, gparams, ws, weight, accumulate, stream=None):
+                           n_contrib, dL_dimg, gscreen, gparams, ws, weight, accumulate, cfg=None, stream=None):
     n = proj.n
     _blocked(params, n, sh_degree)
     _blocked(gparams, n, sh_degree)
@@ -268,7 +267,7 @@ def gs_render_bwd_weighted(params, sh_degree, proj: Proj, vals, ranges, total_pa
     _check(_lib.gs_render_bwd_weighted(C.byref(scene), C.byref(proj.struct), _ptr(vals), _ptr(ranges), total_pairs,
                                        C.byref(cam), _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimg), _ptr(gscreen),
                                        _ptr(gparams), float(weight), int(bool(accumulate)), _ptr(ws), ws.numel(),
-                                       _stream(stream)))
+                                       _cfg(cfg), _stream(stream)))
 
 
 def gs_relocate(params, m, v, n, sh_degree, rand, ws, dead_opacity=0.02, donor_opacity=0.4, max_moves=-1,
@@ -284,7 +283,7 @@ def gs_relocate(params, m, v, n, sh_degree, rand, ws, dead_opacity=0.02, donor_o
 
 
 def gs_camera_grad(params, sh_degree, proj: Proj, cam: GsCamera, gscreen, grad_out, ws, position_only=False,
-                   stream=None):
+                   cfg=None, stream=None):
     """grad_out: device float64[6] = (rotation, translation) gradient of the camera pose
     (with position_only, the trainer's position-path terms alone)."""
     n = proj.n
@@ -293,7 +292,8 @@ def gs_camera_grad(params, sh_degree, proj: Proj, cam: GsCamera, gscreen, grad_o
         raise ValueError("grad_out must hold 6 float64 values")
     scene = GsScene(n, sh_degree, params.data_ptr() if n else None)
     _check(_lib.gs_camera_grad(C.byref(scene), C.byref(proj.struct), C.byref(cam), _ptr(gscreen),
-                               int(bool(position_only)), _ptr(grad_out), _ptr(ws), ws.numel(), _stream(stream)))
+                               int(bool(position_only)), _ptr(grad_out), _ptr(ws), ws.numel(), _cfg(cfg),
+                               _stream(stream)))
 
 
 def gs_adam_step(params, grads, m, v, n, sh_degree, lr, beta1, beta2, eps, step, stream=None):
@@ -305,19 +305,20 @@ def gs_adam_step(params, grads, m, v, n, sh_degree, lr, beta1, beta2, eps, step,
 
 
 def gs_render_bwd_adam(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam: GsCamera, T_final,
-                       n_contrib, dL_dimg, gscreen, m, v, lr, beta1, beta2, eps, step, ws, stream=None):
+                       n_contrib, dL_dimg, gscreen, m, v, lr, beta1, beta2, eps, step, ws, cfg=None, stream=None):
     for t in (params, m, v):
         _blocked(t, proj.n, sh_degree)
     lr_arr = (C.c_float * 5)(*[float(x) for x in lr])
     _check(_lib.gs_render_bwd_adam(_ptr(params), proj.n, sh_degree, C.byref(proj.struct), _ptr(vals), _ptr(ranges),
                                    total_pairs, C.byref(cam), _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimg),
                                    _ptr(gscreen), _ptr(m), _ptr(v), lr_arr, float(beta1), float(beta2),
-                                   float(eps), int(step), _ptr(ws), ws.numel(), _stream(stream)))
+                                   float(eps), int(step), _ptr(ws), ws.numel(), _cfg(cfg), _stream(stream)))
 
 
 def gs_render_bwd_adam_project(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam: GsCamera, T_final,
                                n_contrib, dL_dimg, gscreen, m, v, lr, beta1, beta2, eps, step, ws,
-                               next_cam: GsCamera, next_proj: Proj, pre_ws, densify_stats=None, stream=None) -> int:
+                               next_cam: GsCamera, next_proj: Proj, pre_ws, densify_stats=None, cfg=None,
+                               stream=None) -> int:
     """gs_render_bwd_adam, then the projection of the updated scene for next_cam into
     next_proj (may be proj); returns the next pair count (synchronises once).  With
     densify_stats ([n][2]), this step's observations are added to it."""
@@ -330,7 +331,7 @@ def gs_render_bwd_adam_project(params, sh_degree, proj: Proj, vals, ranges, tota
         _ptr(params), proj.n, sh_degree, C.byref(proj.struct), _ptr(vals), _ptr(ranges), total_pairs, C.byref(cam),
         _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimg), _ptr(gscreen), _ptr(m), _ptr(v), lr_arr, float(beta1),
         float(beta2), float(eps), int(step), _ptr(ws), ws.numel(), C.byref(next_cam), C.byref(next_proj.struct),
-        C.byref(total), _ptr(pre_ws), pre_ws.numel(), _ptr(densify_stats), _stream(stream)))
+        C.byref(total), _ptr(pre_ws), pre_ws.numel(), _ptr(densify_stats), _cfg(cfg), _stream(stream)))
     return int(total.value)
 
 
@@ -359,41 +360,6 @@ def gs_loss_charbonnier(img, target, exposure, loss_out, dL_dimg, ws, delta=0.03
     _, H, W = img.shape
     _check(_lib.gs_loss_charbonnier(_ptr(img), _ptr(target), H, W, float(delta), _ptr(exposure), _ptr(loss_out),
                                     _ptr(dL_dimg), _ptr(dL_dexposure), _ptr(ws), ws.numel(), _stream(stream)))
-
-
-def gs_set_active_sh_degree(degree):
-    """SH degree ramp: bands up to `degree` are evaluated and trained (-1: every stored band)."""
-    _check(_lib.gs_set_active_sh_degree(int(degree)))
-
-
-def gs_get_active_sh_degree():
-    return int(_lib.gs_get_active_sh_degree())
-
-
-def gs_set_mip_compensation(on):
-    """Mip-Splatting opacity compensation for every later projection and chain (off by default)."""
-    _check(_lib.gs_set_mip_compensation(int(bool(on))))
-
-
-def gs_get_mip_compensation():
-    return bool(_lib.gs_get_mip_compensation())
-
-
-def gs_set_grad_sums(mode):
-    """GS_GRAD_SUMS_FLOAT (fp32 atomics) or GS_GRAD_SUMS_FIXED (integer sums, reproducible)."""
-    _check(_lib.gs_set_grad_sums(int(mode)))
-
-
-def gs_get_grad_sums():
-    return int(_lib.gs_get_grad_sums())
-
-
-def gs_set_tuning(key, value):
-    _check(_lib.gs_set_tuning(key, int(value)))
-
-
-def gs_get_tuning(key):
-    return int(_lib.gs_get_tuning(key))
 
 
 def gs_profile_enable(on, only=None):

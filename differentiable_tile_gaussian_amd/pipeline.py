@@ -12,12 +12,34 @@ from . import gs
 DEFAULT_LR = (1.6e-4, 5e-3, 1e-3, 5e-2, 2.5e-3)   # means, log-scales, quaternion, opacity, colour
 
 
+def position_lr_decay(lr_final, max_steps, lr=DEFAULT_LR):
+    """A schedule for Pipeline(lr_schedule=...): the means' rate decays from lr[0] to
+    lr_final over max_steps steps, log-linearly (then stays at lr_final); the other
+    groups keep their constant rates.  One choice of decay among many: the pages say only
+    that position has its own decaying schedule."""
+    import math
+    l0, l1 = math.log(lr[0]), math.log(lr_final)
+
+    def rates(t):
+        f = min(max((t - 1) / max(max_steps - 1, 1), 0.0), 1.0)
+        return (math.exp(l0 + f * (l1 - l0)),) + tuple(lr[1:])
+    return rates
+
+
 class Pipeline:
     def __init__(self, params: torch.Tensor, sh_degree: int, width: int, height: int, lam: float = 0.2,
-                 lr=DEFAULT_LR, betas=(0.9, 0.999), eps=1e-8):
+                 lr=DEFAULT_LR, betas=(0.9, 0.999), eps=1e-8, cfg: gs.GsConfig = None, lr_schedule=None):
         """params: [P][n] float32 device tensor (plane-major); it is copied into the
-        library's blocked layout, in which params, grads, m and v are then kept."""
+        library's blocked layout, in which params, grads, m and v are then kept.
+        cfg: the settings every call of this pipeline passes (gs_config; None: defaults).
+        lr_schedule: None for the constant rates `lr`, or a function of the Adam step
+        t >= 1 returning the five group rates (means, log-scales, quaternion, opacity,
+        colour) that step's update uses; the pages give the means their own decaying
+        rate ([DR] "From a pixel error back to a quaternion") but no formula, so the
+        schedule is the caller's (see position_lr_decay)."""
         assert params.is_cuda and params.dtype == torch.float32 and params.is_contiguous()
+        self.cfg = cfg if cfg is not None else gs.GsConfig()
+        self.lr_schedule = lr_schedule
         self.deg = sh_degree
         self.n = params.shape[1]
         self.params = gs.to_blocked(params, sh_degree)
@@ -65,29 +87,35 @@ class Pipeline:
         need = gs.gs_workspace_bytes(gs.GS_WS_BIN_SORT, self.n, pairs, self.W, self.H)
         if self.ws_sort.numel() < need:
             self.ws_sort = torch.empty(int(need * 1.25) + 4096, dtype=torch.uint8, device=self.params.device)
-        need = gs.gs_workspace_bytes(gs.GS_WS_RENDER, self.n, pairs, self.W, self.H)
+        need = gs.gs_workspace_bytes(gs.GS_WS_RENDER, self.n, pairs, self.W, self.H, self.cfg)
         if self.ws_render.numel() < need:
             self.ws_render = torch.empty(int(need * 1.25) + 4096, dtype=torch.uint8, device=self.params.device)
 
+    def rates(self, t):
+        """The five group learning rates of Adam step t (t >= 1)."""
+        lr = self.lr if self.lr_schedule is None else self.lr_schedule(t)
+        lr = tuple(float(x) for x in lr)
+        assert len(lr) == 5
+        return lr
+
     def forward(self, cam: gs.GsCamera):
         if self.projected_for is not cam:
-            self.pairs = gs.gs_preprocess(self.params, self.deg, cam, self.proj, self.ws_pre)
+            self.pairs = gs.gs_preprocess(self.params, self.deg, cam, self.proj, self.ws_pre, cfg=self.cfg)
         self.projected_for = None
         self._reserve(self.pairs)
         gs.gs_bin_sort(self.proj, cam, self.pairs, self.keys, self.vals, self.ranges, self.ws_sort)
         gs.gs_render_fwd(self.proj, self.vals, self.ranges, self.pairs, cam, self.rgb, self.T, self.nc,
-                         self.ws_render)
+                         self.ws_render, cfg=self.cfg)
         return self.rgb
 
     def backward(self, cam: gs.GsCamera, target: torch.Tensor):
         gs.gs_loss_l1_dssim(self.rgb, target, self.lam, self.loss, self.dLdI, self.ws_loss)
         gs.gs_render_bwd(self.params, self.deg, self.proj, self.vals, self.ranges, self.pairs, cam, self.T, self.nc,
-                         self.dLdI,
-                         self.gscreen, self.grads, self.ws_render)
+                         self.dLdI, self.gscreen, self.grads, self.ws_render, cfg=self.cfg)
 
     def adam(self):
         self.t += 1
-        gs.gs_adam_step(self.params, self.grads, self.m, self.v, self.n, self.deg, self.lr, self.betas[0],
+        gs.gs_adam_step(self.params, self.grads, self.m, self.v, self.n, self.deg, self.rates(self.t), self.betas[0],
                         self.betas[1], self.eps, self.t)
 
     def backward_adam(self, cam: gs.GsCamera, target: torch.Tensor, next_cam: gs.GsCamera = None):
@@ -98,13 +126,14 @@ class Pipeline:
         self.t += 1
         if next_cam is None:
             gs.gs_render_bwd_adam(self.params, self.deg, self.proj, self.vals, self.ranges, self.pairs, cam, self.T,
-                                  self.nc, self.dLdI, self.gscreen, self.m, self.v, self.lr, self.betas[0],
-                                  self.betas[1], self.eps, self.t, self.ws_render)
+                                  self.nc, self.dLdI, self.gscreen, self.m, self.v, self.rates(self.t), self.betas[0],
+                                  self.betas[1], self.eps, self.t, self.ws_render, cfg=self.cfg)
             return
         self.pairs = gs.gs_render_bwd_adam_project(self.params, self.deg, self.proj, self.vals, self.ranges,
                                                    self.pairs, cam, self.T, self.nc, self.dLdI, self.gscreen, self.m,
-                                                   self.v, self.lr, self.betas[0], self.betas[1], self.eps, self.t,
-                                                   self.ws_render, next_cam, self.proj, self.ws_pre, self.dstats)
+                                                   self.v, self.rates(self.t), self.betas[0], self.betas[1], self.eps,
+                                                   self.t, self.ws_render, next_cam, self.proj, self.ws_pre,
+                                                   self.dstats, cfg=self.cfg)
         self.projected_for = next_cam
 
     def step(self, cam: gs.GsCamera, target: torch.Tensor, adam: bool = True, fused: bool = True,
@@ -139,7 +168,8 @@ class Pipeline:
             self.forward(cam)
             gs.gs_loss_l1_dssim(self.rgb, target, self.lam, losses[k], self.dLdI, self.ws_loss)
             gs.gs_render_bwd_weighted(self.params, self.deg, self.proj, self.vals, self.ranges, self.pairs, cam, self.T,
-                                      self.nc, self.dLdI, self.gscreen, self.grads, self.ws_render, 1.0 / B, k > 0)
+                                      self.nc, self.dLdI, self.gscreen, self.grads, self.ws_render, 1.0 / B, k > 0,
+                                      cfg=self.cfg)
             if self.dstats is not None:
                 gs.gs_densify_accumulate(self.proj, self.gscreen, self.dstats)
         self.adam()

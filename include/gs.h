@@ -109,6 +109,53 @@ typedef struct gs_proj {
                            *n_visible entries are written), read by gs_bin_sort */
 } gs_proj;
 
+/* Per-call settings of the method's variants and of the blend's work split.  Every call that
+ * depends on one takes a `const gs_config*`; NULL means GS_CONFIG_DEFAULT.  The library keeps no
+ * settings between calls.
+ *   grad_sums        how the backward blend sums the per-pixel gradient contributions:
+ *     GS_GRAD_SUMS_FLOAT  fp32 atomics; the order of the additions varies from run to run.
+ *     GS_GRAD_SUMS_FIXED  [GSG] "Making the parallel sums exact: fixed-point, and the conic
+ *       trick": every wave-summed moment (position moments, the three second moments divided
+ *       by a footprint size factor 1 + trace of the screen covariance, opacity, colour), times
+ *       16384 and times the loss's element count 3 W H (so that the unit is that of the summed
+ *       loss), clamped to +-1e9 and rounded to the nearest integer, is added with integer
+ *       atomics (i32 within a tile block, i64 across blocks, so a Gaussian's total cannot wrap);
+ *       a decode pass turns the sums into the same partials as the float mode.  Results are
+ *       identical bit for bit from run to run; each addition is exact to 0.5 / (16384 * 3 W H).
+ *       The render workspace then also holds 72 bytes per Gaussian.
+ *   active_sh_degree the SH degree ramp ([GSG] "Spherical harmonics": only the first activeK =
+ *     (activeDeg + 1)^2 - 1 band weights are summed, the active degree stepping up about every
+ *     thousand steps; the inactive ones contribute nothing and receive no gradient until their
+ *     band switches on): the projection and the chain sum the colour over the bands up to
+ *     min(active_sh_degree, the scene's degree), and the other bands' gradients are zero (with
+ *     the fused Adam their parameters stay unchanged while their moments are zero).  -1: every
+ *     stored band.  Read by gs_preprocess, the backward calls and gs_camera_grad.
+ *   mip_compensation Mip-Splatting opacity compensation ([GSG] "Flattening a 3D blob into a 2D
+ *     oval": a correction so that the dilation does not make very small Gaussians brighter
+ *     overall; the trainer's code multiplies the opacity by it in the extent and in alpha).
+ *     With 1 the record's opacity is sigmoid(logit) comp, comp = sqrt(max(det V, 0) / det(V +
+ *     0.3 I)), V the undilated screen covariance (the factor that gives the dilated footprint
+ *     exactly the integral of the undilated one), so it also enters the extent, alpha and the
+ *     skip boxes; the chain adds comp's gradient to the covariance's and scales the logit's by
+ *     comp.  The blend is unchanged (it differentiates the record's opacity).  0: off.  Read by
+ *     gs_preprocess, the backward calls and gs_camera_grad.
+ *   split_first, split_chunk  the blend's work split: every tile's first split_first pairs are
+ *     walked by one block; a tile with pixels still unfinished then has its remaining pairs
+ *     walked in parallel chunks of split_chunk pairs.  0: the defaults 2048 and 512; otherwise
+ *     multiples of 4 in [4, 2^24].  The results do not depend on them beyond rounding.  Read
+ *     by gs_render_fwd, which records them in its workspace: the matching backward walks with
+ *     the forward's values whatever its own cfg says (its cfg's values only size its launch).
+ * Calls return GS_ERR_INVALID_ARG for a value outside these ranges. */
+typedef struct gs_config {
+  int32_t grad_sums;
+  int32_t active_sh_degree;
+  int32_t mip_compensation;
+  int32_t split_first;
+  int32_t split_chunk;
+} gs_config;
+enum { GS_GRAD_SUMS_FLOAT = 0, GS_GRAD_SUMS_FIXED = 1 };
+#define GS_CONFIG_DEFAULT {GS_GRAD_SUMS_FLOAT, -1, 0, 0, 0}
+
 /* Projection of every Gaussian and the tile count prefix sum.
  * [GST] parameter slide (exp log-scales, sigmoid logit, normalised quaternion);
  * [DR] "Forward" (Sigma' = J W Sigma W^T J^T) and "From a pixel error back to a quaternion"
@@ -124,13 +171,14 @@ typedef struct gs_proj {
  * binning: out->order, out->n_visible, out->offs and out->rect_order.
  * out: caller-allocated gs_proj for scene->n Gaussians.  total_pairs: HOST pointer,
  * receives the pair count (= offs[n]).  ws: device workspace of
- * gs_workspace_bytes(GS_WS_PREPROCESS, n, 0, 0, 0) bytes.  Waits for the pair count only:
+ * gs_workspace_bytes(GS_WS_PREPROCESS, n, 0, 0, 0, NULL) bytes.  Waits for the pair count only:
  * it is copied to the host before the depth ordering is enqueued, which may still be
  * running on `stream` when the call returns.  The library keeps one pinned 8-byte host
  * word and one event per device and host thread for this copy.  GS_ERR_CAPACITY if the
  * pair count exceeds 2^32 - 1. */
+/* cfg: active_sh_degree, mip_compensation. */
 int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out, uint32_t* total_pairs,
-                      void* ws, size_t ws_bytes, void* stream);
+                      void* ws, size_t ws_bytes, const gs_config* cfg, void* stream);
 
 /* Duplicate-with-keys, depth sort and tile ranges.  [GSG] "Why tiling, and the five stages"
  * (scatter, per-tile depth sort, ranges with the tie broken by id).  Every (tile, Gaussian)
@@ -145,7 +193,7 @@ int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out,
  * ranges[1][t] = one past the last pair of tile t ((0, 0) for an empty tile).  proj: as
  * gs_preprocess left it (order, n_visible, offs and rect_order are read); total_pairs must be the
  * value gs_preprocess returned for the same proj.  ws: gs_workspace_bytes(GS_WS_BIN_SORT, n,
- * total_pairs, W, H).  GS_ERR_CAPACITY (nothing written) if capacity < total_pairs or the
+ * total_pairs, W, H, NULL).  GS_ERR_CAPACITY (nothing written) if capacity < total_pairs or the
  * workspace is short. */
 int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32_t total_pairs, uint32_t* keys,
                     uint32_t* vals, uint32_t capacity, uint32_t* ranges, void* ws, size_t ws_bytes, void* stream);
@@ -158,19 +206,19 @@ int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32
  * rgb[3][H][W] = C + T bg; T_final[H][W] = T; n_contrib[H][W] = 1 + (index within the tile's
  * range) of the last blended pair, 0 if none ([DR] "The trick": only the final state is kept).
  * total_pairs: the pair count of the sort.  ws: gs_workspace_bytes(GS_WS_RENDER, n, total_pairs,
- * W, H) bytes; it keeps the state that the matching gs_render_bwd reads (the tile order and, for
- * tiles whose list is walked in parallel chunks, the per-chunk boundary states), so pass the same
- * ws, unmodified, to that backward. */
+ * W, H, cfg) bytes; it keeps the state that the matching gs_render_bwd reads (the split sizes used,
+ * the tile order and, for tiles whose list is walked in parallel chunks, the per-chunk boundary
+ * states), so pass the same ws, unmodified, to that backward.  cfg: split_first, split_chunk. */
 int32_t gs_render_fwd(const gs_proj* proj, int64_t n, const uint32_t* vals, const uint32_t* ranges,
                       uint32_t total_pairs, const gs_camera* cam, float* rgb, float* T_final,
-                      uint32_t* n_contrib, void* ws, size_t ws_bytes, void* stream);
+                      uint32_t* n_contrib, void* ws, size_t ws_bytes, const gs_config* cfg, void* stream);
 
 /* Loss (1 - lambda) L1 + lambda (1 - SSIM) and dL/dimg.  [GST] loss slides: L1 mean over
  * 3HW with zero subgradient at zero residual; SSIM with an 11 x 11 Gaussian window of
  * standard deviation 1.5, C1 = 0.01^2, C2 = 0.03^2, zero padding, averaged over pixels and
  * channels; no one-half on D-SSIM; lambda = 0.2 in the method.
  * img, target: [3][H][W].  loss_out: device float[3] = total, L1, mean SSIM.
- * dL_dimg: [3][H][W], overwritten.  ws: gs_workspace_bytes(GS_WS_LOSS, 0, 0, W, H). */
+ * dL_dimg: [3][H][W], overwritten.  ws: gs_workspace_bytes(GS_WS_LOSS, 0, 0, W, H, NULL). */
 int32_t gs_loss_l1_dssim(const float* img, const float* target, int32_t H, int32_t W, float lambda_dssim,
                          float* loss_out, float* dL_dimg, void* ws, size_t ws_bytes, void* stream);
 
@@ -182,7 +230,7 @@ int32_t gs_loss_l1_dssim(const float* img, const float* target, int32_t H, int32
  * means of (err / root) img gain (the log gain's gradient) and err / root (the bias's).
  * img, target, dL_dimg: [3][H][W]; exposure, dL_dexposure: device float[2]; loss_out: device
  * float[1]; delta > 0 (0.03 on the page).  The sums are formed in a fixed order (the result
- * is reproducible).  ws: gs_workspace_bytes(GS_WS_LOSS_CHARBONNIER, 0, 0, W, H). */
+ * is reproducible).  ws: gs_workspace_bytes(GS_WS_LOSS_CHARBONNIER, 0, 0, W, H, NULL). */
 int32_t gs_loss_charbonnier(const float* img, const float* target, int32_t H, int32_t W, float delta,
                             const float* exposure, float* loss_out, float* dL_dimg, float* dL_dexposure, void* ws,
                             size_t ws_bytes, void* stream);
@@ -202,11 +250,15 @@ int32_t gs_loss_charbonnier(const float* img, const float* target, int32_t H, in
  * view-direction term), sigmoid.  gparams: blocked layout, every Gaussian's P parameters
  * overwritten (zero for culled Gaussians); padding untouched.
  * proj, vals, ranges, total_pairs, T_final, n_contrib and ws must be those of the matching
- * forward (ws as that forward left it). */
+ * forward (ws as that forward left it; its header holds the split sizes the forward used, and
+ * a ws no forward of this image and pair count has written makes every screen partial and
+ * parameter gradient NaN).  cfg: grad_sums, active_sh_degree, mip_compensation (the values the
+ * projection used); its split sizes only size the launch; ws must hold gs_workspace_bytes(
+ * GS_WS_RENDER, n, total_pairs, W, H, cfg) bytes. */
 int32_t gs_render_bwd(const gs_scene* scene, const gs_proj* proj, const uint32_t* vals, const uint32_t* ranges,
                       uint32_t total_pairs, const gs_camera* cam, const float* T_final,
                       const uint32_t* n_contrib, const float* dL_dimg, float* gscreen, float* gparams, void* ws,
-                      size_t ws_bytes, void* stream);
+                      size_t ws_bytes, const gs_config* cfg, void* stream);
 
 /* gs_render_bwd for a step over several views (the trainer's loop renders one view per step;
  * a batch of views is the same loop with their gradients summed before one Adam update).
@@ -220,7 +272,7 @@ int32_t gs_render_bwd_weighted(const gs_scene* scene, const gs_proj* proj, const
                                const uint32_t* ranges, uint32_t total_pairs, const gs_camera* cam,
                                const float* T_final, const uint32_t* n_contrib, const float* dL_dimg,
                                float* gscreen, float* gparams, float weight, int32_t accumulate, void* ws,
-                               size_t ws_bytes, void* stream);
+                               size_t ws_bytes, const gs_config* cfg, void* stream);
 
 /* Camera-pose gradient ([GSG] "Forgiving the camera and the light": the pose receives the
  * loss's gradient like any other parameter).  With the rotation perturbed on the left,
@@ -237,9 +289,11 @@ int32_t gs_render_bwd_weighted(const gs_scene* scene, const gs_proj* proj, const
  * gs_render_bwd read and left them: the parameters before any update of this step (the fused
  * update calls overwrite them, so pose optimisation takes gs_render_bwd and gs_adam).  The
  * per-Gaussian terms are formed in double and summed in a fixed order (the result is
- * reproducible).  ws: gs_workspace_bytes(GS_WS_CAMERA_GRAD, n, 0, 0, 0).  Enqueues only. */
+ * reproducible).  ws: gs_workspace_bytes(GS_WS_CAMERA_GRAD, n, 0, 0, 0, NULL).  cfg:
+ * active_sh_degree, mip_compensation (as the projection used them).  Enqueues only. */
 int32_t gs_camera_grad(const gs_scene* scene, const gs_proj* proj, const gs_camera* cam, const float* gscreen,
-                       int32_t position_only, double* grad_out, void* ws, size_t ws_bytes, void* stream);
+                       int32_t position_only, double* grad_out, void* ws, size_t ws_bytes, const gs_config* cfg,
+                       void* stream);
 
 /* Adam, [GSG] Adam section; per-group rates [DR] "From a pixel error back to a quaternion".
  *   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
@@ -261,7 +315,7 @@ int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs
                            const uint32_t* ranges, uint32_t total_pairs, const gs_camera* cam,
                            const float* T_final, const uint32_t* n_contrib, const float* dL_dimg, float* gscreen,
                            float* m, float* v, const float* lr, double beta1, double beta2, double eps,
-                           int32_t step, void* ws, size_t ws_bytes, void* stream);
+                           int32_t step, void* ws, size_t ws_bytes, const gs_config* cfg, void* stream);
 
 /* gs_render_bwd_adam followed by gs_preprocess of the updated scene for the camera of the
  * next step ([GSG] "Putting every stage together": per step, pick a view, project, tile,
@@ -272,18 +326,20 @@ int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs
  * and pair count are those gs_preprocess(scene, next_cam, next_out, next_total_pairs,
  * pre_ws) would produce from the updated params, bit for bit.  next_out may be proj
  * itself (each Gaussian's tile count is read before its new record is written).
- * pre_ws: gs_workspace_bytes(GS_WS_PREPROCESS, n, 0, 0, 0) bytes.  densify_stats (device
+ * pre_ws: gs_workspace_bytes(GS_WS_PREPROCESS, n, 0, 0, 0, NULL) bytes.  densify_stats (device
  * float [n][2], nullable): when given, this step's observations are added to it as
  * gs_densify_accumulate would (from this step's tile counts, before they are replaced).
  * Waits for the next pair count as gs_preprocess does; errors as gs_render_bwd_adam and
- * gs_preprocess. */
+ * gs_preprocess.  cfg as for gs_render_bwd; the projection for next_cam uses its
+ * active_sh_degree and mip_compensation too. */
 int32_t gs_render_bwd_adam_project(float* params, int64_t n, int32_t sh_degree, const gs_proj* proj,
                                    const uint32_t* vals, const uint32_t* ranges, uint32_t total_pairs,
                                    const gs_camera* cam, const float* T_final, const uint32_t* n_contrib,
                                    const float* dL_dimg, float* gscreen, float* m, float* v, const float* lr,
                                    double beta1, double beta2, double eps, int32_t step, void* ws, size_t ws_bytes,
                                    const gs_camera* next_cam, gs_proj* next_out, uint32_t* next_total_pairs,
-                                   void* pre_ws, size_t pre_ws_bytes, float* densify_stats, void* stream);
+                                   void* pre_ws, size_t pre_ws_bytes, float* densify_stats, const gs_config* cfg,
+                                   void* stream);
 
 /* Layout of the per-Gaussian parameter arrays (see the blocked layout above).
  * gs_param_floats: floats in a blocked array for n Gaussians (0 for bad arguments).
@@ -324,7 +380,7 @@ int32_t gs_densify_accumulate(const gs_proj* proj, int64_t n, const float* gscre
  * input.  *n_out (host) receives the new count and counts (host int64[3], nullable) the numbers
  * kept, cloned and split; with params_out == NULL only these are computed.  GS_ERR_CAPACITY
  * (nothing written) if the new count exceeds capacity.  ws: gs_workspace_bytes(GS_WS_DENSIFY,
- * n, 0, 0, 0).  Waits for the counts (one copy to a pinned host word). */
+ * n, 0, 0, 0, NULL).  Waits for the counts (one copy to a pinned host word). */
 int32_t gs_densify(const float* params, const float* m, const float* v, const float* stats, const float* rand,
                    int64_t n, int32_t sh_degree, double grad_threshold, double prune_opacity, double prune_scale,
                    double split_scale, int32_t reset_opacity, double opacity_cap, float* params_out, float* m_out,
@@ -346,7 +402,7 @@ int32_t gs_densify(const float* params, const float* m, const float* v, const fl
  * are lowered by ln 1.6 too; both get zero m and v.  All other Gaussians are unchanged, and
  * so is the count.  params, m, v: blocked layout for n, updated in place; rand [n][3]
  * (device).  *moves_out (host, nullable): the number of moves.  ws: gs_workspace_bytes(
- * GS_WS_RELOCATE, n, 0, 0, 0).  Waits for the two counts (one copy to a pinned host buffer);
+ * GS_WS_RELOCATE, n, 0, 0, 0, NULL).  Waits for the two counts (one copy to a pinned host buffer);
  * the donors are ranked with rocPRIM's stable radix sort. */
 int32_t gs_relocate(float* params, float* m, float* v, int64_t n, int32_t sh_degree, const float* rand,
                     double dead_opacity, double donor_opacity, int64_t max_moves, int64_t* moves_out, void* ws,
@@ -355,54 +411,10 @@ int32_t gs_relocate(float* params, float* m, float* v, int64_t n, int32_t sh_deg
 enum { GS_WS_PREPROCESS = 0, GS_WS_BIN_SORT = 1, GS_WS_LOSS = 2, GS_WS_RENDER = 3, GS_WS_DENSIFY = 4,
        GS_WS_LOSS_CHARBONNIER = 5, GS_WS_CAMERA_GRAD = 6, GS_WS_RELOCATE = 7 };
 
-/* How the backward blend sums the per-pixel gradient contributions of a Gaussian (for the
- * whole process, every backward call enqueued after it; default GS_GRAD_SUMS_FLOAT).
- *   GS_GRAD_SUMS_FLOAT: fp32 atomics; the order of the additions varies from run to run.
- *   GS_GRAD_SUMS_FIXED: [GSG] "Making the parallel sums exact": every wave-summed moment
- *     (position moments, the three second moments divided by a footprint size factor
- *     1 + trace of the screen covariance, opacity, colour), times 16384 and times the
- *     loss's element count 3 W H (so that the unit is that of the summed loss), clamped to
- *     +-1e9, rounded to the nearest integer and added with i32 atomics; a decode pass then
- *     turns the sums into the same partials as the float mode.  Results are identical bit
- *     for bit from run to run; each addition is exact to 0.5 / (16384 * 3 W H), and a
- *     partial's total must stay within 2^31 units (it wraps beyond).
- * GS_ERR_INVALID_ARG for another mode. */
-enum { GS_GRAD_SUMS_FLOAT = 0, GS_GRAD_SUMS_FIXED = 1 };
-int32_t gs_set_grad_sums(int32_t mode);
-int32_t gs_get_grad_sums(void);
-
-/* SH degree ramp ([GSG] "Spherical harmonics": only the first activeK = (activeDeg + 1)^2 - 1
- * band weights are summed, the active degree stepping up about every thousand steps; the
- * inactive ones contribute nothing and receive no gradient until their band switches on).
- * For the whole process, every projection and chain enqueued after it: the colour sums
- * the bands up to min(degree, the scene's SH degree), and the other bands' gradients are
- * zero (with the fused Adam their parameters stay unchanged while their moments are zero).
- * -1 (the default): every stored band.  GS_ERR_INVALID_ARG outside -1..3. */
-int32_t gs_set_active_sh_degree(int32_t degree);
-int32_t gs_get_active_sh_degree(void);
-
-/* Mip-Splatting opacity compensation ([GSG] "Flattening a 3D blob into a 2D oval": a
- * correction so that the dilation does not make very small Gaussians brighter overall; the
- * trainer's code multiplies the opacity by it in the extent and in alpha).  With on = 1, for the whole process, every
- * projection and chain enqueued after it: the record's opacity is
- *   sigmoid(logit) comp,  comp = sqrt(max(det V, 0) / det(V + 0.3 I)),
- * V the undilated screen covariance (the factor that gives the dilated footprint exactly the
- * integral of the undilated one), so it also enters the extent, alpha and the skip boxes;
- * the chain adds comp's gradient to the covariance's and scales the logit's by comp.  The
- * blend is unchanged (it differentiates the record's opacity).  0 (the default): off.
- * GS_ERR_INVALID_ARG for another value. */
-int32_t gs_set_mip_compensation(int32_t on);
-int32_t gs_get_mip_compensation(void);
-size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H);
-
-/* Tuning of the blend's work split (process-wide; set before sizing workspaces, and not between a
- * forward and its backward).  Every tile's first GS_TUNE_SPLIT_FIRST pairs are walked by one
- * block; a tile with pixels still unfinished then has its remaining pairs walked in parallel
- * chunks of GS_TUNE_SPLIT_CHUNK pairs.  Values: multiples of 4 in [4, 2^24]; defaults 2048, 512.
- * The results do not depend on these values beyond rounding. */
-enum { GS_TUNE_SPLIT_FIRST = 0, GS_TUNE_SPLIT_CHUNK = 1 };
-int32_t gs_set_tuning(int32_t key, int64_t value);
-int64_t gs_get_tuning(int32_t key);
+/* Workspace size in bytes for the call `which_call` (GS_WS_*) with n Gaussians, `pairs` pairs
+ * and a W x H image; cfg as the call will receive it (NULL: defaults).  The render workspace
+ * (GS_WS_RENDER) depends on cfg's split sizes and gradient-sum mode; the others do not. */
+size_t gs_workspace_bytes(int32_t which_call, int64_t n, uint32_t pairs, int32_t W, int32_t H, const gs_config* cfg);
 
 /* Optional per-kernel timing (instrumentation, not part of the method).  gs_profile_enable(1, only)
  * makes every later library call bracket each kernel launch whose name equals `only` (every

@@ -16,12 +16,14 @@ CALM = 0.1                 # parameter gradients are checked where flips move no
 SSIM_REACH = 10            # a pixel's loss gradient depends on pixels up to this far away
 
 
-def gpu_forward(params_np, deg, cam):
+def gpu_forward(params_np, deg, cam, cfg=None):
+    """A Pipeline over the scene (cfg: its gs_config, None for the defaults) after one
+    forward for cam."""
     import torch
     from differentiable_tile_gaussian_amd import gs
     from differentiable_tile_gaussian_amd.pipeline import Pipeline
     params = torch.from_numpy(np.ascontiguousarray(params_np, np.float32)).cuda()
-    pl = Pipeline(params, deg, cam.width, cam.height)
+    pl = Pipeline(params, deg, cam.width, cam.height, cfg=cfg)
     c = gs.make_camera(cam)
     pl.forward(c)
     torch.cuda.synchronize()

@@ -45,21 +45,21 @@ def test_argument_errors_without_gpu(gs):
     cam = _cam(gs)
     total = C.c_uint32(0)
     # null scene
-    assert L.gs_preprocess(None, C.byref(cam), None, C.byref(total), None, 0, None) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_preprocess(None, C.byref(cam), None, C.byref(total), None, 0, None, None) == gs.GS_ERR_INVALID_ARG
     assert "scene" in gs.gs_last_error()
     # unsupported SH degree
     sc = gs.GsScene(10, 4, 1234)
     proj = gs.GsProj(1, 1, 1, 1, 1, 1, 1, 1)
-    assert L.gs_preprocess(C.byref(sc), C.byref(cam), C.byref(proj), C.byref(total), None, 0,
+    assert L.gs_preprocess(C.byref(sc), C.byref(cam), C.byref(proj), C.byref(total), None, 0, None,
                            None) == gs.GS_ERR_UNSUPPORTED
     # zero-sized image
     sc = gs.GsScene(10, 0, 1234)
     bad = _cam(gs)
     bad.width = 0
-    assert L.gs_preprocess(C.byref(sc), C.byref(bad), C.byref(proj), C.byref(total), None, 0,
+    assert L.gs_preprocess(C.byref(sc), C.byref(bad), C.byref(proj), C.byref(total), None, 0, None,
                            None) == gs.GS_ERR_INVALID_ARG
     # missing workspace
-    assert L.gs_preprocess(C.byref(sc), C.byref(cam), C.byref(proj), C.byref(total), None, 0,
+    assert L.gs_preprocess(C.byref(sc), C.byref(cam), C.byref(proj), C.byref(total), None, 0, None,
                            None) == gs.GS_ERR_CAPACITY
     # key capacity below the pair count: nothing written
     assert L.gs_bin_sort(C.byref(proj), 10, C.byref(cam), 100, 1, 1, 50, 1, 1, 1 << 30,
@@ -71,10 +71,11 @@ def test_argument_errors_without_gpu(gs):
     # loss with a bad lambda
     assert L.gs_loss_l1_dssim(1, 1, 8, 8, C.c_float(1.5), 1, 1, 1, 1 << 30, None) == gs.GS_ERR_INVALID_ARG
     # negative n
-    assert L.gs_render_fwd(C.byref(proj), -1, None, None, 0, C.byref(cam), 1, 1, 1, None, 0,
+    assert L.gs_render_fwd(C.byref(proj), -1, None, None, 0, C.byref(cam), 1, 1, 1, None, 0, None,
                            None) == gs.GS_ERR_INVALID_ARG
     # render without its workspace
-    assert L.gs_render_fwd(C.byref(proj), 10, 1, 1, 100, C.byref(cam), 1, 1, 1, None, 0, None) == gs.GS_ERR_CAPACITY
+    assert L.gs_render_fwd(C.byref(proj), 10, 1, 1, 100, C.byref(cam), 1, 1, 1, None, 0, None,
+                           None) == gs.GS_ERR_CAPACITY
     # backward + Adam + next projection: the next camera, its pair-count output and the
     # preprocess workspace are checked before anything is enqueued
     nxt = gs.GsCamera.from_buffer_copy(cam)
@@ -83,7 +84,7 @@ def test_argument_errors_without_gpu(gs):
     def bwd_project(next_cam, next_total, pre_ws, pre_bytes):
         return L.gs_render_bwd_adam_project(1, 10, 0, C.byref(proj), 1, 1, 100, C.byref(cam), 1, 1, 1, 1, 1, 1, lr,
                                             0.9, 0.999, 1e-8, 1, 1, 1 << 40, next_cam, C.byref(proj), next_total,
-                                            pre_ws, pre_bytes, None, None)
+                                            pre_ws, pre_bytes, None, None, None)
     assert bwd_project(None, C.byref(nt), 1, 1 << 40) == gs.GS_ERR_INVALID_ARG
     assert bwd_project(C.byref(nxt), None, 1, 1 << 40) == gs.GS_ERR_INVALID_ARG
     assert bwd_project(C.byref(nxt), C.byref(nt), None, 0) == gs.GS_ERR_CAPACITY
@@ -112,23 +113,20 @@ def test_argument_errors_without_gpu(gs):
     assert L.gs_loss_charbonnier(1, 1, 8, 8, C.c_float(0.03), 1, 1, 1, None, None, 0, None) == gs.GS_ERR_CAPACITY
     # camera-pose gradient: scene, output, gscreen and workspace are checked first
     sc = gs.GsScene(10, 1, 1234)
-    assert L.gs_camera_grad(None, C.byref(proj), C.byref(cam), 1, 0, 1, 1, big, None) == gs.GS_ERR_INVALID_ARG
-    assert L.gs_camera_grad(C.byref(sc), C.byref(proj), C.byref(cam), 1, 0, None, 1, big, None) == gs.GS_ERR_INVALID_ARG
+    def camgrad(scene, pr, gsc, pos_only, out, ws_bytes):
+        return L.gs_camera_grad(scene, pr, C.byref(cam), gsc, pos_only, out, 1, ws_bytes, None, None)
+    assert camgrad(None, C.byref(proj), 1, 0, 1, big) == gs.GS_ERR_INVALID_ARG
+    assert camgrad(C.byref(sc), C.byref(proj), 1, 0, None, big) == gs.GS_ERR_INVALID_ARG
     assert "grad_out" in gs.gs_last_error()
-    assert L.gs_camera_grad(C.byref(sc), C.byref(proj), C.byref(cam), None, 0, 1, 1, big, None) == gs.GS_ERR_INVALID_ARG
-    assert L.gs_camera_grad(C.byref(sc), None, C.byref(cam), 1, 0, 1, 1, big, None) == gs.GS_ERR_INVALID_ARG
-    assert L.gs_camera_grad(C.byref(sc), C.byref(proj), C.byref(cam), 1, 0, 1, 1, 47, None) == gs.GS_ERR_CAPACITY
+    assert camgrad(C.byref(sc), C.byref(proj), None, 0, 1, big) == gs.GS_ERR_INVALID_ARG
+    assert camgrad(C.byref(sc), None, 1, 0, 1, big) == gs.GS_ERR_INVALID_ARG
+    assert camgrad(C.byref(sc), C.byref(proj), 1, 0, 1, 47) == gs.GS_ERR_CAPACITY
     assert "camera-gradient workspace" in gs.gs_last_error()
-    assert L.gs_camera_grad(C.byref(sc), C.byref(proj), C.byref(cam), 1, 2, 1, 1, big, None) == gs.GS_ERR_INVALID_ARG
-    # SH degree ramp
-    assert L.gs_get_active_sh_degree() == -1
-    assert L.gs_set_active_sh_degree(4) == gs.GS_ERR_INVALID_ARG
-    assert L.gs_set_active_sh_degree(-2) == gs.GS_ERR_INVALID_ARG
-    assert L.gs_get_active_sh_degree() == -1
+    assert camgrad(C.byref(sc), C.byref(proj), 1, 2, 1, big) == gs.GS_ERR_INVALID_ARG
     # several views per step: the weight and the accumulate flag are checked first
     def weighted(weight, acc):
         return L.gs_render_bwd_weighted(C.byref(sc), C.byref(proj), 1, 1, 100, C.byref(cam), 1, 1, 1, 1, 1,
-                                        C.c_float(weight), acc, 1, big, None)
+                                        C.c_float(weight), acc, 1, big, None, None)
     assert weighted(float("nan"), 0) == gs.GS_ERR_INVALID_ARG
     assert weighted(float("inf"), 1) == gs.GS_ERR_INVALID_ARG
     assert weighted(0.5, 2) == gs.GS_ERR_INVALID_ARG
@@ -141,18 +139,36 @@ def test_argument_errors_without_gpu(gs):
     assert relocate(0.02, 1.0) == gs.GS_ERR_INVALID_ARG
     assert relocate(0.02, 0.4, ws_bytes=16) == gs.GS_ERR_CAPACITY
     assert "relocation workspace" in gs.gs_last_error()
-    # Mip-Splatting compensation switch
-    assert L.gs_get_mip_compensation() == 0
-    assert L.gs_set_mip_compensation(2) == gs.GS_ERR_INVALID_ARG
-    assert L.gs_get_mip_compensation() == 0
-    # gradient-sum modes
-    assert L.gs_get_grad_sums() == gs.GS_GRAD_SUMS_FLOAT
-    assert L.gs_set_grad_sums(7) == gs.GS_ERR_INVALID_ARG
-    assert L.gs_get_grad_sums() == gs.GS_GRAD_SUMS_FLOAT
-    # tuning values are checked
-    assert L.gs_set_tuning(gs.GS_TUNE_SPLIT_CHUNK, 6) == gs.GS_ERR_INVALID_ARG
-    assert L.gs_set_tuning(77, 1024) == gs.GS_ERR_INVALID_ARG
-    assert L.gs_get_tuning(gs.GS_TUNE_SPLIT_FIRST) == 2048
+
+
+
+@pytest.mark.parametrize("field,value", [("grad_sums", 7), ("active_sh_degree", 4), ("active_sh_degree", -2),
+                                         ("mip_compensation", 2), ("split_first", 6), ("split_chunk", -4),
+                                         ("split_chunk", (1 << 24) + 4)])
+def test_config_checked_per_call(gs, field, value):
+    """Every call that takes a gs_config rejects an out-of-range field before anything is
+    enqueued; the library keeps no setting between calls."""
+    L = gs.lib()
+    cam = _cam(gs)
+    cfg = gs.GsConfig()
+    setattr(cfg, field, value)
+    total = C.c_uint32(0)
+    sc = gs.GsScene(10, 0, 1234)
+    proj = gs.GsProj(1, 1, 1, 1, 1, 1, 1, 1)
+    big = 1 << 40
+    assert L.gs_preprocess(C.byref(sc), C.byref(cam), C.byref(proj), C.byref(total), 1, big, C.byref(cfg),
+                           None) == gs.GS_ERR_INVALID_ARG
+    assert "cfg." in gs.gs_last_error()
+    assert L.gs_render_fwd(C.byref(proj), 10, 1, 1, 100, C.byref(cam), 1, 1, 1, 1, big, C.byref(cfg),
+                           None) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_render_bwd(C.byref(sc), C.byref(proj), 1, 1, 100, C.byref(cam), 1, 1, 1, 1, 1, 1, big, C.byref(cfg),
+                           None) == gs.GS_ERR_INVALID_ARG
+    assert L.gs_camera_grad(C.byref(sc), C.byref(proj), C.byref(cam), 1, 0, 1, 1, big, C.byref(cfg),
+                            None) == gs.GS_ERR_INVALID_ARG
+    assert gs.gs_workspace_bytes(gs.GS_WS_RENDER, 10, 100, 64, 48, cfg) == 0
+    # the same call with the defaults passes the check (and fails later, on the workspace)
+    assert L.gs_render_fwd(C.byref(proj), 10, 1, 1, 100, C.byref(cam), 1, 1, 1, 1, 16, None,
+                           None) == gs.GS_ERR_CAPACITY
 
 
 def test_workspace_sizes_grow_with_the_problem(gs):
@@ -170,6 +186,16 @@ def test_workspace_sizes_grow_with_the_problem(gs):
     # camera-pose gradient: six double sums per group of 64 Gaussians
     assert gs.gs_workspace_bytes(gs.GS_WS_CAMERA_GRAD, 1_000_000, 0, 0, 0) == 15625 * 48
     assert gs.gs_workspace_bytes(99, 1, 1, 1, 1) == 0
+    # the render workspace: the forward's header and split state, plus 72 bytes per Gaussian
+    # for fixed-point sums; smaller split sizes need more boundary states
+    base = gs.gs_workspace_bytes(gs.GS_WS_RENDER, 1_000_000, 4_000_000, 1920, 1080)
+    assert base == gs.gs_workspace_bytes(gs.GS_WS_RENDER, 1_000_000, 4_000_000, 1920, 1080, gs.GsConfig())
+    fixed = gs.gs_workspace_bytes(gs.GS_WS_RENDER, 1_000_000, 4_000_000, 1920, 1080,
+                                  gs.GsConfig(grad_sums=gs.GS_GRAD_SUMS_FIXED))
+    assert fixed >= base + 72 * 1_000_000
+    fine = gs.gs_workspace_bytes(gs.GS_WS_RENDER, 1_000_000, 4_000_000, 1920, 1080,
+                                 gs.GsConfig(split_first=512, split_chunk=128))
+    assert fine > base
 
 
 def test_profile_calls_without_gpu(gs):

@@ -25,27 +25,25 @@ def gs_cam():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from differentiable_tile_gaussian_amd import gs
-    try:
-        yield gs
-    finally:
-        gs.gs_set_active_sh_degree(-1)
+    return gs
 
 
-def _backward(torch, gs, params, deg, cam, seed, scale=1e-2):
-    pl, c = pu.gpu_forward(params, deg, cam)
+def _backward(torch, gs, params, deg, cam, seed, scale=1e-2, cfg=None):
+    pl, c = pu.gpu_forward(params, deg, cam, cfg)
     h, w = cam.height, cam.width
     pl.dLdI.copy_(torch.from_numpy((np.random.default_rng(seed).standard_normal((3, h, w)) * scale)
                                    .astype(np.float32)))
     gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI, pl.gscreen,
-                     pl.grads, pl.ws_render)
+                     pl.grads, pl.ws_render, cfg=pl.cfg)
     torch.cuda.synchronize()
     return pl, c
 
 
 def _camera_grad(torch, gs, pl, deg, c, position_only=False):
+    """The pose gradient with the pipeline's own settings (those its backward used)."""
     out = torch.full((6,), float("nan"), dtype=torch.float64, device="cuda")
     ws = gs.workspace(gs.GS_WS_CAMERA_GRAD, n=pl.n)
-    gs.gs_camera_grad(pl.params, deg, pl.proj, c, pl.gscreen, out, ws, position_only=position_only)
+    gs.gs_camera_grad(pl.params, deg, pl.proj, c, pl.gscreen, out, ws, position_only=position_only, cfg=pl.cfg)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -77,10 +75,9 @@ def test_camera_grad_matches_oracle(gs_cam, oracle, deg, active):
     print(f"camera grad: deg={deg} active={active}", flush=True)
     s = _scene(40 + deg, 3000, deg)
     cam = scenes.look_at_origin((0.7, 0.4, -4.5), 160, 120, 150.0)
-    gs.gs_set_active_sh_degree(active)
     oracle.set_active_sh_degree(active)
     try:
-        pl, c = _backward(torch, gs, s.params, deg, cam, seed=deg)
+        pl, c = _backward(torch, gs, s.params, deg, cam, seed=deg, cfg=gs.GsConfig(active_sh_degree=active))
         got = _camera_grad(torch, gs, pl, deg, c)
         _check_against_oracle(oracle, got, s.params, deg, cam, pl.gscreen[:s.n].T.cpu().numpy())
     finally:

@@ -317,25 +317,12 @@ def _deep_case():
     return s, cam
 
 
-@pytest.fixture
-def split_tuning(torch_cuda):
-    from differentiable_tile_gaussian_amd import gs
-    old = (gs.gs_get_tuning(gs.GS_TUNE_SPLIT_FIRST), gs.gs_get_tuning(gs.GS_TUNE_SPLIT_CHUNK))
-
-    def set_(first, chunk):
-        gs.gs_set_tuning(gs.GS_TUNE_SPLIT_FIRST, first)
-        gs.gs_set_tuning(gs.GS_TUNE_SPLIT_CHUNK, chunk)
-
-    yield set_
-    set_(*old)
-
-
 @pytest.mark.parametrize("tune", [(16, 8), (64, 32), (12, 4), (256, 128)])
 @pytest.mark.parametrize("which", ["deep", "small3", "small2"])
-def test_split_path_parity(torch_cuda, oracle, split_tuning, tune, which):
+def test_split_path_parity(torch_cuda, oracle, tune, which):
     torch = torch_cuda
     from differentiable_tile_gaussian_amd import gs
-    split_tuning(*tune)
+    cfg = gs.GsConfig(split_first=tune[0], split_chunk=tune[1])
     if which == "deep":
         s, cam = _deep_case()
     else:
@@ -347,11 +334,11 @@ def test_split_path_parity(torch_cuda, oracle, split_tuning, tune, which):
     lens = (o["ranges"][1].astype(np.int64) - o["ranges"][0])
     if lens.max() <= tune[0] + tune[1]:
         pytest.skip("no tile list long enough for this split size")
-    pl, c = pu.gpu_forward(s.params, deg, cam)
+    pl, c = pu.gpu_forward(s.params, deg, cam, cfg)
     n_flip = pu.check_render(pu.render_to_numpy(pl), o["fwd"], o["risk"])
     pl.dLdI.copy_(torch.from_numpy(dLdI))
     gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI, pl.gscreen,
-                     pl.grads, pl.ws_render)
+                     pl.grads, pl.ws_render, cfg=cfg)
     torch.cuda.synchronize()
     pu.check_screen_grads(pl.gscreen[:s.n].T.cpu().numpy(), o["gscreen"], o["risk"]["g"], o["slack"])
     keep = pu.calm(o["risk"]["g"], o["gscreen"])
@@ -359,6 +346,77 @@ def test_split_path_parity(torch_cuda, oracle, split_tuning, tune, which):
     pu.check_param_grads(g, o, oracle, s.params, deg, cam, keep)
     stopped = float((o["fwd"]["T"] < 1e-4).mean())
     print(f"  flippable px {n_flip}, not calm G {int((~keep).sum())}, saturated px {stopped:.2f}", flush=True)
+
+
+def test_backward_walks_the_forwards_split(torch_cuda):
+    """The backward takes the split sizes from the forward's workspace header: a backward
+    called with other split sizes than its forward (larger or smaller, so its launch has
+    fewer or more chunk blocks than the forward made chunks) gives the same gradients bit
+    for bit (fixed-point sums: no reordering); a workspace that no forward of this image
+    wrote gives NaN everywhere instead of reading a stale split state."""
+    torch = torch_cuda
+    from differentiable_tile_gaussian_amd import gs
+    s, cam = _deep_case()
+    fwd_cfg = gs.GsConfig(grad_sums=gs.GS_GRAD_SUMS_FIXED, split_first=16, split_chunk=8)
+    dLdI = torch.from_numpy((np.random.default_rng(12).standard_normal((3, cam.height, cam.width)) * 1e-3)
+                            .astype(np.float32)).cuda()
+    grads = {}
+    for name, bwd in (("same", (16, 8)), ("larger", (2048, 512)), ("smaller", (8, 4))):
+        bwd_cfg = gs.GsConfig(grad_sums=gs.GS_GRAD_SUMS_FIXED, split_first=bwd[0], split_chunk=bwd[1])
+        pl, c = pu.gpu_forward(s.params, s.sh_degree, cam, fwd_cfg)
+        need = gs.gs_workspace_bytes(gs.GS_WS_RENDER, s.n, pl.pairs, cam.width, cam.height, bwd_cfg)
+        if pl.ws_render.numel() < need:     # the backward's own sizing may ask for more
+            ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+            ws[:pl.ws_render.numel()].copy_(pl.ws_render)
+            pl.ws_render = ws
+        pl.dLdI.copy_(dLdI)
+        gs.gs_render_bwd(pl.params, s.sh_degree, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI,
+                         pl.gscreen, pl.grads, pl.ws_render, cfg=bwd_cfg)
+        torch.cuda.synchronize()
+        grads[name] = pl.planar(pl.grads).cpu().numpy()
+    assert np.isfinite(grads["same"]).all() and np.abs(grads["same"]).max() > 0
+    for name in ("larger", "smaller"):
+        np.testing.assert_array_equal(grads[name].view(np.uint32), grads["same"].view(np.uint32), err_msg=name)
+    # a workspace no forward wrote: NaN partials and gradients, in both sum modes
+    for mode in (gs.GS_GRAD_SUMS_FLOAT, gs.GS_GRAD_SUMS_FIXED):
+        cfg = gs.GsConfig(grad_sums=mode)
+        pl, c = pu.gpu_forward(s.params, s.sh_degree, cam, cfg)
+        pl.ws_render.zero_()
+        gs.gs_render_bwd(pl.params, s.sh_degree, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, dLdI,
+                         pl.gscreen, pl.grads, pl.ws_render, cfg=cfg)
+        torch.cuda.synchronize()
+        assert torch.isnan(pl.gscreen[:s.n]).all()
+        vis = torch.from_numpy(pl.proj.tiles[:s.n].cpu().numpy() > 0)
+        # mean, scale, rotation and logit come from the (NaN) position, conic and opacity
+        # partials; a clamped colour channel's coefficients get an exact 0
+        assert torch.isnan(pl.planar(pl.grads).cpu()[0:11, vis]).all()
+
+
+def test_two_configurations_in_one_process(torch_cuda, oracle):
+    """Two pipelines with different settings (SH degree ramp at 1 with Mip compensation;
+    the defaults), their calls interleaved: each renders what the oracle renders with its
+    own settings.  No setting lives in the library between calls."""
+    from differentiable_tile_gaussian_amd import gs
+    s, cam = _scene_and_camera(*_small_cases()[3])
+    deg = s.sh_degree
+    cfg_a = gs.GsConfig(active_sh_degree=1, mip_compensation=True)
+    pl_a, c = pu.gpu_forward(s.params, deg, cam, cfg_a)
+    pl_b, _ = pu.gpu_forward(s.params, deg, cam)
+    pl_a.forward(c)                     # again, after pl_b's calls
+    torch_cuda.cuda.synchronize()
+    zero = np.zeros((3, cam.height, cam.width), np.float32)
+    for pl, active, mip in ((pl_a, 1, True), (pl_b, -1, False)):
+        oracle.set_active_sh_degree(active)
+        oracle.set_mip_compensation(mip)
+        try:
+            o = oracle.forward(s.params, deg, cam)
+        finally:
+            oracle.set_active_sh_degree(-1)
+            oracle.set_mip_compensation(False)
+        pu.check_preprocess(pu.proj_to_numpy(pl), o[0])
+        risk = oracle.flip_risk(o[0], o[2], o[3], cam, zero)
+        pu.check_render(pu.render_to_numpy(pl), o[4], risk)
+    assert not np.array_equal(pl_a.rgb.cpu().numpy(), pl_b.rgb.cpu().numpy())
 
 
 # ------------------------------------------------------- fused backward + Adam

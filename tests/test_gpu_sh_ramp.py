@@ -1,4 +1,4 @@
-"""The SH degree ramp on the GPU (gs_set_active_sh_degree).
+"""The SH degree ramp on the GPU (gs_config.active_sh_degree).
 
 A degree-3 scene with active degree d against the degree-d scene made of its first planes
 (the degree-d layout is a prefix of the degree-3 one): records, depths, rectangles, tile
@@ -22,11 +22,7 @@ def gs_ramp():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from differentiable_tile_gaussian_amd import gs
-    try:
-        yield gs
-    finally:
-        gs.gs_set_active_sh_degree(-1)
-        gs.gs_set_grad_sums(gs.GS_GRAD_SUMS_FLOAT)
+    return gs
 
 
 def _scene():
@@ -37,11 +33,11 @@ def _scene():
     return s, cam
 
 
-def _forward_backward(torch, gs, params, deg, cam, dLdI):
-    pl, c = pu.gpu_forward(params, deg, cam)
+def _forward_backward(torch, gs, params, deg, cam, dLdI, cfg):
+    pl, c = pu.gpu_forward(params, deg, cam, cfg)
     pl.dLdI.copy_(dLdI)
     gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI, pl.gscreen,
-                     pl.grads, pl.ws_render)
+                     pl.grads, pl.ws_render, cfg=cfg)
     torch.cuda.synchronize()
     return pl
 
@@ -50,14 +46,13 @@ def _forward_backward(torch, gs, params, deg, cam, dLdI):
 def test_active_degree_equals_the_prefix_scene(gs_ramp, d):
     import torch
     gs = gs_ramp
-    gs.gs_set_grad_sums(gs.GS_GRAD_SUMS_FIXED)
     s, cam = _scene()
     dLdI = torch.from_numpy((np.random.default_rng(6).standard_normal((3, 120, 160)) * 1e-2).astype(np.float32)).cuda()
     Pd = scenes.num_planes(d)
-    gs.gs_set_active_sh_degree(-1)
-    ref = _forward_backward(torch, gs, np.ascontiguousarray(s.params[:Pd]), d, cam, dLdI)
-    gs.gs_set_active_sh_degree(d)
-    got = _forward_backward(torch, gs, s.params, 3, cam, dLdI)
+    ref = _forward_backward(torch, gs, np.ascontiguousarray(s.params[:Pd]), d, cam, dLdI,
+                            gs.GsConfig(grad_sums=gs.GS_GRAD_SUMS_FIXED))
+    got = _forward_backward(torch, gs, s.params, 3, cam, dLdI,
+                            gs.GsConfig(grad_sums=gs.GS_GRAD_SUMS_FIXED, active_sh_degree=d))
     n = s.n
     for name in ("splat", "depth", "rect", "tiles"):
         a = getattr(got.proj, name)[:n].cpu().numpy().view(np.uint32)
@@ -75,13 +70,13 @@ def test_ramp_against_the_oracle_and_in_the_fused_update(gs_ramp, oracle):
     import torch
     gs = gs_ramp
     s, cam = _scene()
-    gs.gs_set_active_sh_degree(1)
+    cfg = gs.GsConfig(active_sh_degree=1)
     oracle.set_active_sh_degree(1)
     try:
         o = oracle.forward(s.params, 3, cam)
     finally:
         oracle.set_active_sh_degree(-1)
-    pl, c = pu.gpu_forward(s.params, 3, cam)
+    pl, c = pu.gpu_forward(s.params, 3, cam, cfg)
     risk = oracle.flip_risk(o[0], o[2], o[3], cam, np.zeros((3, 120, 160), np.float32))
     pu.check_render(pu.render_to_numpy(pl), o[4], risk)
     # one fused update with the next projection: the inactive bands keep their values
@@ -91,14 +86,14 @@ def test_ramp_against_the_oracle_and_in_the_fused_update(gs_ramp, oracle):
     cam2 = gs.make_camera(scenes.look_at_origin((-0.5, 0.3, -4.4), 160, 120, 150.0))
     pairs = gs.gs_render_bwd_adam_project(pl.params, 3, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc,
                                           pl.dLdI, pl.gscreen, pl.m, pl.v, pl.lr, 0.9, 0.999, 1e-8, 1, pl.ws_render,
-                                          cam2, pl.proj, pl.ws_pre)
+                                          cam2, pl.proj, pl.ws_pre, cfg=cfg)
     torch.cuda.synchronize()
     after = pl.planar(pl.params).cpu().numpy()
     P1 = scenes.num_planes(1)
     np.testing.assert_array_equal(after[P1:], before[P1:])
     assert np.abs(after[:P1] - before[:P1]).max() > 0
     ref = gs.Proj(s.n)
-    assert pairs == gs.gs_preprocess(pl.params, 3, cam2, ref, gs.workspace(gs.GS_WS_PREPROCESS, n=s.n))
+    assert pairs == gs.gs_preprocess(pl.params, 3, cam2, ref, gs.workspace(gs.GS_WS_PREPROCESS, n=s.n), cfg=cfg)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(pl.proj.splat[:s.n].cpu().numpy().view(np.uint32),
                                   ref.splat[:s.n].cpu().numpy().view(np.uint32))

@@ -1,11 +1,16 @@
 """Several views per step (gs_render_bwd_weighted and Pipeline.step_views), on the GPU.
 
+Against the oracle (float sums, the training path's default): the GPU's gradient of two
+views, weights 0.7 and 0.3, the second accumulated, equals the oracle's per-view
+gradients combined with those weights in fp64, each view's tolerance (the usual 1e-3
+relative bar plus its flip risk and rounding slack carried through the chain) weighted
+likewise.  Each view's backward is fed the oracle's image gradient of that view.
+
 With fixed-point gradient sums every backward is reproducible bit for bit, so the weighted
-and accumulated gradients are checked exactly: weight 1 without accumulation is
+and accumulated gradients are also checked exactly: weight 1 without accumulation is
 gs_render_bwd's gradient; two views with weight 1/2, the second accumulated, give
 fl(fl(g_a / 2) + fl(g_b / 2)) in fp32 element by element; and Pipeline.step_views over
 those two views ends with the parameters and moments of one gs_adam_step on that gradient.
-The single-view gradients themselves are checked against the oracle elsewhere.
 """
 import numpy as np
 import pytest
@@ -18,15 +23,12 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture
 def fixed_sums():
+    """The binding and a gs_config with fixed-point sums."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from differentiable_tile_gaussian_amd import gs
-    gs.gs_set_grad_sums(gs.GS_GRAD_SUMS_FIXED)
-    try:
-        yield gs
-    finally:
-        gs.gs_set_grad_sums(gs.GS_GRAD_SUMS_FLOAT)
+    return gs, gs.GsConfig(grad_sums=gs.GS_GRAD_SUMS_FIXED)
 
 
 def _views():
@@ -39,27 +41,77 @@ def _views():
     return s, cams, targets
 
 
-def _view_grad(torch, gs, pl, cam, target, weight=None, accumulate=False):
+def _view_grad(torch, gs, pl, cam, target, weight=None, accumulate=False, dLdI=None):
+    """The parameter gradient of one view (dLdI: the image gradient to feed the backward,
+    else the GPU loss's)."""
     c = gs.make_camera(cam)
     pl.forward(c)
     gs.gs_loss_l1_dssim(pl.rgb, target, pl.lam, pl.loss, pl.dLdI, pl.ws_loss)
+    if dLdI is not None:
+        pl.dLdI.copy_(torch.from_numpy(np.ascontiguousarray(dLdI, np.float32)))
     if weight is None:
         gs.gs_render_bwd(pl.params, pl.deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI,
-                         pl.gscreen, pl.grads, pl.ws_render)
+                         pl.gscreen, pl.grads, pl.ws_render, cfg=pl.cfg)
     else:
         gs.gs_render_bwd_weighted(pl.params, pl.deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI,
-                                  pl.gscreen, pl.grads, pl.ws_render, weight, accumulate)
+                                  pl.gscreen, pl.grads, pl.ws_render, weight, accumulate, cfg=pl.cfg)
     torch.cuda.synchronize()
     return pl.planar(pl.grads).cpu().numpy()
 
 
+def _view_tolerance(oracle, ref, params, deg, cam, rtol=pu.GRAD_RTOL):
+    """[P][n] tolerance of one view's parameter gradient: rtol of the element plus rtol of its
+    group's rms, plus the view's flip risk and rounding slack on the screen partials carried
+    through the chain (linear in them) plane by plane."""
+    g = ref["gparams"].astype(np.float64)
+    tol = rtol * np.abs(g)
+    for sl in pu.grad_groups(deg).values():
+        tol[sl] += rtol * np.sqrt((g[sl] ** 2).mean())
+    bound = ref["risk"]["g"].astype(np.float64) + ref["slack"]
+    for k in range(9):
+        gk = np.zeros((9, g.shape[1]), np.float32)
+        gk[k] = bound[k]
+        tol += np.abs(oracle.preprocess_bwd(params, deg, cam, gk).astype(np.float64))
+    return tol
+
+
+def test_weighted_views_against_the_oracle(oracle):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from differentiable_tile_gaussian_amd import gs
+    from differentiable_tile_gaussian_amd.pipeline import Pipeline
+    s, cams, targets = _views()
+    deg = 2
+    weights = (0.7, 0.3)
+    refs = [oracle.train_step_grads(s.params, deg, cam, t) for cam, t in zip(cams, targets)]
+    pl = Pipeline(torch.from_numpy(s.params).cuda(), deg, 160, 120)
+    for k, (cam, t, ref, w) in enumerate(zip(cams, targets, refs, weights)):
+        got = _view_grad(torch, gs, pl, cam, torch.from_numpy(t).cuda(), weight=w, accumulate=k > 0,
+                         dLdI=ref["dLdI"])
+    want = sum(w * ref["gparams"].astype(np.float64) for w, ref in zip(weights, refs))
+    tol = sum(w * _view_tolerance(oracle, ref, s.params, deg, cam) for w, ref, cam in zip(weights, refs, cams))
+    keep = np.ones(s.n, bool)
+    for ref in refs:
+        keep &= pu.calm(ref["risk"]["g"], ref["gscreen"])
+    print(f"  views: flips {[r['risk']['flips'] for r in refs]}, Gaussians not calm {int((~keep).sum())} "
+          f"of {s.n}", flush=True)
+    assert keep.mean() > 0.9
+    d = np.abs(got.astype(np.float64) - want)[:, keep]
+    assert (d <= tol[:, keep]).all(), f"{int((d > tol[:, keep]).sum())} elements off, max excess " \
+                                      f"{(d - tol[:, keep]).max()}"
+    for name, sl in pu.grad_groups(deg).items():
+        nb = np.linalg.norm(want[sl][:, keep])
+        assert np.linalg.norm(d[sl]) <= 1e-3 * nb + np.linalg.norm(tol[sl][:, keep] - 1e-3 * np.abs(want[sl][:, keep])), name
+
+
 def test_weighted_and_accumulated_gradients(fixed_sums):
     import torch
-    gs = fixed_sums
+    gs, cfg = fixed_sums
     from differentiable_tile_gaussian_amd.pipeline import Pipeline
     s, cams, targets = _views()
     tg = [torch.from_numpy(t).cuda() for t in targets]
-    pl = Pipeline(torch.from_numpy(s.params).cuda(), 2, 160, 120)
+    pl = Pipeline(torch.from_numpy(s.params).cuda(), 2, 160, 120, cfg=cfg)
     g_a = _view_grad(torch, gs, pl, cams[0], tg[0])
     g_b = _view_grad(torch, gs, pl, cams[1], tg[1])
     assert np.count_nonzero(g_a) > 1000 and np.count_nonzero(g_b) > 1000
@@ -74,16 +126,16 @@ def test_weighted_and_accumulated_gradients(fixed_sums):
 
 def test_step_views_is_one_adam_update_of_the_mean(fixed_sums):
     import torch
-    gs = fixed_sums
+    gs, cfg = fixed_sums
     from differentiable_tile_gaussian_amd.pipeline import Pipeline
     s, cams, targets = _views()
     tg = [torch.from_numpy(t).cuda() for t in targets]
     gcams = [gs.make_camera(c) for c in cams]
-    p1 = Pipeline(torch.from_numpy(s.params).cuda(), 2, 160, 120)
+    p1 = Pipeline(torch.from_numpy(s.params).cuda(), 2, 160, 120, cfg=cfg)
     losses = p1.step_views(gcams, tg)
     torch.cuda.synchronize()
     # the same by hand: the mean gradient, then gs_adam_step
-    p2 = Pipeline(torch.from_numpy(s.params).cuda(), 2, 160, 120)
+    p2 = Pipeline(torch.from_numpy(s.params).cuda(), 2, 160, 120, cfg=cfg)
     g_a = _view_grad(torch, gs, p2, cams[0], tg[0])
     l_a = p2.loss.cpu().numpy().copy()
     g_b = _view_grad(torch, gs, p2, cams[1], tg[1])
@@ -97,3 +149,32 @@ def test_step_views_is_one_adam_update_of_the_mean(fixed_sums):
                                       p2.planar(b).cpu().numpy().view(np.uint32))
     np.testing.assert_array_equal(losses[0].cpu().numpy(), l_a)
     assert np.isfinite(losses.cpu().numpy()).all()
+
+
+def test_position_learning_rate_schedule(fixed_sums):
+    """Pipeline(lr_schedule=...): each fused update uses the rates the schedule gives for
+    its step.  Two fused steps with a decaying means rate end bit for bit where two fused
+    steps end whose constant rates are set by hand to the schedule's before each step,
+    and differ from the constant-rate run in the means only."""
+    import torch
+    gs, cfg = fixed_sums
+    from differentiable_tile_gaussian_amd.pipeline import Pipeline, position_lr_decay, DEFAULT_LR
+    s, cams, targets = _views()
+    tg = [torch.from_numpy(t).cuda() for t in targets]
+    gcams = [gs.make_camera(c) for c in cams]
+    sched = position_lr_decay(1.6e-6, 2)
+    assert sched(1)[0] == pytest.approx(1.6e-4) and sched(2)[0] == pytest.approx(1.6e-6)
+    assert sched(2)[1:] == DEFAULT_LR[1:]
+    runs = {}
+    for name in ("schedule", "by_hand", "constant"):
+        p = Pipeline(torch.from_numpy(s.params).cuda(), 2, 160, 120, cfg=cfg,
+                     lr_schedule=sched if name == "schedule" else None)
+        for k in range(2):
+            if name == "by_hand":
+                p.lr = sched(k + 1)
+            p.step(gcams[k], tg[k])
+        torch.cuda.synchronize()
+        runs[name] = p.planar(p.params).cpu().numpy()
+    np.testing.assert_array_equal(runs["schedule"].view(np.uint32), runs["by_hand"].view(np.uint32))
+    assert not np.array_equal(runs["schedule"][0:3], runs["constant"][0:3])
+    np.testing.assert_array_equal(runs["schedule"][3:].view(np.uint32), runs["constant"][3:].view(np.uint32))
