@@ -304,6 +304,25 @@ int32_t gs_loss_l1_dssim(const float* img, const float* target, int32_t H, int32
   return GS_OK;
 }
 
+int32_t gs_loss_l1_dssim_noalloc(const float* img, const float* target, int32_t H, int32_t W, float lambda_dssim,
+                                 float* loss_out, float* dL_dimg, void* stream) {
+  g_err[0] = 0;
+  if (!img || !target || !loss_out || !dL_dimg) return fail(GS_ERR_INVALID_ARG, "a loss argument is null");
+  if (H <= 0 || W <= 0) return fail(GS_ERR_INVALID_ARG, "image size must be positive");
+  if (int64_t(3) * H * W >= (int64_t(1) << 31)) return fail(GS_ERR_UNSUPPORTED, "image too large");
+  if (!(lambda_dssim >= 0.0f && lambda_dssim <= 1.0f)) return fail(GS_ERR_INVALID_ARG, "lambda must be in [0, 1]");
+  const size_t need = gsk::loss_ws_bytes(H, W);
+  if (need > gsk::loss_scratch_bytes())
+    return fail(GS_ERR_CAPACITY, "a %d x %d image needs %zu bytes of loss scratch; the no-allocation loss has %zu",
+                W, H, need, gsk::loss_scratch_bytes());
+  void* scratch = nullptr;
+  hipError_t e = gsk::loss_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "loss scratch address");
+  e = gsk::launch_loss(img, target, H, W, lambda_dssim, loss_out, dL_dimg, scratch, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "loss");
+  return GS_OK;
+}
+
 static int32_t render_bwd_common(const gs_scene* scene, const gs_proj* proj, const uint32_t* vals,
                                  const uint32_t* ranges, uint32_t total_pairs, const gs_camera* cam,
                                  const float* T_final, const uint32_t* n_contrib, const float* dL_dimg,

@@ -157,6 +157,10 @@ hipError_t launch_render_bwd(const gs_proj& proj, int n, const uint32_t* vals, c
 
 // ---- loss.hip
 size_t loss_ws_bytes(int H, int W);
+// The no-allocation loss's scratch: a file-scope device array of loss_scratch_bytes()
+// bytes; loss_scratch gives its address on the current device (looked up once per device).
+size_t loss_scratch_bytes();
+hipError_t loss_scratch(void** out);
 hipError_t launch_loss(const float* img, const float* target, int H, int W, float lambda, float* loss_out,
                        float* grad, void* ws, hipStream_t s);
 size_t charbonnier_ws_bytes(int H, int W);

@@ -25,6 +25,8 @@
 //                   L1 and mean SSIM
 #include <math.h>
 
+#include <mutex>
+
 #include "gs_internal.h"
 #include "profile.h"
 
@@ -359,6 +361,36 @@ hipError_t launch_charbonnier(const float* img, const float* target, int H, int 
     charbonnier_finalize_kernel<<<1, 256, 0, s>>>(partial, nb, 1.0 / double(count), loss_out, dexp);
   }
   return hipGetLastError();
+}
+
+// Scratch of the no-allocation entry point (gs_loss_l1_dssim_noalloc): the loss's
+// per-block partial sums live in this array, one copy per GPU that the library runs on,
+// held until the process ends.  Host code must not pass the array's name to a kernel (on
+// the host it is a stand-in, not a device address): loss_scratch() looks its device
+// address up once per device and keeps it.  Every partial is written by the loss kernel
+// before the finalize kernel reads it, so nothing needs clearing between calls; calls
+// that overlap on one GPU share the array and race.
+constexpr size_t kLossScratchBytes = size_t(256) << 10;
+static __device__ __align__(256) unsigned char scratch[kLossScratchBytes];
+
+size_t loss_scratch_bytes() { return kLossScratchBytes; }
+
+hipError_t loss_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
 }
 
 size_t loss_ws_bytes(int H, int W) {

@@ -24,7 +24,7 @@ GS_GRAD_SUMS_FLOAT, GS_GRAD_SUMS_FIXED = 0, 1
 EXPORTED = ("gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss_l1_dssim", "gs_render_bwd",
             "gs_adam_step", "gs_render_bwd_adam", "gs_render_bwd_adam_project", "gs_render_bwd_weighted",
             "gs_camera_grad", "gs_densify_accumulate", "gs_densify", "gs_relocate", "gs_loss_charbonnier",
-            "gs_workspace_bytes", "gs_profile_enable", "gs_profile_query", "gs_param_floats", "gs_params_to_blocked",
+            "gs_workspace_bytes", "gs_loss_l1_dssim_noalloc", "gs_profile_enable", "gs_profile_query", "gs_param_floats", "gs_params_to_blocked",
             "gs_params_from_blocked", "gs_last_error")
 
 
@@ -82,6 +82,8 @@ def _load():
                                                C.c_double, C.c_double, I32, P, C.c_size_t, P, P, P, P, C.c_size_t,
                                                P, P, P]
     lib.gs_render_bwd_adam_project.restype = I32
+    lib.gs_loss_l1_dssim_noalloc.argtypes = [P, P, I32, I32, C.c_float, P, P, P]
+    lib.gs_loss_l1_dssim_noalloc.restype = I32
     lib.gs_loss_charbonnier.argtypes = [P, P, I32, I32, C.c_float, P, P, P, P, P, C.c_size_t, P]
     lib.gs_loss_charbonnier.restype = I32
     lib.gs_render_bwd_weighted.argtypes = [P, P, P, P, U32, P, P, P, P, P, P, C.c_float, I32, P, C.c_size_t, P, P]
@@ -244,6 +246,13 @@ def gs_loss_l1_dssim(img, target, lambda_dssim, loss_out, dL_dimg, ws, stream=No
     _, H, W = img.shape
     _check(_lib.gs_loss_l1_dssim(_ptr(img), _ptr(target), H, W, float(lambda_dssim), _ptr(loss_out),
                                  _ptr(dL_dimg), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def gs_loss_l1_dssim_noalloc(img, target, lambda_dssim, loss_out, dL_dimg, stream=None):
+    """gs_loss_l1_dssim without a workspace: the library's static scratch (no allocation)."""
+    _, H, W = img.shape
+    _check(_lib.gs_loss_l1_dssim_noalloc(_ptr(img), _ptr(target), H, W, float(lambda_dssim), _ptr(loss_out),
+                                         _ptr(dL_dimg), _stream(stream)))
 
 
 def gs_render_bwd(params, sh_degree, proj: Proj, vals, ranges, total_pairs, cam: GsCamera, T_final, n_contrib, dL_dimg,

@@ -222,6 +222,17 @@ int32_t gs_render_fwd(const gs_proj* proj, int64_t n, const uint32_t* vals, cons
 int32_t gs_loss_l1_dssim(const float* img, const float* target, int32_t H, int32_t W, float lambda_dssim,
                          float* loss_out, float* dL_dimg, void* ws, size_t ws_bytes, void* stream);
 
+/* gs_loss_l1_dssim for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same loss and image
+ * gradient, bit for bit, with the per-block partial sums in a static device array of the
+ * library (256 KiB per GPU, held until the process ends) instead of a workspace argument.
+ * Calls no allocator.  GS_ERR_CAPACITY for an image whose partial sums do not fit, i.e.
+ * gs_workspace_bytes(GS_WS_LOSS, 0, 0, W, H, NULL) > 256 KiB (about 6000 x 6000 pixels is
+ * the largest square that fits); other errors as gs_loss_l1_dssim.  Calls that overlap on
+ * one GPU (other streams, other host threads) share that array and race: serialise them. */
+int32_t gs_loss_l1_dssim_noalloc(const float* img, const float* target, int32_t H, int32_t W, float lambda_dssim,
+                                 float* loss_out, float* dL_dimg, void* stream);
+
 /* The trainer's other loss: Charbonnier with per-image exposure ([GSG] the loss code after
  * "The painting itself"; "Forgiving the camera and the light").  Per element
  *   err = gain img + bias - target,  root = sqrt(err^2 + delta^2),
