@@ -668,8 +668,11 @@ void chain_one(const R* params, int64_t n, int64_t i, int deg, const Camera& cam
 // Gaussian window of standard deviation 1.5, C1 = 0.01^2, C2 = 0.03^2, zero padding,
 // SSIM averaged over windows and channels); [LAB] combined objective.
 // Written as the direct 2-D windowed sums (no separable pass) and their adjoint.
+// mag (optional, [3][H][W]): per element, the sum of the magnitudes of the SSIM terms its
+// gradient adds up (each window's three derivative terms, factor by factor), the scale of
+// what a reordered or differently rounded evaluation of that gradient can change.
 template <class R>
-void loss_l1_dssim(const R* img, const R* tgt, int H, int W, R lambda, R out[3], R* grad) {
+void loss_l1_dssim(const R* img, const R* tgt, int H, int W, R lambda, R out[3], R* grad, double* mag = nullptr) {
   const int rad = 5;
   const double sigma = 1.5;
   double wsum = 0.0;
@@ -724,6 +727,7 @@ void loss_l1_dssim(const R* img, const R* tgt, int H, int W, R lambda, R out[3],
   for (int64_t k = 0; k < NE; ++k) {
     const R r = img[k] - tgt[k];
     grad[k] = (R(1) - lambda) * inv * (r > R(0) ? R(1) : (r < R(0) ? R(-1) : R(0)));
+    if (mag) mag[k] = 0.0;
   }
   // adjoint of the windowed sums: pixel q receives from every window centre p within reach
   for (int ch = 0; ch < 3; ++ch) {
@@ -741,6 +745,12 @@ void loss_l1_dssim(const R* img, const R* tgt, int H, int W, R lambda, R out[3],
             const R dS = dmu[p] * wt + dsx[p] * (R(2) * X[q] * wt - R(2) * mux[p] * wt) +
                          dsxy[p] * (Y[q] * wt - muy[p] * wt);
             grad[ch * HW + q] += -lambda * inv * dS;
+            if (mag) {
+              const double a = std::fabs(double(dmu[p])) + std::fabs(double(dsx[p])) * 2.0 *
+                               (std::fabs(double(X[q])) + std::fabs(double(mux[p]))) +
+                               std::fabs(double(dsxy[p])) * (std::fabs(double(Y[q])) + std::fabs(double(muy[p])));
+              mag[ch * HW + q] += std::fabs(double(lambda) * double(inv)) * double(wt) * a;
+            }
           }
       }
   }
@@ -1197,10 +1207,22 @@ void or_render_bwd_f64(int64_t n, const double* uv, const double* conic, const d
 //   nc_lo, nc_hi [H][W] the range of last-entry counts the flips produce (the
 //                       unflipped count included);
 //   grisk [9][n]        absolute change of each Gaussian's nine screen partials.
-// Pixels with no such decision add nothing.  Returns the number of flips taken.
+// Pixels with no such decision add nothing.  Optional (nullable): nflip [H][W], the
+// number of decisions taken the other way at the pixel, and alt_rgb [3][H][W], alt_T,
+// alt_nc [H][W], the pixel's colour, T and last-entry count with its last such decision
+// taken the other way (the only one where nflip is 1).
+// Optional obs_rgb [3][H][W], obs_T, obs_nc [H][W]: a render to be checked (another
+// evaluation's forward).  Then grisk leaves out each flip that render rules out: at a
+// pixel whose observed colour and T are within obs_atol of this walk's and whose count
+// is this walk's, a flip that would move the colour or T by more than 2 obs_atol or
+// change the count was not taken there.  (A cap flip never shows in the forward and is
+// always kept.)  px_risk, nc_lo, nc_hi and the flip count are unchanged by this.
+// Returns the number of flips taken.
 int64_t or_flip_risk_f32(int64_t n, const float* uv, const float* conic, const float* opac, const float* rgb,
                          const uint32_t* vals, const uint32_t* ranges, const Camera* cam, const float* dLdI,
-                         double below, float* px_risk, uint32_t* nc_lo, uint32_t* nc_hi, float* grisk) {
+                         double below, float* px_risk, uint32_t* nc_lo, uint32_t* nc_hi, float* grisk,
+                         uint32_t* nflip, float* alt_rgb, float* alt_T, uint32_t* alt_nc, const float* obs_rgb,
+                         const float* obs_T, const uint32_t* obs_nc, double obs_atol) {
   const int W = cam->width, H = cam->height, tx = tiles_x(*cam), ty = tiles_y(*cam);
   const int64_t nt = int64_t(tx) * ty, HW = int64_t(W) * H;
   const float bg[3] = {cam->bg[0], cam->bg[1], cam->bg[2]};
@@ -1223,9 +1245,19 @@ int64_t or_flip_risk_f32(int64_t n, const float* uv, const float* conic, const f
                          &close, below);
       px_risk[p] = px_risk[HW + p] = 0.0f;
       nc_lo[p] = nc_hi[p] = tr.n_contrib;
+      if (nflip) nflip[p] = uint32_t(close.size());
+      if (alt_rgb)
+        for (int ch = 0; ch < 3; ++ch) alt_rgb[ch * HW + p] = out[ch];
+      if (alt_T) alt_T[p] = T;
+      if (alt_nc) alt_nc[p] = tr.n_contrib;
       if (close.empty()) continue;
       const float gI[3] = {dLdI[p], dLdI[HW + p], dLdI[2 * HW + p]};
       blend_pixel_bwd<float>(px, py, list, tr.n_contrib, uv, conic, opac, rgb, n, bg, false, T, gI, g0.data());
+      // does the observed render show this walk's outcome at the pixel?
+      bool matched = obs_rgb != nullptr && obs_nc[p] == tr.n_contrib &&
+                     std::fabs(double(obs_T[p]) - double(T)) <= obs_atol;
+      for (int ch = 0; matched && ch < 3; ++ch)
+        matched = std::fabs(double(obs_rgb[ch * HW + p]) - double(out[ch])) <= obs_atol;
       for (const Decision& f : close) {
         float out1[3], T1;
         PixelTrace tr1;
@@ -1234,6 +1266,14 @@ int64_t or_flip_risk_f32(int64_t n, const float* uv, const float* conic, const f
         for (int ch = 0; ch < 3; ++ch) dc = std::max(dc, std::fabs(out1[ch] - out[ch]));
         px_risk[p] += dc;
         px_risk[HW + p] += std::fabs(T1 - T);
+        const bool visible = f.kind != kDecCap && (double(dc) > 2.0 * obs_atol ||
+                                                   std::fabs(double(T1) - double(T)) > 2.0 * obs_atol ||
+                                                   tr1.n_contrib != tr.n_contrib);
+        const bool ruled_out = matched && visible;
+        if (alt_rgb)
+          for (int ch = 0; ch < 3; ++ch) alt_rgb[ch * HW + p] = out1[ch];
+        if (alt_T) alt_T[p] = T1;
+        if (alt_nc) alt_nc[p] = tr1.n_contrib;
         nc_lo[p] = std::min(nc_lo[p], tr1.n_contrib);
         nc_hi[p] = std::max(nc_hi[p], tr1.n_contrib);
         blend_pixel_bwd<float>(px, py, list, tr1.n_contrib, uv, conic, opac, rgb, n, bg, false, T1, gI, g1.data(),
@@ -1242,7 +1282,7 @@ int64_t or_flip_risk_f32(int64_t n, const float* uv, const float* conic, const f
         for (uint32_t j = 0; j < upto; ++j)
           for (int c = 0; c < 9; ++c) {
             const size_t o = size_t(c) * n + list[j];
-            grisk[o] += std::fabs(g1[o] - g0[o]);
+            if (!ruled_out) grisk[o] += std::fabs(g1[o] - g0[o]);
             g1[o] = 0.0f;
           }
         ++flips;
@@ -1312,8 +1352,8 @@ OR_CAMERA_GRAD(float, f32)
 OR_CAMERA_GRAD(double, f64)
 
 #define OR_LOSS(R, SUF)                                                                                      \
-  void or_loss_##SUF(const R* img, const R* tgt, int H, int W, R lambda, R* out3, R* grad) {                  \
-    loss_l1_dssim<R>(img, tgt, H, W, lambda, out3, grad);                                                    \
+  void or_loss_##SUF(const R* img, const R* tgt, int H, int W, R lambda, R* out3, R* grad, double* mag) {     \
+    loss_l1_dssim<R>(img, tgt, H, W, lambda, out3, grad, mag);                                               \
   }
 OR_LOSS(float, f32)
 OR_LOSS(double, f64)

@@ -74,8 +74,8 @@ def _declare(L):
         getattr(L, f"or_preprocess_bwd_{suf}").argtypes = [I64, I32, P, P, I32, P, P]
         getattr(L, f"or_adam_{suf}").argtypes = [P, P, P, P, I64, I32, P, C.c_double, C.c_double,
                                                  C.c_double, I32]
-    L.or_loss_f32.argtypes = [P, P, I32, I32, C.c_float, P, P]
-    L.or_loss_f64.argtypes = [P, P, I32, I32, C.c_double, P, P]
+    L.or_loss_f32.argtypes = [P, P, I32, I32, C.c_float, P, P, P]
+    L.or_loss_f64.argtypes = [P, P, I32, I32, C.c_double, P, P, P]
     L.or_bin_sort.argtypes = [I64, P, P, P, I32, I32, P, P, P]
     L.or_render_fwd_f32.argtypes = [I64] + [P] * 6 + [P] + [P] * 5
     L.or_render_fwd_f32.restype = I64
@@ -85,7 +85,8 @@ def _declare(L):
     L.or_render_pixels_f32.argtypes = [I64] + [P] * 6 + [P, I64, P, P, P, P, P, P]
     L.or_render_bwd_f32.argtypes = [I64] + [P] * 6 + [P] + [P] * 6
     L.or_render_bwd_f64.argtypes = [I64] + [P] * 6 + [P] + [P] * 4
-    L.or_flip_risk_f32.argtypes = [I64] + [P] * 6 + [P, P, C.c_double, P, P, P, P]
+    L.or_flip_risk_f32.argtypes = [I64] + [P] * 6 + [P, P, C.c_double, P, P, P, P, P, P, P, P, P, P, P,
+                                                     C.c_double]
     L.or_flip_risk_f32.restype = I64
     L.or_densify_accumulate_f32.argtypes = [I64, P, P, P]
     L.or_loss_charbonnier_f32.argtypes = [P, P, I64, C.c_float, C.c_float, C.c_float, P, P]
@@ -289,19 +290,30 @@ def rounding_slack(mass, count):
 RISK_BELOW = 1e-5
 
 
-def flip_risk(pre, vals, ranges, cam, dLdI, below=RISK_BELOW):
+def flip_risk(pre, vals, ranges, cam, dLdI, below=RISK_BELOW, observed=None, obs_atol=1e-5):
     """How much an fp32 evaluation other than the oracle's could move each output:
     px [2][H][W] (colour, largest channel; T), nc_lo / nc_hi [H][W] (range of
-    n_contrib), g [9][n] (screen partials), and the number of flips taken."""
+    n_contrib), g [9][n] (screen partials), and the number of flips taken.  Per pixel
+    also nflip [H][W] (its decisions near a threshold) and alt_rgb [3][H][W], alt_T,
+    alt_nc [H][W]: the pixel with its (last) near decision taken the other way, which
+    is the pixel's one alternative where nflip is 1.  With observed (a dict with rgb, T,
+    n_contrib of another evaluation's forward), g leaves out the flips that render shows
+    were not taken (see or_flip_risk_f32)."""
     n = pre["n"]
     H, W = cam.height, cam.width
     out = dict(px=np.zeros((2, H, W), np.float32), nc_lo=np.zeros((H, W), np.uint32),
-               nc_hi=np.zeros((H, W), np.uint32), g=np.zeros((9, n), np.float32))
+               nc_hi=np.zeros((H, W), np.uint32), g=np.zeros((9, n), np.float32),
+               nflip=np.zeros((H, W), np.uint32), alt_rgb=np.zeros((3, H, W), np.float32),
+               alt_T=np.zeros((H, W), np.float32), alt_nc=np.zeros((H, W), np.uint32))
     c = make_camera(cam)
     out["flips"] = int(lib().or_flip_risk_f32(
         n, _p(pre["uv"]), _p(pre["conic"]), _p(pre["opac"]), _p(pre["rgb"]), _p(_c(vals, np.uint32)),
         _p(_c(ranges, np.uint32)), C.byref(c), _p(_c(dLdI, np.float32)), float(below), _p(out["px"]),
-        _p(out["nc_lo"]), _p(out["nc_hi"]), _p(out["g"])))
+        _p(out["nc_lo"]), _p(out["nc_hi"]), _p(out["g"]), _p(out["nflip"]), _p(out["alt_rgb"]),
+        _p(out["alt_T"]), _p(out["alt_nc"]),
+        _p(_c(observed["rgb"], np.float32)) if observed is not None else None,
+        _p(_c(observed["T"], np.float32)) if observed is not None else None,
+        _p(_c(observed["n_contrib"], np.uint32)) if observed is not None else None, float(obs_atol)))
     return out
 
 
@@ -343,16 +355,19 @@ def smooth_grad(params, sh_degree, cam, dLdI, dtype=np.float64):
 
 
 # -------------------------------------------------------------------- loss
-def loss(img, tgt, lam=0.2, dtype=np.float64, with_grad=True):
-    """0.8 L1 + 0.2 (1 - SSIM); returns ((total, L1, SSIM), dL/dimg)."""
+def loss(img, tgt, lam=0.2, dtype=np.float64, with_grad=True, with_mag=False):
+    """0.8 L1 + 0.2 (1 - SSIM); returns ((total, L1, SSIM), dL/dimg), and with with_mag
+    also the per-element magnitude of the SSIM terms the gradient sums ([3][H][W])."""
     img = _c(img, dtype)
     tgt = _c(tgt, dtype)
     _, H, W = img.shape
     out = np.zeros(3, dtype)
-    grad = np.zeros_like(img) if with_grad else None
+    grad = np.zeros_like(img) if (with_grad or with_mag) else None
+    mag = np.zeros(img.shape, np.float64) if with_mag else None
     fn = lib().or_loss_f64 if dtype == np.float64 else lib().or_loss_f32
-    fn(_p(img), _p(tgt), H, W, lam, _p(out), _p(grad))
-    return tuple(float(x) for x in out), grad
+    fn(_p(img), _p(tgt), H, W, lam, _p(out), _p(grad), _p(mag))
+    terms = tuple(float(x) for x in out)
+    return (terms, grad, mag) if with_mag else (terms, grad)
 
 
 # -------------------------------------------------------------------- Adam

@@ -61,6 +61,7 @@ def test_fixed_sums_match_oracle(fixed_mode, oracle, case):
     _, mass, count = oracle.render_bwd(o["pre"], o["vals"], o["ranges"], cam, o["fwd"], dLdI, with_mass=True)
     o["slack"] = o["slack"] + quantisation_slack(o["pre"], count, w, h)
     pl, c = pu.gpu_forward(s.params, deg, cam, cfg)
+    o["risk"] = pu.observed_risk(oracle, o, cam, pu.render_to_numpy(pl), dLdI)
     pl.dLdI.copy_(torch.from_numpy(dLdI))
     gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI, pl.gscreen,
                      pl.grads, pl.ws_render, cfg=cfg)

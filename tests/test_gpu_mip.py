@@ -45,6 +45,7 @@ def test_mip_forward_and_backward(mip_on, oracle, case):
     plain = 1.0 / (1.0 + np.exp(-s.params[10].astype(np.float64)))
     assert (o["pre"]["opac"][vis] / plain[vis]).min() < 0.8          # the factor matters here
     pl, c = pu.gpu_forward(s.params, deg, cam, cfg)
+    o["risk"] = pu.observed_risk(oracle, o, cam, pu.render_to_numpy(pl), dLdI)
     pu.check_preprocess(pu.proj_to_numpy(pl), o["pre"])
     keys, vals, ranges = pu.sorted_to_numpy(pl)
     np.testing.assert_array_equal(keys, pu.tile_of_key(o["keys"]))

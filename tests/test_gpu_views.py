@@ -89,6 +89,7 @@ def test_weighted_views_against_the_oracle(oracle):
     for k, (cam, t, ref, w) in enumerate(zip(cams, targets, refs, weights)):
         got = _view_grad(torch, gs, pl, cam, torch.from_numpy(t).cuda(), weight=w, accumulate=k > 0,
                          dLdI=ref["dLdI"])
+        ref["risk"] = pu.observed_risk(oracle, ref, cam, pu.render_to_numpy(pl), ref["dLdI"])
     want = sum(w * ref["gparams"].astype(np.float64) for w, ref in zip(weights, refs))
     tol = sum(w * _view_tolerance(oracle, ref, s.params, deg, cam) for w, ref, cam in zip(weights, refs, cams))
     keep = np.ones(s.n, bool)

@@ -71,6 +71,11 @@ def test_skip_flip_equals_nudged_render(oracle):
     assert d > 1e-4                                     # the nudge really changes the pixel
     np.testing.assert_allclose(risk["px"][0, 0, 0], d, rtol=1e-3)
     np.testing.assert_allclose(risk["px"][1, 0, 0], abs(fwd1["T"][0, 0] - fwd0["T"][0, 0]), rtol=1e-3)
+    # one near decision at the pixel; its alternative outcome is the nudged render
+    assert risk["nflip"][0, 0] == 1
+    np.testing.assert_allclose(risk["alt_rgb"][:, 0, 0], fwd1["rgb"][:, 0, 0], rtol=0, atol=1e-6)
+    np.testing.assert_allclose(risk["alt_T"][0, 0], fwd1["T"][0, 0], rtol=1e-5)
+    assert risk["alt_nc"][0, 0] == fwd1["n_contrib"][0, 0]
     # pixel (0, 0) is the only one the nudge changes; all three Gaussians' partials move there
     other = np.ones((cam.height, cam.width), bool)
     other[0, 0] = False
@@ -79,6 +84,13 @@ def test_skip_flip_equals_nudged_render(oracle):
     # the flip moves exactly these amounts, up to the alpha difference of the two opacities
     np.testing.assert_allclose(risk["g"], dg, rtol=2e-3, atol=1e-9)
     assert dg[5, 1] > 0 and dg[5, 2] > 0
+    # an observed render that shows the unflipped outcome rules the (visible) flip out of
+    # the gradient risk; one that shows the flipped outcome keeps it
+    pre, keys, vals, ranges, _ = oracle.forward(scene(logits[below]), 0, cam)
+    seen0 = oracle.flip_risk(pre, vals, ranges, cam, _dLdI(cam), observed=fwd0)
+    seen1 = oracle.flip_risk(pre, vals, ranges, cam, _dLdI(cam), observed=fwd1)
+    assert np.all(seen0["g"] == 0) and np.array_equal(seen0["px"], risk["px"])
+    np.testing.assert_array_equal(seen1["g"], risk["g"])
 
 
 def test_stop_flip_equals_nudged_render(oracle):
@@ -112,6 +124,12 @@ def test_stop_flip_equals_nudged_render(oracle):
     assert risk["nc_lo"][0, 0] == 3 and risk["nc_hi"][0, 0] == 4
     d = np.abs(fwd1["rgb"][:, 0, 0] - fwd0["rgb"][:, 0, 0]).max()
     np.testing.assert_allclose(risk["px"][0, 0, 0], d, rtol=1e-2)
+    assert risk["nflip"][0, 0] == 1 and risk["alt_nc"][0, 0] == 3
+    np.testing.assert_allclose(risk["alt_rgb"][:, 0, 0], fwd1["rgb"][:, 0, 0], rtol=0, atol=1e-6)
+    # pixels without a near decision carry their own render as the alternative
+    quiet = risk["nflip"] == 0
+    assert np.array_equal(risk["alt_rgb"][:, quiet], fwd0["rgb"][:, quiet])
+    assert np.array_equal(risk["alt_nc"][quiet], fwd0["n_contrib"][quiet])
     dg = np.abs(gs1 - gs0).astype(np.float64)
     # the fourth entry's partials appear or vanish; the rest move by the nudge's alpha change
     np.testing.assert_allclose(risk["g"][:, 3], dg[:, 3], rtol=1e-2, atol=1e-12)
@@ -143,6 +161,10 @@ def test_cap_flip_equals_nudged_gradient(oracle):
     np.testing.assert_allclose(risk["g"][5, 0], abs(gs1[5, 0] - gs0[5, 0]), rtol=1e-3)
     # on the axis the position and conic partials vanish at that pixel
     assert np.all(risk["g"][0:5, 0] == 0)
+    # a cap flip never shows in the forward: an observed render cannot rule it out
+    pre, keys, vals, ranges, _ = oracle.forward(scene(logits[over]), 0, cam)
+    seen = oracle.flip_risk(pre, vals, ranges, cam, _dLdI(cam), observed=fwd0)
+    np.testing.assert_array_equal(seen["g"], risk["g"])
 
 
 def test_rounding_slack_bounds_fp32_against_fp64(oracle):
