@@ -553,8 +553,8 @@ __global__ void __launch_bounds__(256) split_combine_kernel(SplitWs ws) {
       stop = 0;
     } else {
       stop = int32_t(nch);
-      // chunks in groups of eight: their partials are loaded before they are chained
-      constexpr int kG = 8;
+      // chunks in groups of sixteen: their partials are loaded before they are chained
+      constexpr int kG = 16;
       for (uint32_t c0g = 1; c0g < nch && stop == int32_t(nch); c0g += kG) {
         float4 pc[kG];
         uint32_t lc[kG];
@@ -569,17 +569,18 @@ __global__ void __launch_bounds__(256) split_combine_kernel(SplitWs ws) {
 #pragma unroll
         for (int k = 0; k < kG; ++k) {
           const uint32_t c = c0g + k;
-          if (c >= nch || stop != int32_t(nch)) break;
-          const float Tn = T * pc[k].x;
-          if (Tn < kTStop) {
-            stop = int32_t(c);
-            break;
+          if (c < nch && stop == int32_t(nch)) {
+            const float Tn = T * pc[k].x;
+            if (Tn < kTStop) {
+              stop = int32_t(c);
+            } else {
+              const float a0 = T * pc[k].y, a1 = T * pc[k].z, a2 = T * pc[k].w;
+              ws.part4[size_t(fi + c) * 256 + tid] = make_float4(Tn, a0, a1, a2);   // T at the chunk end, colour it added
+              c0 += a0; c1 += a1; c2 += a2;
+              T = Tn;
+              if (lc[k]) last = lc[k];
+            }
           }
-          const float a0 = T * pc[k].y, a1 = T * pc[k].z, a2 = T * pc[k].w;
-          ws.part4[size_t(fi + c) * 256 + tid] = make_float4(Tn, a0, a1, a2);   // T at the chunk end, colour it added
-          c0 += a0; c1 += a1; c2 += a2;
-          T = Tn;
-          if (lc[k]) last = lc[k];
         }
       }
     }
@@ -662,8 +663,8 @@ __global__ void __launch_bounds__(256) split_finalize_kernel(SplitWs ws, int tx,
   } else {
     c = int(nch);
   }
-  // chunks c - 1 .. 0, back to front, in groups of eight loaded ahead
-  constexpr int kG = 8;
+  // chunks c - 1 .. 0, back to front, in groups of sixteen loaded ahead
+  constexpr int kG = 16;
   for (int top = c - 1; top >= 0; top -= kG) {
     float4 pc[kG];
 #pragma unroll
@@ -671,9 +672,10 @@ __global__ void __launch_bounds__(256) split_finalize_kernel(SplitWs ws, int tx,
       if (top - k >= 0) pc[k] = ws.part4[size_t(fi + uint32_t(top - k)) * 256 + tid];
 #pragma unroll
     for (int k = 0; k < kG; ++k) {
-      if (top - k < 0) break;
-      ws.part4[size_t(fi + uint32_t(top - k)) * 256 + tid] = make_float4(pc[k].x, S0, S1, S2);
-      S0 += pc[k].y; S1 += pc[k].z; S2 += pc[k].w;
+      if (top - k >= 0) {
+        ws.part4[size_t(fi + uint32_t(top - k)) * 256 + tid] = make_float4(pc[k].x, S0, S1, S2);
+        S0 += pc[k].y; S1 += pc[k].z; S2 += pc[k].w;
+      }
     }
   }
   ws.bnd1[so] = make_float4(ws.st4[so].x, S0, S1, S2);
