@@ -132,7 +132,7 @@ PreWs carve_pre(void* ws, int64_t n) {
 
 // The part of gs_preprocess after the projection kernels: the pair count to the host
 // while the depth order is computed.
-int32_t finish_preprocess(gs_proj* out, int n, const PreWs& w, uint32_t* total_pairs, hipStream_t s);
+int32_t finish_preprocess(gs_proj* out, int n, float znear, const PreWs& w, uint32_t* total_pairs, hipStream_t s);
 
 // Pinned host word the pair count is copied into, and the event that marks the copy,
 // one per device and host thread, created on first use and kept for the process.
@@ -215,14 +215,14 @@ int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out,
   hipError_t e = gsk::launch_preprocess_fwd(scene->params, n, scene->sh_degree, *cam, *out, w.block_tiles,
                                             w.total64, shade_of(scene->sh_degree, c), s);
   if (e != hipSuccess) return hip_fail(e, "preprocess_fwd");
-  return finish_preprocess(out, n, w, total_pairs, s);
+  return finish_preprocess(out, n, cam->znear, w, total_pairs, s);
 }
 
 }  // extern "C"
 
 namespace {
 
-int32_t finish_preprocess(gs_proj* out, int n, const PreWs& w, uint32_t* total_pairs, hipStream_t s) {
+int32_t finish_preprocess(gs_proj* out, int n, float znear, const PreWs& w, uint32_t* total_pairs, hipStream_t s) {
   hipError_t e;
   // the pair count goes to the host while the depth order is computed
   HostSlot* hs = host_slot();
@@ -235,7 +235,7 @@ int32_t finish_preprocess(gs_proj* out, int n, const PreWs& w, uint32_t* total_p
   }
   e = hipEventRecord(hs->copied, s);
   if (e != hipSuccess) return hip_fail(e, "pair count event");
-  e = gsk::launch_depth_order(*out, n, w.depth_ws, s);
+  e = gsk::launch_depth_order(*out, n, znear, w.depth_ws, s);
   if (e != hipSuccess) return hip_fail(e, "depth order");
   e = hipEventSynchronize(hs->copied);
   if (e != hipSuccess) return hip_fail(e, "preprocess sync");
@@ -496,7 +496,7 @@ int32_t gs_render_bwd_adam_project(float* params, int64_t n, int32_t sh_degree, 
                                      adam_args(lr, beta1, beta2, eps, step), np, densify_stats,
                                      shade_of(sh_degree, c), s);
   if (e != hipSuccess) return hip_fail(e, "chain_adam_project");
-  return finish_preprocess(next_out, int(n), w, next_total_pairs, s);
+  return finish_preprocess(next_out, int(n), next_cam->znear, w, next_total_pairs, s);
 }
 
 int32_t gs_adam_step(float* params, const float* grads, float* m, float* v, int64_t n, int32_t sh_degree,

@@ -84,9 +84,10 @@ hipError_t launch_scan_u32(const uint32_t* in, uint32_t* out, int64_t n, uint64_
 
 // ---- sort.hip
 // depth order of the visible Gaussians (proj.order, proj.n_visible) and the pair
-// offsets in that order (proj.offs); then emission and the tile sort of the pairs
+// offsets in that order (proj.offs), for a projection whose visible Gaussians all have
+// depth > znear > 0; then emission and the tile sort of the pairs
 size_t depth_order_ws_bytes(int64_t n);
-hipError_t launch_depth_order(const gs_proj& proj, int n, void* ws, hipStream_t s);
+hipError_t launch_depth_order(const gs_proj& proj, int n, float znear, void* ws, hipStream_t s);
 size_t bin_sort_ws_bytes(uint32_t pairs);
 // Stable ascending sort of count (key, value) pairs by the 32-bit key, in place (the
 // hand-written radix passes of the binning); ws: sort_pairs_ws_bytes(capacity) bytes,

@@ -3,28 +3,38 @@
 // tile, then depth, then Gaussian id, built in three steps:
 //
 //   depth sort    the visible Gaussians (tile count > 0), in id order, are sorted by
-//                 the bits of their (positive) depth with a stable LSD radix sort;
-//                 the first pass also compacts them, so later passes only see the
-//                 visible ones.  Result: visible Gaussian ids by (depth, id).
+//                 d = bits(depth) - bits(znear) with a stable LSD radix sort: positive
+//                 floats order as their bit patterns, and every visible depth exceeds
+//                 znear > 0, so d orders the depths and is below 2^31.  The first pass
+//                 also compacts the visible Gaussians and takes the maximum of d.  Three
+//                 9-bit passes cover d < 2^27 (depths up to 2^27 ulps above znear:
+//                 about 13000 at znear 0.2); a fourth runs only when some d is larger,
+//                 its launches returning at once otherwise.  The device picks every
+//                 pass's buffers from that count, so that the last pass lands in the
+//                 order array; it also gathers each Gaussian's tile rectangle and count.
 //   emit          their tile counts, in that order, are prefix-summed; one thread
 //                 per pair finds its Gaussian by binary search in the sums and
 //                 writes (tile id, Gaussian id): the pairs of each Gaussian are
-//                 consecutive and the Gaussians are in (depth, id) order.
+//                 consecutive and the Gaussians are in (depth, id) order.  Each block
+//                 of 4096 pairs also counts the first tile digit: the histogram of the
+//                 first tile pass.
 //   tile sort     a stable LSD radix sort of the pairs by tile id, so within a
 //                 tile they keep the (depth, id) order.
 //   tile_ranges   first / one-past-last pair of each tile.
 //
-// Radix passes use 8-bit digits, reduce-then-scan:
-//   upsweep   per-block digit histogram (LDS atomics)
-//   scan      exclusive prefix over the digit-major [256][blocks] table
-//   downsweep each wave ranks its 1024 consecutive items against a wave-private digit
-//             histogram (64-lane ballots: no match-any on CDNA, 8 ballots give each
-//             lane its peer mask), one barrier turns the four histograms into run
-//             starts, then a local reorder through LDS and a coalesced scatter.
+// Radix passes use 9-bit digits, reduce-then-scan:
+//   upsweep   per-block digit histogram (LDS atomics) into a digit-major [512][blocks] table
+//   scan      one block per digit: exclusive prefix along its row, and the row total
+//   downsweep the digit bases from the 512 row totals; each wave ranks its 1024
+//             consecutive items against a wave-private digit histogram (64-lane
+//             ballots: no match-any on CDNA, 9 ballots give each lane its peer mask),
+//             one barrier turns the four histograms into run starts, then a local
+//             reorder through LDS and a coalesced scatter.
 // Sorting the Gaussians by depth once, instead of every pair by a 64-bit (tile, depth)
-// key, replaces six passes over 12-byte pairs by four passes over the visible
+// key, replaces six passes over 12-byte pairs by three passes over the visible
 // Gaussians (about 40 % of them at the orbit cameras) and two over 8-byte pairs.
 #include <algorithm>
+#include <cstring>
 
 #include "gs_internal.h"
 #include "profile.h"
@@ -33,15 +43,18 @@ namespace gsk {
 namespace {
 
 constexpr int kSortThreads = 256;
+constexpr int kWaves = kSortThreads / 64;
 constexpr int kSortItems = 16;
 constexpr int kSortTile = kSortThreads * kSortItems;   // 4096 items per block
-constexpr int kRadix = 256;
-constexpr int kDepthPasses = 4;                         // 31 significant bits of a positive float
+constexpr int kDigitBits = 9;
+constexpr int kRadix = 1 << kDigitBits;                 // 512 digits
+constexpr int kDepthPasses = 3;                         // always made: d < 2^27
+constexpr int kDepthPassesMax = 4;                      // 36 bits >= the 31 of d
 
 // Where a radix pass reads its items from.
 enum Source {
   kFromKeys = 0,      // keys[idx], vals[idx], idx < count (count on the device if count_dev)
-  kFromDepth = 1      // depth bits of Gaussian idx, value idx; only Gaussians with tiles[idx] > 0
+  kFromDepth = 1      // d of Gaussian idx, value idx; only Gaussians with tiles[idx] > 0
 };
 
 struct PassIn {
@@ -49,129 +62,300 @@ struct PassIn {
   const uint32_t* vals;
   const float* depth;
   const uint32_t* tiles;
+  uint32_t key_base;   // kFromDepth: the bits of znear
   uint32_t count;
   const uint32_t* count_dev;
 };
 
+// The depth sort's passes: pass p of np (3, or 4 when *dmax >= 2^27) writes buffer set
+// (np - 1 - p) even ? 1 : 0 and reads the other set (p >= 1), so the last pass writes
+// set 1, whose values array is the order array.  pass < 0: an ordinary pass with fixed
+// buffers.
+struct DepthPlan {
+  uint32_t* k[2];
+  uint32_t* v[2];
+  uint32_t* bmax;   // pass 0: each block's maximum of d (0 without visible Gaussians)
+  uint32_t* dmax;   // their maximum, stored by the first pass's scan
+  int pass;
+};
+
+constexpr DepthPlan kNoPlan{{nullptr, nullptr}, {nullptr, nullptr}, nullptr, nullptr, -1};
+
+__device__ inline int depth_passes(const DepthPlan& dp) {
+  return (*dp.dmax >> (kDepthPasses * kDigitBits)) != 0u ? kDepthPassesMax : kDepthPasses;
+}
+// Uniform per launch: whether this pass has anything to do.
+__device__ inline bool pass_runs(const DepthPlan& dp) { return dp.pass < kDepthPasses || dp.pass < depth_passes(dp); }
+__device__ inline int plan_dst(const DepthPlan& dp) { return ((depth_passes(dp) - 1 - dp.pass) & 1) == 0 ? 1 : 0; }
+// A depth pass after the first reads the set the pass before it wrote.
+__device__ inline void plan_source(PassIn& in, const DepthPlan& dp) {
+  if (dp.pass > 0) {
+    const int src = 1 - plan_dst(dp);
+    in.keys = dp.k[src];
+    in.vals = dp.v[src];
+  }
+}
+
+// Item idx of a pass (idx < count, count >= 1).  Loads are unconditional so that a
+// thread's loads of several items are in flight together; returns whether the item
+// takes part (kFromDepth: the Gaussian is visible).
 template <int SRC>
-__device__ inline bool load_item(const PassIn& in, uint32_t count, uint32_t idx, uint32_t& key, uint32_t& val) {
-  if (idx >= count) return false;
+__device__ inline bool load_item(const PassIn& in, uint32_t idx, uint32_t& key, uint32_t& val) {
   if (SRC == kFromDepth) {
-    // both loads issued before either is tested
     const uint32_t t = in.tiles[idx];
-    key = __float_as_uint(in.depth[idx]);
+    const uint32_t b = __float_as_uint(in.depth[idx]);
+    key = b > in.key_base ? b - in.key_base : 0u;
     val = idx;
-    if (t == 0u) return false;
+    return t != 0u;
   } else {
     key = in.keys[idx];
     val = in.vals[idx];
+    return true;
   }
-  return true;
 }
 
 __device__ inline uint32_t pass_count(const PassIn& in) { return in.count_dev ? *in.count_dev : in.count; }
 
+// Exclusive prefix across the block of two independent per-thread values; the block
+// totals go to tx, ty.  s: 2 * kWaves entries.
+__device__ inline uint2 block_scan2(uint32_t x, uint32_t y, uint32_t* s, uint32_t& tx, uint32_t& ty) {
+  const int lane = __lane_id(), wave = threadIdx.x >> 6;
+  uint32_t ix = x, iy = y;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t a = __shfl_up(ix, d, 64), b = __shfl_up(iy, d, 64);
+    if (lane >= d) {
+      ix += a;
+      iy += b;
+    }
+  }
+  if (lane == 63) {
+    s[wave] = ix;
+    s[kWaves + wave] = iy;
+  }
+  __syncthreads();
+  uint32_t px = 0, py = 0;
+  tx = 0;
+  ty = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) {
+      px += s[w];
+      py += s[kWaves + w];
+    }
+    tx += s[w];
+    ty += s[kWaves + w];
+  }
+  __syncthreads();   // s may be written again after this
+  return make_uint2(px + ix - x, py + iy - y);
+}
+
 template <int SRC>
-__global__ void __launch_bounds__(kSortThreads) radix_upsweep_kernel(PassIn in, int shift, int nb,
-                                                                      uint32_t* __restrict__ hist) {
+__global__ void __launch_bounds__(kSortThreads) radix_upsweep_kernel(PassIn in, DepthPlan dp, int shift, uint32_t mask,
+                                                                      int nb, uint32_t* __restrict__ hist) {
   __shared__ uint32_t s_hist[kRadix];
-  s_hist[threadIdx.x] = 0u;
+  if (!pass_runs(dp)) return;
+  plan_source(in, dp);
+  for (int d = threadIdx.x; d < kRadix; d += kSortThreads) s_hist[d] = 0u;
   __syncthreads();
   const uint32_t count = pass_count(in);
   const uint32_t base = blockIdx.x * kSortTile;
+  uint32_t kmax = 0u;
   if (base < count) {
-#pragma unroll 4
+    uint32_t key[kSortItems];
+    bool ok[kSortItems];
+#pragma unroll
     for (int k = 0; k < kSortItems; ++k) {
-      uint32_t key = 0, val = 0;
-      if (load_item<SRC>(in, count, base + k * kSortThreads + threadIdx.x, key, val))
-        atomicAdd(&s_hist[(key >> shift) & 0xffu], 1u);
+      const uint32_t idx = base + k * kSortThreads + threadIdx.x;
+      uint32_t val;
+      ok[k] = load_item<SRC>(in, min(idx, count - 1), key[k], val) && idx < count;
+    }
+    if (dp.pass >= 0) {
+      // depth digits are spread: one LDS atomic per item
+#pragma unroll
+      for (int k = 0; k < kSortItems; ++k) {
+        if (ok[k]) {
+          atomicAdd(&s_hist[(key[k] >> shift) & mask], 1u);
+          kmax = max(kmax, key[k]);
+        }
+      }
+    } else {
+      // tile digits crowd (a block's pairs come from few screen regions): one LDS atomic
+      // per distinct digit of a wave's 64 items (9 ballots give each lane its peers; the
+      // lowest lane adds their number)
+      const uint64_t lt_mask = (uint64_t(1) << __lane_id()) - 1;
+#pragma unroll
+      for (int k = 0; k < kSortItems; ++k) {
+        const uint32_t d = (key[k] >> shift) & mask;
+        uint64_t peers = __ballot(ok[k]);
+#pragma unroll
+        for (int b = 0; b < kDigitBits; ++b) {
+          const bool bit = (d >> b) & 1u;
+          const uint64_t m = __ballot(bit);
+          peers &= bit ? m : ~m;
+        }
+        if (ok[k] && (peers & lt_mask) == 0) atomicAdd(&s_hist[d], uint32_t(__popcll(peers)));
+      }
     }
   }
+  if (SRC == kFromDepth) {
+    __shared__ uint32_t s_max[kWaves];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) kmax = max(kmax, uint32_t(__shfl_xor(kmax, d, 64)));
+    if (__lane_id() == 0) s_max[threadIdx.x >> 6] = kmax;
+    __syncthreads();
+    if (threadIdx.x == 0) dp.bmax[blockIdx.x] = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+  }
   __syncthreads();
-  hist[threadIdx.x * nb + blockIdx.x] = s_hist[threadIdx.x];
+  for (int d = threadIdx.x; d < kRadix; d += kSortThreads) hist[size_t(d) * nb + blockIdx.x] = s_hist[d];
 }
 
-// hist_scan has kRadix * nb + 1 entries, the last one the total: with kFromDepth
-// that is the number of visible Gaussians, which block 0 stores to *count_out.
-// With rect_out, the item's value (a Gaussian id) is also looked up in val_rect and
-// its tile rectangle and tile count written beside it (in the output order).
+// One block per digit: hist_scan[d][b] = sum of hist[d][b'] over b' < b, rowtot[d] the row sum.
+// In the depth sort's first pass, block 0 also reduces the blocks' maxima of d.
+__global__ void __launch_bounds__(kSortThreads) radix_scan_kernel(DepthPlan dp, int nb,
+                                                                   const uint32_t* __restrict__ hist,
+                                                                   uint32_t* __restrict__ hist_scan,
+                                                                   uint32_t* __restrict__ rowtot) {
+  __shared__ uint32_t s_scan[2 * kWaves];
+  if (!pass_runs(dp)) return;
+  if (dp.pass == 0 && blockIdx.x == 0) {
+    uint32_t m = 0u;
+    for (int b = threadIdx.x; b < nb; b += kSortThreads) m = max(m, dp.bmax[b]);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) m = max(m, uint32_t(__shfl_xor(m, d, 64)));
+    if (__lane_id() == 0) s_scan[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) *dp.dmax = max(max(s_scan[0], s_scan[1]), max(s_scan[2], s_scan[3]));
+    __syncthreads();
+  }
+  constexpr int kPer = 4;
+  const uint32_t* row = hist + size_t(blockIdx.x) * nb;
+  uint32_t* out = hist_scan + size_t(blockIdx.x) * nb;
+  uint32_t carry = 0u;
+  for (int base = 0; base < nb; base += kSortThreads * kPer) {
+    const int i0 = base + int(threadIdx.x) * kPer;
+    uint32_t v[kPer], sum = 0u;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      v[k] = i0 + k < nb ? row[i0 + k] : 0u;
+      sum += v[k];
+    }
+    uint32_t total, unused;
+    uint32_t run = carry + block_scan2(sum, 0u, s_scan, total, unused).x;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      if (i0 + k < nb) out[i0 + k] = run;
+      run += v[k];
+    }
+    carry += total;
+  }
+  if (threadIdx.x == 0) rowtot[blockIdx.x] = carry;
+}
+
+// With count_out, block 0 stores the number of items (for kFromDepth, of visible
+// Gaussians).  The depth plan's last pass writes no keys; it looks every value (a
+// Gaussian id) up in val_rect and writes the Gaussian's tile rectangle and tile count
+// beside it.
 template <int SRC>
 __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
-    PassIn in, int shift, int nb, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ hist_scan,
-    uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint32_t* __restrict__ count_out,
+    PassIn in, DepthPlan dp, int shift, uint32_t mask, int nb, const uint32_t* __restrict__ hist_scan,
+    const uint32_t* __restrict__ rowtot, uint32_t* keys_out, uint32_t* vals_out, uint32_t* __restrict__ count_out,
     const uint2* __restrict__ val_rect, uint2* __restrict__ rect_out, uint32_t* __restrict__ counts_out) {
   __shared__ uint32_t s_keys[kSortTile];
   __shared__ uint32_t s_vals[kSortTile];
-  __shared__ uint32_t s_whist[kSortThreads / 64][kRadix];   // per-wave digit counts, then starts
-  __shared__ uint32_t s_local[kRadix];    // block-local start of each digit
-  __shared__ uint32_t s_global[kRadix];   // global start of (digit, this block)
-  __shared__ uint32_t s_wtot[kSortThreads / 64];
+  __shared__ uint16_t s_whist[kWaves][kRadix];   // per-wave digit counts, then starts (<= 4096)
+  __shared__ uint16_t s_local[kRadix];           // block-local start of each digit
+  __shared__ uint32_t s_global[kRadix];          // global start of (digit, this block)
+  __shared__ uint32_t s_scan[2 * kWaves];
 
+  if (!pass_runs(dp)) return;
+  plan_source(in, dp);
+  bool last = false;
+  if (dp.pass >= 0) {
+    const int dst = plan_dst(dp);
+    keys_out = dp.k[dst];
+    vals_out = dp.v[dst];
+    last = dp.pass == depth_passes(dp) - 1;
+  }
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid >> 6;
-  if (count_out && blockIdx.x == 0 && tid == 0) *count_out = hist_scan[kRadix * nb];
+  const int d0 = 2 * tid;   // this thread's two digits
+  // the digit bases: exclusive prefix of the row totals, plus the earlier blocks' counts
+  // of the digit (block 0 also stores the number of items)
+  {
+    const uint32_t g0 = hist_scan[size_t(d0) * nb + blockIdx.x], g1 = hist_scan[size_t(d0 + 1) * nb + blockIdx.x];
+    const uint32_t r0 = rowtot[d0], r1 = rowtot[d0 + 1];
+    uint32_t all_total, unused;
+    const uint32_t pre = block_scan2(r0 + r1, 0u, s_scan, all_total, unused).x;
+    if (count_out && blockIdx.x == 0 && tid == 0) *count_out = all_total;
+    s_global[d0] = pre + g0;
+    s_global[d0 + 1] = pre + r0 + g1;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      s_whist[w][d0] = 0;
+      s_whist[w][d0 + 1] = 0;
+    }
+  }
   const uint32_t count = pass_count(in);
   const uint32_t base = blockIdx.x * kSortTile;
   if (base >= count) return;   // uniform per block
-  // digit counts of this block and their block-local exclusive prefix
-  uint32_t block_total;
-  {
-    const uint32_t cnt = hist[tid * nb + blockIdx.x];
-    s_global[tid] = hist_scan[tid * nb + blockIdx.x];
-    uint32_t v = cnt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t t = __shfl_up(v, d, 64);
-      if (lane >= d) v += t;
-    }
-    if (lane == 63) s_wtot[wave] = v;
-    __syncthreads();
-    uint32_t pre = 0;
-    block_total = 0;
-    for (int w = 0; w < kSortThreads / 64; ++w) {
-      if (w < wave) pre += s_wtot[w];
-      block_total += s_wtot[w];
-    }
-    s_local[tid] = pre + v - cnt;
-    for (int w = 0; w < kSortThreads / 64; ++w) s_whist[w][tid] = 0u;
-  }
   __syncthreads();
   // Each wave ranks its own 1024 consecutive items, 64 per round, with a wave-private
   // digit histogram: an item's rank among equal digits of its wave is the histogram
-  // before its round plus its rank in the round (8 ballots give each lane its peers;
+  // before its round plus its rank in the round (9 ballots give each lane its peers;
   // CDNA has no match-any).  Waves, rounds and lanes follow the items' order, so the
   // placement is stable.
-  constexpr int kWaveItems = kSortTile / (kSortThreads / 64);
+  constexpr int kWaveItems = kSortTile / kWaves;
   constexpr int kRounds = kWaveItems / 64;
   const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
   uint32_t key[kRounds], val[kRounds], rk[kRounds];
+  bool ok[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {   // every round's loads before any ranking
+    const uint32_t idx = base + wave * kWaveItems + r * 64 + lane;
+    ok[r] = load_item<SRC>(in, min(idx, count - 1), key[r], val[r]) && idx < count;
+  }
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
-    key[r] = 0u;
-    val[r] = 0u;
-    const bool valid = load_item<SRC>(in, count, base + wave * kWaveItems + r * 64 + lane, key[r], val[r]);
-    const uint32_t d = (key[r] >> shift) & 0xffu;
+    const bool valid = ok[r];
+    const uint32_t d = (key[r] >> shift) & mask;
     uint64_t peers = __ballot(valid);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int b = 0; b < kDigitBits; ++b) {
       const bool bit = (d >> b) & 1u;
       const uint64_t m = __ballot(bit);
       peers &= bit ? m : ~m;
     }
-    const uint32_t before = valid ? s_whist[wave][d] : 0u;
+    const uint32_t before = valid ? uint32_t(s_whist[wave][d]) : 0u;
     const uint32_t rank = __popcll(peers & lt_mask);
     // the read above is issued before this write, and one wave's LDS operations are
     // performed in order
-    if (valid && rank == 0) s_whist[wave][d] = before + uint32_t(__popcll(peers));
+    if (valid && rank == 0) s_whist[wave][d] = uint16_t(before + uint32_t(__popcll(peers)));
     rk[r] = valid ? before + rank : 0xffffffffu;
   }
   __syncthreads();
-  // per digit, the start of each wave's run: block-local start plus the earlier waves
+  // the block's count of each digit (summed over the waves) and their block-local prefix
+  uint32_t block_total;
   {
-    uint32_t acc = s_local[tid];
+    uint32_t c0 = 0u, c1 = 0u;
 #pragma unroll
-    for (int w = 0; w < kSortThreads / 64; ++w) {
-      const uint32_t t = s_whist[w][tid];
-      s_whist[w][tid] = acc;
+    for (int w = 0; w < kWaves; ++w) {
+      c0 += s_whist[w][d0];
+      c1 += s_whist[w][d0 + 1];
+    }
+    uint32_t unused;
+    const uint32_t pre = block_scan2(c0 + c1, 0u, s_scan, block_total, unused).x;
+    s_local[d0] = uint16_t(pre);
+    s_local[d0 + 1] = uint16_t(pre + c0);
+  }
+  // per digit, the start of each wave's run: block-local start plus the earlier waves
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int d = d0 + j;
+    uint32_t acc = s_local[d];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t t = s_whist[w][d];
+      s_whist[w][d] = uint16_t(acc);
       acc += t;
     }
   }
@@ -179,22 +363,42 @@ __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     if (rk[r] != 0xffffffffu) {
-      const uint32_t pos = s_whist[wave][(key[r] >> shift) & 0xffu] + rk[r];
+      const uint32_t pos = s_whist[wave][(key[r] >> shift) & mask] + rk[r];
       s_keys[pos] = key[r];
       s_vals[pos] = val[r];
     }
   }
   __syncthreads();
-  for (uint32_t k = tid; k < block_total; k += kSortThreads) {
-    const uint32_t key = s_keys[k];
-    const uint32_t d = (key >> shift) & 0xffu;
-    const uint32_t dst = s_global[d] + (k - s_local[d]);
-    keys_out[dst] = key;
-    vals_out[dst] = s_vals[k];
-    if (rect_out) {
-      const uint2 r = val_rect[s_vals[k]];
-      rect_out[dst] = r;
-      counts_out[dst] = ((r.y & 0xffffu) - (r.x & 0xffffu) + 1u) * ((r.y >> 16) - (r.x >> 16) + 1u);
+  // out in sorted order, sixteen places per thread (the last depth pass's rectangle
+  // gathers issued together)
+  uint32_t okey[kSortItems], oval[kSortItems], dst[kSortItems];
+#pragma unroll
+  for (int j = 0; j < kSortItems; ++j) {
+    const uint32_t k = tid + j * kSortThreads;
+    okey[j] = s_keys[k];
+    oval[j] = s_vals[k];
+    const uint32_t d = (okey[j] >> shift) & mask;
+    dst[j] = s_global[d] + (k - s_local[d]);
+  }
+  if (last) {
+    uint2 rc[kSortItems];
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) rc[j] = val_rect[tid + j * kSortThreads < block_total ? oval[j] : 0u];
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+      if (tid + j * kSortThreads < block_total) {
+        vals_out[dst[j]] = oval[j];
+        rect_out[dst[j]] = rc[j];
+        counts_out[dst[j]] = ((rc[j].y & 0xffffu) - (rc[j].x & 0xffffu) + 1u) * ((rc[j].y >> 16) - (rc[j].x >> 16) + 1u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+      if (tid + j * kSortThreads < block_total) {
+        keys_out[dst[j]] = okey[j];
+        vals_out[dst[j]] = oval[j];
+      }
     }
   }
 }
@@ -213,44 +417,57 @@ __global__ void __launch_bounds__(256) block_starts_kernel(const uint32_t* __res
 
 // One thread per pair: the Gaussian (in depth order) that owns it, and its tile.
 // offs[r] is the first pair of the r-th visible Gaussian in depth order and
-// rect_order[r] its tile rectangle.  The block's 256 pairs belong to at most 256
-// consecutive Gaussians starting with block_first[block]; their offsets go to LDS
-// and each thread searches there.
+// rect_order[r] its tile rectangle.  A block covers 4096 pairs (one radix block) in
+// pieces of 256: a piece belongs to at most 256 consecutive Gaussians starting with
+// block_first[piece]; their offsets go to LDS and each thread searches there.  With
+// hist, the block also counts the tiles' low digit (key & mask), hist[d][block]: the
+// upsweep of the first tile pass.
 __global__ void __launch_bounds__(256) emit_pairs_kernel(const uint32_t* __restrict__ offs,
                                                           const uint32_t* __restrict__ n_vis,
                                                           const uint32_t* __restrict__ block_first,
                                                           const uint32_t* __restrict__ order,
                                                           const uint2* __restrict__ rect_order, int n, uint32_t pairs,
                                                           int tx, uint32_t* __restrict__ keys,
-                                                          uint32_t* __restrict__ vals) {
+                                                          uint32_t* __restrict__ vals, int nb, uint32_t mask,
+                                                          uint32_t* __restrict__ hist) {
   __shared__ uint32_t s_offs[256];
-  const uint32_t p0 = blockIdx.x * 256u;
+  __shared__ uint32_t s_hist[kRadix];
+  for (int d = threadIdx.x; d < kRadix; d += 256) s_hist[d] = 0u;
   const int nv = int(*n_vis);
-  const uint32_t bf = block_first[blockIdx.x];
-  const int r0 = int(bf < uint32_t(nv) ? bf : uint32_t(max(nv - 1, 0)));
-  // Gaussians past the visible ones (or past the block) get an offset above every pair
-  const int k = min(256, nv - r0);
-  s_offs[threadIdx.x] = int(threadIdx.x) < k ? offs[r0 + int(threadIdx.x)] : 0xffffffffu;
+  for (int piece = 0; piece < kSortTile / 256; ++piece) {
+    const uint32_t p0 = blockIdx.x * uint32_t(kSortTile) + uint32_t(piece) * 256u;
+    if (p0 >= pairs) break;   // uniform
+    const uint32_t bf = block_first[p0 >> 8];
+    const int r0 = int(bf < uint32_t(nv) ? bf : uint32_t(max(nv - 1, 0)));
+    // Gaussians past the visible ones (or past the piece) get an offset above every pair
+    const int k = min(256, nv - r0);
+    __syncthreads();   // the previous piece's searches are done (and s_hist is zeroed)
+    s_offs[threadIdx.x] = int(threadIdx.x) < k ? offs[r0 + int(threadIdx.x)] : 0xffffffffu;
+    __syncthreads();
+    const uint32_t p = p0 + threadIdx.x;
+    if (p >= pairs) continue;
+    int lo = 0, hi = max(k, 1) - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_offs[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    const uint32_t g = order[r0 + lo];
+    uint32_t key = 0xffffffffu, val = 0u;   // only if total_pairs disagrees with the projection
+    if (g < uint32_t(n)) {
+      const uint32_t j = p - s_offs[lo];
+      const uint2 r = rect_order[r0 + lo];
+      const uint32_t x0 = r.x & 0xffffu, y0 = r.x >> 16, x1 = r.y & 0xffffu;
+      const uint32_t w = x1 - x0 + 1;
+      key = (y0 + j / w) * uint32_t(tx) + (x0 + j % w);
+      val = g;
+    }
+    keys[p] = key;
+    vals[p] = val;
+    if (hist) atomicAdd(&s_hist[key & mask], 1u);
+  }
+  if (!hist) return;
   __syncthreads();
-  const uint32_t p = p0 + threadIdx.x;
-  if (p >= pairs) return;
-  int lo = 0, hi = max(k, 1) - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_offs[mid] <= p) lo = mid; else hi = mid - 1;
-  }
-  const uint32_t g = order[r0 + lo];
-  if (g >= uint32_t(n)) {   // only if total_pairs disagrees with the projection
-    keys[p] = 0xffffffffu;
-    vals[p] = 0u;
-    return;
-  }
-  const uint32_t j = p - s_offs[lo];
-  const uint2 r = rect_order[r0 + lo];
-  const uint32_t x0 = r.x & 0xffffu, y0 = r.x >> 16, x1 = r.y & 0xffffu;
-  const uint32_t w = x1 - x0 + 1;
-  keys[p] = (y0 + j / w) * uint32_t(tx) + (x0 + j % w);
-  vals[p] = g;
+  for (int d = threadIdx.x; d < kRadix; d += 256) hist[size_t(d) * nb + blockIdx.x] = s_hist[d];
 }
 
 __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t count, uint32_t value) {
@@ -325,24 +542,25 @@ struct Carver {
 };
 
 struct RadixWs {
-  uint32_t *hist, *hist_scan;   // kRadix * nb (+ 1)
-  uint64_t* total64;
-  void* scan_ws;
+  uint32_t *hist, *hist_scan;   // kRadix * nb each
+  uint32_t* rowtot;             // kRadix
 };
 
-RadixWs carve_radix(Carver& c, int nb, int64_t also_scan) {
+RadixWs carve_radix(Carver& c, int nb) {
   const int64_t hist_n = int64_t(kRadix) * nb;
   RadixWs w;
   w.hist = c.take(size_t(hist_n) * 4);
-  w.hist_scan = c.take(size_t(hist_n + 1) * 4);
-  w.total64 = reinterpret_cast<uint64_t*>(c.take(8));
-  w.scan_ws = c.take(scan_ws_bytes(std::max<int64_t>(hist_n, also_scan)));
+  w.hist_scan = c.take(size_t(hist_n) * 4);
+  w.rowtot = c.take(size_t(kRadix) * 4);
   return w;
 }
 
 struct DepthWs {
-  uint32_t *dk[2], *dv;         // ping-pong with proj.order, n each
-  uint32_t* counts;             // n: tile counts in depth order
+  uint32_t *dk[2], *dv;         // with proj.order: the depth passes' two buffer sets
+  uint32_t* counts;             // n: tile counts in depth order; counts[n]: the plan's dmax
+  uint32_t* bmax;               // one per radix block
+  uint64_t* total64;            // the offsets scan's total
+  void* scan_ws;
   RadixWs r;
 };
 
@@ -353,8 +571,11 @@ size_t carve_depth(void* ws, int64_t n, DepthWs* out) {
   w.dk[0] = c.take(sn);
   w.dk[1] = c.take(sn);
   w.dv = c.take(sn);
-  w.counts = c.take(sn);
-  w.r = carve_radix(c, blocks_for(n), n);
+  w.counts = c.take(sn + 4);
+  w.bmax = c.take(size_t(blocks_for(n)) * 4);
+  w.total64 = reinterpret_cast<uint64_t*>(c.take(8));
+  w.scan_ws = c.take(scan_ws_bytes(n));
+  w.r = carve_radix(c, blocks_for(n));
   if (out) *out = w;
   return c.off;
 }
@@ -371,24 +592,29 @@ size_t carve_pairs(void* ws, uint32_t pairs, PairWs* out) {
   w.keys_alt = c.take(size_t(pairs) * 4);
   w.vals_alt = c.take(size_t(pairs) * 4);
   w.block_first = c.take(size_t(div_up(pairs > 0 ? pairs : 1, 256)) * 4);
-  w.r = carve_radix(c, blocks_for(pairs), 0);
+  w.r = carve_radix(c, blocks_for(pairs));
   if (out) *out = w;
   return c.off;
 }
 
+// One radix pass over the bits-wide digit at `shift`; without upsweep, w.hist already
+// holds this pass's block histograms.
 template <int SRC>
-hipError_t radix_pass(const PassIn& in, int nb, int shift, const RadixWs& w, uint32_t* keys_out,
-                      uint32_t* vals_out, uint32_t* count_out, const uint2* val_rect, uint2* rect_out,
-                      uint32_t* counts_out, hipStream_t s) {
-  {
+hipError_t radix_pass(const PassIn& in, const DepthPlan& dp, int nb, int shift, int bits, const RadixWs& w,
+                      bool upsweep, uint32_t* keys_out, uint32_t* vals_out, uint32_t* count_out,
+                      const uint2* val_rect, uint2* rect_out, uint32_t* counts_out, hipStream_t s) {
+  const uint32_t mask = (1u << bits) - 1u;
+  if (upsweep) {
     GSK_PROF("radix_upsweep", s);
-    radix_upsweep_kernel<SRC><<<nb, kSortThreads, 0, s>>>(in, shift, nb, w.hist);
+    radix_upsweep_kernel<SRC><<<nb, kSortThreads, 0, s>>>(in, dp, shift, mask, nb, w.hist);
   }
-  hipError_t e = launch_scan_u32(w.hist, w.hist_scan, int64_t(kRadix) * nb, w.total64, w.scan_ws, s);
-  if (e != hipSuccess) return e;
+  {
+    GSK_PROF("radix_scan", s);
+    radix_scan_kernel<<<kRadix, kSortThreads, 0, s>>>(dp, nb, w.hist, w.hist_scan, w.rowtot);
+  }
   GSK_PROF("radix_downsweep", s);
-  radix_downsweep_kernel<SRC><<<nb, kSortThreads, 0, s>>>(in, shift, nb, w.hist, w.hist_scan, keys_out, vals_out,
-                                                          count_out, val_rect, rect_out, counts_out);
+  radix_downsweep_kernel<SRC><<<nb, kSortThreads, 0, s>>>(in, dp, shift, mask, nb, w.hist_scan, w.rowtot, keys_out,
+                                                          vals_out, count_out, val_rect, rect_out, counts_out);
   return hipGetLastError();
 }
 
@@ -396,7 +622,7 @@ hipError_t radix_pass(const PassIn& in, int nb, int shift, const RadixWs& w, uin
 
 size_t depth_order_ws_bytes(int64_t n) { return carve_depth(nullptr, n, nullptr); }
 
-hipError_t launch_depth_order(const gs_proj& proj, int n, void* ws, hipStream_t s) {
+hipError_t launch_depth_order(const gs_proj& proj, int n, float znear, void* ws, hipStream_t s) {
   if (n == 0) {
     GSK_PROF("fill_u32", s);
     fill_u32_kernel<<<1, 256, 0, s>>>(proj.offs, 1, 0u);
@@ -407,34 +633,36 @@ hipError_t launch_depth_order(const gs_proj& proj, int n, void* ws, hipStream_t 
   carve_depth(ws, n, &w);
   hipError_t e;
   const int nb = blocks_for(n);
-  zero_u32(w.counts, n, s);
-  // pass 0 compacts the visible Gaussians into (dk[0], dv); later passes alternate
-  // with (dk[1], order), so the fourth lands in proj.order
+  zero_u32(w.counts, int64_t(n), s);   // the counts of the invisible stay 0
+  uint32_t key_base;
+  std::memcpy(&key_base, &znear, sizeof key_base);
+  DepthPlan dp{{w.dk[0], w.dk[1]}, {w.dv, proj.order}, w.bmax, w.counts + n, 0};
+  const uint2* rect = reinterpret_cast<const uint2*>(proj.rect);
+  uint2* rect_order = reinterpret_cast<uint2*>(proj.rect_order);
+  // pass 0 compacts the visible Gaussians; the last pass (2 or 3, chosen on the device)
+  // lands in proj.order and writes their rectangles and counts in that order
   {
-    PassIn in{nullptr, nullptr, proj.depth, proj.tiles, uint32_t(n), nullptr};
-    if ((e = radix_pass<kFromDepth>(in, nb, 0, w.r, w.dk[0], w.dv, proj.n_visible, nullptr, nullptr, nullptr,
-                                    s)) != hipSuccess)
+    PassIn in{nullptr, nullptr, proj.depth, proj.tiles, key_base, uint32_t(n), nullptr};
+    if ((e = radix_pass<kFromDepth>(in, dp, nb, 0, kDigitBits, w.r, true, nullptr, nullptr, proj.n_visible, rect,
+                                    rect_order, w.counts, s)) != hipSuccess)
       return e;
   }
-  for (int pass = 1; pass < kDepthPasses; ++pass) {
-    const bool odd = pass & 1;
-    PassIn in{odd ? w.dk[0] : w.dk[1], odd ? w.dv : proj.order, nullptr, nullptr, 0u, proj.n_visible};
-    const bool last = pass == kDepthPasses - 1;
-    if ((e = radix_pass<kFromKeys>(in, nb, 8 * pass, w.r, odd ? w.dk[1] : w.dk[0], odd ? proj.order : w.dv,
-                                   nullptr, last ? reinterpret_cast<const uint2*>(proj.rect) : nullptr,
-                                   last ? reinterpret_cast<uint2*>(proj.rect_order) : nullptr,
-                                   last ? w.counts : nullptr, s)) != hipSuccess)
+  for (int pass = 1; pass < kDepthPassesMax; ++pass) {
+    dp.pass = pass;
+    PassIn in{nullptr, nullptr, nullptr, nullptr, 0u, 0u, proj.n_visible};
+    if ((e = radix_pass<kFromKeys>(in, dp, nb, kDigitBits * pass, kDigitBits, w.r, true, nullptr, nullptr, nullptr,
+                                   rect, rect_order, w.counts, s)) != hipSuccess)
       return e;
   }
   // offs: first pair of each visible Gaussian in depth order; offs[n] = the pair count
-  return launch_scan_u32(w.counts, proj.offs, n, w.r.total64, w.r.scan_ws, s);
+  return launch_scan_u32(w.counts, proj.offs, n, w.total64, w.scan_ws, s);
 }
 
 size_t sort_pairs_ws_bytes(int64_t n) {
   Carver c{nullptr};
   c.take(size_t(n > 0 ? n : 1) * 4);
   c.take(size_t(n > 0 ? n : 1) * 4);
-  carve_radix(c, blocks_for(n), 0);
+  carve_radix(c, blocks_for(n));
   return c.off;
 }
 
@@ -444,14 +672,15 @@ hipError_t launch_sort_pairs_u32(uint32_t* keys, uint32_t* vals, uint32_t count,
   Carver c{static_cast<char*>(ws)};
   uint32_t* alt_k = c.take(size_t(capacity) * 4);
   uint32_t* alt_v = c.take(size_t(capacity) * 4);
-  const RadixWs r = carve_radix(c, blocks_for(capacity), 0);
+  const RadixWs r = carve_radix(c, blocks_for(capacity));
   const int nb = blocks_for(count);
-  // four 8-bit passes: keys -> alt -> keys -> alt -> keys
+  // four 9-bit passes: keys -> alt -> keys -> alt -> keys
   for (int pass = 0; pass < 4; ++pass) {
     const bool even = (pass & 1) == 0;
-    PassIn in{even ? keys : alt_k, even ? vals : alt_v, nullptr, nullptr, count, nullptr};
-    const hipError_t e = radix_pass<kFromKeys>(in, nb, 8 * pass, r, even ? alt_k : keys, even ? alt_v : vals, nullptr,
-                                               nullptr, nullptr, nullptr, s);
+    PassIn in{even ? keys : alt_k, even ? vals : alt_v, nullptr, nullptr, 0u, count, nullptr};
+    const hipError_t e = radix_pass<kFromKeys>(in, kNoPlan, nb, kDigitBits * pass, std::min(kDigitBits, 32 - kDigitBits * pass),
+                                               r, true, even ? alt_k : keys, even ? alt_v : vals, nullptr, nullptr,
+                                               nullptr, nullptr, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -471,28 +700,33 @@ hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uin
   PairWs w;
   carve_pairs(ws, pairs, &w);
   hipError_t e;
-  const int tile_passes = (bits_for(uint32_t(num_tiles - 1)) + 7) / 8;
+  // the tile id's bits split evenly over the passes (few distinct values in a digit
+  // would crowd the histogram counters)
+  const int tile_bits = bits_for(uint32_t(num_tiles - 1));
+  const int tile_passes = (tile_bits + kDigitBits - 1) / kDigitBits;
+  const int low_bits = tile_passes > 0 ? (tile_bits + tile_passes - 1) / tile_passes : 0;
   // emit into the buffer that makes the last tile pass land in keys / vals
   uint32_t* k_src = (tile_passes & 1) ? w.keys_alt : keys;
   uint32_t* v_src = (tile_passes & 1) ? w.vals_alt : vals;
   uint32_t* k_dst = (tile_passes & 1) ? keys : w.keys_alt;
   uint32_t* v_dst = (tile_passes & 1) ? vals : w.vals_alt;
+  const int nbp = blocks_for(pairs);
   {
     GSK_PROF("block_starts", s);
     block_starts_kernel<<<div_up(n, 256), 256, 0, s>>>(proj.offs, proj.n_visible, n, pairs, w.block_first);
   }
   {
     GSK_PROF("emit_pairs", s);
-    emit_pairs_kernel<<<div_up(pairs, 256), 256, 0, s>>>(proj.offs, proj.n_visible, w.block_first, proj.order,
-                                                         reinterpret_cast<const uint2*>(proj.rect_order), n, pairs,
-                                                         tx, k_src, v_src);
+    emit_pairs_kernel<<<nbp, 256, 0, s>>>(proj.offs, proj.n_visible, w.block_first, proj.order,
+                                          reinterpret_cast<const uint2*>(proj.rect_order), n, pairs, tx, k_src,
+                                          v_src, nbp, (1u << low_bits) - 1u, tile_passes > 0 ? w.r.hist : nullptr);
   }
-  // stable sort of the pairs by tile
-  const int nbp = blocks_for(pairs);
+  // stable sort of the pairs by tile (the first pass's histogram came with the emit)
   for (int pass = 0; pass < tile_passes; ++pass) {
-    PassIn in{k_src, v_src, nullptr, nullptr, pairs, nullptr};
-    if ((e = radix_pass<kFromKeys>(in, nbp, 8 * pass, w.r, k_dst, v_dst, nullptr, nullptr, nullptr, nullptr, s)) !=
-        hipSuccess)
+    PassIn in{k_src, v_src, nullptr, nullptr, 0u, pairs, nullptr};
+    const int shift = low_bits * pass, bits = std::min(low_bits, tile_bits - shift);
+    if ((e = radix_pass<kFromKeys>(in, kNoPlan, nbp, shift, bits, w.r, pass > 0, k_dst, v_dst, nullptr, nullptr,
+                                   nullptr, nullptr, s)) != hipSuccess)
       return e;
     uint32_t* tk = k_src; k_src = k_dst; k_dst = tk;
     uint32_t* tv = v_src; v_src = v_dst; v_dst = tv;

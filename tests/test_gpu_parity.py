@@ -300,6 +300,36 @@ def test_all_in_one_tile_and_non_finite(torch_cuda, oracle):
     pu.check_render(pu.render_to_numpy(pl), o["fwd"], o["risk"])
 
 
+@pytest.mark.parametrize("far", [900.0, 5.0e4])
+def test_depth_order_over_a_wide_depth_range(torch_cuda, oracle, far):
+    """Depths from just above znear to far, log-uniform, with runs of exactly equal
+    depths (ties broken by id).  At far = 5e4 the depth key (the depth's bits less
+    znear's) needs more than 27 bits, so the depth sort makes its fourth pass; at 900 it
+    makes three.  Pairs and ranges bit-exact against the oracle."""
+    n, w, h, f = 3000, 96, 80, 60.0
+    rng = np.random.default_rng(int(far))
+    s = scenes.random_scene(40, n, 0)
+    cam = scenes.identity_camera(w, h, f)
+    z = np.exp(rng.uniform(math.log(cam.znear * 1.0001), math.log(far), n)).astype(np.float32)
+    z[:40] = np.float32(cam.znear) * np.float32(1.0000001)   # just above the near plane
+    z[40:400] = z[400]                                         # one long run of equal depths
+    z[1000:1100:3] = np.float32(far)                           # equal depths at the far end
+    s.params[2] = z
+    s.params[0] = rng.uniform(-0.7, 0.7, n).astype(np.float32) * z * (w / (2 * f))
+    s.params[1] = rng.uniform(-0.7, 0.7, n).astype(np.float32) * z * (h / (2 * f))
+    s.params[3:6] = np.log(0.04 * z)[None, :].astype(np.float32) + rng.normal(0, 0.2, (3, n)).astype(np.float32)
+    d_bits = z.view(np.uint32).astype(np.int64) - np.array([cam.znear], np.float32).view(np.uint32)[0]
+    assert (d_bits.max() >= 1 << 27) == (far > 2.0e4)
+    pre, okeys, ovals, oranges, _ = oracle.forward(s.params, 0, cam)
+    assert int((pre["tiles"] > 0).sum()) > n // 2
+    pl, c = pu.gpu_forward(s.params, 0, cam)
+    keys, vals, ranges = pu.sorted_to_numpy(pl)
+    assert pl.pairs == len(okeys)
+    np.testing.assert_array_equal(keys, pu.tile_of_key(okeys))
+    np.testing.assert_array_equal(vals, ovals)
+    np.testing.assert_array_equal(ranges, oranges)
+
+
 def test_capacity_error_writes_nothing(torch_cuda):
     import torch
     from differentiable_tile_gaussian_amd import gs
