@@ -49,6 +49,71 @@ def kernel_bytes(kernel, n, deg, P, fuse=True):
     return table.get(kernel)
 
 
+# kernels by stage (the names the library's per-kernel timing uses)
+STAGE_KERNELS = {
+    "preprocess": ("preprocess_fwd", "sum_counts"),
+    "bin_sort": ("radix_upsweep", "radix_scan", "radix_downsweep", "scan_reduce", "scan_apply", "block_starts",
+                 "emit_pairs", "tile_ranges", "fill_u32"),
+    "render_fwd": ("render_fwd", "tile_order", "split_init", "split_chunk", "split_combine", "split_rewalk",
+                   "split_finalize"),
+    "loss": ("ssim", "loss_finalize"),
+    "render_bwd": ("render_bwd", "zero_f32", "fixed_decode", "zero_u64"),
+    "chain_adam": ("chain",),
+}
+# the blend kernels proper (forward walk with its split path, backward walk)
+BLEND_KERNELS = STAGE_KERNELS["render_fwd"] + ("render_bwd",)
+LLC_BYTES = 256 << 20               # MI355X Infinity Cache
+
+
+def stage_kernel_ms(kernel_ms):
+    """Kernel milliseconds per stage from {kernel: ms}."""
+    return {st: round(sum(kernel_ms.get(k, 0.0) for k in ks), 4) for st, ks in STAGE_KERNELS.items()}
+
+
+def sort_bytes(n, vis, pairs, num_tiles, depth_passes):
+    """Algorithmic HBM bytes of one bin/sort (the passes the kernels make; 9-bit digits):
+
+    per Gaussian      counts zeroed 4, pass 0 reads depth and tile count twice (upsweep,
+                      downsweep) 16, the offsets scan reads counts twice and writes offsets 12
+    per visible one   pass 0 writes key and id 8; every further depth pass reads the key
+                      (upsweep) 4 and key and id 8 (downsweep) and writes them 8, the last
+                      one writing no key but the id 4, the gathered rectangle 8 and tile
+                      count 4 (and reading the rectangle 8); block starts read the offsets
+                      4; the emit reads offset, id and rectangle 16
+    per pair          emit writes tile and id 8; every tile pass reads and writes them 16,
+                      those after the first also read the tile 4 for their histogram;
+                      tile ranges read the tile 4
+    per tile          ranges cleared and written 16"""
+    tile_bits = max(int(num_tiles - 1).bit_length(), 0)
+    tile_passes = (tile_bits + 8) // 9
+    per_vis = 8 + (depth_passes - 2) * 20 + (4 + 8 + 4 + 4 + 8 + 8) + 4 + 16
+    per_pair = 8 + 16 * tile_passes + 4 * max(tile_passes - 1, 0) + 4
+    return 32 * n + per_vis * vis + per_pair * pairs + 16 * num_tiles
+
+
+def depth_passes_of(pl, cam, torch):
+    """Passes the depth sort made for the last projection: three, or four when some visible
+    depth's bits exceed znear's by 2^27 or more."""
+    vis = pl.proj.tiles[:pl.n] != 0
+    if not bool(vis.any()):
+        return 3
+    bits = pl.proj.depth[:pl.n][vis].view(torch.int32).to(torch.int64)
+    base = int(np.array([cam.znear], np.float32).view(np.int32)[0])
+    return 4 if int(bits.max()) - base >= (1 << 27) else 3
+
+
+def host_cpu():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -66,6 +131,9 @@ def parse():
     ap.add_argument("--no-fuse-projection", action="store_true",
                     help="project each step's camera in its own preprocess call instead of in the previous "
                          "step's update")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration block (configurations 1-4, measured after the headline)")
+    ap.add_argument("--config-steps", type=int, default=20, help="timed steps per configuration in that block")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy a 1 GiB buffer three times (a plain copy of known size, the "
                          "reference for hardware byte counters)")
@@ -320,6 +388,118 @@ def cpu_baseline(wl):
                 seconds=dt, evals=int(r["fwd"]["evals"] + int(r["fwd"]["n_contrib"].sum())))
 
 
+def oracle_step_seconds(wl):
+    """The oracle (test infrastructure) on one training step of a workload's first camera:
+    all stages including Adam, one core, seeded synthetic target."""
+    from oracle import oracle as O
+    cam = wl.cameras[0]
+    p, deg = wl.scene.params, wl.scene.sh_degree
+    tgt = np.random.default_rng(7).random((3, cam.height, cam.width), dtype=np.float32)
+    lr = np.array([1.6e-4, 5e-3, 1e-3, 5e-2, 2.5e-3])
+    t0 = time.perf_counter()
+    r = O.train_step(p, deg, cam, tgt)
+    z = np.zeros_like(p)
+    O.adam(p, r["gparams"], z, z, deg, lr, step=1, dtype=np.float32)
+    return time.perf_counter() - t0, r
+
+
+def hbm_entry(nbytes, ms, working_set):
+    """Achieved GB/s of a stage; its fraction of the HBM peak only when its working set is at
+    least twice the 256 MB last-level cache (otherwise the time is reported as it is)."""
+    gbps = nbytes / (ms / 1000.0) / 1e9 if ms > 0 else None
+    frac = round(gbps / HBM_PEAK_GBS, 4) if gbps and working_set >= 2 * LLC_BYTES else None
+    return {"ms": round(ms, 4), "bytes": int(nbytes), "GBps": round(gbps, 1) if gbps else None, "frac": frac,
+            "working_set": int(working_set)}
+
+
+def measure_config(k, steps, torch, gs, scenes, Pipeline, cfg, with_oracle):
+    """One configuration's block: the same fused training step as the headline, on its own
+    cameras and target.  Per-stage kernel times, eval counts and the pairs of each sort come
+    from profiled steps (every launch timed, counts read between steps); iter/s from
+    separately timed steps; the projection alone from repeated gs_preprocess calls."""
+    t_setup = time.perf_counter()
+    wl = scenes.CONFIGS[k]()
+    cams = [gs.make_camera(c) for c in wl.cameras]
+    targets = make_targets(wl, cams, Pipeline, torch)
+    params = torch.from_numpy(wl.scene.params).cuda()
+    n, deg = wl.scene.n, wl.scene.sh_degree
+    P = params.shape[0]
+    cam0 = wl.cameras[0]
+    pl = Pipeline(params, deg, cam0.width, cam0.height, cfg=cfg)
+    setup_s = time.perf_counter() - t_setup
+    warm = 3
+    run_steps(pl, cams, targets, 0, warm, gs=gs)
+    torch.cuda.synchronize()
+    prof = min(steps, 10)
+    ev_f = ev_b = 0
+    vis_sum = pairs_sum = sbytes = 0
+    num_tiles = pl.num_tiles
+    gs.gs_profile_enable(True)
+    for i in range(prof):
+        c = wl.cameras[(warm + i) % len(wl.cameras)]
+        if pl.projected_for is not cams[(warm + i) % len(cams)]:
+            pl.pairs = gs.gs_preprocess(pl.params, pl.deg, cams[(warm + i) % len(cams)], pl.proj, pl.ws_pre,
+                                        cfg=pl.cfg)
+            pl.projected_for = cams[(warm + i) % len(cams)]
+        vis = int(pl.proj.n_visible.item())
+        dp = depth_passes_of(pl, c, torch)
+        vis_sum += vis
+        pairs_sum += pl.pairs
+        sbytes += sort_bytes(n, vis, pl.pairs, num_tiles, dp)
+        run_steps(pl, cams, targets, warm + i, 1, gs=gs)
+        f, b = count_evals(pl, torch)
+        ev_f += f
+        ev_b += b
+    torch.cuda.synchronize()
+    kernel_ms = {kk: ms / prof for kk, (cnt, ms) in gs.gs_profile_query().items()}
+    gs.gs_profile_enable(False)
+    stage = stage_kernel_ms(kernel_ms)
+    blend_ms = sum(kernel_ms.get(kk, 0.0) for kk in BLEND_KERNELS)
+    # timed steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(pl, cams, targets, warm + prof, steps, gs=gs)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1000.0 / steps
+    # the projection on its own
+    gs.gs_profile_enable(True, "preprocess_fwd")
+    reps = 5
+    for _ in range(reps):
+        gs.gs_preprocess(pl.params, pl.deg, cams[0], pl.proj, pl.ws_pre, cfg=pl.cfg)
+    torch.cuda.synchronize()
+    pre = gs.gs_profile_query().get("preprocess_fwd", (1, 0.0))
+    gs.gs_profile_enable(False)
+    pl.projected_for = None
+    pre_ms = pre[1] / max(pre[0], 1)
+    pre_bytes = kernel_bytes("preprocess_fwd", n, deg, P)
+    chain_bytes = kernel_bytes("chain", n, deg, P, True)
+    pairs_avg = pairs_sum / prof
+    out = {
+        "workload": wl.name, "gaussians": n, "sh_degree": deg, "image": [cam0.width, cam0.height],
+        "pairs_per_step": int(pairs_avg), "visible_per_step": int(vis_sum / prof),
+        "iter_per_s": round(1000.0 / ms_step, 2), "ms_per_step": round(ms_step, 4), "steps": steps,
+        "stage_kernel_ms": stage,
+        "evals_per_step": {"fwd": ev_f // prof, "bwd": ev_b // prof},
+        "blend_ms": round(blend_ms, 4),
+        "blend_evals_per_s": round((ev_f + ev_b) / prof / (blend_ms / 1000.0), 1) if blend_ms > 0 else None,
+        "hbm": {
+            "preprocess_fwd": hbm_entry(pre_bytes, pre_ms, pre_bytes),
+            "bin_sort": hbm_entry(sbytes / prof, stage["bin_sort"], 16 * pairs_avg + 12 * n),
+            "chain_adam": hbm_entry(chain_bytes, kernel_ms.get("chain", 0.0), chain_bytes),
+        },
+        "setup_s": round(setup_s, 2),
+    }
+    if with_oracle:
+        dt, r = oracle_step_seconds(wl)
+        model, _ = host_cpu()
+        out["oracle"] = {"iter_per_s": round(1.0 / dt, 4), "s_per_step": round(dt, 3), "cores": 1,
+                         "cpu": model, "evals_per_step": int(r["fwd"]["evals"] + int(r["fwd"]["n_contrib"].sum()))}
+    del pl, params, targets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -381,17 +561,22 @@ def main():
     params2 = torch.from_numpy(wl.scene.params).cuda()
     pl2 = Pipeline(params2, deg, cam0.width, cam0.height, cfg=cfg)
     run_steps(pl2, cams, targets, 0, args.warmup, gs=gs, fuse=fuse)
+    torch.cuda.synchronize()
+    gs.gs_profile_enable(True)   # the replayed steps' kernel times, for the blend-only rate
     ev_f = ev_b = 0
     for s in range(args.steps):
         run_steps(pl2, cams, targets, args.warmup + s, 1, gs=gs, fuse=fuse)
         f, b = count_evals(pl2, torch)
         ev_f += f
         ev_b += b
+    torch.cuda.synchronize()
+    replay_ms = {k: ms / args.steps for k, (cnt, ms) in gs.gs_profile_query().items()}
+    gs.gs_profile_enable(False)
+    blend_ms = sum(replay_ms.get(k, 0.0) for k in BLEND_KERNELS)
     del pl2, params2
     densify = measure_densify(pl, cams, targets, args.warmup + args.steps, torch, gs) if not args.no_densify else None
     charbonnier = measure_charbonnier(pl, targets, torch, gs)
     camera_grad = measure_camera_grad(pl, cams[0], torch, gs)
-    t_fb = (stage[:, 2].sum() + stage[:, 4].sum()) / 1000.0
 
     # roofline of the dominant kernel from its live launch times
     dom_launches, dom_ms = live
@@ -423,8 +608,12 @@ def main():
                    "cameras": len(cams), "step": ("sort+fwd+loss+bwd+chain+adam+projection of the next camera (fused; one projection per step)"
                             if fuse else "preprocess+sort+fwd+loss+bwd+chain+adam (fused)"), "parallelism": "none",
                    "blend_split": split, "grad_sums": "fixed" if args.fixed_sums else "float"},
-        "evals_per_s": round((ev_f + ev_b) / t_fb, 1),
+        "evals_per_s": round((ev_f + ev_b) / args.steps / (blend_ms / 1000.0), 1),
+        "evals_basis": "Gaussian-pixel evaluations of the forward and backward walks over the blend kernels' "
+                       "time (forward walk with its split path, backward walk), same cameras replayed",
         "evals_per_step": {"fwd": ev_f // args.steps, "bwd": ev_b // args.steps},
+        "blend_ms_per_step": round(blend_ms, 4),
+        "stage_kernel_ms": stage_kernel_ms(replay_ms),
         "stage_ms": {k: round(float(stage[:, i].mean()), 4) for i, k in enumerate(StageTimer.NAMES)},
         "stage_ms_median": {k: round(float(np.median(stage[:, i])), 4) for i, k in enumerate(StageTimer.NAMES)},
         "kernel_ms_per_step": {k: round(v, 4) for k, v in sorted(kernel_ms.items(), key=lambda kv: -kv[1])},
@@ -435,9 +624,17 @@ def main():
         "camera_grad": camera_grad,
         "setup_s": round(setup_s, 2),
     }
+    if not args.no_configs and args.workload == WORKLOAD_CFG:
+        del pl, params, targets
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        out["configs"] = {str(k): measure_config(k, args.config_steps, torch, gs, scenes, Pipeline, cfg,
+                                                 with_oracle=not args.no_cpu_baseline and k <= 2)
+                          for k in (1, 2, 3, 4)}
     if not args.no_cpu_baseline and args.workload == WORKLOAD_CFG:
         cb = cpu_baseline(wl)
         out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        out["cpu_baseline"]["cpu"], out["cpu_baseline"]["host_cpus"] = host_cpu()
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
