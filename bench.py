@@ -52,8 +52,8 @@ def kernel_bytes(kernel, n, deg, P, fuse=True):
 # kernels by stage (the names the library's per-kernel timing uses)
 STAGE_KERNELS = {
     "preprocess": ("preprocess_fwd", "sum_counts"),
-    "bin_sort": ("radix_upsweep", "radix_scan", "radix_downsweep", "scan_reduce", "scan_apply", "block_starts",
-                 "emit_pairs", "tile_ranges", "fill_u32"),
+    "bin_sort": ("radix_upsweep", "radix_scan", "radix_downsweep", "scan_reduce", "scan_apply", "emit_pairs",
+                 "tile_ranges", "fill_u32"),
     "render_fwd": ("render_fwd", "tile_order", "split_init", "split_chunk", "split_combine", "split_rewalk",
                    "split_finalize"),
     "loss": ("ssim", "loss_finalize"),
@@ -71,24 +71,23 @@ def stage_kernel_ms(kernel_ms):
 
 
 def sort_bytes(n, vis, pairs, num_tiles, depth_passes):
-    """Algorithmic HBM bytes of one bin/sort (the passes the kernels make; 9-bit digits):
+    """Algorithmic HBM bytes of one bin/sort (the passes the kernels make):
 
     per Gaussian      counts zeroed 4, pass 0 reads depth and tile count twice (upsweep,
                       downsweep) 16, the offsets scan reads counts twice and writes offsets 12
     per visible one   pass 0 writes key and id 8; every further depth pass reads the key
                       (upsweep) 4 and key and id 8 (downsweep) and writes them 8, the last
                       one writing no key but the id 4, the gathered rectangle 8 and tile
-                      count 4 (and reading the rectangle 8); block starts read the offsets
-                      4; the emit reads offset, id and rectangle 16
-    per pair          emit writes tile and id 8; every tile pass reads and writes them 16,
-                      those after the first also read the tile 4 for their histogram;
-                      tile ranges read the tile 4
-    per tile          ranges cleared and written 16"""
+                      count 4 (and reading the rectangle 8); the emit reads two offsets, the
+                      id and the rectangle 20
+    per pair          emit writes tile and id 8; every tile pass reads the tile (upsweep) 4
+                      and reads and writes tile and id (downsweep) 16
+    per tile          the range search writes both ends 8 (its reads are a few per tile)"""
     tile_bits = max(int(num_tiles - 1).bit_length(), 0)
     tile_passes = (tile_bits + 8) // 9
-    per_vis = 8 + (depth_passes - 2) * 20 + (4 + 8 + 4 + 4 + 8 + 8) + 4 + 16
-    per_pair = 8 + 16 * tile_passes + 4 * max(tile_passes - 1, 0) + 4
-    return 32 * n + per_vis * vis + per_pair * pairs + 16 * num_tiles
+    per_vis = 8 + (depth_passes - 2) * 20 + (4 + 8 + 4 + 4 + 8 + 8) + 20
+    per_pair = 8 + 20 * tile_passes
+    return 32 * n + per_vis * vis + per_pair * pairs + 8 * num_tiles
 
 
 def depth_passes_of(pl, cam, torch):

@@ -12,23 +12,22 @@
 //                 its launches returning at once otherwise.  The device picks every
 //                 pass's buffers from that count, so that the last pass lands in the
 //                 order array; it also gathers each Gaussian's tile rectangle and count.
-//   emit          their tile counts, in that order, are prefix-summed; one thread
-//                 per pair finds its Gaussian by binary search in the sums and
-//                 writes (tile id, Gaussian id): the pairs of each Gaussian are
-//                 consecutive and the Gaussians are in (depth, id) order.  Each block
-//                 of 4096 pairs also counts the first tile digit: the histogram of the
-//                 first tile pass.
-//   tile sort     a stable LSD radix sort of the pairs by tile id, so within a
-//                 tile they keep the (depth, id) order.
-//   tile_ranges   first / one-past-last pair of each tile.
+//   emit          their tile counts, in that order, are prefix-summed; the pairs are
+//                 written in blocks of consecutive pairs, (tile id, Gaussian id) for the
+//                 tiles of each Gaussian's rectangle: the pairs of each Gaussian are
+//                 consecutive and the Gaussians are in (depth, id) order.
+//   tile sort     a stable LSD radix sort of the pairs by tile id (its bits split evenly
+//                 over the passes), so within a tile they keep the (depth, id) order.
+//   tile_ranges   first / one-past-last pair of each tile, by a 64-ary search per tile.
 //
-// Radix passes use 9-bit digits, reduce-then-scan:
-//   upsweep   per-block digit histogram (LDS atomics) into a digit-major [512][blocks] table
+// Radix passes use digits of up to 9 bits, reduce-then-scan:
+//   upsweep   per-block digit histogram (LDS atomics; for tile digits, which crowd, one
+//             atomic per distinct digit of a wave) into a digit-major [512][blocks] table
 //   scan      one block per digit: exclusive prefix along its row, and the row total
 //   downsweep the digit bases from the 512 row totals; each wave ranks its 1024
-//             consecutive items against a wave-private digit histogram (64-lane
-//             ballots: no match-any on CDNA, 9 ballots give each lane its peer mask),
-//             one barrier turns the four histograms into run starts, then a local
+//             consecutive items against a wave-private digit histogram (64-lane ballots:
+//             no match-any on CDNA, one ballot per digit bit gives each lane its peer
+//             mask), one barrier turns the four histograms into run starts, then a local
 //             reorder through LDS and a coalesced scatter.
 // Sorting the Gaussians by depth once, instead of every pair by a 64-bit (tile, depth)
 // key, replaces six passes over 12-byte pairs by three passes over the visible
@@ -181,15 +180,15 @@ __global__ void __launch_bounds__(kSortThreads) radix_upsweep_kernel(PassIn in, 
       }
     } else {
       // tile digits crowd (a block's pairs come from few screen regions): one LDS atomic
-      // per distinct digit of a wave's 64 items (9 ballots give each lane its peers; the
-      // lowest lane adds their number)
+      // per distinct digit of a wave's 64 items (a ballot per digit bit gives each lane
+      // its peers; the lowest lane adds their number)
       const uint64_t lt_mask = (uint64_t(1) << __lane_id()) - 1;
+      const int nbits = __popc(mask);
 #pragma unroll
       for (int k = 0; k < kSortItems; ++k) {
         const uint32_t d = (key[k] >> shift) & mask;
         uint64_t peers = __ballot(ok[k]);
-#pragma unroll
-        for (int b = 0; b < kDigitBits; ++b) {
+        for (int b = 0; b < nbits; ++b) {
           const bool bit = (d >> b) & 1u;
           const uint64_t m = __ballot(bit);
           peers &= bit ? m : ~m;
@@ -301,12 +300,13 @@ __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
   __syncthreads();
   // Each wave ranks its own 1024 consecutive items, 64 per round, with a wave-private
   // digit histogram: an item's rank among equal digits of its wave is the histogram
-  // before its round plus its rank in the round (9 ballots give each lane its peers;
+  // before its round plus its rank in the round (a ballot per digit bit gives each lane its peers;
   // CDNA has no match-any).  Waves, rounds and lanes follow the items' order, so the
   // placement is stable.
   constexpr int kWaveItems = kSortTile / kWaves;
   constexpr int kRounds = kWaveItems / 64;
   const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
+  const int nbits = __popc(mask);
   uint32_t key[kRounds], val[kRounds], rk[kRounds];
   bool ok[kRounds];
 #pragma unroll
@@ -319,8 +319,7 @@ __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
     const bool valid = ok[r];
     const uint32_t d = (key[r] >> shift) & mask;
     uint64_t peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < kDigitBits; ++b) {
+    for (int b = 0; b < nbits; ++b) {
       const bool bit = (d >> b) & 1u;
       const uint64_t m = __ballot(bit);
       peers &= bit ? m : ~m;
@@ -403,71 +402,111 @@ __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
   }
 }
 
-// For every block of 256 pairs, the visible Gaussian (in depth order) that owns its
-// first pair: Gaussian r owns pairs [offs[r], offs[r + 1]) and marks the blocks
-// whose first pair falls there.  One thread per Gaussian.
+// Pairs of the visible Gaussians in depth order: Gaussian r (its id order[r], its tile
+// rectangle rect_order[r]) owns pairs [offs[r], offs[r + 1]) and writes (tile id, id) for
+// the tiles of its rectangle in row-major order.  A block writes kEmitPairs consecutive
+// pairs: block_first[block] is the Gaussian owning its first pair; the offsets of the
+// Gaussians owning its pairs go to LDS (256 at a time, until they pass the block's end);
+// each thread finds the owner of its first pair by binary search and walks kEmitPerThread
+// consecutive pairs (stepping the rectangle's column and row), staging them in LDS; the
+// block then writes them out coalesced.  Pairs past offs[n_vis] (only if total_pairs
+// disagrees with the projection) get the tile 0xffffffff.
+constexpr int kEmitPerThread = 8;
+constexpr int kEmitPairs = 256 * kEmitPerThread;
+
+// block_first[b]: the visible Gaussian that owns pair b * kEmitPairs (the last one for a
+// block past offs[n_vis]).  One thread per visible Gaussian.
 __global__ void __launch_bounds__(256) block_starts_kernel(const uint32_t* __restrict__ offs,
                                                             const uint32_t* __restrict__ n_vis, int n,
                                                             uint32_t pairs, uint32_t* __restrict__ block_first) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= n || uint32_t(r) >= *n_vis) return;
-  const uint32_t b0 = (offs[r] + 255u) >> 8, e = min(offs[r + 1], pairs);
-  for (uint32_t b = b0; (b << 8) < e; ++b) block_first[b] = uint32_t(r);
+  const int nv = int(*n_vis);
+  if (r >= n || r >= nv) return;
+  const uint32_t e = r == nv - 1 ? max(offs[r + 1], pairs) : min(offs[r + 1], pairs);
+  for (uint32_t b = (offs[r] + kEmitPairs - 1) / kEmitPairs; b * uint32_t(kEmitPairs) < e; ++b) block_first[b] = uint32_t(r);
 }
 
-// One thread per pair: the Gaussian (in depth order) that owns it, and its tile.
-// offs[r] is the first pair of the r-th visible Gaussian in depth order and
-// rect_order[r] its tile rectangle.  A block covers 4096 pairs (one radix block) in
-// pieces of 256: a piece belongs to at most 256 consecutive Gaussians starting with
-// block_first[piece]; their offsets go to LDS and each thread searches there.  With
-// hist, the block also counts the tiles' low digit (key & mask), hist[d][block]: the
-// upsweep of the first tile pass.
 __global__ void __launch_bounds__(256) emit_pairs_kernel(const uint32_t* __restrict__ offs,
                                                           const uint32_t* __restrict__ n_vis,
                                                           const uint32_t* __restrict__ block_first,
                                                           const uint32_t* __restrict__ order,
-                                                          const uint2* __restrict__ rect_order, int n, uint32_t pairs,
+                                                          const uint2* __restrict__ rect_order, uint32_t pairs,
                                                           int tx, uint32_t* __restrict__ keys,
-                                                          uint32_t* __restrict__ vals, int nb, uint32_t mask,
-                                                          uint32_t* __restrict__ hist) {
-  __shared__ uint32_t s_offs[256];
-  __shared__ uint32_t s_hist[kRadix];
-  for (int d = threadIdx.x; d < kRadix; d += 256) s_hist[d] = 0u;
-  const int nv = int(*n_vis);
-  for (int piece = 0; piece < kSortTile / 256; ++piece) {
-    const uint32_t p0 = blockIdx.x * uint32_t(kSortTile) + uint32_t(piece) * 256u;
-    if (p0 >= pairs) break;   // uniform
-    const uint32_t bf = block_first[p0 >> 8];
-    const int r0 = int(bf < uint32_t(nv) ? bf : uint32_t(max(nv - 1, 0)));
-    // Gaussians past the visible ones (or past the piece) get an offset above every pair
-    const int k = min(256, nv - r0);
-    __syncthreads();   // the previous piece's searches are done (and s_hist is zeroed)
-    s_offs[threadIdx.x] = int(threadIdx.x) < k ? offs[r0 + int(threadIdx.x)] : 0xffffffffu;
-    __syncthreads();
-    const uint32_t p = p0 + threadIdx.x;
-    if (p >= pairs) continue;
-    int lo = 0, hi = max(k, 1) - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_offs[mid] <= p) lo = mid; else hi = mid - 1;
-    }
-    const uint32_t g = order[r0 + lo];
-    uint32_t key = 0xffffffffu, val = 0u;   // only if total_pairs disagrees with the projection
-    if (g < uint32_t(n)) {
-      const uint32_t j = p - s_offs[lo];
-      const uint2 r = rect_order[r0 + lo];
-      const uint32_t x0 = r.x & 0xffffu, y0 = r.x >> 16, x1 = r.y & 0xffffu;
-      const uint32_t w = x1 - x0 + 1;
-      key = (y0 + j / w) * uint32_t(tx) + (x0 + j % w);
-      val = g;
-    }
-    keys[p] = key;
-    vals[p] = val;
-    if (hist) atomicAdd(&s_hist[key & mask], 1u);
+                                                          uint32_t* __restrict__ vals) {
+  __shared__ uint32_t s_offs[kEmitPairs + 256];
+  __shared__ uint32_t s_key[kEmitPairs], s_val[kEmitPairs];
+  __shared__ uint32_t s_k;
+  const int tid = threadIdx.x;
+  const uint32_t nv = *n_vis;
+  const uint32_t p0 = blockIdx.x * uint32_t(kEmitPairs);
+  const uint32_t pend = min(p0 + uint32_t(kEmitPairs), pairs);
+  const uint32_t r0 = min(block_first[blockIdx.x], nv);
+  // offsets of Gaussians r0, r0 + 1, ... (offs[nv] is the pair count: an end marker)
+  uint32_t k = 0;
+  for (;;) {
+    const uint32_t r = r0 + k + uint32_t(tid);
+    const uint32_t o = r <= nv ? offs[r] : 0xffffffffu;
+    s_offs[k + tid] = o;
+    // the chunk is the last one needed once some loaded offset reaches the block's end
+    const int past = __syncthreads_count(o >= pend);
+    k += 256;
+    if (past > 0 || k >= uint32_t(kEmitPairs)) break;
   }
-  if (!hist) return;
+  if (tid == 0) s_k = k;
   __syncthreads();
-  for (int d = threadIdx.x; d < kRadix; d += 256) hist[size_t(d) * nb + blockIdx.x] = s_hist[d];
+  const uint32_t kk = s_k;
+  const uint32_t q0 = p0 + uint32_t(tid) * kEmitPerThread;
+  if (q0 < pend) {
+    // owner of q0: the last i with s_offs[i] <= q0
+    uint32_t lo = 0, hi = kk - 1;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi + 1) >> 1;
+      if (s_offs[mid] <= q0) lo = mid; else hi = mid - 1;
+    }
+    uint32_t i = lo;
+    uint32_t next = i + 1 < kk ? s_offs[i + 1] : 0xffffffffu;
+    uint32_t g = 0u, x = 0u, x0 = 0u, x1 = 0u, row = 0u;
+    bool valid = false;
+    auto owner = [&](uint32_t q) {
+      const uint32_t r = r0 + i;
+      valid = r < nv;
+      if (!valid) return;
+      g = order[r];
+      const uint2 rc = rect_order[r];
+      x0 = rc.x & 0xffffu;
+      x1 = rc.y & 0xffffu;
+      const uint32_t w = x1 - x0 + 1u, j = q - s_offs[i];
+      x = x0 + j % w;
+      row = ((rc.x >> 16) + j / w) * uint32_t(tx);
+    };
+    owner(q0);
+#pragma unroll
+    for (int m = 0; m < kEmitPerThread; ++m) {
+      const uint32_t q = q0 + uint32_t(m);
+      if (q >= pend) break;
+      if (m > 0) {
+        if (q >= next) {   // a new Gaussian starts here (each owns at least one pair)
+          ++i;
+          next = i + 1 < kk ? s_offs[i + 1] : 0xffffffffu;
+          owner(q);
+        } else if (++x > x1) {
+          x = x0;
+          row += uint32_t(tx);
+        }
+      }
+      s_key[tid * kEmitPerThread + m] = valid ? row + x : 0xffffffffu;
+      s_val[tid * kEmitPerThread + m] = valid ? g : 0u;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < kEmitPerThread; ++m) {
+    const uint32_t at = uint32_t(tid + 256 * m);
+    if (p0 + at < pend) {
+      keys[p0 + at] = s_key[at];
+      vals[p0 + at] = s_val[at];
+    }
+  }
 }
 
 __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t count, uint32_t value) {
@@ -489,34 +528,40 @@ void zero_u32(uint32_t* p, int64_t count, hipStream_t s) {
   if (count > 4 * c4) fill_u32_kernel<<<div_up(count - 4 * c4, 256), 256, 0, s>>>(p + 4 * c4, count - 4 * c4, 0u);
 }
 
-// Four consecutive pairs per thread (one 16-byte load when the keys are 16-byte
-// aligned); a pair whose tile differs from its left neighbour starts that tile's
-// range, one whose tile differs from its right neighbour ends it.
+// One wave per tile t, four tiles per block: the first index in the sorted tiles whose
+// tile is >= t and the first whose tile is >= t + 1 (pairs if none), both by a 64-ary
+// search, one sample per lane per level; the range is (0, 0) when empty.
 __global__ void __launch_bounds__(256) tile_ranges_kernel(const uint32_t* __restrict__ tile_of_pair, uint32_t pairs,
-                                                           int num_tiles, uint32_t* __restrict__ ranges,
-                                                           bool aligned) {
-  const uint32_t i0 = 4u * (blockIdx.x * blockDim.x + threadIdx.x);
-  if (i0 >= pairs) return;
-  uint32_t t[4];
-  if (aligned && i0 + 3 < pairs) {
-    const uint4 q = reinterpret_cast<const uint4*>(tile_of_pair)[i0 / 4];
-    t[0] = q.x; t[1] = q.y; t[2] = q.z; t[3] = q.w;
-  } else {
+                                                           int num_tiles, uint32_t* __restrict__ ranges) {
+  const uint32_t t = blockIdx.x * 4u + (threadIdx.x >> 6);
+  if (t >= uint32_t(num_tiles)) return;
+  const uint32_t lane = __lane_id();
+  uint32_t lo[2] = {0u, 0u}, hi[2] = {pairs, pairs};   // each answer lies in [lo, hi]
+  while (hi[0] - lo[0] > 64u || hi[1] - lo[1] > 64u) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) t[k] = i0 + k < pairs ? tile_of_pair[i0 + k] : 0u;
+    for (int b = 0; b < 2; ++b) {
+      if (hi[b] - lo[b] <= 64u) continue;   // uniform per wave
+      const uint32_t step = (hi[b] - lo[b] + 63u) / 64u;
+      const uint32_t at = lo[b] + lane * step;
+      const uint32_t c = __popcll(__ballot(at < hi[b] && tile_of_pair[at] < t + uint32_t(b)));
+      if (c > 0) {
+        const uint32_t nlo = lo[b] + (c - 1u) * step + 1u;
+        hi[b] = min(hi[b], lo[b] + c * step);
+        lo[b] = nlo;
+      } else {
+        hi[b] = lo[b];
+      }
+    }
   }
-  const uint32_t left = i0 > 0 ? tile_of_pair[i0 - 1] : 0u;
-  const uint32_t right = i0 + 4 < pairs ? tile_of_pair[i0 + 4] : 0u;
+  uint32_t e[2];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t i = i0 + k;
-    if (i >= pairs) break;
-    const uint32_t tk = t[k];
-    if (tk >= uint32_t(num_tiles)) continue;   // only if total_pairs disagrees with the tile counts
-    const uint32_t l = k == 0 ? left : t[k - 1];
-    const uint32_t r = k == 3 ? right : t[k + 1];
-    if (i == 0 || l != tk) ranges[tk] = i;
-    if (i == pairs - 1 || r != tk) ranges[num_tiles + tk] = i + 1;
+  for (int b = 0; b < 2; ++b) {
+    const uint32_t at = lo[b] + lane;
+    e[b] = lo[b] + uint32_t(__popcll(__ballot(at < hi[b] && tile_of_pair[at] < t + uint32_t(b))));
+  }
+  if (lane == 0) {
+    ranges[t] = e[0] < e[1] ? e[0] : 0u;
+    ranges[num_tiles + t] = e[0] < e[1] ? e[1] : 0u;
   }
 }
 
@@ -582,7 +627,7 @@ size_t carve_depth(void* ws, int64_t n, DepthWs* out) {
 
 struct PairWs {
   uint32_t *keys_alt, *vals_alt;   // pairs each
-  uint32_t* block_first;           // one per 256 pairs
+  uint32_t* block_first;           // one per emit block
   RadixWs r;
 };
 
@@ -591,20 +636,19 @@ size_t carve_pairs(void* ws, uint32_t pairs, PairWs* out) {
   PairWs w;
   w.keys_alt = c.take(size_t(pairs) * 4);
   w.vals_alt = c.take(size_t(pairs) * 4);
-  w.block_first = c.take(size_t(div_up(pairs > 0 ? pairs : 1, 256)) * 4);
+  w.block_first = c.take(size_t(div_up(pairs > 0 ? pairs : 1, kEmitPairs)) * 4);
   w.r = carve_radix(c, blocks_for(pairs));
   if (out) *out = w;
   return c.off;
 }
 
-// One radix pass over the bits-wide digit at `shift`; without upsweep, w.hist already
-// holds this pass's block histograms.
+// One radix pass over the bits-wide digit at `shift`.
 template <int SRC>
 hipError_t radix_pass(const PassIn& in, const DepthPlan& dp, int nb, int shift, int bits, const RadixWs& w,
-                      bool upsweep, uint32_t* keys_out, uint32_t* vals_out, uint32_t* count_out,
-                      const uint2* val_rect, uint2* rect_out, uint32_t* counts_out, hipStream_t s) {
+                      uint32_t* keys_out, uint32_t* vals_out, uint32_t* count_out, const uint2* val_rect,
+                      uint2* rect_out, uint32_t* counts_out, hipStream_t s) {
   const uint32_t mask = (1u << bits) - 1u;
-  if (upsweep) {
+  {
     GSK_PROF("radix_upsweep", s);
     radix_upsweep_kernel<SRC><<<nb, kSortThreads, 0, s>>>(in, dp, shift, mask, nb, w.hist);
   }
@@ -643,14 +687,14 @@ hipError_t launch_depth_order(const gs_proj& proj, int n, float znear, void* ws,
   // lands in proj.order and writes their rectangles and counts in that order
   {
     PassIn in{nullptr, nullptr, proj.depth, proj.tiles, key_base, uint32_t(n), nullptr};
-    if ((e = radix_pass<kFromDepth>(in, dp, nb, 0, kDigitBits, w.r, true, nullptr, nullptr, proj.n_visible, rect,
+    if ((e = radix_pass<kFromDepth>(in, dp, nb, 0, kDigitBits, w.r, nullptr, nullptr, proj.n_visible, rect,
                                     rect_order, w.counts, s)) != hipSuccess)
       return e;
   }
   for (int pass = 1; pass < kDepthPassesMax; ++pass) {
     dp.pass = pass;
     PassIn in{nullptr, nullptr, nullptr, nullptr, 0u, 0u, proj.n_visible};
-    if ((e = radix_pass<kFromKeys>(in, dp, nb, kDigitBits * pass, kDigitBits, w.r, true, nullptr, nullptr, nullptr,
+    if ((e = radix_pass<kFromKeys>(in, dp, nb, kDigitBits * pass, kDigitBits, w.r, nullptr, nullptr, nullptr,
                                    rect, rect_order, w.counts, s)) != hipSuccess)
       return e;
   }
@@ -679,7 +723,7 @@ hipError_t launch_sort_pairs_u32(uint32_t* keys, uint32_t* vals, uint32_t count,
     const bool even = (pass & 1) == 0;
     PassIn in{even ? keys : alt_k, even ? vals : alt_v, nullptr, nullptr, 0u, count, nullptr};
     const hipError_t e = radix_pass<kFromKeys>(in, kNoPlan, nb, kDigitBits * pass, std::min(kDigitBits, 32 - kDigitBits * pass),
-                                               r, true, even ? alt_k : keys, even ? alt_v : vals, nullptr, nullptr,
+                                               r, even ? alt_k : keys, even ? alt_v : vals, nullptr, nullptr,
                                                nullptr, nullptr, s);
     if (e != hipSuccess) return e;
   }
@@ -692,11 +736,11 @@ hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uin
                            uint32_t* vals, uint32_t* ranges, void* ws, hipStream_t s) {
   const int tx = tiles_x(cam), ty = tiles_y(cam);
   const int num_tiles = tx * ty;
-  {
+  if (pairs == 0) {   // every tile empty (with pairs, the range search writes every entry)
     GSK_PROF("fill_u32", s);
     fill_u32_kernel<<<div_up(2 * int64_t(num_tiles), 256), 256, 0, s>>>(ranges, 2 * int64_t(num_tiles), 0u);
+    return hipGetLastError();
   }
-  if (pairs == 0) return hipGetLastError();
   PairWs w;
   carve_pairs(ws, pairs, &w);
   hipError_t e;
@@ -711,30 +755,29 @@ hipError_t launch_bin_sort(const gs_proj& proj, int n, const gs_camera& cam, uin
   uint32_t* k_dst = (tile_passes & 1) ? keys : w.keys_alt;
   uint32_t* v_dst = (tile_passes & 1) ? vals : w.vals_alt;
   const int nbp = blocks_for(pairs);
+  const int nbe = int(div_up(pairs, kEmitPairs));
   {
     GSK_PROF("block_starts", s);
     block_starts_kernel<<<div_up(n, 256), 256, 0, s>>>(proj.offs, proj.n_visible, n, pairs, w.block_first);
   }
   {
     GSK_PROF("emit_pairs", s);
-    emit_pairs_kernel<<<nbp, 256, 0, s>>>(proj.offs, proj.n_visible, w.block_first, proj.order,
-                                          reinterpret_cast<const uint2*>(proj.rect_order), n, pairs, tx, k_src,
-                                          v_src, nbp, (1u << low_bits) - 1u, tile_passes > 0 ? w.r.hist : nullptr);
+    emit_pairs_kernel<<<nbe, 256, 0, s>>>(proj.offs, proj.n_visible, w.block_first, proj.order,
+                                          reinterpret_cast<const uint2*>(proj.rect_order), pairs, tx, k_src, v_src);
   }
-  // stable sort of the pairs by tile (the first pass's histogram came with the emit)
+  // stable sort of the pairs by tile
   for (int pass = 0; pass < tile_passes; ++pass) {
     PassIn in{k_src, v_src, nullptr, nullptr, 0u, pairs, nullptr};
     const int shift = low_bits * pass, bits = std::min(low_bits, tile_bits - shift);
-    if ((e = radix_pass<kFromKeys>(in, kNoPlan, nbp, shift, bits, w.r, pass > 0, k_dst, v_dst, nullptr, nullptr,
-                                   nullptr, nullptr, s)) != hipSuccess)
+    if ((e = radix_pass<kFromKeys>(in, kNoPlan, nbp, shift, bits, w.r, k_dst, v_dst, nullptr, nullptr, nullptr,
+                                   nullptr, s)) != hipSuccess)
       return e;
     uint32_t* tk = k_src; k_src = k_dst; k_dst = tk;
     uint32_t* tv = v_src; v_src = v_dst; v_dst = tv;
   }
   {
     GSK_PROF("tile_ranges", s);
-    tile_ranges_kernel<<<div_up(div_up(pairs, 4), 256), 256, 0, s>>>(
-        keys, pairs, num_tiles, ranges, reinterpret_cast<uintptr_t>(keys) % 16 == 0);
+    tile_ranges_kernel<<<div_up(num_tiles, 4), 256, 0, s>>>(keys, pairs, num_tiles, ranges);
   }
   return hipGetLastError();
 }
