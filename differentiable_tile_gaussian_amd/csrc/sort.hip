@@ -22,7 +22,8 @@
 //
 // Radix passes use digits of up to 9 bits, reduce-then-scan:
 //   upsweep   per-block digit histogram (LDS atomics; for tile digits, which crowd, one
-//             atomic per distinct digit of a wave) into a digit-major [512][blocks] table
+//             atomic per distinct digit of a wave) into a [512][blocks] table (blocks in an
+//             XCD-aware order, below)
 //   scan      one block per digit: exclusive prefix along its row, and the row total
 //   downsweep the digit bases from the 512 row totals; each wave ranks its 1024
 //             consecutive items against a wave-private digit histogram (64-lane ballots:
@@ -49,6 +50,19 @@ constexpr int kDigitBits = 9;
 constexpr int kRadix = 1 << kDigitBits;                 // 512 digits
 constexpr int kDepthPasses = 3;                         // always made: d < 2^27
 constexpr int kDepthPassesMax = 4;                      // 36 bits >= the 31 of d
+
+// The histogram tables hold one count per (digit, block) in an XCD-aware order.  Blocks
+// are handed to the chip's 8 XCDs in turn (block b on XCD b % 8), each XCD with its own
+// L2; a digit's entries of the 16 blocks b, b + 8, ..., b + 120 that share an XCD fill one
+// 64-byte line, so the blocks' scattered 4-byte writes and reads of a digit meet in that
+// L2 instead of each taking a line of HBM traffic.  Blocks go in groups of 128: a group
+// holds, per digit, 128 entries, block 128 g + 8 k + x at position 16 x + k.
+constexpr int kHistGroup = 128;
+__host__ __device__ inline size_t hist_at(uint32_t d, uint32_t b) {
+  const uint32_t g = b / kHistGroup, w = b % kHistGroup;
+  return (size_t(g) * kRadix + d) * kHistGroup + (w % 8u) * 16u + w / 8u;
+}
+inline size_t hist_entries(int nb) { return size_t((nb + kHistGroup - 1) / kHistGroup) * kRadix * kHistGroup; }
 
 // Where a radix pass reads its items from.
 enum Source {
@@ -206,49 +220,70 @@ __global__ void __launch_bounds__(kSortThreads) radix_upsweep_kernel(PassIn in, 
     if (threadIdx.x == 0) dp.bmax[blockIdx.x] = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
   }
   __syncthreads();
-  for (int d = threadIdx.x; d < kRadix; d += kSortThreads) hist[size_t(d) * nb + blockIdx.x] = s_hist[d];
+  for (int d = threadIdx.x; d < kRadix; d += kSortThreads) hist[hist_at(d, blockIdx.x)] = s_hist[d];
 }
 
 // One block per digit: hist_scan[d][b] = sum of hist[d][b'] over b' < b, rowtot[d] the row sum.
-// In the depth sort's first pass, block 0 also reduces the blocks' maxima of d.
+// In the depth sort's first pass, block 0 also reduces the blocks' maxima of d.  The row is
+// taken eight groups (1024 blocks) at a time: loaded in table order (coalesced), put in
+// block order through LDS, scanned, and written back in table order.
 __global__ void __launch_bounds__(kSortThreads) radix_scan_kernel(DepthPlan dp, int nb,
                                                                    const uint32_t* __restrict__ hist,
                                                                    uint32_t* __restrict__ hist_scan,
                                                                    uint32_t* __restrict__ rowtot) {
+  constexpr int kChunk = 8 * kHistGroup;   // blocks per step, four per thread
   __shared__ uint32_t s_scan[2 * kWaves];
+  __shared__ uint32_t s_v[kChunk];
   if (!pass_runs(dp)) return;
+  const int tid = threadIdx.x;
   if (dp.pass == 0 && blockIdx.x == 0) {
     uint32_t m = 0u;
-    for (int b = threadIdx.x; b < nb; b += kSortThreads) m = max(m, dp.bmax[b]);
+    for (int b = tid; b < nb; b += kSortThreads) m = max(m, dp.bmax[b]);
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) m = max(m, uint32_t(__shfl_xor(m, d, 64)));
-    if (__lane_id() == 0) s_scan[threadIdx.x >> 6] = m;
+    if (__lane_id() == 0) s_scan[tid >> 6] = m;
     __syncthreads();
-    if (threadIdx.x == 0) *dp.dmax = max(max(s_scan[0], s_scan[1]), max(s_scan[2], s_scan[3]));
+    if (tid == 0) *dp.dmax = max(max(s_scan[0], s_scan[1]), max(s_scan[2], s_scan[3]));
     __syncthreads();
   }
-  constexpr int kPer = 4;
-  const uint32_t* row = hist + size_t(blockIdx.x) * nb;
-  uint32_t* out = hist_scan + size_t(blockIdx.x) * nb;
+  const uint32_t d = blockIdx.x;
+  const int groups = (nb + kHistGroup - 1) / kHistGroup;
   uint32_t carry = 0u;
-  for (int base = 0; base < nb; base += kSortThreads * kPer) {
-    const int i0 = base + int(threadIdx.x) * kPer;
-    uint32_t v[kPer], sum = 0u;
+  for (int g0 = 0; g0 < groups; g0 += 8) {
+    // table position j (group g0 + j / 128, place j % 128) holds block 128 (g0 + j / 128)
+    // + 8 (place % 16) + place / 16; b0 = that block less 128 g0
+    size_t at[4];
+    uint32_t b0[4];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      v[k] = i0 + k < nb ? row[i0 + k] : 0u;
+    for (int k = 0; k < 4; ++k) {
+      const int j = tid + kSortThreads * k, g = g0 + j / kHistGroup, place = j % kHistGroup;
+      b0[k] = uint32_t(j / kHistGroup) * kHistGroup + uint32_t(place % 16) * 8u + uint32_t(place / 16);
+      at[k] = (size_t(g) * kRadix + d) * kHistGroup + size_t(place);
+      // blocks past nb (the last group's padding, never written) count 0
+      s_v[b0[k]] = uint32_t(g0) * kHistGroup + b0[k] < uint32_t(nb) ? hist[at[k]] : 0u;
+    }
+    __syncthreads();
+    uint32_t v[4], sum = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = s_v[4 * tid + k];
       sum += v[k];
     }
     uint32_t total, unused;
-    uint32_t run = carry + block_scan2(sum, 0u, s_scan, total, unused).x;
+    uint32_t run = carry + block_scan2(sum, 0u, s_scan, total, unused).x;   // (its barriers order s_v)
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      if (i0 + k < nb) out[i0 + k] = run;
+    for (int k = 0; k < 4; ++k) {
+      s_v[4 * tid + k] = run;
       run += v[k];
     }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (uint32_t(g0) * kHistGroup + b0[k] < uint32_t(nb)) hist_scan[at[k]] = s_v[b0[k]];
     carry += total;
+    __syncthreads();   // s_v is loaded again
   }
-  if (threadIdx.x == 0) rowtot[blockIdx.x] = carry;
+  if (tid == 0) rowtot[d] = carry;
 }
 
 // With count_out, block 0 stores the number of items (for kFromDepth, of visible
@@ -281,7 +316,7 @@ __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
   // the digit bases: exclusive prefix of the row totals, plus the earlier blocks' counts
   // of the digit (block 0 also stores the number of items)
   {
-    const uint32_t g0 = hist_scan[size_t(d0) * nb + blockIdx.x], g1 = hist_scan[size_t(d0 + 1) * nb + blockIdx.x];
+    const uint32_t g0 = hist_scan[hist_at(d0, blockIdx.x)], g1 = hist_scan[hist_at(d0 + 1, blockIdx.x)];
     const uint32_t r0 = rowtot[d0], r1 = rowtot[d0 + 1];
     uint32_t all_total, unused;
     const uint32_t pre = block_scan2(r0 + r1, 0u, s_scan, all_total, unused).x;
@@ -587,15 +622,15 @@ struct Carver {
 };
 
 struct RadixWs {
-  uint32_t *hist, *hist_scan;   // kRadix * nb each
+  uint32_t *hist, *hist_scan;   // hist_entries(nb) each
   uint32_t* rowtot;             // kRadix
 };
 
 RadixWs carve_radix(Carver& c, int nb) {
-  const int64_t hist_n = int64_t(kRadix) * nb;
+  const size_t hist_n = hist_entries(nb);
   RadixWs w;
-  w.hist = c.take(size_t(hist_n) * 4);
-  w.hist_scan = c.take(size_t(hist_n) * 4);
+  w.hist = c.take(hist_n * 4);
+  w.hist_scan = c.take(hist_n * 4);
   w.rowtot = c.take(size_t(kRadix) * 4);
   return w;
 }
