@@ -468,8 +468,10 @@ __global__ void __launch_bounds__(256) emit_pairs_kernel(const uint32_t* __restr
                                                           const uint2* __restrict__ rect_order, uint32_t pairs,
                                                           int tx, uint32_t* __restrict__ keys,
                                                           uint32_t* __restrict__ vals) {
+  // staged pair q at q + q / 32: a thread's eight consecutive pairs (stride 8 across the
+  // wave) then fall at most two to an LDS bank, and the read-out's consecutive ones none
   __shared__ uint32_t s_offs[kEmitPairs + 256];
-  __shared__ uint32_t s_key[kEmitPairs], s_val[kEmitPairs];
+  __shared__ uint32_t s_key[kEmitPairs + kEmitPairs / 32], s_val[kEmitPairs + kEmitPairs / 32];
   __shared__ uint32_t s_k;
   const int tid = threadIdx.x;
   const uint32_t nv = *n_vis;
@@ -529,8 +531,9 @@ __global__ void __launch_bounds__(256) emit_pairs_kernel(const uint32_t* __restr
           row += uint32_t(tx);
         }
       }
-      s_key[tid * kEmitPerThread + m] = valid ? row + x : 0xffffffffu;
-      s_val[tid * kEmitPerThread + m] = valid ? g : 0u;
+      const uint32_t at = uint32_t(tid * kEmitPerThread + m);
+      s_key[at + at / 32u] = valid ? row + x : 0xffffffffu;
+      s_val[at + at / 32u] = valid ? g : 0u;
     }
   }
   __syncthreads();
@@ -538,8 +541,8 @@ __global__ void __launch_bounds__(256) emit_pairs_kernel(const uint32_t* __restr
   for (int m = 0; m < kEmitPerThread; ++m) {
     const uint32_t at = uint32_t(tid + 256 * m);
     if (p0 + at < pend) {
-      keys[p0 + at] = s_key[at];
-      vals[p0 + at] = s_val[at];
+      keys[p0 + at] = s_key[at + at / 32u];
+      vals[p0 + at] = s_val[at + at / 32u];
     }
   }
 }
