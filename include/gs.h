@@ -414,7 +414,8 @@ int32_t gs_densify(const float* params, const float* m, const float* v, const fl
  * so is the count.  params, m, v: blocked layout for n, updated in place; rand [n][3]
  * (device).  *moves_out (host, nullable): the number of moves.  ws: gs_workspace_bytes(
  * GS_WS_RELOCATE, n, 0, 0, 0, NULL).  Waits for the two counts (one copy to a pinned host buffer);
- * the donors are ranked with rocPRIM's stable radix sort. */
+ * the donors are ranked by a stable radix sort of their inverted size keys (the library's own
+ * radix passes), so equal sizes keep the order of their indices. */
 int32_t gs_relocate(float* params, float* m, float* v, int64_t n, int32_t sh_degree, const float* rand,
                     double dead_opacity, double donor_opacity, int64_t max_moves, int64_t* moves_out, void* ws,
                     size_t ws_bytes, void* stream);
