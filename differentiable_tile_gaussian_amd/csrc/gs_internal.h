@@ -78,9 +78,10 @@ hipError_t launch_chain_adam_project(float* params, int n, int deg, const gs_cam
 
 // ---- scan.hip: exclusive prefix sum of n u32 values into out[0..n], out[n] = total.
 // The total is also written as u64 to *total64 (device) so that overflow of 32 bits is seen.
+// With n_dev, the count is min(n, *n_dev) (read on the device; ws sized for n).
 size_t scan_ws_bytes(int64_t n);
 hipError_t launch_scan_u32(const uint32_t* in, uint32_t* out, int64_t n, uint64_t* total64, void* ws,
-                           hipStream_t s);
+                           hipStream_t s, const uint32_t* n_dev = nullptr);
 
 // ---- sort.hip
 // depth order of the visible Gaussians (proj.order, proj.n_visible) and the pair

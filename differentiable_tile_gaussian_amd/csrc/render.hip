@@ -183,20 +183,28 @@ __device__ inline bool header_ok(const HeaderCheck& c, RenderHeader& h) {
 
 // ---------------------------------------------------------------- tile order
 // Tiles sorted by bucket 32 - clz(length), longest bucket first (order within a
-// bucket is arbitrary).  One block; num_tiles may exceed the block size.
+// bucket is arbitrary).  One block; num_tiles may exceed the block size.  The block also
+// resets the split path's state (no tile split yet) and writes the workspace header.
 __global__ void __launch_bounds__(1024) tile_order_kernel(const uint32_t* __restrict__ ranges, int num_tiles,
-                                                           uint32_t* __restrict__ order) {
+                                                           uint32_t* __restrict__ order,
+                                                           uint32_t* __restrict__ counters,
+                                                           int32_t* __restrict__ slot_of_tile,
+                                                           RenderHeader* __restrict__ hdr, RenderHeader h) {
   __shared__ uint32_t s_cnt[33];
   __shared__ uint32_t s_pos[33];
-  if (threadIdx.x < 33) s_cnt[threadIdx.x] = 0u;
+  const int tid = threadIdx.x;
+  if (tid < 33) s_cnt[tid] = 0u;
+  if (tid < 2) counters[tid] = 0u;
+  if (tid == 0) *hdr = h;
   __syncthreads();
-  for (int t = threadIdx.x; t < num_tiles; t += blockDim.x) {
+  for (int t = tid; t < num_tiles; t += blockDim.x) {
     const uint32_t len = ranges[num_tiles + t] - ranges[t];
     const int b = len ? 32 - __clz(len) : 0;
     atomicAdd(&s_cnt[b], 1u);
+    slot_of_tile[t] = -1;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     uint32_t acc = 0;
     for (int b = 32; b >= 0; --b) {
       s_pos[b] = acc;
@@ -204,19 +212,11 @@ __global__ void __launch_bounds__(1024) tile_order_kernel(const uint32_t* __rest
     }
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < num_tiles; t += blockDim.x) {
+  for (int t = tid; t < num_tiles; t += blockDim.x) {
     const uint32_t len = ranges[num_tiles + t] - ranges[t];
     const int b = len ? 32 - __clz(len) : 0;
     order[atomicAdd(&s_pos[b], 1u)] = uint32_t(t);
   }
-}
-
-__global__ void split_init_kernel(uint32_t* __restrict__ counters, int32_t* __restrict__ slot_of_tile,
-                                  int num_tiles, RenderHeader* __restrict__ hdr, RenderHeader h) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < 2) counters[i] = 0u;
-  if (i < num_tiles) slot_of_tile[i] = -1;
-  if (i == 0) *hdr = h;
 }
 
 // ------------------------------------------------------------ forward walk
@@ -1140,13 +1140,9 @@ hipError_t launch_render_fwd(const gs_proj& proj, const uint32_t* vals, const ui
                        uint32_t(cam.width), uint32_t(cam.height), 0u, uint64_t(carve_bytes(d))};
   const float4* splat = reinterpret_cast<const float4*>(proj.splat);
   {
-    GSK_PROF("split_init", s);
-    split_init_kernel<<<div_up(num_tiles, 256), 256, 0, s>>>(ws.counters, ws.slot_of_tile, num_tiles,
-                                                             static_cast<RenderHeader*>(wsp), h);
-  }
-  {
     GSK_PROF("tile_order", s);
-    tile_order_kernel<<<1, 1024, 0, s>>>(ranges, num_tiles, ws.order);
+    tile_order_kernel<<<1, 1024, 0, s>>>(ranges, num_tiles, ws.order, ws.counters, ws.slot_of_tile,
+                                         static_cast<RenderHeader*>(wsp), h);
   }
   {
     GSK_PROF("render_fwd", s);

@@ -41,10 +41,18 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, ui
   return base + inc - v;
 }
 
+// The count scanned: n, or min(n, *n_dev) when the count is on the device.
+__device__ inline int64_t scan_count(int64_t n, const uint32_t* n_dev) {
+  return n_dev ? min(n, int64_t(*n_dev)) : n;
+}
+
 __global__ void __launch_bounds__(kScanThreads) scan_reduce_kernel(const uint32_t* __restrict__ in, int64_t n,
+                                                                   const uint32_t* __restrict__ n_dev,
                                                                    uint64_t* __restrict__ block_sums) {
   __shared__ uint32_t s_wave[kScanThreads / 64];
+  n = scan_count(n, n_dev);
   const int64_t base = int64_t(blockIdx.x) * kScanTile;
+  if (base >= n) return;   // uniform per block
   uint32_t sum = 0;
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
@@ -57,13 +65,25 @@ __global__ void __launch_bounds__(kScanThreads) scan_reduce_kernel(const uint32_
 }
 
 __global__ void __launch_bounds__(kScanThreads) scan_apply_kernel(const uint32_t* __restrict__ in, int64_t n,
-                                                                  const uint64_t* __restrict__ block_sums, int nb,
+                                                                  const uint32_t* __restrict__ n_dev,
+                                                                  const uint64_t* __restrict__ block_sums,
                                                                   uint32_t* __restrict__ out,
                                                                   uint64_t* __restrict__ total64, bool vec) {
   __shared__ uint32_t s_wave[kScanThreads / 64];
   __shared__ uint64_t s_part[kScanThreads / 64];
+  n = scan_count(n, n_dev);
+  const int nb = int((n + kScanTile - 1) / kScanTile);   // the blocks with values
+  if (nb == 0) {   // nothing to scan: out[0] = 0
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      *total64 = 0u;
+      out[0] = 0u;
+    }
+    return;
+  }
+  if (int(blockIdx.x) >= nb) return;   // uniform per block
   // the sums of the tiles before this one (the last block also adds its own: the total)
-  const int upto = blockIdx.x == gridDim.x - 1 ? nb : int(blockIdx.x);
+  const bool last = int(blockIdx.x) == nb - 1;
+  const int upto = last ? nb : int(blockIdx.x);
   uint64_t pre = 0;
   for (int t = threadIdx.x; t < upto; t += kScanThreads) pre += block_sums[t];
 #pragma unroll
@@ -73,7 +93,7 @@ __global__ void __launch_bounds__(kScanThreads) scan_apply_kernel(const uint32_t
   pre = 0;
 #pragma unroll
   for (int w = 0; w < kScanThreads / 64; ++w) pre += s_part[w];
-  if (blockIdx.x == gridDim.x - 1) {
+  if (last) {
     if (threadIdx.x == 0) {
       *total64 = pre;
       out[n] = uint32_t(pre);
@@ -123,7 +143,7 @@ __global__ void scan_empty_kernel(uint32_t* out, uint64_t* total64) {
 size_t scan_ws_bytes(int64_t n) { return size_t(div_up(n > 0 ? n : 1, kScanTile)) * sizeof(uint64_t); }
 
 hipError_t launch_scan_u32(const uint32_t* in, uint32_t* out, int64_t n, uint64_t* total64, void* ws,
-                           hipStream_t s) {
+                           hipStream_t s, const uint32_t* n_dev) {
   if (n == 0) {
     {
       GSK_PROF("scan_empty", s);
@@ -135,12 +155,12 @@ hipError_t launch_scan_u32(const uint32_t* in, uint32_t* out, int64_t n, uint64_
   uint64_t* sums = static_cast<uint64_t*>(ws);
   {
     GSK_PROF("scan_reduce", s);
-    scan_reduce_kernel<<<nb, kScanThreads, 0, s>>>(in, n, sums);
+    scan_reduce_kernel<<<nb, kScanThreads, 0, s>>>(in, n, n_dev, sums);
   }
   {
     GSK_PROF("scan_apply", s);
     const bool vec = reinterpret_cast<uintptr_t>(in) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0;
-    scan_apply_kernel<<<nb, kScanThreads, 0, s>>>(in, n, sums, nb, out, total64, vec);
+    scan_apply_kernel<<<nb, kScanThreads, 0, s>>>(in, n, n_dev, sums, out, total64, vec);
   }
   return hipGetLastError();
 }

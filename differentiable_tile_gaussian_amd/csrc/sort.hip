@@ -640,7 +640,7 @@ RadixWs carve_radix(Carver& c, int nb) {
 
 struct DepthWs {
   uint32_t *dk[2], *dv;         // with proj.order: the depth passes' two buffer sets
-  uint32_t* counts;             // n: tile counts in depth order; counts[n]: the plan's dmax
+  uint32_t* counts;             // n: tile counts in depth order (the first n_visible); counts[n]: the plan's dmax
   uint32_t* bmax;               // one per radix block
   uint64_t* total64;            // the offsets scan's total
   void* scan_ws;
@@ -715,7 +715,6 @@ hipError_t launch_depth_order(const gs_proj& proj, int n, float znear, void* ws,
   carve_depth(ws, n, &w);
   hipError_t e;
   const int nb = blocks_for(n);
-  zero_u32(w.counts, int64_t(n), s);   // the counts of the invisible stay 0
   uint32_t key_base;
   std::memcpy(&key_base, &znear, sizeof key_base);
   DepthPlan dp{{w.dk[0], w.dk[1]}, {w.dv, proj.order}, w.bmax, w.counts + n, 0};
@@ -736,8 +735,9 @@ hipError_t launch_depth_order(const gs_proj& proj, int n, float znear, void* ws,
                                    rect, rect_order, w.counts, s)) != hipSuccess)
       return e;
   }
-  // offs: first pair of each visible Gaussian in depth order; offs[n] = the pair count
-  return launch_scan_u32(w.counts, proj.offs, n, w.total64, w.scan_ws, s);
+  // offs: first pair of each visible Gaussian in depth order, offs[n_visible] = the pair
+  // count (the scan covers the n_visible counts the last pass wrote)
+  return launch_scan_u32(w.counts, proj.offs, n, w.total64, w.scan_ws, s, proj.n_visible);
 }
 
 size_t sort_pairs_ws_bytes(int64_t n) {

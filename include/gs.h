@@ -102,9 +102,10 @@ typedef struct gs_proj {
   uint32_t* order;      /* [n] ids of the visible Gaussians (tiles > 0) ordered by depth, then id;
                            the first *n_visible entries are written */
   uint32_t* n_visible;  /* [1] number of visible Gaussians */
-  uint32_t* offs;       /* [n + 1] exclusive prefix sum of tiles[order[r]] over r (0 past the
-                           visible ones): offs[r] is the first pair of the r-th Gaussian in depth
-                           order; offs[n] = pair count */
+  uint32_t* offs;       /* [n + 1] exclusive prefix sum of tiles[order[r]] over the visible r:
+                           offs[r] is the first pair of the r-th Gaussian in depth order and
+                           offs[*n_visible] = pair count (the first *n_visible + 1 entries are
+                           written) */
   uint32_t* rect_order; /* [n][2] rect of the r-th visible Gaussian in depth order (the first
                            *n_visible entries are written), read by gs_bin_sort */
 } gs_proj;

@@ -86,11 +86,10 @@ def check_preprocess(gpu, ora):
     ro = gpu["rect_order"][:len(order)].astype(np.int64)
     np.testing.assert_array_equal(np.stack([ro[:, 0] & 0xFFFF, ro[:, 0] >> 16, ro[:, 1] & 0xFFFF, ro[:, 1] >> 16]),
                                   ora["rect"][:, order])
-    n = len(ora["tiles"])
-    counts = np.zeros(n, np.int64)
-    counts[:len(order)] = ora["tiles"][order]
+    # the pair offsets in depth order: the first n_visible + 1 entries (the rest unspecified)
+    counts = ora["tiles"][order].astype(np.int64)
     expect_offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.uint32)
-    np.testing.assert_array_equal(gpu["offs"], expect_offs)
+    np.testing.assert_array_equal(gpu["offs"][:len(order) + 1], expect_offs)
 
 
 def check_blend_box(gpu, vis):
