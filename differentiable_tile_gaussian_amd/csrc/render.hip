@@ -1109,13 +1109,15 @@ __global__ void __launch_bounds__(256) fixed_decode_kernel(int n, const float4* 
 // check failed).  16-byte non-temporal stores over count4 groups of four floats (a pure
 // write stream), then the count % 4 floats left.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-__global__ void zero_f32x4_kernel(f32x4* __restrict__ p, int64_t count4, float* __restrict__ tail, int ntail,
-                                  HeaderCheck hc) {
-  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+// Grid-stride: a few thousand blocks, each thread storing 16 bytes per step.
+__global__ void __launch_bounds__(256) zero_f32x4_kernel(f32x4* __restrict__ p, int64_t count4,
+                                                          float* __restrict__ tail, int64_t ntail, HeaderCheck hc) {
+  const int64_t i0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   RenderHeader h;
   const float v = header_ok(hc, h) ? 0.0f : __builtin_nanf("");
-  if (i < count4) __builtin_nontemporal_store(f32x4{v, v, v, v}, p + i);
-  if (i < ntail) tail[i] = v;
+  for (int64_t i = i0; i < count4; i += stride) __builtin_nontemporal_store(f32x4{v, v, v, v}, p + i);
+  for (int64_t i = i0; i < ntail; i += stride) tail[i] = v;   // all of it when p is not 16-byte aligned
 }
 
 __global__ void zero_u64_kernel(unsigned long long* __restrict__ p, int64_t count) {
@@ -1200,10 +1202,11 @@ hipError_t launch_render_bwd(const gs_proj& proj, int n, const uint32_t* vals, c
       const int64_t count = 9 * int64_t(n);
       const bool vec = reinterpret_cast<uintptr_t>(gscreen) % 16 == 0;
       const int64_t count4 = vec ? count / 4 : 0;
-      const int ntail = int(count - 4 * count4);
+      const int64_t ntail = count - 4 * count4;
       const int64_t threads = count4 > ntail ? count4 : ntail;
-      zero_f32x4_kernel<<<div_up(threads, 256), 256, 0, s>>>(reinterpret_cast<f32x4*>(gscreen), count4,
-                                                             gscreen + 4 * count4, ntail, hc);
+      const unsigned blocks = div_up(threads, 256) < 2048u ? div_up(threads, 256) : 2048u;
+      zero_f32x4_kernel<<<blocks, 256, 0, s>>>(reinterpret_cast<f32x4*>(gscreen), count4, gscreen + 4 * count4,
+                                               ntail, hc);
     }
   }
   const float unit = kFixedUnit * 3.0f * float(cam.width) * float(cam.height);
