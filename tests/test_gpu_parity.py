@@ -98,6 +98,36 @@ def test_backward_small(torch_cuda, oracle, case):
     assert np.all(gparams[:, culled] == 0.0)
 
 
+def test_backward_into_unaligned_screen_gradients(torch_cuda):
+    """The screen partials written through a pointer that is not 16-byte aligned (the
+    clear then takes its 4-byte path over the whole array): equal to the aligned result
+    after the same forward, with stale values in the buffer beforehand.  Float sums whose
+    atomics may land in another order, so within rounding."""
+    torch = torch_cuda
+    from differentiable_tile_gaussian_amd import gs
+    case = _small_cases()[2]
+    seed, n, deg, w, h = case
+    s, cam = _scene_and_camera(*case)
+    pl, c = pu.gpu_forward(s.params, deg, cam)
+    dLdI = (np.random.default_rng(seed).standard_normal((3, h, w)) * 1e-3).astype(np.float32)
+    pl.dLdI.copy_(torch.from_numpy(dLdI))
+    gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI, pl.gscreen,
+                     pl.grads, pl.ws_render)
+    torch.cuda.synchronize()
+    ref = pl.gscreen[:n].cpu().numpy().astype(np.float64)
+    big = torch.full((9 * n + 8,), 7.0, dtype=torch.float32, device="cuda")   # stale values
+    un = big[1:1 + 9 * n].view(n, 9)
+    assert un.data_ptr() % 16 != 0
+    gs.gs_render_bwd(pl.params, deg, pl.proj, pl.vals, pl.ranges, pl.pairs, c, pl.T, pl.nc, pl.dLdI, un,
+                     pl.grads, pl.ws_render)
+    torch.cuda.synchronize()
+    got = un.cpu().numpy().astype(np.float64)
+    scale = np.abs(ref).max(axis=0) + 1e-30
+    assert np.all(np.abs(got - ref) <= 1e-5 * scale), float((np.abs(got - ref) / scale).max())
+    # the words around the array are untouched
+    assert float(big[0]) == 7.0 and float(big[9 * n + 1]) == 7.0
+
+
 def _full_step_checks(torch, gs, oracle, pl, c, ref, target, params, deg, cam):
     """Every stage of one step against the oracle: projection, pairs and ranges
     bit-exact; pixels, loss and image gradient; then the backward fed the oracle's
