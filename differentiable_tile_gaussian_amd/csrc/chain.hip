@@ -380,43 +380,43 @@ void launch_chain_mode(float* params, int n, int deg, const gs_camera& cam, cons
 //   dL/dw = (M21 - M12, M02 - M20, M10 - M01) with M = G W^T,   dL/dt = dp + W gsh.
 // For the position path alone the rotation term is (p - t) x dp, the pages' torque, and the
 // translation's dp: the trainer's code accumulates exactly those (position_only).
-// The per-Gaussian terms are formed in double from the fp32 chain quantities and summed in
-// double, per wave with a fixed butterfly and over blocks in a fixed order, so the result
-// is reproducible.
+// The per-Gaussian terms are formed in fp32 from the fp32 chain quantities (one fixed
+// sequence of roundings: this file is compiled without contraction) and summed in double,
+// per wave with a fixed butterfly and over blocks in a fixed order, so the result is
+// reproducible; the terms' own rounding is below that of the chain quantities they are
+// formed from.
 __device__ inline void camera_terms(const CamPart& c, const float* mean, const gs_camera& cam, int position_only,
                                     double* out) {
-  double G[3][3];
+  float G[3][3];
 #pragma unroll
   for (int r = 0; r < 3; ++r)
 #pragma unroll
-    for (int k = 0; k < 3; ++k) G[r][k] = double(c.dp[r]) * double(mean[k]);
-  double tr[3] = {double(c.dp[0]), double(c.dp[1]), double(c.dp[2])};
+    for (int k = 0; k < 3; ++k) G[r][k] = c.dp[r] * mean[k];
+  float tr[3] = {c.dp[0], c.dp[1], c.dp[2]};
   if (!position_only) {
-    const double fx = cam.fx, fy = cam.fy, pz = c.p[2];
-    const double J[2][3] = {{fx / pz, 0.0, -fx * double(c.p[0]) / (pz * pz)},
-                            {0.0, fy / pz, -fy * double(c.p[1]) / (pz * pz)}};
+    const float iz = 1.0f / c.p[2];
+    const float j00 = cam.fx * iz, j11 = cam.fy * iz;
+    const float J[2][3] = {{j00, 0.0f, -(j00 * c.p[0]) * iz}, {0.0f, j11, -(j11 * c.p[1]) * iz}};
 #pragma unroll
     for (int r = 0; r < 3; ++r)
 #pragma unroll
       for (int k = 0; k < 3; ++k)
-        G[r][k] = J[0][r] * double(c.dT0[k]) + J[1][r] * double(c.dT1[k]) + G[r][k] +
-                  double(cam.t[r]) * double(c.gsh[k]);
+        G[r][k] = ((J[0][r] * c.dT0[k] + J[1][r] * c.dT1[k]) + G[r][k]) + cam.t[r] * c.gsh[k];
 #pragma unroll
     for (int r = 0; r < 3; ++r)
-      tr[r] = tr[r] + double(cam.R[3 * r]) * double(c.gsh[0]) + double(cam.R[3 * r + 1]) * double(c.gsh[1]) +
-              double(cam.R[3 * r + 2]) * double(c.gsh[2]);
+      tr[r] = ((tr[r] + cam.R[3 * r] * c.gsh[0]) + cam.R[3 * r + 1] * c.gsh[1]) + cam.R[3 * r + 2] * c.gsh[2];
   }
-  double M[3][3];
+  float M[3][3];
 #pragma unroll
   for (int r = 0; r < 3; ++r)
 #pragma unroll
     for (int k = 0; k < 3; ++k)
-      M[r][k] = G[r][0] * double(cam.R[3 * k]) + G[r][1] * double(cam.R[3 * k + 1]) + G[r][2] * double(cam.R[3 * k + 2]);
-  out[0] = M[2][1] - M[1][2];
-  out[1] = M[0][2] - M[2][0];
-  out[2] = M[1][0] - M[0][1];
+      M[r][k] = (G[r][0] * cam.R[3 * k] + G[r][1] * cam.R[3 * k + 1]) + G[r][2] * cam.R[3 * k + 2];
+  out[0] = double(M[2][1] - M[1][2]);
+  out[1] = double(M[0][2] - M[2][0]);
+  out[2] = double(M[1][0] - M[0][1]);
 #pragma unroll
-  for (int r = 0; r < 3; ++r) out[3 + r] = tr[r];
+  for (int r = 0; r < 3; ++r) out[3 + r] = double(tr[r]);
 }
 
 // One block per group of 64 Gaussians, the chain kernel's split: waves 0-2 the view-direction
@@ -500,7 +500,8 @@ __global__ void __launch_bounds__(1024) camera_grad_finalize_kernel(const double
   __shared__ double s[1024];
   const int k = blockIdx.x, t = threadIdx.x;
   double acc = 0.0;
-  for (int b = t; b < nb; b += 1024) acc += part[size_t(k) * nb + b];
+#pragma unroll 8
+  for (int b = t; b < nb; b += 1024) acc += part[size_t(k) * nb + b];   // loads issued eight ahead
   s[t] = acc;
   __syncthreads();
   for (int w = 512; w >= 1; w >>= 1) {

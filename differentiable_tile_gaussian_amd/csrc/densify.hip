@@ -90,55 +90,103 @@ __device__ inline void child_mean(const float* g0, const float* eps, float* out)
 }
 
 // Writes Gaussian g0 (its theta, m, v rows) as output d: fresh ones get zero moments;
-// a child gets its own mean and the log-scales lowered by the shrink.
-__device__ inline void put(const float* g0, const float* m0, const float* v0, float* params_out, float* m_out,
-                           float* v_out, float2* stats_out, int d, int P, bool fresh, const float* mean,
+// a child gets its own mean and the log-scales lowered by the shrink.  The planes go in
+// groups of kPutGroup, all of a group's loads before its stores (the input and output
+// arrays do not overlap), so that a thread keeps that many loads in flight.
+constexpr int kPutGroup = 8;
+__device__ inline void put(const float* __restrict__ g0, const float* __restrict__ m0, const float* __restrict__ v0,
+                           float* __restrict__ params_out, float* __restrict__ m_out, float* __restrict__ v_out,
+                           float2* __restrict__ stats_out, int d, int P, bool fresh, const float* mean,
                            const DensifyArgs& a) {
   float* gp = gaussian_base(params_out, d, P);
   float* gm = gaussian_base(m_out, d, P);
   float* gv = gaussian_base(v_out, d, P);
-  for (int k = 0; k < P; ++k) {
-    float th = g0[k * kGB];
-    if (mean && k < 3) th = mean[k];
-    if (mean && k >= 3 && k < 6) th = th - a.lscale_shrink;
-    float mo = fresh ? 0.0f : m0[k * kGB], vo = fresh ? 0.0f : v0[k * kGB];
-    if (a.reset && k == 10) {
-      th = min_of(th, a.logit_cap);
-      mo = vo = 0.0f;
+  for (int k0 = 0; k0 < P; k0 += kPutGroup) {
+    float th[kPutGroup], mo[kPutGroup], vo[kPutGroup];
+#pragma unroll
+    for (int j = 0; j < kPutGroup; ++j) {
+      const int k = k0 + j;
+      th[j] = mo[j] = vo[j] = 0.0f;
+      if (k < P) {
+        th[j] = g0[k * kGB];
+        if (!fresh) {
+          mo[j] = m0[k * kGB];
+          vo[j] = v0[k * kGB];
+        }
+      }
     }
-    gp[k * kGB] = th;
-    gm[k * kGB] = mo;
-    gv[k * kGB] = vo;
+#pragma unroll
+    for (int j = 0; j < kPutGroup; ++j) {
+      const int k = k0 + j;
+      if (k < P) {
+        float t = th[j], mm = mo[j], vv = vo[j];
+        if (mean && k < 3) t = mean[k];
+        if (mean && k >= 3 && k < 6) t = t - a.lscale_shrink;
+        if (a.reset && k == 10) {
+          t = min_of(t, a.logit_cap);
+          mm = vv = 0.0f;
+        }
+        gp[k * kGB] = t;
+        gm[k * kGB] = mm;
+        gv[k * kGB] = vv;
+      }
+    }
   }
   stats_out[d] = make_float2(0.0f, 0.0f);
 }
 
-// One thread per source Gaussian; its outputs' places are the prefix sums of the flags
-// (offs_keep[n] = kept, offs_clone[n] = cloned).
-__global__ void __launch_bounds__(256) densify_scatter_kernel(
-    const float* __restrict__ params, const float* __restrict__ m, const float* __restrict__ v, int n, int P,
-    const float* __restrict__ rand, const uint32_t* __restrict__ fkeep, const uint32_t* __restrict__ fclone,
-    const uint32_t* __restrict__ fsplit, const uint32_t* __restrict__ offs_keep,
-    const uint32_t* __restrict__ offs_clone, const uint32_t* __restrict__ offs_split, DensifyArgs a,
-    float* __restrict__ params_out, float* __restrict__ m_out, float* __restrict__ v_out,
-    float2* __restrict__ stats_out) {
+// The source of every place in the new population, one thread per source Gaussian: kept
+// ones at their place (the prefix sum of the kept flags) in src_keep; cloned and split ones
+// at their place among the clones or the split parents in src.
+__global__ void __launch_bounds__(256) densify_index_kernel(int n, const uint32_t* __restrict__ fkeep,
+                                                            const uint32_t* __restrict__ fclone,
+                                                            const uint32_t* __restrict__ fsplit,
+                                                            const uint32_t* __restrict__ offs_keep,
+                                                            const uint32_t* __restrict__ offs_clone,
+                                                            const uint32_t* __restrict__ offs_split, uint32_t cloned,
+                                                            uint32_t* __restrict__ src_keep,
+                                                            uint32_t* __restrict__ src) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  const float* g0 = gaussian_base(params, i, P);
-  const float* m0 = gaussian_base(m, i, P);
-  const float* v0 = gaussian_base(v, i, P);
-  const int kept = int(offs_keep[n]), cloned = int(offs_clone[n]), splits = int(offs_split[n]);
-  if (fkeep[i]) put(g0, m0, v0, params_out, m_out, v_out, stats_out, int(offs_keep[i]), P, false, nullptr, a);
-  if (fclone[i])
-    put(g0, m0, v0, params_out, m_out, v_out, stats_out, kept + int(offs_clone[i]), P, true, nullptr, a);
-  if (fsplit[i]) {
-    for (int c = 0; c < 2; ++c) {
-      float mean[3];
-      child_mean(g0, rand + (size_t(2) * i + c) * 3, mean);
-      put(g0, m0, v0, params_out, m_out, v_out, stats_out, kept + cloned + c * splits + int(offs_split[i]), P,
-          true, mean, a);
-    }
+  if (fkeep[i]) src_keep[offs_keep[i]] = uint32_t(i);
+  if (fclone[i]) src[offs_clone[i]] = uint32_t(i);
+  if (fsplit[i]) src[cloned + offs_split[i]] = uint32_t(i);
+}
+
+// The new population, one thread per place j (kept, then clones, then first and second
+// children), so that a wave writes whole rows of the blocked layout; each thread reads its
+// source's rows (a wave's kept sources are nearly consecutive; the new ones' moments start
+// at zero and are not read).
+__global__ void __launch_bounds__(256) densify_write_kernel(const float* __restrict__ params,
+                                                            const float* __restrict__ m, const float* __restrict__ v,
+                                                            int P, const float* __restrict__ rand,
+                                                            const uint32_t* __restrict__ src_keep,
+                                                            const uint32_t* __restrict__ src, uint32_t kept,
+                                                            uint32_t cloned, uint32_t splits, DensifyArgs a,
+                                                            float* __restrict__ params_out, float* __restrict__ m_out,
+                                                            float* __restrict__ v_out, float2* __restrict__ stats_out) {
+  const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t t = j - int64_t(kept);
+  if (t >= int64_t(cloned) + 2 * int64_t(splits)) return;
+  if (t < 0) {
+    const int i = int(src_keep[j]);
+    put(gaussian_base(params, i, P), gaussian_base(m, i, P), gaussian_base(v, i, P), params_out, m_out, v_out,
+        stats_out, int(j), P, false, nullptr, a);
+    return;
   }
+  if (t < int64_t(cloned)) {
+    const int i = int(src[t]);
+    put(gaussian_base(params, i, P), nullptr, nullptr, params_out, m_out, v_out, stats_out, int(j), P, true, nullptr,
+        a);
+    return;
+  }
+  const int64_t u = t - int64_t(cloned);
+  const int c = u >= int64_t(splits) ? 1 : 0;
+  const int i = int(src[int64_t(cloned) + u - int64_t(c) * splits]);
+  const float* g0 = gaussian_base(params, i, P);
+  float mean[3];
+  child_mean(g0, rand + (size_t(2) * i + c) * 3, mean);
+  put(g0, nullptr, nullptr, params_out, m_out, v_out, stats_out, int(j), P, true, mean, a);
 }
 
 // ---- relocation of the dead ([GSG] "Densification", the MCMC-style pass)
@@ -288,7 +336,7 @@ hipError_t launch_densify_accumulate(const uint32_t* tiles, int n, const float* 
 size_t densify_ws_bytes(int64_t n) {
   const size_t flags = (size_t(n > 0 ? n : 1) * 4 + 255) & ~size_t(255);
   const size_t offs = (size_t(n + 1) * 4 + 255) & ~size_t(255);
-  return 3 * flags + 3 * offs + 256 + 3 * ((scan_ws_bytes(n) + 255) & ~size_t(255));
+  return 5 * flags + 3 * offs + 256 + 3 * ((scan_ws_bytes(n) + 255) & ~size_t(255));
 }
 
 hipError_t launch_densify_count(const float* params, int n, int deg, const float* stats, const DensifyArgs& a,
@@ -307,14 +355,22 @@ hipError_t launch_densify_count(const float* params, int n, int deg, const float
 }
 
 hipError_t launch_densify_write(const float* params, const float* m, const float* v, int n, int deg,
-                                const float* rand, const DensifyArgs& a, void* ws, float* params_out, float* m_out,
-                                float* v_out, float* stats_out, hipStream_t s) {
+                                const float* rand, const DensifyArgs& a, void* ws, uint32_t kept, uint32_t cloned,
+                                uint32_t splits, float* params_out, float* m_out, float* v_out, float* stats_out,
+                                hipStream_t s) {
   DensifyWs w = carve_densify(ws, n);
-  GSK_PROF("densify_scatter", s);
-  densify_scatter_kernel<<<div_up(n, 256), 256, 0, s>>>(params, m, v, n, num_planes(deg), rand, w.flag[0],
-                                                        w.flag[1], w.flag[2], w.offs[0], w.offs[1], w.offs[2], a,
-                                                        params_out, m_out, v_out,
-                                                        reinterpret_cast<float2*>(stats_out));
+  {
+    GSK_PROF("densify_index", s);
+    densify_index_kernel<<<div_up(n, 256), 256, 0, s>>>(n, w.flag[0], w.flag[1], w.flag[2], w.offs[0], w.offs[1],
+                                                        w.offs[2], cloned, w.src_keep, w.src);
+  }
+  const int64_t total = int64_t(kept) + int64_t(cloned) + 2 * int64_t(splits);
+  if (total > 0) {
+    GSK_PROF("densify_write", s);
+    densify_write_kernel<<<div_up(total, 256), 256, 0, s>>>(params, m, v, num_planes(deg), rand, w.src_keep, w.src,
+                                                            kept, cloned, splits, a, params_out, m_out, v_out,
+                                                            reinterpret_cast<float2*>(stats_out));
+  }
   return hipGetLastError();
 }
 
@@ -338,6 +394,8 @@ DensifyWs carve_densify(void* ws, int64_t n) {
     w.scan_ws[k] = p;
     p += sw;
   }
+  w.src_keep = reinterpret_cast<uint32_t*>(p);
+  w.src = reinterpret_cast<uint32_t*>(p + flags);
   return w;
 }
 

@@ -621,8 +621,9 @@ int32_t gs_densify(const float* params, const float* m, const float* v, const fl
   if (total > capacity) return fail(GS_ERR_CAPACITY, "the new population (%lld) exceeds capacity (%lld)",
                                     (long long)total, (long long)capacity);
   if (n > 0) {
-    const hipError_t e = gsk::launch_densify_write(params, m, v, int(n), sh_degree, rand, a, ws, params_out, m_out,
-                                                   v_out, stats_out, s);
+    const hipError_t e = gsk::launch_densify_write(params, m, v, int(n), sh_degree, rand, a, ws, uint32_t(tot[0]),
+                                                   uint32_t(tot[1]), uint32_t(tot[2]), params_out, m_out, v_out,
+                                                   stats_out, s);
     if (e != hipSuccess) return hip_fail(e, "densify_write");
   }
   return GS_OK;

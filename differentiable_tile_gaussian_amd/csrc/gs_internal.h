@@ -106,12 +106,15 @@ struct DensifyArgs {
   int reset;
 };
 // Workspace: per-Gaussian flags (kept, cloned, split), their exclusive prefix sums
-// (n + 1 entries each), the three totals (u64) and the scans' block sums.
+// (n + 1 entries each), the three totals (u64), the scans' block sums, the source of each
+// kept place and the sources of the clones and of the split parents, in their order.
 struct DensifyWs {
   uint32_t* flag[3];
   uint32_t* offs[3];
   uint64_t* totals;
   void* scan_ws[3];
+  uint32_t* src_keep;
+  uint32_t* src;
 };
 size_t densify_ws_bytes(int64_t n);
 DensifyWs carve_densify(void* ws, int64_t n);
@@ -139,8 +142,9 @@ hipError_t launch_densify_accumulate(const uint32_t* tiles, int n, const float* 
 hipError_t launch_densify_count(const float* params, int n, int deg, const float* stats, const DensifyArgs& a,
                                 void* ws, hipStream_t s);
 hipError_t launch_densify_write(const float* params, const float* m, const float* v, int n, int deg,
-                                const float* rand, const DensifyArgs& a, void* ws, float* params_out, float* m_out,
-                                float* v_out, float* stats_out, hipStream_t s);
+                                const float* rand, const DensifyArgs& a, void* ws, uint32_t kept, uint32_t cloned,
+                                uint32_t splits, float* params_out, float* m_out, float* v_out, float* stats_out,
+                                hipStream_t s);
 
 // ---- render.hip
 // Render workspace: a header the forward writes (its split sizes), the split state, and
