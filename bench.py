@@ -54,7 +54,7 @@ STAGE_KERNELS = {
     "preprocess": ("preprocess_fwd", "sum_counts"),
     "bin_sort": ("radix_upsweep", "radix_scan", "radix_downsweep", "scan_reduce", "scan_apply", "emit_pairs",
                  "tile_ranges", "fill_u32"),
-    "render_fwd": ("render_fwd", "tile_order", "split_chunk", "split_combine", "split_rewalk",
+    "render_fwd": ("render_fwd", "tile_order", "split_reset", "split_combine", "split_rewalk",
                    "split_finalize"),
     "loss": ("ssim", "loss_finalize"),
     "render_bwd": ("render_bwd", "zero_f32", "fixed_decode", "zero_u64"),

@@ -13,18 +13,22 @@
 // Split path.  One block can only use one CU, and a few tiles carry lists of tens
 // of thousands of pairs, so the first `first` pairs of every tile are walked as
 // above and a tile whose pixels are not all finished then is split: its remaining
-// pairs form chunks of `chunk` pairs that separate blocks walk at the same time.
-//   chunk 0   continues the exact walk from the carried state;
-//   chunk c>0 walks from T = 1 (the local transmittance and colour of the chunk),
-//             stops a pixel once T_first T_local < 1e-4, T_first being its
-//             transmittance after the first segment (it bounds the transmittance in
-//             front of the chunk from above, also in fp32, where every later factor
-//             is at most 1: so the overall T has dropped below 1e-4 by then too, and
-//             the combine finds the stop in this chunk or an earlier one), and drops
-//             pixels that an earlier chunk has already saturated (a per-pixel "first
-//             saturating chunk" marker, polled);
+// pairs form chunks of `chunk` pairs that separate blocks walk at the same time.  The
+// chunks of every tile longer than `first` (a candidate) are blocks of the same launch
+// as the first segments, after them, so that they fill the CUs that the last long first
+// segments leave idle; a tile's first segment publishes, when it ends, whether the tile
+// is split and each pixel's transmittance T_first.
+//   chunk c   walks from T = 1 (the local transmittance and colour of the chunk), stops
+//             a pixel once B T_local < 1e-4, B = T_first once it is out (1 before: an
+//             upper bound of the transmittance in front of the chunk either way, also in
+//             fp32, where every factor is at most 1, so the overall T has dropped below
+//             1e-4 by then too, and the combine finds the stop in this chunk or an earlier
+//             one), drops pixels that an earlier chunk has already saturated (a per-pixel
+//             "first saturating chunk" marker, polled), and stops altogether once the
+//             tile turns out not split;
 //   combine   per pixel, chains the chunks: T_front(c+1) = T_front(c) T_c and
-//             colour += T_front(c) C_c, until the product falls below 1e-4;
+//             colour += T_front(c) C_c, from T_front(0) = T_first, until the product
+//             falls below 1e-4;
 //   re-walk   the chunk where that happens is walked again from T_front with the
 //             test T_front * T_local < 1e-4 to find the exact last pair;
 //   finalize  writes the pixel and, back to front, the state at each chunk end
@@ -33,7 +37,7 @@
 // The split path keeps per pixel one boundary state per chunk of a split tile.
 // It changes only where products are rounded (T_front T_local instead of one
 // running product).
-//
+
 // Backward.  Each pixel walks from its last contributing pair back to the first,
 // recovering T by division and carrying S ([DR] "The trick"); every entry's nine
 // partials are summed over the wave (transposed butterfly), then over the block's
@@ -83,6 +87,9 @@ constexpr float kTStop = 1e-4f;
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr uint32_t kFlag = 0x80000000u;
 constexpr uint32_t kIdx = 0x7fffffffu;
+// A split candidate's first segment (SplitWs::state): still walking, unfinished pixels
+// after it (the tile is split), or all pixels finished within it.
+constexpr uint32_t kPending = 0u, kSplit = 1u, kNotSplit = 2u;
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -99,6 +106,8 @@ struct SplitWs {
   float4* st4;            // [S][256] T and colour after the first segment
   uint32_t* stl;          // [S][256] last pair | done flag
   uint32_t* sat;          // [S][256] first chunk that saturated the pixel
+  uint32_t* state;        // [S] the tile's first segment: kPending, kSplit or kNotSplit
+  float* tfirst;          // [S][256] T after the first segment (0: finished there; -1: not out yet)
   float4* part4;          // [I][256] chunk partials, later (T_end, S_end) boundaries
   uint32_t* partl;        // [I][256] last pair in the chunk | stop flag
   int32_t* stopc;         // [S][256] chunk holding the last pair (-1: first segment, nch: none)
@@ -136,6 +145,8 @@ __host__ __device__ inline SplitWs carve(void* ws, const SplitDims& d) {
   w.st4 = reinterpret_cast<float4*>(take(d.S * 256 * 16));
   w.stl = reinterpret_cast<uint32_t*>(take(d.S * 256 * 4));
   w.sat = reinterpret_cast<uint32_t*>(take(d.S * 256 * 4));
+  w.state = reinterpret_cast<uint32_t*>(take(d.S * 4));
+  w.tfirst = reinterpret_cast<float*>(take(d.S * 256 * 4));
   w.part4 = reinterpret_cast<float4*>(take(d.I * 256 * 16));
   w.partl = reinterpret_cast<uint32_t*>(take(d.I * 256 * 4));
   w.stopc = reinterpret_cast<int32_t*>(take(d.S * 256 * 4));
@@ -147,7 +158,7 @@ __host__ __device__ inline SplitWs carve(void* ws, const SplitDims& d) {
 
 __host__ __device__ inline size_t carve_bytes(const SplitDims& d) {
   return a256(d.NT * 4) + a256(8) + a256(d.NT * 4) + 3 * a256(d.S * 4) + a256(d.I * 8) + a256(d.S * 256 * 16) +
-         2 * a256(d.S * 256 * 4) + a256(d.I * 256 * 16) + a256(d.I * 256 * 4) + a256(d.S * 256 * 4) +
+         2 * a256(d.S * 256 * 4) + a256(d.S * 4) + a256(d.S * 256 * 4) + a256(d.I * 256 * 16) + a256(d.I * 256 * 4) + a256(d.S * 256 * 4) +
          a256(d.S * 256 * 16) + a256(d.S * 256 * 4) + a256(d.S * 256 * 16);
 }
 
@@ -184,24 +195,27 @@ __device__ inline bool header_ok(const HeaderCheck& c, RenderHeader& h) {
 // ---------------------------------------------------------------- tile order
 // Tiles sorted by bucket 32 - clz(length), longest bucket first (order within a
 // bucket is arbitrary).  One block; num_tiles may exceed the block size.  The block also
-// resets the split path's state (no tile split yet) and writes the workspace header.
+// writes the workspace header and gives every tile whose list is longer than `first` (a
+// split candidate: whether it is split is known only when its first segment ends) a slot
+// and the items of its chunks, taking the tiles in that order; the other tiles get none.
 __global__ void __launch_bounds__(1024) tile_order_kernel(const uint32_t* __restrict__ ranges, int num_tiles,
-                                                           uint32_t* __restrict__ order,
-                                                           uint32_t* __restrict__ counters,
-                                                           int32_t* __restrict__ slot_of_tile,
+                                                           SplitWs ws, int first, int chunk,
                                                            RenderHeader* __restrict__ hdr, RenderHeader h) {
   __shared__ uint32_t s_cnt[33];
   __shared__ uint32_t s_pos[33];
+  __shared__ uint32_t s_slots, s_items;
   const int tid = threadIdx.x;
   if (tid < 33) s_cnt[tid] = 0u;
-  if (tid < 2) counters[tid] = 0u;
-  if (tid == 0) *hdr = h;
+  if (tid == 0) {
+    *hdr = h;
+    s_slots = s_items = 0u;
+  }
   __syncthreads();
   for (int t = tid; t < num_tiles; t += blockDim.x) {
     const uint32_t len = ranges[num_tiles + t] - ranges[t];
     const int b = len ? 32 - __clz(len) : 0;
     atomicAdd(&s_cnt[b], 1u);
-    slot_of_tile[t] = -1;
+    ws.slot_of_tile[t] = -1;
   }
   __syncthreads();
   if (tid == 0) {
@@ -212,11 +226,47 @@ __global__ void __launch_bounds__(1024) tile_order_kernel(const uint32_t* __rest
     }
   }
   __syncthreads();
+  // the candidates sit in the buckets from that of first + 1 up: the order's first `span`
+  const int bf = 32 - __clz(uint32_t(first) + 1u);
+  const int span = int(s_pos[bf] + s_cnt[bf]);
+  __syncthreads();
   for (int t = tid; t < num_tiles; t += blockDim.x) {
     const uint32_t len = ranges[num_tiles + t] - ranges[t];
     const int b = len ? 32 - __clz(len) : 0;
-    order[atomicAdd(&s_pos[b], 1u)] = uint32_t(t);
+    ws.order[atomicAdd(&s_pos[b], 1u)] = uint32_t(t);
   }
+  __syncthreads();
+  for (int p = tid; p < span; p += blockDim.x) {
+    const uint32_t tile = ws.order[p];
+    const int len = int(ranges[num_tiles + tile] - ranges[tile]);
+    if (len > first) {
+      const uint32_t nch = uint32_t((len - first + chunk - 1) / chunk);
+      const uint32_t slot = atomicAdd(&s_slots, 1u);
+      ws.slot_tile[slot] = tile;
+      ws.slot_first[slot] = atomicAdd(&s_items, nch);
+      ws.slot_nch[slot] = nch;
+      ws.slot_of_tile[tile] = int32_t(slot);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    ws.counters[0] = s_slots;
+    ws.counters[1] = s_items;
+  }
+}
+
+// One block per slot: the slot's items, and its state reset (first segment pending, no T
+// out yet, no chunk has saturated a pixel).
+__global__ void __launch_bounds__(256) split_reset_kernel(SplitWs ws) {
+  const uint32_t slot = blockIdx.x;
+  if (slot >= ws.counters[0]) return;
+  const int tid = threadIdx.x;
+  const size_t so = size_t(slot) * 256 + tid;
+  ws.sat[so] = 0xffffffffu;
+  ws.tfirst[so] = -1.0f;
+  if (tid == 0) ws.state[slot] = kPending;
+  const uint32_t fi = ws.slot_first[slot], nch = ws.slot_nch[slot];
+  for (uint32_t c = tid; c < nch; c += 256) ws.items[fi + c] = make_uint2(slot, c);
 }
 
 // ------------------------------------------------------------ forward walk
@@ -366,12 +416,16 @@ struct PixelFwd {
 
 // Walks the pairs [lo, hi) of a tile list starting at `start`.  A pixel stops once
 // pre * T < 1e-4 (pre = 1 for a walk whose T is the overall transmittance).  With
-// POLL, a pixel also stops when sat[tid] < chunk_id; a pixel that saturates here
-// records chunk_id in sat[tid].  Must be called by all 256 threads of the block.
+// POLL (a chunk of a split candidate), after every batch: a pixel also stops when
+// sat[tid] < chunk_id, and a pixel that saturates records chunk_id in sat[tid]; a pixel
+// whose bound is not yet known (pre = 1) takes the tile's T after its first segment once
+// tfirst[tid] holds it (>= 0); and every pixel stops once the tile turns out not split.
+// Must be called by all 256 threads of the block.
 template <bool POLL>
 __device__ void fwd_walk(FwdLds& L, const float4* __restrict__ splat, const uint32_t* __restrict__ vals,
                          uint32_t start, int lo, int hi, float ox, float oy, float fx, float fy, float pre,
-                         PixelFwd& s, uint32_t* sat, uint32_t chunk_id) {
+                         PixelFwd& s, uint32_t* sat, uint32_t chunk_id, const float* tfirst = nullptr,
+                         const uint32_t* state = nullptr, bool known = true) {
   const int tid = threadIdx.x;
   if (lo >= hi) return;
   {
@@ -434,14 +488,68 @@ __device__ void fwd_walk(FwdLds& L, const float4* __restrict__ splat, const uint
           reported = true;
         }
       }
+      if (!s.done && !known) {
+        const float tf = __hip_atomic_load(&tfirst[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tf >= 0.0f) {
+          known = true;
+          pre = tf;
+          if (pre * s.T < kTStop) {   // a claim of its own, as in the blend
+            s.done = true;
+          }
+        }
+      }
+      if (!s.done && __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kNotSplit) {
+        s.done = true;
+        reported = true;   // not a saturation: nothing to record
+      }
     }
     if (__syncthreads_count(s.done) == kBatch) break;
     buf ^= 1;
   }
 }
 
-// Phase 1: the first `first` pairs of every tile; tiles that are not finished then
-// are registered for the split path and write no output here.
+// One chunk of a split candidate, walked from T = 1 (the chunk's own transmittance and
+// colour).  Its pixels stop once B T < 1e-4, B an upper bound of the transmittance in front
+// of the chunk: 1 while the tile's first segment still runs, its T after the first
+// segment once that is out (every later factor is at most 1, also in fp32, so the overall
+// T has dropped below 1e-4 by then too, and the combine finds the stop in this chunk or
+// an earlier one); pixels that an earlier chunk has already saturated are dropped (a
+// per-pixel "first saturating chunk", polled), and the whole walk once the first segment
+// has finished every pixel (the tile is not split; what the chunk writes is then unused).
+__device__ void split_chunk(FwdLds& L, const float4* __restrict__ splat, const uint32_t* __restrict__ vals,
+                            const uint32_t* __restrict__ ranges, const SplitWs& ws, int num_tiles, int tx, int first,
+                            int chunk, uint32_t item) {
+  if (item >= ws.counters[1]) return;
+  const uint2 sc = ws.items[item];
+  const uint32_t slot = sc.x, c = sc.y;
+  const int tid = threadIdx.x;
+  const uint32_t* state = ws.state + slot;
+  if (__syncthreads_count(__hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kNotSplit) == kBlock)
+    return;
+  const int tile = int(ws.slot_tile[slot]);
+  const int px = (tile % tx) * kTile + pixel_x(tid);
+  const int py = (tile / tx) * kTile + pixel_y(tid);
+  const uint32_t start = ranges[tile];
+  const int n = int(ranges[num_tiles + tile] - start);
+  const int lo = first + int(c) * chunk, hi = min(lo + chunk, n);
+  const size_t so = size_t(slot) * 256 + tid;
+  const float tf = __hip_atomic_load(&ws.tfirst[so], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool known = tf >= 0.0f;
+  const float pre = known ? tf : 1.0f;
+  PixelFwd s{1.0f, 0.0f, 0.0f, 0.0f, 0u, pre < kTStop};
+  fwd_walk<true>(L, splat, vals, start, lo, hi, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f,
+                 float(py) + 0.5f, pre, s, ws.sat + size_t(slot) * 256, c, ws.tfirst + size_t(slot) * 256, state,
+                 known);
+  const size_t io = size_t(item) * 256 + tid;
+  ws.part4[io] = make_float4(s.T, s.c0, s.c1, s.c2);
+  ws.partl[io] = s.last;
+}
+
+// Phase 1, one launch: blocks [0, num_tiles) walk the first `first` pairs of every tile,
+// longest list first; the blocks after them walk the chunks of the split candidates, so
+// that they fill the CUs that the last long first segments leave idle.  A candidate whose
+// pixels are not all finished after its first segment is split: its block writes no
+// output, leaves its state for the combine and publishes its per-pixel T for the chunks.
 __global__ void __launch_bounds__(256) render_fwd_kernel(const float4* __restrict__ splat,
                                                           const uint32_t* __restrict__ vals,
                                                           const uint32_t* __restrict__ ranges, SplitWs ws,
@@ -450,7 +558,10 @@ __global__ void __launch_bounds__(256) render_fwd_kernel(const float4* __restric
                                                           float* __restrict__ T_final,
                                                           uint32_t* __restrict__ n_contrib) {
   __shared__ FwdLds L;
-  __shared__ uint32_t s_slot, s_first, s_nch;
+  if (blockIdx.x >= uint32_t(num_tiles)) {
+    split_chunk(L, splat, vals, ranges, ws, num_tiles, tx, first, chunk, blockIdx.x - uint32_t(num_tiles));
+    return;
+  }
   const int tile = int(ws.order[blockIdx.x]);
   const int tid = threadIdx.x;
   const int px = (tile % tx) * kTile + pixel_x(tid);
@@ -462,25 +573,17 @@ __global__ void __launch_bounds__(256) render_fwd_kernel(const float4* __restric
   fwd_walk<false>(L, splat, vals, start, 0, min(n, first), tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f,
                   float(py) + 0.5f, 1.0f, s, nullptr, 0u);
   if (n > first) {
+    const uint32_t slot = uint32_t(ws.slot_of_tile[tile]);
     if (__syncthreads_count(s.done) < kBatch) {
-      if (tid == 0) {
-        const uint32_t slot = atomicAdd(&ws.counters[0], 1u);
-        const uint32_t nch = uint32_t((n - first + chunk - 1) / chunk);
-        const uint32_t fi = atomicAdd(&ws.counters[1], nch);
-        ws.slot_tile[slot] = uint32_t(tile);
-        ws.slot_first[slot] = fi;
-        ws.slot_nch[slot] = nch;
-        ws.slot_of_tile[tile] = int32_t(slot);
-        s_slot = slot; s_first = fi; s_nch = nch;
-      }
-      __syncthreads();
-      const size_t o = size_t(s_slot) * 256 + tid;
+      const size_t o = size_t(slot) * 256 + tid;
       ws.st4[o] = make_float4(s.T, s.c0, s.c1, s.c2);
       ws.stl[o] = s.last | (s.done ? kFlag : 0u);
-      ws.sat[o] = s.done ? 0u : 0xffffffffu;
-      for (uint32_t c = tid; c < s_nch; c += 256) ws.items[s_first + c] = make_uint2(s_slot, c);
+      __hip_atomic_store(&ws.tfirst[o], s.done ? 0.0f : s.T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(ws.state + slot, kSplit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
+    if (tid == 0) __hip_atomic_store(ws.state + slot, kNotSplit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (inside) {
     const int p = py * W + px;
@@ -493,45 +596,12 @@ __global__ void __launch_bounds__(256) render_fwd_kernel(const float4* __restric
   }
 }
 
-// Phase 2: one block per chunk of a split tile.
-__global__ void __launch_bounds__(256) split_chunk_kernel(const float4* __restrict__ splat,
-                                                           const uint32_t* __restrict__ vals,
-                                                           const uint32_t* __restrict__ ranges, SplitWs ws,
-                                                           int num_tiles, int tx, int first, int chunk) {
-  __shared__ FwdLds L;
-  const uint32_t item = blockIdx.x;
-  if (item >= ws.counters[1]) return;
-  const uint2 sc = ws.items[item];
-  const uint32_t slot = sc.x, c = sc.y;
-  const int tile = int(ws.slot_tile[slot]);
-  const int tid = threadIdx.x;
-  const int px = (tile % tx) * kTile + pixel_x(tid);
-  const int py = (tile / tx) * kTile + pixel_y(tid);
-  const uint32_t start = ranges[tile];
-  const int n = int(ranges[num_tiles + tile] - start);
-  const int lo = first + int(c) * chunk, hi = min(lo + chunk, n);
-  const size_t so = size_t(slot) * 256 + tid;
-  const bool done0 = (ws.stl[so] & kFlag) != 0u;
-  const float T_first = ws.st4[so].x;   // transmittance after the first segment
-  PixelFwd s{c == 0 ? T_first : 1.0f, 0.0f, 0.0f, 0.0f, 0u, done0};
-  if (c == 0)
-    fwd_walk<false>(L, splat, vals, start, lo, hi, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f,
-                    float(py) + 0.5f, 1.0f, s, nullptr, 0u);
-  else   // T_first bounds the transmittance in front of this chunk from above
-    fwd_walk<true>(L, splat, vals, start, lo, hi, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f,
-                   float(py) + 0.5f, T_first, s, ws.sat + size_t(slot) * 256, c);
-  const size_t io = size_t(item) * 256 + tid;
-  ws.part4[io] = make_float4(s.T, s.c0, s.c1, s.c2);
-  // chunk 0 continues the exact walk: its flag means "stopped here"
-  const bool stopped0 = c == 0 && !done0 && s.T < kTStop;
-  ws.partl[io] = s.last | (stopped0 ? kFlag : 0u);
-  if (c == 0 && stopped0) atomicMin(&ws.sat[so], 0u);
-}
-
-// Phase 3: per split tile and pixel, chain the chunks and find the one holding the stop.
+// Phase 2: per split tile and pixel, chain the chunks from the first segment's state,
+// T_front(c + 1) = T_front(c) T_c and colour += T_front(c) C_c, until the product falls
+// below 1e-4: the chunk where it does holds the stop.
 __global__ void __launch_bounds__(256) split_combine_kernel(SplitWs ws) {
   const uint32_t slot = blockIdx.x;
-  if (slot >= ws.counters[0]) return;
+  if (slot >= ws.counters[0] || ws.state[slot] != kSplit) return;
   const int tid = threadIdx.x;
   const size_t so = size_t(slot) * 256 + tid;
   const uint32_t fi = ws.slot_first[slot], nch = ws.slot_nch[slot];
@@ -543,19 +613,11 @@ __global__ void __launch_bounds__(256) split_combine_kernel(SplitWs ws) {
   if (l1 & kFlag) {
     stop = -1;
   } else {
-    const size_t o0 = size_t(fi) * 256 + tid;
-    const float4 p0 = ws.part4[o0];   // absolute T after chunk 0 and the colour chunk 0 added
-    const uint32_t l0 = ws.partl[o0];
-    T = p0.x;
-    c0 += p0.y; c1 += p0.z; c2 += p0.w;
-    if (l0 & kIdx) last = l0 & kIdx;
-    if (l0 & kFlag) {
-      stop = 0;
-    } else {
+    {
       stop = int32_t(nch);
       // chunks in groups of sixteen: their partials are loaded before they are chained
       constexpr int kG = 16;
-      for (uint32_t c0g = 1; c0g < nch && stop == int32_t(nch); c0g += kG) {
+      for (uint32_t c0g = 0; c0g < nch && stop == int32_t(nch); c0g += kG) {
         float4 pc[kG];
         uint32_t lc[kG];
 #pragma unroll
@@ -590,7 +652,7 @@ __global__ void __launch_bounds__(256) split_combine_kernel(SplitWs ws) {
   ws.finl[so] = last;
 }
 
-// Phase 4: walk again the chunk that holds a pixel's stop, from T_front, to find the pair.
+// Phase 3: walk again the chunk that holds a pixel's stop, from T_front, to find the pair.
 __global__ void __launch_bounds__(256) split_rewalk_kernel(const float4* __restrict__ splat,
                                                             const uint32_t* __restrict__ vals,
                                                             const uint32_t* __restrict__ ranges, SplitWs ws,
@@ -600,7 +662,7 @@ __global__ void __launch_bounds__(256) split_rewalk_kernel(const float4* __restr
   if (item >= ws.counters[1]) return;
   const uint2 sc = ws.items[item];
   const uint32_t slot = sc.x, c = sc.y;
-  if (c == 0) return;
+  if (ws.state[slot] != kSplit) return;
   const int tid = threadIdx.x;
   const size_t so = size_t(slot) * 256 + tid;
   const bool need = ws.stopc[so] == int32_t(c);
@@ -629,14 +691,14 @@ __global__ void __launch_bounds__(256) split_rewalk_kernel(const float4* __restr
   }
 }
 
-// Phase 5: outputs of split tiles, and the chunk-end states for the backward
+// Phase 4: outputs of split tiles, and the chunk-end states for the backward
 // (T there and S = colour behind, summed from the background forward).
 __global__ void __launch_bounds__(256) split_finalize_kernel(SplitWs ws, int tx, int W, int H, float bg0,
                                                               float bg1, float bg2, float* __restrict__ rgb,
                                                               float* __restrict__ T_final,
                                                               uint32_t* __restrict__ n_contrib) {
   const uint32_t slot = blockIdx.x;
-  if (slot >= ws.counters[0]) return;
+  if (slot >= ws.counters[0] || ws.state[slot] != kSplit) return;
   const int tid = threadIdx.x;
   const int tile = int(ws.slot_tile[slot]);
   const int px = (tile % tx) * kTile + pixel_x(tid);
@@ -979,7 +1041,7 @@ __device__ void bwd_tile(BwdLds& L, const BwdArgs& A, const SplitWs& ws, int til
     s.g1 = dL_dimg[HW + p];
     s.g2 = dL_dimg[2 * HW + p];
     const int32_t slot = ws.slot_of_tile[tile];
-    if (slot >= 0 && ws.stopc[size_t(slot) * 256 + tid] >= 0) {
+    if (slot >= 0 && ws.state[slot] == kSplit && ws.stopc[size_t(slot) * 256 + tid] >= 0) {
       // the pixel's pairs continue past the first segment: start from its end state
       const float4 b = ws.bnd1[size_t(slot) * 256 + tid];
       s.T = b.x; s.S0 = b.y; s.S1 = b.z; s.S2 = b.w;
@@ -1008,6 +1070,7 @@ __device__ void bwd_chunk(BwdLds& L, const BwdArgs& A, const SplitWs& ws, uint32
   float* __restrict__ gscreen = A.gscreen;
   const uint2 sc = ws.items[item];
   const uint32_t slot = sc.x, c = sc.y;
+  if (ws.state[slot] != kSplit) return;   // a candidate that its first segment finished
   const int tile = int(ws.slot_tile[slot]);
   const int tid = threadIdx.x;
   const int px = (tile % tx) * kTile + pixel_x(tid);
@@ -1143,21 +1206,21 @@ hipError_t launch_render_fwd(const gs_proj& proj, const uint32_t* vals, const ui
   const float4* splat = reinterpret_cast<const float4*>(proj.splat);
   {
     GSK_PROF("tile_order", s);
-    tile_order_kernel<<<1, 1024, 0, s>>>(ranges, num_tiles, ws.order, ws.counters, ws.slot_of_tile,
-                                         static_cast<RenderHeader*>(wsp), h);
+    tile_order_kernel<<<1, 1024, 0, s>>>(ranges, num_tiles, ws, first, chunk, static_cast<RenderHeader*>(wsp), h);
+  }
+  const bool split = pairs > uint32_t(first);
+  if (split) {
+    GSK_PROF("split_reset", s);
+    split_reset_kernel<<<unsigned(d.S), 256, 0, s>>>(ws);
   }
   {
     GSK_PROF("render_fwd", s);
-    render_fwd_kernel<<<num_tiles, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, cam.width, cam.height,
-                                                cam.bg[0], cam.bg[1], cam.bg[2], first, chunk, rgb, T_final,
-                                                n_contrib);
+    const unsigned blocks = unsigned(num_tiles) + (split ? unsigned(d.I) : 0u);
+    render_fwd_kernel<<<blocks, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, cam.width, cam.height, cam.bg[0],
+                                             cam.bg[1], cam.bg[2], first, chunk, rgb, T_final, n_contrib);
   }
-  if (pairs > uint32_t(first)) {
+  if (split) {
     const unsigned items = unsigned(d.I), slots = unsigned(d.S);
-    {
-      GSK_PROF("split_chunk", s);
-      split_chunk_kernel<<<items, 256, 0, s>>>(splat, vals, ranges, ws, num_tiles, tx, first, chunk);
-    }
     {
       GSK_PROF("split_combine", s);
       split_combine_kernel<<<slots, 256, 0, s>>>(ws);
