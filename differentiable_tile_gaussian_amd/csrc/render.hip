@@ -598,58 +598,99 @@ __global__ void __launch_bounds__(256) render_fwd_kernel(const float4* __restric
 
 // Phase 2: per split tile and pixel, chain the chunks from the first segment's state,
 // T_front(c + 1) = T_front(c) T_c and colour += T_front(c) C_c, until the product falls
-// below 1e-4: the chunk where it does holds the stop.
-__global__ void __launch_bounds__(256) split_combine_kernel(SplitWs ws) {
+// below 1e-4: the chunk where it does holds the stop.  Four threads per pixel, each a
+// quarter of the chunks: each first multiplies its quarter's T_c, the fronts of the
+// quarters follow from those in quarter order, then each chains its quarter from its
+// front; the first quarter that finds the stop decides it.  Chunk partials are loaded
+// sixteen at a time before they are used.
+constexpr int kCombG = 16;
+__global__ void __launch_bounds__(1024) split_combine_kernel(SplitWs ws) {
+  __shared__ float s_P[4][256];
+  __shared__ float4 s_st[4][256];   // T at the quarter's stop (or end), colour the quarter added
+  __shared__ int32_t s_stop[4][256];
+  __shared__ uint32_t s_last[4][256];
   const uint32_t slot = blockIdx.x;
   if (slot >= ws.counters[0] || ws.state[slot] != kSplit) return;
-  const int tid = threadIdx.x;
-  const size_t so = size_t(slot) * 256 + tid;
+  const int tid = threadIdx.x, q = tid >> 8, p = tid & 255;
+  const size_t so = size_t(slot) * 256 + p;
   const uint32_t fi = ws.slot_first[slot], nch = ws.slot_nch[slot];
+  const uint32_t m = (nch + 3u) / 4u, c0 = min(nch, uint32_t(q) * m), c1 = min(nch, c0 + m);
   const uint32_t l1 = ws.stl[so];
   const float4 s1 = ws.st4[so];
-  float T = s1.x, c0 = s1.y, c1 = s1.z, c2 = s1.w;
-  uint32_t last = l1 & kIdx;
-  int32_t stop;
-  if (l1 & kFlag) {
-    stop = -1;
-  } else {
-    {
-      stop = int32_t(nch);
-      // chunks in groups of sixteen: their partials are loaded before they are chained
-      constexpr int kG = 16;
-      for (uint32_t c0g = 0; c0g < nch && stop == int32_t(nch); c0g += kG) {
-        float4 pc[kG];
-        uint32_t lc[kG];
+  const bool done0 = (l1 & kFlag) != 0u;
+  // the quarter's own product
+  float P = 1.0f;
+  if (!done0) {
+    for (uint32_t g = c0; g < c1; g += kCombG) {
+      float t[kCombG];
 #pragma unroll
-        for (int k = 0; k < kG; ++k) {
-          const uint32_t c = c0g + k;
-          if (c < nch) {
-            pc[k] = ws.part4[size_t(fi + c) * 256 + tid];
-            lc[k] = ws.partl[size_t(fi + c) * 256 + tid] & kIdx;
-          }
+      for (int k = 0; k < kCombG; ++k) t[k] = g + k < c1 ? ws.part4[size_t(fi + g + k) * 256 + p].x : 1.0f;
+#pragma unroll
+      for (int k = 0; k < kCombG; ++k) P = P * t[k];
+    }
+  }
+  s_P[q][p] = P;
+  __syncthreads();
+  float T = s1.x;
+  for (int k = 0; k < q; ++k) T = T * s_P[k][p];
+  // the quarter chained from its front
+  int32_t stop = -1;
+  float a0s = 0.0f, a1s = 0.0f, a2s = 0.0f;
+  uint32_t last = 0u;
+  if (!done0) {
+    for (uint32_t g = c0; g < c1 && stop < 0; g += kCombG) {
+      float4 pc[kCombG];
+      uint32_t lc[kCombG];
+#pragma unroll
+      for (int k = 0; k < kCombG; ++k) {
+        if (g + k < c1) {
+          pc[k] = ws.part4[size_t(fi + g + k) * 256 + p];
+          lc[k] = ws.partl[size_t(fi + g + k) * 256 + p] & kIdx;
         }
+      }
 #pragma unroll
-        for (int k = 0; k < kG; ++k) {
-          const uint32_t c = c0g + k;
-          if (c < nch && stop == int32_t(nch)) {
-            const float Tn = T * pc[k].x;
-            if (Tn < kTStop) {
-              stop = int32_t(c);
-            } else {
-              const float a0 = T * pc[k].y, a1 = T * pc[k].z, a2 = T * pc[k].w;
-              ws.part4[size_t(fi + c) * 256 + tid] = make_float4(Tn, a0, a1, a2);   // T at the chunk end, colour it added
-              c0 += a0; c1 += a1; c2 += a2;
-              T = Tn;
-              if (lc[k]) last = lc[k];
-            }
+      for (int k = 0; k < kCombG; ++k) {
+        const uint32_t c = g + k;
+        if (c < c1 && stop < 0) {
+          const float Tn = T * pc[k].x;
+          if (Tn < kTStop) {
+            stop = int32_t(c);
+          } else {
+            const float a0 = T * pc[k].y, a1 = T * pc[k].z, a2 = T * pc[k].w;
+            ws.part4[size_t(fi + c) * 256 + p] = make_float4(Tn, a0, a1, a2);   // T at the chunk end, colour it added
+            a0s += a0; a1s += a1; a2s += a2;
+            T = Tn;
+            if (lc[k]) last = lc[k];
           }
         }
       }
     }
   }
-  ws.stopc[so] = stop;
-  ws.fin4[so] = make_float4(T, c0, c1, c2);
-  ws.finl[so] = last;
+  s_st[q][p] = make_float4(T, a0s, a1s, a2s);
+  s_stop[q][p] = stop;
+  s_last[q][p] = last;
+  __syncthreads();
+  if (q != 0) return;
+  float c0f = s1.y, c1f = s1.z, c2f = s1.w;
+  uint32_t lastf = l1 & kIdx;
+  float Tf = s1.x;
+  int32_t stopf = -1;
+  if (!done0) {
+    stopf = int32_t(nch);
+    for (int k = 0; k < 4; ++k) {
+      const float4 st = s_st[k][p];
+      c0f += st.y; c1f += st.z; c2f += st.w;
+      if (s_last[k][p]) lastf = s_last[k][p];
+      Tf = st.x;
+      if (s_stop[k][p] >= 0) {
+        stopf = s_stop[k][p];
+        break;
+      }
+    }
+  }
+  ws.stopc[so] = stopf;
+  ws.fin4[so] = make_float4(Tf, c0f, c1f, c2f);
+  ws.finl[so] = lastf;
 }
 
 // Phase 3: walk again the chunk that holds a pixel's stop, from T_front, to find the pair.
@@ -1223,7 +1264,7 @@ hipError_t launch_render_fwd(const gs_proj& proj, const uint32_t* vals, const ui
     const unsigned items = unsigned(d.I), slots = unsigned(d.S);
     {
       GSK_PROF("split_combine", s);
-      split_combine_kernel<<<slots, 256, 0, s>>>(ws);
+      split_combine_kernel<<<slots, 1024, 0, s>>>(ws);
     }
     {
       GSK_PROF("split_rewalk", s);
