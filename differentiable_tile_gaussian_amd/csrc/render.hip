@@ -88,8 +88,17 @@ constexpr float kLog2e = 1.44269504088896341f;
 constexpr uint32_t kFlag = 0x80000000u;
 constexpr uint32_t kIdx = 0x7fffffffu;
 // A split candidate's first segment (SplitWs::state): still walking, unfinished pixels
-// after it (the tile is split), or all pixels finished within it.
-constexpr uint32_t kPending = 0u, kSplit = 1u, kNotSplit = 2u;
+// after it (the tile is split), or all pixels finished within it; kDoneBase + c: split,
+// and the chunks' running transmittance chain has found every pixel finished by the end
+// of chunk c (the later chunks are not walked).
+constexpr uint32_t kPending = 0u, kSplit = 1u, kNotSplit = 2u, kDoneBase = 3u;
+__host__ __device__ inline bool is_split(uint32_t st) { return st == kSplit || st >= kDoneBase; }
+// The chain's products are bounds of the combine's own (other roundings): a chunk stops a
+// pixel against its bound times kChainSlack, and the chain calls a pixel finished only
+// below kTChainDone, so that the combine finds every stop in a chunk that was walked.
+constexpr float kChainSlack = 1.001f;
+constexpr float kTChainDone = 0.999e-4f;
+constexpr uint32_t kChainLook = 8;   // chunks between the chain and the one moving it, at most
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -106,8 +115,13 @@ struct SplitWs {
   float4* st4;            // [S][256] T and colour after the first segment
   uint32_t* stl;          // [S][256] last pair | done flag
   uint32_t* sat;          // [S][256] first chunk that saturated the pixel
-  uint32_t* state;        // [S] the tile's first segment: kPending, kSplit or kNotSplit
-  float* tfirst;          // [S][256] T after the first segment (0: finished there; -1: not out yet)
+  uint32_t* state;        // [S] the tile's first segment: kPending, kSplit or kNotSplit; or kDoneBase + c
+  float* tfirst;          // [S][256] T in front of chunk chain[slot] (first: after the first segment;
+                          // 0: finished there; -1: not out yet); the chunks advance it in order
+  uint32_t* chain;        // [S] the chunk whose front tfirst holds (none before the first segment ends)
+  uint32_t* disp;         // [I] chunks in dispatch order (chunk index major)
+  uint32_t* rbase;        // [I] first dispatch place of the chunks with index c
+  float* tl;              // [I][256] each chunk's own transmittance once walked (-1 before)
   float4* part4;          // [I][256] chunk partials, later (T_end, S_end) boundaries
   uint32_t* partl;        // [I][256] last pair in the chunk | stop flag
   int32_t* stopc;         // [S][256] chunk holding the last pair (-1: first segment, nch: none)
@@ -147,6 +161,10 @@ __host__ __device__ inline SplitWs carve(void* ws, const SplitDims& d) {
   w.sat = reinterpret_cast<uint32_t*>(take(d.S * 256 * 4));
   w.state = reinterpret_cast<uint32_t*>(take(d.S * 4));
   w.tfirst = reinterpret_cast<float*>(take(d.S * 256 * 4));
+  w.chain = reinterpret_cast<uint32_t*>(take(d.S * 4));
+  w.disp = reinterpret_cast<uint32_t*>(take(d.I * 4));
+  w.rbase = reinterpret_cast<uint32_t*>(take(d.I * 4));
+  w.tl = reinterpret_cast<float*>(take(d.I * 256 * 4));
   w.part4 = reinterpret_cast<float4*>(take(d.I * 256 * 16));
   w.partl = reinterpret_cast<uint32_t*>(take(d.I * 256 * 4));
   w.stopc = reinterpret_cast<int32_t*>(take(d.S * 256 * 4));
@@ -158,7 +176,7 @@ __host__ __device__ inline SplitWs carve(void* ws, const SplitDims& d) {
 
 __host__ __device__ inline size_t carve_bytes(const SplitDims& d) {
   return a256(d.NT * 4) + a256(8) + a256(d.NT * 4) + 3 * a256(d.S * 4) + a256(d.I * 8) + a256(d.S * 256 * 16) +
-         2 * a256(d.S * 256 * 4) + a256(d.S * 4) + a256(d.S * 256 * 4) + a256(d.I * 256 * 16) + a256(d.I * 256 * 4) + a256(d.S * 256 * 4) +
+         2 * a256(d.S * 256 * 4) + 2 * a256(d.S * 4) + a256(d.S * 256 * 4) + 2 * a256(d.I * 4) + a256(d.I * 256 * 4) + a256(d.I * 256 * 16) + a256(d.I * 256 * 4) + a256(d.S * 256 * 4) +
          a256(d.S * 256 * 16) + a256(d.S * 256 * 4) + a256(d.S * 256 * 16);
 }
 
@@ -193,23 +211,62 @@ __device__ inline bool header_ok(const HeaderCheck& c, RenderHeader& h) {
 }
 
 // ---------------------------------------------------------------- tile order
+// Exclusive prefix sums of one value per thread of a 1024-thread block (wave sums by
+// shuffles, then the sixteen waves' totals), and their total.  All threads must call it.
+__device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* s_w, uint32_t& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) s_w[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    uint32_t t = lane < 16 ? s_w[lane] : 0u;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const uint32_t y = __shfl_up(t, d, 64);
+      if (lane >= d) t += y;
+    }
+    if (lane < 16) s_w[16 + lane] = t;
+  }
+  __syncthreads();
+  const uint32_t wbase = w ? s_w[16 + w - 1] : 0u;
+  total = s_w[31];
+  __syncthreads();
+  return wbase + x - v;
+}
+
 // Tiles sorted by bucket 32 - clz(length), longest bucket first (order within a
 // bucket is arbitrary).  One block; num_tiles may exceed the block size.  The block also
 // writes the workspace header and gives every tile whose list is longer than `first` (a
 // split candidate: whether it is split is known only when its first segment ends) a slot
 // and the items of its chunks, taking the tiles in that order; the other tiles get none.
+// The chunks are dispatched chunk index first (every candidate's chunk 0, then chunk 1,
+// ...), so that a tile's chunk has mostly finished before its next ones start and the
+// running transmittance chain can tell them when their tile is finished; with more than
+// kMaxChunksOrdered chunks in a tile, tile by tile instead.
+constexpr uint32_t kMaxChunksOrdered = 2048;
 __global__ void __launch_bounds__(1024) tile_order_kernel(const uint32_t* __restrict__ ranges, int num_tiles,
                                                            SplitWs ws, int first, int chunk,
                                                            RenderHeader* __restrict__ hdr, RenderHeader h) {
   __shared__ uint32_t s_cnt[33];
   __shared__ uint32_t s_pos[33];
-  __shared__ uint32_t s_slots, s_items;
+  __shared__ uint32_t s_slots, s_items, s_maxnch;
+  __shared__ uint32_t s_h[kMaxChunksOrdered + 1];      // slots with that many chunks
+  __shared__ uint32_t s_oslot[kMaxChunksOrdered + 1];  // first slot of those
+  __shared__ uint32_t s_oitem[kMaxChunksOrdered + 1];  // their first item
+  __shared__ uint32_t s_fill[kMaxChunksOrdered + 1];
+  __shared__ uint32_t s_w[32];
   const int tid = threadIdx.x;
   if (tid < 33) s_cnt[tid] = 0u;
   if (tid == 0) {
     *hdr = h;
-    s_slots = s_items = 0u;
+    s_slots = s_items = s_maxnch = 0u;
   }
+  for (uint32_t c = tid; c <= kMaxChunksOrdered; c += blockDim.x) s_h[c] = s_fill[c] = 0u;
   __syncthreads();
   for (int t = tid; t < num_tiles; t += blockDim.x) {
     const uint32_t len = ranges[num_tiles + t] - ranges[t];
@@ -236,22 +293,76 @@ __global__ void __launch_bounds__(1024) tile_order_kernel(const uint32_t* __rest
     ws.order[atomicAdd(&s_pos[b], 1u)] = uint32_t(t);
   }
   __syncthreads();
+  // the candidates' chunk counts; the slots sorted by them, most first, so that the
+  // candidates with more than c chunks are the first slots and dispatch round c is
+  // places rbase[c] + slot (tile order again with longer lists than the LDS tables hold)
   for (int p = tid; p < span; p += blockDim.x) {
     const uint32_t tile = ws.order[p];
     const int len = int(ranges[num_tiles + tile] - ranges[tile]);
     if (len > first) {
       const uint32_t nch = uint32_t((len - first + chunk - 1) / chunk);
-      const uint32_t slot = atomicAdd(&s_slots, 1u);
+      atomicMax(&s_maxnch, nch);
+      atomicAdd(&s_h[nch < kMaxChunksOrdered ? nch : kMaxChunksOrdered], 1u);
+    }
+  }
+  __syncthreads();
+  const uint32_t maxnch = s_maxnch;
+  const bool ordered = maxnch <= kMaxChunksOrdered;
+  uint32_t run_s = 0u, run_i = 0u;   // slots and items (ordered)
+  if (ordered) {
+    // j = maxnch - k runs over the chunk counts k from the most down: the first slot and
+    // item of the slots with k chunks are the sums over the counts above k
+    for (uint32_t j0 = 0; j0 < maxnch; j0 += 1024) {
+      const uint32_t j = j0 + uint32_t(tid), k = maxnch - j;
+      const uint32_t h = j < maxnch ? s_h[k] : 0u;
+      uint32_t ts, ti;
+      const uint32_t es = block_excl_scan(h, s_w, ts), ei = block_excl_scan(h * k, s_w, ti);
+      if (j < maxnch) {
+        s_oslot[k] = run_s + es;
+        s_oitem[k] = run_i + ei;
+      }
+      run_s += ts;
+      run_i += ti;
+    }
+    __syncthreads();
+    // round c (the chunks with index c) holds the slots with more than c chunks, s_oslot[c]
+    // of them for c >= 1 and all of them for c = 0; rbase: the rounds' first places
+    uint32_t run = 0u;
+    for (uint32_t c0 = 0; c0 < maxnch; c0 += 1024) {
+      const uint32_t c = c0 + uint32_t(tid);
+      const uint32_t size = c < maxnch ? (c == 0 ? run_s : s_oslot[c]) : 0u;
+      uint32_t tot;
+      const uint32_t e = block_excl_scan(size, s_w, tot);
+      if (c < maxnch) ws.rbase[c] = run + e;
+      run += tot;
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < span; p += blockDim.x) {
+    const uint32_t tile = ws.order[p];
+    const int len = int(ranges[num_tiles + tile] - ranges[tile]);
+    if (len > first) {
+      const uint32_t nch = uint32_t((len - first + chunk - 1) / chunk);
+      uint32_t slot, fi;
+      if (ordered) {
+        const uint32_t r = atomicAdd(&s_fill[nch], 1u);
+        slot = s_oslot[nch] + r;
+        fi = s_oitem[nch] + r * nch;
+      } else {
+        slot = atomicAdd(&s_slots, 1u);
+        fi = atomicAdd(&s_items, nch);
+      }
       ws.slot_tile[slot] = tile;
-      ws.slot_first[slot] = atomicAdd(&s_items, nch);
+      ws.slot_first[slot] = fi;
       ws.slot_nch[slot] = nch;
       ws.slot_of_tile[tile] = int32_t(slot);
     }
   }
   __syncthreads();
   if (tid == 0) {
-    ws.counters[0] = s_slots;
-    ws.counters[1] = s_items;
+    ws.counters[0] = ordered ? run_s : s_slots;
+    ws.counters[1] = ordered ? run_i : s_items;
+    ws.counters[3] = ordered ? 1u : 0u;
   }
 }
 
@@ -264,9 +375,17 @@ __global__ void __launch_bounds__(256) split_reset_kernel(SplitWs ws) {
   const size_t so = size_t(slot) * 256 + tid;
   ws.sat[so] = 0xffffffffu;
   ws.tfirst[so] = -1.0f;
-  if (tid == 0) ws.state[slot] = kPending;
+  if (tid == 0) {
+    ws.state[slot] = kPending;
+    ws.chain[slot] = 0xffffffffu;
+  }
   const uint32_t fi = ws.slot_first[slot], nch = ws.slot_nch[slot];
-  for (uint32_t c = tid; c < nch; c += 256) ws.items[fi + c] = make_uint2(slot, c);
+  const bool ordered = ws.counters[3] != 0u;
+  for (uint32_t c = tid; c < nch; c += 256) {
+    ws.items[fi + c] = make_uint2(slot, c);
+    ws.disp[ordered ? ws.rbase[c] + slot : fi + c] = fi + c;
+  }
+  for (uint32_t c = 0; c < nch; ++c) ws.tl[size_t(fi + c) * 256 + tid] = -1.0f;
 }
 
 // ------------------------------------------------------------ forward walk
@@ -488,19 +607,22 @@ __device__ void fwd_walk(FwdLds& L, const float4* __restrict__ splat, const uint
           reported = true;
         }
       }
-      if (!s.done && !known) {
+      if (!s.done) {   // the chain may have moved on: a tighter bound
         const float tf = __hip_atomic_load(&tfirst[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (tf >= 0.0f) {
           known = true;
-          pre = tf;
+          pre = fminf(pre, tf * kChainSlack);
           if (pre * s.T < kTStop) {   // a claim of its own, as in the blend
             s.done = true;
           }
         }
       }
-      if (!s.done && __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kNotSplit) {
-        s.done = true;
-        reported = true;   // not a saturation: nothing to record
+      if (!s.done) {
+        const uint32_t st = __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (st == kNotSplit || (st >= kDoneBase && chunk_id > st - kDoneBase)) {
+          s.done = true;
+          reported = true;   // not a saturation: nothing to record
+        }
       }
     }
     if (__syncthreads_count(s.done) == kBatch) break;
@@ -519,13 +641,17 @@ __device__ void fwd_walk(FwdLds& L, const float4* __restrict__ splat, const uint
 __device__ void split_chunk(FwdLds& L, const float4* __restrict__ splat, const uint32_t* __restrict__ vals,
                             const uint32_t* __restrict__ ranges, const SplitWs& ws, int num_tiles, int tx, int first,
                             int chunk, uint32_t item) {
-  if (item >= ws.counters[1]) return;
+  __shared__ uint32_t s_chain;
   const uint2 sc = ws.items[item];
   const uint32_t slot = sc.x, c = sc.y;
   const int tid = threadIdx.x;
   const uint32_t* state = ws.state + slot;
-  if (__syncthreads_count(__hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kNotSplit) == kBlock)
-    return;
+  // not walked: the tile turned out not split, or its chain found every pixel finished before
+  const auto cut = [&]() {
+    const uint32_t st = __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return st == kNotSplit || (st >= kDoneBase && c > st - kDoneBase);
+  };
+  if (__syncthreads_count(cut()) == kBlock) return;
   const int tile = int(ws.slot_tile[slot]);
   const int px = (tile % tx) * kTile + pixel_x(tid);
   const int py = (tile / tx) * kTile + pixel_y(tid);
@@ -535,14 +661,48 @@ __device__ void split_chunk(FwdLds& L, const float4* __restrict__ splat, const u
   const size_t so = size_t(slot) * 256 + tid;
   const float tf = __hip_atomic_load(&ws.tfirst[so], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const bool known = tf >= 0.0f;
-  const float pre = known ? tf : 1.0f;
+  const float pre = known ? tf * kChainSlack : 1.0f;
   PixelFwd s{1.0f, 0.0f, 0.0f, 0.0f, 0u, pre < kTStop};
   fwd_walk<true>(L, splat, vals, start, lo, hi, tile_ox(tile, tx), tile_oy(tile, tx), float(px) + 0.5f,
                  float(py) + 0.5f, pre, s, ws.sat + size_t(slot) * 256, c, ws.tfirst + size_t(slot) * 256, state,
                  known);
+  if (__syncthreads_count(cut()) == kBlock) return;   // nothing of it is read
   const size_t io = size_t(item) * 256 + tid;
   ws.part4[io] = make_float4(s.T, s.c0, s.c1, s.c2);
   ws.partl[io] = s.last;
+  // the chain: from where it stands (k <= c), past this chunk if the chunks in between have
+  // published their own transmittance: T in front of the next chunk, an upper bound of the
+  // combine's (every value any chunk writes here is one, also when two chunks move the
+  // chain at once: a product that misses factors <= 1 is larger); one of them wins the
+  // move; every pixel below kTChainDone: the later chunks are not needed
+  __hip_atomic_store(&ws.tl[io], s.T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) s_chain = __hip_atomic_load(ws.chain + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t k = s_chain;
+  if (k > c || c - k > kChainLook) return;
+  const uint32_t fi = ws.slot_first[slot];
+  float f = __hip_atomic_load(&ws.tfirst[so], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  bool ok = f >= 0.0f;
+  float t[kChainLook];
+#pragma unroll
+  for (uint32_t j = 0; j < kChainLook; ++j)
+    t[j] = k + j < c ? __hip_atomic_load(&ws.tl[size_t(fi + k + j) * 256 + tid], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT)
+                     : 1.0f;
+#pragma unroll
+  for (uint32_t j = 0; j < kChainLook; ++j) {
+    ok = ok && t[j] >= 0.0f;
+    f = f * t[j];
+  }
+  f = f * s.T;
+  if (__syncthreads_count(ok) < kBlock) return;   // not all out yet: the chain stays
+  if (tid == 0) s_chain = atomicCAS(ws.chain + slot, k, c + 1u);
+  __syncthreads();
+  if (s_chain != k) return;                        // another chunk moved it
+  __hip_atomic_store(&ws.tfirst[so], f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int alive = __syncthreads_count(f >= kTChainDone);
+  if (tid == 0 && alive == 0)
+    __hip_atomic_store(ws.state + slot, kDoneBase + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Phase 1, one launch: blocks [0, num_tiles) walk the first `first` pairs of every tile,
@@ -559,7 +719,8 @@ __global__ void __launch_bounds__(256) render_fwd_kernel(const float4* __restric
                                                           uint32_t* __restrict__ n_contrib) {
   __shared__ FwdLds L;
   if (blockIdx.x >= uint32_t(num_tiles)) {
-    split_chunk(L, splat, vals, ranges, ws, num_tiles, tx, first, chunk, blockIdx.x - uint32_t(num_tiles));
+    const uint32_t j = blockIdx.x - uint32_t(num_tiles);
+    if (j < ws.counters[1]) split_chunk(L, splat, vals, ranges, ws, num_tiles, tx, first, chunk, ws.disp[j]);
     return;
   }
   const int tile = int(ws.order[blockIdx.x]);
@@ -580,7 +741,10 @@ __global__ void __launch_bounds__(256) render_fwd_kernel(const float4* __restric
       ws.stl[o] = s.last | (s.done ? kFlag : 0u);
       __hip_atomic_store(&ws.tfirst[o], s.done ? 0.0f : s.T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
-      if (tid == 0) __hip_atomic_store(ws.state + slot, kSplit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) {
+        __hip_atomic_store(ws.state + slot, kSplit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ws.chain + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       return;
     }
     if (tid == 0) __hip_atomic_store(ws.state + slot, kNotSplit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -610,7 +774,7 @@ __global__ void __launch_bounds__(1024) split_combine_kernel(SplitWs ws) {
   __shared__ int32_t s_stop[4][256];
   __shared__ uint32_t s_last[4][256];
   const uint32_t slot = blockIdx.x;
-  if (slot >= ws.counters[0] || ws.state[slot] != kSplit) return;
+  if (slot >= ws.counters[0] || !is_split(ws.state[slot])) return;
   const int tid = threadIdx.x, q = tid >> 8, p = tid & 255;
   const size_t so = size_t(slot) * 256 + p;
   const uint32_t fi = ws.slot_first[slot], nch = ws.slot_nch[slot];
@@ -703,7 +867,7 @@ __global__ void __launch_bounds__(256) split_rewalk_kernel(const float4* __restr
   if (item >= ws.counters[1]) return;
   const uint2 sc = ws.items[item];
   const uint32_t slot = sc.x, c = sc.y;
-  if (ws.state[slot] != kSplit) return;
+  if (!is_split(ws.state[slot])) return;
   const int tid = threadIdx.x;
   const size_t so = size_t(slot) * 256 + tid;
   const bool need = ws.stopc[so] == int32_t(c);
@@ -739,7 +903,7 @@ __global__ void __launch_bounds__(256) split_finalize_kernel(SplitWs ws, int tx,
                                                               float* __restrict__ T_final,
                                                               uint32_t* __restrict__ n_contrib) {
   const uint32_t slot = blockIdx.x;
-  if (slot >= ws.counters[0] || ws.state[slot] != kSplit) return;
+  if (slot >= ws.counters[0] || !is_split(ws.state[slot])) return;
   const int tid = threadIdx.x;
   const int tile = int(ws.slot_tile[slot]);
   const int px = (tile % tx) * kTile + pixel_x(tid);
@@ -1082,7 +1246,7 @@ __device__ void bwd_tile(BwdLds& L, const BwdArgs& A, const SplitWs& ws, int til
     s.g1 = dL_dimg[HW + p];
     s.g2 = dL_dimg[2 * HW + p];
     const int32_t slot = ws.slot_of_tile[tile];
-    if (slot >= 0 && ws.state[slot] == kSplit && ws.stopc[size_t(slot) * 256 + tid] >= 0) {
+    if (slot >= 0 && is_split(ws.state[slot]) && ws.stopc[size_t(slot) * 256 + tid] >= 0) {
       // the pixel's pairs continue past the first segment: start from its end state
       const float4 b = ws.bnd1[size_t(slot) * 256 + tid];
       s.T = b.x; s.S0 = b.y; s.S1 = b.z; s.S2 = b.w;
@@ -1111,7 +1275,7 @@ __device__ void bwd_chunk(BwdLds& L, const BwdArgs& A, const SplitWs& ws, uint32
   float* __restrict__ gscreen = A.gscreen;
   const uint2 sc = ws.items[item];
   const uint32_t slot = sc.x, c = sc.y;
-  if (ws.state[slot] != kSplit) return;   // a candidate that its first segment finished
+  if (!is_split(ws.state[slot])) return;   // a candidate that its first segment finished
   const int tile = int(ws.slot_tile[slot]);
   const int tid = threadIdx.x;
   const int px = (tile % tx) * kTile + pixel_x(tid);
