@@ -16,19 +16,24 @@
 // pairs form chunks of `chunk` pairs that separate blocks walk at the same time.  The
 // chunks of every tile longer than `first` (a candidate) are blocks of the same launch
 // as the first segments, after them, so that they fill the CUs that the last long first
-// segments leave idle; a tile's first segment publishes, when it ends, whether the tile
-// is split and each pixel's transmittance T_first.
+// segments leave idle, taken chunk index first (every candidate's chunk 0, then chunk 1,
+// ...); a tile's first segment publishes, when it ends, whether the tile is split and
+// each pixel's transmittance T_first.
 //   chunk c   walks from T = 1 (the local transmittance and colour of the chunk), stops
-//             a pixel once B T_local < 1e-4, B = T_first once it is out (1 before: an
-//             upper bound of the transmittance in front of the chunk either way, also in
-//             fp32, where every factor is at most 1, so the overall T has dropped below
-//             1e-4 by then too, and the combine finds the stop in this chunk or an earlier
-//             one), drops pixels that an earlier chunk has already saturated (a per-pixel
-//             "first saturating chunk" marker, polled), and stops altogether once the
-//             tile turns out not split;
+//             a pixel once B T_local < 1e-4, B an upper bound of the transmittance in
+//             front of the chunk (1 before T_first is out; then the tile's running chain,
+//             below), also in fp32, where every factor is at most 1, so the overall T
+//             has dropped below 1e-4 by then too and the combine finds the stop in this
+//             chunk or an earlier one; drops pixels that an earlier chunk has already
+//             saturated (a per-pixel "first saturating chunk" marker, polled); stops
+//             altogether once the tile turns out not split.  Then it publishes its own
+//             T and moves the tile's chain past itself: the chain holds, per pixel, the
+//             product of T_first and the chunks' own T up to some chunk (an upper bound
+//             of the front the combine will compute); once it is below 1e-4 for every
+//             pixel, the tile's later chunks are not walked;
 //   combine   per pixel, chains the chunks: T_front(c+1) = T_front(c) T_c and
 //             colour += T_front(c) C_c, from T_front(0) = T_first, until the product
-//             falls below 1e-4;
+//             falls below 1e-4 (four threads per pixel, a quarter of the chunks each);
 //   re-walk   the chunk where that happens is walked again from T_front with the
 //             test T_front * T_local < 1e-4 to find the exact last pair;
 //   finalize  writes the pixel and, back to front, the state at each chunk end
@@ -36,7 +41,8 @@
 //             accumulated from the background and each chunk's own colour sum).
 // The split path keeps per pixel one boundary state per chunk of a split tile.
 // It changes only where products are rounded (T_front T_local instead of one
-// running product).
+// running product).  No block ever waits for another: what a chunk reads from the
+// others (device-scope loads) only tightens its bound when it is out.
 
 // Backward.  Each pixel walks from its last contributing pair back to the first,
 // recovering T by division and carrying S ([DR] "The trick"); every entry's nine
