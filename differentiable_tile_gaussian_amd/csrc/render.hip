@@ -112,7 +112,8 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // entries per split tile, per-item arrays 256 entries per chunk.
 struct SplitWs {
   uint32_t* order;        // [NT] tiles, longest list first
-  uint32_t* counters;     // [0] split tiles (slots), [1] chunks (items)
+  uint32_t* counters;     // [0] split candidates (slots), [1] chunks (items), [2] tiles walked
+                          // before the chunks, [3] 1 if the dispatch is chunk index first
   int32_t* slot_of_tile;  // [NT] slot or -1
   uint32_t* slot_tile;    // [S]
   uint32_t* slot_first;   // [S] first item of the slot
@@ -156,7 +157,7 @@ __host__ __device__ inline SplitWs carve(void* ws, const SplitDims& d) {
   SplitWs w;
   auto take = [&](size_t bytes) { char* q = p; p += a256(bytes); return q; };
   w.order = reinterpret_cast<uint32_t*>(take(d.NT * 4));
-  w.counters = reinterpret_cast<uint32_t*>(take(8));
+  w.counters = reinterpret_cast<uint32_t*>(take(16));
   w.slot_of_tile = reinterpret_cast<int32_t*>(take(d.NT * 4));
   w.slot_tile = reinterpret_cast<uint32_t*>(take(d.S * 4));
   w.slot_first = reinterpret_cast<uint32_t*>(take(d.S * 4));
@@ -181,7 +182,7 @@ __host__ __device__ inline SplitWs carve(void* ws, const SplitDims& d) {
 }
 
 __host__ __device__ inline size_t carve_bytes(const SplitDims& d) {
-  return a256(d.NT * 4) + a256(8) + a256(d.NT * 4) + 3 * a256(d.S * 4) + a256(d.I * 8) + a256(d.S * 256 * 16) +
+  return a256(d.NT * 4) + a256(16) + a256(d.NT * 4) + 3 * a256(d.S * 4) + a256(d.I * 8) + a256(d.S * 256 * 16) +
          2 * a256(d.S * 256 * 4) + 2 * a256(d.S * 4) + a256(d.S * 256 * 4) + 2 * a256(d.I * 4) + a256(d.I * 256 * 4) + a256(d.I * 256 * 16) + a256(d.I * 256 * 4) + a256(d.S * 256 * 4) +
          a256(d.S * 256 * 16) + a256(d.S * 256 * 4) + a256(d.S * 256 * 16);
 }
@@ -255,6 +256,9 @@ __device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* s_w, uint32_t& 
 // running transmittance chain can tell them when their tile is finished; with more than
 // kMaxChunksOrdered chunks in a tile, tile by tile instead.
 constexpr uint32_t kMaxChunksOrdered = 2048;
+// Tiles of at least 2^(kEarlyBucket - 1) pairs (and every split candidate) are dispatched
+// before the split chunks.
+constexpr int kEarlyBucket = 9;
 __global__ void __launch_bounds__(1024) tile_order_kernel(const uint32_t* __restrict__ ranges, int num_tiles,
                                                            SplitWs ws, int first, int chunk,
                                                            RenderHeader* __restrict__ hdr, RenderHeader h) {
@@ -292,6 +296,10 @@ __global__ void __launch_bounds__(1024) tile_order_kernel(const uint32_t* __rest
   // the candidates sit in the buckets from that of first + 1 up: the order's first `span`
   const int bf = 32 - __clz(uint32_t(first) + 1u);
   const int span = int(s_pos[bf] + s_cnt[bf]);
+  // the tiles of bucket eb and longer (every candidate among them) are walked before the
+  // chunks, the others after them
+  const int eb = min(kEarlyBucket, bf);
+  const uint32_t early = s_pos[eb] + s_cnt[eb];
   __syncthreads();
   for (int t = tid; t < num_tiles; t += blockDim.x) {
     const uint32_t len = ranges[num_tiles + t] - ranges[t];
@@ -368,6 +376,7 @@ __global__ void __launch_bounds__(1024) tile_order_kernel(const uint32_t* __rest
   if (tid == 0) {
     ws.counters[0] = ordered ? run_s : s_slots;
     ws.counters[1] = ordered ? run_i : s_items;
+    ws.counters[2] = early;
     ws.counters[3] = ordered ? 1u : 0u;
   }
 }
@@ -539,6 +548,36 @@ struct PixelFwd {
   bool done;
 };
 
+// Blends, in order, the entries of a wave's list (byte offsets of records within recs),
+// four at a time, until every pixel of the wave is done; a pixel stops once pre * T < 1e-4.
+// The calling wave has a pixel that is not done.
+__device__ __forceinline__ void walk_list(const uint32_t* list, int len, const char* recs, PixelFwd& s, float fx,
+                                          float fy, float pre) {
+  bool all_done = false;
+  for (int k = 0; k < len && !all_done; k += 4) {
+    const uint4 ix = *reinterpret_cast<const uint4*>(list + k);
+    const uint32_t off[4] = {ix.x, ix.y, ix.z, ix.w};
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const FwdRec& r = *reinterpret_cast<const FwdRec*>(recs + off[q4]);
+      const float4 a = r.a, b = r.b;
+      const float2 c = make_float2(r.c.x, r.c.y);
+      const float dx = fx - a.x, dy = fy - a.y;
+      float alpha = fminf(kAlphaCap, fast_exp2(pair_q(a.z, a.w, b.x, b.y, dx, dy)));
+      const bool ok = !s.done && alpha >= kAlphaMin;
+      alpha = ok ? alpha : 0.0f;
+      const float w = alpha * s.T;
+      s.c0 += w * b.z;
+      s.c1 += w * b.w;
+      s.c2 += w * c.x;
+      s.T = s.T * (1.0f - alpha);
+      s.last = ok ? __float_as_uint(c.y) : s.last;
+      s.done = s.done || (pre * s.T < kTStop);
+    }
+    all_done = __all(s.done);
+  }
+}
+
 // Walks the pairs [lo, hi) of a tile list starting at `start`.  A pixel stops once
 // pre * T < 1e-4 (pre = 1 for a walk whose T is the overall transmittance).  With
 // POLL (a chunk of a split candidate), after every batch: a pixel also stops when
@@ -571,32 +610,10 @@ __device__ void fwd_walk(FwdLds& L, const float4* __restrict__ splat, const uint
     uint32_t nm = 0u;
     if (nxt < hi) stage_fwd(splat, vals[start + uint32_t(nxt)], nxt, ox, oy, nr, nm);
     // walk the batch entries whose quadrant bit is set, in order, four at a time
-    bool all_done = __all(s.done);
-    if (!all_done) {
+    if (!__all(s.done)) {
       const int len = build_list(L.m[buf], kBatch - 1, list, uint32_t(buf * (kBatch + 1) * sizeof(FwdRec)),
                                  uint32_t(sizeof(FwdRec)));
-      for (int k = 0; k < len && !all_done; k += 4) {
-        const uint4 ix = *reinterpret_cast<const uint4*>(list + k);
-        const uint32_t off[4] = {ix.x, ix.y, ix.z, ix.w};
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const FwdRec& r = *reinterpret_cast<const FwdRec*>(recs + off[q4]);
-          const float4 a = r.a, b = r.b;
-          const float2 c = make_float2(r.c.x, r.c.y);
-          const float dx = fx - a.x, dy = fy - a.y;
-          float alpha = fminf(kAlphaCap, fast_exp2(pair_q(a.z, a.w, b.x, b.y, dx, dy)));
-          const bool ok = !s.done && alpha >= kAlphaMin;
-          alpha = ok ? alpha : 0.0f;
-          const float w = alpha * s.T;
-          s.c0 += w * b.z;
-          s.c1 += w * b.w;
-          s.c2 += w * c.x;
-          s.T = s.T * (1.0f - alpha);
-          s.last = ok ? __float_as_uint(c.y) : s.last;
-          s.done = s.done || (pre * s.T < kTStop);
-        }
-        all_done = __all(s.done);
-      }
+      walk_list(list, len, recs, s, fx, fy, pre);
     }
     if (base + kBatch < hi) {
       L.rec[buf ^ 1][tid] = nr; L.m[buf ^ 1][tid] = nm;
@@ -711,11 +728,12 @@ __device__ void split_chunk(FwdLds& L, const float4* __restrict__ splat, const u
     __hip_atomic_store(ws.state + slot, kDoneBase + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Phase 1, one launch: blocks [0, num_tiles) walk the first `first` pairs of every tile,
-// longest list first; the blocks after them walk the chunks of the split candidates, so
-// that they fill the CUs that the last long first segments leave idle.  A candidate whose
-// pixels are not all finished after its first segment is split: its block writes no
-// output, leaves its state for the combine and publishes its per-pixel T for the chunks.
+// Phase 1, one launch over num_tiles + the items' capacity blocks, in dispatch order: the
+// first segments of the tiles of at least 256 pairs (longest list first), the chunks of the
+// split candidates, the first segments of the other tiles (the short walks fill the CUs at
+// the end), then blocks with nothing to do.  A candidate whose pixels are not all finished
+// after its first segment is split: its block writes no output, leaves its state for the
+// combine and publishes its per-pixel T for the chunks.
 __global__ void __launch_bounds__(256) render_fwd_kernel(const float4* __restrict__ splat,
                                                           const uint32_t* __restrict__ vals,
                                                           const uint32_t* __restrict__ ranges, SplitWs ws,
@@ -724,12 +742,17 @@ __global__ void __launch_bounds__(256) render_fwd_kernel(const float4* __restric
                                                           float* __restrict__ T_final,
                                                           uint32_t* __restrict__ n_contrib) {
   __shared__ FwdLds L;
-  if (blockIdx.x >= uint32_t(num_tiles)) {
-    const uint32_t j = blockIdx.x - uint32_t(num_tiles);
-    if (j < ws.counters[1]) split_chunk(L, splat, vals, ranges, ws, num_tiles, tx, first, chunk, ws.disp[j]);
-    return;
+  const uint32_t early = ws.counters[2], items = ws.counters[1], b = blockIdx.x;
+  uint32_t pos = b;   // place in the tile order
+  if (b >= early) {
+    if (b < early + items) {
+      split_chunk(L, splat, vals, ranges, ws, num_tiles, tx, first, chunk, ws.disp[b - early]);
+      return;
+    }
+    pos = b - items;
+    if (pos >= uint32_t(num_tiles)) return;
   }
-  const int tile = int(ws.order[blockIdx.x]);
+  const int tile = int(ws.order[pos]);
   const int tid = threadIdx.x;
   const int px = (tile % tx) * kTile + pixel_x(tid);
   const int py = (tile / tx) * kTile + pixel_y(tid);
