@@ -52,7 +52,7 @@ def kernel_bytes(kernel, n, deg, P, fuse=True):
 # kernels by stage (the names the library's per-kernel timing uses)
 STAGE_KERNELS = {
     "preprocess": ("preprocess_fwd", "sum_counts"),
-    "bin_sort": ("radix_upsweep", "radix_scan", "radix_downsweep", "scan_reduce", "scan_apply", "emit_pairs",
+    "bin_sort": ("radix_upsweep", "radix_scan", "radix_downsweep", "scan_reduce", "scan_apply", "block_starts", "emit_pairs",
                  "tile_ranges", "fill_u32"),
     "render_fwd": ("render_fwd", "tile_order", "split_reset", "split_combine", "split_rewalk",
                    "split_finalize"),

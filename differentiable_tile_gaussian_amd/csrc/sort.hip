@@ -457,7 +457,9 @@ __global__ void __launch_bounds__(256) block_starts_kernel(const uint32_t* __res
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   const int nv = int(*n_vis);
   if (r >= n || r >= nv) return;
-  const uint32_t e = r == nv - 1 ? max(offs[r + 1], pairs) : min(offs[r + 1], pairs);
+  // the last one also owns the blocks past its pairs; no block at or past `pairs` exists
+  // (a pair count below the projection's must not write past the array)
+  const uint32_t e = r == nv - 1 ? pairs : min(offs[r + 1], pairs);
   for (uint32_t b = (offs[r] + kEmitPairs - 1) / kEmitPairs; b * uint32_t(kEmitPairs) < e; ++b) block_first[b] = uint32_t(r);
 }
 
