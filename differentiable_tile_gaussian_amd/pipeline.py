@@ -26,6 +26,35 @@ def position_lr_decay(lr_final, max_steps, lr=DEFAULT_LR):
     return rates
 
 
+class TrainingSchedule:
+    """When the trainer's discrete operations happen, by Adam step t >= 1 (host logic; the
+    operations themselves are library calls).
+
+    Density control ([GST] density-control slide, its explanation of the usual settings:
+    densification starts after step 500, repeats every 100 steps and stops at 15000, and
+    opacity is reset every 3000 steps, capped at 0.01), read as: densify after the steps
+    t with start < t < stop and t % every == 0; reset opacity after the steps t with
+    t < stop and t % reset_every == 0 (resets belong to the densification phase); a reset
+    at a densification step is made by that densification's gs_densify call.
+
+    SH degree ramp ([GSG] "Spherical harmonics": one more band about every 1000 steps),
+    read as: step t sums the bands up to min(scene degree, t // sh_every)."""
+
+    def __init__(self, start=500, every=100, stop=15000, reset_every=3000, opacity_cap=0.01, sh_every=1000):
+        assert every > 0 and reset_every > 0 and sh_every > 0 and 0.0 < opacity_cap < 1.0
+        self.start, self.every, self.stop, self.reset_every = start, every, stop, reset_every
+        self.opacity_cap, self.sh_every = opacity_cap, sh_every
+
+    def densify_after(self, t):
+        return self.start < t < self.stop and t % self.every == 0
+
+    def reset_after(self, t):
+        return t < self.stop and t % self.reset_every == 0
+
+    def sh_degree(self, t, scene_degree):
+        return min(scene_degree, t // self.sh_every)
+
+
 class Pipeline:
     def __init__(self, params: torch.Tensor, sh_degree: int, width: int, height: int, lam: float = 0.2,
                  lr=DEFAULT_LR, betas=(0.9, 0.999), eps=1e-8, cfg: gs.GsConfig = None, lr_schedule=None):
@@ -204,6 +233,29 @@ class Pipeline:
         assert n_chk == n_new
         self.params, self.m, self.v, self.dstats = params, m, v, stats
         self._resize(n_new)
+        return counts
+
+    def after_step(self, sched: TrainingSchedule, grad_threshold, prune_opacity, prune_scale, split_scale,
+                   generator=None):
+        """What `sched` puts after the Adam step just made (step self.t): a densification
+        (with the opacity reset if one also falls there), or the reset alone (a gs_densify
+        that prunes, clones and splits nothing; like every densification it also zeroes the
+        statistics); then the active SH degree of the next step.  Returns the counts
+        (kept, cloned, split) of a densification, else None."""
+        t = self.t
+        counts = None
+        reset = sched.reset_after(t)
+        if sched.densify_after(t):
+            counts = self.densify(grad_threshold, prune_opacity, prune_scale, split_scale, reset_opacity=reset,
+                                  opacity_cap=sched.opacity_cap, generator=generator)
+        elif reset:
+            self.densify(float("inf"), 0.0, float("inf"), 1.0, reset_opacity=True, opacity_cap=sched.opacity_cap,
+                         generator=generator)
+        deg = sched.sh_degree(t + 1, self.deg)
+        if deg != self.cfg.active_sh_degree:   # a new settings object: the caller's is not changed
+            c = self.cfg
+            self.cfg = gs.GsConfig(c.grad_sums, deg, c.mip_compensation, c.split_first, c.split_chunk)
+            self.projected_for = None   # a projection made for the next camera used the old degree
         return counts
 
     def _resize(self, n):

@@ -206,3 +206,41 @@ def test_training_loop_with_density_control(torch_cuda):
         a = getattr(pl.proj, name)[:pl.n].cpu().numpy()
         b = getattr(ref, name)[:pl.n].cpu().numpy()
         np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32), err_msg=name)
+
+
+def test_scheduled_density_control_and_sh_ramp(torch_cuda):
+    """Pipeline.after_step with a compressed TrainingSchedule (densify after steps 2 and 4,
+    the opacity reset with the one after step 4, one more SH band every two steps): the
+    population changes only after those steps, by the counts gs_densify reports, every
+    opacity is at most the cap right after the reset, and each step passes the active SH
+    degree the ramp gives."""
+    import math
+    torch = torch_cuda
+    from differentiable_tile_gaussian_amd import gs
+    from differentiable_tile_gaussian_amd.pipeline import Pipeline, TrainingSchedule
+    s = scenes.random_scene(71, 4000, 3, spread=1.3, logscale_std=0.5)
+    s.params[0:3] *= 0.8
+    cams = [gs.make_camera(scenes.look_at_origin((0.6, 0.4, -4.5), 160, 120, 150.0)),
+            gs.make_camera(scenes.look_at_origin((-2.5, 0.2, -3.8), 160, 120, 150.0))]
+    rng = np.random.default_rng(8)
+    targets = [torch.from_numpy(rng.random((3, 120, 160), dtype=np.float32)).cuda() for _ in cams]
+    sched = TrainingSchedule(start=1, every=2, stop=6, reset_every=4, sh_every=2)
+    pl = Pipeline(torch.from_numpy(s.params).cuda(), 3, 160, 120, cfg=gs.GsConfig(active_sh_degree=sched.sh_degree(1, 3)))
+    pl.enable_density_stats()
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    cap = float(np.float32(math.log(0.01 / 0.99)))
+    for t in range(1, 7):
+        assert pl.cfg.active_sh_degree == sched.sh_degree(t, 3)
+        loss = pl.step(cams[t % 2], targets[t % 2], next_cam=cams[(t + 1) % 2])
+        assert pl.t == t
+        n0 = pl.n
+        counts = pl.after_step(sched, 0.0, 0.005, 1.0, 0.05, generator=gen)
+        torch.cuda.synchronize()
+        assert np.isfinite(loss.cpu().numpy()).all()
+        if t in (2, 4):
+            kept, cloned, split = counts
+            assert pl.n == kept + cloned + 2 * split and cloned + split > 0
+        else:
+            assert counts is None and pl.n == n0
+        if t == 4:
+            assert (pl.planar(pl.params)[10].cpu().numpy() <= cap).all()
