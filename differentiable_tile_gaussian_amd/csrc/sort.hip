@@ -22,10 +22,10 @@
 //
 // Radix passes use digits of up to 9 bits, reduce-then-scan:
 //   upsweep   per-block digit histogram (LDS atomics; for tile digits, which crowd, one
-//             atomic per distinct digit of a wave) into a [512][blocks] table (blocks in an
-//             XCD-aware order, below)
+//             atomic per distinct digit of a wave) into a [digits][blocks] table (blocks in an
+//             XCD-aware order, below; rows for the pass's 2^bits digits only)
 //   scan      one block per digit: exclusive prefix along its row, and the row total
-//   downsweep the digit bases from the 512 row totals; each wave ranks its 1024
+//   downsweep the digit bases from the row totals; each wave ranks its 1024
 //             consecutive items against a wave-private digit histogram (64-lane ballots:
 //             no match-any on CDNA, one ballot per digit bit gives each lane its peer
 //             mask), one barrier turns the four histograms into run starts, then a local
@@ -220,7 +220,8 @@ __global__ void __launch_bounds__(kSortThreads) radix_upsweep_kernel(PassIn in, 
     if (threadIdx.x == 0) dp.bmax[blockIdx.x] = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
   }
   __syncthreads();
-  for (int d = threadIdx.x; d < kRadix; d += kSortThreads) hist[hist_at(d, blockIdx.x)] = s_hist[d];
+  // only the pass's digits have rows (a tile pass of 6 bits uses 64 of them)
+  for (int d = threadIdx.x; d <= int(mask); d += kSortThreads) hist[hist_at(d, blockIdx.x)] = s_hist[d];
 }
 
 // One block per digit: hist_scan[d][b] = sum of hist[d][b'] over b' < b, rowtot[d] the row sum.
@@ -316,8 +317,10 @@ __global__ void __launch_bounds__(kSortThreads) radix_downsweep_kernel(
   // the digit bases: exclusive prefix of the row totals, plus the earlier blocks' counts
   // of the digit (block 0 also stores the number of items)
   {
-    const uint32_t g0 = hist_scan[hist_at(d0, blockIdx.x)], g1 = hist_scan[hist_at(d0 + 1, blockIdx.x)];
-    const uint32_t r0 = rowtot[d0], r1 = rowtot[d0 + 1];
+    // digits above mask have no rows (and no items)
+    const bool u0 = uint32_t(d0) <= mask, u1 = uint32_t(d0 + 1) <= mask;
+    const uint32_t g0 = u0 ? hist_scan[hist_at(d0, blockIdx.x)] : 0u, g1 = u1 ? hist_scan[hist_at(d0 + 1, blockIdx.x)] : 0u;
+    const uint32_t r0 = u0 ? rowtot[d0] : 0u, r1 = u1 ? rowtot[d0 + 1] : 0u;
     uint32_t all_total, unused;
     const uint32_t pre = block_scan2(r0 + r1, 0u, s_scan, all_total, unused).x;
     if (count_out && blockIdx.x == 0 && tid == 0) *count_out = all_total;
@@ -694,7 +697,7 @@ hipError_t radix_pass(const PassIn& in, const DepthPlan& dp, int nb, int shift, 
   }
   {
     GSK_PROF("radix_scan", s);
-    radix_scan_kernel<<<kRadix, kSortThreads, 0, s>>>(dp, nb, w.hist, w.hist_scan, w.rowtot);
+    radix_scan_kernel<<<int(mask) + 1, kSortThreads, 0, s>>>(dp, nb, w.hist, w.hist_scan, w.rowtot);
   }
   GSK_PROF("radix_downsweep", s);
   radix_downsweep_kernel<SRC><<<nb, kSortThreads, 0, s>>>(in, dp, shift, mask, nb, w.hist_scan, w.rowtot, keys_out,
