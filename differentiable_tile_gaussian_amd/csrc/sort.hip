@@ -226,13 +226,16 @@ __global__ void __launch_bounds__(kSortThreads) radix_upsweep_kernel(PassIn in, 
 
 // One block per digit: hist_scan[d][b] = sum of hist[d][b'] over b' < b, rowtot[d] the row sum.
 // In the depth sort's first pass, block 0 also reduces the blocks' maxima of d.  The row is
-// taken eight groups (1024 blocks) at a time: loaded in table order (coalesced), put in
-// block order through LDS, scanned, and written back in table order.
+// taken sixteen groups (2048 blocks, eight per thread) at a time: loaded in table order
+// (coalesced), put in block order through LDS, scanned, and written back in table order.
+// A row is one block's chain of such steps, so fewer, wider steps shorten it.
 __global__ void __launch_bounds__(kSortThreads) radix_scan_kernel(DepthPlan dp, int nb,
                                                                    const uint32_t* __restrict__ hist,
                                                                    uint32_t* __restrict__ hist_scan,
                                                                    uint32_t* __restrict__ rowtot) {
-  constexpr int kChunk = 8 * kHistGroup;   // blocks per step, four per thread
+  constexpr int kPer = 8;                                   // blocks per thread and step
+  constexpr int kStepGroups = kPer * kSortThreads / kHistGroup;
+  constexpr int kChunk = kStepGroups * kHistGroup;          // blocks per step
   __shared__ uint32_t s_scan[2 * kWaves];
   __shared__ uint32_t s_v[kChunk];
   if (!pass_runs(dp)) return;
@@ -250,13 +253,13 @@ __global__ void __launch_bounds__(kSortThreads) radix_scan_kernel(DepthPlan dp, 
   const uint32_t d = blockIdx.x;
   const int groups = (nb + kHistGroup - 1) / kHistGroup;
   uint32_t carry = 0u;
-  for (int g0 = 0; g0 < groups; g0 += 8) {
+  for (int g0 = 0; g0 < groups; g0 += kStepGroups) {
     // table position j (group g0 + j / 128, place j % 128) holds block 128 (g0 + j / 128)
     // + 8 (place % 16) + place / 16; b0 = that block less 128 g0
-    size_t at[4];
-    uint32_t b0[4];
+    size_t at[kPer];
+    uint32_t b0[kPer];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kPer; ++k) {
       const int j = tid + kSortThreads * k, g = g0 + j / kHistGroup, place = j % kHistGroup;
       b0[k] = uint32_t(j / kHistGroup) * kHistGroup + uint32_t(place % 16) * 8u + uint32_t(place / 16);
       at[k] = (size_t(g) * kRadix + d) * kHistGroup + size_t(place);
@@ -264,22 +267,22 @@ __global__ void __launch_bounds__(kSortThreads) radix_scan_kernel(DepthPlan dp, 
       s_v[b0[k]] = uint32_t(g0) * kHistGroup + b0[k] < uint32_t(nb) ? hist[at[k]] : 0u;
     }
     __syncthreads();
-    uint32_t v[4], sum = 0u;
+    uint32_t v[kPer], sum = 0u;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[k] = s_v[4 * tid + k];
+    for (int k = 0; k < kPer; ++k) {
+      v[k] = s_v[kPer * tid + k];
       sum += v[k];
     }
     uint32_t total, unused;
     uint32_t run = carry + block_scan2(sum, 0u, s_scan, total, unused).x;   // (its barriers order s_v)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      s_v[4 * tid + k] = run;
+    for (int k = 0; k < kPer; ++k) {
+      s_v[kPer * tid + k] = run;
       run += v[k];
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < kPer; ++k)
       if (uint32_t(g0) * kHistGroup + b0[k] < uint32_t(nb)) hist_scan[at[k]] = s_v[b0[k]];
     carry += total;
     __syncthreads();   // s_v is loaded again
