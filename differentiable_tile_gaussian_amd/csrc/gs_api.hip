@@ -26,6 +26,17 @@ int32_t hip_fail(hipError_t e, const char* where) {
   return fail(GS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
+// The most (tile, Gaussian) pairs a call accepts: 2^32 - 2^25.  Kernels keep pair indices
+// in 32 bits and add to an index below the count at most a split size (<= 2^24) or a
+// block's items, which this margin keeps below 2^32.
+constexpr uint64_t kMaxPairs = (uint64_t(1) << 32) - (uint64_t(1) << 25);
+
+int32_t check_pairs(uint32_t total_pairs) {
+  if (total_pairs > kMaxPairs)
+    return fail(GS_ERR_CAPACITY, "pair count %u exceeds 2^32 - 2^25", total_pairs);
+  return GS_OK;
+}
+
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 constexpr int32_t kDefaultSplitFirst = 2048;
@@ -240,8 +251,8 @@ int32_t finish_preprocess(gs_proj* out, int n, float znear, const PreWs& w, uint
   e = hipEventSynchronize(hs->copied);
   if (e != hipSuccess) return hip_fail(e, "preprocess sync");
   const uint64_t host_total = *hs->pinned;
-  if (host_total > 0xffffffffull)
-    return fail(GS_ERR_CAPACITY, "pair count %llu exceeds 2^32 - 1", (unsigned long long)host_total);
+  if (host_total > kMaxPairs)
+    return fail(GS_ERR_CAPACITY, "pair count %llu exceeds 2^32 - 2^25", (unsigned long long)host_total);
   *total_pairs = uint32_t(host_total);
   return GS_OK;
 }
@@ -260,6 +271,7 @@ int32_t gs_bin_sort(const gs_proj* proj, int64_t n, const gs_camera* cam, uint32
   if (!ranges) return fail(GS_ERR_INVALID_ARG, "ranges is null");
   if (total_pairs > 0 && (!keys || !vals)) return fail(GS_ERR_INVALID_ARG, "keys or vals is null");
   if (total_pairs > 0 && n == 0) return fail(GS_ERR_INVALID_ARG, "pairs without Gaussians");
+  if ((st = check_pairs(total_pairs)) != GS_OK) return st;
   if (capacity < total_pairs)
     return fail(GS_ERR_CAPACITY, "key capacity %u < %u pairs", capacity, total_pairs);
   const size_t need = gsk::bin_sort_ws_bytes(total_pairs);
@@ -282,6 +294,7 @@ int32_t gs_render_fwd(const gs_proj* proj, int64_t n, const uint32_t* vals, cons
   if ((st = check_proj(proj, n, false)) != GS_OK) return st;
   if (!ranges || !rgb || !T_final || !n_contrib) return fail(GS_ERR_INVALID_ARG, "an output or ranges is null");
   if (total_pairs > 0 && !vals) return fail(GS_ERR_INVALID_ARG, "vals is null");
+  if ((st = check_pairs(total_pairs)) != GS_OK) return st;
   const size_t need = gsk::render_ws_bytes(cam->width, cam->height, total_pairs, c.split_first, c.split_chunk, 0);
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "render workspace needs %zu bytes", need);
   hipError_t e = gsk::launch_render_fwd(*proj, vals, ranges, *cam, total_pairs, rgb, T_final, n_contrib, ws,
@@ -337,6 +350,7 @@ static int32_t render_bwd_common(const gs_scene* scene, const gs_proj* proj, con
   if (!ranges || !T_final || !n_contrib || !dL_dimg) return fail(GS_ERR_INVALID_ARG, "a render input is null");
   if (scene->n > 0 && (!gscreen || !gparams)) return fail(GS_ERR_INVALID_ARG, "gscreen or gparams is null");
   if (total_pairs > 0 && !vals) return fail(GS_ERR_INVALID_ARG, "vals is null");
+  if ((st = check_pairs(total_pairs)) != GS_OK) return st;
   const size_t need = render_ws(scene->n, total_pairs, cam->width, cam->height, c);
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "render workspace needs %zu bytes", need);
   hipStream_t s = as_stream(stream);
@@ -437,6 +451,7 @@ int32_t gs_render_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs
   if (!ranges || !T_final || !n_contrib || !dL_dimg) return fail(GS_ERR_INVALID_ARG, "a render input is null");
   if (n > 0 && (!gscreen || !m || !v)) return fail(GS_ERR_INVALID_ARG, "gscreen, m or v is null");
   if (total_pairs > 0 && !vals) return fail(GS_ERR_INVALID_ARG, "vals is null");
+  if ((st = check_pairs(total_pairs)) != GS_OK) return st;
   const size_t need = render_ws(n, total_pairs, cam->width, cam->height, c);
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "render workspace needs %zu bytes", need);
   hipStream_t s = as_stream(stream);
@@ -472,6 +487,7 @@ int32_t gs_render_bwd_adam_project(float* params, int64_t n, int32_t sh_degree, 
   if (!ranges || !T_final || !n_contrib || !dL_dimg) return fail(GS_ERR_INVALID_ARG, "a render input is null");
   if (n > 0 && (!gscreen || !m || !v)) return fail(GS_ERR_INVALID_ARG, "gscreen, m or v is null");
   if (total_pairs > 0 && !vals) return fail(GS_ERR_INVALID_ARG, "vals is null");
+  if ((st = check_pairs(total_pairs)) != GS_OK) return st;
   const size_t need = render_ws(n, total_pairs, cam->width, cam->height, c);
   if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "render workspace needs %zu bytes", need);
   const size_t need_pre = pre_ws_bytes(n);

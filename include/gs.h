@@ -61,7 +61,8 @@ extern "C" {
 typedef enum gs_status {
   GS_OK = 0,
   GS_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad camera, step < 1 ... */
-  GS_ERR_CAPACITY = -2,     /* key buffer or workspace too small, or more than 2^32 - 1 pairs */
+  GS_ERR_CAPACITY = -2,     /* key buffer or workspace too small, or more than 2^32 - 2^25 pairs
+                               (every call that takes or returns a pair count checks it) */
   GS_ERR_UNSUPPORTED = -3,  /* SH degree outside 0..3, image larger than 65535 tiles per side */
   GS_ERR_HIP = -4           /* a HIP launch or runtime call failed */
 } gs_status;
@@ -176,7 +177,7 @@ enum { GS_GRAD_SUMS_FLOAT = 0, GS_GRAD_SUMS_FIXED = 1 };
  * it is copied to the host before the depth ordering is enqueued, which may still be
  * running on `stream` when the call returns.  The library keeps one pinned 8-byte host
  * word and one event per device and host thread for this copy.  GS_ERR_CAPACITY if the
- * pair count exceeds 2^32 - 1. */
+ * pair count exceeds 2^32 - 2^25 (the kernels keep pair indices in 32 bits). */
 /* cfg: active_sh_degree, mip_compensation. */
 int32_t gs_preprocess(const gs_scene* scene, const gs_camera* cam, gs_proj* out, uint32_t* total_pairs,
                       void* ws, size_t ws_bytes, const gs_config* cfg, void* stream);

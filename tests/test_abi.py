@@ -65,6 +65,16 @@ def test_argument_errors_without_gpu(gs):
     assert L.gs_bin_sort(C.byref(proj), 10, C.byref(cam), 100, 1, 1, 50, 1, 1, 1 << 30,
                          None) == gs.GS_ERR_CAPACITY
     assert "capacity" in gs.gs_last_error()
+    # more pairs than the kernels' 32-bit pair indices allow (2^32 - 2^25): refused by every
+    # call that takes a pair count; at the limit the next check (the workspace) decides
+    top = (1 << 32) - (1 << 25)
+    for pairs, msg in ((top + 1, "2^32 - 2^25"), (0xffffffff, "2^32 - 2^25"), (top, "workspace")):
+        assert L.gs_bin_sort(C.byref(proj), 10, C.byref(cam), pairs, 1, 1, 0xffffffff, 1, 1, 1,
+                             None) == gs.GS_ERR_CAPACITY
+        assert msg in gs.gs_last_error()
+        assert L.gs_render_fwd(C.byref(proj), 10, 1, 1, pairs, C.byref(cam), 1, 1, 1, 1, 1, None,
+                               None) == gs.GS_ERR_CAPACITY
+        assert msg in gs.gs_last_error()
     # Adam step must start at 1
     lr = (C.c_float * 5)(1, 1, 1, 1, 1)
     assert L.gs_adam_step(1, 1, 1, 1, 10, 0, lr, 0.9, 0.999, 1e-8, 0, None) == gs.GS_ERR_INVALID_ARG
