@@ -58,6 +58,9 @@ constexpr int kDepthPassesMax = 4;                      // 36 bits >= the 31 of 
 // L2 instead of each taking a line of HBM traffic.  Blocks go in groups of 128: a group
 // holds, per digit, 128 entries, block 128 g + 8 k + x at position 16 x + k.
 constexpr int kHistGroup = 128;
+// The scan takes a row kScanStepGroups groups (kScanPer entries per thread) per block.
+constexpr int kScanPer = 8;
+constexpr int kScanStepGroups = kScanPer * kSortThreads / kHistGroup;   // 16
 __host__ __device__ inline size_t hist_at(uint32_t d, uint32_t b) {
   const uint32_t g = b / kHistGroup, w = b % kHistGroup;
   return (size_t(g) * kRadix + d) * kHistGroup + (w % 8u) * 16u + w / 8u;
@@ -224,23 +227,25 @@ __global__ void __launch_bounds__(kSortThreads) radix_upsweep_kernel(PassIn in, 
   for (int d = threadIdx.x; d <= int(mask); d += kSortThreads) hist[hist_at(d, blockIdx.x)] = s_hist[d];
 }
 
-// One block per digit: hist_scan[d][b] = sum of hist[d][b'] over b' < b, rowtot[d] the row sum.
-// In the depth sort's first pass, block 0 also reduces the blocks' maxima of d.  The row is
-// taken sixteen groups (2048 blocks, eight per thread) at a time: loaded in table order
-// (coalesced), put in block order through LDS, scanned, and written back in table order.
-// A row is one block's chain of such steps, so fewer, wider steps shorten it.
+// Blocks (digit d, segment s): hist_scan[d][b] = sum of hist[d][b'] over b' < b, rowtot[d]
+// the row sum.  A row is cut into segments of kScanStepGroups groups (2048 blocks), one block
+// each: the block sums the row's complete groups before its segment, then takes the segment
+// in one step (eight entries per thread): loaded in table order (coalesced), put in block
+// order through LDS, scanned, and written back in table order; the last segment's block
+// stores the row sum.  In the depth sort's first pass, block (0, 0) also reduces the blocks'
+// maxima of d.
 __global__ void __launch_bounds__(kSortThreads) radix_scan_kernel(DepthPlan dp, int nb,
                                                                    const uint32_t* __restrict__ hist,
                                                                    uint32_t* __restrict__ hist_scan,
                                                                    uint32_t* __restrict__ rowtot) {
-  constexpr int kPer = 8;                                   // blocks per thread and step
-  constexpr int kStepGroups = kPer * kSortThreads / kHistGroup;
+  constexpr int kPer = kScanPer;
+  constexpr int kStepGroups = kScanStepGroups;
   constexpr int kChunk = kStepGroups * kHistGroup;          // blocks per step
   __shared__ uint32_t s_scan[2 * kWaves];
   __shared__ uint32_t s_v[kChunk];
   if (!pass_runs(dp)) return;
   const int tid = threadIdx.x;
-  if (dp.pass == 0 && blockIdx.x == 0) {
+  if (dp.pass == 0 && blockIdx.x == 0 && blockIdx.y == 0) {
     uint32_t m = 0u;
     for (int b = tid; b < nb; b += kSortThreads) m = max(m, dp.bmax[b]);
 #pragma unroll
@@ -252,8 +257,20 @@ __global__ void __launch_bounds__(kSortThreads) radix_scan_kernel(DepthPlan dp, 
   }
   const uint32_t d = blockIdx.x;
   const int groups = (nb + kHistGroup - 1) / kHistGroup;
+  const int g_begin = int(blockIdx.y) * kStepGroups, g_end = min(groups, g_begin + kStepGroups);
+  // carry: the row's sum over the groups before the segment (whole groups: only the last
+  // group of a row can hold padding past nb, and it is in the last segment)
   uint32_t carry = 0u;
-  for (int g0 = 0; g0 < groups; g0 += kStepGroups) {
+  if (g_begin > 0) {
+    uint32_t part = 0u;
+    const size_t row = size_t(d) * kHistGroup;
+#pragma unroll 8
+    for (int idx = tid; idx < g_begin * kHistGroup; idx += kSortThreads)
+      part += hist[size_t(idx / kHistGroup) * kRadix * kHistGroup + row + size_t(idx % kHistGroup)];
+    uint32_t unused;
+    block_scan2(part, 0u, s_scan, carry, unused);
+  }
+  for (int g0 = g_begin; g0 < g_end; g0 += kStepGroups) {
     // table position j (group g0 + j / 128, place j % 128) holds block 128 (g0 + j / 128)
     // + 8 (place % 16) + place / 16; b0 = that block less 128 g0
     size_t at[kPer];
@@ -287,7 +304,7 @@ __global__ void __launch_bounds__(kSortThreads) radix_scan_kernel(DepthPlan dp, 
     carry += total;
     __syncthreads();   // s_v is loaded again
   }
-  if (tid == 0) rowtot[d] = carry;
+  if (tid == 0 && blockIdx.y == gridDim.y - 1) rowtot[d] = carry;
 }
 
 // With count_out, block 0 stores the number of items (for kFromDepth, of visible
@@ -700,7 +717,8 @@ hipError_t radix_pass(const PassIn& in, const DepthPlan& dp, int nb, int shift, 
   }
   {
     GSK_PROF("radix_scan", s);
-    radix_scan_kernel<<<int(mask) + 1, kSortThreads, 0, s>>>(dp, nb, w.hist, w.hist_scan, w.rowtot);
+    const int segs = std::max(1, int(div_up(div_up(nb, kHistGroup), kScanStepGroups)));
+    radix_scan_kernel<<<dim3(int(mask) + 1, segs), kSortThreads, 0, s>>>(dp, nb, w.hist, w.hist_scan, w.rowtot);
   }
   GSK_PROF("radix_downsweep", s);
   radix_downsweep_kernel<SRC><<<nb, kSortThreads, 0, s>>>(in, dp, shift, mask, nb, w.hist_scan, w.rowtot, keys_out,
