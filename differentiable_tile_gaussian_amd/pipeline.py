@@ -5,6 +5,7 @@ torch allocates memory and provides the stream; every stage runs in libgs.so.
 """
 from __future__ import annotations
 
+import numpy as np
 import torch
 
 from . import gs
@@ -24,6 +25,14 @@ def position_lr_decay(lr_final, max_steps, lr=DEFAULT_LR):
         f = min(max((t - 1) / max(max_steps - 1, 1), 0.0), 1.0)
         return (math.exp(l0 + f * (l1 - l0)),) + tuple(lr[1:])
     return rates
+
+
+def blocked_to_planar(blocked: np.ndarray, n: int) -> np.ndarray:
+    """Host copy of a blocked parameter array ([groups][P][64]: parameter p of Gaussian i at
+    [i // 64][p][i % 64]) as [P][n]."""
+    groups, P, w = blocked.shape
+    assert w == 64 and groups * 64 >= n
+    return np.ascontiguousarray(blocked.transpose(1, 0, 2).reshape(P, groups * 64)[:, :n])
 
 
 class TrainingSchedule:
@@ -257,6 +266,53 @@ class Pipeline:
             self.cfg = gs.GsConfig(c.grad_sums, deg, c.mip_compensation, c.split_first, c.split_chunk)
             self.projected_for = None   # a projection made for the next camera used the old degree
         return counts
+
+    # ------------------------------------------------------------ checkpoint / resume
+    def checkpoint_state(self) -> dict:
+        """The training state as host arrays: the Gaussian count, SH degree, Adam step, the
+        parameters and both Adam moments in the blocked layout ([groups][P][64]), the
+        density statistics (an empty array when not kept), and the settings (image size,
+        loss weight, rates, betas, eps, the gs_config fields).  A learning-rate schedule
+        is code, not state: pass it again when resuming."""
+        c = self.cfg
+        return {
+            "n": np.int64(self.n), "sh_degree": np.int64(self.deg), "t": np.int64(self.t),
+            "size": np.array([self.W, self.H], np.int64), "lam": np.float64(self.lam),
+            "lr": np.array(self.lr, np.float64), "betas": np.array(self.betas, np.float64),
+            "eps": np.float64(self.eps),
+            "cfg": np.array([c.grad_sums, c.active_sh_degree, c.mip_compensation, c.split_first, c.split_chunk],
+                            np.int64),
+            "params": self.params.cpu().numpy(), "m": self.m.cpu().numpy(), "v": self.v.cpu().numpy(),
+            "dstats": (self.dstats.cpu().numpy() if self.dstats is not None else np.zeros((0, 2), np.float32)),
+        }
+
+    def save_checkpoint(self, path):
+        """checkpoint_state() to an uncompressed .npz file (plain arrays, no pickled objects)."""
+        np.savez(path, **self.checkpoint_state())
+
+    @classmethod
+    def from_checkpoint(cls, path, device="cuda", lr_schedule=None) -> "Pipeline":
+        """A pipeline in the state save_checkpoint wrote: the next step is Adam step t + 1 on
+        the same parameters and moments (the next camera is projected again)."""
+        with np.load(path) as z:
+            st = {k: z[k] for k in z.files}
+        n, deg = int(st["n"]), int(st["sh_degree"])
+        P = 11 + 3 * (deg + 1) ** 2
+        groups = max((n + 63) // 64, 1)
+        for k in ("params", "m", "v"):
+            assert st[k].shape == (groups, P, 64) and st[k].dtype == np.float32, k
+        planar = blocked_to_planar(st["params"], n)
+        cfg = gs.GsConfig(*(int(x) for x in st["cfg"]))
+        W, H = (int(x) for x in st["size"])
+        pl = cls(torch.from_numpy(planar).to(device), deg, W, H, lam=float(st["lam"]),
+                 lr=tuple(float(x) for x in st["lr"]), betas=tuple(float(x) for x in st["betas"]),
+                 eps=float(st["eps"]), cfg=cfg, lr_schedule=lr_schedule)
+        pl.m = torch.from_numpy(st["m"]).to(device)
+        pl.v = torch.from_numpy(st["v"]).to(device)
+        pl.t = int(st["t"])
+        if st["dstats"].shape[0] > 0:
+            pl.dstats = torch.from_numpy(st["dstats"]).to(device)
+        return pl
 
     def _resize(self, n):
         """Buffers sized by the Gaussian count, after the population changed."""
