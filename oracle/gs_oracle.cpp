@@ -1154,6 +1154,31 @@ void or_render_pixels_f32(int64_t n, const float* uv, const float* conic, const 
   }
 }
 
+// Depth complexity of a subset of pixels: how many entries of the pixel's tile list have
+// an alpha (capped, as in the blend) of at least 1/255, over the whole list, with no early
+// stop.  This is the quantity the high depth-complexity workload is built to make large
+// (a median of at least 200 entries per pixel); the alpha is the blend's, [GST] opacity
+// slide and [GSG] "The painting itself".
+void or_overlap_pixels_f32(int64_t n, const float* uv, const float* conic, const float* opac, const uint32_t* vals,
+                           const uint32_t* ranges, const Camera* cam, int64_t npix, const int32_t* px,
+                           const int32_t* py, uint32_t* count) {
+  const int tx = tiles_x(*cam), ty = tiles_y(*cam);
+  const int64_t nt = int64_t(tx) * ty;
+  for (int64_t k = 0; k < npix; ++k) {
+    const float fx = float(px[k]) + 0.5f, fy = float(py[k]) + 0.5f;
+    const int64_t t = int64_t(py[k] / kTile) * tx + px[k] / kTile;
+    uint32_t c = 0;
+    for (uint32_t i = ranges[t]; i < ranges[nt + t]; ++i) {
+      const uint32_t g = vals[i];
+      const float dx = fx - uv[g], dy = fy - uv[n + g];
+      const float e = 0.5f * (conic[g] * dx * dx + conic[2 * n + g] * dy * dy) + conic[n + g] * dx * dy;
+      const float alpha = std::min(float(kAlphaCap), opac[g] * exp_r(-e));
+      if (!(alpha < alpha_min<float>())) ++c;
+    }
+    count[k] = c;
+  }
+}
+
 // Tiled backward blend: gscreen [9][n] is overwritten; mass ([2][9][n]) and count
 // ([n]), when given, are overwritten with the term magnitudes blend_pixel_bwd records.
 void or_render_bwd_f32(int64_t n, const float* uv, const float* conic, const float* opac, const float* rgb,

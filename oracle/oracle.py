@@ -83,6 +83,7 @@ def _declare(L):
     L.or_render_fwd_f64.restype = I64
     L.or_render_untiled_f32.argtypes = [I64] + [P] * 6 + [P, P, P]
     L.or_render_pixels_f32.argtypes = [I64] + [P] * 6 + [P, I64, P, P, P, P, P, P]
+    L.or_overlap_pixels_f32.argtypes = [I64] + [P] * 5 + [P, I64, P, P, P]
     L.or_render_bwd_f32.argtypes = [I64] + [P] * 6 + [P] + [P] * 6
     L.or_render_bwd_f64.argtypes = [I64] + [P] * 6 + [P] + [P] * 4
     L.or_flip_risk_f32.argtypes = [I64] + [P] * 6 + [P, P, C.c_double, P, P, P, P, P, P, P, P, P, P, P,
@@ -244,6 +245,18 @@ def render_pixels(pre, vals, ranges, cam, xs, ys):
                                _p(_c(vals, np.uint32)), _p(_c(ranges, np.uint32)), C.byref(c), k, _p(xs),
                                _p(ys), _p(rgb), _p(T), _p(nc), _p(margin))
     return dict(rgb=rgb, T=T, n_contrib=nc, margin=margin)
+
+
+def overlap_pixels(pre, vals, ranges, cam, xs, ys):
+    """Per listed pixel, the entries of its tile's list whose alpha reaches 1/255, counted
+    over the whole list (no early stop): the depth complexity a workload puts on it."""
+    xs = _c(xs, np.int32)
+    ys = _c(ys, np.int32)
+    count = np.zeros(xs.shape[0], np.uint32)
+    c = make_camera(cam)
+    lib().or_overlap_pixels_f32(pre["n"], _p(pre["uv"]), _p(pre["conic"]), _p(pre["opac"]), _p(_c(vals, np.uint32)),
+                                _p(_c(ranges, np.uint32)), C.byref(c), xs.shape[0], _p(xs), _p(ys), _p(count))
+    return count
 
 
 def render_bwd(pre, vals, ranges, cam, fwd, dLdI, with_mass=False):
