@@ -4,10 +4,10 @@ list whose alpha reaches 1/255 over the whole list, with no early stop.
 A hand-built pin: forty Gaussians of opacity 0.5 centred on one pixel count forty there
 although the blend stops after fourteen (0.5^14 < 1e-4, [GSG] "The painting itself"), a
 Gaussian of opacity 0.003 (below 1/255 everywhere, [GST] opacity slide) is listed but not
-counted, and a pixel of the same tile far from the centre counts none.  Then the property
-the high depth-complexity workload (3M Gaussians in a slab before a 1280x720 camera) is
-built to have: a median overlap of at least 200 entries per pixel, over a seeded sample of
-pixels."""
+counted, and a pixel of the same tile far from the centre counts none.  Then, per workload,
+the tile-list lengths and the overlap over a seeded sample of pixels, and the property the
+high depth-complexity workload (3M Gaussians in a slab before a 1280x720 camera) is built
+to have: a median overlap of at least 200 entries per pixel."""
 import math
 
 import numpy as np
@@ -37,14 +37,22 @@ def test_overlap_counts_every_entry_at_or_above_the_floor(oracle):
 
 
 @pytest.mark.slow
-def test_stress_workload_median_overlap(oracle):
-    wl = scenes.config4()
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_workload_depth_complexity(oracle, cfg):
+    """Per workload (camera 0): pairs, median and largest tile-list length, and the overlap
+    over 2048 seeded pixels; the high depth-complexity workload (3M Gaussians) must reach a
+    median overlap of 200."""
+    wl = scenes.CONFIGS[cfg]()
     cam = wl.cameras[0]
     pre = oracle.preprocess(wl.scene.params, wl.scene.sh_degree, cam)
     _, vals, ranges = oracle.bin_sort(pre, cam)
-    rng = np.random.default_rng(404)
+    lens = ranges[1].astype(np.int64) - ranges[0]
+    rng = np.random.default_rng(400 + cfg)
     xs, ys = rng.integers(0, cam.width, 2048), rng.integers(0, cam.height, 2048)
     c = oracle.overlap_pixels(pre, vals, ranges, cam, xs, ys)
     q = np.percentile(c, [25, 50, 75])
-    print(f"overlap over 2048 pixels: quartiles {q}, max {c.max()}, pairs {len(vals)}")
-    assert np.median(c) >= 200
+    print(f"workload {cfg}: {len(vals)} pairs, tile lists median {int(np.median(lens))} max {lens.max()}, "
+          f"overlap quartiles {q} max {c.max()}")
+    assert lens.sum() == len(vals) and c.max() <= lens.max()
+    if cfg == 4:
+        assert np.median(c) >= 200
