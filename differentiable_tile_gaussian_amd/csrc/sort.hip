@@ -24,7 +24,8 @@
 //   upsweep   per-block digit histogram (LDS atomics; for tile digits, which crowd, one
 //             atomic per distinct digit of a wave) into a [digits][blocks] table (blocks in an
 //             XCD-aware order, below; rows for the pass's 2^bits digits only)
-//   scan      one block per digit: exclusive prefix along its row, and the row total
+//   scan      per digit, exclusive prefix along its row and the row total, a row taken in
+//             segments of 2048 blocks, one scan block each (the carry summed directly)
 //   downsweep the digit bases from the row totals; each wave ranks its 1024
 //             consecutive items against a wave-private digit histogram (64-lane ballots:
 //             no match-any on CDNA, one ballot per digit bit gives each lane its peer
