@@ -12,6 +12,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
+from tests import test_oracle_overlap as opins
 from tests import test_oracle_pins as pins
 from tests import test_oracle_threshold_pins as tpins
 
@@ -82,6 +83,41 @@ MUTANTS = {
         "dsx[idx] = -(A1 * A2) / (B1 * B2 * B2);",
         "dsx[idx] = (A1 * A2) / (B1 * B2 * B2);",
         [_pin(pins.test_loss_gradient_finite_difference)]),
+    # the method's constants and the other stages
+    "dilation_dropped": (
+        "constexpr double kDilation = 0.3;",
+        "constexpr double kDilation = 0.0;",
+        [_pin(pins.test_projected_spread, 10.0, 5.0), _pin(pins.test_projected_spread, 20.0, 2.5)]),
+    "alpha_floor_one_in_256": (
+        "constexpr double kAlphaMinInv = 255.0;",
+        "constexpr double kAlphaMinInv = 256.0;",
+        [_pin(pins.test_alpha_floor_is_one_in_255)]),
+    "early_stop_threshold_looser": (
+        "constexpr double kTStop = 1e-4;",
+        "constexpr double kTStop = 1e-3;",
+        [_pin(pins.test_early_stop_and_contributor_count),
+         _pin(opins.test_overlap_counts_every_entry_at_or_above_the_floor)]),
+    "extent_cut_smaller": (
+        "constexpr double kExtentCut = 4.5;",
+        "constexpr double kExtentCut = 3.0;",
+        [_pin(pins.test_tiled_render_equals_untiled_below_extent_opacity)]),
+    "tile_id_column_major": (
+        "keys[pos] = (uint64_t(uint32_t(y * tx + x)) << 32) | dbits;",
+        "keys[pos] = (uint64_t(uint32_t(x * ty + y)) << 32) | dbits;",
+        [_pin(pins.test_sort_and_ranges_brute_force, 0), _pin(pins.test_sort_and_ranges_brute_force, 1)]),
+    "ssim_window_sigma": (
+        "const double sigma = 1.5;",
+        "const double sigma = 2.0;",
+        [_pin(pins.test_loss_matches_independent_separable_ssim)]),
+    "loss_weights_swapped": (
+        "out[0] = (R(1) - lambda) * L1 + lambda * (R(1) - SS);",
+        "out[0] = lambda * L1 + (R(1) - lambda) * (R(1) - SS);",
+        [_pin(pins.test_loss_gradient_finite_difference), _pin(pins.test_l1_subgradient_and_normaliser)]),
+    "adam_bias_correction_dropped": (
+        "const R mh = m[k] / R(bc1), vh = v[k] / R(bc2);",
+        "const R mh = m[k], vh = v[k];",
+        [_pin(pins.test_adam_first_step_closed_form),
+         _pin(pins.test_adam_zero_gradient_keeps_moving_with_momentum)]),
 }
 
 

@@ -389,6 +389,19 @@ def test_early_stop_and_contributor_count(oracle):
     np.testing.assert_allclose(fwd["rgb"][:, 0, 0], 1.0 - fwd["T"][0, 0], atol=1e-6)
 
 
+def test_alpha_floor_is_one_in_255(oracle):
+    """[GST] opacity slide: an entry whose alpha is below 1/255 is skipped, one at or above
+    it blends.  One Gaussian centred on pixel (0, 0) (alpha there = its opacity), with an
+    opacity between 1/256 and 1/255 and then just above 1/255."""
+    cam = axis_camera()
+    for o, blended in ((0.003912, False), (0.003930, True)):
+        assert (o >= 1.0 / 255.0) == blended and o > 1.0 / 256.0
+        p = hand_scene([dict(mean=(0, 0, 2.0), opacity=o, colour=(1, 1, 1))])
+        pre, keys, vals, ranges, fwd = oracle.forward(p, 0, cam)
+        assert fwd["n_contrib"][0, 0] == (1 if blended else 0)
+        assert (fwd["T"][0, 0] < 1.0) == blended
+
+
 # ------------------------------------------------------------------ loss
 def _ssim_separable(x, y):
     """Independent SSIM: separable 1-D Gaussian correlation with zero padding (scipy)."""
