@@ -113,6 +113,23 @@ MUTANTS = {
         "out[0] = (R(1) - lambda) * L1 + lambda * (R(1) - SS);",
         "out[0] = lambda * L1 + (R(1) - lambda) * (R(1) - SS);",
         [_pin(pins.test_loss_gradient_finite_difference), _pin(pins.test_l1_subgradient_and_normaliser)]),
+    "colour_clamp_dropped": (
+        "f.rgb[ch] = smooth ? col : std::max(col, R(0));",
+        "f.rgb[ch] = col;",
+        [_pin(tpins.test_clamped_channel_closed_form)]),
+    "sh_band1_sign": (
+        "const R n10 = R(sh_norm(1, 0)), n11 = R(-sh_norm(1, 1));",
+        "const R n10 = R(sh_norm(1, 0)), n11 = R(sh_norm(1, 1));",
+        [_pin(pins.test_sh_printed_constants)]),
+    "depth_order_reversed": (
+        "    std::memcpy(&dbits, &depth[i], 4);\n",
+        "    std::memcpy(&dbits, &depth[i], 4);\n    dbits = ~dbits;\n",
+        [_pin(pins.test_sort_and_ranges_brute_force, 0), _pin(pins.test_two_gaussian_compositing,
+                                                               "two_gaussians_nearest_first")]),
+    "opacity_activation_exp": (
+        "  f.ob = sigmoid_r(P(10));",
+        "  f.ob = exp_r(P(10));",
+        [_pin(pins.test_opacity_gradient_worked_example), _fd_smooth([0])]),
     "adam_bias_correction_dropped": (
         "const R mh = m[k] / R(bc1), vh = v[k] / R(bc2);",
         "const R mh = m[k], vh = v[k];",
