@@ -12,7 +12,12 @@ from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
+from tests import test_oracle_camera_grad as cpins
+from tests import test_oracle_charbonnier as chpins
+from tests import test_oracle_densify as dpins
+from tests import test_oracle_mip as mpins
 from tests import test_oracle_overlap as opins
+from tests import test_oracle_relocate as rpins
 from tests import test_oracle_pins as pins
 from tests import test_oracle_threshold_pins as tpins
 
@@ -35,6 +40,17 @@ def _fd_thresholded(cases):
 
 def _pin(fn, *args):
     return lambda O: fn(O, *args)
+
+
+def _with_mip(fn, *args):
+    """A pin that needs the Mip-Splatting compensation switched on (its fixture's job)."""
+    def run(O):
+        O.set_mip_compensation(True)
+        try:
+            fn(O, *args)
+        finally:
+            O.set_mip_compensation(False)
+    return run
 
 
 # name: (statement as written in the oracle, the planted version, pins that must catch it)
@@ -130,6 +146,27 @@ MUTANTS = {
         "  f.ob = sigmoid_r(P(10));",
         "  f.ob = exp_r(P(10));",
         [_pin(pins.test_opacity_gradient_worked_example), _fd_smooth([0])]),
+    # the trainer's variants and density control
+    "camera_rotation_sign": (
+        "out[0] += M[2][1] - M[1][2];",
+        "out[0] += M[1][2] - M[2][1];",
+        [_pin(cpins.test_camera_grad_matches_central_differences), _pin(cpins.test_position_only_is_the_pages_torque)]),
+    "split_children_not_shrunk": (
+        "if (shrink && k >= 3 && k < 6) th = th - lscale_shrink;",
+        "",
+        [_pin(dpins.test_hand_built_population)]),
+    "relocated_donor_not_shrunk": (
+        "for (int pl = 3; pl < 6; ++pl) params[pl * n + bd] = params[pl * n + bd] - lscale_shrink;",
+        "",
+        [_pin(rpins.test_hand_worked_population)]),
+    "charbonnier_delta_kept": (
+        "sl += double(root - delta);",
+        "sl += double(root);",
+        [_pin(chpins.test_zero_error_is_zero), _pin(chpins.test_single_element_closed_form)]),
+    "mip_compensation_inverted": (
+        "f.comp = std::sqrt(std::max(f.detv, R(0)) / f.det);",
+        "f.comp = std::sqrt(f.det / std::max(f.detv, R(1e-30)));",
+        [_with_mip(mpins.test_isotropic_closed_form)]),
     "adam_bias_correction_dropped": (
         "const R mh = m[k] / R(bc1), vh = v[k] / R(bc2);",
         "const R mh = m[k], vh = v[k];",
